@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--rotate R]
+                    [--cpu-seconds S] [--no-cpu-baseline]
+
+One step is the whole path over one batch: the gate front end (la_gate: g = decay, beta)
+followed by the decode step (rgdr_decode, in place on the state pool), both in the HIP
+library through its C ABI. The default workload is the batched GQA decode shape
+(B=64, H_q=16, H_v=32, T=1, D_k=D_v=128, a 256-slot pool, 64 slots in use), with gate
+inputs that reproduce its g/beta recipe.
+
+Measurement:
+  * R independent buffer sets (pool and every per-step input/output) are rotated so that
+    consecutive steps stream their state from HBM, not from the 256 MB Infinity Cache;
+    R is chosen so one rotation touches >= 1 GiB of distinct state.
+  * W eager warmup steps; then the K timed steps are captured in one HIP graph (so
+    Python launch overhead is not measured), uploaded with one untimed replay, and timed
+    with events on the launch stream around a single replay.
+  * The decode kernel's average duration comes from event pairs around each of K eager
+    launches on the same stream (second pass); its roofline uses the method's
+    algorithmic bytes per launch.
+  * cpu_baseline: the fp64 C oracle (single-threaded) repeats the same step on the host
+    for about --cpu-seconds.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) + token·head steps/sec, gated-delta decode"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(inp):
+    """Algorithmic bytes of one decode call: the state tile of every served (b, h) read and
+    written once (bf16), per valid token-head q+k (shared over H_v/H_q heads), v, out,
+    beta, g, gk, and 12 B of index data per batch entry."""
+    import numpy as np
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    n_pairs = int(valid.sum()) * inp.Hv
+    tok_heads = int(lens[valid].sum()) * inp.Hv
+    per_tok = (4 * inp.Dk * inp.Hq / inp.Hv + 2 * inp.Dv + 2 * inp.Dv + 2 + 4 + 4 * inp.Dk)
+    return int(n_pairs * 4 * inp.Dk * inp.Dv + tok_heads * per_tok + 12 * inp.B), tok_heads
+
+
+def gate_bytes(inp):
+    n = inp.B * inp.T * inp.Hv
+    return n * (4 + 4 + 4 + 2) + 2 * 4 * inp.Hv  # a, b in; decay fp32, beta bf16 out; 2 [H]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the decode path has "
+              "no cross-GPU work; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_rgdr_amd as rg
+    import workloads
+
+    rg.library()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wid = args.workload
+    inp = workloads.make_workload(wid, gate_inputs=True)
+    B, Hq, Hv, T, Dk, Dv, N = inp.B, inp.Hq, inp.Hv, inp.T, inp.Dk, inp.Dv, inp.N_slots
+    dbytes, tok_heads = decode_bytes(inp)
+    gbytes = gate_bytes(inp)
+    step_bytes = dbytes + gbytes
+    touched = int(((inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < N)).sum()) \
+        * Hv * Dk * Dv * 2
+    R = args.rotate or max(2, math.ceil((1 << 30) / max(touched, 1)))
+    R = min(R, args.steps) if args.steps > 0 else R
+    log(f"workload {wid}: {workloads.WORKLOAD_NAMES[wid]}; decode bytes/call {dbytes}, "
+        f"gate bytes/call {gbytes}; rotation sets {R}")
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = dict(q=bits(inp.query), k=bits(inp.key), v=bits(inp.value), pool=bits(inp.state),
+                gk=torch.from_numpy(inp.gk).to(dev), a=torch.from_numpy(inp.gate_a).to(dev),
+                b=torch.from_numpy(inp.gate_b).to(dev))
+    dt = torch.from_numpy(inp.dt_bias).to(dev)
+    ds = torch.from_numpy(inp.decay_scale).to(dev)
+    lens = torch.from_numpy(inp.actual_seq_lengths).to(dev)
+    idx = torch.from_numpy(inp.ssm_state_indices).to(dev)
+    nacc = torch.from_numpy(inp.num_accepted_tokens).to(dev)
+    sets = []
+    for _ in range(R):
+        s = {k_: v_.clone() for k_, v_ in base.items()}
+        s["g"] = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+        s["beta"] = torch.empty((B, T, Hv), dtype=torch.bfloat16, device=dev)
+        s["out"] = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=dev)
+        sets.append(s)
+    del base
+    torch.cuda.synchronize()
+
+    # g and beta come out of the gate as [B, T, H_v]; the decode reads [B, H_v, T]. With
+    # T = 1 these are the same bytes; otherwise the step would need the fused gate.
+    if T != 1:
+        log("note: T > 1; the gate output layout differs from the decode's, so the step "
+            "transposes g/beta with torch (not timed as part of the kernels)")
+
+    def gate(s):
+        rg.la_gate(s["a"], dt, ds, s["b"], decay_dtype=torch.float32,
+                   beta_dtype=torch.bfloat16, decay_out=s["g"], beta_out=s["beta"])
+
+    def decode(s):
+        g_ = s["g"].view(B, Hv, T) if T == 1 else s["g"].transpose(1, 2).contiguous()
+        be = s["beta"].view(B, Hv, T) if T == 1 else s["beta"].transpose(1, 2).contiguous()
+        rg.rgdr_decode(s["q"], s["k"], s["v"], be, s["pool"], lens, idx, g_, s["gk"], nacc,
+                       inp.scale, out=s["out"])
+
+    def step(i):
+        s = sets[i % R]
+        gate(s)
+        decode(s)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup: {args.warmup} eager steps done")
+
+    # K timed steps in one graph.
+    K = args.steps
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(args.warmup + i)
+    stream.wait_stream(cap)
+    graph.replay()  # upload (untimed)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    e1.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / K
+    log(f"timed: {K} steps in {total_ms:.3f} ms ({ms_per_step * 1e3:.2f} us/step)")
+
+    # Second pass: per-launch event pairs around the decode kernel on the launch stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i in range(K):
+        s = sets[i % R]
+        gev[i][0].record(stream)
+        gate(s)
+        gev[i][1].record(stream)
+        ev[i][0].record(stream)
+        decode(s)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    gate_us = np.array([a.elapsed_time(b) * 1e3 for a, b in gev])
+    log(f"decode kernel: mean {dec_us.mean():.2f} us, median {np.median(dec_us):.2f} us, "
+        f"min {dec_us.min():.2f} us; gate kernel mean {gate_us.mean():.2f} us")
+
+    kernel_gbs = dbytes / (dec_us.mean() * 1e-6) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    steps_per_s = tok_heads / (ms_per_step * 1e-3)
+
+    traffic = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            d64, b64 = oracle.la_gate(inp.gate_a, inp.dt_bias, inp.decay_scale, inp.gate_b)
+            g32 = d64.astype(np.float32).reshape(B, T, Hv).transpose(0, 2, 1)
+            beta_bits = oracle.f64_to_bf16(b64).reshape(B, T, Hv).transpose(0, 2, 1)
+            oracle.rgdr_bf16(inp.query, inp.key, inp.value, beta_bits, inp.state,
+                             inp.actual_seq_lengths, inp.ssm_state_indices, g32, inp.gk,
+                             inp.num_accepted_tokens, inp.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds and reps >= 1:
+                break
+        cpu = {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps} full steps of this workload (gate + decode, fp64 C oracle, "
+                         f"one thread) in {el:.1f} s",
+               "token_head_steps_per_s": round(tok_heads * reps / el, 1)}
+        log(f"cpu oracle: {reps} steps in {el:.1f} s")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "storage_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workloads.WORKLOAD_NAMES[wid] + " (gate + decode step)",
+                   "B": B, "H_q": Hq, "H_v": Hv, "T": T, "D_k": Dk, "D_v": Dv,
+                   "N_slots": N, "rotation_sets": R, "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "token_head_steps_per_s": round(steps_per_s, 1),
+        "step_bytes": step_bytes,
+        "roofline": {"kernel": "rgdr_decode", "bound": "hbm", "achieved": round(kernel_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": dbytes,
+                     "avg_launch_us": round(float(dec_us.mean()), 3)},
+        "gate_avg_launch_us": round(float(gate_us.mean()), 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

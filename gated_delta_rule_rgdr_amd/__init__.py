@@ -1,0 +1,216 @@
+"""Gated-delta-rule decode for AMD MI355X (gfx950): Python binding of ``include/rgdr.h``.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``librgdr.so``; PyTorch supplies device memory and the current stream. There is no CPU
+fallback: if the library is missing, importing the binding's functions raises.
+
+* ``rgdr_decode``  -- the recurrent gated-delta-rule decode step (MindSpore Lite API page
+  "lite_boost.ops.recurrent_gated_delta_rule"), in place on a bf16 state pool.
+* ``recurrent_gated_delta_rule`` -- the page's functional form: returns ``(out, state_out)``
+  and leaves ``state`` untouched.
+* ``la_gate`` -- the gate front end (README "com.microsoft.LinearAttentionGate").
+* ``rgdr_validate`` -- synchronous check of the index arrays.
+
+A non-OK status from the library raises ``RuntimeError`` (the page's error behaviour).
+"""
+import ctypes as C
+import os
+
+import torch
+
+__all__ = ["rgdr_decode", "recurrent_gated_delta_rule", "la_gate", "rgdr_validate",
+           "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
+           "RGDR_F16", "RGDR_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librgdr.so")
+
+RGDR_F32, RGDR_F16, RGDR_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: RGDR_F32, torch.float16: RGDR_F16, torch.bfloat16: RGDR_BF16}
+
+_lib = None
+
+
+def library():
+    """Load ``librgdr.so`` (built by ``gated_delta_rule_rgdr_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_rgdr_amd.build` "
+            "(there is no fallback path)")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+    lib.rgdr_decode.restype = C.c_int
+    lib.rgdr_decode.argtypes = [vp] * 10 + [f32] + [i32] * 7 + [vp, vp, vp]
+    lib.la_gate.restype = C.c_int
+    lib.la_gate.argtypes = [vp, vp, vp, vp, C.c_int, i64, i32, vp, C.c_int, vp, C.c_int, vp]
+    lib.rgdr_validate.restype = C.c_int
+    lib.rgdr_validate.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.rgdr_validate_host.restype = C.c_int
+    lib.rgdr_validate_host.argtypes = [vp, vp, vp, i32, i32, i32]
+    lib.rgdr_status_string.restype = C.c_char_p
+    lib.rgdr_status_string.argtypes = [C.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return library().rgdr_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise RuntimeError(f"{what}: {status_string(code)}")
+
+
+def _stream_handle(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise RuntimeError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise RuntimeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise RuntimeError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+    return t
+
+
+def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
+                g, gk, num_accepted_tokens, scale=1.0, *, out=None, state_out=None,
+                stream=None):
+    """One decode step; returns ``(out, state_out)``.
+
+    Shapes (page parameter list; the state is a slot pool): query/key bf16
+    ``[B,H_q,T,D_k]``, value bf16 ``[B,H_v,T,D_v]``, beta bf16 ``[B,H_v,T]``, state_pool bf16
+    ``[N_slots,H_v,D_k,D_v]``, g fp32 ``[B,H_v,T]``, gk fp32 ``[B,H_v,T,D_k]``, the three index
+    arrays int32 ``[B]``. ``state_out`` defaults to ``state_pool`` (in-place update of the
+    named slots); ``out`` is allocated if not given.
+    """
+    lib = library()
+    _dev(query, "query", torch.bfloat16, 4)
+    B, Hq, T, Dk = query.shape
+    _dev(key, "key", torch.bfloat16, 4)
+    _dev(value, "value", torch.bfloat16, 4)
+    _dev(beta, "beta", torch.bfloat16, 3)
+    _dev(state_pool, "state_pool", torch.bfloat16, 4)
+    _dev(g, "g", torch.float32, 3)
+    _dev(gk, "gk", torch.float32, 4)
+    for nm, t in (("actual_seq_lengths", actual_seq_lengths),
+                  ("ssm_state_indices", ssm_state_indices),
+                  ("num_accepted_tokens", num_accepted_tokens)):
+        _dev(t, nm, torch.int32, 1)
+        if t.shape[0] != B:
+            raise RuntimeError(f"{nm} must have shape [{B}]")
+    Hv, Dv = value.shape[1], value.shape[3]
+    N = state_pool.shape[0]
+    if tuple(key.shape) != (B, Hq, T, Dk) or tuple(value.shape) != (B, Hv, T, Dv) \
+            or tuple(beta.shape) != (B, Hv, T) or tuple(g.shape) != (B, Hv, T) \
+            or tuple(gk.shape) != (B, Hv, T, Dk) or tuple(state_pool.shape) != (N, Hv, Dk, Dv):
+        raise RuntimeError("rgdr_decode: inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=query.device)
+    else:
+        _dev(out, "out", torch.bfloat16, 4)
+        if tuple(out.shape) != (B, Hv, T, Dv):
+            raise RuntimeError("out must be [B, H_v, T, D_v]")
+    if state_out is None:
+        state_out = state_pool
+    else:
+        _dev(state_out, "state_out", torch.bfloat16, 4)
+        if state_out.shape != state_pool.shape:
+            raise RuntimeError("state_out must have the pool's shape")
+    rc = lib.rgdr_decode(query.data_ptr(), key.data_ptr(), value.data_ptr(), beta.data_ptr(),
+                         state_pool.data_ptr(), actual_seq_lengths.data_ptr(),
+                         ssm_state_indices.data_ptr(), g.data_ptr(), gk.data_ptr(),
+                         num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T, Dk, Dv, N,
+                         out.data_ptr(), state_out.data_ptr(), _stream_handle(stream))
+    _check(rc, "rgdr_decode")
+    return out, state_out
+
+
+def recurrent_gated_delta_rule(query, key, value, beta, state, actual_seq_lengths,
+                               ssm_state_indices, g, gk, num_accepted_tokens, scale_value=1.0):
+    """The page's functional signature: ``(out, state_out)`` with ``state`` left unchanged.
+
+    ``state_out`` starts as a device copy of ``state``; the kernel then writes every slot a
+    batch entry names. Feed it back as ``state`` for the next step.
+    """
+    state_out = torch.empty_like(state)
+    state_out.copy_(state)
+    return rgdr_decode(query, key, value, beta, state_out, actual_seq_lengths,
+                       ssm_state_indices, g, gk, num_accepted_tokens, scale_value)
+
+
+def la_gate(a, dt_bias, decay_scale, b=None, *, want_beta=None, decay_dtype=None,
+            beta_dtype=None, decay_out=None, beta_out=None, stream=None):
+    """``decay = decay_scale * softplus(a + dt_bias)``, ``beta = sigmoid(b)`` (fp32 math).
+
+    ``a``/``b``: float32 or float16, any rank >= 1, head axis last. ``dt_bias`` and
+    ``decay_scale``: float32 ``[H]``. ``decay`` has ``decay_dtype`` (default: a's dtype);
+    ``beta`` (computed when ``want_beta``, default ``b is not None``) has ``beta_dtype``
+    (default a's dtype; ``torch.bfloat16`` feeds ``rgdr_decode`` directly).
+    """
+    lib = library()
+    if a.dtype not in (torch.float32, torch.float16):
+        raise RuntimeError("a must be float32 or float16")
+    _dev(a, "a", a.dtype)
+    if a.dim() < 1:
+        raise RuntimeError("a must have rank >= 1")
+    H = a.shape[-1]
+    _dev(dt_bias, "dt_bias", torch.float32, 1)
+    _dev(decay_scale, "decay_scale", torch.float32, 1)
+    if dt_bias.shape[0] != H or decay_scale.shape[0] != H:
+        raise RuntimeError("dt_bias and decay_scale must be [H]")
+    if want_beta is None:
+        want_beta = b is not None
+    if b is not None:
+        _dev(b, "b", a.dtype)
+        if b.shape != a.shape:
+            raise RuntimeError("b must have a's shape")
+    decay_dtype = decay_dtype or a.dtype
+    if decay_out is None:
+        decay_out = torch.empty(a.shape, dtype=decay_dtype, device=a.device)
+    _dev(decay_out, "decay_out", decay_dtype)
+    beta_t = None
+    if want_beta:
+        beta_dtype = beta_dtype or a.dtype
+        beta_t = beta_out if beta_out is not None else torch.empty(a.shape, dtype=beta_dtype,
+                                                                   device=a.device)
+        _dev(beta_t, "beta_out", beta_dtype)
+    n_rows = a.numel() // H if H else 0
+    rc = lib.la_gate(a.data_ptr(), dt_bias.data_ptr(), decay_scale.data_ptr(),
+                     b.data_ptr() if b is not None else None, _DTYPE_CODE[a.dtype], n_rows, H,
+                     decay_out.data_ptr(), _DTYPE_CODE[decay_dtype],
+                     beta_t.data_ptr() if beta_t is not None else None,
+                     _DTYPE_CODE[beta_dtype] if beta_t is not None else 0,
+                     _stream_handle(stream))
+    _check(rc, "la_gate")
+    return decay_out, beta_t
+
+
+def rgdr_validate(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N_slots,
+                  stream=None):
+    """Synchronous check of device index arrays; returns the status code (0 = valid)."""
+    lib = library()
+    B = actual_seq_lengths.shape[0]
+    return lib.rgdr_validate(actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
+                             num_accepted_tokens.data_ptr(), B, T, N_slots,
+                             _stream_handle(stream))
+
+
+def rgdr_validate_host(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N_slots):
+    """The same checks on host (CPU) int32 tensors; returns the status code."""
+    lib = library()
+    ts = [torch.as_tensor(x, dtype=torch.int32).contiguous()
+          for x in (actual_seq_lengths, ssm_state_indices, num_accepted_tokens)]
+    B = ts[0].shape[0]
+    return lib.rgdr_validate_host(ts[0].data_ptr(), ts[1].data_ptr(), ts[2].data_ptr(),
+                                  B, T, N_slots)

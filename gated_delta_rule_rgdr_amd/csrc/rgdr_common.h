@@ -1,0 +1,31 @@
+// rgdr_common.h -- small device helpers shared by the library's kernels (not part of the
+// C ABI). bf16 values travel as raw 16-bit patterns; fp32 is the arithmetic type.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rgdr.h"
+
+namespace rgdr {
+
+// bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__host__ __device__ __forceinline__ bool aligned(const void *p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+}  // namespace rgdr

@@ -1,0 +1,151 @@
+/*
+ * rgdr.h -- C ABI of the gfx950 (MI355X) gated-delta-rule decode library.
+ *
+ * Two operations:
+ *
+ *   rgdr_decode  The recurrent gated-delta-rule decode step of the MindSpore Lite API page
+ *                "lite_boost.ops.recurrent_gated_delta_rule" (algorithm section, parameter
+ *                list, returns, notes). For every batch entry b, every value head h and
+ *                every valid token t, in token order, on the state S (D_k rows = key
+ *                dimension, D_v columns = value dimension):
+ *                  1. decay   S = S * exp(g[t]) * exp(gk[t][i])        (row i scaled)
+ *                  2. read    kv = S^T k_t
+ *                  3. update  S = S + k_t (x) ((v_t - kv) * beta[t])   (outer product)
+ *                  4. output  o_t = S^T (q_t * scale)
+ *   la_gate      The gate front end of the kernel README "com.microsoft.LinearAttentionGate"
+ *                (Description; Inputs, Outputs, Type constraints tables):
+ *                  decay = decay_scale[h] * softplus(a + dt_bias[h]),  beta = sigmoid(b),
+ *                computed in fp32 and narrowed only on store.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers to row-major, contiguous buffers owned by
+ *     the caller. The library allocates nothing and keeps no pointer after returning.
+ *   - Calls are asynchronous on `stream` (0 = the null stream). The return value reports
+ *     only errors that the host can see before launching (arguments, shapes, alignment,
+ *     a failed launch); when it is not RGDR_OK nothing was launched.
+ *   - bf16 is the 16-bit brain float (1 sign, 8 exponent, 7 fraction bits); outputs are
+ *     rounded to it with round-to-nearest-even. Arithmetic is fp32.
+ */
+#ifndef RGDR_H
+#define RGDR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RGDR_OK = 0,
+    RGDR_ERR_NULL = 1,        /* a required pointer is NULL                                */
+    RGDR_ERR_SHAPE = 2,       /* a size is negative, or zero where not allowed; T > 8;
+                                 H_v % H_q != 0; grid too large; beta requested without b */
+    RGDR_ERR_UNSUPPORTED = 3, /* D_k not in {64, 128} or D_v not a multiple of 64           */
+    RGDR_ERR_RANGE = 4,       /* (validate) a length, count or slot index out of range     */
+    RGDR_ERR_DUPLICATE = 5,   /* (validate) two batch entries name the same slot           */
+    RGDR_ERR_DTYPE = 6,       /* a dtype code not allowed for that argument                 */
+    RGDR_ERR_HIP = 7,         /* a HIP runtime call failed                                  */
+    RGDR_ERR_ALIGN = 8        /* a pointer is not aligned as its argument requires          */
+} rgdr_status;
+
+typedef enum { RGDR_F32 = 0, RGDR_F16 = 1, RGDR_BF16 = 2 } rgdr_dtype;
+
+/*
+ * rgdr_decode -- one decode step over a batch (MindSpore Lite page above; arguments keep
+ * the page's names and meaning).
+ *
+ *   query               bf16 [B, H_q, T, D_k]  L2-normalised per head vector (caller's
+ *                       precondition, not checked). 2-byte aligned.
+ *   key                 bf16 [B, H_q, T, D_k]  as query. Value head h reads query/key head
+ *                       h / (H_v / H_q), i.e. floor(h * H_q / H_v).
+ *   value               bf16 [B, H_v, T, D_v]  16-byte aligned.
+ *   beta                bf16 [B, H_v, T]       delta step size, in (0, 1) (not checked).
+ *   state_pool          bf16 [N_slots, H_v, D_k, D_v]  the recurrent states; entry b uses
+ *                       slot ssm_state_indices[b]. 16-byte aligned.
+ *   actual_seq_lengths  int32 [B]  valid tokens L of entry b. Tokens t >= L are never read
+ *                       and their out rows are written as +0.0. Values outside [0, T] act
+ *                       as clamped to [0, T].
+ *   ssm_state_indices   int32 [B]  slot of entry b. Must be distinct (two entries naming one
+ *                       slot race). An index outside [0, N_slots) skips the entry: its out
+ *                       rows are +0.0 and no state is read or written.
+ *   g                   fp32 [B, H_v, T]        global log-decay, negative (not checked).
+ *   gk                  fp32 [B, H_v, T, D_k]   per-key-dimension log-decay, negative.
+ *   num_accepted_tokens int32 [B]  n: the state committed for entry b is the state after
+ *                       its first n tokens (clamped to [0, L]); n = L in ordinary decoding.
+ *   scale               q is multiplied by it before step 4 (the page's scale_value).
+ *   B, H_q, H_v, T, D_k, D_v, N_slots   sizes; T <= 8 (decode only), H_v % H_q == 0,
+ *                       D_k in {64, 128}, D_v a multiple of 64. B = 0 is an empty batch:
+ *                       RGDR_OK, nothing is read or launched.
+ *   out                 bf16 [B, H_v, T, D_v]  written entirely. 16-byte aligned.
+ *   state_out           bf16 [N_slots, H_v, D_k, D_v]  receives the committed state of every
+ *                       slot some entry names; other slots are not touched. It may be the
+ *                       same buffer as state_pool (in-place update); any other overlap is
+ *                       undefined. 16-byte aligned.
+ *   stream              HIP stream the kernel is enqueued on.
+ * Errors: RGDR_ERR_NULL, RGDR_ERR_SHAPE, RGDR_ERR_UNSUPPORTED, RGDR_ERR_ALIGN,
+ * RGDR_ERR_HIP (launch failure). Device-side data (lengths, indices) never causes an
+ * out-of-bounds access; rgdr_validate reports bad values.
+ */
+rgdr_status rgdr_decode(const void *query, const void *key, const void *value,
+                        const void *beta, const void *state_pool,
+                        const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+                        const float *g, const float *gk, const int32_t *num_accepted_tokens,
+                        float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                        int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                        void *state_out, hipStream_t stream);
+
+/*
+ * la_gate -- decay = decay_scale * softplus(a + dt_bias) and, when beta_out != NULL,
+ * beta = sigmoid(b) ("com.microsoft.LinearAttentionGate" README, Description and tables).
+ *
+ *   a            [n_rows, H] of ab_dtype: the decay projection; any rank >= 1 with the head
+ *                axis last, leading axes folded into n_rows.
+ *   dt_bias      fp32 [H]  per-head bias added to a.
+ *   decay_scale  fp32 [H]  per-head multiplier; for gated DeltaNet it is -exp(A_log).
+ *   b            [n_rows, H] of ab_dtype: the update-rate projection. Required when
+ *                beta_out != NULL; may be given (and is then unused) when it is NULL.
+ *   ab_dtype     RGDR_F32 or RGDR_F16 (the README's T).
+ *   n_rows, H    sizes; n_rows >= 0, H >= 1. n_rows = 0 returns RGDR_OK without reading
+ *                any pointer or launching.
+ *   decay_out    [n_rows, H] of decay_dtype (RGDR_F32 or RGDR_F16).
+ *   beta_out     [n_rows, H] of beta_dtype (RGDR_F32, RGDR_F16, or RGDR_BF16 so that it can
+ *                feed rgdr_decode's beta directly), or NULL.
+ * Arithmetic is fp32 (precise expf/log1pf); values are narrowed once, on store, with
+ * round-to-nearest-even. With T = 1, the gate's [B, 1, H] layout is the [B, H, 1] layout
+ * rgdr_decode reads for g and beta.
+ * Errors: RGDR_ERR_NULL, RGDR_ERR_SHAPE (also beta_out without b), RGDR_ERR_DTYPE,
+ * RGDR_ERR_ALIGN (element alignment), RGDR_ERR_HIP.
+ */
+rgdr_status la_gate(const void *a, const float *dt_bias, const float *decay_scale,
+                    const void *b, rgdr_dtype ab_dtype, int64_t n_rows, int32_t H,
+                    void *decay_out, rgdr_dtype decay_dtype, void *beta_out,
+                    rgdr_dtype beta_dtype, hipStream_t stream);
+
+/*
+ * rgdr_validate_host -- checks the index arrays of one rgdr_decode call, given as HOST
+ * pointers: every length in [0, T], every accepted count in [0, length], every slot index
+ * in [0, N_slots), no slot named twice. Returns RGDR_OK, RGDR_ERR_RANGE,
+ * RGDR_ERR_DUPLICATE, RGDR_ERR_NULL or RGDR_ERR_SHAPE. Pure host code.
+ */
+rgdr_status rgdr_validate_host(const int32_t *actual_seq_lengths,
+                               const int32_t *ssm_state_indices,
+                               const int32_t *num_accepted_tokens, int32_t B, int32_t T,
+                               int32_t N_slots);
+
+/*
+ * rgdr_validate -- the same checks for DEVICE pointers: copies the 3 x B int32 values to
+ * the host on `stream` and waits for that stream (synchronous; not for the hot path).
+ */
+rgdr_status rgdr_validate(const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+                          const int32_t *num_accepted_tokens, int32_t B, int32_t T,
+                          int32_t N_slots, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char *rgdr_status_string(rgdr_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGDR_H */

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every function include/rgdr.h
+declares, and rejects bad arguments on the host before launching anything.
+
+The argument checks return before any HIP call, so the fake (never dereferenced) device
+addresses used here are safe.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rgdr.h")
+
+OK, NULL, SHAPE, UNSUP, RANGE, DUP, DTYPE, HIP, ALIGN = range(9)
+F32, F16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_delta_rule_rgdr_amd as g
+    return g.library()
+
+
+def test_header_declares_the_operations():
+    names = declared_functions()
+    for want in ("rgdr_decode", "la_gate", "rgdr_validate", "rgdr_validate_host",
+                 "rgdr_status_string"):
+        assert want in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"librgdr.so does not export {name}"
+
+
+def test_status_strings(lib):
+    import gated_delta_rule_rgdr_amd as g
+    for code in range(9):
+        s = g.status_string(code)
+        assert s.startswith("RGDR_")
+    assert g.status_string(99) == "unknown rgdr_status"
+
+
+def _decode(lib, ptrs=None, **kw):
+    dims = dict(B=2, Hq=2, Hv=4, T=1, Dk=128, Dv=128, N=4)
+    dims.update(kw)
+    p = [0x10000] * 10 if ptrs is None else ptrs
+    out = kw.get("out", 0x20000)
+    so = kw.get("state_out", 0x30000)
+    return lib.rgdr_decode(*p[:10], 1.0, dims["B"], dims["Hq"], dims["Hv"], dims["T"],
+                           dims["Dk"], dims["Dv"], dims["N"], out, so, None)
+
+
+def test_decode_argument_checks(lib):
+    assert _decode(lib, ptrs=[None] + [0x10000] * 9) == NULL
+    assert _decode(lib, out=None) == NULL
+    assert _decode(lib, state_out=None) == NULL
+    assert _decode(lib, T=9) == SHAPE          # decode only: T <= 8
+    assert _decode(lib, T=0) == SHAPE
+    assert _decode(lib, B=-1) == SHAPE
+    assert _decode(lib, ptrs=[None] * 10, B=0, out=None, state_out=None) == OK  # empty batch
+    assert _decode(lib, Hq=3, Hv=4) == SHAPE   # H_v must be a multiple of H_q
+    assert _decode(lib, Hq=8, Hv=4) == SHAPE   # more query heads than value heads
+    assert _decode(lib, N=0) == SHAPE
+    assert _decode(lib, Dk=96) == UNSUP
+    assert _decode(lib, Dk=256) == UNSUP
+    assert _decode(lib, Dv=96) == UNSUP
+    bad = [0x10000] * 10
+    bad[2] = 0x10002  # value not 16-byte aligned
+    assert _decode(lib, ptrs=bad) == ALIGN
+    bad = [0x10000] * 10
+    bad[4] = 0x10008  # state pool not 16-byte aligned
+    assert _decode(lib, ptrs=bad) == ALIGN
+    bad = [0x10000] * 10
+    bad[7] = 0x10002  # g not 4-byte aligned
+    assert _decode(lib, ptrs=bad) == ALIGN
+    assert _decode(lib, out=0x20004) == ALIGN
+
+
+def test_gate_argument_checks(lib):
+    P = 0x10000
+    assert lib.la_gate(None, P, P, P, F32, 4, 2, P, F32, P, F32, None) == NULL
+    assert lib.la_gate(P, None, P, P, F32, 4, 2, P, F32, P, F32, None) == NULL
+    assert lib.la_gate(P, P, P, P, F32, 4, 2, None, F32, P, F32, None) == NULL
+    assert lib.la_gate(P, P, P, None, F32, 4, 2, P, F32, P, F32, None) == SHAPE  # beta needs b
+    assert lib.la_gate(P, P, P, P, F32, -1, 2, P, F32, None, F32, None) == SHAPE
+    assert lib.la_gate(P, P, P, P, F32, 4, 0, P, F32, None, F32, None) == SHAPE
+    assert lib.la_gate(P, P, P, P, BF16, 4, 2, P, F32, None, F32, None) == DTYPE
+    assert lib.la_gate(P, P, P, P, F32, 4, 2, P, BF16, None, F32, None) == DTYPE
+    assert lib.la_gate(P, P, P, P, F32, 4, 2, P, F32, P, 7, None) == DTYPE
+    assert lib.la_gate(P + 2, P, P, P, F32, 4, 2, P, F32, None, F32, None) == ALIGN
+    # zero rows: nothing to do, nothing read or launched
+    assert lib.la_gate(P, P, P, P, F32, 0, 2, P, F32, P, BF16, None) == OK
+    assert lib.la_gate(None, None, None, None, F32, 0, 2, None, F32, None, F32, None) == OK
+    # an unconsumed b is allowed when beta is not requested (checked before launch via n=0)
+    assert lib.la_gate(P, P, P, P, F16, 0, 3, P, F16, None, F32, None) == OK
+
+
+def test_validate_host():
+    import gated_delta_rule_rgdr_amd as g
+    T, N = 8, 6
+    assert g.rgdr_validate_host([3, 8, 0], [5, 0, 2], [3, 8, 0], T, N) == OK
+    assert g.rgdr_validate_host([3, 9, 0], [5, 0, 2], [3, 8, 0], T, N) == RANGE   # L > T
+    assert g.rgdr_validate_host([3, -1, 0], [5, 0, 2], [3, 0, 0], T, N) == RANGE  # L < 0
+    assert g.rgdr_validate_host([3, 8, 0], [5, 0, 2], [4, 8, 0], T, N) == RANGE   # n > L
+    assert g.rgdr_validate_host([3, 8, 0], [5, 6, 2], [3, 8, 0], T, N) == RANGE   # slot >= N
+    assert g.rgdr_validate_host([3, 8, 0], [5, -1, 2], [3, 8, 0], T, N) == RANGE  # slot < 0
+    assert g.rgdr_validate_host([3, 8, 0], [5, 0, 5], [3, 8, 0], T, N) == DUP
+    lib = g.library()
+    assert lib.rgdr_validate_host(None, None, None, 3, T, N) == NULL
+    z = np.zeros(3, np.int32)
+    assert lib.rgdr_validate_host(z.ctypes.data, z.ctypes.data, z.ctypes.data, 0, T, N) == SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import gated_delta_rule_rgdr_amd as g
+    q = torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="GPU"):
+        g.rgdr_decode(q, q, q, q[..., 0], q, *([torch.zeros(1, dtype=torch.int32)] * 2),
+                      q.float()[..., 0], q.float(), torch.zeros(1, dtype=torch.int32))

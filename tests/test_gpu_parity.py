@@ -1,0 +1,338 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded
+bytes, at the five workloads' full sizes and on edge cases.
+
+Values: bf16 out/state_out within 2e-2 + 2e-2 |ref| of the unrounded oracle value.
+Indexing (pool gather/scatter, untouched slots, varlen masking, padded +0.0 rows,
+skipped entries) bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (assert_tol, bf16_dev_to_f64, bits_to_dev, check_decode, dev_to_bits,
+                      gpu_decode, oracle_decode, say, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_delta_rule_rgdr_amd as m
+    m.library()
+    return m
+
+
+# ---------------------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2, 3])
+def test_workload_parity(rg, wid):
+    say(f"workload {wid}: {workloads.WORKLOAD_NAMES[wid]}")
+    inp = workloads.make_workload(wid)
+    out, st = gpu_decode(inp)
+    ref = oracle_decode(inp)
+    check_decode(inp, out, st, ref, f"workload {wid}")
+
+
+def test_workload3_nan_padding_bitexact(rg):
+    """Padded tokens filled with NaN change no valid output or state, bit for bit."""
+    inp = workloads.make_workload(3)
+    out0, st0 = gpu_decode(inp)
+    nan_bf16 = np.uint16(0x7FC0)
+    for b in range(inp.B):
+        L = inp.actual_seq_lengths[b]
+        inp.query[b, :, L:] = nan_bf16
+        inp.key[b, :, L:] = nan_bf16
+        inp.value[b, :, L:] = nan_bf16
+        inp.beta[b, :, L:] = nan_bf16
+        inp.g[b, :, L:] = np.nan
+        inp.gk[b, :, L:] = np.nan
+    out1, st1 = gpu_decode(inp)
+    assert np.array_equal(dev_to_bits(out0), dev_to_bits(out1))
+    assert np.array_equal(dev_to_bits(st0), dev_to_bits(st1))
+    ref = oracle_decode(inp)
+    check_decode(inp, out1, st1, ref, "workload 3 NaN padding")
+
+
+def test_workload4_gate_then_decode(rg):
+    """la_gate feeds rgdr_decode (g fp32, beta bf16); the oracle chain uses its own gate."""
+    inp = workloads.make_workload(4)
+    B, Hv = inp.B, inp.Hv
+    say(f"workload 4: {workloads.WORKLOAD_NAMES[4]}")
+    d = upload(inp)
+    a = torch.from_numpy(inp.gate_a).cuda()
+    b = torch.from_numpy(inp.gate_b).cuda()
+    dt = torch.from_numpy(inp.dt_bias).cuda()
+    ds = torch.from_numpy(inp.decay_scale).cuda()
+    g_dev, beta_dev = rg.la_gate(a, dt, ds, b, decay_dtype=torch.float32,
+                                 beta_dtype=torch.bfloat16)
+    pool = d["state"].clone()
+    # T = 1: the gate's [B, 1, H] buffers are the [B, H, 1] layout the decode reads
+    out, st = rg.rgdr_decode(d["query"], d["key"], d["value"], beta_dev.view(B, Hv, 1), pool,
+                             d["actual_seq_lengths"], d["ssm_state_indices"],
+                             g_dev.view(B, Hv, 1), d["gk"], d["num_accepted_tokens"], inp.scale)
+    torch.cuda.synchronize()
+    dec64, beta64 = oracle.la_gate(inp.gate_a, inp.dt_bias, inp.decay_scale, inp.gate_b)
+    assert_tol(g_dev.cpu().numpy().astype(np.float64), dec64, "workload 4 decay", 1e-6, 1e-5)
+    beta_gpu = bf16_dev_to_f64(beta_dev)
+    ulp = np.exp2(np.floor(np.log2(np.abs(beta64))) - 7)
+    assert np.all(np.abs(beta_gpu - beta64) <= ulp), "beta not within 1 bf16 ulp"
+    g32 = dec64.astype(np.float32).reshape(B, Hv, 1)
+    beta_bits = oracle.f64_to_bf16(beta64).reshape(B, Hv, 1)
+    ref = oracle_decode(inp, g=g32, beta=beta_bits)
+    inp.g, inp.beta = g32, beta_bits
+    check_decode(inp, out, st, ref, "workload 4")
+
+
+def test_page_example_shapes(rg):
+    """The page's example decode shape (workload 1) returns out [1,64,1,512] and a state
+    [1,64,64,512] through the functional form; the input state is left unchanged."""
+    inp = workloads.make_workload(1)
+    d = upload(inp)
+    before = dev_to_bits(d["state"])
+    out, st = rg.recurrent_gated_delta_rule(
+        d["query"], d["key"], d["value"], d["beta"], d["state"], d["actual_seq_lengths"],
+        d["ssm_state_indices"], d["g"], d["gk"], d["num_accepted_tokens"], scale_value=inp.scale)
+    torch.cuda.synchronize()
+    assert list(out.shape) == [1, 64, 1, 512]
+    assert list(st.shape) == [1, 64, 64, 512]
+    assert np.array_equal(dev_to_bits(d["state"]), before)
+    check_decode(inp, out, st, oracle_decode(inp), "functional form")
+
+
+# ---------------------------------------------------------------------------------------
+# Shapes: several tiles, ragged tile counts, both D_k, T up to 8
+# ---------------------------------------------------------------------------------------
+
+SHAPES = [
+    # B, Hq, Hv, T, Dk, Dv, N_slots
+    (3, 2, 4, 1, 64, 64, 5),
+    (2, 1, 3, 3, 64, 192, 4),     # 64-wide tiles, 3 per row
+    (4, 2, 2, 8, 128, 320, 6),    # 64-wide tiles, 5 per row
+    (2, 4, 8, 5, 128, 384, 3),    # 128-wide tiles, 3 per row
+    (5, 5, 5, 2, 128, 64, 9),
+    (1, 1, 8, 8, 64, 512, 2),     # MQA
+    (7, 2, 6, 4, 128, 128, 11),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_Hq%d_Hv%d_T%d_Dk%d_Dv%d" % s[:6])
+def test_shapes(rg, shape):
+    B, Hq, Hv, T, Dk, Dv, N = shape
+    inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=hash(shape) % 2**31,
+                              indices="choice", lengths="uniform")
+    out, st = gpu_decode(inp)
+    check_decode(inp, out, st, oracle_decode(inp), "shape %s" % (shape,))
+
+
+# ---------------------------------------------------------------------------------------
+# Indexing semantics, bit for bit
+# ---------------------------------------------------------------------------------------
+
+
+def small_case(seed=5, B=6, T=4, lengths="uniform", **kw):
+    return workloads.make_case(B, 2, 4, T, 128, 128, 10, seed=seed, indices="choice",
+                               lengths=lengths, **kw)
+
+
+def test_permutation_equivariance(rg):
+    inp = small_case()
+    out, st = gpu_decode(inp)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    p = small_case()
+    for name in ("query", "key", "value", "beta", "g", "gk", "ssm_state_indices",
+                 "actual_seq_lengths", "num_accepted_tokens"):
+        setattr(p, name, np.ascontiguousarray(getattr(inp, name)[perm]))
+    out_p, st_p = gpu_decode(p)
+    assert np.array_equal(dev_to_bits(out_p), dev_to_bits(out)[perm])
+    assert np.array_equal(dev_to_bits(st_p), dev_to_bits(st))
+
+
+def test_out_of_range_slot_skips_row(rg):
+    inp = small_case()
+    out, st = gpu_decode(inp)
+    bad = small_case()
+    bad.ssm_state_indices = inp.ssm_state_indices.copy()
+    bad.ssm_state_indices[1] = -1
+    bad.ssm_state_indices[4] = inp.N_slots + 5
+    out_b, st_b = gpu_decode(bad)
+    ob = dev_to_bits(out_b)
+    assert np.all(ob[[1, 4]] == 0)
+    keep = [0, 2, 3, 5]
+    assert np.array_equal(ob[keep], dev_to_bits(out)[keep])
+    sb = dev_to_bits(st_b)
+    for b in (1, 4):
+        s = inp.ssm_state_indices[b]
+        assert np.array_equal(sb[s], inp.state[s])  # the row's own slot was not written
+    for b in keep:
+        s = inp.ssm_state_indices[b]
+        assert np.array_equal(sb[s], dev_to_bits(st)[s])
+    check_decode(bad, out_b, st_b, oracle_decode(bad), "out-of-range slots")
+
+
+def test_gqa_expansion_bitexact(rg):
+    """Value head h reads query/key head floor(h H_q / H_v): expanding the shared heads
+    and calling with H_q = H_v gives identical bytes."""
+    inp = workloads.make_case(3, 4, 16, 2, 128, 128, 4, seed=9, indices="choice")
+    out, st = gpu_decode(inp)
+    e = workloads.make_case(3, 4, 16, 2, 128, 128, 4, seed=9, indices="choice")
+    e.query = np.ascontiguousarray(np.repeat(inp.query, 4, axis=1))
+    e.key = np.ascontiguousarray(np.repeat(inp.key, 4, axis=1))
+    e.Hq = 16
+    out_e, st_e = gpu_decode(e)
+    assert np.array_equal(dev_to_bits(out), dev_to_bits(out_e))
+    assert np.array_equal(dev_to_bits(st), dev_to_bits(st_e))
+
+
+def test_length_and_count_clamping(rg):
+    inp = small_case(B=4, lengths=[-3, 11, 2, 4])
+    inp.num_accepted_tokens = np.array([2, 9, -1, 4], np.int32)
+    out, st = gpu_decode(inp)
+    ref = small_case(B=4, lengths=[0, 4, 2, 4])
+    ref.num_accepted_tokens = np.array([0, 4, 0, 4], np.int32)
+    out_r, st_r = gpu_decode(ref)
+    assert np.array_equal(dev_to_bits(out), dev_to_bits(out_r))
+    assert np.array_equal(dev_to_bits(st), dev_to_bits(st_r))
+
+
+def test_accepted_prefix_commit(rg):
+    """n < L: outputs equal the n = L call; the committed state equals a call that stops
+    after n tokens; both against the oracle too."""
+    full = small_case(B=5, T=8, lengths=[8, 6, 5, 8, 3])
+    out_f, _ = gpu_decode(full)
+    acc = small_case(B=5, T=8, lengths=[8, 6, 5, 8, 3])
+    acc.num_accepted_tokens = np.array([3, 6, 0, 1, 2], np.int32)
+    out_a, st_a = gpu_decode(acc)
+    assert np.array_equal(dev_to_bits(out_a), dev_to_bits(out_f))
+    short = small_case(B=5, T=8, lengths=[8, 6, 5, 8, 3])
+    short.actual_seq_lengths = acc.num_accepted_tokens.copy()
+    short.num_accepted_tokens = acc.num_accepted_tokens.copy()
+    _, st_s = gpu_decode(short)
+    assert np.array_equal(dev_to_bits(st_a), dev_to_bits(st_s))
+    check_decode(acc, out_a, st_a, oracle_decode(acc), "accepted prefix")
+
+
+def test_zero_lengths_write_state_back(rg):
+    inp = small_case(B=3, lengths=[0, 0, 0])
+    out, st = gpu_decode(inp)
+    assert np.all(dev_to_bits(out) == 0)
+    assert np.array_equal(dev_to_bits(st), inp.state)
+
+
+def test_inplace_equals_out_of_place(rg):
+    inp = small_case()
+    out1, st1 = gpu_decode(inp)
+    out2, st2 = gpu_decode(inp, inplace=True)
+    assert np.array_equal(dev_to_bits(out1), dev_to_bits(out2))
+    assert np.array_equal(dev_to_bits(st1), dev_to_bits(st2))
+
+
+def test_deterministic(rg):
+    inp = workloads.make_workload(3)
+    a = gpu_decode(inp)
+    b = gpu_decode(inp)
+    assert np.array_equal(dev_to_bits(a[0]), dev_to_bits(b[0]))
+    assert np.array_equal(dev_to_bits(a[1]), dev_to_bits(b[1]))
+
+
+def test_chaining_two_calls_of_four(rg):
+    """Two T=4 calls (state fed back) match one T=8 oracle call within tolerance."""
+    inp = workloads.make_case(4, 2, 4, 8, 128, 128, 6, seed=33, indices="choice",
+                              lengths=[8, 8, 8, 8])
+    ref = oracle_decode(inp)
+    d = upload(inp)
+    pool = d["state"].clone()
+    outs = []
+    for lo in (0, 4):
+        sl = slice(lo, lo + 4)
+        o, _ = rg.rgdr_decode(d["query"][:, :, sl].contiguous(), d["key"][:, :, sl].contiguous(),
+                              d["value"][:, :, sl].contiguous(), d["beta"][:, :, sl].contiguous(),
+                              pool, torch.full((4,), 4, dtype=torch.int32, device="cuda"),
+                              d["ssm_state_indices"], d["g"][:, :, sl].contiguous(),
+                              d["gk"][:, :, sl].contiguous(),
+                              torch.full((4,), 4, dtype=torch.int32, device="cuda"), inp.scale)
+        outs.append(o)
+    torch.cuda.synchronize()
+    out = torch.cat(outs, dim=2)
+    check_decode(inp, out, pool, ref, "two calls of four")
+
+
+def test_empty_batch_is_noop(rg):
+    z = torch.empty((0, 2, 1, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((0, 4, 1, 128), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((3, 4, 128, 128), dtype=torch.bfloat16, device="cuda")
+    i = torch.empty((0,), dtype=torch.int32, device="cuda")
+    out, st = rg.rgdr_decode(z, z, v, v[..., 0], pool, i, i,
+                             torch.empty((0, 4, 1), device="cuda"),
+                             torch.empty((0, 4, 1, 128), device="cuda"), i, 1.0)
+    assert out.shape == (0, 4, 1, 128)
+
+
+def test_bad_arguments_raise(rg):
+    inp = small_case(T=4)
+    d = upload(inp)
+    q9 = torch.zeros((inp.B, 2, 9, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError):
+        rg.rgdr_decode(q9, q9, torch.zeros((inp.B, 4, 9, 128), dtype=torch.bfloat16, device="cuda"),
+                       torch.zeros((inp.B, 4, 9), dtype=torch.bfloat16, device="cuda"), d["state"],
+                       d["actual_seq_lengths"], d["ssm_state_indices"],
+                       torch.zeros((inp.B, 4, 9), device="cuda"),
+                       torch.zeros((inp.B, 4, 9, 128), device="cuda"), d["num_accepted_tokens"])
+
+
+def test_validate_on_device(rg):
+    lens = torch.tensor([3, 8, 0], dtype=torch.int32, device="cuda")
+    idx = torch.tensor([5, 0, 2], dtype=torch.int32, device="cuda")
+    assert rg.rgdr_validate(lens, idx, lens, 8, 6) == 0
+    idx_dup = torch.tensor([5, 0, 5], dtype=torch.int32, device="cuda")
+    assert rg.rgdr_validate(lens, idx_dup, lens, 8, 6) == 5
+    idx_bad = torch.tensor([5, 0, 6], dtype=torch.int32, device="cuda")
+    assert rg.rgdr_validate(lens, idx_bad, lens, 8, 6) == 4
+
+
+def test_graph_replay_matches_eager(rg):
+    """The gate and the decode captured in a HIP graph give the eager bytes on every replay
+    (out-of-place, so each replay starts from the same state)."""
+    inp = workloads.make_workload(2, gate_inputs=True)
+    B, Hv = inp.B, inp.Hv
+    d = upload(inp)
+    a = torch.from_numpy(inp.gate_a).cuda()
+    b = torch.from_numpy(inp.gate_b).cuda()
+    dt = torch.from_numpy(inp.dt_bias).cuda()
+    ds = torch.from_numpy(inp.decay_scale).cuda()
+    g_buf = torch.empty((B, 1, Hv), device="cuda")
+    beta_buf = torch.empty((B, 1, Hv), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, Hv, 1, inp.Dv), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty_like(d["state"])
+
+    def step():
+        rg.la_gate(a, dt, ds, b, decay_dtype=torch.float32, beta_dtype=torch.bfloat16,
+                   decay_out=g_buf, beta_out=beta_buf)
+        rg.rgdr_decode(d["query"], d["key"], d["value"], beta_buf.view(B, Hv, 1), d["state"],
+                       d["actual_seq_lengths"], d["ssm_state_indices"], g_buf.view(B, Hv, 1),
+                       d["gk"], d["num_accepted_tokens"], inp.scale, out=out, state_out=st)
+
+    st.copy_(d["state"])
+    step()
+    torch.cuda.synchronize()
+    want_out, want_st = dev_to_bits(out), dev_to_bits(st)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.zero_()
+        st.copy_(d["state"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_to_bits(out), want_out), f"replay {rep}: out differs"
+        assert np.array_equal(dev_to_bits(st), want_st), f"replay {rep}: state differs"

@@ -22,6 +22,12 @@ Recipe (one numpy ``default_rng(1000 + id)`` stream, drawn in this order):
   a, b ~ N(0,1) fp32 [B,T,H_v]; dt_bias ~ N(0,1) fp32 [H_v]; A_log ~ U(0, ln 16) fp32
   [H_v]; decay_scale = -exp(A_log) in fp32 (the gated-DeltaNet choice the README names).
 
+With ``gate_inputs=True`` a workload without its own gate inputs (0-3) also gets raw gate
+projections, drawn after everything else: a, b ~ N(0,1) fp32 [B,T,H_v], dt_bias = 0 and
+decay_scale = -1. The gate then yields g = -softplus(a) and beta = sigmoid(b), the same
+distributions the recipe draws g and beta from, so the whole path (gate, then decode)
+runs at that workload's shape.
+
 bf16 values are stored as uint16 bit patterns. The conversion to bf16 uses torch's CPU
 cast (round to nearest even); it only shapes the inputs.
 """
@@ -142,18 +148,26 @@ def make_case(B, Hq, Hv, T, Dk, Dv, N_slots, seed, *, zero_state=False, gk_hi=0.
     return inp
 
 
-def make_workload(wid: int) -> Inputs:
-    """The five workloads, seeded with 1000 + id."""
+def make_workload(wid: int, gate_inputs: bool = False) -> Inputs:
+    """The five workloads, seeded with 1000 + id (see the module docstring)."""
     w = WORKLOADS[wid]
     seed = 1000 + wid
     if wid == 0:
-        return make_case(**w, seed=seed, zero_state=True, indices="identity")
-    if wid == 1:
-        return make_case(**w, seed=seed, indices="identity")
-    if wid == 2:
-        return make_case(**w, seed=seed, indices="choice")
-    if wid == 3:
-        return make_case(**w, seed=seed, indices="permutation", lengths="uniform")
-    if wid == 4:
+        inp = make_case(**w, seed=seed, zero_state=True, indices="identity")
+    elif wid == 1:
+        inp = make_case(**w, seed=seed, indices="identity")
+    elif wid == 2:
+        inp = make_case(**w, seed=seed, indices="choice")
+    elif wid == 3:
+        inp = make_case(**w, seed=seed, indices="permutation", lengths="uniform")
+    elif wid == 4:
         return make_case(**w, seed=seed, indices="choice", gk_hi=0.05, gate=True)
-    raise KeyError(wid)
+    else:
+        raise KeyError(wid)
+    if gate_inputs:
+        rng = np.random.default_rng(seed + 100000)
+        inp.gate_a = rng.standard_normal((inp.B, inp.T, inp.Hv)).astype(np.float32)
+        inp.gate_b = rng.standard_normal((inp.B, inp.T, inp.Hv)).astype(np.float32)
+        inp.dt_bias = np.zeros(inp.Hv, np.float32)
+        inp.decay_scale = np.full(inp.Hv, -1.0, np.float32)
+    return inp
