@@ -17,9 +17,10 @@ Measurement:
   * W eager warmup steps; then the K timed steps are captured in one HIP graph (so
     Python launch overhead is not measured), uploaded with one untimed replay, and timed
     with events on the launch stream around a single replay.
-  * The decode kernel's average duration comes from event pairs around each of K eager
-    launches on the same stream (second pass); its roofline uses the method's
-    algorithmic bytes per launch.
+  * The decode kernel's average duration: K back-to-back decode launches over the same
+    rotation, captured in a graph and timed with events around one replay (the duration
+    rocprofv3's kernel trace reports); its roofline uses the method's algorithmic bytes
+    per launch. The gate kernel is timed the same way.
   * cpu_baseline: the fp64 C oracle (single-threaded) repeats the same step on the host
     for about --cpu-seconds.
 
@@ -61,6 +62,30 @@ def gate_bytes(inp):
     return n * (4 + 4 + 4 + 2) + 2 * 4 * inp.Hv  # a, b in; decay fp32, beta bf16 out; 2 [H]
 
 
+KERNEL_SOURCES = ("gated_delta_rule_rgdr_amd/csrc/rgdr_decode.hip",
+                  "gated_delta_rule_rgdr_amd/csrc/rgdr_common.h")
+TRAFFIC_PROFILE = "profiles/rgdr_decode_b64_gqa_d128.md"
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
+    when the decode kernel's sources have changed since those counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    mt = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    mh = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not (mt and mh):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return int(mt.group(1)) if h.hexdigest() == mh.group(1) else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,6 +95,11 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB copy (read 256 MiB, write 256 MiB) five "
+                         "times, as the reference for the HBM byte counters")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="profiling pass: W + K eager steps, no graphs, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the decode path has "
@@ -140,11 +170,28 @@ def main():
         gate(s)
         decode(s)
 
+    def copy_calibration():
+        # A plain elementwise copy of known size: 64 Mi fp32 elements read and written once.
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 x (read 256 MiB + write 256 MiB)")
+
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"warmup: {args.warmup} eager steps done")
+    if args.eager_only:
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        log(f"eager pass: {args.steps} steps done")
+        if args.copy_calibration:
+            copy_calibration()
+        return
 
     # K timed steps in one graph.
     K = args.steps
@@ -169,30 +216,40 @@ def main():
     ms_per_step = total_ms / K
     log(f"timed: {K} steps in {total_ms:.3f} ms ({ms_per_step * 1e3:.2f} us/step)")
 
-    # Second pass: per-launch event pairs around the decode kernel on the launch stream.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for i in range(K):
-        s = sets[i % R]
-        gev[i][0].record(stream)
-        gate(s)
-        gev[i][1].record(stream)
-        ev[i][0].record(stream)
-        decode(s)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    gate_us = np.array([a.elapsed_time(b) * 1e3 for a, b in gev])
-    log(f"decode kernel: mean {dec_us.mean():.2f} us, median {np.median(dec_us):.2f} us, "
-        f"min {dec_us.min():.2f} us; gate kernel mean {gate_us.mean():.2f} us")
+    # Kernel durations: K back-to-back launches of one kernel, captured in a graph, timed
+    # with events on the launch stream around one replay (no per-launch event overhead;
+    # this is the duration rocprofv3's kernel trace reports).
+    def kernel_avg_us(fn):
+        g = torch.cuda.CUDAGraph()
+        c = torch.cuda.Stream()
+        c.wait_stream(stream)
+        with torch.cuda.stream(c):
+            with torch.cuda.graph(g, stream=c):
+                for i in range(K):
+                    fn(sets[i % R])
+        stream.wait_stream(c)
+        g.replay()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        g.replay()
+        a1.record(stream)
+        a1.synchronize()
+        return a0.elapsed_time(a1) * 1e3 / K
 
-    kernel_gbs = dbytes / (dec_us.mean() * 1e-6) / 1e9
+    dec_us = kernel_avg_us(decode)
+    gate_us = kernel_avg_us(gate)
+    log(f"decode kernel: {dec_us:.2f} us per launch; gate kernel {gate_us:.2f} us per launch")
+
+    if args.copy_calibration:
+        copy_calibration()
+
+    kernel_gbs = dbytes / (dec_us * 1e-6) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     steps_per_s = tok_heads / (ms_per_step * 1e-3)
 
-    traffic = None
+    traffic = measured_traffic() if wid == 2 else None
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -240,8 +297,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dbytes,
-                     "avg_launch_us": round(float(dec_us.mean()), 3)},
-        "gate_avg_launch_us": round(float(gate_us.mean()), 3),
+                     "avg_launch_us": round(dec_us, 3)},
+        "gate_avg_launch_us": round(gate_us, 3),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

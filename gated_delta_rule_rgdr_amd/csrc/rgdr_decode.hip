@@ -4,21 +4,31 @@
 // section (decay, memory read, delta update, output, token by token) and parameter list.
 //
 // The step is HBM-bound: each (batch entry, value head) pair streams its D_k x D_v bf16
-// state in once and out once, and everything else is small. One workgroup owns one
-// (b, h, D_v tile) and keeps that tile in fp32 registers across all tokens:
+// state in once and out once; everything else is small. The kernel is built around that
+// stream:
 //
-//   * a thread owns 8 consecutive columns (one 16-byte bf16 vector) of R rows spaced
-//     RPP apart, so every load/store instruction of the workgroup covers RPP whole tile
-//     rows, contiguous in memory; all state loads are issued before anything else;
-//   * per-token operands (decay factors exp(g) exp(gk), k, q * scale, the v tile, beta)
-//     are staged once in LDS for all tokens;
-//   * per token, steps 2 and 4 share ONE reduction over D_k: with S' the decayed state,
-//     p = S'^T k and r = S'^T (scale q) are reduced together with the scalar k.(scale q),
-//     then u = beta (v - p), o = r + (k.(scale q)) u, which equals S_new^T (scale q), and
-//     S_new = S' + k (x) u is one FMA per element;
-//   * the reduction is in-thread over R rows, then a butterfly across the lanes of the
-//     wave that hold the same columns, then a fixed-order sum over the waves through a
-//     double-buffered LDS slot (one barrier per token). Results are deterministic.
+//   * Work item = one (b, h, D_v tile) state tile. Workgroups are persistent: workgroup w
+//     takes items w, w + G, w + 2G, ... (G = grid size, what fits on the CUs at once), so
+//     the items in flight at one moment are neighbours in the pool.
+//   * State tiles travel through a ring of NBUF register buffers filled by 16-byte
+//     nontemporal buffer loads. As soon as item s has been widened to fp32, its ring slot
+//     receives item s + NBUF, so NBUF tiles are in flight while item s is computed and
+//     stored. The item loop is unrolled over the ring, so every slot is a fixed register
+//     set and no register copy waits on a load in flight. Loads past the last item, or of
+//     a skipped entry, use an empty buffer range and move no data.
+//   * The small per-item operands (gk, g, k, q, the v tile, beta) of item s+1 are loaded
+//     into registers during item s and staged in LDS when item s+1 starts; the decay
+//     factors exp(g) exp(gk) are formed there, once per element.
+//   * A thread owns 8 consecutive columns (one 16-byte bf16 vector) of R rows spaced RPP
+//     apart; each load/store instruction of the workgroup covers RPP whole tile rows.
+//   * Per token, steps 2 and 4 share ONE reduction over D_k: with S' the decayed state,
+//     p = S'^T k and r = S'^T (scale q) are reduced together with the scalar k.(scale q);
+//     then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q),
+//     and S_new = S' + k (x) u is one FMA per element.
+//   * The reduction: in-thread over R rows, then across the lanes of the wave holding the
+//     same columns with v_permlane16/32_swap (and a DPP row rotate for 64-wide tiles), then
+//     a fixed-order sum over the waves through a double-buffered LDS slot: one barrier per
+//     token, deterministic results.
 //
 // No matrix cores: the work per token is a matrix-vector product and a rank-1 update.
 #include "rgdr_common.h"
@@ -27,16 +37,42 @@ namespace rgdr {
 
 constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 
+// Launch shape (compile-time tuning knobs): threads per workgroup, the D_v tile width
+// (0 = 128 columns when D_v allows it, else 64), and the number of state tiles in flight
+// per workgroup (1 to 3).
+#ifndef RGDR_DECODE_THREADS
+#define RGDR_DECODE_THREADS 256
+#endif
+#ifndef RGDR_DECODE_TILE_V
+#define RGDR_DECODE_TILE_V 0
+#endif
+#ifndef RGDR_DECODE_DEPTH
+#define RGDR_DECODE_DEPTH 1
+#endif
+// Minimum waves per SIMD the register allocation must allow (occupancy floor).
+#ifndef RGDR_DECODE_MIN_WAVES
+#define RGDR_DECODE_MIN_WAVES 2
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBufWord3 = 0x00020000;  // raw (unformatted) buffer descriptor, gfx9 family
+constexpr int kCacheNT = 2;            // cache policy bits: nontemporal (streaming)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3);
+}
+
 struct DecodeArgs {
     const uint16_t *q, *k, *v, *beta, *pool;
-    const int32_t *lens, *idx, *nacc;
     const float *g, *gk;
     uint16_t *out, *pool_out;
     float scale;
-    int Hq, Hv, T, Dv, N_slots, ntiles, group;
+    int Hq, Hv, T, Dv, N_slots, ntiles, group, n_items;
 };
 
-template <int DK, int TV, int NT>
+template <int DK, int TV, int NT, int TMAX = kMaxT>
 struct TileShape {
     static constexpr int CPL = 8;         // columns per lane: one 16-byte bf16 vector
     static constexpr int LPR = TV / CPL;  // lanes across one tile row
@@ -44,187 +80,577 @@ struct TileShape {
     static constexpr int R = DK / RPP;    // rows held by each thread
     static constexpr int NW = NT / 64;    // waves per workgroup
     static_assert(NT % 64 == 0 && 64 % LPR == 0 && DK % RPP == 0 && R >= 1, "tile shape");
-    // LDS, in floats. Per token: decay[DK] | k[DK] | scale*q[DK] | v[TV] | beta.
-    static constexpr int TOK = 3 * DK + TV + 1;
-    // Reduction exchange, two buffers of: per wave p[TV] | r[TV] | k.q.
-    static constexpr int EXW = 2 * TV + 1;
-    static constexpr int EX = NW * EXW;
-    static size_t lds_bytes(int T) { return sizeof(float) * (size_t)(T * TOK + 2 * EX); }
+    static_assert(LPR == 8 || LPR == 16, "lane reduction handles 64- and 128-wide tiles");
+    // Per-thread operand vectors of one item (up to TMAX tokens).
+    static constexpr int GKV = (TMAX * DK / 4 + NT - 1) / NT;  // float4 of gk
+    static constexpr int KQV = (TMAX * DK / 8 + NT - 1) / NT;  // 8 x bf16 of k (and of q)
+    static constexpr int VV = (TMAX * TV / 8 + NT - 1) / NT;   // 8 x bf16 of the v tile
+    static_assert(NT >= TMAX, "one thread per token for beta");
+    // LDS, in floats. Per token: rows[DK] of (decay, k, scale*q, 0) | v[TV] | beta, pad.
+    static constexpr int TOK = 4 * DK + TV + 4;
+    static constexpr int OPS = TMAX * TOK;   // one operand buffer; two are used
+    static constexpr int EXW = 2 * TV + 4;   // reduction exchange per wave: p[TV] r[TV] kq
+    static constexpr int EX = NW * EXW;      // one exchange buffer; two are used
+    static constexpr int LDS_FLOATS = 2 * OPS + 2 * EX;
 };
 
-template <int DK, int TV, int NT>
-__global__ __launch_bounds__(NT) void decode_kernel(const DecodeArgs a) {
-    using Sh = TileShape<DK, TV, NT>;
-    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, R = Sh::R, NW = Sh::NW;
-    extern __shared__ float lds[];
+// The per-entry index arrays. They are only read, never written by the kernel; passing them
+// as separate restrict-qualified kernel arguments lets the compiler read them with scalar
+// loads, which do not count against the vector memory counter the state stream uses.
+struct Index {
+    const int32_t *__restrict__ lens;
+    const int32_t *__restrict__ idx;
+    const int32_t *__restrict__ nacc;
+};
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int cg = tid % LPR;  // column group: columns cg*8 .. cg*8+7 of the tile
-    const int rg = tid / LPR;  // row group: rows rg, rg+RPP, ...
+// Everything about one work item that is uniform across the workgroup.
+struct Item {
+    int b, h, hq, tile, slot, L, n;
+    bool state;  // a live item whose slot is in range: its state is read and committed
+};
 
-    const int tile = blockIdx.x % a.ntiles;
-    const int bh = blockIdx.x / a.ntiles;  // b * H_v + h
-    const int h = bh % a.Hv;
-    const int b = bh / a.Hv;
-    const int hq = h / a.group;  // shared query/key head, floor(h * H_q / H_v)
-    const int T = a.T;
+__device__ __forceinline__ Item resolve(const DecodeArgs &a, const Index &x, int it) {
+    Item m;
+    const bool live = it < a.n_items;
+    const int itc = live ? it : 0;
+    m.tile = itc % a.ntiles;
+    const int bh = itc / a.ntiles;
+    m.h = bh % a.Hv;
+    m.b = bh / a.Hv;
+    m.hq = m.h / a.group;  // shared query/key head, floor(h * H_q / H_v)
+    m.slot = x.idx[m.b];
+    const bool valid = m.slot >= 0 && m.slot < a.N_slots;
+    const int L = min(max(x.lens[m.b], 0), a.T);
+    m.n = min(max(x.nacc[m.b], 0), L);
+    m.state = live && valid;
+    m.L = m.state ? L : 0;  // skipped entry (or no item): no tokens, zero output
+    return m;
+}
 
-    // Index resolve: the slot, the valid length L and the committed prefix n.
-    const int slot = a.idx[b];
-    const bool valid = slot >= 0 && slot < a.N_slots;
-    int L = min(max(a.lens[b], 0), T);
-    const int n = min(max(a.nacc[b], 0), L);
-    if (!valid) L = 0;  // skipped entry: zero output, no state access
+template <int DK, int TV, int NT, int TMAX>
+struct Ops {
+    using Sh = TileShape<DK, TV, NT, TMAX>;
+    f32x4 gk[Sh::GKV];
+    float g[Sh::GKV];
+    u32x4 k[Sh::KQV], q[Sh::KQV], v[Sh::VV];
+    uint32_t beta;
+};
 
-    const int col0 = tile * TV + cg * CPL;
-    const size_t bhT = (size_t)bh * T;
-    uint16_t *out_row = a.out + bhT * a.Dv + col0;
-    const size_t srow0 = ((size_t)slot * a.Hv + h) * DK;  // first state row of the pair
-
-    // State gather: every 16-byte load of the tile is in flight before other work.
-    uint4 raw[R];
-    if (valid) {
-        const uint16_t *src = a.pool + srow0 * a.Dv + col0;
+// Issue the loads of one item's operands. Ranges cover only the L valid tokens, so padded
+// tokens are never read (lanes past the range receive zeros and move no data).
+template <int DK, int TV, int NT, int TMAX>
+__device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
+                                         Ops<DK, TV, NT, TMAX> &o, int tid) {
+    using Sh = TileShape<DK, TV, NT, TMAX>;
+    const size_t bhT = ((size_t)m.b * a.Hv + m.h) * a.T;
+    const uint32_t L = (uint32_t)m.L;
+    const auto rgk = make_rsrc(a.gk + bhT * DK, L * DK * 4);
+    const auto rg = make_rsrc(a.g + bhT, L * 4);
+    const size_t qk0 = ((size_t)m.b * a.Hq + m.hq) * a.T * DK;
+    const auto rk = make_rsrc(a.k + qk0, L * DK * 2);
+    const auto rq = make_rsrc(a.q + qk0, L * DK * 2);
+    const auto rv = make_rsrc(a.v + bhT * a.Dv, L * (uint32_t)a.Dv * 2);
+    const auto rb = make_rsrc(a.beta + bhT, L * 2);
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            raw[r] = *reinterpret_cast<const uint4 *>(src + (size_t)(rg + r * RPP) * a.Dv);
+    for (int j = 0; j < Sh::GKV; ++j) {
+        const int e = tid + j * NT;  // float4 index in the [L, DK] block
+        o.gk[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rgk, e * 16, 0, 0));
+        o.g[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (e * 4 / DK) * 4, 0, 0));
     }
-
-    // Operand staging for the L valid tokens.
-    const size_t qk0 = ((size_t)b * a.Hq + hq) * T;
-    for (int e = tid; e < L * DK; e += NT) {
-        const int t = e / DK, i = e - t * DK;
-        float *tok = lds + t * Sh::TOK;
-        tok[i] = __expf(a.g[bhT + t]) * __expf(a.gk[(bhT + t) * DK + i]);
-        tok[DK + i] = bf16_to_f32(a.k[(qk0 + t) * DK + i]);
-        tok[2 * DK + i] = bf16_to_f32(a.q[(qk0 + t) * DK + i]) * a.scale;
-    }
-    for (int e = tid; e < L * TV; e += NT) {
-        const int t = e / TV, c = e - t * TV;
-        lds[t * Sh::TOK + 3 * DK + c] = bf16_to_f32(a.v[(bhT + t) * a.Dv + tile * TV + c]);
-    }
-    if (tid < L) lds[tid * Sh::TOK + 3 * DK + TV] = bf16_to_f32(a.beta[bhT + tid]);
-    __syncthreads();
-
-    float S[R][CPL];
-    if (valid) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+    for (int j = 0; j < Sh::KQV; ++j) {
+        const int e = tid + j * NT;  // 8-element index in the [L, DK] block
+        o.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, e * 16, 0, 0);
+        o.q[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, e * 16, 0, 0);
+    }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                S[r][2 * j] = bf16_lo(w[j]);
-                S[r][2 * j + 1] = bf16_hi(w[j]);
+    for (int j = 0; j < Sh::VV; ++j) {
+        const int e = tid + j * NT;
+        const int t = e / (TV / 8), c8 = e % (TV / 8);
+        o.v[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rv, (uint32_t)((t * a.Dv + m.tile * TV + c8 * 8) * 2), 0, 0);
+    }
+    o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, tid * 2, 0, 0);
+}
+
+// Write one item's operands into an LDS operand buffer (decay factors formed here).
+template <int DK, int TV, int NT, int TMAX>
+__device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float *ob,
+                                          float scale, int tid) {
+    using Sh = TileShape<DK, TV, NT, TMAX>;
+#pragma unroll
+    for (int j = 0; j < Sh::GKV; ++j) {
+        const int e = tid + j * NT;
+        const int t = e * 4 / DK, i0 = e * 4 % DK;
+        if (t < TMAX) {
+            const float eg = __expf(o.g[j]);
+            float *row = ob + t * Sh::TOK + 4 * i0;
+            row[0] = eg * __expf(o.gk[j].x);
+            row[4] = eg * __expf(o.gk[j].y);
+            row[8] = eg * __expf(o.gk[j].z);
+            row[12] = eg * __expf(o.gk[j].w);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < Sh::KQV; ++j) {
+        const int e = tid + j * NT;
+        const int t = e * 8 / DK, i0 = e * 8 % DK;
+        if (t < TMAX) {
+            float *row = ob + t * Sh::TOK + 4 * i0;
+            const uint32_t kw[4] = {o.k[j].x, o.k[j].y, o.k[j].z, o.k[j].w};
+            const uint32_t qw[4] = {o.q[j].x, o.q[j].y, o.q[j].z, o.q[j].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                row[8 * w + 1] = bf16_lo(kw[w]);
+                row[8 * w + 5] = bf16_hi(kw[w]);
+                row[8 * w + 2] = bf16_lo(qw[w]) * scale;
+                row[8 * w + 6] = bf16_hi(qw[w]) * scale;
             }
         }
     }
+#pragma unroll
+    for (int j = 0; j < Sh::VV; ++j) {
+        const int e = tid + j * NT;
+        const int t = e / (TV / 8), c8 = e % (TV / 8);
+        if (t < TMAX) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(ob + t * Sh::TOK + 4 * DK + c8 * 8);
+            dst[0] = f32x4{bf16_lo(o.v[j].x), bf16_hi(o.v[j].x), bf16_lo(o.v[j].y), bf16_hi(o.v[j].y)};
+            dst[1] = f32x4{bf16_lo(o.v[j].z), bf16_hi(o.v[j].z), bf16_lo(o.v[j].w), bf16_hi(o.v[j].w)};
+        }
+    }
+    if (tid < TMAX) ob[tid * Sh::TOK + 4 * DK + TV] = bf16_to_f32((uint16_t)o.beta);
+}
 
+// Element offset of one item's state tile in the pool.
+template <int DK, int TV>
+__device__ __forceinline__ size_t tile_base(const DecodeArgs &a, const Item &m) {
+    return ((size_t)m.slot * a.Hv + m.h) * DK * a.Dv + (size_t)m.tile * TV;
+}
+
+// Bytes from the tile's first element to the end of its (slot, head) block.
+template <int DK, int TV>
+__device__ __forceinline__ uint32_t tile_range(const DecodeArgs &a, const Item &m) {
+    return m.state ? (uint32_t)(DK * a.Dv - m.tile * TV) * 2 : 0u;
+}
+
+template <int DK, int TV, int NT>
+__device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
+                                           u32x4 (&raw)[TileShape<DK, TV, NT>::R], int rg,
+                                           int cg) {
+    using Sh = TileShape<DK, TV, NT>;
+    const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
+                              tile_range<DK, TV>(a, m));
+#pragma unroll
+    for (int r = 0; r < Sh::R; ++r)
+        raw[r] = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (uint32_t)(((rg + r * Sh::RPP) * a.Dv + cg * 8) * 2), 0, kCacheNT);
+}
+
+// Sum of x over the lanes of this wave that hold the same columns (LPR apart). Every lane
+// ends with the same value (each step adds a pair of lanes in both orders, and IEEE
+// addition is commutative).
+template <int LPR>
+__device__ __forceinline__ float colsum(float x) {
+    if constexpr (LPR == 8) {
+        // row_ror:8 within each 16-lane row pairs lane i with lane i ^ 8
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    }
+    {
+        // lanes 16-31 <-> 0-15 and 48-63 <-> 32-47: each lane meets lane ^ 16
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        // the two halves of the wave: each lane meets lane ^ 32
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+
+template <int DK, int TV, int NT, int NBUF, int TMAX>
+struct Pipeline {
+    using Sh = TileShape<DK, TV, NT, TMAX>;
+    u32x4 raw[NBUF][Sh::R];        // state tiles in flight (ring)
+    Ops<DK, TV, NT, TMAX> ops[2];  // operands of the current and the next item
+};
+
+// One token on the thread's part of the state: step 1 (decay) fused with the partial sums
+// of steps 2 and 4, the reduction over D_k, then step 3 (update). Leaves in o the output
+// columns of this thread (every row group holds them). `exb` is this token's exchange
+// buffer; the one barrier inside must be reached by the whole workgroup.
+template <int DK, int TV, int NT, int R>
+__device__ __forceinline__ void token_step(float (&S)[R][8], const float *tok, float *exb,
+                                           int tid, float (&o)[8]) {
+    using Sh = TileShape<DK, TV, NT>;
+    static_assert(R == Sh::R, "rows per thread");
+    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, NW = Sh::NW;
+    const int lane = tid & 63, wave = tid >> 6, cg = tid % LPR, rg = tid / LPR;
+    float pk[CPL], pq[CPL], kr[R];
+    float kq = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) pk[c] = pq[c] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const f32x4 dkq = *reinterpret_cast<const f32x4 *>(tok + 4 * (rg + r * RPP));
+        const float d = dkq.x, kk = dkq.y, qq = dkq.z;
+        kr[r] = kk;
+        kq = fmaf(kk, qq, kq);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float s = S[r][c] * d;
+            S[r][c] = s;
+            pk[c] = fmaf(s, kk, pk[c]);
+            pq[c] = fmaf(s, qq, pq[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        pk[c] = colsum<LPR>(pk[c]);
+        pq[c] = colsum<LPR>(pq[c]);
+    }
+    kq = colsum<LPR>(kq);
+    if (lane < LPR) {
+        f32x4 *dp = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + cg * CPL);
+        dp[0] = f32x4{pk[0], pk[1], pk[2], pk[3]};
+        dp[1] = f32x4{pk[4], pk[5], pk[6], pk[7]};
+        f32x4 *dq = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + TV + cg * CPL);
+        dq[0] = f32x4{pq[0], pq[1], pq[2], pq[3]};
+        dq[1] = f32x4{pq[4], pq[5], pq[6], pq[7]};
+        if (lane == 0) exb[wave * Sh::EXW + 2 * TV] = kq;
+    }
+    __syncthreads();
+    f32x4 P0 = {0.f, 0.f, 0.f, 0.f}, P1 = P0, Q0 = P0, Q1 = P0;
+    float KQ = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const f32x4 *sp = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + cg * CPL);
+        const f32x4 *sq = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + TV + cg * CPL);
+        P0 += sp[0];
+        P1 += sp[1];
+        Q0 += sq[0];
+        Q1 += sq[1];
+        KQ += exb[w * Sh::EXW + 2 * TV];
+    }
+    const float Pv[CPL] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
+    const float Qv[CPL] = {Q0.x, Q0.y, Q0.z, Q0.w, Q1.x, Q1.y, Q1.z, Q1.w};
+    const f32x4 *vv = reinterpret_cast<const f32x4 *>(tok + 4 * DK + cg * CPL);
+    const f32x4 v0 = vv[0], v1 = vv[1];
+    const float V[CPL] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float bt = tok[4 * DK + TV];
+    float u[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        u[c] = bt * (V[c] - Pv[c]);
+        o[c] = fmaf(KQ, u[c], Qv[c]);  // = S_new^T (scale q) on these columns
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[r][c] = fmaf(kr[r], u[c], S[r][c]);
+}
+
+// Every item issues the same sequence of vector memory instructions whatever its lengths
+// and slot (empty buffer ranges drop the accesses that must not happen), so the counter
+// waits the compiler places before the next item's first use of its prefetched data stay
+// exact and never wait on this item's stores.
+
+// Output rows of one (b, h): row group 0 writes its 8 columns, the other lanes aim past the
+// range (their stores are dropped).
+struct OutRows {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t off;
+    bool writer;
+};
+
+template <int TV>
+__device__ __forceinline__ OutRows out_rows(const DecodeArgs &a, const Item &m, int cg, int rg) {
+    const size_t bhT = ((size_t)m.b * a.Hv + m.h) * a.T;
+    OutRows r;
+    r.rs = make_rsrc(a.out + bhT * a.Dv, (uint32_t)(a.T * a.Dv * 2));
+    r.writer = rg == 0;
+    r.off = (uint32_t)((m.tile * TV + cg * 8) * 2);
+    return r;
+}
+
+__device__ __forceinline__ void store_out_row(const DecodeArgs &a, const OutRows &w, int t,
+                                              const float (&o)[8]) {
+    u32x4 v;
+    v.x = pack_bf16x2(o[0], o[1]);
+    v.y = pack_bf16x2(o[2], o[3]);
+    v.z = pack_bf16x2(o[4], o[5]);
+    v.w = pack_bf16x2(o[6], o[7]);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        v, w.rs, w.writer ? w.off + (uint32_t)(t * a.Dv * 2) : 0x7FFFFFF0u, 0, 0);
+}
+
+// General form (T > 1): the tile is widened to fp32 registers once and kept there across
+// the tokens. Loop phase P. Returns false when the workgroup has no item left.
+template <int DK, int TV, int NT, int NBUF, int P>
+__device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &x,
+                                              Pipeline<DK, TV, NT, NBUF, kMaxT> &pl, float *lds,
+                                              int &it, int &xc, int tid) {
+    using Sh = TileShape<DK, TV, NT, kMaxT>;
+    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, R = Sh::R;
+    if (it >= a.n_items) return false;
+    const int G = gridDim.x;
+    const int cg = tid % LPR, rg = tid / LPR;
+    const Item m = resolve(a, x, it);
+
+    // Operands of the next item go in flight; this item's are staged in LDS.
+    load_ops<DK, TV, NT, kMaxT>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
+    float *ob = lds + (P & 1) * Sh::OPS;
+    stage_ops<DK, TV, NT, kMaxT>(pl.ops[P & 1], ob, a.scale, tid);
+    __syncthreads();
+
+    float S[R][CPL];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const u32x4 w = pl.raw[P % NBUF][r];
+        S[r][0] = bf16_lo(w.x); S[r][1] = bf16_hi(w.x);
+        S[r][2] = bf16_lo(w.y); S[r][3] = bf16_hi(w.y);
+        S[r][4] = bf16_lo(w.z); S[r][5] = bf16_hi(w.z);
+        S[r][6] = bf16_lo(w.w); S[r][7] = bf16_hi(w.w);
+    }
+    // The ring slot just widened receives the state of the item NBUF ahead.
+    load_state<DK, TV, NT>(a, resolve(a, x, it + NBUF * G), pl.raw[P % NBUF], rg, cg);
+
+    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
+                               tile_range<DK, TV>(a, m));
     auto commit = [&]() {
-        uint16_t *dst = a.pool_out + srow0 * a.Dv + col0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            uint4 w;
+            u32x4 w;
             w.x = pack_bf16x2(S[r][0], S[r][1]);
             w.y = pack_bf16x2(S[r][2], S[r][3]);
             w.z = pack_bf16x2(S[r][4], S[r][5]);
             w.w = pack_bf16x2(S[r][6], S[r][7]);
-            *reinterpret_cast<uint4 *>(dst + (size_t)(rg + r * RPP) * a.Dv) = w;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                w, rso, (uint32_t)(((rg + r * RPP) * a.Dv + cg * CPL) * 2), 0, kCacheNT);
         }
     };
-    if (valid && n == 0) commit();
+    const OutRows orow = out_rows<TV>(a, m, cg, rg);
+    float *ex = lds + 2 * Sh::OPS;
+    float o[CPL];
+    if (m.n == 0) commit();
+    for (int t = 0; t < m.L; ++t) {
+        float *exb = ex + (xc & 1) * Sh::EX;
+        ++xc;
+        token_step<DK, TV, NT, R>(S, ob + t * Sh::TOK, exb, tid, o);
+        store_out_row(a, orow, t, o);
+        if (t + 1 == m.n) commit();
+    }
+    // Padded tokens and skipped entries: +0.0 output rows.
+    const float zero[CPL] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = m.L; t < a.T; ++t) store_out_row(a, orow, t, zero);
+    it += G;
+    return true;
+}
 
-    float *ex = lds + T * Sh::TOK;
-    for (int t = 0; t < L; ++t) {
-        const float *tok = lds + t * Sh::TOK;
-        float pk[CPL], pq[CPL], kr[R];
-        float kq = 0.f;
+// Single-token form (T = 1). The tile stays in its packed bf16 registers: the reductions
+// widen it on the fly, and the update recomputes the decayed element, adds k (x) u and packs
+// straight into the commit stores, so no fp32 copy of the tile is held. A token that is
+// absent (L = 0) reads only zeros: decay 1, u = 0, output +0.0. A rejected token (n = 0)
+// commits the incoming bytes unchanged. The ring slot of item s is refilled (item s + NBUF)
+// once its commit has been issued.
+template <int DK, int TV, int NT, int NBUF, int P>
+__device__ __forceinline__ bool process_one(const DecodeArgs &a, const Index &x,
+                                            Pipeline<DK, TV, NT, NBUF, 1> &pl, float *lds,
+                                            int &it, int tid) {
+    using Sh = TileShape<DK, TV, NT, 1>;
+    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, R = Sh::R, NW = Sh::NW;
+    if (it >= a.n_items) return false;
+    const int G = gridDim.x;
+    const int lane = tid & 63, wave = tid >> 6, cg = tid % LPR, rg = tid / LPR;
+    const Item m = resolve(a, x, it);
+
+    load_ops<DK, TV, NT, 1>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
+    float *ob = lds + (P & 1) * Sh::OPS;
+    stage_ops<DK, TV, NT, 1>(pl.ops[P & 1], ob, a.scale, tid);
+    __syncthreads();
+
+    u32x4(&W)[R] = pl.raw[P % NBUF];
+    // Step 1 (decay) fused with the partial sums of steps 2 and 4.
+    float pk[CPL], pq[CPL], kr[R], dr[R];
+    float kq = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) pk[c] = pq[c] = 0.f;
-        // Step 1 (decay) fused with the partial sums of steps 2 and 4.
+    for (int c = 0; c < CPL; ++c) pk[c] = pq[c] = 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int i = rg + r * RPP;
-            const float d = tok[i], kk = tok[DK + i], qq = tok[2 * DK + i];
-            kr[r] = kk;
-            kq = fmaf(kk, qq, kq);
+    for (int r = 0; r < R; ++r) {
+        const f32x4 dkq = *reinterpret_cast<const f32x4 *>(ob + 4 * (rg + r * RPP));
+        const float d = dkq.x, kk = dkq.y, qq = dkq.z;
+        dr[r] = d;
+        kr[r] = kk;
+        kq = fmaf(kk, qq, kq);
+        const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const float s = S[r][c] * d;
-                S[r][c] = s;
-                pk[c] = fmaf(s, kk, pk[c]);
-                pq[c] = fmaf(s, qq, pq[c]);
-            }
+        for (int j = 0; j < 4; ++j) {
+            const float s0 = bf16_lo(w[j]) * d, s1 = bf16_hi(w[j]) * d;
+            pk[2 * j] = fmaf(s0, kk, pk[2 * j]);
+            pq[2 * j] = fmaf(s0, qq, pq[2 * j]);
+            pk[2 * j + 1] = fmaf(s1, kk, pk[2 * j + 1]);
+            pq[2 * j + 1] = fmaf(s1, qq, pq[2 * j + 1]);
         }
-        // Lanes of one wave holding the same columns are LPR apart.
+    }
 #pragma unroll
-        for (int m = LPR; m < 64; m <<= 1) {
+    for (int c = 0; c < CPL; ++c) {
+        pk[c] = colsum<LPR>(pk[c]);
+        pq[c] = colsum<LPR>(pq[c]);
+    }
+    kq = colsum<LPR>(kq);
+    float *exb = lds + 2 * Sh::OPS + (P & 1) * Sh::EX;
+    if (lane < LPR) {
+        f32x4 *dp = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + cg * CPL);
+        dp[0] = f32x4{pk[0], pk[1], pk[2], pk[3]};
+        dp[1] = f32x4{pk[4], pk[5], pk[6], pk[7]};
+        f32x4 *dq = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + TV + cg * CPL);
+        dq[0] = f32x4{pq[0], pq[1], pq[2], pq[3]};
+        dq[1] = f32x4{pq[4], pq[5], pq[6], pq[7]};
+        if (lane == 0) exb[wave * Sh::EXW + 2 * TV] = kq;
+    }
+    __syncthreads();
+    f32x4 P0 = {0.f, 0.f, 0.f, 0.f}, P1 = P0, Q0 = P0, Q1 = P0;
+    float KQ = 0.f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                pk[c] += __shfl_xor(pk[c], m);
-                pq[c] += __shfl_xor(pq[c], m);
-            }
-            kq += __shfl_xor(kq, m);
-        }
-        float *exb = ex + (t & 1) * Sh::EX;
-        if (lane < LPR) {
-            float *dst = exb + wave * Sh::EXW;
+    for (int w = 0; w < NW; ++w) {
+        const f32x4 *sp = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + cg * CPL);
+        const f32x4 *sq = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + TV + cg * CPL);
+        P0 += sp[0];
+        P1 += sp[1];
+        Q0 += sq[0];
+        Q1 += sq[1];
+        KQ += exb[w * Sh::EXW + 2 * TV];
+    }
+    const float Pv[CPL] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
+    const float Qv[CPL] = {Q0.x, Q0.y, Q0.z, Q0.w, Q1.x, Q1.y, Q1.z, Q1.w};
+    const f32x4 *vv = reinterpret_cast<const f32x4 *>(ob + 4 * DK + cg * CPL);
+    const f32x4 v0 = vv[0], v1 = vv[1];
+    const float V[CPL] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float bt = ob[4 * DK + TV];
+    // Step 3 (delta update) and step 4 (output with the updated state).
+    float u[CPL], o[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                dst[cg * CPL + c] = pk[c];
-                dst[TV + cg * CPL + c] = pq[c];
-            }
-            if (lane == 0) dst[2 * TV] = kq;
-        }
-        __syncthreads();
-        float P[CPL], Q[CPL], KQ = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) P[c] = Q[c] = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float *src = exb + w * Sh::EXW;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                P[c] += src[cg * CPL + c];
-                Q[c] += src[TV + cg * CPL + c];
-            }
-            KQ += src[2 * TV];
-        }
-        // Step 3 (delta update) and step 4 (output with the updated state).
-        const float bt = tok[3 * DK + TV];
-        float u[CPL], o[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            u[c] = bt * (tok[3 * DK + cg * CPL + c] - P[c]);
-            o[c] = fmaf(KQ, u[c], Q[c]);
-        }
-        if (rg == 0) {
-            uint4 w;
-            w.x = pack_bf16x2(o[0], o[1]);
-            w.y = pack_bf16x2(o[2], o[3]);
-            w.z = pack_bf16x2(o[4], o[5]);
-            w.w = pack_bf16x2(o[6], o[7]);
-            *reinterpret_cast<uint4 *>(out_row + (size_t)t * a.Dv) = w;
-        }
+    for (int c = 0; c < CPL; ++c) {
+        u[c] = bt * (V[c] - Pv[c]);
+        o[c] = fmaf(KQ, u[c], Qv[c]);
+    }
+    store_out_row(a, out_rows<TV>(a, m, cg, rg), 0, o);
+
+    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
+                               tile_range<DK, TV>(a, m));
+    if (m.n == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                W[r], rso, (uint32_t)(((rg + r * RPP) * a.Dv + cg * CPL) * 2), 0, kCacheNT);
+    } else {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) S[r][c] = fmaf(kr[r], u[c], S[r][c]);
-        if (t + 1 == n) commit();
+        for (int r = 0; r < R; ++r) {
+            const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
+            uint32_t nw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                nw[j] = pack_bf16x2(fmaf(kr[r], u[2 * j], bf16_lo(w[j]) * dr[r]),
+                                    fmaf(kr[r], u[2 * j + 1], bf16_hi(w[j]) * dr[r]));
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{nw[0], nw[1], nw[2], nw[3]}, rso,
+                (uint32_t)(((rg + r * RPP) * a.Dv + cg * CPL) * 2), 0, kCacheNT);
+        }
     }
-    // Padded tokens (and skipped entries): +0.0 output rows.
-    if (rg == 0)
-        for (int t = L; t < T; ++t)
-            *reinterpret_cast<uint4 *>(out_row + (size_t)t * a.Dv) = make_uint4(0, 0, 0, 0);
+    load_state<DK, TV, NT>(a, resolve(a, x, it + NBUF * G), W, rg, cg);
+    it += G;
+    return true;
+}
+
+// Phases P .. U-1 of the unrolled item loop; false once the workgroup has no item left.
+template <int DK, int TV, int NT, int NBUF, bool ONE_TOKEN, int P, int U>
+__device__ __forceinline__ bool run_phases(const DecodeArgs &a, const Index &x,
+                                           Pipeline<DK, TV, NT, NBUF, ONE_TOKEN ? 1 : kMaxT> &pl,
+                                           float *lds, int &it, int &xc, int tid) {
+    if constexpr (P == U) {
+        return true;
+    } else {
+        bool more;
+        if constexpr (ONE_TOKEN)
+            more = process_one<DK, TV, NT, NBUF, P>(a, x, pl, lds, it, tid);
+        else
+            more = process_multi<DK, TV, NT, NBUF, P>(a, x, pl, lds, it, xc, tid);
+        return more && run_phases<DK, TV, NT, NBUF, ONE_TOKEN, P + 1, U>(a, x, pl, lds, it, xc, tid);
+    }
+}
+
+template <int DK, int TV, int NT, int NBUF, bool ONE_TOKEN>
+__global__ __launch_bounds__(NT, RGDR_DECODE_MIN_WAVES) void decode_kernel(const DecodeArgs a,
+                                                       const int32_t *__restrict__ lens,
+                                                       const int32_t *__restrict__ idx,
+                                                       const int32_t *__restrict__ nacc) {
+    constexpr int TMAX = ONE_TOKEN ? 1 : kMaxT;
+    using Sh = TileShape<DK, TV, NT, TMAX>;
+    const Index x{lens, idx, nacc};
+    __shared__ f32x4 lds4[Sh::LDS_FLOATS / 4];
+    float *lds = reinterpret_cast<float *>(lds4);
+    const int tid = threadIdx.x;
+    const int cg = tid % Sh::LPR, rg = tid / Sh::LPR;
+    const int G = gridDim.x;
+    int it = blockIdx.x;
+    int xc = 0;
+    Pipeline<DK, TV, NT, NBUF, TMAX> pl;
+    // Prologue: state of the first item, operands of the first item, state of the next
+    // NBUF-1 items.
+    load_state<DK, TV, NT>(a, resolve(a, x, it), pl.raw[0], rg, cg);
+    load_ops<DK, TV, NT, TMAX>(a, resolve(a, x, it), pl.ops[0], tid);
+#pragma unroll
+    for (int j = 1; j < NBUF; ++j)
+        load_state<DK, TV, NT>(a, resolve(a, x, it + j * G), pl.raw[j], rg, cg);
+    // Item loop, unrolled over the ring and the two operand buffers, so that every buffer
+    // index is a compile-time constant.
+    constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
+    while (run_phases<DK, TV, NT, NBUF, ONE_TOKEN, 0, U>(a, x, pl, lds, it, xc, tid)) {
+    }
+}
+
+// Workgroups that fit on the device at once (CUs x resident per CU), per device, queried once.
+template <int DK, int TV, int NT, int NBUF, bool ONE_TOKEN>
+static int resident_grid() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] > 0) return cached[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, decode_kernel<DK, TV, NT, NBUF, ONE_TOKEN>, NT, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    cached[dev] = cus * per_cu;
+    return cached[dev];
+}
+
+template <int DK, int TV, bool ONE_TOKEN>
+static hipError_t launch_decode_t(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
+                                  const int32_t *nacc, hipStream_t stream) {
+    constexpr int NT = RGDR_DECODE_THREADS;
+    // Ring length: the general form refills a slot as soon as it is widened, the single-token
+    // form only after its commit, so it needs one more slot for the same depth.
+    constexpr int NBUF = RGDR_DECODE_DEPTH + (ONE_TOKEN ? 1 : 0);
+    static_assert(RGDR_DECODE_DEPTH >= 1 && RGDR_DECODE_DEPTH <= 3, "state tiles in flight: 1-3");
+    const int resident = resident_grid<DK, TV, NT, NBUF, ONE_TOKEN>();
+    if (resident <= 0) return hipErrorInvalidDevice;
+    const int grid = a.n_items < resident ? a.n_items : resident;
+    hipLaunchKernelGGL((decode_kernel<DK, TV, NT, NBUF, ONE_TOKEN>), dim3(grid), dim3(NT), 0,
+                       stream, a, lens, idx, nacc);
+    return hipGetLastError();
 }
 
 template <int DK, int TV>
-static hipError_t launch_decode(const DecodeArgs &a, unsigned grid, hipStream_t stream) {
-    constexpr int NT = 256;
-    const size_t lds = TileShape<DK, TV, NT>::lds_bytes(a.T);
-    hipLaunchKernelGGL((decode_kernel<DK, TV, NT>), dim3(grid), dim3(NT), lds, stream, a);
-    return hipGetLastError();
+static hipError_t launch_decode(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
+                                const int32_t *nacc, hipStream_t stream) {
+    return a.T == 1 ? launch_decode_t<DK, TV, true>(a, lens, idx, nacc, stream)
+                    : launch_decode_t<DK, TV, false>(a, lens, idx, nacc, stream);
 }
 
 }  // namespace rgdr
@@ -242,20 +668,20 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
     if (!query || !key || !value || !beta || !state_pool || !actual_seq_lengths ||
         !ssm_state_indices || !g || !gk || !num_accepted_tokens || !out || !state_out)
         return RGDR_ERR_NULL;
-    if (B <= 0 || H_q <= 0 || H_v <= 0 || T <= 0 || D_k <= 0 || D_v <= 0 || N_slots <= 0)
+    if (B < 0 || H_q <= 0 || H_v <= 0 || T <= 0 || D_k <= 0 || D_v <= 0 || N_slots <= 0)
         return RGDR_ERR_SHAPE;
     if (T > kMaxT || H_v % H_q != 0) return RGDR_ERR_SHAPE;
-    if ((D_k != 64 && D_k != 128) || D_v % 64 != 0) return RGDR_ERR_UNSUPPORTED;
+    if ((D_k != 64 && D_k != 128) || D_v % 64 != 0 || D_v > 4096) return RGDR_ERR_UNSUPPORTED;
     if (!aligned(value, 16) || !aligned(state_pool, 16) || !aligned(out, 16) ||
-        !aligned(state_out, 16) || !aligned(query, 2) || !aligned(key, 2) ||
-        !aligned(beta, 2) || !aligned(g, 4) || !aligned(gk, 4) ||
+        !aligned(state_out, 16) || !aligned(query, 16) || !aligned(key, 16) ||
+        !aligned(beta, 2) || !aligned(g, 4) || !aligned(gk, 16) ||
         !aligned(actual_seq_lengths, 4) || !aligned(ssm_state_indices, 4) ||
         !aligned(num_accepted_tokens, 4))
         return RGDR_ERR_ALIGN;
 
-    const int tile_v = (D_v % 128 == 0) ? 128 : 64;
-    const long long grid = (long long)B * H_v * (D_v / tile_v);
-    if (grid > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
+    const int tile_v = (D_v % 128 == 0 && RGDR_DECODE_TILE_V != 64) ? 128 : 64;
+    const long long items = (long long)B * H_v * (D_v / tile_v);
+    if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
 
     DecodeArgs a;
     a.q = static_cast<const uint16_t *>(query);
@@ -263,9 +689,6 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
     a.v = static_cast<const uint16_t *>(value);
     a.beta = static_cast<const uint16_t *>(beta);
     a.pool = static_cast<const uint16_t *>(state_pool);
-    a.lens = actual_seq_lengths;
-    a.idx = ssm_state_indices;
-    a.nacc = num_accepted_tokens;
     a.g = g;
     a.gk = gk;
     a.out = static_cast<uint16_t *>(out);
@@ -278,13 +701,15 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
     a.N_slots = N_slots;
     a.ntiles = D_v / tile_v;
     a.group = H_v / H_q;
+    a.n_items = (int)items;
 
+    const int32_t *L = actual_seq_lengths, *I = ssm_state_indices, *N = num_accepted_tokens;
     hipError_t err;
     if (D_k == 128)
-        err = tile_v == 128 ? launch_decode<128, 128>(a, (unsigned)grid, stream)
-                            : launch_decode<128, 64>(a, (unsigned)grid, stream);
+        err = tile_v == 128 ? launch_decode<128, 128>(a, L, I, N, stream)
+                            : launch_decode<128, 64>(a, L, I, N, stream);
     else
-        err = tile_v == 128 ? launch_decode<64, 128>(a, (unsigned)grid, stream)
-                            : launch_decode<64, 64>(a, (unsigned)grid, stream);
+        err = tile_v == 128 ? launch_decode<64, 128>(a, L, I, N, stream)
+                            : launch_decode<64, 64>(a, L, I, N, stream);
     return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
 }

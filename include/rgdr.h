@@ -56,8 +56,8 @@ typedef enum { RGDR_F32 = 0, RGDR_F16 = 1, RGDR_BF16 = 2 } rgdr_dtype;
  * the page's names and meaning).
  *
  *   query               bf16 [B, H_q, T, D_k]  L2-normalised per head vector (caller's
- *                       precondition, not checked). 2-byte aligned.
- *   key                 bf16 [B, H_q, T, D_k]  as query. Value head h reads query/key head
+ *                       precondition, not checked). 16-byte aligned.
+ *   key                 bf16 [B, H_q, T, D_k]  as query (16-byte aligned). Value head h reads query/key head
  *                       h / (H_v / H_q), i.e. floor(h * H_q / H_v).
  *   value               bf16 [B, H_v, T, D_v]  16-byte aligned.
  *   beta                bf16 [B, H_v, T]       delta step size, in (0, 1) (not checked).
@@ -71,6 +71,7 @@ typedef enum { RGDR_F32 = 0, RGDR_F16 = 1, RGDR_BF16 = 2 } rgdr_dtype;
  *                       rows are +0.0 and no state is read or written.
  *   g                   fp32 [B, H_v, T]        global log-decay, negative (not checked).
  *   gk                  fp32 [B, H_v, T, D_k]   per-key-dimension log-decay, negative.
+ *                       16-byte aligned.
  *   num_accepted_tokens int32 [B]  n: the state committed for entry b is the state after
  *                       its first n tokens (clamped to [0, L]); n = L in ordinary decoding.
  *   scale               q is multiplied by it before step 4 (the page's scale_value).
