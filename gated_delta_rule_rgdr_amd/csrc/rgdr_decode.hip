@@ -4,33 +4,36 @@
 // section (decay, memory read, delta update, output, token by token) and parameter list.
 //
 // The step is HBM-bound: each (batch entry, value head) pair streams its D_k x D_v bf16
-// state in once and out once; everything else is small. The kernel is built around that
-// stream:
+// state in once and out once; everything else is small. Two kernel forms share the
+// plumbing below; T decides which one runs.
 //
-//   * Work item = one (b, h, D_v tile) state tile. Workgroups are persistent: workgroup w
-//     takes items w, w + G, w + 2G, ... (G = grid size, what fits on the CUs at once), so
-//     the items in flight at one moment are neighbours in the pool.
-//   * State tiles travel through a ring of NBUF register buffers filled by 16-byte
-//     nontemporal buffer loads. As soon as item s has been widened to fp32, its ring slot
-//     receives item s + NBUF, so NBUF tiles are in flight while item s is computed and
-//     stored. The item loop is unrolled over the ring, so every slot is a fixed register
-//     set and no register copy waits on a load in flight. Loads past the last item, or of
-//     a skipped entry, use an empty buffer range and move no data.
-//   * The small per-item operands (gk, g, k, q, the v tile, beta) of item s+1 are loaded
-//     into registers during item s and staged in LDS when item s+1 starts; the decay
-//     factors exp(g) exp(gk) are formed there, once per element.
-//   * A thread owns 8 consecutive columns (one 16-byte bf16 vector) of R rows spaced RPP
-//     apart; each load/store instruction of the workgroup covers RPP whole tile rows.
-//   * Per token, steps 2 and 4 share ONE reduction over D_k: with S' the decayed state,
-//     p = S'^T k and r = S'^T (scale q) are reduced together with the scalar k.(scale q);
-//     then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q),
-//     and S_new = S' + k (x) u is one FMA per element.
-//   * The reduction: in-thread over R rows, then across the lanes of the wave holding the
-//     same columns with v_permlane16/32_swap (and a DPP row rotate for 64-wide tiles), then
-//     a fixed-order sum over the waves through a double-buffered LDS slot: one barrier per
-//     token, deterministic results.
+// Wave form (T = 1, every decode workload). One wave owns one (b, h, 128- or 64-column)
+// tile over all D_k rows:
+//   * lane (cg, rg) holds 8 consecutive columns (a 16-byte bf16 vector) of the rows rg,
+//     rg + RG, ...; a wave-wide load covers RG whole tile rows (1 KiB contiguous at 128
+//     columns), with 16-byte nontemporal buffer loads;
+//   * the tile stays packed in bf16 registers: the reduction widens it on the fly, the
+//     update widens it again, adds k (x) u and packs straight into the commit stores;
+//   * the D_k reduction finishes inside the wave (in-lane over the lane's rows, then
+//     v_permlane16/32_swap and a DPP row rotate), so waves need no LDS exchange and no
+//     barrier and run independently; operands sit in a wave-private LDS area;
+//   * waves are persistent over items (w, w + G, ...) with a ring of packed tiles; items
+//     past the end and skipped entries use empty buffer ranges (no data moves).
 //
-// No matrix cores: the work per token is a matrix-vector product and a rank-1 update.
+// Workgroup form (1 < T <= 8). One 256-thread workgroup owns one (b, h, tile) and keeps it
+// in fp32 registers across the tokens; the next item's state and operands are in flight
+// while the current item is computed; per token the D_k reduction ends with a fixed-order
+// sum over the waves through a double-buffered LDS slot (one barrier per token).
+//
+// Both forms: per token, steps 2 and 4 share ONE reduction over D_k. With S' the decayed
+// state, p = S'^T k and r = S'^T (scale q) are reduced together with the scalar
+// k.(scale q); then u = beta (v - p) and o = r + (k.(scale q)) u, which equals
+// S_new^T (scale q), and S_new = S' + k (x) u. Every item issues the same sequence of vector
+// memory instructions whatever its lengths and slot (the accesses that must not happen get
+// empty buffer ranges), and the per-entry index arrays are read with scalar loads, so the
+// in-order vector-memory counter waits never drain the prefetched state. Results are
+// deterministic. No matrix cores: per token the work is a matrix-vector product and a
+// rank-1 update.
 #include "rgdr_common.h"
 
 namespace rgdr {
@@ -53,12 +56,46 @@ constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 #ifndef RGDR_DECODE_MIN_WAVES
 #define RGDR_DECODE_MIN_WAVES 2
 #endif
+// Wave form (T = 1): ring length per tile width, and its grid: 0 = as many waves as fit at
+// once (persistent), 1 = one wave per item.
+#ifndef RGDR_WAVE_NBUF
+#define RGDR_WAVE_NBUF 2
+#endif
+#ifndef RGDR_WAVE_NBUF_128
+#define RGDR_WAVE_NBUF_128 1
+#endif
+// Tile width of the wave form: 128 columns (whole 256-byte rows at D_v = 128) when D_v
+// allows it, or 64.
+#ifndef RGDR_WAVE_TILE_V
+#define RGDR_WAVE_TILE_V 128
+#endif
+#ifndef RGDR_WAVE_ONE_SHOT
+#define RGDR_WAVE_ONE_SHOT 0
+#endif
+#ifndef RGDR_WAVE_MIN_WAVES
+#define RGDR_WAVE_MIN_WAVES 2
+#endif
+// Persistent waves per CU for the wave form (0 = as many as fit).
+#ifndef RGDR_WAVE_PER_CU
+#define RGDR_WAVE_PER_CU 0
+#endif
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBufWord3 = 0x00020000;  // raw (unformatted) buffer descriptor, gfx9 family
-constexpr int kCacheNT = 2;            // cache policy bits: nontemporal (streaming)
+// Cache policy bits of the state stream's buffer loads and stores (2 = nontemporal: the
+// state is touched once per call) and of the small operand loads.
+#ifndef RGDR_STATE_LOAD_POLICY
+#define RGDR_STATE_LOAD_POLICY 2
+#endif
+#ifndef RGDR_STATE_STORE_POLICY
+#define RGDR_STATE_STORE_POLICY 2
+#endif
+#ifndef RGDR_OPS_LOAD_POLICY
+#define RGDR_OPS_LOAD_POLICY 0
+#endif
+constexpr int kCacheNT = 2;  // nontemporal (streaming)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3);
@@ -449,144 +486,25 @@ __device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &
     return true;
 }
 
-// Single-token form (T = 1). The tile stays in its packed bf16 registers: the reductions
-// widen it on the fly, and the update recomputes the decayed element, adds k (x) u and packs
-// straight into the commit stores, so no fp32 copy of the tile is held. A token that is
-// absent (L = 0) reads only zeros: decay 1, u = 0, output +0.0. A rejected token (n = 0)
-// commits the incoming bytes unchanged. The ring slot of item s is refilled (item s + NBUF)
-// once its commit has been issued.
-template <int DK, int TV, int NT, int NBUF, int P>
-__device__ __forceinline__ bool process_one(const DecodeArgs &a, const Index &x,
-                                            Pipeline<DK, TV, NT, NBUF, 1> &pl, float *lds,
-                                            int &it, int tid) {
-    using Sh = TileShape<DK, TV, NT, 1>;
-    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, R = Sh::R, NW = Sh::NW;
-    if (it >= a.n_items) return false;
-    const int G = gridDim.x;
-    const int lane = tid & 63, wave = tid >> 6, cg = tid % LPR, rg = tid / LPR;
-    const Item m = resolve(a, x, it);
-
-    load_ops<DK, TV, NT, 1>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
-    float *ob = lds + (P & 1) * Sh::OPS;
-    stage_ops<DK, TV, NT, 1>(pl.ops[P & 1], ob, a.scale, tid);
-    __syncthreads();
-
-    u32x4(&W)[R] = pl.raw[P % NBUF];
-    // Step 1 (decay) fused with the partial sums of steps 2 and 4.
-    float pk[CPL], pq[CPL], kr[R], dr[R];
-    float kq = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) pk[c] = pq[c] = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const f32x4 dkq = *reinterpret_cast<const f32x4 *>(ob + 4 * (rg + r * RPP));
-        const float d = dkq.x, kk = dkq.y, qq = dkq.z;
-        dr[r] = d;
-        kr[r] = kk;
-        kq = fmaf(kk, qq, kq);
-        const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float s0 = bf16_lo(w[j]) * d, s1 = bf16_hi(w[j]) * d;
-            pk[2 * j] = fmaf(s0, kk, pk[2 * j]);
-            pq[2 * j] = fmaf(s0, qq, pq[2 * j]);
-            pk[2 * j + 1] = fmaf(s1, kk, pk[2 * j + 1]);
-            pq[2 * j + 1] = fmaf(s1, qq, pq[2 * j + 1]);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        pk[c] = colsum<LPR>(pk[c]);
-        pq[c] = colsum<LPR>(pq[c]);
-    }
-    kq = colsum<LPR>(kq);
-    float *exb = lds + 2 * Sh::OPS + (P & 1) * Sh::EX;
-    if (lane < LPR) {
-        f32x4 *dp = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + cg * CPL);
-        dp[0] = f32x4{pk[0], pk[1], pk[2], pk[3]};
-        dp[1] = f32x4{pk[4], pk[5], pk[6], pk[7]};
-        f32x4 *dq = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + TV + cg * CPL);
-        dq[0] = f32x4{pq[0], pq[1], pq[2], pq[3]};
-        dq[1] = f32x4{pq[4], pq[5], pq[6], pq[7]};
-        if (lane == 0) exb[wave * Sh::EXW + 2 * TV] = kq;
-    }
-    __syncthreads();
-    f32x4 P0 = {0.f, 0.f, 0.f, 0.f}, P1 = P0, Q0 = P0, Q1 = P0;
-    float KQ = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const f32x4 *sp = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + cg * CPL);
-        const f32x4 *sq = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + TV + cg * CPL);
-        P0 += sp[0];
-        P1 += sp[1];
-        Q0 += sq[0];
-        Q1 += sq[1];
-        KQ += exb[w * Sh::EXW + 2 * TV];
-    }
-    const float Pv[CPL] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
-    const float Qv[CPL] = {Q0.x, Q0.y, Q0.z, Q0.w, Q1.x, Q1.y, Q1.z, Q1.w};
-    const f32x4 *vv = reinterpret_cast<const f32x4 *>(ob + 4 * DK + cg * CPL);
-    const f32x4 v0 = vv[0], v1 = vv[1];
-    const float V[CPL] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const float bt = ob[4 * DK + TV];
-    // Step 3 (delta update) and step 4 (output with the updated state).
-    float u[CPL], o[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        u[c] = bt * (V[c] - Pv[c]);
-        o[c] = fmaf(KQ, u[c], Qv[c]);
-    }
-    store_out_row(a, out_rows<TV>(a, m, cg, rg), 0, o);
-
-    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
-                               tile_range<DK, TV>(a, m));
-    if (m.n == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                W[r], rso, (uint32_t)(((rg + r * RPP) * a.Dv + cg * CPL) * 2), 0, kCacheNT);
-    } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
-            uint32_t nw[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                nw[j] = pack_bf16x2(fmaf(kr[r], u[2 * j], bf16_lo(w[j]) * dr[r]),
-                                    fmaf(kr[r], u[2 * j + 1], bf16_hi(w[j]) * dr[r]));
-            __builtin_amdgcn_raw_buffer_store_b128(
-                u32x4{nw[0], nw[1], nw[2], nw[3]}, rso,
-                (uint32_t)(((rg + r * RPP) * a.Dv + cg * CPL) * 2), 0, kCacheNT);
-        }
-    }
-    load_state<DK, TV, NT>(a, resolve(a, x, it + NBUF * G), W, rg, cg);
-    it += G;
-    return true;
-}
-
 // Phases P .. U-1 of the unrolled item loop; false once the workgroup has no item left.
-template <int DK, int TV, int NT, int NBUF, bool ONE_TOKEN, int P, int U>
+template <int DK, int TV, int NT, int NBUF, int P, int U>
 __device__ __forceinline__ bool run_phases(const DecodeArgs &a, const Index &x,
-                                           Pipeline<DK, TV, NT, NBUF, ONE_TOKEN ? 1 : kMaxT> &pl,
-                                           float *lds, int &it, int &xc, int tid) {
+                                           Pipeline<DK, TV, NT, NBUF, kMaxT> &pl, float *lds,
+                                           int &it, int &xc, int tid) {
     if constexpr (P == U) {
         return true;
     } else {
-        bool more;
-        if constexpr (ONE_TOKEN)
-            more = process_one<DK, TV, NT, NBUF, P>(a, x, pl, lds, it, tid);
-        else
-            more = process_multi<DK, TV, NT, NBUF, P>(a, x, pl, lds, it, xc, tid);
-        return more && run_phases<DK, TV, NT, NBUF, ONE_TOKEN, P + 1, U>(a, x, pl, lds, it, xc, tid);
+        return process_multi<DK, TV, NT, NBUF, P>(a, x, pl, lds, it, xc, tid) &&
+               run_phases<DK, TV, NT, NBUF, P + 1, U>(a, x, pl, lds, it, xc, tid);
     }
 }
 
-template <int DK, int TV, int NT, int NBUF, bool ONE_TOKEN>
+template <int DK, int TV, int NT, int NBUF>
 __global__ __launch_bounds__(NT, RGDR_DECODE_MIN_WAVES) void decode_kernel(const DecodeArgs a,
                                                        const int32_t *__restrict__ lens,
                                                        const int32_t *__restrict__ idx,
                                                        const int32_t *__restrict__ nacc) {
-    constexpr int TMAX = ONE_TOKEN ? 1 : kMaxT;
+    constexpr int TMAX = kMaxT;
     using Sh = TileShape<DK, TV, NT, TMAX>;
     const Index x{lens, idx, nacc};
     __shared__ f32x4 lds4[Sh::LDS_FLOATS / 4];
@@ -607,12 +525,245 @@ __global__ __launch_bounds__(NT, RGDR_DECODE_MIN_WAVES) void decode_kernel(const
     // Item loop, unrolled over the ring and the two operand buffers, so that every buffer
     // index is a compile-time constant.
     constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
-    while (run_phases<DK, TV, NT, NBUF, ONE_TOKEN, 0, U>(a, x, pl, lds, it, xc, tid)) {
+    while (run_phases<DK, TV, NT, NBUF, 0, U>(a, x, pl, lds, it, xc, tid)) {
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave-level form for T = 1: one wave owns one (b, h, TVW-column) tile, all D_k rows, so the
+// reduction over D_k finishes inside the wave (in-lane over the lane's rows, then lane
+// swaps) with no LDS exchange and no barrier; waves run independently. Lane (cg, rg) holds
+// columns cg*8 .. cg*8+7 of rows rg, rg + RG, ... (RW = D_k / RG rows, packed bf16); a
+// wave-wide load covers RG consecutive tile rows. Operands are staged in a wave-private LDS
+// area (program order within one wave needs no barrier). Items are walked persistently
+// (item w, w + G, ...); a ring slot is refilled once its tile's commit has been issued.
+// ---------------------------------------------------------------------------------------
+
+template <int DK, int TVW>
+struct WaveShape {
+    static constexpr int LPW = TVW / 8;   // lanes across one tile row
+    static constexpr int RG = 64 / LPW;   // row groups in the wave
+    static constexpr int RW = DK / RG;    // rows per lane
+    static constexpr int RPL = DK / 64;   // operand rows loaded per lane (1 or 2)
+    static constexpr int VPL = TVW / 64;  // v values loaded per lane (1 or 2)
+    static constexpr int OPS = 4 * DK + TVW + 4;  // (d, k, scale*q, 0) per row | v | beta
+    static_assert(DK == 64 || DK == 128, "D_k");
+    static_assert(TVW == 64 || TVW == 128, "tile width");
+};
+
+template <int DK>
+struct WaveOps {
+    float gk[DK / 64];
+    float g;
+    uint32_t k, q;  // DK/64 bf16 values each (low half first)
+    uint32_t v;     // TVW/64 bf16 values of the v tile (low half first)
+    uint32_t beta;
+};
+
+template <int DK, int TVW>
+__device__ __forceinline__ void wave_load_ops(const DecodeArgs &a, const Item &m, WaveOps<DK> &o,
+                                              int lane) {
+    using Sh = WaveShape<DK, TVW>;
+    const size_t bh = (size_t)m.b * a.Hv + m.h;  // T = 1
+    const uint32_t L = (uint32_t)m.L;          // 0 or 1
+    const auto rgk = make_rsrc(a.gk + bh * DK, L * DK * 4);
+    const size_t qk0 = ((size_t)m.b * a.Hq + m.hq) * DK;
+    const auto rk = make_rsrc(a.k + qk0, L * DK * 2);
+    const auto rq = make_rsrc(a.q + qk0, L * DK * 2);
+    const auto rv = make_rsrc(a.v + bh * a.Dv, L * (uint32_t)a.Dv * 2);
+    const auto rs = make_rsrc(a.g + bh, L * 4);
+    const auto rb = make_rsrc(a.beta + bh, L * 2);
+    if constexpr (Sh::RPL == 2) {
+        const auto g2 = __builtin_amdgcn_raw_buffer_load_b64(rgk, lane * 8, 0, RGDR_OPS_LOAD_POLICY);
+        o.gk[0] = __uint_as_float(g2[0]);
+        o.gk[1] = __uint_as_float(g2[1]);
+        o.k = __builtin_amdgcn_raw_buffer_load_b32(rk, lane * 4, 0, RGDR_OPS_LOAD_POLICY);
+        o.q = __builtin_amdgcn_raw_buffer_load_b32(rq, lane * 4, 0, RGDR_OPS_LOAD_POLICY);
+    } else {
+        o.gk[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rgk, lane * 4, 0, RGDR_OPS_LOAD_POLICY));
+        o.k = __builtin_amdgcn_raw_buffer_load_b16(rk, lane * 2, 0, RGDR_OPS_LOAD_POLICY);
+        o.q = __builtin_amdgcn_raw_buffer_load_b16(rq, lane * 2, 0, RGDR_OPS_LOAD_POLICY);
+    }
+    if constexpr (Sh::VPL == 2)
+        o.v = __builtin_amdgcn_raw_buffer_load_b32(rv, (uint32_t)((m.tile * TVW + lane * 2) * 2), 0, RGDR_OPS_LOAD_POLICY);
+    else
+        o.v = __builtin_amdgcn_raw_buffer_load_b16(rv, (uint32_t)((m.tile * TVW + lane) * 2), 0, RGDR_OPS_LOAD_POLICY);
+    o.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 0, 0, RGDR_OPS_LOAD_POLICY));
+    o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, 0, 0, RGDR_OPS_LOAD_POLICY);
+}
+
+template <int DK, int TVW>
+__device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, float scale,
+                                               int lane) {
+    using Sh = WaveShape<DK, TVW>;
+    const float eg = __expf(o.g);
+#pragma unroll
+    for (int j = 0; j < Sh::RPL; ++j) {
+        const uint32_t kb = j ? o.k & 0xFFFF0000u : o.k << 16;
+        const uint32_t qb = j ? o.q & 0xFFFF0000u : o.q << 16;
+        *reinterpret_cast<f32x4 *>(ob + 4 * (lane * Sh::RPL + j)) =
+            f32x4{eg * __expf(o.gk[j]), __uint_as_float(kb), __uint_as_float(qb) * scale, 0.f};
+    }
+    if constexpr (Sh::VPL == 2)
+        *reinterpret_cast<float2 *>(ob + 4 * DK + 2 * lane) = make_float2(bf16_lo(o.v), bf16_hi(o.v));
+    else
+        ob[4 * DK + lane] = bf16_lo(o.v);
+    if (lane == 0) ob[4 * DK + TVW] = bf16_to_f32((uint16_t)o.beta);
+}
+
+template <int DK, int TVW, int NBUF>
+struct WavePipe {
+    u32x4 raw[NBUF][WaveShape<DK, TVW>::RW];
+    WaveOps<DK> ops[2];
+};
+
+template <int DK, int TVW>
+__device__ __forceinline__ void wave_load_state(const DecodeArgs &a, const Item &m,
+                                                u32x4 (&raw)[WaveShape<DK, TVW>::RW], int cg,
+                                                int rg) {
+    using Sh = WaveShape<DK, TVW>;
+    const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TVW>(a, m) : 0),
+                              tile_range<DK, TVW>(a, m));
+#pragma unroll
+    for (int r = 0; r < Sh::RW; ++r)
+        raw[r] = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (uint32_t)(((rg + Sh::RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_LOAD_POLICY);
+}
+
+template <int DK, int TVW, int NBUF, int P>
+__device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x,
+                                             WavePipe<DK, TVW, NBUF> &pl, float *lds, int &it,
+                                             int lane) {
+    using Sh = WaveShape<DK, TVW>;
+    constexpr int RW = Sh::RW, RG = Sh::RG, LPW = Sh::LPW;
+    if (it >= a.n_items) return false;
+    const int G = gridDim.x;
+    const int cg = lane % LPW, rg = lane / LPW;
+    const Item m = resolve(a, x, it);
+
+    wave_load_ops<DK, TVW>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], lane);
+    float *ob = lds + (P & 1) * Sh::OPS;
+    wave_stage_ops<DK, TVW>(pl.ops[P & 1], ob, a.scale, lane);
+
+    u32x4(&W)[RW] = pl.raw[P % NBUF];
+    // Step 1 (decay) fused with the partial sums of steps 2 and 4.
+    float pk[8], pq[8];
+    float kq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pk[c] = pq[c] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const f32x4 dkq = *reinterpret_cast<const f32x4 *>(ob + 4 * (rg + RG * r));
+        const float d = dkq.x, kk = dkq.y, qq = dkq.z;
+        kq = fmaf(kk, qq, kq);
+        const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float s0 = bf16_lo(w[j]) * d, s1 = bf16_hi(w[j]) * d;
+            pk[2 * j] = fmaf(s0, kk, pk[2 * j]);
+            pq[2 * j] = fmaf(s0, qq, pq[2 * j]);
+            pk[2 * j + 1] = fmaf(s1, kk, pk[2 * j + 1]);
+            pq[2 * j + 1] = fmaf(s1, qq, pq[2 * j + 1]);
+        }
+    }
+    // Full sums over D_k: the row groups of this wave are LPW lanes apart.
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        pk[c] = colsum<LPW>(pk[c]);
+        pq[c] = colsum<LPW>(pq[c]);
+    }
+    kq = colsum<LPW>(kq);
+    const f32x4 *vv = reinterpret_cast<const f32x4 *>(ob + 4 * DK + cg * 8);
+    const f32x4 v0 = vv[0], v1 = vv[1];
+    const float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float bt = ob[4 * DK + TVW];
+    // Step 3 (delta update) and step 4 (output with the updated state).
+    float u[8], o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        u[c] = bt * (V[c] - pk[c]);
+        o[c] = fmaf(kq, u[c], pq[c]);
+    }
+    {
+        const size_t bh = (size_t)m.b * a.Hv + m.h;
+        const auto rout = make_rsrc(a.out + bh * a.Dv, (uint32_t)(a.Dv * 2));
+        u32x4 ov;
+        ov.x = pack_bf16x2(o[0], o[1]);
+        ov.y = pack_bf16x2(o[2], o[3]);
+        ov.z = pack_bf16x2(o[4], o[5]);
+        ov.w = pack_bf16x2(o[6], o[7]);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            ov, rout, rg == 0 ? (uint32_t)((m.tile * TVW + cg * 8) * 2) : 0x7FFFFFF0u, 0, 0);
+    }
+    // The update widens the packed tile again (decay and k re-read from LDS) instead of
+    // keeping the reduction's widened values alive; the empty asm marks the packed
+    // registers as redefined so the compiler cannot reuse those values.
+#pragma unroll
+    for (int r = 0; r < RW; ++r) asm volatile("" : "+v"(W[r]));
+    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TVW>(a, m) : 0),
+                               tile_range<DK, TVW>(a, m));
+    if (m.n == 0) {  // nothing accepted: commit the incoming bytes
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                W[r], rso, (uint32_t)(((rg + RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_STORE_POLICY);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const f32x4 dkq = *reinterpret_cast<const f32x4 *>(ob + 4 * (rg + RG * r));
+            const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
+            uint32_t nw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                nw[j] = pack_bf16x2(fmaf(dkq.y, u[2 * j], bf16_lo(w[j]) * dkq.x),
+                                    fmaf(dkq.y, u[2 * j + 1], bf16_hi(w[j]) * dkq.x));
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{nw[0], nw[1], nw[2], nw[3]}, rso,
+                (uint32_t)(((rg + RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_STORE_POLICY);
+        }
+    }
+    wave_load_state<DK, TVW>(a, resolve(a, x, it + NBUF * G), W, cg, rg);
+    it += G;
+    return true;
+}
+
+template <int DK, int TVW, int NBUF, int P, int U>
+__device__ __forceinline__ bool wave_phases(const DecodeArgs &a, const Index &x,
+                                            WavePipe<DK, TVW, NBUF> &pl, float *lds, int &it,
+                                            int lane) {
+    if constexpr (P == U) {
+        return true;
+    } else {
+        return wave_process<DK, TVW, NBUF, P>(a, x, pl, lds, it, lane) &&
+               wave_phases<DK, TVW, NBUF, P + 1, U>(a, x, pl, lds, it, lane);
+    }
+}
+
+template <int DK, int TVW, int NBUF>
+__global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
+    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nacc) {
+    using Sh = WaveShape<DK, TVW>;
+    const Index x{lens, idx, nacc};
+    __shared__ f32x4 lds4[2 * Sh::OPS / 4];
+    float *lds = reinterpret_cast<float *>(lds4);
+    const int lane = threadIdx.x;
+    const int cg = lane % Sh::LPW, rg = lane / Sh::LPW;
+    const int G = gridDim.x;
+    int it = blockIdx.x;
+    WavePipe<DK, TVW, NBUF> pl;
+    wave_load_state<DK, TVW>(a, resolve(a, x, it), pl.raw[0], cg, rg);
+    wave_load_ops<DK, TVW>(a, resolve(a, x, it), pl.ops[0], lane);
+#pragma unroll
+    for (int j = 1; j < NBUF; ++j)
+        wave_load_state<DK, TVW>(a, resolve(a, x, it + j * G), pl.raw[j], cg, rg);
+    constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
+    while (wave_phases<DK, TVW, NBUF, 0, U>(a, x, pl, lds, it, lane)) {
     }
 }
 
 // Workgroups that fit on the device at once (CUs x resident per CU), per device, queried once.
-template <int DK, int TV, int NT, int NBUF, bool ONE_TOKEN>
+template <int DK, int TV, int NT, int NBUF>
 static int resident_grid() {
     static int cached[64] = {0};
     int dev = 0;
@@ -622,35 +773,51 @@ static int resident_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, decode_kernel<DK, TV, NT, NBUF, ONE_TOKEN>, NT, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<DK, TV, NT, NBUF>,
+                                                     NT, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     cached[dev] = cus * per_cu;
     return cached[dev];
 }
 
-template <int DK, int TV, bool ONE_TOKEN>
-static hipError_t launch_decode_t(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
-                                  const int32_t *nacc, hipStream_t stream) {
-    constexpr int NT = RGDR_DECODE_THREADS;
-    // Ring length: the general form refills a slot as soon as it is widened, the single-token
-    // form only after its commit, so it needs one more slot for the same depth.
-    constexpr int NBUF = RGDR_DECODE_DEPTH + (ONE_TOKEN ? 1 : 0);
-    static_assert(RGDR_DECODE_DEPTH >= 1 && RGDR_DECODE_DEPTH <= 3, "state tiles in flight: 1-3");
-    const int resident = resident_grid<DK, TV, NT, NBUF, ONE_TOKEN>();
-    if (resident <= 0) return hipErrorInvalidDevice;
-    const int grid = a.n_items < resident ? a.n_items : resident;
-    hipLaunchKernelGGL((decode_kernel<DK, TV, NT, NBUF, ONE_TOKEN>), dim3(grid), dim3(NT), 0,
-                       stream, a, lens, idx, nacc);
-    return hipGetLastError();
-}
-
 template <int DK, int TV>
 static hipError_t launch_decode(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                 const int32_t *nacc, hipStream_t stream) {
-    return a.T == 1 ? launch_decode_t<DK, TV, true>(a, lens, idx, nacc, stream)
-                    : launch_decode_t<DK, TV, false>(a, lens, idx, nacc, stream);
+    constexpr int NT = RGDR_DECODE_THREADS;
+    constexpr int NBUF = RGDR_DECODE_DEPTH;
+    static_assert(NBUF >= 1 && NBUF <= 3, "state tiles in flight: 1-3");
+    const int resident = resident_grid<DK, TV, NT, NBUF>();
+    if (resident <= 0) return hipErrorInvalidDevice;
+    const int grid = a.n_items < resident ? a.n_items : resident;
+    hipLaunchKernelGGL((decode_kernel<DK, TV, NT, NBUF>), dim3(grid), dim3(NT), 0, stream, a,
+                       lens, idx, nacc);
+    return hipGetLastError();
+}
+
+template <int DK, int TVW>
+static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
+                              const int32_t *nacc, hipStream_t stream) {
+    constexpr int NBUF = TVW == 128 ? RGDR_WAVE_NBUF_128 : RGDR_WAVE_NBUF;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cached[dev] <= 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return hipErrorInvalidDevice;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, decode_wave_kernel<DK, TVW, NBUF>, 64, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        if (RGDR_WAVE_PER_CU > 0 && RGDR_WAVE_PER_CU < per_cu) per_cu = RGDR_WAVE_PER_CU;
+        cached[dev] = cus * per_cu;
+    }
+    const int grid = (RGDR_WAVE_ONE_SHOT || a.n_items < cached[dev]) ? a.n_items : cached[dev];
+    hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, NBUF>), dim3(grid), dim3(64), 0, stream, a,
+                       lens, idx, nacc);
+    return hipGetLastError();
 }
 
 }  // namespace rgdr
@@ -679,7 +846,9 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
         !aligned(num_accepted_tokens, 4))
         return RGDR_ERR_ALIGN;
 
-    const int tile_v = (D_v % 128 == 0 && RGDR_DECODE_TILE_V != 64) ? 128 : 64;
+    const bool wave_form = T == 1;
+    const int tile_v = wave_form ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
+                                 : ((D_v % 128 != 0 || RGDR_DECODE_TILE_V == 64) ? 64 : 128);
     const long long items = (long long)B * H_v * (D_v / tile_v);
     if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
 
@@ -705,7 +874,15 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
 
     const int32_t *L = actual_seq_lengths, *I = ssm_state_indices, *N = num_accepted_tokens;
     hipError_t err;
-    if (D_k == 128)
+    if (wave_form) {
+        if (tile_v == 128)
+            err = D_k == 128 ? launch_wave<128, 128>(a, L, I, N, stream)
+                             : launch_wave<64, 128>(a, L, I, N, stream);
+        else
+            err = D_k == 128 ? launch_wave<128, 64>(a, L, I, N, stream)
+                             : launch_wave<64, 64>(a, L, I, N, stream);
+    }
+    else if (D_k == 128)
         err = tile_v == 128 ? launch_decode<128, 128>(a, L, I, N, stream)
                             : launch_decode<128, 64>(a, L, I, N, stream);
     else
