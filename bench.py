@@ -4,11 +4,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--rotate R]
                     [--cpu-seconds S] [--no-cpu-baseline]
 
-One step is the whole path over one batch: the gate front end (la_gate: g = decay, beta)
-followed by the decode step (rgdr_decode, in place on the state pool), both in the HIP
-library through its C ABI. The default workload is the batched GQA decode shape
-(B=64, H_q=16, H_v=32, T=1, D_k=D_v=128, a 256-slot pool, 64 slots in use), with gate
-inputs that reproduce its g/beta recipe.
+One step is the whole path over one batch: the gate front end (g = decay_scale *
+softplus(a + dt_bias), beta = sigmoid(b)) and the decode step, in place on the state pool,
+in the HIP library through its C ABI. By default the step is one launch of
+rgdr_decode_gated (the gate computed in the decode kernel's prologue); the two-launch chain
+la_gate -> rgdr_decode is timed as well and reported as `unfused_ms_per_step`. The default
+workload is the batched GQA decode shape (B=64, H_q=16, H_v=32, T=1, D_k=D_v=128, a
+256-slot pool, 64 slots in use), with gate inputs that reproduce its g/beta recipe.
 
 Measurement:
   * R independent buffer sets (pool and every per-step input/output) are rotated so that
@@ -60,6 +62,12 @@ def decode_bytes(inp):
 def gate_bytes(inp):
     n = inp.B * inp.T * inp.Hv
     return n * (4 + 4 + 4 + 2) + 2 * 4 * inp.Hv  # a, b in; decay fp32, beta bf16 out; 2 [H]
+
+
+def fused_bytes(inp, decode_b, tok_heads):
+    """The fused step reads the raw gate projections a, b (fp32) instead of g (fp32) and
+    beta (bf16) for each valid token-head, and the two per-head vectors once."""
+    return decode_b + tok_heads * (4 + 4 - 4 - 2) + 2 * 4 * inp.Hv
 
 
 KERNEL_SOURCES = ("gated_delta_rule_rgdr_amd/csrc/rgdr_decode.hip",
@@ -120,13 +128,13 @@ def main():
     B, Hq, Hv, T, Dk, Dv, N = inp.B, inp.Hq, inp.Hv, inp.T, inp.Dk, inp.Dv, inp.N_slots
     dbytes, tok_heads = decode_bytes(inp)
     gbytes = gate_bytes(inp)
-    step_bytes = dbytes + gbytes
+    step_bytes = fused_bytes(inp, dbytes, tok_heads)
     touched = int(((inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < N)).sum()) \
         * Hv * Dk * Dv * 2
     R = args.rotate or max(2, math.ceil((1 << 30) / max(touched, 1)))
     R = min(R, args.steps) if args.steps > 0 else R
-    log(f"workload {wid}: {workloads.WORKLOAD_NAMES[wid]}; decode bytes/call {dbytes}, "
-        f"gate bytes/call {gbytes}; rotation sets {R}")
+    log(f"workload {wid}: {workloads.WORKLOAD_NAMES[wid]}; fused step bytes {step_bytes}, "
+        f"unfused decode {dbytes} + gate {gbytes}; rotation sets {R}")
 
     def bits(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -165,7 +173,14 @@ def main():
         rg.rgdr_decode(s["q"], s["k"], s["v"], be, s["pool"], lens, idx, g_, s["gk"], nacc,
                        inp.scale, out=s["out"])
 
+    def fused(s):
+        rg.rgdr_decode_gated(s["q"], s["k"], s["v"], s["a"], s["b"], dt, ds, s["pool"], lens, idx,
+                             s["gk"], nacc, inp.scale, out=s["out"])
+
     def step(i):
+        fused(sets[i % R])
+
+    def unfused_step(i):
         s = sets[i % R]
         gate(s)
         decode(s)
@@ -187,6 +202,7 @@ def main():
     if args.eager_only:
         for i in range(args.steps):
             step(args.warmup + i)
+            unfused_step(args.warmup + i)
         torch.cuda.synchronize()
         log(f"eager pass: {args.steps} steps done")
         if args.copy_calibration:
@@ -195,26 +211,33 @@ def main():
 
     # K timed steps in one graph.
     K = args.steps
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(K):
-                step(args.warmup + i)
-    stream.wait_stream(cap)
-    graph.replay()  # upload (untimed)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    graph.replay()
-    e1.record(stream)
-    e1.synchronize()
-    total_ms = e0.elapsed_time(e1)
+
+    def graph_ms(body, first):
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(K):
+                    body(first + i)
+        stream.wait_stream(cap)
+        graph.replay()  # upload (untimed)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    total_ms = graph_ms(step, args.warmup)
     ms_per_step = total_ms / K
     log(f"timed: {K} steps in {total_ms:.3f} ms ({ms_per_step * 1e3:.2f} us/step)")
+    for i in range(args.warmup):
+        unfused_step(i)
+    unfused_ms = graph_ms(unfused_step, args.warmup) / K
+    log(f"unfused chain (la_gate + rgdr_decode): {unfused_ms * 1e3:.2f} us/step")
 
     # Kernel durations: K back-to-back launches of one kernel, captured in a graph, timed
     # with events on the launch stream around one replay (no per-launch event overhead;
@@ -238,14 +261,16 @@ def main():
         a1.synchronize()
         return a0.elapsed_time(a1) * 1e3 / K
 
+    fused_us = kernel_avg_us(fused)
     dec_us = kernel_avg_us(decode)
     gate_us = kernel_avg_us(gate)
-    log(f"decode kernel: {dec_us:.2f} us per launch; gate kernel {gate_us:.2f} us per launch")
+    log(f"fused decode kernel: {fused_us:.2f} us per launch; unfused: decode {dec_us:.2f} us, "
+        f"gate {gate_us:.2f} us")
 
     if args.copy_calibration:
         copy_calibration()
 
-    kernel_gbs = dbytes / (dec_us * 1e-6) / 1e9
+    kernel_gbs = step_bytes / (fused_us * 1e-6) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     steps_per_s = tok_heads / (ms_per_step * 1e-3)
 
@@ -257,8 +282,8 @@ def main():
         reps = 0
         while True:
             d64, b64 = oracle.la_gate(inp.gate_a, inp.dt_bias, inp.decay_scale, inp.gate_b)
-            g32 = d64.astype(np.float32).reshape(B, T, Hv).transpose(0, 2, 1)
-            beta_bits = oracle.f64_to_bf16(b64).reshape(B, T, Hv).transpose(0, 2, 1)
+            g32 = np.ascontiguousarray(d64.astype(np.float32).transpose(0, 2, 1))
+            beta_bits = np.ascontiguousarray(oracle.f64_to_bf16(b64).transpose(0, 2, 1))
             oracle.rgdr_bf16(inp.query, inp.key, inp.value, beta_bits, inp.state,
                              inp.actual_seq_lengths, inp.ssm_state_indices, g32, inp.gk,
                              inp.num_accepted_tokens, inp.scale)
@@ -288,17 +313,18 @@ def main():
         "storage_dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workloads.WORKLOAD_NAMES[wid] + " (gate + decode step)",
+                   "step": "rgdr_decode_gated (gate fused into the decode kernel)",
                    "B": B, "H_q": Hq, "H_v": Hv, "T": T, "D_k": Dk, "D_v": Dv,
                    "N_slots": N, "rotation_sets": R, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "token_head_steps_per_s": round(steps_per_s, 1),
         "step_bytes": step_bytes,
-        "roofline": {"kernel": "rgdr_decode", "bound": "hbm", "achieved": round(kernel_gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"kernel": "rgdr_decode_gated", "bound": "hbm",
+                     "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": dbytes,
-                     "avg_launch_us": round(dec_us, 3)},
-        "gate_avg_launch_us": round(gate_us, 3),
+                     "bytes_per_launch": step_bytes, "avg_launch_us": round(fused_us, 3)},
+        "unfused_ms_per_step": round(unfused_ms, 6),
+        "unfused_kernels_avg_us": {"la_gate": round(gate_us, 3), "rgdr_decode": round(dec_us, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -8,6 +8,8 @@ fallback: if the library is missing, importing the binding's functions raises.
   "lite_boost.ops.recurrent_gated_delta_rule"), in place on a bf16 state pool.
 * ``recurrent_gated_delta_rule`` -- the page's functional form: returns ``(out, state_out)``
   and leaves ``state`` untouched.
+* ``rgdr_decode_gated`` -- the decode step with the gate front end fused in: takes the raw
+  gate projections instead of g and beta.
 * ``la_gate`` -- the gate front end (README "com.microsoft.LinearAttentionGate").
 * ``rgdr_validate`` -- synchronous check of the index arrays.
 
@@ -18,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["rgdr_decode", "recurrent_gated_delta_rule", "la_gate", "rgdr_validate",
+__all__ = ["rgdr_decode", "rgdr_decode_gated", "recurrent_gated_delta_rule", "la_gate",
+           "rgdr_validate",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
            "RGDR_F16", "RGDR_BF16"]
 
@@ -43,6 +46,8 @@ def library():
     vp, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
     lib.rgdr_decode.restype = C.c_int
     lib.rgdr_decode.argtypes = [vp] * 10 + [f32] + [i32] * 7 + [vp, vp, vp]
+    lib.rgdr_decode_gated.restype = C.c_int
+    lib.rgdr_decode_gated.argtypes = [vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7 + [vp] * 3
     lib.la_gate.restype = C.c_int
     lib.la_gate.argtypes = [vp, vp, vp, vp, C.c_int, i64, i32, vp, C.c_int, vp, C.c_int, vp]
     lib.rgdr_validate.restype = C.c_int
@@ -133,6 +138,65 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
                          num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T, Dk, Dv, N,
                          out.data_ptr(), state_out.data_ptr(), _stream_handle(stream))
     _check(rc, "rgdr_decode")
+    return out, state_out
+
+
+def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
+                      actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens, scale=1.0,
+                      *, out=None, state_out=None, stream=None):
+    """One decode step with the gate fused in; returns ``(out, state_out)``.
+
+    ``a``, ``b``: raw gate projections ``[B, T, H_v]`` (float32 or float16, head axis last);
+    ``dt_bias``, ``decay_scale``: float32 ``[H_v]``. ``g = decay_scale * softplus(a + dt_bias)``
+    and ``beta = sigmoid(b)`` are computed in the kernel in fp32. Other arguments as
+    ``rgdr_decode`` (which takes g and beta instead).
+    """
+    lib = library()
+    _dev(query, "query", torch.bfloat16, 4)
+    B, Hq, T, Dk = query.shape
+    _dev(key, "key", torch.bfloat16, 4)
+    _dev(value, "value", torch.bfloat16, 4)
+    _dev(state_pool, "state_pool", torch.bfloat16, 4)
+    _dev(gk, "gk", torch.float32, 4)
+    if a.dtype not in (torch.float32, torch.float16):
+        raise RuntimeError("gate projections must be float32 or float16")
+    _dev(a, "a", a.dtype, 3)
+    _dev(b, "b", a.dtype, 3)
+    _dev(dt_bias, "dt_bias", torch.float32, 1)
+    _dev(decay_scale, "decay_scale", torch.float32, 1)
+    for nm, t in (("actual_seq_lengths", actual_seq_lengths),
+                  ("ssm_state_indices", ssm_state_indices),
+                  ("num_accepted_tokens", num_accepted_tokens)):
+        _dev(t, nm, torch.int32, 1)
+        if t.shape[0] != B:
+            raise RuntimeError(f"{nm} must have shape [{B}]")
+    Hv, Dv = value.shape[1], value.shape[3]
+    N = state_pool.shape[0]
+    if tuple(key.shape) != (B, Hq, T, Dk) or tuple(value.shape) != (B, Hv, T, Dv) \
+            or tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv) \
+            or tuple(gk.shape) != (B, Hv, T, Dk) or tuple(state_pool.shape) != (N, Hv, Dk, Dv) \
+            or dt_bias.shape[0] != Hv or decay_scale.shape[0] != Hv:
+        raise RuntimeError("rgdr_decode_gated: inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=query.device)
+    else:
+        _dev(out, "out", torch.bfloat16, 4)
+        if tuple(out.shape) != (B, Hv, T, Dv):
+            raise RuntimeError("out must be [B, H_v, T, D_v]")
+    if state_out is None:
+        state_out = state_pool
+    else:
+        _dev(state_out, "state_out", torch.bfloat16, 4)
+        if state_out.shape != state_pool.shape:
+            raise RuntimeError("state_out must have the pool's shape")
+    rc = lib.rgdr_decode_gated(query.data_ptr(), key.data_ptr(), value.data_ptr(), a.data_ptr(),
+                               b.data_ptr(), dt_bias.data_ptr(), decay_scale.data_ptr(),
+                               _DTYPE_CODE[a.dtype], state_pool.data_ptr(),
+                               actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
+                               gk.data_ptr(), num_accepted_tokens.data_ptr(), float(scale), B, Hq,
+                               Hv, T, Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
+                               _stream_handle(stream))
+    _check(rc, "rgdr_decode_gated")
     return out, state_out
 
 

@@ -41,12 +41,8 @@ __global__ __launch_bounds__(256) void la_gate_kernel(const GateArgs g) {
     for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < g.n; e += stride) {
         const int h = (int)(e % g.H);
         const float x = load_in<TIn>(g.a, e) + g.dt_bias[h];
-        const float sp = x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
-        store_out(g.decay, g.decay_dtype, e, g.decay_scale[h] * sp);
-        if (g.beta) {
-            const float y = load_in<TIn>(g.b, e);
-            store_out(g.beta, g.beta_dtype, e, 1.0f / (1.0f + expf(-y)));
-        }
+        store_out(g.decay, g.decay_dtype, e, g.decay_scale[h] * softplus_f32(x));
+        if (g.beta) store_out(g.beta, g.beta_dtype, e, sigmoid_f32(load_in<TIn>(g.b, e)));
     }
 }
 

@@ -24,6 +24,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// Gate arithmetic ("com.microsoft.LinearAttentionGate" README, Description), fp32:
+// softplus(x) = ln(1 + e^x) in the overflow-safe form, sigmoid(x) = 1 / (1 + e^-x).
+__device__ __forceinline__ float softplus_f32(float x) {
+    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+}
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// A gate input element held as raw bits: fp32 (the bits themselves) or fp16 (low 16 bits).
+template <bool F16>
+__device__ __forceinline__ float gate_value(uint32_t bits) {
+    if constexpr (F16)
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+    else
+        return __uint_as_float(bits);
+}
+
 __host__ __device__ __forceinline__ bool aligned(const void *p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }

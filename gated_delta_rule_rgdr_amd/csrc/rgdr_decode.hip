@@ -104,10 +104,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 struct DecodeArgs {
     const uint16_t *q, *k, *v, *beta, *pool;
     const float *g, *gk;
+    // Fused gate front end: raw projections [B, T, H_v] (fp32 or fp16) and per-head fp32
+    // vectors; g and beta are then computed in the kernel instead of read.
+    const void *ga, *gb;
+    const float *dt_bias, *dscale;
     uint16_t *out, *pool_out;
     float scale;
     int Hq, Hv, T, Dv, N_slots, ntiles, group, n_items;
 };
+
+// How an item's g and beta arrive: given (bf16 beta, fp32 g), or computed from raw gate
+// projections in fp32 or fp16.
+enum GateMode { kGateGiven = 0, kGateF32 = 1, kGateF16 = 2 };
+
+// Element offset of gate entry (b, t, h) in a [B, T, H_v] gate tensor, and the raw load of
+// it (lanes whose token is absent aim past the range: zero, no data moved).
+__device__ __forceinline__ uint32_t gate_raw(const DecodeArgs &a, const void *base, int gate,
+                                             int b, int t, int h, bool present) {
+    const uint32_t esz = gate == kGateF16 ? 2u : 4u;
+    const auto rs = make_rsrc(static_cast<const char *>(base) + (size_t)b * a.T * a.Hv * esz,
+                              (uint32_t)(a.T * a.Hv) * esz);
+    const uint32_t off = present ? (uint32_t)(t * a.Hv + h) * esz : 0x7FFFFFF0u;
+    return gate == kGateF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0)
+                            : __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+}
+
+// Per-head gate vectors of value head h (every lane loads the same two words).
+__device__ __forceinline__ void gate_head(const DecodeArgs &a, int h, float &dt, float &ds) {
+    const auto rd = make_rsrc(a.dt_bias, (uint32_t)a.Hv * 4);
+    const auto rc = make_rsrc(a.dscale, (uint32_t)a.Hv * 4);
+    dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, h * 4, 0, 0));
+    ds = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, h * 4, 0, 0));
+}
 
 template <int DK, int TV, int NT, int TMAX = kMaxT>
 struct TileShape {
@@ -168,14 +196,15 @@ template <int DK, int TV, int NT, int TMAX>
 struct Ops {
     using Sh = TileShape<DK, TV, NT, TMAX>;
     f32x4 gk[Sh::GKV];
-    float g[Sh::GKV];
+    uint32_t g[Sh::GKV];  // g, or the raw gate projection a, of this vector's token
     u32x4 k[Sh::KQV], q[Sh::KQV], v[Sh::VV];
-    uint32_t beta;
+    uint32_t beta;        // beta (bf16), or the raw projection b, of token tid
+    float dt, ds;         // per-head gate vectors (fused gate only)
 };
 
 // Issue the loads of one item's operands. Ranges cover only the L valid tokens, so padded
 // tokens are never read (lanes past the range receive zeros and move no data).
-template <int DK, int TV, int NT, int TMAX>
+template <int DK, int TV, int NT, int TMAX, int GATE>
 __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
                                          Ops<DK, TV, NT, TMAX> &o, int tid) {
     using Sh = TileShape<DK, TV, NT, TMAX>;
@@ -192,7 +221,10 @@ __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
     for (int j = 0; j < Sh::GKV; ++j) {
         const int e = tid + j * NT;  // float4 index in the [L, DK] block
         o.gk[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rgk, e * 16, 0, 0));
-        o.g[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (e * 4 / DK) * 4, 0, 0));
+        if constexpr (GATE == kGateGiven)
+            o.g[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, (e * 4 / DK) * 4, 0, 0);
+        else
+            o.g[j] = gate_raw(a, a.ga, GATE, m.b, e * 4 / DK, m.h, e * 4 / DK < m.L);
     }
 #pragma unroll
     for (int j = 0; j < Sh::KQV; ++j) {
@@ -207,11 +239,17 @@ __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
         o.v[j] = __builtin_amdgcn_raw_buffer_load_b128(
             rv, (uint32_t)((t * a.Dv + m.tile * TV + c8 * 8) * 2), 0, 0);
     }
-    o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, tid * 2, 0, 0);
+    if constexpr (GATE == kGateGiven) {
+        o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, tid * 2, 0, 0);
+    } else {
+        o.beta = gate_raw(a, a.gb, GATE, m.b, tid, m.h, tid < m.L);
+        gate_head(a, m.h, o.dt, o.ds);
+    }
 }
 
-// Write one item's operands into an LDS operand buffer (decay factors formed here).
-template <int DK, int TV, int NT, int TMAX>
+// Write one item's operands into an LDS operand buffer (decay factors formed here; with the
+// fused gate, g and beta are computed here too).
+template <int DK, int TV, int NT, int TMAX, int GATE>
 __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float *ob,
                                           float scale, int tid) {
     using Sh = TileShape<DK, TV, NT, TMAX>;
@@ -220,7 +258,12 @@ __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float 
         const int e = tid + j * NT;
         const int t = e * 4 / DK, i0 = e * 4 % DK;
         if (t < TMAX) {
-            const float eg = __expf(o.g[j]);
+            float g;
+            if constexpr (GATE == kGateGiven)
+                g = __uint_as_float(o.g[j]);
+            else
+                g = o.ds * softplus_f32(gate_value<GATE == kGateF16>(o.g[j]) + o.dt);
+            const float eg = __expf(g);
             float *row = ob + t * Sh::TOK + 4 * i0;
             row[0] = eg * __expf(o.gk[j].x);
             row[4] = eg * __expf(o.gk[j].y);
@@ -255,7 +298,14 @@ __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float 
             dst[1] = f32x4{bf16_lo(o.v[j].z), bf16_hi(o.v[j].z), bf16_lo(o.v[j].w), bf16_hi(o.v[j].w)};
         }
     }
-    if (tid < TMAX) ob[tid * Sh::TOK + 4 * DK + TV] = bf16_to_f32((uint16_t)o.beta);
+    if (tid < TMAX) {
+        float bt;
+        if constexpr (GATE == kGateGiven)
+            bt = bf16_to_f32((uint16_t)o.beta);
+        else
+            bt = sigmoid_f32(gate_value<GATE == kGateF16>(o.beta));
+        ob[tid * Sh::TOK + 4 * DK + TV] = bt;
+    }
 }
 
 // Element offset of one item's state tile in the pool.
@@ -425,7 +475,7 @@ __device__ __forceinline__ void store_out_row(const DecodeArgs &a, const OutRows
 
 // General form (T > 1): the tile is widened to fp32 registers once and kept there across
 // the tokens. Loop phase P. Returns false when the workgroup has no item left.
-template <int DK, int TV, int NT, int NBUF, int P>
+template <int DK, int TV, int NT, int NBUF, int GATE, int P>
 __device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &x,
                                               Pipeline<DK, TV, NT, NBUF, kMaxT> &pl, float *lds,
                                               int &it, int &xc, int tid) {
@@ -437,9 +487,9 @@ __device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &
     const Item m = resolve(a, x, it);
 
     // Operands of the next item go in flight; this item's are staged in LDS.
-    load_ops<DK, TV, NT, kMaxT>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
+    load_ops<DK, TV, NT, kMaxT, GATE>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
     float *ob = lds + (P & 1) * Sh::OPS;
-    stage_ops<DK, TV, NT, kMaxT>(pl.ops[P & 1], ob, a.scale, tid);
+    stage_ops<DK, TV, NT, kMaxT, GATE>(pl.ops[P & 1], ob, a.scale, tid);
     __syncthreads();
 
     float S[R][CPL];
@@ -487,19 +537,19 @@ __device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &
 }
 
 // Phases P .. U-1 of the unrolled item loop; false once the workgroup has no item left.
-template <int DK, int TV, int NT, int NBUF, int P, int U>
+template <int DK, int TV, int NT, int NBUF, int GATE, int P, int U>
 __device__ __forceinline__ bool run_phases(const DecodeArgs &a, const Index &x,
                                            Pipeline<DK, TV, NT, NBUF, kMaxT> &pl, float *lds,
                                            int &it, int &xc, int tid) {
     if constexpr (P == U) {
         return true;
     } else {
-        return process_multi<DK, TV, NT, NBUF, P>(a, x, pl, lds, it, xc, tid) &&
-               run_phases<DK, TV, NT, NBUF, P + 1, U>(a, x, pl, lds, it, xc, tid);
+        return process_multi<DK, TV, NT, NBUF, GATE, P>(a, x, pl, lds, it, xc, tid) &&
+               run_phases<DK, TV, NT, NBUF, GATE, P + 1, U>(a, x, pl, lds, it, xc, tid);
     }
 }
 
-template <int DK, int TV, int NT, int NBUF>
+template <int DK, int TV, int NT, int NBUF, int GATE>
 __global__ __launch_bounds__(NT, RGDR_DECODE_MIN_WAVES) void decode_kernel(const DecodeArgs a,
                                                        const int32_t *__restrict__ lens,
                                                        const int32_t *__restrict__ idx,
@@ -518,14 +568,14 @@ __global__ __launch_bounds__(NT, RGDR_DECODE_MIN_WAVES) void decode_kernel(const
     // Prologue: state of the first item, operands of the first item, state of the next
     // NBUF-1 items.
     load_state<DK, TV, NT>(a, resolve(a, x, it), pl.raw[0], rg, cg);
-    load_ops<DK, TV, NT, TMAX>(a, resolve(a, x, it), pl.ops[0], tid);
+    load_ops<DK, TV, NT, TMAX, GATE>(a, resolve(a, x, it), pl.ops[0], tid);
 #pragma unroll
     for (int j = 1; j < NBUF; ++j)
         load_state<DK, TV, NT>(a, resolve(a, x, it + j * G), pl.raw[j], rg, cg);
     // Item loop, unrolled over the ring and the two operand buffers, so that every buffer
     // index is a compile-time constant.
     constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
-    while (run_phases<DK, TV, NT, NBUF, 0, U>(a, x, pl, lds, it, xc, tid)) {
+    while (run_phases<DK, TV, NT, NBUF, GATE, 0, U>(a, x, pl, lds, it, xc, tid)) {
     }
 }
 
@@ -554,13 +604,15 @@ struct WaveShape {
 template <int DK>
 struct WaveOps {
     float gk[DK / 64];
-    float g;
+    uint32_t g;     // g, or the raw gate projection a
     uint32_t k, q;  // DK/64 bf16 values each (low half first)
     uint32_t v;     // TVW/64 bf16 values of the v tile (low half first)
-    uint32_t beta;
+    uint32_t beta;  // beta (bf16), or the raw projection b
+    float dt, ds;   // per-head gate vectors (fused gate only)
+    bool present;   // the item has its token (L = 1)
 };
 
-template <int DK, int TVW>
+template <int DK, int TVW, int GATE>
 __device__ __forceinline__ void wave_load_ops(const DecodeArgs &a, const Item &m, WaveOps<DK> &o,
                                               int lane) {
     using Sh = WaveShape<DK, TVW>;
@@ -588,15 +640,31 @@ __device__ __forceinline__ void wave_load_ops(const DecodeArgs &a, const Item &m
         o.v = __builtin_amdgcn_raw_buffer_load_b32(rv, (uint32_t)((m.tile * TVW + lane * 2) * 2), 0, RGDR_OPS_LOAD_POLICY);
     else
         o.v = __builtin_amdgcn_raw_buffer_load_b16(rv, (uint32_t)((m.tile * TVW + lane) * 2), 0, RGDR_OPS_LOAD_POLICY);
-    o.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 0, 0, RGDR_OPS_LOAD_POLICY));
-    o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, 0, 0, RGDR_OPS_LOAD_POLICY);
+    if constexpr (GATE == kGateGiven) {
+        o.g = __builtin_amdgcn_raw_buffer_load_b32(rs, 0, 0, RGDR_OPS_LOAD_POLICY);
+        o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, 0, 0, RGDR_OPS_LOAD_POLICY);
+    } else {
+        o.g = gate_raw(a, a.ga, GATE, m.b, 0, m.h, m.L > 0);
+        o.beta = gate_raw(a, a.gb, GATE, m.b, 0, m.h, m.L > 0);
+        gate_head(a, m.h, o.dt, o.ds);
+    }
+    o.present = m.L > 0;
 }
 
-template <int DK, int TVW>
+template <int DK, int TVW, int GATE>
 __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, float scale,
                                                int lane) {
     using Sh = WaveShape<DK, TVW>;
-    const float eg = __expf(o.g);
+    float g, bt;
+    if constexpr (GATE == kGateGiven) {
+        g = __uint_as_float(o.g);
+        bt = bf16_to_f32((uint16_t)o.beta);
+    } else {
+        // An absent token keeps decay 1 (its other operands are all zero).
+        g = o.present ? o.ds * softplus_f32(gate_value<GATE == kGateF16>(o.g) + o.dt) : 0.f;
+        bt = sigmoid_f32(gate_value<GATE == kGateF16>(o.beta));
+    }
+    const float eg = __expf(g);
 #pragma unroll
     for (int j = 0; j < Sh::RPL; ++j) {
         const uint32_t kb = j ? o.k & 0xFFFF0000u : o.k << 16;
@@ -608,7 +676,7 @@ __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, 
         *reinterpret_cast<float2 *>(ob + 4 * DK + 2 * lane) = make_float2(bf16_lo(o.v), bf16_hi(o.v));
     else
         ob[4 * DK + lane] = bf16_lo(o.v);
-    if (lane == 0) ob[4 * DK + TVW] = bf16_to_f32((uint16_t)o.beta);
+    if (lane == 0) ob[4 * DK + TVW] = bt;
 }
 
 template <int DK, int TVW, int NBUF>
@@ -630,7 +698,7 @@ __device__ __forceinline__ void wave_load_state(const DecodeArgs &a, const Item 
             rs, (uint32_t)(((rg + Sh::RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_LOAD_POLICY);
 }
 
-template <int DK, int TVW, int NBUF, int P>
+template <int DK, int TVW, int NBUF, int GATE, int P>
 __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x,
                                              WavePipe<DK, TVW, NBUF> &pl, float *lds, int &it,
                                              int lane) {
@@ -641,9 +709,9 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
     const int cg = lane % LPW, rg = lane / LPW;
     const Item m = resolve(a, x, it);
 
-    wave_load_ops<DK, TVW>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], lane);
+    wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], lane);
     float *ob = lds + (P & 1) * Sh::OPS;
-    wave_stage_ops<DK, TVW>(pl.ops[P & 1], ob, a.scale, lane);
+    wave_stage_ops<DK, TVW, GATE>(pl.ops[P & 1], ob, a.scale, lane);
 
     u32x4(&W)[RW] = pl.raw[P % NBUF];
     // Step 1 (decay) fused with the partial sums of steps 2 and 4.
@@ -727,19 +795,19 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
     return true;
 }
 
-template <int DK, int TVW, int NBUF, int P, int U>
+template <int DK, int TVW, int NBUF, int GATE, int P, int U>
 __device__ __forceinline__ bool wave_phases(const DecodeArgs &a, const Index &x,
                                             WavePipe<DK, TVW, NBUF> &pl, float *lds, int &it,
                                             int lane) {
     if constexpr (P == U) {
         return true;
     } else {
-        return wave_process<DK, TVW, NBUF, P>(a, x, pl, lds, it, lane) &&
-               wave_phases<DK, TVW, NBUF, P + 1, U>(a, x, pl, lds, it, lane);
+        return wave_process<DK, TVW, NBUF, GATE, P>(a, x, pl, lds, it, lane) &&
+               wave_phases<DK, TVW, NBUF, GATE, P + 1, U>(a, x, pl, lds, it, lane);
     }
 }
 
-template <int DK, int TVW, int NBUF>
+template <int DK, int TVW, int NBUF, int GATE>
 __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
@@ -753,17 +821,17 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     int it = blockIdx.x;
     WavePipe<DK, TVW, NBUF> pl;
     wave_load_state<DK, TVW>(a, resolve(a, x, it), pl.raw[0], cg, rg);
-    wave_load_ops<DK, TVW>(a, resolve(a, x, it), pl.ops[0], lane);
+    wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it), pl.ops[0], lane);
 #pragma unroll
     for (int j = 1; j < NBUF; ++j)
         wave_load_state<DK, TVW>(a, resolve(a, x, it + j * G), pl.raw[j], cg, rg);
     constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
-    while (wave_phases<DK, TVW, NBUF, 0, U>(a, x, pl, lds, it, lane)) {
+    while (wave_phases<DK, TVW, NBUF, GATE, 0, U>(a, x, pl, lds, it, lane)) {
     }
 }
 
 // Workgroups that fit on the device at once (CUs x resident per CU), per device, queried once.
-template <int DK, int TV, int NT, int NBUF>
+template <int DK, int TV, int NT, int NBUF, int GATE>
 static int resident_grid() {
     static int cached[64] = {0};
     int dev = 0;
@@ -773,29 +841,29 @@ static int resident_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<DK, TV, NT, NBUF>,
-                                                     NT, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, decode_kernel<DK, TV, NT, NBUF, GATE>, NT, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     cached[dev] = cus * per_cu;
     return cached[dev];
 }
 
-template <int DK, int TV>
+template <int DK, int TV, int GATE>
 static hipError_t launch_decode(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                 const int32_t *nacc, hipStream_t stream) {
     constexpr int NT = RGDR_DECODE_THREADS;
     constexpr int NBUF = RGDR_DECODE_DEPTH;
     static_assert(NBUF >= 1 && NBUF <= 3, "state tiles in flight: 1-3");
-    const int resident = resident_grid<DK, TV, NT, NBUF>();
+    const int resident = resident_grid<DK, TV, NT, NBUF, GATE>();
     if (resident <= 0) return hipErrorInvalidDevice;
     const int grid = a.n_items < resident ? a.n_items : resident;
-    hipLaunchKernelGGL((decode_kernel<DK, TV, NT, NBUF>), dim3(grid), dim3(NT), 0, stream, a,
-                       lens, idx, nacc);
+    hipLaunchKernelGGL((decode_kernel<DK, TV, NT, NBUF, GATE>), dim3(grid), dim3(NT), 0, stream,
+                       a, lens, idx, nacc);
     return hipGetLastError();
 }
 
-template <int DK, int TVW>
+template <int DK, int TVW, int GATE>
 static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                               const int32_t *nacc, hipStream_t stream) {
     constexpr int NBUF = TVW == 128 ? RGDR_WAVE_NBUF_128 : RGDR_WAVE_NBUF;
@@ -808,16 +876,70 @@ static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const in
             cus <= 0)
             return hipErrorInvalidDevice;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, decode_wave_kernel<DK, TVW, NBUF>, 64, 0) != hipSuccess ||
+                &per_cu, decode_wave_kernel<DK, TVW, NBUF, GATE>, 64, 0) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         if (RGDR_WAVE_PER_CU > 0 && RGDR_WAVE_PER_CU < per_cu) per_cu = RGDR_WAVE_PER_CU;
         cached[dev] = cus * per_cu;
     }
     const int grid = (RGDR_WAVE_ONE_SHOT || a.n_items < cached[dev]) ? a.n_items : cached[dev];
-    hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, NBUF>), dim3(grid), dim3(64), 0, stream, a,
-                       lens, idx, nacc);
+    hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, NBUF, GATE>), dim3(grid), dim3(64), 0, stream,
+                       a, lens, idx, nacc);
     return hipGetLastError();
+}
+
+// Shape/alignment checks shared by both entry points, then the launch of the form T picks.
+template <int GATE>
+static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, bool wave_form,
+                           const int32_t *L, const int32_t *I, const int32_t *N,
+                           hipStream_t stream) {
+    if (wave_form) {
+        if (tile_v == 128)
+            return D_k == 128 ? launch_wave<128, 128, GATE>(a, L, I, N, stream)
+                              : launch_wave<64, 128, GATE>(a, L, I, N, stream);
+        return D_k == 128 ? launch_wave<128, 64, GATE>(a, L, I, N, stream)
+                          : launch_wave<64, 64, GATE>(a, L, I, N, stream);
+    }
+    if (D_k == 128)
+        return tile_v == 128 ? launch_decode<128, 128, GATE>(a, L, I, N, stream)
+                             : launch_decode<128, 64, GATE>(a, L, I, N, stream);
+    return tile_v == 128 ? launch_decode<64, 128, GATE>(a, L, I, N, stream)
+                         : launch_decode<64, 64, GATE>(a, L, I, N, stream);
+}
+
+static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
+                                int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
+                                const int32_t *lens, const int32_t *idx, const int32_t *nacc,
+                                hipStream_t stream) {
+    if (B < 0 || H_q <= 0 || H_v <= 0 || T <= 0 || D_k <= 0 || D_v <= 0 || N_slots <= 0)
+        return RGDR_ERR_SHAPE;
+    if (T > kMaxT || H_v % H_q != 0) return RGDR_ERR_SHAPE;
+    if ((D_k != 64 && D_k != 128) || D_v % 64 != 0 || D_v > 4096) return RGDR_ERR_UNSUPPORTED;
+    if (!aligned(a.v, 16) || !aligned(a.pool, 16) || !aligned(a.out, 16) ||
+        !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
+        !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
+        return RGDR_ERR_ALIGN;
+    const bool wave_form = T == 1;
+    const int tile_v = wave_form ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
+                                 : ((D_v % 128 != 0 || RGDR_DECODE_TILE_V == 64) ? 64 : 128);
+    const long long items = (long long)B * H_v * (D_v / tile_v);
+    if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
+    a.Hq = H_q;
+    a.Hv = H_v;
+    a.T = T;
+    a.Dv = D_v;
+    a.N_slots = N_slots;
+    a.ntiles = D_v / tile_v;
+    a.group = H_v / H_q;
+    a.n_items = (int)items;
+    hipError_t err;
+    if (gate == kGateGiven)
+        err = dispatch<kGateGiven>(a, D_k, tile_v, wave_form, lens, idx, nacc, stream);
+    else if (gate == kGateF32)
+        err = dispatch<kGateF32>(a, D_k, tile_v, wave_form, lens, idx, nacc, stream);
+    else
+        err = dispatch<kGateF16>(a, D_k, tile_v, wave_form, lens, idx, nacc, stream);
+    return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
 }
 
 }  // namespace rgdr
@@ -835,24 +957,8 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
     if (!query || !key || !value || !beta || !state_pool || !actual_seq_lengths ||
         !ssm_state_indices || !g || !gk || !num_accepted_tokens || !out || !state_out)
         return RGDR_ERR_NULL;
-    if (B < 0 || H_q <= 0 || H_v <= 0 || T <= 0 || D_k <= 0 || D_v <= 0 || N_slots <= 0)
-        return RGDR_ERR_SHAPE;
-    if (T > kMaxT || H_v % H_q != 0) return RGDR_ERR_SHAPE;
-    if ((D_k != 64 && D_k != 128) || D_v % 64 != 0 || D_v > 4096) return RGDR_ERR_UNSUPPORTED;
-    if (!aligned(value, 16) || !aligned(state_pool, 16) || !aligned(out, 16) ||
-        !aligned(state_out, 16) || !aligned(query, 16) || !aligned(key, 16) ||
-        !aligned(beta, 2) || !aligned(g, 4) || !aligned(gk, 16) ||
-        !aligned(actual_seq_lengths, 4) || !aligned(ssm_state_indices, 4) ||
-        !aligned(num_accepted_tokens, 4))
-        return RGDR_ERR_ALIGN;
-
-    const bool wave_form = T == 1;
-    const int tile_v = wave_form ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
-                                 : ((D_v % 128 != 0 || RGDR_DECODE_TILE_V == 64) ? 64 : 128);
-    const long long items = (long long)B * H_v * (D_v / tile_v);
-    if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
-
-    DecodeArgs a;
+    if (!aligned(beta, 2) || !aligned(g, 4)) return RGDR_ERR_ALIGN;
+    DecodeArgs a = {};
     a.q = static_cast<const uint16_t *>(query);
     a.k = static_cast<const uint16_t *>(key);
     a.v = static_cast<const uint16_t *>(value);
@@ -863,30 +969,45 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
     a.out = static_cast<uint16_t *>(out);
     a.pool_out = static_cast<uint16_t *>(state_out);
     a.scale = scale;
-    a.Hq = H_q;
-    a.Hv = H_v;
-    a.T = T;
-    a.Dv = D_v;
-    a.N_slots = N_slots;
-    a.ntiles = D_v / tile_v;
-    a.group = H_v / H_q;
-    a.n_items = (int)items;
+    return decode_entry(a, kGateGiven, B, H_q, H_v, T, D_k, D_v, N_slots, actual_seq_lengths,
+                        ssm_state_indices, num_accepted_tokens, stream);
+}
 
-    const int32_t *L = actual_seq_lengths, *I = ssm_state_indices, *N = num_accepted_tokens;
-    hipError_t err;
-    if (wave_form) {
-        if (tile_v == 128)
-            err = D_k == 128 ? launch_wave<128, 128>(a, L, I, N, stream)
-                             : launch_wave<64, 128>(a, L, I, N, stream);
-        else
-            err = D_k == 128 ? launch_wave<128, 64>(a, L, I, N, stream)
-                             : launch_wave<64, 64>(a, L, I, N, stream);
-    }
-    else if (D_k == 128)
-        err = tile_v == 128 ? launch_decode<128, 128>(a, L, I, N, stream)
-                            : launch_decode<128, 64>(a, L, I, N, stream);
-    else
-        err = tile_v == 128 ? launch_decode<64, 128>(a, L, I, N, stream)
-                            : launch_decode<64, 64>(a, L, I, N, stream);
-    return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
+extern "C" rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *value,
+                                         const void *gate_a, const void *gate_b,
+                                         const float *dt_bias, const float *decay_scale,
+                                         rgdr_dtype gate_dtype, const void *state_pool,
+                                         const int32_t *actual_seq_lengths,
+                                         const int32_t *ssm_state_indices, const float *gk,
+                                         const int32_t *num_accepted_tokens, float scale,
+                                         int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                         int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                                         void *state_out, hipStream_t stream) {
+    using namespace rgdr;
+    if (B == 0) return RGDR_OK;
+    if (!query || !key || !value || !gate_a || !gate_b || !dt_bias || !decay_scale ||
+        !state_pool || !actual_seq_lengths || !ssm_state_indices || !gk ||
+        !num_accepted_tokens || !out || !state_out)
+        return RGDR_ERR_NULL;
+    if (gate_dtype != RGDR_F32 && gate_dtype != RGDR_F16) return RGDR_ERR_DTYPE;
+    const uintptr_t esz = gate_dtype == RGDR_F16 ? 2 : 4;
+    if (!aligned(gate_a, esz) || !aligned(gate_b, esz) || !aligned(dt_bias, 4) ||
+        !aligned(decay_scale, 4))
+        return RGDR_ERR_ALIGN;
+    DecodeArgs a = {};
+    a.q = static_cast<const uint16_t *>(query);
+    a.k = static_cast<const uint16_t *>(key);
+    a.v = static_cast<const uint16_t *>(value);
+    a.pool = static_cast<const uint16_t *>(state_pool);
+    a.gk = gk;
+    a.ga = gate_a;
+    a.gb = gate_b;
+    a.dt_bias = dt_bias;
+    a.dscale = decay_scale;
+    a.out = static_cast<uint16_t *>(out);
+    a.pool_out = static_cast<uint16_t *>(state_out);
+    a.scale = scale;
+    return decode_entry(a, gate_dtype == RGDR_F16 ? kGateF16 : kGateF32, B, H_q, H_v, T, D_k,
+                        D_v, N_slots, actual_seq_lengths, ssm_state_indices,
+                        num_accepted_tokens, stream);
 }

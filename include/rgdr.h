@@ -97,6 +97,30 @@ rgdr_status rgdr_decode(const void *query, const void *key, const void *value,
                         void *state_out, hipStream_t stream);
 
 /*
+ * rgdr_decode_gated -- rgdr_decode with the gate front end fused in: instead of g and beta,
+ * it takes the raw gate projections of the "com.microsoft.LinearAttentionGate" README and
+ * computes, per token and value head, in fp32 and without storing them,
+ *   g    = decay_scale[h] * softplus(gate_a[b, t, h] + dt_bias[h]),
+ *   beta = sigmoid(gate_b[b, t, h]),
+ * then runs the same four steps as rgdr_decode on them.
+ *
+ *   gate_a, gate_b  [B, T, H_v] (the README's head-axis-last layout) of gate_dtype, RGDR_F32
+ *                   or RGDR_F16; element-aligned. Entries of padded tokens are not read.
+ *   dt_bias, decay_scale  fp32 [H_v].
+ *   All other arguments: as rgdr_decode (g and beta are not taken).
+ * Unlike rgdr_decode fed by la_gate, beta is not rounded to bf16 in between.
+ * Errors: as rgdr_decode, plus RGDR_ERR_DTYPE for another gate_dtype.
+ */
+rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *value,
+                              const void *gate_a, const void *gate_b, const float *dt_bias,
+                              const float *decay_scale, rgdr_dtype gate_dtype,
+                              const void *state_pool, const int32_t *actual_seq_lengths,
+                              const int32_t *ssm_state_indices, const float *gk,
+                              const int32_t *num_accepted_tokens, float scale, int32_t B,
+                              int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
+                              int32_t N_slots, void *out, void *state_out, hipStream_t stream);
+
+/*
  * la_gate -- decay = decay_scale * softplus(a + dt_bias) and, when beta_out != NULL,
  * beta = sigmoid(b) ("com.microsoft.LinearAttentionGate" README, Description and tables).
  *

@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for want in ("rgdr_decode", "la_gate", "rgdr_validate", "rgdr_validate_host",
-                 "rgdr_status_string"):
+    for want in ("rgdr_decode", "rgdr_decode_gated", "la_gate", "rgdr_validate",
+                 "rgdr_validate_host", "rgdr_status_string"):
         assert want in names, names
 
 
@@ -84,6 +84,31 @@ def test_decode_argument_checks(lib):
     bad[7] = 0x10002  # g not 4-byte aligned
     assert _decode(lib, ptrs=bad) == ALIGN
     assert _decode(lib, out=0x20004) == ALIGN
+
+
+def _gated(lib, ptrs=None, gdt=F32, **kw):
+    dims = dict(B=2, Hq=2, Hv=4, T=1, Dk=128, Dv=128, N=4)
+    dims.update(kw)
+    p = [0x10000] * 12 if ptrs is None else ptrs
+    return lib.rgdr_decode_gated(*p[:7], gdt, *p[7:12], 1.0, dims["B"], dims["Hq"], dims["Hv"],
+                                 dims["T"], dims["Dk"], dims["Dv"], dims["N"],
+                                 kw.get("out", 0x20000), kw.get("state_out", 0x30000), None)
+
+
+def test_gated_decode_argument_checks(lib):
+    assert _gated(lib, ptrs=[None] * 12, B=0, out=None, state_out=None) == OK  # empty batch
+    for i in range(12):
+        p = [0x10000] * 12
+        p[i] = None
+        assert _gated(lib, ptrs=p) == NULL, i
+    assert _gated(lib, gdt=BF16) == DTYPE
+    assert _gated(lib, T=9) == SHAPE
+    assert _gated(lib, Hq=3) == SHAPE
+    assert _gated(lib, Dk=32) == UNSUP
+    p = [0x10000] * 12
+    p[3] = 0x10002  # fp32 gate projection a not 4-byte aligned
+    assert _gated(lib, ptrs=p) == ALIGN
+    assert _gated(lib, ptrs=p, gdt=F16) != ALIGN  # fp16 needs only 2-byte alignment: goes on
 
 
 def test_gate_argument_checks(lib):

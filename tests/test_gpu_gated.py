@@ -1,0 +1,163 @@
+"""GPU parity of rgdr_decode_gated (gate front end fused into the decode) against the oracle
+chain: the fp64 gate, then the fp64 recurrence core on the decoded inputs (no rounding of g
+or beta in between, as in the fused kernel).
+
+Bars as for rgdr_decode: 2e-2 + 2e-2 |ref| on bf16 out/state_out against unrounded fp64
+values; padding, untouched slots and absent tokens bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import assert_tol, bf16_dev_to_f64, bits_to_dev, dev_to_bits, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_delta_rule_rgdr_amd as m
+    m.library()
+    return m
+
+
+def gate_tensors(inp, dtype=np.float32):
+    return (torch.from_numpy(inp.gate_a.astype(dtype)).cuda(),
+            torch.from_numpy(inp.gate_b.astype(dtype)).cuda(),
+            torch.from_numpy(inp.dt_bias).cuda(), torch.from_numpy(inp.decay_scale).cuda())
+
+
+def gpu_gated(rg, inp, dtype=np.float32, d=None):
+    d = d or upload(inp)
+    a, b, dt, ds = gate_tensors(inp, dtype)
+    pool = d["state"].clone()
+    out, st = rg.rgdr_decode_gated(d["query"], d["key"], d["value"], a, b, dt, ds, pool,
+                                   d["actual_seq_lengths"], d["ssm_state_indices"], d["gk"],
+                                   d["num_accepted_tokens"], inp.scale)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def oracle_gated(inp, entries=None, dtype=np.float32):
+    """Oracle chain for the batch entries `entries` (all when None): returns fp64 out
+    [n, H_v, T, D_v] and each entry's committed state [n, H_v, D_k, D_v] (NaN if skipped)."""
+    sel = np.arange(inp.B) if entries is None else np.asarray(entries)
+    g64, b64 = oracle.la_gate(inp.gate_a[sel].astype(dtype), inp.dt_bias, inp.decay_scale,
+                              inp.gate_b[sel].astype(dtype))
+    g64 = np.ascontiguousarray(g64.transpose(0, 2, 1))  # [n, H_v, T]
+    b64 = np.ascontiguousarray(b64.transpose(0, 2, 1))
+    idx = inp.ssm_state_indices[sel]
+    valid = (idx >= 0) & (idx < inp.N_slots)
+    pool_small = oracle.bf16_to_f64(inp.state[idx[valid]])
+    idx_small = np.full(len(sel), -1, np.int32)
+    idx_small[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+    if pool_small.shape[0] == 0:
+        pool_small = np.zeros((1, inp.Hv, inp.Dk, inp.Dv))
+    out, pool_out = oracle.rgdr_f64(
+        oracle.bf16_to_f64(inp.query[sel]), oracle.bf16_to_f64(inp.key[sel]),
+        oracle.bf16_to_f64(inp.value[sel]), b64, pool_small, inp.actual_seq_lengths[sel],
+        idx_small, g64, inp.gk[sel].astype(np.float64), inp.num_accepted_tokens[sel],
+        float(np.float32(inp.scale)))
+    rows = np.full((len(sel), inp.Hv, inp.Dk, inp.Dv), np.nan)
+    rows[valid] = pool_out[idx_small[valid]]
+    return out, rows
+
+
+def check_gated(inp, out_t, st_t, ref, label, entries=None):
+    out_ref, rows = ref
+    sel = np.arange(inp.B) if entries is None else np.asarray(entries)
+    out = bf16_dev_to_f64(out_t)[sel]
+    lens = np.clip(inp.actual_seq_lengths[sel], 0, inp.T)
+    idx = inp.ssm_state_indices[sel]
+    valid = (idx >= 0) & (idx < inp.N_slots)
+    mask = np.zeros((len(sel), inp.Hv, inp.T), bool)
+    for i in range(len(sel)):
+        if valid[i]:
+            mask[i, :, :lens[i]] = True
+    assert_tol(out[mask], out_ref[mask], f"{label} out")
+    assert np.all(dev_to_bits(out_t)[sel][~mask] == 0), f"{label}: padded rows not +0.0"
+    pool = bf16_dev_to_f64(st_t)
+    assert_tol(pool[idx[valid]], rows[valid], f"{label} state_out")
+    if entries is None:
+        untouched = np.setdiff1d(np.arange(inp.N_slots), idx[valid])
+        assert np.array_equal(dev_to_bits(st_t)[untouched], inp.state[untouched])
+
+
+def test_gated_bench_workload_full(rg):
+    """The bench's step at full size: workload 2 with gate inputs, one fused launch."""
+    inp = workloads.make_workload(2, gate_inputs=True)
+    say(f"gated: {workloads.WORKLOAD_NAMES[2]}")
+    out, st = gpu_gated(rg, inp)
+    check_gated(inp, out, st, oracle_gated(inp), "gated workload 2")
+
+
+def test_gated_workload4_sampled(rg):
+    """Workload 4 at full size (B=256, 512 slots); the oracle recomputes 32 sampled entries."""
+    inp = workloads.make_workload(4)
+    out, st = gpu_gated(rg, inp)
+    entries = np.random.default_rng(5).choice(inp.B, 32, replace=False)
+    check_gated(inp, out, st, oracle_gated(inp, entries), "gated workload 4", entries)
+    # slots no entry names are untouched, bit for bit
+    untouched = np.setdiff1d(np.arange(inp.N_slots), inp.ssm_state_indices)
+    assert np.array_equal(dev_to_bits(st)[untouched], inp.state[untouched])
+
+
+def test_gated_varlen_T8_nan_padding(rg):
+    """Multi-token form with the fused gate: varlen, T = 8; NaN in the padded gate entries
+    changes nothing (they are never read)."""
+    inp = workloads.make_workload(3, gate_inputs=True)
+    out0, st0 = gpu_gated(rg, inp)
+    check_gated(inp, out0, st0, oracle_gated(inp), "gated workload 3")
+    for b in range(inp.B):
+        L = inp.actual_seq_lengths[b]
+        inp.gate_a[b, L:] = np.nan
+        inp.gate_b[b, L:] = np.nan
+    out1, st1 = gpu_gated(rg, inp)
+    assert np.array_equal(dev_to_bits(out0), dev_to_bits(out1))
+    assert np.array_equal(dev_to_bits(st0), dev_to_bits(st1))
+
+
+def test_gated_fp16_projections(rg):
+    for shape in [(5, 2, 4, 1, 128, 128, 8), (3, 2, 2, 3, 64, 192, 4)]:
+        B, Hq, Hv, T, Dk, Dv, N = shape
+        inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=77, indices="choice",
+                                  lengths="uniform", gate=True)
+        out, st = gpu_gated(rg, inp, np.float16)
+        check_gated(inp, out, st, oracle_gated(inp, dtype=np.float16), f"gated fp16 {shape}")
+
+
+def test_gated_absent_and_rejected_token(rg):
+    """T = 1: an absent token (L = 0) leaves the state bit-exact and writes +0.0; a rejected
+    token (n = 0) still produces its output and commits the incoming state bit-exact."""
+    inp = workloads.make_case(4, 2, 4, 1, 128, 128, 6, seed=31, indices="choice",
+                              lengths=[1, 0, 1, 0], gate=True)
+    inp.num_accepted_tokens = np.array([1, 0, 0, 0], np.int32)
+    out, st = gpu_gated(rg, inp)
+    bits = dev_to_bits(st)
+    for b in (1, 2, 3):
+        s = inp.ssm_state_indices[b]
+        assert np.array_equal(bits[s], inp.state[s]), f"entry {b}: state changed"
+    ob = dev_to_bits(out)
+    assert np.all(ob[[1, 3]] == 0)
+    check_gated(inp, out, st, oracle_gated(inp), "gated absent/rejected")
+
+
+def test_gated_matches_unfused_chain(rg):
+    """Fused and unfused (la_gate storing bf16 beta, then rgdr_decode) agree within the bar."""
+    inp = workloads.make_workload(2, gate_inputs=True)
+    out_f, st_f = gpu_gated(rg, inp)
+    d = upload(inp)
+    a, b, dt, ds = gate_tensors(inp)
+    g, beta = rg.la_gate(a, dt, ds, b, decay_dtype=torch.float32, beta_dtype=torch.bfloat16)
+    pool = d["state"].clone()
+    out_u, st_u = rg.rgdr_decode(d["query"], d["key"], d["value"],
+                                 beta.view(inp.B, inp.Hv, 1), pool, d["actual_seq_lengths"],
+                                 d["ssm_state_indices"], g.view(inp.B, inp.Hv, 1), d["gk"],
+                                 d["num_accepted_tokens"], inp.scale)
+    torch.cuda.synchronize()
+    assert_tol(bf16_dev_to_f64(out_f), bf16_dev_to_f64(out_u), "fused vs unfused out")
+    idx = inp.ssm_state_indices
+    assert_tol(bf16_dev_to_f64(st_f)[idx], bf16_dev_to_f64(st_u)[idx], "fused vs unfused state")
