@@ -31,6 +31,23 @@ __device__ __forceinline__ float softplus_f32(float x) {
 }
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Short branch-free forms for the fused decode, where the gate of each item sits on the path
+// between its state tile's arrival and its reduction. They use the hardware exp2/log2 (about
+// 1 ulp each) and keep log1p accurate for small arguments by the correction
+// log1p(e) = log(u) * e / (u - 1) with u = 1 + e rounded (Goldberg, "What Every Computer
+// Scientist Should Know About Floating-Point Arithmetic", Theorem 4). Error: a few ulp of fp32,
+// far below the bf16 state's rounding. Infinities and NaN pass as in the precise forms.
+__device__ __forceinline__ float softplus_fast(float x) {
+    const float e = __expf(-fabsf(x));  // (0, 1]
+    const float u = 1.0f + e;
+    const float d = u - 1.0f;
+    const float l = d == 0.f ? e : __logf(u) * __fdividef(e, d);
+    return fmaxf(x, 0.f) + l;
+}
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 // A gate input element held as raw bits: fp32 (the bits themselves) or fp16 (low 16 bits).
 template <bool F16>
 __device__ __forceinline__ float gate_value(uint32_t bits) {

@@ -80,6 +80,7 @@ constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 #define RGDR_WAVE_PER_CU 0
 #endif
 
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -262,7 +263,7 @@ __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float 
             if constexpr (GATE == kGateGiven)
                 g = __uint_as_float(o.g[j]);
             else
-                g = o.ds * softplus_f32(gate_value<GATE == kGateF16>(o.g[j]) + o.dt);
+                g = o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g[j]) + o.dt);
             const float eg = __expf(g);
             float *row = ob + t * Sh::TOK + 4 * i0;
             row[0] = eg * __expf(o.gk[j].x);
@@ -303,7 +304,7 @@ __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float 
         if constexpr (GATE == kGateGiven)
             bt = bf16_to_f32((uint16_t)o.beta);
         else
-            bt = sigmoid_f32(gate_value<GATE == kGateF16>(o.beta));
+            bt = sigmoid_fast(gate_value<GATE == kGateF16>(o.beta));
         ob[tid * Sh::TOK + 4 * DK + TV] = bt;
     }
 }
@@ -661,8 +662,8 @@ __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, 
         bt = bf16_to_f32((uint16_t)o.beta);
     } else {
         // An absent token keeps decay 1 (its other operands are all zero).
-        g = o.present ? o.ds * softplus_f32(gate_value<GATE == kGateF16>(o.g) + o.dt) : 0.f;
-        bt = sigmoid_f32(gate_value<GATE == kGateF16>(o.beta));
+        g = o.present ? o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g) + o.dt) : 0.f;
+        bt = sigmoid_fast(gate_value<GATE == kGateF16>(o.beta));
     }
     const float eg = __expf(g);
 #pragma unroll
@@ -692,10 +693,14 @@ __device__ __forceinline__ void wave_load_state(const DecodeArgs &a, const Item 
     using Sh = WaveShape<DK, TVW>;
     const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TVW>(a, m) : 0),
                               tile_range<DK, TVW>(a, m));
+    // Per-lane part of the offset in a vector register, the per-row part (uniform) in the
+    // instruction's scalar offset, so the loop keeps one offset register, not RW of them.
+    const uint32_t lane_off = (uint32_t)((rg * a.Dv + cg * 8) * 2);
+    const uint32_t row_step = (uint32_t)(Sh::RG * a.Dv * 2);
 #pragma unroll
     for (int r = 0; r < Sh::RW; ++r)
-        raw[r] = __builtin_amdgcn_raw_buffer_load_b128(
-            rs, (uint32_t)(((rg + Sh::RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_LOAD_POLICY);
+        raw[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, r * row_step,
+                                                       RGDR_STATE_LOAD_POLICY);
 }
 
 template <int DK, int TVW, int NBUF, int GATE, int P>
@@ -724,14 +729,16 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
         const f32x4 dkq = *reinterpret_cast<const f32x4 *>(ob + 4 * (rg + RG * r));
         const float d = dkq.x, kk = dkq.y, qq = dkq.z;
         kq = fmaf(kk, qq, kq);
+        // (S_ij d_i) k_i summed over i, as S_ij (d_i k_i): the decay folds into the FMA.
+        const float dk = d * kk, dq = d * qq;
         const uint32_t w[4] = {W[r].x, W[r].y, W[r].z, W[r].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float s0 = bf16_lo(w[j]) * d, s1 = bf16_hi(w[j]) * d;
-            pk[2 * j] = fmaf(s0, kk, pk[2 * j]);
-            pq[2 * j] = fmaf(s0, qq, pq[2 * j]);
-            pk[2 * j + 1] = fmaf(s1, kk, pk[2 * j + 1]);
-            pq[2 * j + 1] = fmaf(s1, qq, pq[2 * j + 1]);
+            const float s0 = bf16_lo(w[j]), s1 = bf16_hi(w[j]);
+            pk[2 * j] = fmaf(s0, dk, pk[2 * j]);
+            pq[2 * j] = fmaf(s0, dq, pq[2 * j]);
+            pk[2 * j + 1] = fmaf(s1, dk, pk[2 * j + 1]);
+            pq[2 * j + 1] = fmaf(s1, dq, pq[2 * j + 1]);
         }
     }
     // Full sums over D_k: the row groups of this wave are LPW lanes apart.
@@ -770,11 +777,13 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
     for (int r = 0; r < RW; ++r) asm volatile("" : "+v"(W[r]));
     const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TVW>(a, m) : 0),
                                tile_range<DK, TVW>(a, m));
+    const uint32_t lane_off = (uint32_t)((rg * a.Dv + cg * 8) * 2);
+    const uint32_t row_step = (uint32_t)(RG * a.Dv * 2);
     if (m.n == 0) {  // nothing accepted: commit the incoming bytes
 #pragma unroll
         for (int r = 0; r < RW; ++r)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                W[r], rso, (uint32_t)(((rg + RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_STORE_POLICY);
+            __builtin_amdgcn_raw_buffer_store_b128(W[r], rso, lane_off, r * row_step,
+                                                   RGDR_STATE_STORE_POLICY);
     } else {
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
@@ -785,9 +794,9 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
             for (int j = 0; j < 4; ++j)
                 nw[j] = pack_bf16x2(fmaf(dkq.y, u[2 * j], bf16_lo(w[j]) * dkq.x),
                                     fmaf(dkq.y, u[2 * j + 1], bf16_hi(w[j]) * dkq.x));
-            __builtin_amdgcn_raw_buffer_store_b128(
-                u32x4{nw[0], nw[1], nw[2], nw[3]}, rso,
-                (uint32_t)(((rg + RG * r) * a.Dv + cg * 8) * 2), 0, RGDR_STATE_STORE_POLICY);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{nw[0], nw[1], nw[2], nw[3]}, rso,
+                                                   lane_off, r * row_step,
+                                                   RGDR_STATE_STORE_POLICY);
         }
     }
     wave_load_state<DK, TVW>(a, resolve(a, x, it + NBUF * G), W, cg, rg);
@@ -813,17 +822,17 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     const int32_t *__restrict__ nacc) {
     using Sh = WaveShape<DK, TVW>;
     const Index x{lens, idx, nacc};
-    __shared__ f32x4 lds4[2 * Sh::OPS / 4];
+    __shared__ f32x4 lds4[2 * Sh::OPS / 4];  // two operand buffers (item parity)
     float *lds = reinterpret_cast<float *>(lds4);
     const int lane = threadIdx.x;
     const int cg = lane % Sh::LPW, rg = lane / Sh::LPW;
     const int G = gridDim.x;
     int it = blockIdx.x;
     WavePipe<DK, TVW, NBUF> pl;
-    wave_load_state<DK, TVW>(a, resolve(a, x, it), pl.raw[0], cg, rg);
+    // Operands first: staging them waits only for them, while the tile is still in flight.
     wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it), pl.ops[0], lane);
 #pragma unroll
-    for (int j = 1; j < NBUF; ++j)
+    for (int j = 0; j < NBUF; ++j)
         wave_load_state<DK, TVW>(a, resolve(a, x, it + j * G), pl.raw[j], cg, rg);
     constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
     while (wave_phases<DK, TVW, NBUF, GATE, 0, U>(a, x, pl, lds, it, lane)) {
