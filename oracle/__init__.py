@@ -51,11 +51,11 @@ def _bind(lib):
     lib.oracle_rgdr_bf16.restype = C.c_int
     lib.oracle_rgdr_bf16.argtypes = (
         [_u16p, _u16p, _u16p, _u16p, _u16p, _i32p, _i32p, _f32p, _f32p, _i32p, C.c_float]
-        + ints + [_f64p, _u16p, C.c_void_p])
+        + ints + [_f64p, _u16p, C.c_void_p, C.c_int])
     lib.oracle_rgdr_f64.restype = C.c_int
     lib.oracle_rgdr_f64.argtypes = (
         [_f64p, _f64p, _f64p, _f64p, _f64p, _i32p, _i32p, _f64p, _f64p, _i32p, C.c_double]
-        + ints + [_f64p, _f64p])
+        + ints + [_f64p, _f64p, C.c_int])
     lib.oracle_la_gate.restype = C.c_int
     lib.oracle_la_gate.argtypes = [C.c_void_p, _f32p, _f32p, C.c_void_p, C.c_int,
                                    C.c_longlong, C.c_int, _f64p, C.c_void_p]
@@ -113,8 +113,11 @@ class Oracle:
 
     def rgdr_bf16(self, query, key, value, beta, state_pool, actual_seq_lengths,
                   ssm_state_indices, g, gk, num_accepted_tokens, scale_value=1.0, *,
-                  want_rows=False):
+                  want_rows=False, normalize_qk=False):
         """The decode operator with bf16 storage: returns ``(out, state_out, rows)``.
+
+        With ``normalize_qk`` each token's query and key head vector is first divided by
+        its L2 norm (the operator's unit-norm precondition established by the oracle).
 
         ``out`` is fp64 ``[B, H_v, T, D_v]`` (unrounded); ``state_out`` a bf16 copy of the
         pool in which every named slot holds its committed state (others unchanged);
@@ -134,13 +137,14 @@ class Oracle:
             np.ascontiguousarray(g, np.float32), np.ascontiguousarray(gk, np.float32),
             np.ascontiguousarray(num_accepted_tokens, np.int32),
             float(np.float32(scale_value)), B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out,
-            rows.ctypes.data if rows is not None else None)
+            rows.ctypes.data if rows is not None else None, int(bool(normalize_qk)))
         if rc != 0:
             raise RuntimeError(f"oracle_rgdr_bf16 failed with code {rc}")
         return out, state_out, rows
 
     def rgdr_f64(self, query, key, value, beta, state_pool, actual_seq_lengths,
-                 ssm_state_indices, g, gk, num_accepted_tokens, scale_value=1.0):
+                 ssm_state_indices, g, gk, num_accepted_tokens, scale_value=1.0, *,
+                 normalize_qk=False):
         """The same recurrence with fp64 inputs and an fp64 pool, no rounding at all.
 
         Returns ``(out, state_out)``: fp64 ``[B, H_v, T, D_v]`` and the fp64 pool.
@@ -153,7 +157,8 @@ class Oracle:
         rc = self.lib.oracle_rgdr_f64(f(query), f(key), f(value), f(beta), f(state_pool),
                                       i(actual_seq_lengths), i(ssm_state_indices), f(g),
                                       f(gk), i(num_accepted_tokens), float(scale_value),
-                                      B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out)
+                                      B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out,
+                                      int(bool(normalize_qk)))
         if rc != 0:
             raise RuntimeError(f"oracle_rgdr_f64 failed with code {rc}")
         return out, state_out

@@ -31,6 +31,10 @@
  *   - num_accepted_tokens[b] = n is clamped to [0, L]; outputs are produced for all L
  *     tokens and the committed state is the state after the first n tokens.
  *   - q is multiplied by scale before step 4 (the scale_value parameter).
+ *   - Unit-norm q and k are a precondition of the operator (its query and key parameters).
+ *     On request (normalize_qk) the oracle establishes it itself: each token's query and
+ *     key head vector is divided by its L2 norm over D_k before the four steps (and before
+ *     the scale); an all-zero vector stays zero.
  *   - Step 3's "k^T @ (...)" is the outer product k (x) u, shape [D_k, D_v].
  *   - Gate: softplus(x) = ln(1 + e^x) with no beta/threshold parameters, evaluated in
  *     the overflow-safe form x + log1p(e^-x) for x > 0 and log1p(e^x) otherwise, which
@@ -184,6 +188,21 @@ static void gdr_pair(double *S, double *Scommit, int L, int n, int T, int Dk, in
             out[(size_t)t * Dv + j] = 0.0;
 }
 
+/* q/k normalisation  [R], parameters query and key (unit L2 norm per head vector):
+ * x = x / ||x||_2 over the n elements, the norm the square root of the sum of squares taken
+ * in index order; an all-zero vector is left as it is. */
+static void l2_normalize(double *x, int n)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i)
+        ss += x[i] * x[i];
+    if (ss == 0.0)
+        return;
+    double nrm = sqrt(ss);
+    for (int i = 0; i < n; ++i)
+        x[i] = x[i] / nrm;
+}
+
 typedef struct {
     const void *q, *k, *v, *beta, *g, *gk; /* inputs, element types below */
     int q_ty, k_ty, v_ty, beta_ty, g_ty, gk_ty;
@@ -194,6 +213,7 @@ typedef struct {
     double *out;                           /* [B, H_v, T, D_v], unrounded */
     void *pool_out; int pool_out_ty;       /* [N_slots, H_v, D_k, D_v]; may alias pool */
     double *rows_out;                      /* optional [B, H_v, D_k, D_v], unrounded */
+    int normalize_qk;                      /* nonzero: L2-normalise q and k per token */
 } rgdr_args;
 
 static int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -251,6 +271,10 @@ static int rgdr_drive(const rgdr_args *a)
                     v[(size_t)t * Dv + j] = rd(a->v, a->v_ty, vo + (size_t)t * Dv + j);
                 beta[t] = rd(a->beta, a->beta_ty, go + t);
                 g[t] = rd(a->g, a->g_ty, go + t);
+                if (a->normalize_qk) {
+                    l2_normalize(q + (size_t)t * Dk, Dk);
+                    l2_normalize(k + (size_t)t * Dk, Dk);
+                }
             }
             for (size_t e = 0; e < nS; ++e)
                 S[e] = rd(a->pool, a->pool_ty, so + e);
@@ -278,17 +302,19 @@ static int rgdr_drive(const rgdr_args *a)
  * int32 index arrays, fp32 scale. out is returned unrounded (fp64); state_out receives
  * the committed bf16 state of every named slot (it may be the same buffer as pool);
  * rows_out, if not NULL, receives each batch entry's committed state unrounded.
+ * normalize_qk nonzero: q and k are L2-normalised per token and head first.
  * Returns 0, or nonzero for a NULL pointer or a non-positive size.
  */
 int oracle_rgdr_bf16(const uint16_t *query, const uint16_t *key, const uint16_t *value,
                      const uint16_t *beta, const uint16_t *pool, const int32_t *lens,
                      const int32_t *idx, const float *g, const float *gk, const int32_t *nacc,
                      float scale, int B, int Hq, int Hv, int T, int Dk, int Dv, int N_slots,
-                     double *out, uint16_t *state_out, double *rows_out)
+                     double *out, uint16_t *state_out, double *rows_out, int normalize_qk)
 {
     rgdr_args a = {query, key, value, beta, g, gk, TY_BF16, TY_BF16, TY_BF16, TY_BF16,
                    TY_F32, TY_F32, pool, TY_BF16, lens, idx, nacc, (double)scale,
-                   B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_BF16, rows_out};
+                   B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_BF16, rows_out,
+                   normalize_qk};
     return rgdr_drive(&a);
 }
 
@@ -298,11 +324,12 @@ int oracle_rgdr_f64(const double *query, const double *key, const double *value,
                     const double *beta, const double *pool, const int32_t *lens,
                     const int32_t *idx, const double *g, const double *gk,
                     const int32_t *nacc, double scale, int B, int Hq, int Hv, int T, int Dk,
-                    int Dv, int N_slots, double *out, double *state_out)
+                    int Dv, int N_slots, double *out, double *state_out, int normalize_qk)
 {
     rgdr_args a = {query, key, value, beta, g, gk, TY_F64, TY_F64, TY_F64, TY_F64,
                    TY_F64, TY_F64, pool, TY_F64, lens, idx, nacc, scale,
-                   B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_F64, NULL};
+                   B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_F64, NULL,
+                   normalize_qk};
     return rgdr_drive(&a);
 }
 

@@ -531,4 +531,108 @@ def pin_gate_types_and_shapes(o):
         raise AssertionError("beta without b must fail")
 
 
+# ------------------------------------------------------------------------------------
+# q/k normalisation (the operator's unit-norm precondition on query and key, established
+# by the oracle on request)
+# ------------------------------------------------------------------------------------
+
+
+def _raw_qk_case(rng, B, Hq, Hv, T, Dk, Dv, N):
+    c = f64_case(rng, B, Hq, Hv, T, Dk, Dv, N)
+    # raw projections: magnitudes far from 1, different per token and head
+    c["query"] = c["query"] * rng.uniform(0.2, 7.0, (B, Hq, T, 1))
+    c["key"] = c["key"] * rng.uniform(0.2, 7.0, (B, Hq, T, 1))
+    return c
+
+
+def pin_normalize_matches_prenormalized(o):
+    """normalize_qk on raw q, k equals the plain call on q / ||q||, k / ||k|| computed by
+    numpy (its own norm routine), with head sharing, varlen and a scale != 1."""
+    rng = np.random.default_rng(24)
+    c = _raw_qk_case(rng, 3, 2, 4, 3, 9, 5, 5)
+    c["actual_seq_lengths"] = np.array([3, 1, 2], np.int32)
+    c["num_accepted_tokens"] = c["actual_seq_lengths"].copy()
+    c["scale_value"] = 0.37
+    args = (c["value"], c["beta"], c["state_pool"], c["actual_seq_lengths"],
+            c["ssm_state_indices"], c["g"], c["gk"], c["num_accepted_tokens"], c["scale_value"])
+    out_n, pool_n = o.rgdr_f64(c["query"], c["key"], *args, normalize_qk=True)
+    qn = c["query"] / np.linalg.norm(c["query"], axis=-1, keepdims=True)
+    kn = c["key"] / np.linalg.norm(c["key"], axis=-1, keepdims=True)
+    out_p, pool_p = o.rgdr_f64(qn, kn, *args)
+    close(out_n, out_p, 1e-12, 1e-14)
+    close(pool_n, pool_p, 1e-12, 1e-14)
+    # and the flag matters: without it the raw magnitudes change the result
+    out_raw, _ = o.rgdr_f64(c["query"], c["key"], *args)
+    assert np.abs(out_raw - out_p).max() > 1e-3
+
+
+def pin_normalize_scale_invariance(o):
+    """With normalize_qk, multiplying each q and k head vector by its own positive power of
+    two changes nothing, bit for bit (the norm scales by exactly that factor)."""
+    rng = np.random.default_rng(25)
+    c = _raw_qk_case(rng, 2, 2, 2, 2, 8, 6, 3)
+    base = o.rgdr_f64(c["query"], c["key"], c["value"], c["beta"], c["state_pool"],
+                      c["actual_seq_lengths"], c["ssm_state_indices"], c["g"], c["gk"],
+                      c["num_accepted_tokens"], c["scale_value"], normalize_qk=True)
+    fq = 2.0 ** rng.integers(-6, 7, (2, 2, 2, 1))
+    fk = 2.0 ** rng.integers(-6, 7, (2, 2, 2, 1))
+    scaled = o.rgdr_f64(c["query"] * fq, c["key"] * fk, c["value"], c["beta"],
+                        c["state_pool"], c["actual_seq_lengths"], c["ssm_state_indices"],
+                        c["g"], c["gk"], c["num_accepted_tokens"], c["scale_value"],
+                        normalize_qk=True)
+    bits_equal(base[0], scaled[0])
+    bits_equal(base[1], scaled[1])
+
+
+def pin_normalize_zero_vectors(o):
+    """A zero query gives a zero output row; a zero key leaves the state at its decayed
+    value (no update). Both without NaN, and equal to the call without normalisation,
+    which sees the same zero vectors."""
+    rng = np.random.default_rng(26)
+    c = _raw_qk_case(rng, 2, 1, 1, 2, 6, 4, 2)
+    c["query"][0, 0, 1] = 0.0
+    c["key"][1, 0, 0] = 0.0
+    c["query"][1, 0, 0] = 0.0
+    out_n, pool_n = o.rgdr_f64(c["query"], c["key"], c["value"], c["beta"], c["state_pool"],
+                               c["actual_seq_lengths"], c["ssm_state_indices"], c["g"],
+                               c["gk"], c["num_accepted_tokens"], c["scale_value"],
+                               normalize_qk=True)
+    assert np.all(np.isfinite(out_n)) and np.all(np.isfinite(pool_n))
+    assert np.all(out_n[0, 0, 1] == 0.0) and np.all(out_n[1, 0, 0] == 0.0)
+    qn = c["query"].copy()
+    kn = c["key"].copy()
+    for arr in (qn, kn):
+        nrm = np.linalg.norm(arr, axis=-1, keepdims=True)
+        np.divide(arr, nrm, out=arr, where=nrm > 0)
+    out_p, pool_p = o.rgdr_f64(qn, kn, c["value"], c["beta"], c["state_pool"],
+                               c["actual_seq_lengths"], c["ssm_state_indices"], c["g"],
+                               c["gk"], c["num_accepted_tokens"], c["scale_value"])
+    close(out_n, out_p, 1e-12, 1e-14)
+    close(pool_n, pool_p, 1e-12, 1e-14)
+
+
+def pin_normalize_bf16_api(o):
+    """The bf16 entry point with normalize_qk is the fp64 core with normalize_qk on the
+    decoded inputs (unrounded out, state rounded once)."""
+    rng = np.random.default_rng(27)
+    B, Hq, Hv, T, Dk, Dv, N = 2, 1, 2, 2, 8, 8, 3
+    c = _raw_qk_case(rng, B, Hq, Hv, T, Dk, Dv, N)
+    enc = lambda x: o.f64_to_bf16(x)
+    q16, k16, v16 = enc(c["query"]), enc(c["key"]), enc(c["value"])
+    b16, p16 = enc(c["beta"]), enc(c["state_pool"])
+    g32 = c["g"].astype(np.float32)
+    gk32 = c["gk"].astype(np.float32)
+    scale = float(np.float32(c["scale_value"]))
+    out, pool, _ = o.rgdr_bf16(q16, k16, v16, b16, p16, c["actual_seq_lengths"],
+                               c["ssm_state_indices"], g32, gk32, c["num_accepted_tokens"],
+                               scale, normalize_qk=True)
+    dec = o.bf16_to_f64
+    out_c, pool_c = o.rgdr_f64(dec(q16), dec(k16), dec(v16), dec(b16), dec(p16),
+                               c["actual_seq_lengths"], c["ssm_state_indices"],
+                               g32.astype(np.float64), gk32.astype(np.float64),
+                               c["num_accepted_tokens"], scale, normalize_qk=True)
+    bits_equal(out, out_c)
+    bits_equal(pool, enc(pool_c))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

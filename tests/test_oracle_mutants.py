@@ -46,6 +46,11 @@ MUTANTS = {
                              "double x = rd(a, ab_ty, e) + (double)dt_bias[r % H];"),
     "f16_exponent_bias": ("x = ldexp((double)(1024 + m), e - 25);",
                           "x = ldexp((double)(1024 + m), e - 24);"),
+    "normalize_missing_sqrt": ("double nrm = sqrt(ss);", "double nrm = ss;"),
+    "normalize_skips_key": ("l2_normalize(k + (size_t)t * Dk, Dk);", "(void)k;"),
+    "normalize_short_vector": ("l2_normalize(q + (size_t)t * Dk, Dk);",
+                               "l2_normalize(q + (size_t)t * Dk, Dk - 1);"),
+    "normalize_abs_sum": ("ss += x[i] * x[i];", "ss += fabs(x[i]);"),
 }
 
 
