@@ -28,6 +28,8 @@ __all__ = ["rgdr_decode", "rgdr_decode_gated", "recurrent_gated_delta_rule", "la
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librgdr.so")
 
 RGDR_F32, RGDR_F16, RGDR_BF16 = 0, 1, 2
+RGDR_NORMALIZE_QK = 1  # option bit of rgdr_decode_gated
+NORMALIZE_QK = RGDR_NORMALIZE_QK
 _DTYPE_CODE = {torch.float32: RGDR_F32, torch.float16: RGDR_F16, torch.bfloat16: RGDR_BF16}
 
 _lib = None
@@ -47,7 +49,8 @@ def library():
     lib.rgdr_decode.restype = C.c_int
     lib.rgdr_decode.argtypes = [vp] * 10 + [f32] + [i32] * 7 + [vp, vp, vp]
     lib.rgdr_decode_gated.restype = C.c_int
-    lib.rgdr_decode_gated.argtypes = [vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7 + [vp] * 3
+    lib.rgdr_decode_gated.argtypes = ([vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7
+                                      + [vp] * 2 + [C.c_uint32, vp])
     lib.la_gate.restype = C.c_int
     lib.la_gate.argtypes = [vp, vp, vp, vp, C.c_int, i64, i32, vp, C.c_int, vp, C.c_int, vp]
     lib.rgdr_validate.restype = C.c_int
@@ -143,12 +146,14 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
 
 def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
                       actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens, scale=1.0,
-                      *, out=None, state_out=None, stream=None):
+                      *, normalize_qk=False, out=None, state_out=None, stream=None):
     """One decode step with the gate fused in; returns ``(out, state_out)``.
 
     ``a``, ``b``: raw gate projections ``[B, T, H_v]`` (float32 or float16, head axis last);
     ``dt_bias``, ``decay_scale``: float32 ``[H_v]``. ``g = decay_scale * softplus(a + dt_bias)``
-    and ``beta = sigmoid(b)`` are computed in the kernel in fp32. Other arguments as
+    and ``beta = sigmoid(b)`` are computed in the kernel in fp32. With ``normalize_qk`` the
+    kernel also divides each token's query and key head vector by its L2 norm (the
+    operator's unit-norm precondition), so raw projections may be passed. Other arguments as
     ``rgdr_decode`` (which takes g and beta instead).
     """
     lib = library()
@@ -195,7 +200,7 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
                                actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
                                gk.data_ptr(), num_accepted_tokens.data_ptr(), float(scale), B, Hq,
                                Hv, T, Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
-                               _stream_handle(stream))
+                               NORMALIZE_QK if normalize_qk else 0, _stream_handle(stream))
     _check(rc, "rgdr_decode_gated")
     return out, state_out
 

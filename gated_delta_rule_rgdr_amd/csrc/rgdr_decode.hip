@@ -112,6 +112,7 @@ struct DecodeArgs {
     uint16_t *out, *pool_out;
     float scale;
     int Hq, Hv, T, Dv, N_slots, ntiles, group, n_items;
+    int norm_qk;  // fused front end only: L2-normalise each token's q and k head vector
 };
 
 // How an item's g and beta arrive: given (bf16 beta, fp32 g), or computed from raw gate
@@ -193,6 +194,50 @@ __device__ __forceinline__ Item resolve(const DecodeArgs &a, const Index &x, int
     return m;
 }
 
+// Sum of x over the lanes of this wave that hold the same columns (LPR apart). Every lane
+// ends with the same value (each step adds a pair of lanes in both orders, and IEEE
+// addition is commutative).
+template <int LPR>
+__device__ __forceinline__ float colsum(float x) {
+    if constexpr (LPR == 8) {
+        // row_ror:8 within each 16-lane row pairs lane i with lane i ^ 8
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    }
+    {
+        // lanes 16-31 <-> 0-15 and 48-63 <-> 32-47: each lane meets lane ^ 16
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        // the two halves of the wave: each lane meets lane ^ 32
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+
+// Sum of x over aligned groups of N consecutive lanes (N = 8, 16 or 64). Every lane of a group
+// ends with the same value, as in colsum. Must be reached by the whole wave.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16 || N == 64, "group size");
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // other quad of 8
+    if constexpr (N >= 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // other 8 of 16
+    if constexpr (N == 64) x = colsum<16>(x);
+    return x;
+}
+
+// Multipliers that L2-normalise a head vector from its sum of squares: 1/||x||, and 0 for an
+// all-zero vector (which then stays zero).
+__device__ __forceinline__ float inv_norm(float ss) {
+    return ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+}
+
 template <int DK, int TV, int NT, int TMAX>
 struct Ops {
     using Sh = TileShape<DK, TV, NT, TMAX>;
@@ -252,7 +297,7 @@ __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
 // fused gate, g and beta are computed here too).
 template <int DK, int TV, int NT, int TMAX, int GATE>
 __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float *ob,
-                                          float scale, int tid) {
+                                          float scale, bool norm, int tid) {
     using Sh = TileShape<DK, TV, NT, TMAX>;
 #pragma unroll
     for (int j = 0; j < Sh::GKV; ++j) {
@@ -276,16 +321,32 @@ __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float 
     for (int j = 0; j < Sh::KQV; ++j) {
         const int e = tid + j * NT;
         const int t = e * 8 / DK, i0 = e * 8 % DK;
+        const uint32_t kw[4] = {o.k[j].x, o.k[j].y, o.k[j].z, o.k[j].w};
+        const uint32_t qw[4] = {o.q[j].x, o.q[j].y, o.q[j].z, o.q[j].w};
+        float ks = 1.f, qs = scale;
+        if constexpr (GATE != kGateGiven) {
+            if (norm) {  // uniform: the whole workgroup takes it
+                // One token's head vector lies in DK/8 consecutive, aligned lanes.
+                float kss = 0.f, qss = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    kss = fmaf(bf16_lo(kw[w]), bf16_lo(kw[w]), kss);
+                    kss = fmaf(bf16_hi(kw[w]), bf16_hi(kw[w]), kss);
+                    qss = fmaf(bf16_lo(qw[w]), bf16_lo(qw[w]), qss);
+                    qss = fmaf(bf16_hi(qw[w]), bf16_hi(qw[w]), qss);
+                }
+                ks = inv_norm(group_sum<DK / 8>(kss));
+                qs = scale * inv_norm(group_sum<DK / 8>(qss));
+            }
+        }
         if (t < TMAX) {
             float *row = ob + t * Sh::TOK + 4 * i0;
-            const uint32_t kw[4] = {o.k[j].x, o.k[j].y, o.k[j].z, o.k[j].w};
-            const uint32_t qw[4] = {o.q[j].x, o.q[j].y, o.q[j].z, o.q[j].w};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                row[8 * w + 1] = bf16_lo(kw[w]);
-                row[8 * w + 5] = bf16_hi(kw[w]);
-                row[8 * w + 2] = bf16_lo(qw[w]) * scale;
-                row[8 * w + 6] = bf16_hi(qw[w]) * scale;
+                row[8 * w + 1] = bf16_lo(kw[w]) * ks;
+                row[8 * w + 5] = bf16_hi(kw[w]) * ks;
+                row[8 * w + 2] = bf16_lo(qw[w]) * qs;
+                row[8 * w + 6] = bf16_hi(qw[w]) * qs;
             }
         }
     }
@@ -332,30 +393,6 @@ __device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
     for (int r = 0; r < Sh::R; ++r)
         raw[r] = __builtin_amdgcn_raw_buffer_load_b128(
             rs, (uint32_t)(((rg + r * Sh::RPP) * a.Dv + cg * 8) * 2), 0, kCacheNT);
-}
-
-// Sum of x over the lanes of this wave that hold the same columns (LPR apart). Every lane
-// ends with the same value (each step adds a pair of lanes in both orders, and IEEE
-// addition is commutative).
-template <int LPR>
-__device__ __forceinline__ float colsum(float x) {
-    if constexpr (LPR == 8) {
-        // row_ror:8 within each 16-lane row pairs lane i with lane i ^ 8
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-    }
-    {
-        // lanes 16-31 <-> 0-15 and 48-63 <-> 32-47: each lane meets lane ^ 16
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    {
-        // the two halves of the wave: each lane meets lane ^ 32
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    return x;
 }
 
 template <int DK, int TV, int NT, int NBUF, int TMAX>
@@ -490,7 +527,7 @@ __device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &
     // Operands of the next item go in flight; this item's are staged in LDS.
     load_ops<DK, TV, NT, kMaxT, GATE>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
     float *ob = lds + (P & 1) * Sh::OPS;
-    stage_ops<DK, TV, NT, kMaxT, GATE>(pl.ops[P & 1], ob, a.scale, tid);
+    stage_ops<DK, TV, NT, kMaxT, GATE>(pl.ops[P & 1], ob, a.scale, a.norm_qk != 0, tid);
     __syncthreads();
 
     float S[R][CPL];
@@ -654,7 +691,7 @@ __device__ __forceinline__ void wave_load_ops(const DecodeArgs &a, const Item &m
 
 template <int DK, int TVW, int GATE>
 __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, float scale,
-                                               int lane) {
+                                               bool norm, int lane) {
     using Sh = WaveShape<DK, TVW>;
     float g, bt;
     if constexpr (GATE == kGateGiven) {
@@ -666,12 +703,27 @@ __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, 
         bt = sigmoid_fast(gate_value<GATE == kGateF16>(o.beta));
     }
     const float eg = __expf(g);
+    float ks = 1.f, qs = scale;
+    if constexpr (GATE != kGateGiven) {
+        if (norm) {  // uniform; the wave holds the whole head vector (RPL values per lane)
+            float kss = 0.f, qss = 0.f;
+#pragma unroll
+            for (int j = 0; j < Sh::RPL; ++j) {
+                const float kv = __uint_as_float(j ? o.k & 0xFFFF0000u : o.k << 16);
+                const float qv = __uint_as_float(j ? o.q & 0xFFFF0000u : o.q << 16);
+                kss = fmaf(kv, kv, kss);
+                qss = fmaf(qv, qv, qss);
+            }
+            ks = inv_norm(group_sum<64>(kss));
+            qs = scale * inv_norm(group_sum<64>(qss));
+        }
+    }
 #pragma unroll
     for (int j = 0; j < Sh::RPL; ++j) {
         const uint32_t kb = j ? o.k & 0xFFFF0000u : o.k << 16;
         const uint32_t qb = j ? o.q & 0xFFFF0000u : o.q << 16;
         *reinterpret_cast<f32x4 *>(ob + 4 * (lane * Sh::RPL + j)) =
-            f32x4{eg * __expf(o.gk[j]), __uint_as_float(kb), __uint_as_float(qb) * scale, 0.f};
+            f32x4{eg * __expf(o.gk[j]), __uint_as_float(kb) * ks, __uint_as_float(qb) * qs, 0.f};
     }
     if constexpr (Sh::VPL == 2)
         *reinterpret_cast<float2 *>(ob + 4 * DK + 2 * lane) = make_float2(bf16_lo(o.v), bf16_hi(o.v));
@@ -716,7 +768,7 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
 
     wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], lane);
     float *ob = lds + (P & 1) * Sh::OPS;
-    wave_stage_ops<DK, TVW, GATE>(pl.ops[P & 1], ob, a.scale, lane);
+    wave_stage_ops<DK, TVW, GATE>(pl.ops[P & 1], ob, a.scale, a.norm_qk != 0, lane);
 
     u32x4(&W)[RW] = pl.raw[P % NBUF];
     // Step 1 (decay) fused with the partial sums of steps 2 and 4.
@@ -991,8 +1043,9 @@ extern "C" rgdr_status rgdr_decode_gated(const void *query, const void *key, con
                                          const int32_t *num_accepted_tokens, float scale,
                                          int32_t B, int32_t H_q, int32_t H_v, int32_t T,
                                          int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
-                                         void *state_out, hipStream_t stream) {
+                                         void *state_out, uint32_t flags, hipStream_t stream) {
     using namespace rgdr;
+    if (flags & ~(uint32_t)RGDR_NORMALIZE_QK) return RGDR_ERR_UNSUPPORTED;
     if (B == 0) return RGDR_OK;
     if (!query || !key || !value || !gate_a || !gate_b || !dt_bias || !decay_scale ||
         !state_pool || !actual_seq_lengths || !ssm_state_indices || !gk ||
@@ -1013,6 +1066,7 @@ extern "C" rgdr_status rgdr_decode_gated(const void *query, const void *key, con
     a.gb = gate_b;
     a.dt_bias = dt_bias;
     a.dscale = decay_scale;
+    a.norm_qk = (flags & RGDR_NORMALIZE_QK) ? 1 : 0;
     a.out = static_cast<uint16_t *>(out);
     a.pool_out = static_cast<uint16_t *>(state_out);
     a.scale = scale;

@@ -41,7 +41,8 @@ typedef enum {
     RGDR_ERR_NULL = 1,        /* a required pointer is NULL                                */
     RGDR_ERR_SHAPE = 2,       /* a size is negative, or zero where not allowed; T > 8;
                                  H_v % H_q != 0; grid too large; beta requested without b */
-    RGDR_ERR_UNSUPPORTED = 3, /* D_k not in {64, 128} or D_v not a multiple of 64           */
+    RGDR_ERR_UNSUPPORTED = 3, /* D_k not in {64, 128}, D_v not a multiple of 64, or an
+                                 unknown option bit                                         */
     RGDR_ERR_RANGE = 4,       /* (validate) a length, count or slot index out of range     */
     RGDR_ERR_DUPLICATE = 5,   /* (validate) two batch entries name the same slot           */
     RGDR_ERR_DTYPE = 6,       /* a dtype code not allowed for that argument                 */
@@ -50,6 +51,9 @@ typedef enum {
 } rgdr_status;
 
 typedef enum { RGDR_F32 = 0, RGDR_F16 = 1, RGDR_BF16 = 2 } rgdr_dtype;
+
+/* Option bits of rgdr_decode_gated. */
+enum { RGDR_NORMALIZE_QK = 1u /* L2-normalise each token's query and key head vector */ };
 
 /*
  * rgdr_decode -- one decode step over a batch (MindSpore Lite page above; arguments keep
@@ -109,7 +113,14 @@ rgdr_status rgdr_decode(const void *query, const void *key, const void *value,
  *   dt_bias, decay_scale  fp32 [H_v].
  *   All other arguments: as rgdr_decode (g and beta are not taken).
  * Unlike rgdr_decode fed by la_gate, beta is not rounded to bf16 in between.
- * Errors: as rgdr_decode, plus RGDR_ERR_DTYPE for another gate_dtype.
+ *
+ *   flags  0, or RGDR_NORMALIZE_QK: establish the operator's unit-norm precondition on
+ *          query and key (MindSpore Lite page, parameters query and key) in the kernel:
+ *          each token's q and k head vector is divided by its L2 norm over D_k (fp32 sum
+ *          of squares, reciprocal square root) before the four steps and before the scale;
+ *          an all-zero vector stays zero. The inputs are not modified.
+ * Errors: as rgdr_decode, plus RGDR_ERR_DTYPE for another gate_dtype and
+ * RGDR_ERR_UNSUPPORTED for an unknown flag bit.
  */
 rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *value,
                               const void *gate_a, const void *gate_b, const float *dt_bias,
@@ -118,7 +129,8 @@ rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *va
                               const int32_t *ssm_state_indices, const float *gk,
                               const int32_t *num_accepted_tokens, float scale, int32_t B,
                               int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
-                              int32_t N_slots, void *out, void *state_out, hipStream_t stream);
+                              int32_t N_slots, void *out, void *state_out, uint32_t flags,
+                              hipStream_t stream);
 
 /*
  * la_gate -- decay = decay_scale * softplus(a + dt_bias) and, when beta_out != NULL,

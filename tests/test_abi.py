@@ -92,7 +92,8 @@ def _gated(lib, ptrs=None, gdt=F32, **kw):
     p = [0x10000] * 12 if ptrs is None else ptrs
     return lib.rgdr_decode_gated(*p[:7], gdt, *p[7:12], 1.0, dims["B"], dims["Hq"], dims["Hv"],
                                  dims["T"], dims["Dk"], dims["Dv"], dims["N"],
-                                 kw.get("out", 0x20000), kw.get("state_out", 0x30000), None)
+                                 kw.get("out", 0x20000), kw.get("state_out", 0x30000),
+                                 kw.get("flags", 0), None)
 
 
 def test_gated_decode_argument_checks(lib):
@@ -109,6 +110,10 @@ def test_gated_decode_argument_checks(lib):
     p[3] = 0x10002  # fp32 gate projection a not 4-byte aligned
     assert _gated(lib, ptrs=p) == ALIGN
     assert _gated(lib, ptrs=p, gdt=F16) != ALIGN  # fp16 needs only 2-byte alignment: goes on
+    # option bits: RGDR_NORMALIZE_QK (1) is known, any other bit is refused before launch
+    assert _gated(lib, flags=2) == UNSUP
+    assert _gated(lib, flags=0x80000001) == UNSUP
+    assert _gated(lib, ptrs=[None] * 12, B=0, out=None, state_out=None, flags=1) == OK
 
 
 def test_gate_argument_checks(lib):

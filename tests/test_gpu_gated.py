@@ -30,18 +30,19 @@ def gate_tensors(inp, dtype=np.float32):
             torch.from_numpy(inp.dt_bias).cuda(), torch.from_numpy(inp.decay_scale).cuda())
 
 
-def gpu_gated(rg, inp, dtype=np.float32, d=None):
+def gpu_gated(rg, inp, dtype=np.float32, d=None, normalize_qk=False):
     d = d or upload(inp)
     a, b, dt, ds = gate_tensors(inp, dtype)
     pool = d["state"].clone()
     out, st = rg.rgdr_decode_gated(d["query"], d["key"], d["value"], a, b, dt, ds, pool,
                                    d["actual_seq_lengths"], d["ssm_state_indices"], d["gk"],
-                                   d["num_accepted_tokens"], inp.scale)
+                                   d["num_accepted_tokens"], inp.scale,
+                                   normalize_qk=normalize_qk)
     torch.cuda.synchronize()
     return out, st
 
 
-def oracle_gated(inp, entries=None, dtype=np.float32):
+def oracle_gated(inp, entries=None, dtype=np.float32, normalize_qk=False):
     """Oracle chain for the batch entries `entries` (all when None): returns fp64 out
     [n, H_v, T, D_v] and each entry's committed state [n, H_v, D_k, D_v] (NaN if skipped)."""
     sel = np.arange(inp.B) if entries is None else np.asarray(entries)
@@ -60,7 +61,7 @@ def oracle_gated(inp, entries=None, dtype=np.float32):
         oracle.bf16_to_f64(inp.query[sel]), oracle.bf16_to_f64(inp.key[sel]),
         oracle.bf16_to_f64(inp.value[sel]), b64, pool_small, inp.actual_seq_lengths[sel],
         idx_small, g64, inp.gk[sel].astype(np.float64), inp.num_accepted_tokens[sel],
-        float(np.float32(inp.scale)))
+        float(np.float32(inp.scale)), normalize_qk=normalize_qk)
     rows = np.full((len(sel), inp.Hv, inp.Dk, inp.Dv), np.nan)
     rows[valid] = pool_out[idx_small[valid]]
     return out, rows
@@ -161,3 +162,59 @@ def test_gated_matches_unfused_chain(rg):
     assert_tol(bf16_dev_to_f64(out_f), bf16_dev_to_f64(out_u), "fused vs unfused out")
     idx = inp.ssm_state_indices
     assert_tol(bf16_dev_to_f64(st_f)[idx], bf16_dev_to_f64(st_u)[idx], "fused vs unfused state")
+
+
+def raw_qk(inp, seed):
+    """Replace the case's unit-norm q and k by raw projections: each head vector scaled by
+    its own factor in [0.05, 20] (bf16 again), so the unit-norm precondition does not hold."""
+    rng = np.random.default_rng(seed)
+    for name in ("query", "key"):
+        x = oracle.bf16_to_f64(getattr(inp, name))
+        f = rng.uniform(0.05, 20.0, x.shape[:-1] + (1,))
+        setattr(inp, name, workloads.to_bf16_bits(x * f))
+    return inp
+
+
+@pytest.mark.parametrize("shape", [
+    (4, 2, 4, 1, 128, 128, 6),   # wave form, 128-column tiles, D_k = 128
+    (3, 2, 2, 1, 64, 128, 4),    # wave form, D_k = 64
+    (3, 1, 2, 1, 128, 192, 5),   # wave form, 64-column tiles
+    (4, 2, 4, 6, 128, 128, 6),   # workgroup form (T > 1), varlen
+    (3, 2, 2, 8, 64, 192, 4),    # workgroup form, D_k = 64, 64-column tiles
+])
+def test_gated_normalize_qk(rg, shape):
+    """RGDR_NORMALIZE_QK: raw q, k in, the oracle normalises them per token and head (fp64);
+    the kernel's fp32 normalisation must meet the same bar."""
+    B, Hq, Hv, T, Dk, Dv, N = shape
+    say(f"normalize_qk {shape}")
+    inp = raw_qk(workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=91, indices="choice",
+                                     lengths="uniform", gate=True), 92)
+    out, st = gpu_gated(rg, inp, normalize_qk=True)
+    check_gated(inp, out, st, oracle_gated(inp, normalize_qk=True), f"normalize {shape}")
+    # the flag matters: without it the raw magnitudes give a different result
+    out0, _ = gpu_gated(rg, inp)
+    assert not torch.equal(out0, out)
+
+
+def test_gated_normalize_qk_bench_shape_and_zero_vectors(rg):
+    """The bench shape with raw q, k, some of them all-zero (those stay zero: no NaN)."""
+    inp = raw_qk(workloads.make_workload(2, gate_inputs=True), 93)
+    inp.query[3, 5, 0] = 0
+    inp.key[7, 2, 0] = 0
+    inp.key[11, 9, 0] = 0
+    inp.query[11, 9, 0] = 0
+    out, st = gpu_gated(rg, inp, normalize_qk=True)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(st.float()).all()
+    check_gated(inp, out, st, oracle_gated(inp, normalize_qk=True), "normalize bench shape")
+
+
+def test_gated_normalize_qk_is_noop_on_unit_inputs(rg):
+    """On inputs that already have unit-norm q, k (up to their bf16 rounding), the flag
+    changes the result by no more than the bar."""
+    inp = workloads.make_case(4, 2, 4, 3, 128, 128, 6, seed=94, indices="choice",
+                              lengths="uniform", gate=True)
+    out1, st1 = gpu_gated(rg, inp, normalize_qk=True)
+    out0, st0 = gpu_gated(rg, inp)
+    assert_tol(bf16_dev_to_f64(out1), bf16_dev_to_f64(out0), "unit inputs out")
+    idx = inp.ssm_state_indices
+    assert_tol(bf16_dev_to_f64(st1)[idx], bf16_dev_to_f64(st0)[idx], "unit inputs state")
