@@ -23,8 +23,11 @@ Measurement:
     rotation, captured in a graph and timed with events around one replay (the duration
     rocprofv3's kernel trace reports); its roofline uses the method's algorithmic bytes
     per launch. The gate kernel is timed the same way.
-  * cpu_baseline: the fp64 C oracle (single-threaded) repeats the same step on the host
-    for about --cpu-seconds.
+  * copy_reference: a plain 256 MiB device copy (torch elementwise, read + write), timed
+    the same way, as the box's practical streaming rate.
+  * cpu_baseline: the fp64 C oracle repeats the same step on the host for about
+    --cpu-seconds, on one thread and on one thread per host core (batch entries split
+    into contiguous slices, each slice with its own compact copy of its state slots).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -94,6 +97,80 @@ def measured_traffic():
     return int(mt.group(1)) if h.hexdigest() == mh.group(1) else None
 
 
+def cpu_baseline(inp, step_bytes, tok_heads, seconds):
+    """Time the oracle on the host: the whole step (gate, then decode) over the workload,
+    first on one thread, then on one thread per host core. Each thread takes a contiguous
+    slice of batch entries with a compact copy of the state slots they name (prepared before
+    the clock starts); the oracle runs unchanged on each slice (its C calls release the
+    GIL). Each mode repeats the step for about `seconds`."""
+    import concurrent.futures as cf
+    import platform
+
+    import numpy as np
+
+    import oracle
+
+    def slices(n):
+        out = []
+        for bs in np.array_split(np.arange(inp.B), n):
+            if len(bs) == 0:
+                continue
+            idx = inp.ssm_state_indices[bs]
+            valid = (idx >= 0) & (idx < inp.N_slots)
+            pool = inp.state[idx[valid]]
+            if pool.shape[0] == 0:
+                pool = np.zeros((1,) + inp.state.shape[1:], np.uint16)
+            cidx = np.full(len(bs), -1, np.int32)
+            cidx[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+            out.append(dict(a=inp.gate_a[bs], b=inp.gate_b[bs], q=inp.query[bs], k=inp.key[bs],
+                            v=inp.value[bs], gk=inp.gk[bs], lens=inp.actual_seq_lengths[bs],
+                            nacc=inp.num_accepted_tokens[bs], pool=pool, idx=cidx))
+        return out
+
+    def run(sl):
+        d64, b64 = oracle.la_gate(sl["a"], inp.dt_bias, inp.decay_scale, sl["b"])
+        g32 = np.ascontiguousarray(d64.astype(np.float32).transpose(0, 2, 1))
+        beta_bits = np.ascontiguousarray(oracle.f64_to_bf16(b64).transpose(0, 2, 1))
+        oracle.rgdr_bf16(sl["q"], sl["k"], sl["v"], beta_bits, sl["pool"], sl["lens"],
+                         sl["idx"], g32, sl["gk"], sl["nacc"], inp.scale)
+
+    def timed(n):
+        parts = slices(n)
+        t0 = time.perf_counter()
+        reps = 0
+        with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+            while True:
+                list(ex.map(run, parts))
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    return reps, el, len(parts)
+
+    oracle.default()
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    r1, e1, _ = timed(1)
+    log(f"cpu oracle, 1 thread: {r1} steps in {e1:.1f} s")
+    rn, en, used = timed(cores)
+    log(f"cpu oracle, {used} threads: {rn} steps in {en:.1f} s")
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(step_bytes * rn / en / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{rn} full steps of this workload (gate + decode, fp64 C oracle) on "
+                      f"{used} threads in {en:.1f} s, batch entries split into {used} slices",
+            "token_head_steps_per_s": round(tok_heads * rn / en, 1),
+            "single_thread": {"value": round(step_bytes * r1 / e1 / 1e9, 4),
+                              "token_head_steps_per_s": round(tok_heads * r1 / e1, 1),
+                              "sample": f"{r1} full steps on 1 thread in {e1:.1f} s"},
+            "cpu_model": model}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,23 +230,31 @@ def main():
         s["g"] = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
         s["beta"] = torch.empty((B, T, Hv), dtype=torch.bfloat16, device=dev)
         s["out"] = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=dev)
+        if T != 1:
+            s["gT"] = torch.empty((B, Hv, T), dtype=torch.float32, device=dev)
+            s["betaT"] = torch.empty((B, Hv, T), dtype=torch.bfloat16, device=dev)
         sets.append(s)
     del base
     torch.cuda.synchronize()
 
     # g and beta come out of the gate as [B, T, H_v]; the decode reads [B, H_v, T]. With
-    # T = 1 these are the same bytes; otherwise the step would need the fused gate.
+    # T = 1 these are the same bytes. For T > 1 the unfused chain transposes them with torch
+    # (part of the chain's time), while the decode kernel's own timing reads copies that
+    # were transposed once beforehand.
     if T != 1:
-        log("note: T > 1; the gate output layout differs from the decode's, so the step "
-            "transposes g/beta with torch (not timed as part of the kernels)")
+        log("note: T > 1; the unfused chain transposes g/beta with torch between its kernels")
 
     def gate(s):
         rg.la_gate(s["a"], dt, ds, s["b"], decay_dtype=torch.float32,
                    beta_dtype=torch.bfloat16, decay_out=s["g"], beta_out=s["beta"])
 
+    def transpose(s):
+        s["gT"].copy_(s["g"].transpose(1, 2))
+        s["betaT"].copy_(s["beta"].transpose(1, 2))
+
     def decode(s):
-        g_ = s["g"].view(B, Hv, T) if T == 1 else s["g"].transpose(1, 2).contiguous()
-        be = s["beta"].view(B, Hv, T) if T == 1 else s["beta"].transpose(1, 2).contiguous()
+        g_ = s["g"].view(B, Hv, T) if T == 1 else s["gT"]
+        be = s["beta"].view(B, Hv, T) if T == 1 else s["betaT"]
         rg.rgdr_decode(s["q"], s["k"], s["v"], be, s["pool"], lens, idx, g_, s["gk"], nacc,
                        inp.scale, out=s["out"])
 
@@ -183,6 +268,8 @@ def main():
     def unfused_step(i):
         s = sets[i % R]
         gate(s)
+        if T != 1:
+            transpose(s)
         decode(s)
 
     def copy_calibration():
@@ -267,6 +354,30 @@ def main():
     log(f"fused decode kernel: {fused_us:.2f} us per launch; unfused: decode {dec_us:.2f} us, "
         f"gate {gate_us:.2f} us")
 
+    # The box's practical streaming rate: a plain 256 MiB copy (read + write), graph-timed.
+    csrc = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    cg = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(cg, stream=cs):
+            for _ in range(20):
+                torch.mul(csrc, 1.0, out=cdst)
+    stream.wait_stream(cs)
+    cg.replay()
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    cg.replay()
+    c1.record(stream)
+    c1.synchronize()
+    copy_us = c0.elapsed_time(c1) * 1e3 / 20
+    copy_gbs = 2 * csrc.numel() * 4 / (copy_us * 1e-6) / 1e9
+    del cg, csrc, cdst
+    log(f"copy reference: 256 MiB read + 256 MiB write in {copy_us:.1f} us ({copy_gbs:.0f} GB/s)")
+
     if args.copy_calibration:
         copy_calibration()
 
@@ -277,26 +388,8 @@ def main():
     traffic = measured_traffic() if wid == 2 else None
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            d64, b64 = oracle.la_gate(inp.gate_a, inp.dt_bias, inp.decay_scale, inp.gate_b)
-            g32 = np.ascontiguousarray(d64.astype(np.float32).transpose(0, 2, 1))
-            beta_bits = np.ascontiguousarray(oracle.f64_to_bf16(b64).transpose(0, 2, 1))
-            oracle.rgdr_bf16(inp.query, inp.key, inp.value, beta_bits, inp.state,
-                             inp.actual_seq_lengths, inp.ssm_state_indices, g32, inp.gk,
-                             inp.num_accepted_tokens, inp.scale)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds and reps >= 1:
-                break
-        cpu = {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{reps} full steps of this workload (gate + decode, fp64 C oracle, "
-                         f"one thread) in {el:.1f} s",
-               "token_head_steps_per_s": round(tok_heads * reps / el, 1)}
-        log(f"cpu oracle: {reps} steps in {el:.1f} s")
+        cpu = cpu_baseline(inp, step_bytes, tok_heads, args.cpu_seconds)
+    n_pairs = int(((inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < N)).sum()) * Hv
 
     rec = {
         "metric": METRIC,
@@ -319,6 +412,9 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "token_head_steps_per_s": round(steps_per_s, 1),
         "step_bytes": step_bytes,
+        "bytes_per_state_element": round(step_bytes / (n_pairs * Dk * Dv), 4),
+        "copy_reference": {"gbs": round(copy_gbs, 1), "us": round(copy_us, 2),
+                           "what": "torch elementwise copy, 256 MiB read + 256 MiB write"},
         "roofline": {"kernel": "rgdr_decode_gated", "bound": "hbm",
                      "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
