@@ -20,8 +20,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
+// Two values, one instruction (v_cvt_pk_bf16_f32 with both sources), lo in the low half.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Gate arithmetic ("com.microsoft.LinearAttentionGate" README, Description), fp32:

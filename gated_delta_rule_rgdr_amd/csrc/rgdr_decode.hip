@@ -92,6 +92,15 @@ constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 #ifndef RGDR_WAVE_CHUNK_DIV
 #define RGDR_WAVE_CHUNK_DIV 1
 #endif
+// 1 < T <= 8: 1 = the multi-token wave form, 0 = the workgroup form; the multi-token wave
+// form launches at most the resident grid at a time when RGDR_MULTI_CHUNKED is 1, else all
+// items at once (the hardware starts waves as slots free up).
+#ifndef RGDR_MULTI_WAVE
+#define RGDR_MULTI_WAVE 1
+#endif
+#ifndef RGDR_MULTI_CHUNKED
+#define RGDR_MULTI_CHUNKED 0
+#endif
 
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -905,6 +914,117 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Wave form for 1 < T <= 8: one wave owns one (b, h, TV-column) tile over all D_k rows and
+// keeps it in fp32 registers through the tokens (R rows x 8 columns per lane, 128 values at
+// most); per token the D_k reduction finishes inside the wave (in-lane over the lane's rows,
+// then lane swaps), so there is no barrier and no LDS exchange. The operands of all of the
+// item's tokens are staged once in the wave's LDS area. One item per wave: a launch covers
+// at most as many items as fit on the device at once.
+// ---------------------------------------------------------------------------------------
+template <int DK, int TV, int GATE>
+__global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_kernel(
+    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nacc) {
+    using Sh = TileShape<DK, TV, 64, kMaxT>;
+    constexpr int LPR = Sh::LPR, RPP = Sh::RPP, R = Sh::R;
+    static_assert(R * Sh::CPL <= 128, "fp32 tile per lane");
+    __shared__ f32x4 lds4[Sh::OPS / 4];
+    float *ob = reinterpret_cast<float *>(lds4);
+    const Index x{lens, idx, nacc};
+    const int lane = threadIdx.x;
+    const int cg = lane % LPR, rg = lane / LPR;
+    const Item m = resolve(a, x, a.item0 + blockIdx.x);
+
+    Ops<DK, TV, 64, kMaxT> o;
+    load_ops<DK, TV, 64, kMaxT, GATE>(a, m, o, lane);
+    u32x4 raw[R];
+    load_state<DK, TV, 64>(a, m, raw, rg, cg);
+    stage_ops<DK, TV, 64, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, lane);
+
+    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
+                               tile_range<DK, TV>(a, m));
+    const uint32_t lane_off = (uint32_t)((rg * a.Dv + cg * 8) * 2);
+    const uint32_t row_step = (uint32_t)(RPP * a.Dv * 2);
+    if (m.n == 0) {  // nothing accepted: commit the incoming bytes
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            __builtin_amdgcn_raw_buffer_store_b128(raw[r], rso, lane_off, r * row_step,
+                                                   RGDR_STATE_STORE_POLICY);
+    }
+    float S[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            S[r][2 * j] = bf16_lo(w[j]);
+            S[r][2 * j + 1] = bf16_hi(w[j]);
+        }
+    }
+    const size_t bh = (size_t)m.b * a.Hv + m.h;
+    const auto rout = make_rsrc(a.out + bh * a.T * a.Dv, (uint32_t)(a.T * a.Dv * 2));
+    const uint32_t ocol = (uint32_t)((m.tile * TV + cg * 8) * 2);
+    for (int t = 0; t < m.L; ++t) {
+        const float *tb = ob + t * Sh::TOK;
+        // Step 1 (decay) fused with the partial sums of steps 2 and 4.
+        float pk[8], pq[8];
+        float kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pk[c] = pq[c] = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const f32x4 dkq = *reinterpret_cast<const f32x4 *>(tb + 4 * (rg + RPP * r));
+            kq = fmaf(dkq.y, dkq.z, kq);
+            const float dk = dkq.x * dkq.y, dq = dkq.x * dkq.z;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                pk[c] = fmaf(S[r][c], dk, pk[c]);
+                pq[c] = fmaf(S[r][c], dq, pq[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            pk[c] = colsum<LPR>(pk[c]);
+            pq[c] = colsum<LPR>(pq[c]);
+        }
+        kq = colsum<LPR>(kq);
+        const f32x4 *vv = reinterpret_cast<const f32x4 *>(tb + 4 * DK + cg * 8);
+        const f32x4 v0 = vv[0], v1 = vv[1];
+        const float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const float bt = tb[4 * DK + TV];
+        // Step 3 (delta update) and step 4 (output with the updated state).
+        float u[8], ov[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u[c] = bt * (V[c] - pk[c]);
+            ov[c] = fmaf(kq, u[c], pq[c]);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]),
+                  pack_bf16x2(ov[4], ov[5]), pack_bf16x2(ov[6], ov[7])},
+            rout, rg == 0 ? (uint32_t)(t * a.Dv * 2) + ocol : 0x7FFFFFF0u, 0, 0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const f32x4 dkq = *reinterpret_cast<const f32x4 *>(tb + 4 * (rg + RPP * r));
+#pragma unroll
+            for (int c = 0; c < 8; ++c) S[r][c] = fmaf(dkq.y, u[c], S[r][c] * dkq.x);
+        }
+        if (t + 1 == m.n) {  // the accepted prefix ends here: commit
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{pack_bf16x2(S[r][0], S[r][1]), pack_bf16x2(S[r][2], S[r][3]),
+                          pack_bf16x2(S[r][4], S[r][5]), pack_bf16x2(S[r][6], S[r][7])},
+                    rso, lane_off, r * row_step, RGDR_STATE_STORE_POLICY);
+        }
+    }
+    for (int t = m.L; t < a.T; ++t)  // padded (or skipped) tokens: +0.0 rows
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{0u, 0u, 0u, 0u}, rout, rg == 0 ? (uint32_t)(t * a.Dv * 2) + ocol : 0x7FFFFFF0u,
+            0, 0);
+}
+
 // Workgroups that fit on the device at once (CUs x resident per CU), per device, queried once.
 template <int DK, int TV, int NT, int NBUF, int GATE>
 static int resident_grid() {
@@ -976,12 +1096,50 @@ static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const in
     return hipGetLastError();
 }
 
+template <int DK, int TV, int GATE>
+static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
+                                    const int32_t *idx, const int32_t *nacc,
+                                    hipStream_t stream) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cached[dev] <= 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            return hipErrorInvalidDevice;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, decode_wave_multi_kernel<DK, TV, GATE>, 64, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        cached[dev] = cus * per_cu;
+    }
+    const int chunk = RGDR_MULTI_CHUNKED ? cached[dev] : a.n_items;
+    DecodeArgs c = a;
+    for (int first = 0; first < a.n_items; first += chunk) {
+        c.item0 = first;
+        c.n_items = a.n_items - first < chunk ? a.n_items : first + chunk;
+        hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE>), dim3(c.n_items - first),
+                           dim3(64), 0, stream, c, lens, idx, nacc);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Shape/alignment checks shared by both entry points, then the launch of the form T picks.
+enum Form { kFormWave = 0, kFormWaveMulti = 1, kFormWorkgroup = 2 };
+
 template <int GATE>
-static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, bool wave_form,
+static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
                            const int32_t *L, const int32_t *I, const int32_t *N,
                            hipStream_t stream) {
-    if (wave_form) {
+    if (form == kFormWaveMulti) {
+        if (D_k == 128) return launch_wave_multi<128, 64, GATE>(a, L, I, N, stream);
+        return tile_v == 128 ? launch_wave_multi<64, 128, GATE>(a, L, I, N, stream)
+                             : launch_wave_multi<64, 64, GATE>(a, L, I, N, stream);
+    }
+    if (form == kFormWave) {
         if (tile_v == 128)
             return D_k == 128 ? launch_wave<128, 128, GATE>(a, L, I, N, stream)
                               : launch_wave<64, 128, GATE>(a, L, I, N, stream);
@@ -1007,9 +1165,14 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const bool wave_form = T == 1;
-    const int tile_v = wave_form ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
-                                 : ((D_v % 128 != 0 || RGDR_DECODE_TILE_V == 64) ? 64 : 128);
+    const Form form = T == 1 ? kFormWave : (RGDR_MULTI_WAVE ? kFormWaveMulti : kFormWorkgroup);
+    // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token wave
+    // form the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
+    const int tile_v = form == kFormWave
+                           ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
+                       : form == kFormWaveMulti
+                           ? ((D_k == 64 && D_v % 128 == 0) ? 128 : 64)
+                           : ((D_v % 128 != 0 || RGDR_DECODE_TILE_V == 64) ? 64 : 128);
     const long long items = (long long)B * H_v * (D_v / tile_v);
     if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
     a.Hq = H_q;
@@ -1022,11 +1185,11 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
     a.n_items = (int)items;
     hipError_t err;
     if (gate == kGateGiven)
-        err = dispatch<kGateGiven>(a, D_k, tile_v, wave_form, lens, idx, nacc, stream);
+        err = dispatch<kGateGiven>(a, D_k, tile_v, form, lens, idx, nacc, stream);
     else if (gate == kGateF32)
-        err = dispatch<kGateF32>(a, D_k, tile_v, wave_form, lens, idx, nacc, stream);
+        err = dispatch<kGateF32>(a, D_k, tile_v, form, lens, idx, nacc, stream);
     else
-        err = dispatch<kGateF16>(a, D_k, tile_v, wave_form, lens, idx, nacc, stream);
+        err = dispatch<kGateF16>(a, D_k, tile_v, form, lens, idx, nacc, stream);
     return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
 }
 
