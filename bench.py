@@ -75,19 +75,24 @@ def fused_bytes(inp, decode_b, tok_heads):
 
 KERNEL_SOURCES = ("gated_delta_rule_rgdr_amd/csrc/rgdr_decode.hip",
                   "gated_delta_rule_rgdr_amd/csrc/rgdr_common.h")
-TRAFFIC_PROFILE = "profiles/rgdr_decode_b64_gqa_d128.md"
+TRAFFIC_PROFILES = {2: "profiles/rgdr_decode_b64_gqa_d128.md",
+                    3: "profiles/rgdr_decode_varlen_b32_t8_d128.md",
+                    4: "profiles/rgdr_decode_b256_gqa_d128.md"}
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
-    when the decode kernel's sources have changed since those counters were taken."""
+def measured_traffic(wid=2):
+    """HBM bytes per fused call from the committed rocprofv3 counter summary of workload
+    `wid`, or None when there is none or the decode kernel's sources have changed since
+    those counters were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if wid not in TRAFFIC_PROFILES:
+        return None
+    path = os.path.join(ROOT, TRAFFIC_PROFILES[wid])
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    mt = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    mt = re.search(r"^traffic_bytes_per_call:\s*(\d+)", text, re.M)
     mh = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})", text, re.M)
     if not (mt and mh):
         return None
@@ -385,7 +390,7 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     steps_per_s = tok_heads / (ms_per_step * 1e-3)
 
-    traffic = measured_traffic() if wid == 2 else None
+    traffic = measured_traffic(wid)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, step_bytes, tok_heads, args.cpu_seconds)

@@ -184,6 +184,20 @@ struct TileShape {
     static constexpr int LDS_FLOATS = 2 * OPS + 2 * EX;
 };
 
+// Workgroups are handed to the device's 8 XCDs (each with its own L2) round-robin by
+// workgroup id. Remapped, each XCD works through one contiguous range of items instead, so
+// items that share operands (the D_v tiles of one head; value heads that share a query/key
+// head) meet in the same L2. A bijection of [0, grid) for any grid size.
+#ifndef RGDR_XCD_REMAP
+#define RGDR_XCD_REMAP 1
+#endif
+__device__ __forceinline__ int xcd_item(int blk, int grid) {
+    if (!RGDR_XCD_REMAP) return blk;
+    constexpr int kXcd = 8;
+    const int q = grid / kXcd, r = grid % kXcd, x = blk % kXcd;
+    return x * q + (x < r ? x : r) + blk / kXcd;
+}
+
 // The per-entry index arrays. They are only read, never written by the kernel; passing them
 // as separate restrict-qualified kernel arguments lets the compiler read them with scalar
 // loads, which do not count against the vector memory counter the state stream uses.
@@ -902,7 +916,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     const int lane = threadIdx.x;
     const int cg = lane % Sh::LPW, rg = lane / Sh::LPW;
     const int G = gridDim.x;
-    int it = a.item0 + blockIdx.x;
+    int it = a.item0 + xcd_item(blockIdx.x, gridDim.x);
     WavePipe<DK, TVW, NBUF> pl;
     // Operands first: staging them waits only for them, while the tile is still in flight.
     wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it), pl.ops[0], lane);
@@ -934,7 +948,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
     const Index x{lens, idx, nacc};
     const int lane = threadIdx.x;
     const int cg = lane % LPR, rg = lane / LPR;
-    const Item m = resolve(a, x, a.item0 + blockIdx.x);
+    const Item m = resolve(a, x, a.item0 + xcd_item(blockIdx.x, gridDim.x));
 
     Ops<DK, TV, 64, kMaxT> o;
     load_ops<DK, TV, 64, kMaxT, GATE>(a, m, o, lane);
