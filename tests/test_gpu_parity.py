@@ -131,6 +131,35 @@ def test_shapes(rg, shape):
 
 
 # ---------------------------------------------------------------------------------------
+# Decays far from 1 over several tokens. The multi-token kernel keeps each tile as
+# diag(c) St with c the decay not yet applied, and folds c into St when c would leave
+# [2^-64, 2^64]; the oracle applies every decay directly in fp64.
+# ---------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("Dk", [128, 64])
+@pytest.mark.parametrize("case", ["strong_decay", "growth", "zero_decay", "mixed_rows"])
+def test_extreme_decays(rg, case, Dk):
+    rng = np.random.default_rng(61)
+    inp = workloads.make_case(4, 2, 4, 8, Dk, 128, 6, seed=62, indices="choice",
+                              lengths=[8, 5, 8, 3])
+    inp.num_accepted_tokens = np.array([8, 5, 6, 3], np.int32)  # one early commit
+    if case == "strong_decay":    # c falls below 2^-64 every other token
+        inp.g[:] = -30.0
+    elif case == "growth":        # c passes 2^64 after six tokens
+        inp.g[:] = 8.0
+    elif case == "zero_decay":    # exp(g) is exactly 0 at token 3: the state is wiped
+        inp.g[:] = -1.0
+        inp.g[:, :, 3] = -1000.0
+    else:                         # every row on its own path
+        inp.g[:] = rng.uniform(-25.0, 5.0, inp.g.shape).astype(np.float32)
+        inp.gk[:] = -rng.uniform(0.0, 12.0, inp.gk.shape).astype(np.float32)
+    say(f"extreme decays: {case}, D_k {Dk}")
+    out, st = gpu_decode(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"extreme {case} Dk{Dk}")
+
+
+# ---------------------------------------------------------------------------------------
 # Indexing semantics, bit for bit
 # ---------------------------------------------------------------------------------------
 
