@@ -4,8 +4,8 @@
 // section (decay, memory read, delta update, output, token by token) and parameter list.
 //
 // The step is HBM-bound: each (batch entry, value head) pair streams its D_k x D_v bf16
-// state in once and out once; everything else is small. Two kernel forms share the
-// plumbing below; T decides which one runs.
+// state in once and out once; everything else is small. Two wave-level kernel forms share
+// the plumbing below; T decides which one runs.
 //
 // Wave form (T = 1, every decode workload). One wave owns one (b, h, 128- or 64-column)
 // tile over all D_k rows:
@@ -17,13 +17,14 @@
 //   * the D_k reduction finishes inside the wave (in-lane over the lane's rows, then
 //     v_permlane16/32_swap and a DPP row rotate), so waves need no LDS exchange and no
 //     barrier and run independently; operands sit in a wave-private LDS area;
-//   * waves are persistent over items (w, w + G, ...) with a ring of packed tiles; items
-//     past the end and skipped entries use empty buffer ranges (no data moves).
+//   * one item per wave per launch (a call with more items than resident waves becomes
+//     several launches); items past the end and skipped entries use empty buffer ranges
+//     (no data moves).
 //
-// Workgroup form (1 < T <= 8). One 256-thread workgroup owns one (b, h, tile) and keeps it
-// in fp32 registers across the tokens; the next item's state and operands are in flight
-// while the current item is computed; per token the D_k reduction ends with a fixed-order
-// sum over the waves through a double-buffered LDS slot (one barrier per token).
+// Multi-token form (1 < T <= 8). One wave owns one (b, h, 64- or 128-column) tile and keeps
+// it in fp32 registers across the tokens, in a scaled form that leaves three FMAs per
+// element and token (see decode_wave_multi_kernel); the D_k reduction also finishes inside
+// the wave.
 //
 // Both forms: per token, steps 2 and 4 share ONE reduction over D_k. With S' the decayed
 // state, p = S'^T k and r = S'^T (scale q) are reduced together with the scalar
@@ -40,22 +41,6 @@ namespace rgdr {
 
 constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 
-// Launch shape (compile-time tuning knobs): threads per workgroup, the D_v tile width
-// (0 = 128 columns when D_v allows it, else 64), and the number of state tiles in flight
-// per workgroup (1 to 3).
-#ifndef RGDR_DECODE_THREADS
-#define RGDR_DECODE_THREADS 256
-#endif
-#ifndef RGDR_DECODE_TILE_V
-#define RGDR_DECODE_TILE_V 0
-#endif
-#ifndef RGDR_DECODE_DEPTH
-#define RGDR_DECODE_DEPTH 1
-#endif
-// Minimum waves per SIMD the register allocation must allow (occupancy floor).
-#ifndef RGDR_DECODE_MIN_WAVES
-#define RGDR_DECODE_MIN_WAVES 2
-#endif
 // Wave form (T = 1): ring length per tile width, and its grid: 0 = as many waves as fit at
 // once (persistent), 1 = one wave per item.
 #ifndef RGDR_WAVE_NBUF
@@ -92,12 +77,8 @@ constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 #ifndef RGDR_WAVE_CHUNK_DIV
 #define RGDR_WAVE_CHUNK_DIV 1
 #endif
-// 1 < T <= 8: 1 = the multi-token wave form, 0 = the workgroup form; the multi-token wave
-// form launches at most the resident grid at a time when RGDR_MULTI_CHUNKED is 1, else all
-// items at once (the hardware starts waves as slots free up).
-#ifndef RGDR_MULTI_WAVE
-#define RGDR_MULTI_WAVE 1
-#endif
+// Multi-token form: 1 = launch at most the resident grid at a time, 0 = all items at once
+// (the hardware starts waves as slots free up).
 #ifndef RGDR_MULTI_CHUNKED
 #define RGDR_MULTI_CHUNKED 0
 #endif
@@ -176,9 +157,8 @@ template <int DK, int TV, int NT, int TMAX = kMaxT>
 struct TileShape {
     static constexpr int CPL = 8;         // columns per lane: one 16-byte bf16 vector
     static constexpr int LPR = TV / CPL;  // lanes across one tile row
-    static constexpr int RPP = NT / LPR;  // tile rows covered per pass of the workgroup
+    static constexpr int RPP = NT / LPR;  // tile rows covered per pass of the NT threads
     static constexpr int R = DK / RPP;    // rows held by each thread
-    static constexpr int NW = NT / 64;    // waves per workgroup
     static_assert(NT % 64 == 0 && 64 % LPR == 0 && DK % RPP == 0 && R >= 1, "tile shape");
     static_assert(LPR == 8 || LPR == 16, "lane reduction handles 64- and 128-wide tiles");
     // Per-thread operand vectors of one item (up to TMAX tokens).
@@ -186,12 +166,10 @@ struct TileShape {
     static constexpr int KQV = (TMAX * DK / 8 + NT - 1) / NT;  // 8 x bf16 of k (and of q)
     static constexpr int VV = (TMAX * TV / 8 + NT - 1) / NT;   // 8 x bf16 of the v tile
     static_assert(NT >= TMAX, "one thread per token for beta");
-    // LDS, in floats. Per token: rows[DK] of (decay, k, scale*q, 0) | v[TV] | beta, pad.
+    // LDS, in floats. Per token: rows[DK] of (decay, k, scale*q, .) | v[TV] | beta and
+    // three scalars of the multi-token form.
     static constexpr int TOK = 4 * DK + TV + 4;
-    static constexpr int OPS = TMAX * TOK;   // one operand buffer; two are used
-    static constexpr int EXW = 2 * TV + 4;   // reduction exchange per wave: p[TV] r[TV] kq
-    static constexpr int EX = NW * EXW;      // one exchange buffer; two are used
-    static constexpr int LDS_FLOATS = 2 * OPS + 2 * EX;
+    static constexpr int OPS = TMAX * TOK;  // the operands of all tokens of one item
 };
 
 // Workgroups are handed to the device's 8 XCDs (each with its own L2) round-robin by
@@ -217,7 +195,7 @@ struct Index {
     const int32_t *__restrict__ nacc;
 };
 
-// Everything about one work item that is uniform across the workgroup.
+// Everything about one work item that is uniform across the wave.
 struct Item {
     int b, h, hq, tile, slot, L, n;
     bool state;  // a live item whose slot is in range: its state is read and committed
@@ -372,7 +350,7 @@ __device__ __forceinline__ void stage_ops(const Ops<DK, TV, NT, TMAX> &o, float 
         const uint32_t qw[4] = {o.q[j].x, o.q[j].y, o.q[j].z, o.q[j].w};
         float ks = 1.f, qs = scale;
         if constexpr (GATE != kGateGiven) {
-            if (norm) {  // uniform: the whole workgroup takes it
+            if (norm) {  // uniform: the whole wave takes it
                 // One token's head vector lies in DK/8 consecutive, aligned lanes.
                 float kss = 0.f, qss = 0.f;
 #pragma unroll
@@ -440,228 +418,6 @@ __device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
     for (int r = 0; r < Sh::R; ++r)
         raw[r] = __builtin_amdgcn_raw_buffer_load_b128(
             rs, (uint32_t)(((rg + r * Sh::RPP) * a.Dv + cg * 8) * 2), 0, kCacheNT);
-}
-
-template <int DK, int TV, int NT, int NBUF, int TMAX>
-struct Pipeline {
-    using Sh = TileShape<DK, TV, NT, TMAX>;
-    u32x4 raw[NBUF][Sh::R];        // state tiles in flight (ring)
-    Ops<DK, TV, NT, TMAX> ops[2];  // operands of the current and the next item
-};
-
-// One token on the thread's part of the state: step 1 (decay) fused with the partial sums
-// of steps 2 and 4, the reduction over D_k, then step 3 (update). Leaves in o the output
-// columns of this thread (every row group holds them). `exb` is this token's exchange
-// buffer; the one barrier inside must be reached by the whole workgroup.
-template <int DK, int TV, int NT, int R>
-__device__ __forceinline__ void token_step(float (&S)[R][8], const float *tok, float *exb,
-                                           int tid, float (&o)[8]) {
-    using Sh = TileShape<DK, TV, NT>;
-    static_assert(R == Sh::R, "rows per thread");
-    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, NW = Sh::NW;
-    const int lane = tid & 63, wave = tid >> 6, cg = tid % LPR, rg = tid / LPR;
-    float pk[CPL], pq[CPL], kr[R];
-    float kq = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) pk[c] = pq[c] = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const f32x4 dkq = *reinterpret_cast<const f32x4 *>(tok + 4 * (rg + r * RPP));
-        const float d = dkq.x, kk = dkq.y, qq = dkq.z;
-        kr[r] = kk;
-        kq = fmaf(kk, qq, kq);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float s = S[r][c] * d;
-            S[r][c] = s;
-            pk[c] = fmaf(s, kk, pk[c]);
-            pq[c] = fmaf(s, qq, pq[c]);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        pk[c] = colsum<LPR>(pk[c]);
-        pq[c] = colsum<LPR>(pq[c]);
-    }
-    kq = colsum<LPR>(kq);
-    if (lane < LPR) {
-        f32x4 *dp = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + cg * CPL);
-        dp[0] = f32x4{pk[0], pk[1], pk[2], pk[3]};
-        dp[1] = f32x4{pk[4], pk[5], pk[6], pk[7]};
-        f32x4 *dq = reinterpret_cast<f32x4 *>(exb + wave * Sh::EXW + TV + cg * CPL);
-        dq[0] = f32x4{pq[0], pq[1], pq[2], pq[3]};
-        dq[1] = f32x4{pq[4], pq[5], pq[6], pq[7]};
-        if (lane == 0) exb[wave * Sh::EXW + 2 * TV] = kq;
-    }
-    __syncthreads();
-    f32x4 P0 = {0.f, 0.f, 0.f, 0.f}, P1 = P0, Q0 = P0, Q1 = P0;
-    float KQ = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const f32x4 *sp = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + cg * CPL);
-        const f32x4 *sq = reinterpret_cast<const f32x4 *>(exb + w * Sh::EXW + TV + cg * CPL);
-        P0 += sp[0];
-        P1 += sp[1];
-        Q0 += sq[0];
-        Q1 += sq[1];
-        KQ += exb[w * Sh::EXW + 2 * TV];
-    }
-    const float Pv[CPL] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
-    const float Qv[CPL] = {Q0.x, Q0.y, Q0.z, Q0.w, Q1.x, Q1.y, Q1.z, Q1.w};
-    const f32x4 *vv = reinterpret_cast<const f32x4 *>(tok + 4 * DK + cg * CPL);
-    const f32x4 v0 = vv[0], v1 = vv[1];
-    const float V[CPL] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const float bt = tok[4 * DK + TV];
-    float u[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        u[c] = bt * (V[c] - Pv[c]);
-        o[c] = fmaf(KQ, u[c], Qv[c]);  // = S_new^T (scale q) on these columns
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) S[r][c] = fmaf(kr[r], u[c], S[r][c]);
-}
-
-// Every item issues the same sequence of vector memory instructions whatever its lengths
-// and slot (empty buffer ranges drop the accesses that must not happen), so the counter
-// waits the compiler places before the next item's first use of its prefetched data stay
-// exact and never wait on this item's stores.
-
-// Output rows of one (b, h): row group 0 writes its 8 columns, the other lanes aim past the
-// range (their stores are dropped).
-struct OutRows {
-    __amdgpu_buffer_rsrc_t rs;
-    uint32_t off;
-    bool writer;
-};
-
-template <int TV>
-__device__ __forceinline__ OutRows out_rows(const DecodeArgs &a, const Item &m, int cg, int rg) {
-    const size_t bhT = ((size_t)m.b * a.Hv + m.h) * a.T;
-    OutRows r;
-    r.rs = make_rsrc(a.out + bhT * a.Dv, (uint32_t)(a.T * a.Dv * 2));
-    r.writer = rg == 0;
-    r.off = (uint32_t)((m.tile * TV + cg * 8) * 2);
-    return r;
-}
-
-__device__ __forceinline__ void store_out_row(const DecodeArgs &a, const OutRows &w, int t,
-                                              const float (&o)[8]) {
-    u32x4 v;
-    v.x = pack_bf16x2(o[0], o[1]);
-    v.y = pack_bf16x2(o[2], o[3]);
-    v.z = pack_bf16x2(o[4], o[5]);
-    v.w = pack_bf16x2(o[6], o[7]);
-    __builtin_amdgcn_raw_buffer_store_b128(
-        v, w.rs, w.writer ? w.off + (uint32_t)(t * a.Dv * 2) : 0x7FFFFFF0u, 0, 0);
-}
-
-// General form (T > 1): the tile is widened to fp32 registers once and kept there across
-// the tokens. Loop phase P. Returns false when the workgroup has no item left.
-template <int DK, int TV, int NT, int NBUF, int GATE, int P>
-__device__ __forceinline__ bool process_multi(const DecodeArgs &a, const Index &x,
-                                              Pipeline<DK, TV, NT, NBUF, kMaxT> &pl, float *lds,
-                                              int &it, int &xc, int tid) {
-    using Sh = TileShape<DK, TV, NT, kMaxT>;
-    constexpr int CPL = Sh::CPL, LPR = Sh::LPR, RPP = Sh::RPP, R = Sh::R;
-    if (it >= a.n_items) return false;
-    const int G = gridDim.x;
-    const int cg = tid % LPR, rg = tid / LPR;
-    const Item m = resolve(a, x, it);
-
-    // Operands of the next item go in flight; this item's are staged in LDS.
-    load_ops<DK, TV, NT, kMaxT, GATE>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], tid);
-    float *ob = lds + (P & 1) * Sh::OPS;
-    stage_ops<DK, TV, NT, kMaxT, GATE>(pl.ops[P & 1], ob, a.scale, a.norm_qk != 0, tid);
-    __syncthreads();
-
-    float S[R][CPL];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const u32x4 w = pl.raw[P % NBUF][r];
-        S[r][0] = bf16_lo(w.x); S[r][1] = bf16_hi(w.x);
-        S[r][2] = bf16_lo(w.y); S[r][3] = bf16_hi(w.y);
-        S[r][4] = bf16_lo(w.z); S[r][5] = bf16_hi(w.z);
-        S[r][6] = bf16_lo(w.w); S[r][7] = bf16_hi(w.w);
-    }
-    // The ring slot just widened receives the state of the item NBUF ahead.
-    load_state<DK, TV, NT>(a, resolve(a, x, it + NBUF * G), pl.raw[P % NBUF], rg, cg);
-
-    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
-                               tile_range<DK, TV>(a, m));
-    auto commit = [&]() {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            u32x4 w;
-            w.x = pack_bf16x2(S[r][0], S[r][1]);
-            w.y = pack_bf16x2(S[r][2], S[r][3]);
-            w.z = pack_bf16x2(S[r][4], S[r][5]);
-            w.w = pack_bf16x2(S[r][6], S[r][7]);
-            __builtin_amdgcn_raw_buffer_store_b128(
-                w, rso, (uint32_t)(((rg + r * RPP) * a.Dv + cg * CPL) * 2), 0, kCacheNT);
-        }
-    };
-    const OutRows orow = out_rows<TV>(a, m, cg, rg);
-    float *ex = lds + 2 * Sh::OPS;
-    float o[CPL];
-    if (m.n == 0) commit();
-    for (int t = 0; t < m.L; ++t) {
-        float *exb = ex + (xc & 1) * Sh::EX;
-        ++xc;
-        token_step<DK, TV, NT, R>(S, ob + t * Sh::TOK, exb, tid, o);
-        store_out_row(a, orow, t, o);
-        if (t + 1 == m.n) commit();
-    }
-    // Padded tokens and skipped entries: +0.0 output rows.
-    const float zero[CPL] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = m.L; t < a.T; ++t) store_out_row(a, orow, t, zero);
-    it += G;
-    return true;
-}
-
-// Phases P .. U-1 of the unrolled item loop; false once the workgroup has no item left.
-template <int DK, int TV, int NT, int NBUF, int GATE, int P, int U>
-__device__ __forceinline__ bool run_phases(const DecodeArgs &a, const Index &x,
-                                           Pipeline<DK, TV, NT, NBUF, kMaxT> &pl, float *lds,
-                                           int &it, int &xc, int tid) {
-    if constexpr (P == U) {
-        return true;
-    } else {
-        return process_multi<DK, TV, NT, NBUF, GATE, P>(a, x, pl, lds, it, xc, tid) &&
-               run_phases<DK, TV, NT, NBUF, GATE, P + 1, U>(a, x, pl, lds, it, xc, tid);
-    }
-}
-
-template <int DK, int TV, int NT, int NBUF, int GATE>
-__global__ __launch_bounds__(NT, RGDR_DECODE_MIN_WAVES) void decode_kernel(const DecodeArgs a,
-                                                       const int32_t *__restrict__ lens,
-                                                       const int32_t *__restrict__ idx,
-                                                       const int32_t *__restrict__ nacc) {
-    constexpr int TMAX = kMaxT;
-    using Sh = TileShape<DK, TV, NT, TMAX>;
-    const Index x{lens, idx, nacc};
-    __shared__ f32x4 lds4[Sh::LDS_FLOATS / 4];
-    float *lds = reinterpret_cast<float *>(lds4);
-    const int tid = threadIdx.x;
-    const int cg = tid % Sh::LPR, rg = tid / Sh::LPR;
-    const int G = gridDim.x;
-    int it = blockIdx.x;
-    int xc = 0;
-    Pipeline<DK, TV, NT, NBUF, TMAX> pl;
-    // Prologue: state of the first item, operands of the first item, state of the next
-    // NBUF-1 items.
-    load_state<DK, TV, NT>(a, resolve(a, x, it), pl.raw[0], rg, cg);
-    load_ops<DK, TV, NT, TMAX, GATE>(a, resolve(a, x, it), pl.ops[0], tid);
-#pragma unroll
-    for (int j = 1; j < NBUF; ++j)
-        load_state<DK, TV, NT>(a, resolve(a, x, it + j * G), pl.raw[j], rg, cg);
-    // Item loop, unrolled over the ring and the two operand buffers, so that every buffer
-    // index is a compile-time constant.
-    constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
-    while (run_phases<DK, TV, NT, NBUF, GATE, 0, U>(a, x, pl, lds, it, xc, tid)) {
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1190,39 +946,6 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
     }
 }
 
-// Workgroups that fit on the device at once (CUs x resident per CU), per device, queried once.
-template <int DK, int TV, int NT, int NBUF, int GATE>
-static int resident_grid() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] > 0) return cached[dev];
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, decode_kernel<DK, TV, NT, NBUF, GATE>, NT, 0) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    cached[dev] = cus * per_cu;
-    return cached[dev];
-}
-
-template <int DK, int TV, int GATE>
-static hipError_t launch_decode(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
-                                const int32_t *nacc, hipStream_t stream) {
-    constexpr int NT = RGDR_DECODE_THREADS;
-    constexpr int NBUF = RGDR_DECODE_DEPTH;
-    static_assert(NBUF >= 1 && NBUF <= 3, "state tiles in flight: 1-3");
-    const int resident = resident_grid<DK, TV, NT, NBUF, GATE>();
-    if (resident <= 0) return hipErrorInvalidDevice;
-    const int grid = a.n_items < resident ? a.n_items : resident;
-    hipLaunchKernelGGL((decode_kernel<DK, TV, NT, NBUF, GATE>), dim3(grid), dim3(NT), 0, stream,
-                       a, lens, idx, nacc);
-    return hipGetLastError();
-}
-
 template <int DK, int TVW, int GATE>
 static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                               const int32_t *nacc, hipStream_t stream) {
@@ -1293,7 +1016,7 @@ static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
 }
 
 // Shape/alignment checks shared by both entry points, then the launch of the form T picks.
-enum Form { kFormWave = 0, kFormWaveMulti = 1, kFormWorkgroup = 2 };
+enum Form { kFormWave = 0, kFormWaveMulti = 1 };
 
 template <int GATE>
 static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
@@ -1304,18 +1027,11 @@ static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
         return tile_v == 128 ? launch_wave_multi<64, 128, GATE>(a, L, I, N, stream)
                              : launch_wave_multi<64, 64, GATE>(a, L, I, N, stream);
     }
-    if (form == kFormWave) {
-        if (tile_v == 128)
-            return D_k == 128 ? launch_wave<128, 128, GATE>(a, L, I, N, stream)
-                              : launch_wave<64, 128, GATE>(a, L, I, N, stream);
-        return D_k == 128 ? launch_wave<128, 64, GATE>(a, L, I, N, stream)
-                          : launch_wave<64, 64, GATE>(a, L, I, N, stream);
-    }
-    if (D_k == 128)
-        return tile_v == 128 ? launch_decode<128, 128, GATE>(a, L, I, N, stream)
-                             : launch_decode<128, 64, GATE>(a, L, I, N, stream);
-    return tile_v == 128 ? launch_decode<64, 128, GATE>(a, L, I, N, stream)
-                         : launch_decode<64, 64, GATE>(a, L, I, N, stream);
+    if (tile_v == 128)
+        return D_k == 128 ? launch_wave<128, 128, GATE>(a, L, I, N, stream)
+                          : launch_wave<64, 128, GATE>(a, L, I, N, stream);
+    return D_k == 128 ? launch_wave<128, 64, GATE>(a, L, I, N, stream)
+                      : launch_wave<64, 64, GATE>(a, L, I, N, stream);
 }
 
 static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
@@ -1330,14 +1046,12 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const Form form = T == 1 ? kFormWave : (RGDR_MULTI_WAVE ? kFormWaveMulti : kFormWorkgroup);
-    // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token wave
-    // form the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
+    const Form form = T == 1 ? kFormWave : kFormWaveMulti;
+    // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token form
+    // the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
     const int tile_v = form == kFormWave
                            ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
-                       : form == kFormWaveMulti
-                           ? ((D_k == 64 && D_v % 128 == 0) ? 128 : 64)
-                           : ((D_v % 128 != 0 || RGDR_DECODE_TILE_V == 64) ? 64 : 128);
+                           : ((D_k == 64 && D_v % 128 == 0) ? 128 : 64);
     const long long items = (long long)B * H_v * (D_v / tile_v);
     if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
     a.Hq = H_q;
