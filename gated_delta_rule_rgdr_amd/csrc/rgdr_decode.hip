@@ -946,6 +946,345 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Chunk form for 1 < T <= 8 at D_k = 128 with 128-column tiles: the item's L tokens are
+// evaluated together, on the matrix cores where the work is a dense contraction.
+//
+// With d_t the row decays of token t, c_t = d_0 ... d_t and g(t,s) = d_{s+1} ... d_t
+// (g(t,t) = 1; every factor lies in [0, 1] for decays, so nothing here can overflow), the
+// recurrence unrolls exactly to
+//   p_t = S0^T (c_t k_t)        + sum_{s<t}  M[t][s] u_s,  M[t][s] = sum_i g(t,s)_i k_s,i k_t,i
+//   o_t = S0^T (c_t scale q_t)  + sum_{s<=t} N[t][s] u_s,  N[t][s] = sum_i g(t,s)_i k_s,i scale q_t,i
+//   u_t = beta_t (v_t - p_t)
+//   S_n = diag(c_{n-1}) S0 + sum_{s<n} (g(n-1,s) k_s) (x) u_s        (the committed state)
+// The two sums over D_k x D_v x L (S0^T [c k | c scale q] and the rank-n update) are
+// bf16 MFMAs (16x16x32, fp32 accumulation): S0 is bf16 already, and every fp32 operand is
+// split into a bf16 high part and a bf16 remainder, so the products keep about 16 bits
+// of each operand. The rest (decay products, the 8 x 8 matrices M and N, and the
+// triangular solve for u, column by column) is fp32 VALU.
+//
+// Lane layout. Lane l = (kg, n16) = (l / 16, l % 16) loads rows 16 rb + 4 kg + i
+// (rb < 8, i < 4), columns 8 n16 .. 8 n16 + 7 of the tile: 16 lanes cover one 256-byte row.
+// For the MFMA the tile's row index is the contraction index (the 8 k slots of lane group
+// kg hold rows 4 kg + i of two row blocks, or one block's rows twice) and column 8 n + c is
+// element n of column set c; the accumulator of block (rb, c) then holds exactly the lane's
+// own elements of rows 16 rb + 4 kg + i, column 8 n16 + c, so the update lands in the
+// layout the commit stores.
+// ---------------------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// The chunk form serves calls with T >= RGDR_CHUNK_MIN_T (at D_k = 128, D_v a multiple of
+// 128). Its time hardly depends on the tokens per item; the per-token form's grows with the
+// longest item and is lower up to about 3 tokens.
+#ifndef RGDR_CHUNK_FORM
+#define RGDR_CHUNK_FORM 1
+#endif
+#ifndef RGDR_CHUNK_MIN_T
+#define RGDR_CHUNK_MIN_T 4
+#endif
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
+    hi = f32_to_bf16(x);
+    lo = f32_to_bf16(x - bf16_to_f32(hi));  // x - hi is exact in fp32
+}
+
+// Element c (0..7) of four packed rows, as one MFMA fragment (rows in k order).
+__device__ __forceinline__ s16x4 column_frag(const u32x4 (&w)[4], int c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    const int e = c >> 1;
+    const uint32_t lo = __builtin_amdgcn_perm(w[1][e], w[0][e], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(w[3][e], w[2][e], sel);
+    return __builtin_bit_cast(s16x4, make_uint2(lo, hi));
+}
+
+// The phases below reuse LDS areas under other element types; this keeps the compiler from
+// moving an access across a phase boundary (the hardware keeps one wave's LDS accesses in
+// order).
+__device__ __forceinline__ void lds_phase() { asm volatile("" ::: "memory"); }
+
+template <int GATE>
+__global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
+    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nacc) {
+    constexpr int DK = 128, TV = 128;
+    using Sh = TileShape<DK, TV, 64, kMaxT>;
+    constexpr int TOK = Sh::TOK;
+    // LDS: staged operands | XT hi, lo [16][XS] (later: Y [16][XS] fp32) | KA hi, lo
+    // [128][8] | UT hi, lo [8 column sets][16][8] | c_{n-1} per row | G [8][8]. Row strides
+    // of XT and Y are padded (XS = 132) so the fragment reads and the Y writes of the 16
+    // lanes of a lane group fall in different LDS banks; UT is ordered by column set for
+    // the same reason.
+    constexpr int XS = 132;
+    constexpr int OFF_XT = Sh::OPS * 4;
+    constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
+    constexpr int OFF_UT = OFF_KA + 2 * 128 * 8 * 2;
+    constexpr int OFF_CN = OFF_UT + 2 * 128 * 8 * 2;
+    constexpr int OFF_G = OFF_CN + 128 * 4;
+    constexpr int BYTES = OFF_G + 64 * 4;
+    static_assert(BYTES % 16 == 0 && 2 * 16 * XS * 2 == 16 * XS * 4, "LDS carve");
+    __shared__ f32x4 lds4[BYTES / 16];
+    char *lb = reinterpret_cast<char *>(lds4);
+    float *ob = reinterpret_cast<float *>(lb);
+    uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
+    float *ys = reinterpret_cast<float *>(lb + OFF_XT);  // reuses XT after the reduction
+    uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + 128 * 8;
+    uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT), *ut_lo = ut_hi + 128 * 8;
+    float *cn = reinterpret_cast<float *>(lb + OFF_CN);
+    float *G = reinterpret_cast<float *>(lb + OFF_G);
+
+    const Index x{lens, idx, nacc};
+    const int lane = threadIdx.x, n16 = lane & 15, kg = lane >> 4;
+    const Item m = resolve(a, x, a.item0 + xcd_item(blockIdx.x, gridDim.x));
+    const int L = m.L, n = m.n;
+
+    // The operands first, alone: staging them waits only for their own (small) loads, not
+    // behind the device-wide stream of state tiles; the tile then streams in during the
+    // per-row preparation.
+    Ops<DK, TV, 64, kMaxT> o;
+    load_ops<DK, TV, 64, kMaxT, GATE>(a, m, o, lane);
+    stage_ops<DK, TV, 64, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, lane);
+    lds_phase();
+    const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
+                              tile_range<DK, TV>(a, m));
+    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 8 * n16) * 2);
+    u32x4 raw[8][4];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_LOAD_POLICY);
+
+    // Per-row preparation: lane l owns rows l and l + 64.
+    float gp[64];  // partial G: [t][s] (s <= t) holds N[t][s], [s][t] (s < t) holds M[t][s]
+#pragma unroll
+    for (int e = 0; e < 64; ++e) gp[e] = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = lane + 64 * h;
+        float d[8], k[8], q[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 e = *reinterpret_cast<const f32x4 *>(ob + t * TOK + 4 * row);
+            const bool live = t < L;
+            d[t] = live ? e.x : 1.f;
+            k[t] = live ? e.y : 0.f;
+            q[t] = live ? e.z : 0.f;
+        }
+        float c = 1.f, cnv = 1.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            c *= d[t];
+            uint16_t hk, lk, hq, lq;
+            split_bf16(c * k[t], hk, lk);
+            split_bf16(c * q[t], hq, lq);
+            xt_hi[t * XS + row] = hk;
+            xt_lo[t * XS + row] = lk;
+            xt_hi[(8 + t) * XS + row] = hq;
+            xt_lo[(8 + t) * XS + row] = lq;
+            if (t + 1 == n) cnv = c;
+        }
+        cn[row] = cnv;
+        float ka[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            float w = k[s];  // g(s,s) k_s
+            ka[s] = (s + 1 == n) ? w : 0.f;
+            gp[s * 8 + s] = fmaf(w, q[s], gp[s * 8 + s]);
+#pragma unroll
+            for (int t = s + 1; t < 8; ++t) {
+                w *= d[t];  // g(t,s) k_s
+                gp[s * 8 + t] = fmaf(w, k[t], gp[s * 8 + t]);
+                gp[t * 8 + s] = fmaf(w, q[t], gp[t * 8 + s]);
+                if (t + 1 == n) ka[s] = w;
+            }
+        }
+        uint16_t kh[8], kl[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) split_bf16(ka[s], kh[s], kl[s]);
+        *reinterpret_cast<u32x4 *>(ka_hi + row * 8) =
+            u32x4{kh[0] | ((uint32_t)kh[1] << 16), kh[2] | ((uint32_t)kh[3] << 16),
+                  kh[4] | ((uint32_t)kh[5] << 16), kh[6] | ((uint32_t)kh[7] << 16)};
+        *reinterpret_cast<u32x4 *>(ka_lo + row * 8) =
+            u32x4{kl[0] | ((uint32_t)kl[1] << 16), kl[2] | ((uint32_t)kl[3] << 16),
+                  kl[4] | ((uint32_t)kl[5] << 16), kl[6] | ((uint32_t)kl[7] << 16)};
+    }
+    // Every staged row has been read (one wave, LDS in order): the rows area of token e / 8
+    // now takes the partials of G entries e (8 per token area), one 64-float line per entry
+    // with lane l at position l.
+    lds_phase();
+#pragma unroll
+    for (int e = 0; e < 64; ++e) ob[(e >> 3) * TOK + (e & 7) * 64 + lane] = gp[e];
+    lds_phase();
+    // G[e] (e = lane) = sum of its line, in lane order.
+    {
+        const f32x4 *line = reinterpret_cast<const f32x4 *>(ob + (lane >> 3) * TOK + (lane & 7) * 64);
+        float sum = 0.f;
+#pragma unroll
+        for (int v4 = 0; v4 < 16; ++v4) {
+            const f32x4 w = line[v4];
+            sum += w.x;
+            sum += w.y;
+            sum += w.z;
+            sum += w.w;
+        }
+        G[lane] = sum;
+    }
+
+    lds_phase();
+    // Y = [c k | c scale q]^T S0 (16 x 128): column set c, accumulated over row-block pairs;
+    // the k slots of lane group kg are rows 4 kg .. 4 kg + 3 of block 2p, then of block 2p+1.
+    auto pair8 = [](const uint16_t *p0, const uint16_t *p1) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(p0), y = *reinterpret_cast<const uint2 *>(p1);
+        return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
+    };
+    auto frag8 = [](const s16x4 f0, const s16x4 f1) {
+        const uint2 x = __builtin_bit_cast(uint2, f0), y = __builtin_bit_cast(uint2, f1);
+        return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
+    };
+    f32x4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+        const int r0 = 32 * pb + 4 * kg;
+        const bf16x8 ah = pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
+        const bf16x8 al = pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const bf16x8 bf = frag8(column_frag(raw[2 * pb], c), column_frag(raw[2 * pb + 1], c));
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bf, acc[c], 0, 0, 0);
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf, acc[c], 0, 0, 0);
+        }
+    }
+    // Y to LDS (over XT, whose last reads fed the MFMAs above): row m = 4 kg + j holds
+    // columns 8 n16 + c.
+    lds_phase();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float *yr = ys + (4 * kg + j) * XS + 8 * n16;
+        *reinterpret_cast<f32x4 *>(yr) = f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
+        *reinterpret_cast<f32x4 *>(yr + 4) = f32x4{acc[4][j], acc[5][j], acc[6][j], acc[7][j]};
+    }
+
+    lds_phase();
+    // Triangular solve, columns 2 lane and 2 lane + 1; outputs; u of the accepted prefix.
+    const size_t bh = (size_t)m.b * a.Hv + m.h;
+    const auto rout = make_rsrc(a.out + bh * a.T * a.Dv, (uint32_t)(a.T * a.Dv * 2));
+    const uint32_t ocol = (uint32_t)((m.tile * TV + 2 * lane) * 2);
+    float u0[8], u1[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        u0[t] = u1[t] = 0.f;
+        if (t < L) {  // uniform
+            const float2 A = *reinterpret_cast<const float2 *>(ys + t * XS + 2 * lane);
+            const float2 Bq = *reinterpret_cast<const float2 *>(ys + (8 + t) * XS + 2 * lane);
+            const float2 v = *reinterpret_cast<const float2 *>(ob + t * TOK + 4 * DK + 2 * lane);
+            const float bt = ob[t * TOK + 4 * DK + TV];
+            float p0 = A.x, p1 = A.y;
+#pragma unroll
+            for (int s2 = 0; s2 < t; ++s2) {
+                const float mts = G[s2 * 8 + t];
+                p0 = fmaf(mts, u0[s2], p0);
+                p1 = fmaf(mts, u1[s2], p1);
+            }
+            u0[t] = bt * (v.x - p0);
+            u1[t] = bt * (v.y - p1);
+            float o0 = Bq.x, o1 = Bq.y;
+#pragma unroll
+            for (int s2 = 0; s2 <= t; ++s2) {
+                const float nts = G[t * 8 + s2];
+                o0 = fmaf(nts, u0[s2], o0);
+                o1 = fmaf(nts, u1[s2], o1);
+            }
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(o0, o1), rout,
+                                                  (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
+        }
+    }
+    for (int t = L; t < a.T; ++t)  // padded (or skipped) tokens: +0.0 rows
+        __builtin_amdgcn_raw_buffer_store_b32(0u, rout, (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
+    {
+        uint16_t h0[8], l0[8], h1[8], l1[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+            split_bf16(s2 < n ? u0[s2] : 0.f, h0[s2], l0[s2]);
+            split_bf16(s2 < n ? u1[s2] : 0.f, h1[s2], l1[s2]);
+        }
+        auto pk = [](const uint16_t (&v)[8]) {
+            return u32x4{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                         v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
+        };
+        // column j = 8 n + c goes to UT position c * 16 + n
+        const int j0 = 2 * lane, j1 = 2 * lane + 1;
+        const int p0 = (j0 & 7) * 16 + (j0 >> 3), p1 = (j1 & 7) * 16 + (j1 >> 3);
+        *reinterpret_cast<u32x4 *>(ut_hi + p0 * 8) = pk(h0);
+        *reinterpret_cast<u32x4 *>(ut_lo + p0 * 8) = pk(l0);
+        *reinterpret_cast<u32x4 *>(ut_hi + p1 * 8) = pk(h1);
+        *reinterpret_cast<u32x4 *>(ut_lo + p1 * 8) = pk(l1);
+    }
+
+    lds_phase();
+    // Commit.
+    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
+                               tile_range<DK, TV>(a, m));
+    if (n == 0) {  // nothing accepted: the incoming bytes
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                store16<RGDR_STATE_STORE_POLICY>(raw[rb][i], rso,
+                                                 lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
+        return;
+    }
+    // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block, two MFMAs per 16 x 16 block:
+    //  * diag(c) S0: lane group kg's 8 k slots are rows 4 kg .. 4 kg + 3 of the block, then
+    //    the same rows again; A holds c's high part on the first copy, its remainder on the
+    //    second, B holds the rows (twice);
+    //  * [g k]^T U: slots of lane group 0, 1, 2 are the 8 tokens, carrying (A high, U high),
+    //    (A remainder, U high), (A high, U remainder); group 3 is zero.
+    const u32x4 z16 = {0u, 0u, 0u, 0u};
+    bf16x8 bu[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint16_t *up = (kg == 2 ? ut_lo : ut_hi) + (c * 16 + n16) * 8;
+        bu[c] = __builtin_bit_cast(bf16x8, kg < 3 ? *reinterpret_cast<const u32x4 *>(up) : z16);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+        const uint16_t *kp = (kg == 1 ? ka_lo : ka_hi) + (16 * rb + n16) * 8;
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, kg < 3 ? *reinterpret_cast<const u32x4 *>(kp) : z16);
+        bf16x8 ad;
+        {
+            uint16_t ch, cl;
+            split_bf16(cn[16 * rb + n16], ch, cl);
+            const int j = n16 - 4 * kg;  // this lane's row within the group, if any
+            uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                if (jj == j) {
+                    e[jj] = ch;
+                    e[jj + 4] = cl;
+                }
+            ad = __builtin_bit_cast(bf16x8, u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                                                  e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)});
+        }
+        f32x4 D[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const s16x4 sf = column_frag(raw[rb], c);
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, frag8(sf, sf), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bu[c], D[c], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            store16<RGDR_STATE_STORE_POLICY>(
+                u32x4{pack_bf16x2(D[0][i], D[1][i]), pack_bf16x2(D[2][i], D[3][i]),
+                      pack_bf16x2(D[4][i], D[5][i]), pack_bf16x2(D[6][i], D[7][i])},
+                rso, lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
+    }
+}
+
 template <int DK, int TVW, int GATE>
 static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                               const int32_t *nacc, hipStream_t stream) {
@@ -1016,12 +1355,21 @@ static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
 }
 
 // Shape/alignment checks shared by both entry points, then the launch of the form T picks.
-enum Form { kFormWave = 0, kFormWaveMulti = 1 };
+template <int GATE>
+static hipError_t launch_chunk(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
+                               const int32_t *nacc, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_chunk_kernel<GATE>), dim3(a.n_items), dim3(64), 0, stream, a,
+                       lens, idx, nacc);
+    return hipGetLastError();
+}
+
+enum Form { kFormWave = 0, kFormWaveMulti = 1, kFormChunk = 2 };
 
 template <int GATE>
 static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
                            const int32_t *L, const int32_t *I, const int32_t *N,
                            hipStream_t stream) {
+    if (form == kFormChunk) return launch_chunk<GATE>(a, L, I, N, stream);
     if (form == kFormWaveMulti) {
         if (D_k == 128) return launch_wave_multi<128, 64, GATE>(a, L, I, N, stream);
         return tile_v == 128 ? launch_wave_multi<64, 128, GATE>(a, L, I, N, stream)
@@ -1046,12 +1394,15 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const Form form = T == 1 ? kFormWave : kFormWaveMulti;
+    const Form form = T == 1 ? kFormWave
+                      : (RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_k == 128 && D_v % 128 == 0)
+                          ? kFormChunk
+                                                                          : kFormWaveMulti;
     // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token form
     // the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
-    const int tile_v = form == kFormWave
-                           ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
-                           : ((D_k == 64 && D_v % 128 == 0) ? 128 : 64);
+    const int tile_v = form == kFormWave ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
+                       : form == kFormChunk ? 128
+                                            : ((D_k == 64 && D_v % 128 == 0) ? 128 : 64);
     const long long items = (long long)B * H_v * (D_v / tile_v);
     if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
     a.Hq = H_q;

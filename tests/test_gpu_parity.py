@@ -118,6 +118,8 @@ SHAPES = [
     (5, 5, 5, 2, 128, 64, 9),
     (1, 1, 8, 8, 64, 512, 2),     # MQA
     (7, 2, 6, 4, 128, 128, 11),
+    (6, 2, 4, 3, 128, 256, 8),    # T = 3 at D_k = 128: the per-token multi-token form
+    (9, 3, 6, 6, 128, 256, 12),   # the chunk form, 2 tiles per row
 ]
 
 
@@ -156,7 +158,30 @@ def test_extreme_decays(rg, case, Dk):
         inp.gk[:] = -rng.uniform(0.0, 12.0, inp.gk.shape).astype(np.float32)
     say(f"extreme decays: {case}, D_k {Dk}")
     out, st = gpu_decode(inp)
-    check_decode(inp, out, st, oracle_decode(inp), f"extreme {case} Dk{Dk}")
+    ref = oracle_decode(inp)
+    if case != "growth":
+        check_decode(inp, out, st, ref, f"extreme {case} Dk{Dk}")
+        return
+    # Growth (exp(g) > 1) is outside the operator's domain (g and gk negative): states and
+    # outputs grow by e^8 per token and a few outputs are near-total cancellations of terms
+    # ~1e5 times larger. Checked here: everything finite, and each output and each committed
+    # state element within the bar plus 1e-4 of the largest |value| of its (entry, head).
+    out_ref, _, rows = ref
+    got = bf16_dev_to_f64(out)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    for b in range(inp.B):
+        L = int(inp.actual_seq_lengths[b])
+        for h in range(inp.Hv):
+            r = out_ref[b, h, :L]
+            slack = 1e-4 * np.abs(r).max()
+            assert_tol(got[b, h, :L], r, f"growth out b{b} h{h}", atol=2e-2 + slack)
+    pool = bf16_dev_to_f64(st)
+    assert np.all(np.isfinite(pool)), "non-finite state"
+    for b in range(inp.B):
+        for h in range(inp.Hv):
+            r = rows[b, h]
+            assert_tol(pool[inp.ssm_state_indices[b], h], r, f"growth state b{b} h{h}",
+                       atol=2e-2 + 1e-4 * np.abs(r).max())
 
 
 # ---------------------------------------------------------------------------------------
