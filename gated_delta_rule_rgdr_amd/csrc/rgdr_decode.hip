@@ -963,16 +963,22 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 // of each operand. The rest (decay products, the 8 x 8 matrices M and N, and the
 // triangular solve for u, column by column) is fp32 VALU.
 //
-// Lane layout. Lane l = (kg, n16) = (l / 16, l % 16) loads rows 16 rb + 4 kg + i
-// (rb < 8, i < 4), columns 8 n16 .. 8 n16 + 7 of the tile: 16 lanes cover one 256-byte row.
-// For the MFMA the tile's row index is the contraction index (the 8 k slots of lane group
-// kg hold rows 4 kg + i of two row blocks, or one block's rows twice) and column 8 n + c is
-// element n of column set c; the accumulator of block (rb, c) then holds exactly the lane's
-// own elements of rows 16 rb + 4 kg + i, column 8 n16 + c, so the update lands in the
-// layout the commit stores.
+// Two waves per item. Wave w owns tile columns 64 w .. 64 w + 63 over all 128 rows, so
+// each wave's contraction, solve and update are complete for its columns; only the per-row
+// preparation (thread r: row r) is shared, through LDS, and two workgroup barriers suffice
+// (operands staged; rows prepared). Four items fit one compute unit, two waves per SIMD.
+//
+// Lane layout. Lane l = (kg, n16) = (l / 16, l % 16) of wave w loads rows 16 rb + 4 kg + i
+// (rb < 8, i < 4), columns 64 w + 4 n16 .. + 3: 16 lanes cover the wave's 128 bytes of a
+// row. For the MFMA the tile's row index is the contraction index (the 8 k slots of lane
+// group kg hold rows 4 kg + i of two row blocks, or one block's rows twice) and column
+// 64 w + 4 n + c is element n of column set c; the accumulator of block (rb, c) then holds
+// exactly the lane's own elements of rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c, so the
+// update lands in the layout the commit stores.
 // ---------------------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // The chunk form serves calls with T >= RGDR_CHUNK_MIN_T (at D_k = 128, D_v a multiple of
 // 128). Its time hardly depends on the tokens per item; the per-token form's grows with the
@@ -989,8 +995,8 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
     lo = f32_to_bf16(x - bf16_to_f32(hi));  // x - hi is exact in fp32
 }
 
-// Element c (0..7) of four packed rows, as one MFMA fragment (rows in k order).
-__device__ __forceinline__ s16x4 column_frag(const u32x4 (&w)[4], int c) {
+// Element c (0..3) of four packed rows of 4 columns, as one MFMA fragment (rows in k order).
+__device__ __forceinline__ s16x4 column_frag(const u32x2 (&w)[4], int c) {
     const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
     const int e = c >> 1;
     const uint32_t lo = __builtin_amdgcn_perm(w[1][e], w[0][e], sel);
@@ -998,71 +1004,129 @@ __device__ __forceinline__ s16x4 column_frag(const u32x4 (&w)[4], int c) {
     return __builtin_bit_cast(s16x4, make_uint2(lo, hi));
 }
 
+// 8-byte state stores take the same form as the 16-byte ones (whole offset in the vector
+// operand).
+template <int POLICY>
+__device__ __forceinline__ void store8(u32x2 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, POLICY);
+}
+
 // The phases below reuse LDS areas under other element types; this keeps the compiler from
 // moving an access across a phase boundary (the hardware keeps one wave's LDS accesses in
 // order).
 __device__ __forceinline__ void lds_phase() { asm volatile("" ::: "memory"); }
 
+// Workgroup barrier that orders LDS only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// lane ^ 4 within each group of 8 lanes: mirror the 8 (lane -> 7 - lane), then reverse each
+// 4 (lane -> lane ^ 3).
+__device__ __forceinline__ float lane_xor4(float x) {
+    const int m = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+// One halving level of the transposed wave sum: lanes with the level's bit clear keep
+// values 0 .. H-1, the others H .. 2H-1, each plus the partner's copy of the same value.
+template <int H, typename X>
+__device__ __forceinline__ void fold_level(const float (&in)[2 * H], float (&out)[H], bool bit, X xch) {
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+        const float keep = bit ? in[j + H] : in[j], give = bit ? in[j] : in[j + H];
+        out[j] = keep + xch(give);
+    }
+}
+// Sum each of 64 per-lane values over the wave, transposed: lane l ends with the total of
+// value l. Partners at each level: lane ^ 32, ^ 16, ^ 8, ^ 4, ^ 2, ^ 1.
+__device__ __forceinline__ float wave_sum64_transposed(const float (&v)[64], int lane) {
+    float a32[32], a16[16], a8[8], a4[4], a2[2], a1[1];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float2 s = swap32(v[j], v[j + 32]);
+        a32[j] = s.x + s.y;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float2 s = swap16(a32[j], a32[j + 16]);
+        a16[j] = s.x + s.y;
+    }
+    fold_level<8>(a16, a8, (lane & 8) != 0, [](float x) { return lane_xor8(x); });
+    fold_level<4>(a8, a4, (lane & 4) != 0, [](float x) { return lane_xor4(x); });
+    fold_level<2>(a4, a2, (lane & 2) != 0, [](float x) { return lane_xor2(x); });
+    fold_level<1>(a2, a1, (lane & 1) != 0, [](float x) { return lane_xor1(x); });
+    return a1[0];
+}
+
 template <int GATE>
-__global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
+__global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
-    constexpr int DK = 128, TV = 128;
-    using Sh = TileShape<DK, TV, 64, kMaxT>;
+    constexpr int DK = 128, TV = 128, NT = 128;
+    using Sh = TileShape<DK, TV, NT, kMaxT>;
     constexpr int TOK = Sh::TOK;
-    // LDS: staged operands | XT hi, lo [16][XS] (later: Y [16][XS] fp32) | KA hi, lo
-    // [128][8] | UT hi, lo [8 column sets][16][8] | c_{n-1} per row | G [8][8]. Row strides
-    // of XT and Y are padded (XS = 132) so the fragment reads and the Y writes of the 16
-    // lanes of a lane group fall in different LDS banks; UT is ordered by column set for
-    // the same reason.
+    // LDS: staged operands | XT hi, lo [16][XS] | KA hi, lo [128][8] | UT [wave][hi, lo]
+    // [4 column sets][16][8] | c_{n-1} per row | G partials [wave][64]. Y [16][128] fp32 takes
+    // the rows area of the staged operands once both waves have prepared their rows: row m
+    // at token area m / 2, offset 256 floats for odd m. The row stride of XT is padded
+    // (XS = 132) so the fragment reads of the 16 lanes of a lane group fall in different LDS
+    // banks; UT is ordered by column set for the same reason.
     constexpr int XS = 132;
     constexpr int OFF_XT = Sh::OPS * 4;
     constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
     constexpr int OFF_UT = OFF_KA + 2 * 128 * 8 * 2;
-    constexpr int OFF_CN = OFF_UT + 2 * 128 * 8 * 2;
-    constexpr int OFF_G = OFF_CN + 128 * 4;
-    constexpr int BYTES = OFF_G + 64 * 4;
-    static_assert(BYTES % 16 == 0 && 2 * 16 * XS * 2 == 16 * XS * 4, "LDS carve");
+    constexpr int OFF_CN = OFF_UT + 2 * 2 * 64 * 8 * 2;
+    constexpr int OFF_GP = OFF_CN + 128 * 4;
+    constexpr int BYTES = OFF_GP + 2 * 64 * 4;
+    static_assert(BYTES % 16 == 0 && BYTES <= 40960, "LDS carve: four items per compute unit");
+    static_assert(2 * 256 <= 4 * DK && (TOK * 4) % 16 == 0, "Y rows fit the rows area");
     __shared__ f32x4 lds4[BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
     float *ob = reinterpret_cast<float *>(lb);
     uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
-    float *ys = reinterpret_cast<float *>(lb + OFF_XT);  // reuses XT after the reduction
     uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + 128 * 8;
-    uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT), *ut_lo = ut_hi + 128 * 8;
     float *cn = reinterpret_cast<float *>(lb + OFF_CN);
-    float *G = reinterpret_cast<float *>(lb + OFF_G);
+    float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
 
     const Index x{lens, idx, nacc};
-    const int lane = threadIdx.x, n16 = lane & 15, kg = lane >> 4;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, kg = lane >> 4;
+    uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT) + w * 2 * 64 * 8, *ut_lo = ut_hi + 64 * 8;
     const Item m = resolve(a, x, a.item0 + xcd_item(blockIdx.x, gridDim.x));
     const int L = m.L, n = m.n;
+    auto yrow = [&](int mm) { return ob + (mm >> 1) * TOK + (mm & 1) * 256; };
 
     // The operands first, alone: staging them waits only for their own (small) loads, not
     // behind the device-wide stream of state tiles; the tile then streams in during the
     // per-row preparation.
-    Ops<DK, TV, 64, kMaxT> o;
-    load_ops<DK, TV, 64, kMaxT, GATE>(a, m, o, lane);
-    stage_ops<DK, TV, 64, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, lane);
-    lds_phase();
+    Ops<DK, TV, NT, kMaxT> o;
+    load_ops<DK, TV, NT, kMaxT, GATE>(a, m, o, tid);
+    stage_ops<DK, TV, NT, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, tid);
     const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
                               tile_range<DK, TV>(a, m));
-    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 8 * n16) * 2);
-    u32x4 raw[8][4];
+    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 64 * w + 4 * n16) * 2);
+    u32x2 raw[8][4];
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b64(
                 rs, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_LOAD_POLICY);
+    lds_barrier();
 
-    // Per-row preparation: lane l owns rows l and l + 64.
+    // Per-row preparation: thread r owns row r.
     float gp[64];  // partial G: [t][s] (s <= t) holds N[t][s], [s][t] (s < t) holds M[t][s]
 #pragma unroll
     for (int e = 0; e < 64; ++e) gp[e] = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = lane + 64 * h;
+    {
+        const int row = tid;
         float d[8], k[8], q[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -1089,15 +1153,15 @@ __global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
         float ka[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            float w = k[s];  // g(s,s) k_s
-            ka[s] = (s + 1 == n) ? w : 0.f;
-            gp[s * 8 + s] = fmaf(w, q[s], gp[s * 8 + s]);
+            float wv = k[s];  // g(s,s) k_s
+            ka[s] = (s + 1 == n) ? wv : 0.f;
+            gp[s * 8 + s] = wv * q[s];
 #pragma unroll
             for (int t = s + 1; t < 8; ++t) {
-                w *= d[t];  // g(t,s) k_s
-                gp[s * 8 + t] = fmaf(w, k[t], gp[s * 8 + t]);
-                gp[t * 8 + s] = fmaf(w, q[t], gp[t * 8 + s]);
-                if (t + 1 == n) ka[s] = w;
+                wv *= d[t];  // g(t,s) k_s
+                gp[s * 8 + t] = wv * k[t];
+                gp[t * 8 + s] = wv * q[t];
+                if (t + 1 == n) ka[s] = wv;
             }
         }
         uint16_t kh[8], kl[8];
@@ -1110,31 +1174,15 @@ __global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
             u32x4{kl[0] | ((uint32_t)kl[1] << 16), kl[2] | ((uint32_t)kl[3] << 16),
                   kl[4] | ((uint32_t)kl[5] << 16), kl[6] | ((uint32_t)kl[7] << 16)};
     }
-    // Every staged row has been read (one wave, LDS in order): the rows area of token e / 8
-    // now takes the partials of G entries e (8 per token area), one 64-float line per entry
-    // with lane l at position l.
-    lds_phase();
-#pragma unroll
-    for (int e = 0; e < 64; ++e) ob[(e >> 3) * TOK + (e & 7) * 64 + lane] = gp[e];
-    lds_phase();
-    // G[e] (e = lane) = sum of its line, in lane order.
-    {
-        const f32x4 *line = reinterpret_cast<const f32x4 *>(ob + (lane >> 3) * TOK + (lane & 7) * 64);
-        float sum = 0.f;
-#pragma unroll
-        for (int v4 = 0; v4 < 16; ++v4) {
-            const f32x4 w = line[v4];
-            sum += w.x;
-            sum += w.y;
-            sum += w.z;
-            sum += w.w;
-        }
-        G[lane] = sum;
-    }
+    // G over this wave's 64 rows: lane e holds entry e.
+    gpart[64 * w + lane] = wave_sum64_transposed(gp, lane);
+    lds_barrier();
+    const float g_e = gpart[lane] + gpart[64 + lane];  // entry `lane` of G (the two halves of the rows)
+    auto G = [&](int e) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_e), e)); };
 
-    lds_phase();
-    // Y = [c k | c scale q]^T S0 (16 x 128): column set c, accumulated over row-block pairs;
-    // the k slots of lane group kg are rows 4 kg .. 4 kg + 3 of block 2p, then of block 2p+1.
+    // Y = [c k | c scale q]^T S0 (16 x 64, this wave's columns): column set c, accumulated
+    // over row-block pairs; the k slots of lane group kg are rows 4 kg .. 4 kg + 3 of block
+    // 2p, then of block 2p+1.
     auto pair8 = [](const uint16_t *p0, const uint16_t *p1) {
         const uint2 x = *reinterpret_cast<const uint2 *>(p0), y = *reinterpret_cast<const uint2 *>(p1);
         return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
@@ -1143,85 +1191,67 @@ __global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
         const uint2 x = __builtin_bit_cast(uint2, f0), y = __builtin_bit_cast(uint2, f1);
         return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
     };
-    f32x4 acc[8];
+    f32x4 acc[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int pb = 0; pb < 4; ++pb) {
         const int r0 = 32 * pb + 4 * kg;
         const bf16x8 ah = pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
         const bf16x8 al = pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 4; ++c) {
             const bf16x8 bf = frag8(column_frag(raw[2 * pb], c), column_frag(raw[2 * pb + 1], c));
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bf, acc[c], 0, 0, 0);
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf, acc[c], 0, 0, 0);
         }
     }
-    // Y to LDS (over XT, whose last reads fed the MFMAs above): row m = 4 kg + j holds
-    // columns 8 n16 + c.
+    // Y to LDS: row m = 4 kg + j holds columns 64 w + 4 n16 + c.
     lds_phase();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float *yr = ys + (4 * kg + j) * XS + 8 * n16;
-        *reinterpret_cast<f32x4 *>(yr) = f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
-        *reinterpret_cast<f32x4 *>(yr + 4) = f32x4{acc[4][j], acc[5][j], acc[6][j], acc[7][j]};
-    }
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4 *>(yrow(4 * kg + j) + 64 * w + 4 * n16) =
+            f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
 
     lds_phase();
-    // Triangular solve, columns 2 lane and 2 lane + 1; outputs; u of the accepted prefix.
+    // Triangular solve, column 64 w + lane; outputs; u of the accepted prefix.
+    const int col = 64 * w + lane;
     const size_t bh = (size_t)m.b * a.Hv + m.h;
     const auto rout = make_rsrc(a.out + bh * a.T * a.Dv, (uint32_t)(a.T * a.Dv * 2));
-    const uint32_t ocol = (uint32_t)((m.tile * TV + 2 * lane) * 2);
-    float u0[8], u1[8];
+    const uint32_t ocol = (uint32_t)((m.tile * TV + col) * 2);
+    float u[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        u0[t] = u1[t] = 0.f;
+        u[t] = 0.f;
         if (t < L) {  // uniform
-            const float2 A = *reinterpret_cast<const float2 *>(ys + t * XS + 2 * lane);
-            const float2 Bq = *reinterpret_cast<const float2 *>(ys + (8 + t) * XS + 2 * lane);
-            const float2 v = *reinterpret_cast<const float2 *>(ob + t * TOK + 4 * DK + 2 * lane);
+            const float A = yrow(t)[col], Bq = yrow(8 + t)[col];
+            const float v = ob[t * TOK + 4 * DK + col];
             const float bt = ob[t * TOK + 4 * DK + TV];
-            float p0 = A.x, p1 = A.y;
+            float p = A;
 #pragma unroll
-            for (int s2 = 0; s2 < t; ++s2) {
-                const float mts = G[s2 * 8 + t];
-                p0 = fmaf(mts, u0[s2], p0);
-                p1 = fmaf(mts, u1[s2], p1);
-            }
-            u0[t] = bt * (v.x - p0);
-            u1[t] = bt * (v.y - p1);
-            float o0 = Bq.x, o1 = Bq.y;
+            for (int s2 = 0; s2 < t; ++s2) p = fmaf(G(s2 * 8 + t), u[s2], p);
+            u[t] = bt * (v - p);
+            float ov = Bq;
 #pragma unroll
-            for (int s2 = 0; s2 <= t; ++s2) {
-                const float nts = G[t * 8 + s2];
-                o0 = fmaf(nts, u0[s2], o0);
-                o1 = fmaf(nts, u1[s2], o1);
-            }
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(o0, o1), rout,
+            for (int s2 = 0; s2 <= t; ++s2) ov = fmaf(G(t * 8 + s2), u[s2], ov);
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(ov), rout,
                                                   (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
         }
     }
     for (int t = L; t < a.T; ++t)  // padded (or skipped) tokens: +0.0 rows
-        __builtin_amdgcn_raw_buffer_store_b32(0u, rout, (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rout, (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
     {
-        uint16_t h0[8], l0[8], h1[8], l1[8];
+        uint16_t h[8], l[8];
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) {
-            split_bf16(s2 < n ? u0[s2] : 0.f, h0[s2], l0[s2]);
-            split_bf16(s2 < n ? u1[s2] : 0.f, h1[s2], l1[s2]);
-        }
-        auto pk = [](const uint16_t (&v)[8]) {
-            return u32x4{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                         v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
-        };
-        // column j = 8 n + c goes to UT position c * 16 + n
-        const int j0 = 2 * lane, j1 = 2 * lane + 1;
-        const int p0 = (j0 & 7) * 16 + (j0 >> 3), p1 = (j1 & 7) * 16 + (j1 >> 3);
-        *reinterpret_cast<u32x4 *>(ut_hi + p0 * 8) = pk(h0);
-        *reinterpret_cast<u32x4 *>(ut_lo + p0 * 8) = pk(l0);
-        *reinterpret_cast<u32x4 *>(ut_hi + p1 * 8) = pk(h1);
-        *reinterpret_cast<u32x4 *>(ut_lo + p1 * 8) = pk(l1);
+        for (int s2 = 0; s2 < 8; ++s2) split_bf16(s2 < n ? u[s2] : 0.f, h[s2], l[s2]);
+        // local column j = 4 n + c goes to UT position c * 16 + n
+        const int p = (lane & 3) * 16 + (lane >> 2);
+        *reinterpret_cast<u32x4 *>(ut_hi + p * 8) =
+            u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                  h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+        *reinterpret_cast<u32x4 *>(ut_lo + p * 8) =
+            u32x4{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16),
+                  l[4] | ((uint32_t)l[5] << 16), l[6] | ((uint32_t)l[7] << 16)};
     }
 
     lds_phase();
@@ -1233,8 +1263,8 @@ __global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
         for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                store16<RGDR_STATE_STORE_POLICY>(raw[rb][i], rso,
-                                                 lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
+                store8<RGDR_STATE_STORE_POLICY>(raw[rb][i], rso,
+                                                lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
         return;
     }
     // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block, two MFMAs per 16 x 16 block:
@@ -1244,9 +1274,9 @@ __global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
     //  * [g k]^T U: slots of lane group 0, 1, 2 are the 8 tokens, carrying (A high, U high),
     //    (A remainder, U high), (A high, U remainder); group 3 is zero.
     const u32x4 z16 = {0u, 0u, 0u, 0u};
-    bf16x8 bu[8];
+    bf16x8 bu[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 4; ++c) {
         const uint16_t *up = (kg == 2 ? ut_lo : ut_hi) + (c * 16 + n16) * 8;
         bu[c] = __builtin_bit_cast(bf16x8, kg < 3 ? *reinterpret_cast<const u32x4 *>(up) : z16);
     }
@@ -1269,18 +1299,17 @@ __global__ __launch_bounds__(64, 1) void decode_chunk_kernel(
             ad = __builtin_bit_cast(bf16x8, u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
                                                   e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)});
         }
-        f32x4 D[8];
+        f32x4 D[4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 4; ++c) {
             const s16x4 sf = column_frag(raw[rb], c);
             D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, frag8(sf, sf), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bu[c], D[c], 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            store16<RGDR_STATE_STORE_POLICY>(
-                u32x4{pack_bf16x2(D[0][i], D[1][i]), pack_bf16x2(D[2][i], D[3][i]),
-                      pack_bf16x2(D[4][i], D[5][i]), pack_bf16x2(D[6][i], D[7][i])},
+            store8<RGDR_STATE_STORE_POLICY>(
+                u32x2{pack_bf16x2(D[0][i], D[1][i]), pack_bf16x2(D[2][i], D[3][i])},
                 rso, lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
     }
 }
@@ -1358,7 +1387,7 @@ static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
 template <int GATE>
 static hipError_t launch_chunk(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                const int32_t *nacc, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_chunk_kernel<GATE>), dim3(a.n_items), dim3(64), 0, stream, a,
+    hipLaunchKernelGGL((decode_chunk_kernel<GATE>), dim3(a.n_items), dim3(128), 0, stream, a,
                        lens, idx, nacc);
     return hipGetLastError();
 }
