@@ -989,6 +989,15 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #ifndef RGDR_CHUNK_MIN_T
 #define RGDR_CHUNK_MIN_T 4
 #endif
+// Where the chunk form issues its tile loads: RGDR_CHUNK_PRE row blocks with the operand
+// loads, RGDR_CHUNK_POST more once the operands are staged, the rest one block per token
+// step of the per-row preparation.
+#ifndef RGDR_CHUNK_PRE
+#define RGDR_CHUNK_PRE 3
+#endif
+#ifndef RGDR_CHUNK_POST
+#define RGDR_CHUNK_POST 1
+#endif
 
 __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
     hi = f32_to_bf16(x);
@@ -1106,19 +1115,27 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // The operands first, alone: staging them waits only for their own (small) loads, not
     // behind the device-wide stream of state tiles; the tile then streams in during the
     // per-row preparation.
-    Ops<DK, TV, NT, kMaxT> o;
-    load_ops<DK, TV, NT, kMaxT, GATE>(a, m, o, tid);
-    stage_ops<DK, TV, NT, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, tid);
+    constexpr int PRE = RGDR_CHUNK_PRE, POST = RGDR_CHUNK_POST;
+    static_assert(PRE >= 0 && POST >= 0 && PRE + POST <= 8, "tile load placement");
     const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
                               tile_range<DK, TV>(a, m));
     const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 64 * w + 4 * n16) * 2);
     u32x2 raw[8][4];
-#pragma unroll
-    for (int rb = 0; rb < 8; ++rb)
+    auto load_rb = [&](int rb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b64(
                 rs, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_LOAD_POLICY);
+    };
+    Ops<DK, TV, NT, kMaxT> o;
+    load_ops<DK, TV, NT, kMaxT, GATE>(a, m, o, tid);
+#pragma unroll
+    for (int rb = 0; rb < PRE; ++rb) load_rb(rb);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_ops<DK, TV, NT, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, tid);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = PRE; rb < PRE + POST; ++rb) load_rb(rb);
     lds_barrier();
 
     // Per-row preparation: thread r owns row r.
@@ -1139,6 +1156,11 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
         float c = 1.f, cnv = 1.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
+            if (PRE + POST + t < 8) {  // the remaining tile loads, one row block per step
+                __builtin_amdgcn_sched_barrier(0);
+                load_rb(PRE + POST + t);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             c *= d[t];
             uint16_t hk, lk, hq, lq;
             split_bf16(c * k[t], hk, lk);
