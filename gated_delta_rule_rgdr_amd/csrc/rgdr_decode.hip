@@ -1083,34 +1083,39 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     using Sh = TileShape<DK, TV, NT, kMaxT>;
     constexpr int TOK = Sh::TOK;
     // LDS: staged operands | XT hi, lo [16][XS] | KA hi, lo [128][8] | UT [wave][hi, lo]
-    // [4 column sets][16][8] | c_{n-1} per row | G partials [wave][64]. Y [16][128] fp32 takes
-    // the rows area of the staged operands once both waves have prepared their rows: row m
-    // at token area m / 2, offset 256 floats for odd m. The row stride of XT is padded
+    // [4 column sets][16][8] | diag(c_{n-1}) operands per row | G partials [wave][64] |
+    // M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row) takes the
+    // rows area of the staged operands once both waves have prepared their rows: column j
+    // at token area j / 16, offset 20 (j % 16) floats. The row stride of XT is padded
     // (XS = 132) so the fragment reads of the 16 lanes of a lane group fall in different LDS
     // banks; UT is ordered by column set for the same reason.
     constexpr int XS = 132;
     constexpr int OFF_XT = Sh::OPS * 4;
     constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
     constexpr int OFF_UT = OFF_KA + 2 * 128 * 8 * 2;
-    constexpr int OFF_CN = OFF_UT + 2 * 2 * 64 * 8 * 2;
-    constexpr int OFF_GP = OFF_CN + 128 * 4;
-    constexpr int BYTES = OFF_GP + 2 * 64 * 4;
+    constexpr int OFF_DG = OFF_UT + 2 * 2 * 64 * 8 * 2;
+    constexpr int OFF_GP = OFF_DG + 128 * 16;
+    constexpr int OFF_GS = OFF_GP + 2 * 64 * 4;
+    constexpr int BYTES = OFF_GS + 2 * 2 * 64 * 4;
     static_assert(BYTES % 16 == 0 && BYTES <= 40960, "LDS carve: four items per compute unit");
-    static_assert(2 * 256 <= 4 * DK && (TOK * 4) % 16 == 0, "Y rows fit the rows area");
+    constexpr int YS = 20;  // floats per Y^T row: 16 values and a pad that spreads LDS banks
+    static_assert(16 * YS <= 4 * DK && (TOK * 4) % 16 == 0 && (YS * 4) % 16 == 0,
+                  "Y^T rows fit the rows area");
     __shared__ f32x4 lds4[BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
     float *ob = reinterpret_cast<float *>(lb);
     uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
     uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + 128 * 8;
-    float *cn = reinterpret_cast<float *>(lb + OFF_CN);
+    u32x4 *dg = reinterpret_cast<u32x4 *>(lb + OFF_DG);
     float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
 
     const Index x{lens, idx, nacc};
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, kg = lane >> 4;
     uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT) + w * 2 * 64 * 8, *ut_lo = ut_hi + 64 * 8;
+    float *gsM = reinterpret_cast<float *>(lb + OFF_GS) + w * 2 * 64, *gsN = gsM + 64;
     const Item m = resolve(a, x, a.item0 + xcd_item(blockIdx.x, gridDim.x));
     const int L = m.L, n = m.n;
-    auto yrow = [&](int mm) { return ob + (mm >> 1) * TOK + (mm & 1) * 256; };
+    auto ycol = [&](int j) { return ob + (j >> 4) * TOK + (j & 15) * YS; };
 
     // The operands first, alone: staging them waits only for their own (small) loads, not
     // behind the device-wide stream of state tiles; the tile then streams in during the
@@ -1171,7 +1176,16 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
             xt_lo[(8 + t) * XS + row] = lq;
             if (t + 1 == n) cnv = c;
         }
-        cn[row] = cnv;
+        {
+            // This row's entry of diag(c_{n-1}) as the A operand of a 16x16x16 MFMA (4 k
+            // slots per lane group): high part, then remainder, each in k slot row % 4 of
+            // the lane group that holds the row.
+            uint16_t ch, cl;
+            split_bf16(cnv, ch, cl);
+            const int j = row & 3, sh = 16 * (j & 1);
+            const uint32_t hw = (uint32_t)ch << sh, lw = (uint32_t)cl << sh;
+            dg[row] = (j >> 1) ? u32x4{0u, hw, 0u, lw} : u32x4{hw, 0u, lw, 0u};
+        }
         float ka[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -1199,8 +1213,17 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // G over this wave's 64 rows: lane e holds entry e.
     gpart[64 * w + lane] = wave_sum64_transposed(gp, lane);
     lds_barrier();
-    const float g_e = gpart[lane] + gpart[64 + lane];  // entry `lane` of G (the two halves of the rows)
-    auto G = [&](int e) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_e), e)); };
+    {
+        // Entry e = 8 a + b of G, summed over the two halves of the rows, into this wave's
+        // tables: M[t][s] (s < t) and N[t][s] (s <= t), rows read as broadcast vectors.
+        const float g_e = gpart[lane] + gpart[64 + lane];
+        const int ea = lane >> 3, eb = lane & 7;
+        if (ea < eb)
+            gsM[eb * 8 + ea] = g_e;
+        else
+            gsN[ea * 8 + eb] = g_e;
+    }
+    lds_phase();
 
     // Y = [c k | c scale q]^T S0 (16 x 64, this wave's columns): column set c, accumulated
     // over row-block pairs; the k slots of lane group kg are rows 4 kg .. 4 kg + 3 of block
@@ -1228,12 +1251,12 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bf, acc[c], 0, 0, 0);
         }
     }
-    // Y to LDS: row m = 4 kg + j holds columns 64 w + 4 n16 + c.
+    // Y to LDS, transposed: accumulator c holds rows 4 kg .. 4 kg + 3 of column
+    // 64 w + 4 n16 + c.
     lds_phase();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4 *>(yrow(4 * kg + j) + 64 * w + 4 * n16) =
-            f32x4{acc[0][j], acc[1][j], acc[2][j], acc[3][j]};
+    for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4 *>(ycol(64 * w + 4 * n16 + c) + 4 * kg) = acc[c];
 
     lds_phase();
     // Triangular solve, column 64 w + lane; outputs; u of the accepted prefix.
@@ -1241,21 +1264,30 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const size_t bh = (size_t)m.b * a.Hv + m.h;
     const auto rout = make_rsrc(a.out + bh * a.T * a.Dv, (uint32_t)(a.T * a.Dv * 2));
     const uint32_t ocol = (uint32_t)((m.tile * TV + col) * 2);
+    float yc[16];  // this column of Y: [c k]^T S0 for t < 8, then [c scale q]^T S0
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+        const f32x4 e = *reinterpret_cast<const f32x4 *>(ycol(col) + 4 * v4);
+        yc[4 * v4] = e.x;
+        yc[4 * v4 + 1] = e.y;
+        yc[4 * v4 + 2] = e.z;
+        yc[4 * v4 + 3] = e.w;
+    }
     float u[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         u[t] = 0.f;
         if (t < L) {  // uniform
-            const float A = yrow(t)[col], Bq = yrow(8 + t)[col];
+            const float A = yc[t], Bq = yc[8 + t];
             const float v = ob[t * TOK + 4 * DK + col];
             const float bt = ob[t * TOK + 4 * DK + TV];
             float p = A;
 #pragma unroll
-            for (int s2 = 0; s2 < t; ++s2) p = fmaf(G(s2 * 8 + t), u[s2], p);
+            for (int s2 = 0; s2 < t; ++s2) p = fmaf(gsM[t * 8 + s2], u[s2], p);
             u[t] = bt * (v - p);
             float ov = Bq;
 #pragma unroll
-            for (int s2 = 0; s2 <= t; ++s2) ov = fmaf(G(t * 8 + s2), u[s2], ov);
+            for (int s2 = 0; s2 <= t; ++s2) ov = fmaf(gsN[t * 8 + s2], u[s2], ov);
             __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(ov), rout,
                                                   (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
         }
@@ -1289,44 +1321,39 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
                                                 lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
         return;
     }
-    // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block, two MFMAs per 16 x 16 block:
-    //  * diag(c) S0: lane group kg's 8 k slots are rows 4 kg .. 4 kg + 3 of the block, then
-    //    the same rows again; A holds c's high part on the first copy, its remainder on the
-    //    second, B holds the rows (twice);
-    //  * [g k]^T U: slots of lane group 0, 1, 2 are the 8 tokens, carrying (A high, U high),
-    //    (A remainder, U high), (A high, U remainder); group 3 is zero.
-    const u32x4 z16 = {0u, 0u, 0u, 0u};
-    bf16x8 bu[4];
+    // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block, four 16x16x16 MFMAs per 16 x 16
+    // block, all accumulating into one register set:
+    //  * diag(c) S0: c's high part, then its remainder, against the block's rows as the lane
+    //    group holds them (k slots 4 kg .. 4 kg + 3); the diagonal operand is the row's, in
+    //    the lanes of the group that holds the row, else zero;
+    //  * [g k]^T U: lane group kg carries tokens 4 (kg & 1) .. 4 (kg & 1) + 3 of A's high part
+    //    (kg < 2) or its remainder (kg >= 2), against U's high part, then U's remainder, so
+    //    the four products of the split parts are all taken.
+    // One instruction shape per accumulation chain: on this part a matrix-core instruction
+    // that takes its accumulator from one of another shape can read it before it is
+    // written (the compiler does not separate them), which loses the earlier terms.
+    s16x4 buh[4], bul[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const uint16_t *up = (kg == 2 ? ut_lo : ut_hi) + (c * 16 + n16) * 8;
-        bu[c] = __builtin_bit_cast(bf16x8, kg < 3 ? *reinterpret_cast<const u32x4 *>(up) : z16);
+        buh[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_hi + (c * 16 + n16) * 8 + 4 * (kg & 1)));
+        bul[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_lo + (c * 16 + n16) * 8 + 4 * (kg & 1)));
     }
+    const uint16_t *ka_lane = (kg >> 1 ? ka_lo : ka_hi) + n16 * 8 + 4 * (kg & 1);
+    const bool on_diag = (n16 >> 2) == kg;
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
-        const uint16_t *kp = (kg == 1 ? ka_lo : ka_hi) + (16 * rb + n16) * 8;
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, kg < 3 ? *reinterpret_cast<const u32x4 *>(kp) : z16);
-        bf16x8 ad;
-        {
-            uint16_t ch, cl;
-            split_bf16(cn[16 * rb + n16], ch, cl);
-            const int j = n16 - 4 * kg;  // this lane's row within the group, if any
-            uint16_t e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                if (jj == j) {
-                    e[jj] = ch;
-                    e[jj + 4] = cl;
-                }
-            ad = __builtin_bit_cast(bf16x8, u32x4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                                  e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)});
-        }
+        const s16x4 ak = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ka_lane + 16 * rb * 8));
+        const u32x4 dv = dg[16 * rb + n16];
+        const s16x4 dh = __builtin_bit_cast(s16x4, make_uint2(on_diag ? dv.x : 0u, on_diag ? dv.y : 0u));
+        const s16x4 dl = __builtin_bit_cast(s16x4, make_uint2(on_diag ? dv.z : 0u, on_diag ? dv.w : 0u));
         f32x4 D[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const s16x4 sf = column_frag(raw[rb], c);
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, frag8(sf, sf), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bu[c], D[c], 0, 0, 0);
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dh, sf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dl, sf, D[c], 0, 0, 0);
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, buh[c], D[c], 0, 0, 0);
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bul[c], D[c], 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
