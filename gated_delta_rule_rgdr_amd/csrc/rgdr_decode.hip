@@ -1273,27 +1273,28 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
         yc[4 * v4 + 2] = e.z;
         yc[4 * v4 + 3] = e.w;
     }
+    // Straight-line over all 8 token slots (no branch on L, so the LDS reads can be issued
+    // together): every staged value of a padded token is finite (its loads returned zeros),
+    // and its u and output are masked to 0.
     float u[8];
+    uint16_t o16[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        u[t] = 0.f;
-        if (t < L) {  // uniform
-            const float A = yc[t], Bq = yc[8 + t];
-            const float v = ob[t * TOK + 4 * DK + col];
-            const float bt = ob[t * TOK + 4 * DK + TV];
-            float p = A;
+        const float v = ob[t * TOK + 4 * DK + col];
+        const float bt = ob[t * TOK + 4 * DK + TV];
+        float p = yc[t];
 #pragma unroll
-            for (int s2 = 0; s2 < t; ++s2) p = fmaf(gsM[t * 8 + s2], u[s2], p);
-            u[t] = bt * (v - p);
-            float ov = Bq;
+        for (int s2 = 0; s2 < t; ++s2) p = fmaf(gsM[t * 8 + s2], u[s2], p);
+        u[t] = t < L ? bt * (v - p) : 0.f;
+        float ov = yc[8 + t];
 #pragma unroll
-            for (int s2 = 0; s2 <= t; ++s2) ov = fmaf(gsN[t * 8 + s2], u[s2], ov);
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(ov), rout,
-                                                  (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
-        }
+        for (int s2 = 0; s2 <= t; ++s2) ov = fmaf(gsN[t * 8 + s2], u[s2], ov);
+        o16[t] = t < L ? f32_to_bf16(ov) : (uint16_t)0;  // padded (or skipped) tokens: +0.0
     }
-    for (int t = L; t < a.T; ++t)  // padded (or skipped) tokens: +0.0 rows
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rout, (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        if (t < a.T)
+            __builtin_amdgcn_raw_buffer_store_b16(o16[t], rout, (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
     {
         uint16_t h[8], l[8];
 #pragma unroll
