@@ -982,12 +982,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // The chunk form serves calls with T >= RGDR_CHUNK_MIN_T (at D_k = 128, D_v a multiple of
 // 128). Its time hardly depends on the tokens per item; the per-token form's grows with the
-// longest item and is lower up to about 3 tokens.
+// longest item, and is no lower even at 2 tokens.
 #ifndef RGDR_CHUNK_FORM
 #define RGDR_CHUNK_FORM 1
 #endif
 #ifndef RGDR_CHUNK_MIN_T
-#define RGDR_CHUNK_MIN_T 4
+#define RGDR_CHUNK_MIN_T 2
 #endif
 // Where the chunk form issues its tile loads: RGDR_CHUNK_PRE row blocks with the operand
 // loads, RGDR_CHUNK_POST more once the operands are staged, the rest one block per token

@@ -179,8 +179,8 @@ def raw_qk(inp, seed):
     (4, 2, 4, 1, 128, 128, 6),   # wave form, 128-column tiles, D_k = 128
     (3, 2, 2, 1, 64, 128, 4),    # wave form, D_k = 64
     (3, 1, 2, 1, 128, 192, 5),   # wave form, 64-column tiles
-    (4, 2, 4, 6, 128, 128, 6),   # workgroup form (T > 1), varlen
-    (3, 2, 2, 8, 64, 192, 4),    # workgroup form, D_k = 64, 64-column tiles
+    (4, 2, 4, 6, 128, 128, 6),   # chunk form (T > 1, D_k = 128), varlen
+    (3, 2, 2, 8, 64, 192, 4),    # per-token multi-token form, D_k = 64, 64-column tiles
 ])
 def test_gated_normalize_qk(rg, shape):
     """RGDR_NORMALIZE_QK: raw q, k in, the oracle normalises them per token and head (fp64);
