@@ -59,6 +59,17 @@ def test_workload3_nan_padding_bitexact(rg):
     check_decode(inp, out1, st1, ref, "workload 3 NaN padding")
 
 
+def test_chunk_form_more_items_than_resident(rg):
+    """The matrix-core form with more items than the device holds at once (48 x 32 =
+    1536 tiles against four per compute unit): later items start as earlier ones finish.
+    Every entry is checked against the oracle."""
+    inp = workloads.make_case(48, 32, 32, 8, 128, 128, 96, seed=47, indices="permutation",
+                              lengths="uniform")
+    say(f"chunk form, {inp.B * inp.Hv} items")
+    out, st = gpu_decode(inp)
+    check_decode(inp, out, st, oracle_decode(inp), "chunk form, 1536 items")
+
+
 def test_workload4_gate_then_decode(rg):
     """la_gate feeds rgdr_decode (g fp32, beta bf16); the oracle chain uses its own gate."""
     inp = workloads.make_workload(4)
