@@ -4,10 +4,10 @@
 // section (decay, memory read, delta update, output, token by token) and parameter list.
 //
 // The step is HBM-bound: each (batch entry, value head) pair streams its D_k x D_v bf16
-// state in once and out once; everything else is small. Two wave-level kernel forms share
-// the plumbing below; T decides which one runs.
+// state in once and out once; everything else is small. Three kernel forms share the
+// plumbing below; T and the head sizes decide which one runs.
 //
-// Wave form (T = 1, every decode workload). One wave owns one (b, h, 128- or 64-column)
+// Wave form (T = 1, every single-token decode). One wave owns one (b, h, 128- or 64-column)
 // tile over all D_k rows:
 //   * lane (cg, rg) holds 8 consecutive columns (a 16-byte bf16 vector) of the rows rg,
 //     rg + RG, ...; a wave-wide load covers RG whole tile rows (1 KiB contiguous at 128
@@ -20,21 +20,25 @@
 //   * one item per wave per launch (a call with more items than resident waves becomes
 //     several launches); items past the end and skipped entries use empty buffer ranges
 //     (no data moves).
+//   Per token, steps 2 and 4 share ONE reduction over D_k. With S' the decayed state,
+//   p = S'^T k and r = S'^T (scale q) are reduced together with the scalar k.(scale q);
+//   then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q), and
+//   S_new = S' + k (x) u.
 //
-// Multi-token form (1 < T <= 8). One wave owns one (b, h, 64- or 128-column) tile and keeps
-// it in fp32 registers across the tokens, in a scaled form that leaves three FMAs per
-// element and token (see decode_wave_multi_kernel); the D_k reduction also finishes inside
-// the wave.
+// Chunk form (1 < T <= 8 at D_k = 128, D_v a multiple of 128; decode_chunk_kernel). Two
+// waves own one (b, h, 128-column) tile; the item's L tokens are unrolled in closed form
+// (decay products, two 8 x 8 Gram matrices, a triangular solve), and the two dense
+// contractions of that form run on the matrix cores.
 //
-// Both forms: per token, steps 2 and 4 share ONE reduction over D_k. With S' the decayed
-// state, p = S'^T k and r = S'^T (scale q) are reduced together with the scalar
-// k.(scale q); then u = beta (v - p) and o = r + (k.(scale q)) u, which equals
-// S_new^T (scale q), and S_new = S' + k (x) u. Every item issues the same sequence of vector
-// memory instructions whatever its lengths and slot (the accesses that must not happen get
-// empty buffer ranges), and the per-entry index arrays are read with scalar loads, so the
-// in-order vector-memory counter waits never drain the prefetched state. Results are
-// deterministic. No matrix cores: per token the work is a matrix-vector product and a
-// rank-1 update.
+// Multi-token form (other 1 < T <= 8 shapes; decode_wave_multi_kernel). One wave owns one
+// (b, h, 64- or 128-column) tile and keeps it in fp32 registers across the tokens, in a
+// scaled form that leaves three FMAs per element and token; the D_k reduction also
+// finishes inside the wave.
+//
+// All forms: every item issues the same sequence of vector memory instructions whatever
+// its lengths and slot (the accesses that must not happen get empty buffer ranges), and the
+// per-entry index arrays are read with scalar loads, so the in-order vector-memory counter
+// waits never drain the prefetched state. Results are deterministic.
 #include "rgdr_common.h"
 
 namespace rgdr {
@@ -693,7 +697,8 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Wave form for 1 < T <= 8: one wave owns one (b, h, TV-column) tile over all D_k rows and
+// Wave form for 1 < T <= 8 where the chunk form does not apply (D_k = 64, or D_v not a
+// multiple of 128): one wave owns one (b, h, TV-column) tile over all D_k rows and
 // keeps it in fp32 registers through the tokens (R rows x 8 columns per lane, 128 values at
 // most); per token the D_k reduction finishes inside the wave, with no barrier and no LDS
 // exchange. One item per wave; the operands of all of the item's tokens are staged once in
