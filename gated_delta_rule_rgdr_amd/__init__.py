@@ -72,9 +72,23 @@ def _check(code: int, what: str):
         raise RuntimeError(f"{what}: {status_string(code)}")
 
 
-def _stream_handle(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream_handle(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
+
+
+def _same_device(ref, **tensors):
+    """Every tensor on ref's GPU: the library launches on the current device and takes the
+    pointers as that device's addresses."""
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise RuntimeError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _dtype_code(dtype, name):
+    if dtype not in _DTYPE_CODE:
+        raise RuntimeError(f"{name}: unsupported dtype {dtype}")
+    return _DTYPE_CODE[dtype]
 
 
 def _dev(t, name, dtype, ndim=None):
@@ -135,11 +149,17 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
         _dev(state_out, "state_out", torch.bfloat16, 4)
         if state_out.shape != state_pool.shape:
             raise RuntimeError("state_out must have the pool's shape")
-    rc = lib.rgdr_decode(query.data_ptr(), key.data_ptr(), value.data_ptr(), beta.data_ptr(),
-                         state_pool.data_ptr(), actual_seq_lengths.data_ptr(),
-                         ssm_state_indices.data_ptr(), g.data_ptr(), gk.data_ptr(),
-                         num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T, Dk, Dv, N,
-                         out.data_ptr(), state_out.data_ptr(), _stream_handle(stream))
+    _same_device(query, key=key, value=value, beta=beta, state_pool=state_pool,
+                 actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
+                 g=g, gk=gk, num_accepted_tokens=num_accepted_tokens, out=out,
+                 state_out=state_out)
+    with torch.cuda.device(query.device):
+        rc = lib.rgdr_decode(query.data_ptr(), key.data_ptr(), value.data_ptr(),
+                             beta.data_ptr(), state_pool.data_ptr(),
+                             actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
+                             g.data_ptr(), gk.data_ptr(), num_accepted_tokens.data_ptr(),
+                             float(scale), B, Hq, Hv, T, Dk, Dv, N, out.data_ptr(),
+                             state_out.data_ptr(), _stream_handle(stream, query.device))
     _check(rc, "rgdr_decode")
     return out, state_out
 
@@ -194,13 +214,20 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
         _dev(state_out, "state_out", torch.bfloat16, 4)
         if state_out.shape != state_pool.shape:
             raise RuntimeError("state_out must have the pool's shape")
-    rc = lib.rgdr_decode_gated(query.data_ptr(), key.data_ptr(), value.data_ptr(), a.data_ptr(),
-                               b.data_ptr(), dt_bias.data_ptr(), decay_scale.data_ptr(),
-                               _DTYPE_CODE[a.dtype], state_pool.data_ptr(),
-                               actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
-                               gk.data_ptr(), num_accepted_tokens.data_ptr(), float(scale), B, Hq,
-                               Hv, T, Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
-                               NORMALIZE_QK if normalize_qk else 0, _stream_handle(stream))
+    _same_device(query, key=key, value=value, a=a, b=b, dt_bias=dt_bias,
+                 decay_scale=decay_scale, state_pool=state_pool,
+                 actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
+                 gk=gk, num_accepted_tokens=num_accepted_tokens, out=out, state_out=state_out)
+    with torch.cuda.device(query.device):
+        rc = lib.rgdr_decode_gated(query.data_ptr(), key.data_ptr(), value.data_ptr(),
+                                   a.data_ptr(), b.data_ptr(), dt_bias.data_ptr(),
+                                   decay_scale.data_ptr(), _DTYPE_CODE[a.dtype],
+                                   state_pool.data_ptr(), actual_seq_lengths.data_ptr(),
+                                   ssm_state_indices.data_ptr(), gk.data_ptr(),
+                                   num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T,
+                                   Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
+                                   NORMALIZE_QK if normalize_qk else 0,
+                                   _stream_handle(stream, query.device))
     _check(rc, "rgdr_decode_gated")
     return out, state_out
 
@@ -255,12 +282,15 @@ def la_gate(a, dt_bias, decay_scale, b=None, *, want_beta=None, decay_dtype=None
                                                                    device=a.device)
         _dev(beta_t, "beta_out", beta_dtype)
     n_rows = a.numel() // H if H else 0
-    rc = lib.la_gate(a.data_ptr(), dt_bias.data_ptr(), decay_scale.data_ptr(),
-                     b.data_ptr() if b is not None else None, _DTYPE_CODE[a.dtype], n_rows, H,
-                     decay_out.data_ptr(), _DTYPE_CODE[decay_dtype],
-                     beta_t.data_ptr() if beta_t is not None else None,
-                     _DTYPE_CODE[beta_dtype] if beta_t is not None else 0,
-                     _stream_handle(stream))
+    _same_device(a, dt_bias=dt_bias, decay_scale=decay_scale, b=b, decay_out=decay_out,
+                 beta_out=beta_t)
+    with torch.cuda.device(a.device):
+        rc = lib.la_gate(a.data_ptr(), dt_bias.data_ptr(), decay_scale.data_ptr(),
+                         b.data_ptr() if b is not None else None, _DTYPE_CODE[a.dtype], n_rows,
+                         H, decay_out.data_ptr(), _dtype_code(decay_dtype, "decay_out"),
+                         beta_t.data_ptr() if beta_t is not None else None,
+                         _dtype_code(beta_dtype, "beta_out") if beta_t is not None else 0,
+                         _stream_handle(stream, a.device))
     _check(rc, "la_gate")
     return decay_out, beta_t
 
@@ -270,9 +300,18 @@ def rgdr_validate(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T,
     """Synchronous check of device index arrays; returns the status code (0 = valid)."""
     lib = library()
     B = actual_seq_lengths.shape[0]
-    return lib.rgdr_validate(actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
-                             num_accepted_tokens.data_ptr(), B, T, N_slots,
-                             _stream_handle(stream))
+    for nm, t in (("actual_seq_lengths", actual_seq_lengths),
+                  ("ssm_state_indices", ssm_state_indices),
+                  ("num_accepted_tokens", num_accepted_tokens)):
+        _dev(t, nm, torch.int32, 1)
+        if t.shape[0] != B:
+            raise RuntimeError(f"{nm} must have shape [{B}]")
+    _same_device(actual_seq_lengths, ssm_state_indices=ssm_state_indices,
+                 num_accepted_tokens=num_accepted_tokens)
+    with torch.cuda.device(actual_seq_lengths.device):
+        return lib.rgdr_validate(actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
+                                 num_accepted_tokens.data_ptr(), B, T, N_slots,
+                                 _stream_handle(stream, actual_seq_lengths.device))
 
 
 def rgdr_validate_host(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N_slots):
