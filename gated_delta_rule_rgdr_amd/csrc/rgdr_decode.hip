@@ -1478,10 +1478,8 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const Form form = T == 1 ? kFormWave
-                      : (RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_k == 128 && D_v % 128 == 0)
-                          ? kFormChunk
-                                                                          : kFormWaveMulti;
+    const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_k == 128 && D_v % 128 == 0;
+    const Form form = T == 1 ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;
     // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token form
     // the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
     const int tile_v = form == kFormWave ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)

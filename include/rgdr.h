@@ -41,8 +41,8 @@ typedef enum {
     RGDR_ERR_NULL = 1,        /* a required pointer is NULL                                */
     RGDR_ERR_SHAPE = 2,       /* a size is negative, or zero where not allowed; T > 8;
                                  H_v % H_q != 0; grid too large; beta requested without b */
-    RGDR_ERR_UNSUPPORTED = 3, /* D_k not in {64, 128}, D_v not a multiple of 64, or an
-                                 unknown option bit                                         */
+    RGDR_ERR_UNSUPPORTED = 3, /* D_k not in {64, 128}, D_v not a multiple of 64 or above
+                                 4096, or an unknown option bit                             */
     RGDR_ERR_RANGE = 4,       /* (validate) a length, count or slot index out of range     */
     RGDR_ERR_DUPLICATE = 5,   /* (validate) two batch entries name the same slot           */
     RGDR_ERR_DTYPE = 6,       /* a dtype code not allowed for that argument                 */
@@ -80,8 +80,8 @@ enum { RGDR_NORMALIZE_QK = 1u /* L2-normalise each token's query and key head ve
  *                       its first n tokens (clamped to [0, L]); n = L in ordinary decoding.
  *   scale               q is multiplied by it before step 4 (the page's scale_value).
  *   B, H_q, H_v, T, D_k, D_v, N_slots   sizes; T <= 8 (decode only), H_v % H_q == 0,
- *                       D_k in {64, 128}, D_v a multiple of 64. B = 0 is an empty batch:
- *                       RGDR_OK, nothing is read or launched.
+ *                       D_k in {64, 128}, D_v a multiple of 64 and at most 4096.
+ *                       B = 0 is an empty batch: RGDR_OK, nothing is read or launched.
  *   out                 bf16 [B, H_v, T, D_v]  written entirely. 16-byte aligned.
  *   state_out           bf16 [N_slots, H_v, D_k, D_v]  receives the committed state of every
  *                       slot some entry names; other slots are not touched. It may be the

@@ -74,6 +74,7 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, Dk=96) == UNSUP
     assert _decode(lib, Dk=256) == UNSUP
     assert _decode(lib, Dv=96) == UNSUP
+    assert _decode(lib, Dv=4160) == UNSUP     # above the 4096 bound
     bad = [0x10000] * 10
     bad[2] = 0x10002  # value not 16-byte aligned
     assert _decode(lib, ptrs=bad) == ALIGN
