@@ -61,8 +61,8 @@ extern "C" rgdr_status la_gate(const void *a, const float *dt_bias, const float 
     if (beta_out && beta_dtype != RGDR_F32 && beta_dtype != RGDR_F16 && beta_dtype != RGDR_BF16)
         return RGDR_ERR_DTYPE;
     if (beta_out && !b) return RGDR_ERR_SHAPE;
-    const long long n = (long long)n_rows * H;
-    if (n_rows != 0 && n / n_rows != H) return RGDR_ERR_SHAPE;
+    long long n = 0;
+    if (__builtin_mul_overflow((long long)n_rows, (long long)H, &n)) return RGDR_ERR_SHAPE;
     if (n == 0) return RGDR_OK;  // empty input: nothing to do, no pointer is read
     if (!a || !dt_bias || !decay_scale || !decay_out) return RGDR_ERR_NULL;
     const size_t in_sz = dtype_size(ab_dtype);

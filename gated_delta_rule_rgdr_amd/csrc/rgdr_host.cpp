@@ -57,7 +57,7 @@ extern "C" const char *rgdr_status_string(rgdr_status s) {
     case RGDR_ERR_SHAPE: return "RGDR_ERR_SHAPE: invalid size (<= 0, T > 8, H_v % H_q != 0, "
                                 "grid too large, or beta requested without b)";
     case RGDR_ERR_UNSUPPORTED: return "RGDR_ERR_UNSUPPORTED: D_k must be 64 or 128 and D_v a "
-                                      "multiple of 64";
+                                      "multiple of 64 up to 4096; unknown option bit";
     case RGDR_ERR_RANGE: return "RGDR_ERR_RANGE: a length, accepted count or slot index is out "
                                 "of range";
     case RGDR_ERR_DUPLICATE: return "RGDR_ERR_DUPLICATE: two batch entries name the same slot";
