@@ -14,6 +14,11 @@ fallback: if the library is missing, importing the binding's functions raises.
 * ``rgdr_validate`` -- synchronous check of the index arrays.
 
 A non-OK status from the library raises ``RuntimeError`` (the page's error behaviour).
+
+With ``RGDR_VALIDATE=1`` in the environment (read at import; ``VALIDATE`` holds it), every
+decode call first checks its index arrays with ``rgdr_validate``: a synchronous copy to the
+host, for debugging only (it cannot run under graph capture). A bad length, count or slot
+then raises ``RuntimeError`` instead of being clamped or skipped by the kernel.
 """
 import ctypes as C
 import os
@@ -21,7 +26,7 @@ import os
 import torch
 
 __all__ = ["rgdr_decode", "rgdr_decode_gated", "recurrent_gated_delta_rule", "la_gate",
-           "rgdr_validate",
+           "rgdr_validate", "VALIDATE",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
            "RGDR_F16", "RGDR_BF16"]
 
@@ -33,6 +38,7 @@ NORMALIZE_QK = RGDR_NORMALIZE_QK
 _DTYPE_CODE = {torch.float32: RGDR_F32, torch.float16: RGDR_F16, torch.bfloat16: RGDR_BF16}
 
 _lib = None
+VALIDATE = os.environ.get("RGDR_VALIDATE", "") == "1"
 
 
 def library():
@@ -83,6 +89,11 @@ def _same_device(ref, **tensors):
     for name, t in tensors.items():
         if t is not None and t.device != ref.device:
             raise RuntimeError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _validate_indices(lens, idx, nacc, T, N):
+    code = rgdr_validate(lens, idx, nacc, T, N)
+    _check(code, "index arrays (RGDR_VALIDATE)")
 
 
 def _dtype_code(dtype, name):
@@ -153,6 +164,8 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
                  actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
                  g=g, gk=gk, num_accepted_tokens=num_accepted_tokens, out=out,
                  state_out=state_out)
+    if VALIDATE:
+        _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
         rc = lib.rgdr_decode(query.data_ptr(), key.data_ptr(), value.data_ptr(),
                              beta.data_ptr(), state_pool.data_ptr(),
@@ -218,6 +231,8 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
                  decay_scale=decay_scale, state_pool=state_pool,
                  actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
                  gk=gk, num_accepted_tokens=num_accepted_tokens, out=out, state_out=state_out)
+    if VALIDATE:
+        _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
         rc = lib.rgdr_decode_gated(query.data_ptr(), key.data_ptr(), value.data_ptr(),
                                    a.data_ptr(), b.data_ptr(), dt_bias.data_ptr(),

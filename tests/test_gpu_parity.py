@@ -361,6 +361,24 @@ def test_validate_on_device(rg):
     assert rg.rgdr_validate(lens, idx_bad, lens, 8, 6) == 4
 
 
+def test_validate_switch_checks_each_call(rg, monkeypatch):
+    """With the RGDR_VALIDATE switch on, a call whose index arrays name one slot twice
+    raises before launching; valid arrays go through and match the unchecked call."""
+    inp = small_case(seed=21)
+    d = upload(inp)
+    ref_out, ref_st = gpu_decode(inp, d)
+    monkeypatch.setattr(rg, "VALIDATE", True)
+    out, st = gpu_decode(inp, d)
+    assert np.array_equal(dev_to_bits(out), dev_to_bits(ref_out))
+    assert np.array_equal(dev_to_bits(st), dev_to_bits(ref_st))
+    dup = d["ssm_state_indices"].clone()
+    dup[1] = dup[0]
+    with pytest.raises(RuntimeError, match="RGDR_ERR_DUPLICATE"):
+        rg.rgdr_decode(d["query"], d["key"], d["value"], d["beta"], d["state"].clone(),
+                       d["actual_seq_lengths"], dup, d["g"], d["gk"],
+                       d["num_accepted_tokens"], inp.scale)
+
+
 def test_graph_replay_matches_eager(rg):
     """The gate and the decode captured in a HIP graph give the eager bytes on every replay
     (out-of-place, so each replay starts from the same state)."""
