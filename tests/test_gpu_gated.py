@@ -122,7 +122,8 @@ def test_gated_varlen_T8_nan_padding(rg):
 
 
 def test_gated_fp16_projections(rg):
-    for shape in [(5, 2, 4, 1, 128, 128, 8), (3, 2, 2, 3, 64, 192, 4)]:
+    # wave form (T = 1), chunk form (T > 1, D_k = 128), per-token multi-token form (D_k = 64)
+    for shape in [(5, 2, 4, 1, 128, 128, 8), (4, 2, 4, 5, 128, 256, 8), (3, 2, 2, 3, 64, 192, 4)]:
         B, Hq, Hv, T, Dk, Dv, N = shape
         inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=77, indices="choice",
                                   lengths="uniform", gate=True)
