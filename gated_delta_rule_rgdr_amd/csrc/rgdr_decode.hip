@@ -1080,22 +1080,98 @@ __device__ __forceinline__ float wave_sum64_transposed(const float (&v)[64], int
     return a1[0];
 }
 
+// Operand staging of the chunk form (128 threads, D_k = 128, 128-column tiles). Planar
+// per token: the row decays d [8][128], k [8][128] and scale q [8][128], then the tile's v
+// [8][128] and beta [8]. Each thread writes whole 16-byte runs of consecutive rows, so the
+// stores of a wave fall in distinct LDS banks (an interleaved (d, k, q) record per row
+// would put 8 to 16 lanes of every store on one bank).
+constexpr int kChunkOps = 32 * 128 + 16;  // floats: d, k, q, v planes, beta (padded)
+
+template <int GATE>
+__device__ __forceinline__ void chunk_stage_ops(const Ops<128, 128, 128, kMaxT> &o, float *ob,
+                                                float scale, bool norm, int tid) {
+    using Sh = TileShape<128, 128, 128, kMaxT>;
+    constexpr int DK = 128, TV = 128;
+    float *sd = ob, *sk = ob + 8 * DK, *sq = ob + 16 * DK, *sv = ob + 24 * DK;
+    float *sb = ob + 24 * DK + 8 * TV;
+#pragma unroll
+    for (int j = 0; j < Sh::GKV; ++j) {
+        const int e = tid + j * 128;
+        const int t = e * 4 / DK, i0 = e * 4 % DK;
+        float g;
+        if constexpr (GATE == kGateGiven)
+            g = __uint_as_float(o.g[j]);
+        else
+            g = o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g[j]) + o.dt);
+        const float eg = __expf(g);
+        *reinterpret_cast<f32x4 *>(sd + t * DK + i0) =
+            f32x4{eg * __expf(o.gk[j].x), eg * __expf(o.gk[j].y), eg * __expf(o.gk[j].z),
+                  eg * __expf(o.gk[j].w)};
+    }
+#pragma unroll
+    for (int j = 0; j < Sh::KQV; ++j) {
+        const int e = tid + j * 128;
+        const int t = e * 8 / DK, i0 = e * 8 % DK;
+        const uint32_t kw[4] = {o.k[j].x, o.k[j].y, o.k[j].z, o.k[j].w};
+        const uint32_t qw[4] = {o.q[j].x, o.q[j].y, o.q[j].z, o.q[j].w};
+        float ks = 1.f, qs = scale;
+        if constexpr (GATE != kGateGiven) {
+            if (norm) {  // uniform: the whole wave takes it
+                // One token's head vector lies in 16 consecutive, aligned lanes.
+                float kss = 0.f, qss = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    kss = fmaf(bf16_lo(kw[w]), bf16_lo(kw[w]), kss);
+                    kss = fmaf(bf16_hi(kw[w]), bf16_hi(kw[w]), kss);
+                    qss = fmaf(bf16_lo(qw[w]), bf16_lo(qw[w]), qss);
+                    qss = fmaf(bf16_hi(qw[w]), bf16_hi(qw[w]), qss);
+                }
+                ks = inv_norm(group_sum<DK / 8>(kss));
+                qs = scale * inv_norm(group_sum<DK / 8>(qss));
+            }
+        }
+        float *kr = sk + t * DK + i0, *qr = sq + t * DK + i0;
+        *reinterpret_cast<f32x4 *>(kr) = f32x4{bf16_lo(kw[0]) * ks, bf16_hi(kw[0]) * ks,
+                                               bf16_lo(kw[1]) * ks, bf16_hi(kw[1]) * ks};
+        *reinterpret_cast<f32x4 *>(kr + 4) = f32x4{bf16_lo(kw[2]) * ks, bf16_hi(kw[2]) * ks,
+                                                   bf16_lo(kw[3]) * ks, bf16_hi(kw[3]) * ks};
+        *reinterpret_cast<f32x4 *>(qr) = f32x4{bf16_lo(qw[0]) * qs, bf16_hi(qw[0]) * qs,
+                                               bf16_lo(qw[1]) * qs, bf16_hi(qw[1]) * qs};
+        *reinterpret_cast<f32x4 *>(qr + 4) = f32x4{bf16_lo(qw[2]) * qs, bf16_hi(qw[2]) * qs,
+                                                   bf16_lo(qw[3]) * qs, bf16_hi(qw[3]) * qs};
+    }
+#pragma unroll
+    for (int j = 0; j < Sh::VV; ++j) {
+        const int e = tid + j * 128;
+        const int t = e / (TV / 8), c8 = e % (TV / 8);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(sv + t * TV + c8 * 8);
+        dst[0] = f32x4{bf16_lo(o.v[j].x), bf16_hi(o.v[j].x), bf16_lo(o.v[j].y), bf16_hi(o.v[j].y)};
+        dst[1] = f32x4{bf16_lo(o.v[j].z), bf16_hi(o.v[j].z), bf16_lo(o.v[j].w), bf16_hi(o.v[j].w)};
+    }
+    if (tid < kMaxT) {
+        float bt;
+        if constexpr (GATE == kGateGiven)
+            bt = bf16_to_f32((uint16_t)o.beta);
+        else
+            bt = sigmoid_fast(gate_value<GATE == kGateF16>(o.beta));
+        sb[tid] = bt;
+    }
+}
+
 template <int GATE>
 __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
     constexpr int DK = 128, TV = 128, NT = 128;
-    using Sh = TileShape<DK, TV, NT, kMaxT>;
-    constexpr int TOK = Sh::TOK;
-    // LDS: staged operands | XT hi, lo [16][XS] | KA hi, lo [128][8] | UT [wave][hi, lo]
-    // [4 column sets][16][8] | diag(c_{n-1}) operands per row | G partials [wave][64] |
-    // M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row) takes the
-    // rows area of the staged operands once both waves have prepared their rows: column j
-    // at token area j / 16, offset 20 (j % 16) floats. The row stride of XT is padded
+    // LDS: staged operands (chunk_stage_ops) | XT hi, lo [16][XS] | KA hi, lo [128][8] |
+    // UT [wave][hi, lo] [4 column sets][16][8] | diag(c_{n-1}) operands per row | G partials
+    // [wave][64] | M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row)
+    // takes the d, k and q planes of the staged operands once both waves have prepared their
+    // rows. The row stride of XT is padded
     // (XS = 132) so the fragment reads of the 16 lanes of a lane group fall in different LDS
     // banks; UT is ordered by column set for the same reason.
     constexpr int XS = 132;
-    constexpr int OFF_XT = Sh::OPS * 4;
+    constexpr int OFF_XT = kChunkOps * 4;
     constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
     constexpr int OFF_UT = OFF_KA + 2 * 128 * 8 * 2;
     constexpr int OFF_DG = OFF_UT + 2 * 2 * 64 * 8 * 2;
@@ -1104,8 +1180,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     constexpr int BYTES = OFF_GS + 2 * 2 * 64 * 4;
     static_assert(BYTES % 16 == 0 && BYTES <= 40960, "LDS carve: four items per compute unit");
     constexpr int YS = 20;  // floats per Y^T row: 16 values and a pad that spreads LDS banks
-    static_assert(16 * YS <= 4 * DK && (TOK * 4) % 16 == 0 && (YS * 4) % 16 == 0,
-                  "Y^T rows fit the rows area");
+    static_assert(128 * YS <= 24 * DK && (YS * 4) % 16 == 0, "Y^T fits the d, k, q planes");
+    static_assert(kChunkOps % 4 == 0, "16-byte aligned carve");
     __shared__ f32x4 lds4[BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
     float *ob = reinterpret_cast<float *>(lb);
@@ -1120,7 +1196,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     float *gsM = reinterpret_cast<float *>(lb + OFF_GS) + w * 2 * 64, *gsN = gsM + 64;
     const Item m = resolve(a, x, a.item0 + xcd_item(blockIdx.x, gridDim.x));
     const int L = m.L, n = m.n;
-    auto ycol = [&](int j) { return ob + (j >> 4) * TOK + (j & 15) * YS; };
+    auto ycol = [&](int j) { return ob + j * YS; };
 
     // The operands first, alone: staging them waits only for their own (small) loads, not
     // behind the device-wide stream of state tiles; the tile then streams in during the
@@ -1142,7 +1218,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 #pragma unroll
     for (int rb = 0; rb < PRE; ++rb) load_rb(rb);
     __builtin_amdgcn_sched_barrier(0);
-    stage_ops<DK, TV, NT, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, tid);
+    chunk_stage_ops<GATE>(o, ob, a.scale, a.norm_qk != 0, tid);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = PRE; rb < PRE + POST; ++rb) load_rb(rb);
@@ -1157,11 +1233,10 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
         float d[8], k[8], q[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const f32x4 e = *reinterpret_cast<const f32x4 *>(ob + t * TOK + 4 * row);
             const bool live = t < L;
-            d[t] = live ? e.x : 1.f;
-            k[t] = live ? e.y : 0.f;
-            q[t] = live ? e.z : 0.f;
+            d[t] = live ? ob[t * DK + row] : 1.f;
+            k[t] = live ? ob[8 * DK + t * DK + row] : 0.f;
+            q[t] = live ? ob[16 * DK + t * DK + row] : 0.f;
         }
         float c = 1.f, cnv = 1.f;
 #pragma unroll
@@ -1285,8 +1360,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     uint16_t o16[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const float v = ob[t * TOK + 4 * DK + col];
-        const float bt = ob[t * TOK + 4 * DK + TV];
+        const float v = ob[24 * DK + t * TV + col];
+        const float bt = ob[24 * DK + 8 * TV + t];
         float p = yc[t];
 #pragma unroll
         for (int s2 = 0; s2 < t; ++s2) p = fmaf(gsM[t * 8 + s2], u[s2], p);
