@@ -1084,12 +1084,14 @@ __device__ __forceinline__ float wave_sum64_transposed(const float (&v)[64], int
 // per token: the row decays d [8][128], k [8][128] and scale q [8][128], then the tile's v
 // [8][128] and beta [8]. Each thread writes whole 16-byte runs of consecutive rows, so the
 // stores of a wave fall in distinct LDS banks (an interleaved (d, k, q) record per row
-// would put 8 to 16 lanes of every store on one bank).
+// would put 8 to 16 lanes of every store on one bank). Tokens t >= L come out neutral
+// (d = 1, k = q = v = 0): their ranged loads returned zeros, and the fused gate's decay is
+// forced to 0 for them.
 constexpr int kChunkOps = 32 * 128 + 16;  // floats: d, k, q, v planes, beta (padded)
 
 template <int GATE>
 __device__ __forceinline__ void chunk_stage_ops(const Ops<128, 128, 128, kMaxT> &o, float *ob,
-                                                float scale, bool norm, int tid) {
+                                                float scale, bool norm, int L, int tid) {
     using Sh = TileShape<128, 128, 128, kMaxT>;
     constexpr int DK = 128, TV = 128;
     float *sd = ob, *sk = ob + 8 * DK, *sq = ob + 16 * DK, *sv = ob + 24 * DK;
@@ -1102,7 +1104,7 @@ __device__ __forceinline__ void chunk_stage_ops(const Ops<128, 128, 128, kMaxT> 
         if constexpr (GATE == kGateGiven)
             g = __uint_as_float(o.g[j]);
         else
-            g = o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g[j]) + o.dt);
+            g = t < L ? o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g[j]) + o.dt) : 0.f;
         const float eg = __expf(g);
         *reinterpret_cast<f32x4 *>(sd + t * DK + i0) =
             f32x4{eg * __expf(o.gk[j].x), eg * __expf(o.gk[j].y), eg * __expf(o.gk[j].z),
@@ -1218,7 +1220,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 #pragma unroll
     for (int rb = 0; rb < PRE; ++rb) load_rb(rb);
     __builtin_amdgcn_sched_barrier(0);
-    chunk_stage_ops<GATE>(o, ob, a.scale, a.norm_qk != 0, tid);
+    chunk_stage_ops<GATE>(o, ob, a.scale, a.norm_qk != 0, L, tid);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = PRE; rb < PRE + POST; ++rb) load_rb(rb);
@@ -1233,10 +1235,9 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
         float d[8], k[8], q[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const bool live = t < L;
-            d[t] = live ? ob[t * DK + row] : 1.f;
-            k[t] = live ? ob[8 * DK + t * DK + row] : 0.f;
-            q[t] = live ? ob[16 * DK + t * DK + row] : 0.f;
+            d[t] = ob[t * DK + row];  // padded tokens were staged neutral
+            k[t] = ob[8 * DK + t * DK + row];
+            q[t] = ob[16 * DK + t * DK + row];
         }
         float c = 1.f, cnv = 1.f;
 #pragma unroll
