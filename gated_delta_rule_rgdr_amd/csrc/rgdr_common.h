@@ -44,7 +44,7 @@ __device__ __forceinline__ float softplus_fast(float x) {
     const float e = __expf(-fabsf(x));  // (0, 1]
     const float u = 1.0f + e;
     const float d = u - 1.0f;
-    const float l = d == 0.f ? e : __logf(u) * __fdividef(e, d);
+    const float l = d == 0.f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(d));
     return fmaxf(x, 0.f) + l;
 }
 __device__ __forceinline__ float sigmoid_fast(float x) {
