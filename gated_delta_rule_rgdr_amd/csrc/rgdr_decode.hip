@@ -962,11 +962,12 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 //   o_t = S0^T (c_t scale q_t)  + sum_{s<=t} N[t][s] u_s,  N[t][s] = sum_i g(t,s)_i k_s,i scale q_t,i
 //   u_t = beta_t (v_t - p_t)
 //   S_n = diag(c_{n-1}) S0 + sum_{s<n} (g(n-1,s) k_s) (x) u_s        (the committed state)
-// The two sums over D_k x D_v x L (S0^T [c k | c scale q] and the rank-n update) are
-// bf16 MFMAs (16x16x32, fp32 accumulation): S0 is bf16 already, and every fp32 operand is
-// split into a bf16 high part and a bf16 remainder, so the products keep about 16 bits
-// of each operand. The rest (decay products, the 8 x 8 matrices M and N, and the
-// triangular solve for u, column by column) is fp32 VALU.
+// The two sums over D_k x D_v x L (S0^T [c k | c scale q], and diag(c) S0 plus the rank-n
+// update) are bf16 MFMAs with fp32 accumulation (16x16x32 for the first, 16x16x16 for the
+// second): S0 is bf16 already, and every fp32 operand is split into a bf16 high part and a
+// bf16 remainder, so the products keep about 16 bits of each operand. The rest (decay
+// products, the 8 x 8 matrices M and N, and the triangular solve for u, column by column)
+// is fp32 VALU.
 //
 // Two waves per item. Wave w owns tile columns 64 w .. 64 w + 63 over all 128 rows, so
 // each wave's contraction, solve and update are complete for its columns; only the per-row
@@ -975,11 +976,12 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 //
 // Lane layout. Lane l = (kg, n16) = (l / 16, l % 16) of wave w loads rows 16 rb + 4 kg + i
 // (rb < 8, i < 4), columns 64 w + 4 n16 .. + 3: 16 lanes cover the wave's 128 bytes of a
-// row. For the MFMA the tile's row index is the contraction index (the 8 k slots of lane
-// group kg hold rows 4 kg + i of two row blocks, or one block's rows twice) and column
-// 64 w + 4 n + c is element n of column set c; the accumulator of block (rb, c) then holds
-// exactly the lane's own elements of rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c, so the
-// update lands in the layout the commit stores.
+// row. For the contraction the tile's row index is the k index (the 8 k slots of lane group
+// kg hold its rows 4 kg + i of two row blocks) and column 64 w + 4 n + c is element n of
+// column set c. In the commit the block's own 4 rows per lane group are the k slots of
+// diag(c) S0, and the accumulator of block (rb, c) holds exactly the lane's own elements of
+// rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c, so the update lands in the layout the
+// commit stores.
 // ---------------------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
