@@ -1171,9 +1171,9 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // UT [wave][hi, lo] [4 column sets][16][8] | diag(c_{n-1}) operands per row | G partials
     // [wave][64] | M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row)
     // takes the d, k and q planes of the staged operands once both waves have prepared their
-    // rows. The row stride of XT is padded
-    // (XS = 132) so the fragment reads of the 16 lanes of a lane group fall in different LDS
-    // banks; UT is ordered by column set for the same reason.
+    // rows. The row stride of XT is padded (XS = 132) so the fragment reads of the 16 lanes
+    // of a lane group fall in different LDS banks; UT is ordered by column set for the same
+    // reason.
     constexpr int XS = 132;
     constexpr int OFF_XT = kChunkOps * 4;
     constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
@@ -1202,9 +1202,11 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const int L = m.L, n = m.n;
     auto ycol = [&](int j) { return ob + j * YS; };
 
-    // The operands first, alone: staging them waits only for their own (small) loads, not
-    // behind the device-wide stream of state tiles; the tile then streams in during the
-    // per-row preparation.
+    // The operands first, with a few row blocks of the tile (PRE); more once the operands
+    // are staged (POST); the rest one block per token step of the per-row preparation. Issued
+    // all at once, the tile loads would block the wave for microseconds (the memory queues
+    // are full) before it could stage or prepare anything; issued after the operands alone,
+    // the memory system would idle while they arrive.
     constexpr int PRE = RGDR_CHUNK_PRE, POST = RGDR_CHUNK_POST;
     static_assert(PRE >= 0 && POST >= 0 && PRE + POST <= 8, "tile load placement");
     const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
