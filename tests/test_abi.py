@@ -4,7 +4,6 @@ declares, and rejects bad arguments on the host before launching anything.
 The argument checks return before any HIP call, so the fake (never dereferenced) device
 addresses used here are safe.
 """
-import ctypes as C
 import os
 import re
 

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import assert_tol, bf16_dev_to_f64, bits_to_dev, dev_to_bits, say, upload
+from gpu_util import assert_tol, bf16_dev_to_f64, dev_to_bits, say, upload
 
 pytestmark = pytest.mark.gpu
 

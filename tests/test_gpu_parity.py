@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import (assert_tol, bf16_dev_to_f64, bits_to_dev, check_decode, dev_to_bits,
+from gpu_util import (assert_tol, bf16_dev_to_f64, check_decode, dev_to_bits,
                       gpu_decode, oracle_decode, say, upload)
 
 pytestmark = pytest.mark.gpu
