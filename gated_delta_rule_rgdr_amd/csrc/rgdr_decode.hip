@@ -996,6 +996,10 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #ifndef RGDR_CHUNK_MIN_T
 #define RGDR_CHUNK_MIN_T 2
 #endif
+// The chunk form at D_k = 64 too (0: those calls take the per-token form).
+#ifndef RGDR_CHUNK_DK64
+#define RGDR_CHUNK_DK64 1
+#endif
 // Where the chunk form issues its tile loads: RGDR_CHUNK_PRE row blocks with the operand
 // loads, RGDR_CHUNK_POST more once the operands are staged, the rest one block per token
 // step of the per-row preparation.
@@ -1082,26 +1086,33 @@ __device__ __forceinline__ float wave_sum64_transposed(const float (&v)[64], int
     return a1[0];
 }
 
-// Operand staging of the chunk form (128 threads, D_k = 128, 128-column tiles). Planar
-// per token: the row decays d [8][128], k [8][128] and scale q [8][128], then the tile's v
-// [8][128] and beta [8]. Each thread writes whole 16-byte runs of consecutive rows, so the
+// Operand staging of the chunk form (128 threads, D_k = 64 or 128, 128-column tiles).
+// Planar per token: the row decays d [8][D_k], k [8][D_k] and scale q [8][D_k], then the
+// tile's v [8][128] and beta [8]. Each thread writes whole 16-byte runs of consecutive rows, so the
 // stores of a wave fall in distinct LDS banks (an interleaved (d, k, q) record per row
 // would put 8 to 16 lanes of every store on one bank). Tokens t >= L come out neutral
 // (d = 1, k = q = v = 0): their ranged loads returned zeros, and the fused gate's decay is
 // forced to 0 for them.
-constexpr int kChunkOps = 32 * 128 + 16;  // floats: d, k, q, v planes, beta (padded)
+// After the per-row preparation the d, k and q planes are dead; Y^T [128 columns][kChunkYS]
+// then takes their place, so that region is at least that large.
+constexpr int kChunkYS = 20;  // floats per Y^T row: 16 values and a pad that spreads LDS banks
+template <int DK>
+constexpr int chunk_vbase() { return 24 * DK > 128 * kChunkYS ? 24 * DK : 128 * kChunkYS; }
+template <int DK>
+constexpr int chunk_ops() { return chunk_vbase<DK>() + 8 * 128 + 16; }  // floats, 16-B multiple
 
-template <int GATE>
-__device__ __forceinline__ void chunk_stage_ops(const Ops<128, 128, 128, kMaxT> &o, float *ob,
+template <int DK, int GATE>
+__device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, 128, kMaxT> &o, float *ob,
                                                 float scale, bool norm, int L, int tid) {
-    using Sh = TileShape<128, 128, 128, kMaxT>;
-    constexpr int DK = 128, TV = 128;
-    float *sd = ob, *sk = ob + 8 * DK, *sq = ob + 16 * DK, *sv = ob + 24 * DK;
-    float *sb = ob + 24 * DK + 8 * TV;
+    using Sh = TileShape<DK, 128, 128, kMaxT>;
+    constexpr int TV = 128;
+    float *sd = ob, *sk = ob + 8 * DK, *sq = ob + 16 * DK, *sv = ob + chunk_vbase<DK>();
+    float *sb = sv + 8 * TV;
 #pragma unroll
     for (int j = 0; j < Sh::GKV; ++j) {
         const int e = tid + j * 128;
         const int t = e * 4 / DK, i0 = e * 4 % DK;
+        if (t >= kMaxT) continue;
         float g;
         if constexpr (GATE == kGateGiven)
             g = __uint_as_float(o.g[j]);
@@ -1116,6 +1127,7 @@ __device__ __forceinline__ void chunk_stage_ops(const Ops<128, 128, 128, kMaxT> 
     for (int j = 0; j < Sh::KQV; ++j) {
         const int e = tid + j * 128;
         const int t = e * 8 / DK, i0 = e * 8 % DK;
+        if (t >= kMaxT) continue;  // uniform per 8-lane group; past the last token
         const uint32_t kw[4] = {o.k[j].x, o.k[j].y, o.k[j].z, o.k[j].w};
         const uint32_t qw[4] = {o.q[j].x, o.q[j].y, o.q[j].z, o.q[j].w};
         float ks = 1.f, qs = scale;
@@ -1162,35 +1174,38 @@ __device__ __forceinline__ void chunk_stage_ops(const Ops<128, 128, 128, kMaxT> 
     }
 }
 
-template <int GATE>
+template <int DK, int GATE>
 __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
-    constexpr int DK = 128, TV = 128, NT = 128;
-    // LDS: staged operands (chunk_stage_ops) | XT hi, lo [16][XS] | KA hi, lo [128][8] |
+    static_assert(DK == 64 || DK == 128, "chunk form: D_k = 64 or 128");
+    constexpr int TV = 128, NT = 128;
+    constexpr int NRB = DK / 16, NPB = DK / 32;  // row blocks of the tile, and their pairs
+    // LDS: staged operands (chunk_stage_ops) | XT hi, lo [16][XS] | KA hi, lo [D_k][8] |
     // UT [wave][hi, lo] [4 column sets][16][8] | diag(c_{n-1}) operands per row | G partials
     // [wave][64] | M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row)
     // takes the d, k and q planes of the staged operands once both waves have prepared their
-    // rows. The row stride of XT is padded (XS = 132) so the fragment reads of the 16 lanes
-    // of a lane group fall in different LDS banks; UT is ordered by column set for the same
-    // reason.
-    constexpr int XS = 132;
-    constexpr int OFF_XT = kChunkOps * 4;
+    // rows. The row stride of XT is padded (XS = D_k + 4) so the fragment reads of the 16
+    // lanes of a lane group fall in different LDS banks; UT is ordered by column set for the
+    // same reason. At D_k = 64 only wave 0 has rows to prepare.
+    constexpr int XS = DK + 4;
+    constexpr int VB = chunk_vbase<DK>();  // v plane, then beta, in the staged operands
+    constexpr int OFF_XT = chunk_ops<DK>() * 4;
     constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
-    constexpr int OFF_UT = OFF_KA + 2 * 128 * 8 * 2;
+    constexpr int OFF_UT = OFF_KA + 2 * DK * 8 * 2;
     constexpr int OFF_DG = OFF_UT + 2 * 2 * 64 * 8 * 2;
-    constexpr int OFF_GP = OFF_DG + 128 * 16;
+    constexpr int OFF_GP = OFF_DG + DK * 16;
     constexpr int OFF_GS = OFF_GP + 2 * 64 * 4;
     constexpr int BYTES = OFF_GS + 2 * 2 * 64 * 4;
     static_assert(BYTES % 16 == 0 && BYTES <= 40960, "LDS carve: four items per compute unit");
-    constexpr int YS = 20;  // floats per Y^T row: 16 values and a pad that spreads LDS banks
-    static_assert(128 * YS <= 24 * DK && (YS * 4) % 16 == 0, "Y^T fits the d, k, q planes");
-    static_assert(kChunkOps % 4 == 0, "16-byte aligned carve");
+    constexpr int YS = kChunkYS;
+    static_assert(128 * YS <= VB && (YS * 4) % 16 == 0, "Y^T fits the d, k, q planes");
+    static_assert(chunk_ops<DK>() % 4 == 0 && (2 * 16 * XS * 2) % 16 == 0, "16-byte aligned carve");
     __shared__ f32x4 lds4[BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
     float *ob = reinterpret_cast<float *>(lb);
     uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
-    uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + 128 * 8;
+    uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + DK * 8;
     u32x4 *dg = reinterpret_cast<u32x4 *>(lb + OFF_DG);
     float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
 
@@ -1207,12 +1222,16 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // all at once, the tile loads would block the wave for microseconds (the memory queues
     // are full) before it could stage or prepare anything; issued after the operands alone,
     // the memory system would idle while they arrive.
-    constexpr int PRE = RGDR_CHUNK_PRE, POST = RGDR_CHUNK_POST;
-    static_assert(PRE >= 0 && POST >= 0 && PRE + POST <= 8, "tile load placement");
+    constexpr int PRE = RGDR_CHUNK_PRE < NRB ? RGDR_CHUNK_PRE : NRB;
+    constexpr int POST = RGDR_CHUNK_POST < NRB - PRE ? RGDR_CHUNK_POST : NRB - PRE;
+    static_assert(PRE >= 0 && POST >= 0 && PRE + POST <= NRB, "tile load placement");
+    // Row blocks left for the preparation are issued by every thread's loop, so each wave
+    // must prepare rows then: true at D_k = 128; at D_k = 64 none are left.
+    static_assert(DK == 128 || PRE + POST == NRB, "interleaved loads need rows in both waves");
     const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
                               tile_range<DK, TV>(a, m));
     const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 64 * w + 4 * n16) * 2);
-    u32x2 raw[8][4];
+    u32x2 raw[NRB][4];
     auto load_rb = [&](int rb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1224,17 +1243,18 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 #pragma unroll
     for (int rb = 0; rb < PRE; ++rb) load_rb(rb);
     __builtin_amdgcn_sched_barrier(0);
-    chunk_stage_ops<GATE>(o, ob, a.scale, a.norm_qk != 0, L, tid);
+    chunk_stage_ops<DK, GATE>(o, ob, a.scale, a.norm_qk != 0, L, tid);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = PRE; rb < PRE + POST; ++rb) load_rb(rb);
     lds_barrier();
 
-    // Per-row preparation: thread r owns row r.
+    // Per-row preparation: thread r owns row r (uniform per wave: at D_k = 64 wave 1 has none).
     float gp[64];  // partial G: [t][s] (s <= t) holds N[t][s], [s][t] (s < t) holds M[t][s]
 #pragma unroll
     for (int e = 0; e < 64; ++e) gp[e] = 0.f;
-    {
+    const bool has_rows = 64 * w < DK;
+    if (has_rows) {
         const int row = tid;
         float d[8], k[8], q[8];
 #pragma unroll
@@ -1246,7 +1266,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
         float c = 1.f, cnv = 1.f;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            if (PRE + POST + t < 8) {  // the remaining tile loads, one row block per step
+            if (PRE + POST + t < NRB) {  // the remaining tile loads, one row block per step
                 __builtin_amdgcn_sched_barrier(0);
                 load_rb(PRE + POST + t);
                 __builtin_amdgcn_sched_barrier(0);
@@ -1296,7 +1316,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
                   kl[4] | ((uint32_t)kl[5] << 16), kl[6] | ((uint32_t)kl[7] << 16)};
     }
     // G over this wave's 64 rows: lane e holds entry e.
-    gpart[64 * w + lane] = wave_sum64_transposed(gp, lane);
+    gpart[64 * w + lane] = has_rows ? wave_sum64_transposed(gp, lane) : 0.f;
     lds_barrier();
     {
         // Entry e = 8 a + b of G, summed over the two halves of the rows, into this wave's
@@ -1325,7 +1345,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
+    for (int pb = 0; pb < NPB; ++pb) {
         const int r0 = 32 * pb + 4 * kg;
         const bf16x8 ah = pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
         const bf16x8 al = pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
@@ -1365,8 +1385,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     uint16_t o16[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const float v = ob[24 * DK + t * TV + col];
-        const float bt = ob[24 * DK + 8 * TV + t];
+        const float v = ob[VB + t * TV + col];
+        const float bt = ob[VB + 8 * TV + t];
         float p = yc[t];
 #pragma unroll
         for (int s2 = 0; s2 < t; ++s2) p = fmaf(gsM[t * 8 + s2], u[s2], p);
@@ -1400,7 +1420,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
                                tile_range<DK, TV>(a, m));
     if (n == 0) {  // nothing accepted: the incoming bytes
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb)
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 store8<RGDR_STATE_STORE_POLICY>(raw[rb][i], rso,
@@ -1427,7 +1447,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const uint16_t *ka_lane = (kg >> 1 ? ka_lo : ka_hi) + n16 * 8 + 4 * (kg & 1);
     const bool on_diag = (n16 >> 2) == kg;
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
+    for (int rb = 0; rb < NRB; ++rb) {
         const s16x4 ak = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ka_lane + 16 * rb * 8));
         const u32x4 dv = dg[16 * rb + n16];
         const s16x4 dh = __builtin_bit_cast(s16x4, make_uint2(on_diag ? dv.x : 0u, on_diag ? dv.y : 0u));
@@ -1519,10 +1539,10 @@ static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
 }
 
 // Shape/alignment checks shared by both entry points, then the launch of the form T picks.
-template <int GATE>
+template <int DK, int GATE>
 static hipError_t launch_chunk(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                const int32_t *nacc, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_chunk_kernel<GATE>), dim3(a.n_items), dim3(128), 0, stream, a,
+    hipLaunchKernelGGL((decode_chunk_kernel<DK, GATE>), dim3(a.n_items), dim3(128), 0, stream, a,
                        lens, idx, nacc);
     return hipGetLastError();
 }
@@ -1533,7 +1553,9 @@ template <int GATE>
 static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
                            const int32_t *L, const int32_t *I, const int32_t *N,
                            hipStream_t stream) {
-    if (form == kFormChunk) return launch_chunk<GATE>(a, L, I, N, stream);
+    if (form == kFormChunk)
+        return D_k == 128 ? launch_chunk<128, GATE>(a, L, I, N, stream)
+                          : launch_chunk<64, GATE>(a, L, I, N, stream);
     if (form == kFormWaveMulti) {
         if (D_k == 128) return launch_wave_multi<128, 64, GATE>(a, L, I, N, stream);
         return tile_v == 128 ? launch_wave_multi<64, 128, GATE>(a, L, I, N, stream)
@@ -1558,7 +1580,8 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_k == 128 && D_v % 128 == 0;
+    const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_v % 128 == 0 &&
+                       (D_k == 128 || RGDR_CHUNK_DK64);
     const Form form = T == 1 ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;
     // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token form
     // the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
