@@ -25,12 +25,13 @@
 //   then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q), and
 //   S_new = S' + k (x) u.
 //
-// Chunk form (1 < T <= 8 at D_k = 128, D_v a multiple of 128; decode_chunk_kernel). Two
+// Chunk form (1 < T <= 8, D_v a multiple of 128; decode_chunk_kernel). Two
 // waves own one (b, h, 128-column) tile; the item's L tokens are unrolled in closed form
 // (decay products, two 8 x 8 Gram matrices, a triangular solve), and the two dense
 // contractions of that form run on the matrix cores.
 //
-// Multi-token form (other 1 < T <= 8 shapes; decode_wave_multi_kernel). One wave owns one
+// Multi-token form (1 < T <= 8, D_v not a multiple of 128; decode_wave_multi_kernel). One
+// wave owns one
 // (b, h, 64- or 128-column) tile and keeps it in fp32 registers across the tokens, in a
 // scaled form that leaves three FMAs per element and token; the D_k reduction also
 // finishes inside the wave.
@@ -697,8 +698,8 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Wave form for 1 < T <= 8 where the chunk form does not apply (D_k = 64, or D_v not a
-// multiple of 128): one wave owns one (b, h, TV-column) tile over all D_k rows and
+// Wave form for 1 < T <= 8 where the chunk form does not apply (D_v not a multiple of
+// 128): one wave owns one (b, h, TV-column) tile over all D_k rows and
 // keeps it in fp32 registers through the tokens (R rows x 8 columns per lane, 128 values at
 // most); per token the D_k reduction finishes inside the wave, with no barrier and no LDS
 // exchange. One item per wave; the operands of all of the item's tokens are staged once in
@@ -952,7 +953,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 }
 
 // ---------------------------------------------------------------------------------------
-// Chunk form for 1 < T <= 8 at D_k = 128 with 128-column tiles: the item's L tokens are
+// Chunk form for 1 < T <= 8 at D_k = 64 or 128 with 128-column tiles: the item's L tokens are
 // evaluated together, on the matrix cores where the work is a dense contraction.
 //
 // With d_t the row decays of token t, c_t = d_0 ... d_t and g(t,s) = d_{s+1} ... d_t
@@ -969,13 +970,14 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 // products, the 8 x 8 matrices M and N, and the triangular solve for u, column by column)
 // is fp32 VALU.
 //
-// Two waves per item. Wave w owns tile columns 64 w .. 64 w + 63 over all 128 rows, so
+// Two waves per item. Wave w owns tile columns 64 w .. 64 w + 63 over all D_k rows, so
 // each wave's contraction, solve and update are complete for its columns; only the per-row
-// preparation (thread r: row r) is shared, through LDS, and two workgroup barriers suffice
-// (operands staged; rows prepared). Four items fit one compute unit, two waves per SIMD.
+// preparation (thread r: row r; at D_k = 64 wave 0 alone) is shared, through LDS, and two
+// workgroup barriers suffice (operands staged; rows prepared). At D_k = 128 four items fit
+// one compute unit, two waves per SIMD.
 //
 // Lane layout. Lane l = (kg, n16) = (l / 16, l % 16) of wave w loads rows 16 rb + 4 kg + i
-// (rb < 8, i < 4), columns 64 w + 4 n16 .. + 3: 16 lanes cover the wave's 128 bytes of a
+// (rb < D_k / 16, i < 4), columns 64 w + 4 n16 .. + 3: 16 lanes cover the wave's 128 bytes of a
 // row. For the contraction the tile's row index is the k index (the 8 k slots of lane group
 // kg hold its rows 4 kg + i of two row blocks) and column 64 w + 4 n + c is element n of
 // column set c. In the commit the block's own 4 rows per lane group are the k slots of
@@ -987,8 +989,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// The chunk form serves calls with T >= RGDR_CHUNK_MIN_T (at D_k = 128, D_v a multiple of
-// 128). Its time hardly depends on the tokens per item; the per-token form's grows with the
+// The chunk form serves calls with T >= RGDR_CHUNK_MIN_T and D_v a multiple of 128. Its time hardly depends on the tokens per item; the per-token form's grows with the
 // longest item, and is no lower even at 2 tokens.
 #ifndef RGDR_CHUNK_FORM
 #define RGDR_CHUNK_FORM 1

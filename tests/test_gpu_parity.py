@@ -127,14 +127,14 @@ SHAPES = [
     (4, 2, 2, 8, 128, 320, 6),    # 64-wide tiles, 5 per row (per-token form)
     (2, 4, 8, 5, 128, 384, 3),    # 128-wide tiles, 3 per row
     (5, 5, 5, 2, 128, 64, 9),
-    (1, 1, 8, 8, 64, 512, 2),     # MQA
+    (1, 1, 8, 8, 64, 512, 2),     # MQA; chunk form at D_k = 64
     (7, 2, 6, 4, 128, 128, 11),
     (6, 2, 4, 3, 128, 256, 8),    # T = 3 at D_k = 128: the chunk form, ragged items
     (4, 2, 4, 3, 128, 192, 7),    # T = 3 at D_k = 128, D_v = 192: the per-token multi-token form
     (9, 3, 6, 6, 128, 256, 12),   # the chunk form, 2 tiles per row
     (2, 1, 2, 1, 128, 4096, 3),   # the largest D_v: wave form, 32 tiles per row
     (2, 2, 2, 3, 128, 4096, 3),   # the largest D_v: chunk form
-    (2, 1, 1, 4, 64, 4096, 2),    # the largest D_v at D_k = 64: per-token multi-token form
+    (2, 1, 1, 4, 64, 4096, 2),    # the largest D_v at D_k = 64: chunk form, four row blocks
 ]
 
 
