@@ -122,8 +122,9 @@ def test_gated_varlen_T8_nan_padding(rg):
 
 
 def test_gated_fp16_projections(rg):
-    # wave form (T = 1), chunk form (T > 1, D_k = 128), per-token multi-token form (D_k = 64)
-    for shape in [(5, 2, 4, 1, 128, 128, 8), (4, 2, 4, 5, 128, 256, 8), (3, 2, 2, 3, 64, 192, 4)]:
+    # wave form (T = 1), chunk form (T > 1) at D_k = 128 and 64, per-token form (D_v = 192)
+    for shape in [(5, 2, 4, 1, 128, 128, 8), (4, 2, 4, 5, 128, 256, 8), (2, 2, 2, 4, 64, 128, 4),
+                  (3, 2, 2, 3, 64, 192, 4)]:
         B, Hq, Hv, T, Dk, Dv, N = shape
         inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=77, indices="choice",
                                   lengths="uniform", gate=True)
@@ -182,6 +183,7 @@ def raw_qk(inp, seed):
     (3, 1, 2, 1, 128, 192, 5),   # wave form, 64-column tiles
     (4, 2, 4, 6, 128, 128, 6),   # chunk form (T > 1, D_k = 128), varlen
     (3, 2, 2, 8, 64, 192, 4),    # per-token multi-token form, D_k = 64, 64-column tiles
+    (3, 2, 2, 5, 64, 256, 4),    # chunk form at D_k = 64
 ])
 def test_gated_normalize_qk(rg, shape):
     """RGDR_NORMALIZE_QK: raw q, k in, the oracle normalises them per token and head (fp64);
