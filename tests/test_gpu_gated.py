@@ -221,3 +221,48 @@ def test_gated_normalize_qk_is_noop_on_unit_inputs(rg):
     assert_tol(bf16_dev_to_f64(out1), bf16_dev_to_f64(out0), "unit inputs out")
     idx = inp.ssm_state_indices
     assert_tol(bf16_dev_to_f64(st1)[idx], bf16_dev_to_f64(st0)[idx], "unit inputs state")
+
+
+@pytest.mark.parametrize("case", ["workload3", "workload4", "per_token"])
+def test_gated_graph_replay_matches_eager(rg, case):
+    """The fused call captured in a HIP graph gives the eager bytes on every replay: the chunk
+    form (varlen T = 8), the wave form over several launches of the resident grid (B = 256)
+    and the per-token multi-token form (D_v = 192). Out-of-place, so every replay starts from
+    the same state; the output and state buffers are reset eagerly between replays."""
+    if case == "workload3":
+        inp = workloads.make_workload(3, gate_inputs=True)
+    elif case == "workload4":
+        inp = workloads.make_workload(4, gate_inputs=True)
+    else:
+        inp = workloads.make_case(6, 2, 4, 4, 128, 192, 8, seed=41, indices="choice",
+                                  lengths="uniform", gate=True)
+    say(f"gated graph replay: {case}")
+    d = upload(inp)
+    a, b, dt, ds = gate_tensors(inp)
+    out = torch.empty((inp.B, inp.Hv, inp.T, inp.Dv), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty_like(d["state"])
+
+    def step():
+        rg.rgdr_decode_gated(d["query"], d["key"], d["value"], a, b, dt, ds, d["state"],
+                             d["actual_seq_lengths"], d["ssm_state_indices"], d["gk"],
+                             d["num_accepted_tokens"], inp.scale, out=out, state_out=st)
+
+    st.copy_(d["state"])
+    step()
+    torch.cuda.synchronize()
+    want_out, want_st = dev_to_bits(out), dev_to_bits(st)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.fill_(1.0)
+        st.copy_(d["state"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_to_bits(out), want_out), f"{case} replay {rep}: out differs"
+        assert np.array_equal(dev_to_bits(st), want_st), f"{case} replay {rep}: state differs"

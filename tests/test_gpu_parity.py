@@ -204,16 +204,23 @@ def test_extreme_decays(rg, case, Dk):
 # ---------------------------------------------------------------------------------------
 
 
-def small_case(seed=5, B=6, T=4, lengths="uniform", **kw):
-    return workloads.make_case(B, 2, 4, T, 128, 128, 10, seed=seed, indices="choice",
+def small_case(seed=5, B=6, T=4, lengths="uniform", Dv=128, **kw):
+    return workloads.make_case(B, 2, 4, T, 128, Dv, 10, seed=seed, indices="choice",
                                lengths=lengths, **kw)
 
 
-def test_permutation_equivariance(rg):
-    inp = small_case()
+# (T, D_v) that select each kernel form: the wave form (T = 1), the chunk form (T > 1, D_v a
+# multiple of 128) and the per-token multi-token form (T > 1, D_v = 192)
+FORMS = {"wave": (1, 128), "chunk": (4, 128), "per_token": (4, 192)}
+
+
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_permutation_equivariance(rg, form):
+    T, Dv = FORMS[form]
+    inp = small_case(T=T, Dv=Dv)
     out, st = gpu_decode(inp)
     perm = np.array([3, 0, 5, 1, 4, 2])
-    p = small_case()
+    p = small_case(T=T, Dv=Dv)
     for name in ("query", "key", "value", "beta", "g", "gk", "ssm_state_indices",
                  "actual_seq_lengths", "num_accepted_tokens"):
         setattr(p, name, np.ascontiguousarray(getattr(inp, name)[perm]))
@@ -222,10 +229,12 @@ def test_permutation_equivariance(rg):
     assert np.array_equal(dev_to_bits(st_p), dev_to_bits(st))
 
 
-def test_out_of_range_slot_skips_row(rg):
-    inp = small_case()
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_out_of_range_slot_skips_row(rg, form):
+    T, Dv = FORMS[form]
+    inp = small_case(T=T, Dv=Dv)
     out, st = gpu_decode(inp)
-    bad = small_case()
+    bad = small_case(T=T, Dv=Dv)
     bad.ssm_state_indices = inp.ssm_state_indices.copy()
     bad.ssm_state_indices[1] = -1
     bad.ssm_state_indices[4] = inp.N_slots + 5
@@ -241,15 +250,17 @@ def test_out_of_range_slot_skips_row(rg):
     for b in keep:
         s = inp.ssm_state_indices[b]
         assert np.array_equal(sb[s], dev_to_bits(st)[s])
-    check_decode(bad, out_b, st_b, oracle_decode(bad), "out-of-range slots")
+    check_decode(bad, out_b, st_b, oracle_decode(bad), f"out-of-range slots ({form})")
 
 
-def test_gqa_expansion_bitexact(rg):
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_gqa_expansion_bitexact(rg, form):
     """Value head h reads query/key head floor(h H_q / H_v): expanding the shared heads
     and calling with H_q = H_v gives identical bytes."""
-    inp = workloads.make_case(3, 4, 16, 2, 128, 128, 4, seed=9, indices="choice")
+    T, Dv = FORMS[form]
+    inp = workloads.make_case(3, 4, 16, T, 128, Dv, 4, seed=9, indices="choice")
     out, st = gpu_decode(inp)
-    e = workloads.make_case(3, 4, 16, 2, 128, 128, 4, seed=9, indices="choice")
+    e = workloads.make_case(3, 4, 16, T, 128, Dv, 4, seed=9, indices="choice")
     e.query = np.ascontiguousarray(np.repeat(inp.query, 4, axis=1))
     e.key = np.ascontiguousarray(np.repeat(inp.key, 4, axis=1))
     e.Hq = 16
@@ -293,8 +304,10 @@ def test_zero_lengths_write_state_back(rg):
     assert np.array_equal(dev_to_bits(st), inp.state)
 
 
-def test_inplace_equals_out_of_place(rg):
-    inp = small_case()
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_inplace_equals_out_of_place(rg, form):
+    T, Dv = FORMS[form]
+    inp = small_case(T=T, Dv=Dv)
     out1, st1 = gpu_decode(inp)
     out2, st2 = gpu_decode(inp, inplace=True)
     assert np.array_equal(dev_to_bits(out1), dev_to_bits(out2))
