@@ -40,54 +40,23 @@
 // its lengths and slot (the accesses that must not happen get empty buffer ranges), and the
 // per-entry index arrays are read with scalar loads, so the in-order vector-memory counter
 // waits never drain the prefetched state. Results are deterministic.
+#include <atomic>
+
 #include "rgdr_common.h"
 
 namespace rgdr {
 
 constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 
-// Wave form (T = 1): ring length per tile width, and its grid: 0 = as many waves as fit at
-// once (persistent), 1 = one wave per item.
-#ifndef RGDR_WAVE_NBUF
-#define RGDR_WAVE_NBUF 2
-#endif
-#ifndef RGDR_WAVE_NBUF_128
-#define RGDR_WAVE_NBUF_128 1
-#endif
 // Tile width of the wave form: 128 columns (whole 256-byte rows at D_v = 128) when D_v
 // allows it, or 64.
 #ifndef RGDR_WAVE_TILE_V
 #define RGDR_WAVE_TILE_V 128
 #endif
-#ifndef RGDR_WAVE_ONE_SHOT
-#define RGDR_WAVE_ONE_SHOT 0
-#endif
+// Waves per SIMD the wave forms are compiled for (the register budget).
 #ifndef RGDR_WAVE_MIN_WAVES
 #define RGDR_WAVE_MIN_WAVES 2
 #endif
-// Persistent waves per CU for the wave form (0 = as many as fit).
-#ifndef RGDR_WAVE_PER_CU
-#define RGDR_WAVE_PER_CU 0
-#endif
-// Wave form with more items than resident waves: 1 = one launch per chunk of
-// (resident waves / RGDR_WAVE_CHUNK_DIV) items, one item per wave; 0 = one persistent launch
-// (waves walk items w, w + G, ...). Chunks keep each launch's reads ahead of its writes (the
-// whole chunk's tiles are requested at once, the commits follow), which streams faster on
-// MI355X than the read/write mix of persistent waves (71% against 63% of 8 TB/s at
-// B = 256, H_v = 32, D = 128); chunks smaller than the resident grid pay the launch's ramp
-// and drain more often and are slower.
-#ifndef RGDR_WAVE_CHUNKED
-#define RGDR_WAVE_CHUNKED 1
-#endif
-#ifndef RGDR_WAVE_CHUNK_DIV
-#define RGDR_WAVE_CHUNK_DIV 1
-#endif
-// Multi-token form: 1 = launch at most the resident grid at a time, 0 = all items at once
-// (the hardware starts waves as slots free up).
-#ifndef RGDR_MULTI_CHUNKED
-#define RGDR_MULTI_CHUNKED 0
-#endif
-
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -431,9 +400,20 @@ __device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
 // swaps) with no LDS exchange and no barrier; waves run independently. Lane (cg, rg) holds
 // columns cg*8 .. cg*8+7 of rows rg, rg + RG, ... (RW = D_k / RG rows, packed bf16); a
 // wave-wide load covers RG consecutive tile rows. Operands are staged in a wave-private LDS
-// area (program order within one wave needs no barrier). Items are walked persistently
-// (item w, w + G, ...); a ring slot is refilled once its tile's commit has been issued.
+// area (program order within one wave needs no barrier). One item per wave: a call with
+// more items than the device holds waves at once is split into launches of the resident
+// grid (launch_wave).
 // ---------------------------------------------------------------------------------------
+
+// LDS per wave of the T = 1 wave form, in bytes. The operand area needs under 3 KiB; the
+// launch requests the rest as padding, which holds each compute unit to eight of these waves
+// (160 KiB of LDS), two per SIMD, as many as the register budget RGDR_WAVE_MIN_WAVES is built
+// for. With room for a third wave per SIMD the dispatcher fills some SIMDs with three and
+// leaves others short, and a call with more items than resident waves streams slower: 98.3
+// to 100.5 against 96.4 us at B = 256, H_v = 32, D = 128. The padding is requested at launch
+// (dynamic LDS), not declared in the kernel: declared, it changed the compiler's schedule
+// (169 VGPRs, 96 SGPRs against 166 and 73) and the same workload took 98.2 us.
+constexpr int kWaveLdsBytes = 19968;
 
 template <int DK, int TVW>
 struct WaveShape {
@@ -443,6 +423,8 @@ struct WaveShape {
     static constexpr int RPL = DK / 64;   // operand rows loaded per lane (1 or 2)
     static constexpr int VPL = TVW / 64;  // v values loaded per lane (1 or 2)
     static constexpr int OPS = 4 * DK + TVW + 4;  // (d, k, scale*q, 0) per row | v | beta
+    static constexpr int LDS_PAD = kWaveLdsBytes - 4 * OPS;  // dynamic LDS requested at launch
+    static_assert(LDS_PAD >= 0, "operand area");
     static_assert(DK == 64 || DK == 128, "D_k");
     static_assert(TVW == 64 || TVW == 128, "tile width");
 };
@@ -540,12 +522,6 @@ __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, 
     if (lane == 0) ob[4 * DK + TVW] = bt;
 }
 
-template <int DK, int TVW, int NBUF>
-struct WavePipe {
-    u32x4 raw[NBUF][WaveShape<DK, TVW>::RW];
-    WaveOps<DK> ops[2];
-};
-
 template <int DK, int TVW>
 __device__ __forceinline__ void wave_load_state(const DecodeArgs &a, const Item &m,
                                                 u32x4 (&raw)[WaveShape<DK, TVW>::RW], int cg,
@@ -563,22 +539,27 @@ __device__ __forceinline__ void wave_load_state(const DecodeArgs &a, const Item 
                                                        RGDR_STATE_LOAD_POLICY);
 }
 
-template <int DK, int TVW, int NBUF, int GATE, int P>
-__device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x,
-                                             WavePipe<DK, TVW, NBUF> &pl, float *lds, int &it,
-                                             int lane) {
+template <int DK, int TVW, int GATE>
+__global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
+    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nacc) {
     using Sh = WaveShape<DK, TVW>;
     constexpr int RW = Sh::RW, RG = Sh::RG, LPW = Sh::LPW;
-    if (it >= a.n_items) return false;
-    const int G = gridDim.x;
+    __shared__ f32x4 lds4[Sh::OPS / 4];
+    float *ob = reinterpret_cast<float *>(lds4);
+    const int lane = threadIdx.x;
     const int cg = lane % LPW, rg = lane / LPW;
-    const Item m = resolve(a, x, it);
+    const Item m = resolve(a, Index{lens, idx, nacc}, a.item0 + xcd_item(blockIdx.x, gridDim.x));
+    // The tile first, then the operands. Staging the operands then waits for the whole tile
+    // (the vector memory counter is in order), which costs nothing because the reduction
+    // needs all of it anyway, and the tile's requests reach the memory queues sooner: 23.9
+    // against 25.0 us at B = 64, H_v = 32, D = 128 with the operands issued first.
+    u32x4 W[RW];
+    wave_load_state<DK, TVW>(a, m, W, cg, rg);
+    WaveOps<DK> ops;
+    wave_load_ops<DK, TVW, GATE>(a, m, ops, lane);
+    wave_stage_ops<DK, TVW, GATE>(ops, ob, a.scale, a.norm_qk != 0, lane);
 
-    wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it + G), pl.ops[(P + 1) & 1], lane);
-    float *ob = lds + (P & 1) * Sh::OPS;
-    wave_stage_ops<DK, TVW, GATE>(pl.ops[P & 1], ob, a.scale, a.norm_qk != 0, lane);
-
-    u32x4(&W)[RW] = pl.raw[P % NBUF];
     // Step 1 (decay) fused with the partial sums of steps 2 and 4.
     float pk[8], pq[8];
     float kq = 0.f;
@@ -656,44 +637,6 @@ __device__ __forceinline__ bool wave_process(const DecodeArgs &a, const Index &x
             store16<RGDR_STATE_STORE_POLICY>(u32x4{nw[0], nw[1], nw[2], nw[3]}, rso,
                                              lane_off + r * row_step);
         }
-    }
-    wave_load_state<DK, TVW>(a, resolve(a, x, it + NBUF * G), W, cg, rg);
-    it += G;
-    return true;
-}
-
-template <int DK, int TVW, int NBUF, int GATE, int P, int U>
-__device__ __forceinline__ bool wave_phases(const DecodeArgs &a, const Index &x,
-                                            WavePipe<DK, TVW, NBUF> &pl, float *lds, int &it,
-                                            int lane) {
-    if constexpr (P == U) {
-        return true;
-    } else {
-        return wave_process<DK, TVW, NBUF, GATE, P>(a, x, pl, lds, it, lane) &&
-               wave_phases<DK, TVW, NBUF, GATE, P + 1, U>(a, x, pl, lds, it, lane);
-    }
-}
-
-template <int DK, int TVW, int NBUF, int GATE>
-__global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
-    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nacc) {
-    using Sh = WaveShape<DK, TVW>;
-    const Index x{lens, idx, nacc};
-    __shared__ f32x4 lds4[2 * Sh::OPS / 4];  // two operand buffers (item parity)
-    float *lds = reinterpret_cast<float *>(lds4);
-    const int lane = threadIdx.x;
-    const int cg = lane % Sh::LPW, rg = lane / Sh::LPW;
-    const int G = gridDim.x;
-    int it = a.item0 + xcd_item(blockIdx.x, gridDim.x);
-    WavePipe<DK, TVW, NBUF> pl;
-    // Operands first: staging them waits only for them, while the tile is still in flight.
-    wave_load_ops<DK, TVW, GATE>(a, resolve(a, x, it), pl.ops[0], lane);
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j)
-        wave_load_state<DK, TVW>(a, resolve(a, x, it + j * G), pl.raw[j], cg, rg);
-    constexpr int U = NBUF % 2 == 0 ? NBUF : 2 * NBUF;
-    while (wave_phases<DK, TVW, NBUF, GATE, 0, U>(a, x, pl, lds, it, lane)) {
     }
 }
 
@@ -1470,76 +1413,65 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     }
 }
 
+// Waves of decode_wave_kernel<DK, TVW, GATE> the current device holds at once (compute units
+// times waves per compute unit), queried once per device; 0 if the query fails.
+template <int DK, int TVW, int GATE>
+static int resident_waves() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, decode_wave_kernel<DK, TVW, GATE>, 64, WaveShape<DK, TVW>::LDS_PAD) !=
+                hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    n = cus * per_cu;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// T = 1: one wave per item. A call with more items than resident waves becomes launches of
+// the resident grid, one after another on the stream. Each launch requests all of its tiles
+// before its commits start, which streams faster than waves that walk several items and
+// mix one item's commit with the next one's reads (71% against 63% of 8 TB/s at B = 256,
+// H_v = 32, D = 128); launches of a smaller grid pay the ramp and drain more often.
 template <int DK, int TVW, int GATE>
 static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                               const int32_t *nacc, hipStream_t stream) {
-    constexpr int NBUF = TVW == 128 ? RGDR_WAVE_NBUF_128 : RGDR_WAVE_NBUF;
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cached[dev] <= 0) {
-        int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            return hipErrorInvalidDevice;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, decode_wave_kernel<DK, TVW, NBUF, GATE>, 64, 0) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        if (RGDR_WAVE_PER_CU > 0 && RGDR_WAVE_PER_CU < per_cu) per_cu = RGDR_WAVE_PER_CU;
-        cached[dev] = cus * per_cu;
-    }
-    const int chunk = cached[dev] / RGDR_WAVE_CHUNK_DIV > 0 ? cached[dev] / RGDR_WAVE_CHUNK_DIV : 1;
-    if (RGDR_WAVE_CHUNKED && a.n_items > chunk) {
-        DecodeArgs c = a;
-        for (int first = 0; first < a.n_items; first += chunk) {
-            c.item0 = first;
-            c.n_items = a.n_items - first < chunk ? a.n_items : first + chunk;
-            hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, NBUF, GATE>),
-                               dim3(c.n_items - first), dim3(64), 0, stream, c, lens, idx, nacc);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }
-    const int grid = (RGDR_WAVE_ONE_SHOT || a.n_items < cached[dev]) ? a.n_items : cached[dev];
-    hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, NBUF, GATE>), dim3(grid), dim3(64), 0, stream,
-                       a, lens, idx, nacc);
-    return hipGetLastError();
-}
-
-template <int DK, int TV, int GATE>
-static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
-                                    const int32_t *idx, const int32_t *nacc,
-                                    hipStream_t stream) {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cached[dev] <= 0) {
-        int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            return hipErrorInvalidDevice;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, decode_wave_multi_kernel<DK, TV, GATE>, 64, 0) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        cached[dev] = cus * per_cu;
-    }
-    const int chunk = RGDR_MULTI_CHUNKED ? cached[dev] : a.n_items;
+    constexpr int pad = WaveShape<DK, TVW>::LDS_PAD;
+    const int chunk = resident_waves<DK, TVW, GATE>();
+    if (chunk <= 0) return hipErrorInvalidDevice;
     DecodeArgs c = a;
     for (int first = 0; first < a.n_items; first += chunk) {
         c.item0 = first;
         c.n_items = a.n_items - first < chunk ? a.n_items : first + chunk;
-        hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE>), dim3(c.n_items - first),
-                           dim3(64), 0, stream, c, lens, idx, nacc);
+        hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, GATE>), dim3(c.n_items - first), dim3(64),
+                           pad, stream, c, lens, idx, nacc);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-// Shape/alignment checks shared by both entry points, then the launch of the form T picks.
+// 1 < T <= 8 with D_v not a multiple of 128: one wave per item, all items in one launch (the
+// hardware starts waves as slots free up).
+template <int DK, int TV, int GATE>
+static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
+                                    const int32_t *idx, const int32_t *nacc,
+                                    hipStream_t stream) {
+    hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE>), dim3(a.n_items), dim3(64), 0,
+                       stream, a, lens, idx, nacc);
+    return hipGetLastError();
+}
+
+// 2 <= T <= 8 with D_v a multiple of 128: one workgroup of two waves per item, all items in
+// one launch.
 template <int DK, int GATE>
 static hipError_t launch_chunk(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                const int32_t *nacc, hipStream_t stream) {
@@ -1569,6 +1501,8 @@ static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
                       : launch_wave<64, 64, GATE>(a, L, I, N, stream);
 }
 
+// Shape and alignment checks shared by both entry points, then the launch of the form that
+// T and the head sizes pick.
 static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
                                 int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
                                 const int32_t *lens, const int32_t *idx, const int32_t *nacc,
