@@ -408,11 +408,11 @@ __device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
 // LDS per wave of the T = 1 wave form, in bytes. The operand area needs under 3 KiB; the
 // launch requests the rest as padding, which holds each compute unit to eight of these waves
 // (160 KiB of LDS), two per SIMD, as many as the register budget RGDR_WAVE_MIN_WAVES is built
-// for. With room for a third wave per SIMD the dispatcher fills some SIMDs with three and
-// leaves others short, and a call with more items than resident waves streams slower: 98.3
-// to 100.5 against 96.4 us at B = 256, H_v = 32, D = 128. The padding is requested at launch
-// (dynamic LDS), not declared in the kernel: declared, it changed the compiler's schedule
-// (169 VGPRs, 96 SGPRs against 166 and 73) and the same workload took 98.2 us.
+// for. With room for a third wave per SIMD, a call with more items than resident waves
+// (split into launches of the larger resident grid) streams slower: 98.3 to 100.5 against
+// 96.4 us at B = 256, H_v = 32, D = 128. The padding is requested at launch (dynamic LDS),
+// not declared in the kernel: declared, it changed the compiler's schedule (169 VGPRs and
+// 96 SGPRs against 166 and 73) and the same workload took 98.2 us.
 constexpr int kWaveLdsBytes = 19968;
 
 template <int DK, int TVW>
