@@ -101,6 +101,9 @@ struct DecodeArgs {
     int Hq, Hv, T, Dv, N_slots, ntiles, group, n_items;
     int norm_qk;  // fused front end only: L2-normalise each token's q and k head vector
     int item0;    // first item of this launch (items item0 .. n_items-1)
+    // T = 1 wave form: ticks of the constant wall clock (s_memrealtime) each wave waits,
+    // counted from its own start, before it writes its tile back; 0 = no wait.
+    int hold;
 };
 
 // How an item's g and beta arrive: given (bf16 beta, fp32 g), or computed from raw gate
@@ -415,6 +418,16 @@ __device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
 // 96 SGPRs against 166 and 73) and the same workload took 98.2 us.
 constexpr int kWaveLdsBytes = 19968;
 
+// Commit hold of the T = 1 wave form: the read rate its length assumes, in GB/s (HBM's
+// streaming read rate on this part for large reads), and a cap on its polls of the clock
+// (each poll sleeps 128 cycles). Swept at B = 64 and 256, H_v = 32, D = 128: 6000 GB/s
+// 23.3 and 93.4 us, 6250 22.8 and 92.0, 6500 22.8 and 92.3, 6750 23.1 and 93.4, 7000 23.3
+// and 94.3, no hold 23.9 and 96.7.
+#ifndef RGDR_HOLD_READ_GBPS
+#define RGDR_HOLD_READ_GBPS 6400
+#endif
+constexpr int kHoldMaxPolls = 4096;
+
 template <int DK, int TVW>
 struct WaveShape {
     static constexpr int LPW = TVW / 8;   // lanes across one tile row
@@ -422,7 +435,7 @@ struct WaveShape {
     static constexpr int RW = DK / RG;    // rows per lane
     static constexpr int RPL = DK / 64;   // operand rows loaded per lane (1 or 2)
     static constexpr int VPL = TVW / 64;  // v values loaded per lane (1 or 2)
-    static constexpr int OPS = 4 * DK + TVW + 4;  // (d, k, scale*q, 0) per row | v | beta
+    static constexpr int OPS = 4 * DK + TVW;  // (d, k, scale*q, 0) per row | v
     static constexpr int LDS_PAD = kWaveLdsBytes - 4 * OPS;  // dynamic LDS requested at launch
     static_assert(LDS_PAD >= 0, "operand area");
     static_assert(DK == 64 || DK == 128, "D_k");
@@ -479,34 +492,42 @@ __device__ __forceinline__ void wave_load_ops(const DecodeArgs &a, const Item &m
     o.present = m.L > 0;
 }
 
+// Stages the rows' (d, k, scale q) and the v tile in the wave's LDS area and returns beta.
+// Every lane loaded beta (or b) itself and keeps it in a register: a value that only one
+// lane wrote to LDS let the compiler sink its load into that lane's branch, after the
+// tile's arrival, which put a memory round trip into the middle of the reduction.
 template <int DK, int TVW, int GATE>
-__device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, float scale,
-                                               bool norm, int lane) {
+__device__ __forceinline__ float wave_stage_ops(const WaveOps<DK> &o, float *ob, float scale,
+                                                bool norm, int lane) {
     using Sh = WaveShape<DK, TVW>;
     float g, bt;
     if constexpr (GATE == kGateGiven) {
         g = __uint_as_float(o.g);
         bt = bf16_to_f32((uint16_t)o.beta);
     } else {
-        // An absent token keeps decay 1 (its other operands are all zero).
-        g = o.present ? o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g) + o.dt) : 0.f;
+        // An absent token keeps decay 1 (its other operands are all zero): the gate is
+        // computed either way and masked, with no branch. A uniform branch here let the
+        // compiler sink the tile loads below it, after the gate loads and their waits.
+        const float sp = o.ds * softplus_fast(gate_value<GATE == kGateF16>(o.g) + o.dt);
+        g = __uint_as_float(__float_as_uint(sp) & (0u - (uint32_t)o.present));
         bt = sigmoid_fast(gate_value<GATE == kGateF16>(o.beta));
     }
     const float eg = __expf(g);
     float ks = 1.f, qs = scale;
     if constexpr (GATE != kGateGiven) {
-        if (norm) {  // uniform; the wave holds the whole head vector (RPL values per lane)
-            float kss = 0.f, qss = 0.f;
+        // Optional L2 normalisation, also without a branch (the wave holds the whole head
+        // vector, RPL values per lane).
+        float kss = 0.f, qss = 0.f;
 #pragma unroll
-            for (int j = 0; j < Sh::RPL; ++j) {
-                const float kv = __uint_as_float(j ? o.k & 0xFFFF0000u : o.k << 16);
-                const float qv = __uint_as_float(j ? o.q & 0xFFFF0000u : o.q << 16);
-                kss = fmaf(kv, kv, kss);
-                qss = fmaf(qv, qv, qss);
-            }
-            ks = inv_norm(group_sum<64>(kss));
-            qs = scale * inv_norm(group_sum<64>(qss));
+        for (int j = 0; j < Sh::RPL; ++j) {
+            const float kv = __uint_as_float(j ? o.k & 0xFFFF0000u : o.k << 16);
+            const float qv = __uint_as_float(j ? o.q & 0xFFFF0000u : o.q << 16);
+            kss = fmaf(kv, kv, kss);
+            qss = fmaf(qv, qv, qss);
         }
+        const float kn = inv_norm(group_sum<64>(kss)), qn = inv_norm(group_sum<64>(qss));
+        ks = norm ? kn : 1.f;
+        qs = norm ? scale * qn : scale;
     }
 #pragma unroll
     for (int j = 0; j < Sh::RPL; ++j) {
@@ -519,7 +540,7 @@ __device__ __forceinline__ void wave_stage_ops(const WaveOps<DK> &o, float *ob, 
         *reinterpret_cast<float2 *>(ob + 4 * DK + 2 * lane) = make_float2(bf16_lo(o.v), bf16_hi(o.v));
     else
         ob[4 * DK + lane] = bf16_lo(o.v);
-    if (lane == 0) ob[4 * DK + TVW] = bt;
+    return bt;
 }
 
 template <int DK, int TVW>
@@ -549,16 +570,19 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     float *ob = reinterpret_cast<float *>(lds4);
     const int lane = threadIdx.x;
     const int cg = lane % LPW, rg = lane / LPW;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const Item m = resolve(a, Index{lens, idx, nacc}, a.item0 + xcd_item(blockIdx.x, gridDim.x));
     // The tile first, then the operands. Staging the operands then waits for the whole tile
     // (the vector memory counter is in order), which costs nothing because the reduction
     // needs all of it anyway, and the tile's requests reach the memory queues sooner: 23.9
-    // against 25.0 us at B = 64, H_v = 32, D = 128 with the operands issued first.
+    // against 25.0 us at B = 64, H_v = 32, D = 128 with the operands issued first. The
+    // staging has no branch: the compiler sinks loads whose results are used only after a
+    // branch below it, which had put the operand loads and their waits ahead of the tile.
     u32x4 W[RW];
     wave_load_state<DK, TVW>(a, m, W, cg, rg);
     WaveOps<DK> ops;
     wave_load_ops<DK, TVW, GATE>(a, m, ops, lane);
-    wave_stage_ops<DK, TVW, GATE>(ops, ob, a.scale, a.norm_qk != 0, lane);
+    const float bt = wave_stage_ops<DK, TVW, GATE>(ops, ob, a.scale, a.norm_qk != 0, lane);
 
     // Step 1 (decay) fused with the partial sums of steps 2 and 4.
     float pk[8], pq[8];
@@ -592,7 +616,6 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     const f32x4 *vv = reinterpret_cast<const f32x4 *>(ob + 4 * DK + cg * 8);
     const f32x4 v0 = vv[0], v1 = vv[1];
     const float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const float bt = ob[4 * DK + TVW];
     // Step 3 (delta update) and step 4 (output with the updated state).
     float u[8], o[8];
 #pragma unroll
@@ -616,6 +639,18 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     // registers as redefined so the compiler cannot reuse those values.
 #pragma unroll
     for (int r = 0; r < RW; ++r) asm volatile("" : "+v"(W[r]));
+    // Commit hold: no tile is written back before the launch's reads could all have
+    // completed (a.hold, set by launch_wave). HBM streams reads and writes best in separate
+    // phases, and waves whose tiles arrive early would otherwise start writing while most
+    // reads are still in flight. The wait is bounded by the clock and by an iteration cap,
+    // so it ends whatever other work shares the device; results never depend on it.
+    if (a.hold > 0) {
+        const uint64_t until = t0 + (uint64_t)a.hold;
+        for (int i = 0; i < kHoldMaxPolls; ++i) {
+            if (__builtin_amdgcn_s_memrealtime() >= until) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
     const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TVW>(a, m) : 0),
                                tile_range<DK, TVW>(a, m));
     const uint32_t lane_off = (uint32_t)((rg * a.Dv + cg * 8) * 2);
@@ -1436,6 +1471,23 @@ static int resident_waves() {
     return n;
 }
 
+// Ticks of the device's constant wall clock per microsecond (100 on this part), queried once
+// per device; 0 if the query fails (then no commit hold).
+static int wall_ticks_per_us() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz < 1000)
+        return 0;
+    n = khz / 1000;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // T = 1: one wave per item. A call with more items than resident waves becomes launches of
 // the resident grid, one after another on the stream. Each launch requests all of its tiles
 // before its commits start, which streams faster than waves that walk several items and
@@ -1447,10 +1499,15 @@ static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const in
     constexpr int pad = WaveShape<DK, TVW>::LDS_PAD;
     const int chunk = resident_waves<DK, TVW, GATE>();
     if (chunk <= 0) return hipErrorInvalidDevice;
+    const int ticks_per_us = wall_ticks_per_us();
     DecodeArgs c = a;
     for (int first = 0; first < a.n_items; first += chunk) {
         c.item0 = first;
         c.n_items = a.n_items - first < chunk ? a.n_items : first + chunk;
+        // The launch's tile bytes at the assumed read rate, in clock ticks (bytes / (GB/s)
+        // is in nanoseconds).
+        const double read_ns = (double)(c.n_items - first) * DK * TVW * 2 / RGDR_HOLD_READ_GBPS;
+        c.hold = (int)(read_ns * 1e-3 * ticks_per_us);
         hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, GATE>), dim3(c.n_items - first), dim3(64),
                            pad, stream, c, lens, idx, nacc);
         const hipError_t e = hipGetLastError();
