@@ -436,3 +436,40 @@ def test_graph_replay_matches_eager(rg):
         torch.cuda.synchronize()
         assert np.array_equal(dev_to_bits(out), want_out), f"replay {rep}: out differs"
         assert np.array_equal(dev_to_bits(st), want_st), f"replay {rep}: state differs"
+
+
+def test_concurrent_streams_and_host_threads(rg):
+    """Calls on two streams at once, issued from two host threads, give the bytes of the same
+    calls made one after another: a wave-form call (T = 1, several launches of the resident
+    grid) and a chunk-form call (T = 8) on separate pools."""
+    import threading
+
+    cases = [workloads.make_case(96, 16, 32, 1, 128, 128, 128, seed=71, indices="choice"),
+             workloads.make_case(24, 8, 16, 8, 128, 256, 30, seed=72, indices="choice",
+                                 lengths="uniform")]
+    devs = [upload(c) for c in cases]
+    want = [gpu_decode(c, d) for c, d in zip(cases, devs)]
+    got = [None, None]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    start = threading.Barrier(2)
+
+    def run(i):
+        c, d = cases[i], devs[i]
+        with torch.cuda.stream(streams[i]):
+            pool = d["state"].clone()
+            start.wait()
+            got[i] = rg.rgdr_decode(d["query"], d["key"], d["value"], d["beta"], pool,
+                                    d["actual_seq_lengths"], d["ssm_state_indices"], d["g"],
+                                    d["gk"], d["num_accepted_tokens"], c.scale,
+                                    stream=streams[i])
+            streams[i].synchronize()
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert np.array_equal(dev_to_bits(got[i][0]), dev_to_bits(want[i][0])), f"case {i}: out"
+        assert np.array_equal(dev_to_bits(got[i][1]), dev_to_bits(want[i][1])), f"case {i}: state"
