@@ -414,8 +414,8 @@ __device__ __forceinline__ void load_state(const DecodeArgs &a, const Item &m,
 // for. With room for a third wave per SIMD, a call with more items than resident waves
 // (split into launches of the larger resident grid) streams slower: 98.3 to 100.5 against
 // 96.4 us at B = 256, H_v = 32, D = 128. The padding is requested at launch (dynamic LDS),
-// not declared in the kernel: declared, it changed the compiler's schedule (169 VGPRs and
-// 96 SGPRs against 166 and 73) and the same workload took 98.2 us.
+// not declared in the kernel: declared, it let the compiler schedule for the lower
+// occupancy (more registers, a different order) and the same workload took 98.2 us.
 constexpr int kWaveLdsBytes = 19968;
 
 // Commit hold of the T = 1 wave form: the read rate its length assumes, in GB/s (HBM's
