@@ -1558,6 +1558,17 @@ static hipError_t dispatch(const DecodeArgs &a, int D_k, int tile_v, Form form,
                       : launch_wave<64, 64, GATE>(a, L, I, N, stream);
 }
 
+// Waves of the T = 1 wave form with 64-column tiles that the current device holds at once.
+static int wave_resident_64(int D_k, int gate) {
+    if (D_k == 128)
+        return gate == kGateGiven ? resident_waves<128, 64, kGateGiven>()
+               : gate == kGateF32 ? resident_waves<128, 64, kGateF32>()
+                                  : resident_waves<128, 64, kGateF16>();
+    return gate == kGateGiven ? resident_waves<64, 64, kGateGiven>()
+           : gate == kGateF32 ? resident_waves<64, 64, kGateF32>()
+                              : resident_waves<64, 64, kGateF16>();
+}
+
 // Shape and alignment checks shared by both entry points, then the launch of the form that
 // T and the head sizes pick.
 static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
@@ -1575,11 +1586,21 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
     const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_v % 128 == 0 &&
                        (D_k == 128 || RGDR_CHUNK_DK64);
     const Form form = T == 1 ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;
-    // Tile widths: whole 256-byte rows for T = 1 when D_v allows; for the multi-token form
-    // the widest tile whose fp32 copy fits a lane (D_k x TV <= 64 x 128 values / wave).
-    const int tile_v = form == kFormWave ? ((RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) ? 128 : 64)
-                       : form == kFormChunk ? 128
-                                            : ((D_k == 64 && D_v % 128 == 0) ? 128 : 64);
+    // Tile widths. For the multi-token form, the widest tile whose fp32 copy fits a lane
+    // (D_k x TV <= 64 x 128 values per wave). For T = 1, 64-column tiles while the whole call
+    // then fits in one launch of the resident grid: twice the waves, each with half the
+    // bytes and half the arithmetic, shorten a launch whose waves are not limited by the
+    // memory system's rate (at H_v = 32, D = 128: 5.4 against 7.6 us at B = 1, 9.1 against
+    // 10.6 at B = 16, 12.9 against 15.2 at B = 32). Past that, whole 256-byte rows (128
+    // columns) when D_v allows: at B = 48 the narrow tiles need two launches (21.8 against
+    // 19.2 us), and at B = 64 they stream worse (25.7 against 23.1 us).
+    int tile_v = form == kFormChunk ? 128 : 64;
+    if (form == kFormWaveMulti && D_k == 64 && D_v % 128 == 0) tile_v = 128;
+    if (form == kFormWave && RGDR_WAVE_TILE_V == 128 && D_v % 128 == 0) {
+        const int resident = wave_resident_64(D_k, gate);
+        if (resident <= 0) return RGDR_ERR_HIP;
+        if ((long long)B * H_v * (D_v / 64) > resident) tile_v = 128;
+    }
     const long long items = (long long)B * H_v * (D_v / tile_v);
     if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
     a.Hq = H_q;

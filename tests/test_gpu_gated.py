@@ -178,12 +178,13 @@ def raw_qk(inp, seed):
 
 
 @pytest.mark.parametrize("shape", [
-    (4, 2, 4, 1, 128, 128, 6),   # wave form, 128-column tiles, D_k = 128
+    (4, 2, 4, 1, 128, 128, 6),   # wave form, D_k = 128 (64-column tiles: a small call)
     (3, 2, 2, 1, 64, 128, 4),    # wave form, D_k = 64
     (3, 1, 2, 1, 128, 192, 5),   # wave form, 64-column tiles
     (4, 2, 4, 6, 128, 128, 6),   # chunk form (T > 1, D_k = 128), varlen
     (3, 2, 2, 8, 64, 192, 4),    # per-token multi-token form, D_k = 64, 64-column tiles
     (3, 2, 2, 5, 64, 256, 4),    # chunk form at D_k = 64
+    (40, 4, 16, 1, 64, 512, 48),  # wave form, 128-column tiles at D_k = 64 (large call)
 ])
 def test_gated_normalize_qk(rg, shape):
     """RGDR_NORMALIZE_QK: raw q, k in, the oracle normalises them per token and head (fp64);

@@ -132,9 +132,11 @@ SHAPES = [
     (6, 2, 4, 3, 128, 256, 8),    # T = 3 at D_k = 128: the chunk form, ragged items
     (4, 2, 4, 3, 128, 192, 7),    # T = 3 at D_k = 128, D_v = 192: the per-token multi-token form
     (9, 3, 6, 6, 128, 256, 12),   # the chunk form, 2 tiles per row
-    (2, 1, 2, 1, 128, 4096, 3),   # the largest D_v: wave form, 32 tiles per row
+    (2, 1, 2, 1, 128, 4096, 3),   # the largest D_v: wave form, 64 tiles per row
     (2, 2, 2, 3, 128, 4096, 3),   # the largest D_v: chunk form
     (2, 1, 1, 4, 64, 4096, 2),    # the largest D_v at D_k = 64: chunk form, four row blocks
+    (40, 4, 16, 1, 64, 512, 48),  # T = 1 with more 64-column items than resident waves:
+                                  # 128-column tiles at D_k = 64, two launches
 ]
 
 
