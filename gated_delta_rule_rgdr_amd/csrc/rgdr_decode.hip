@@ -19,7 +19,12 @@
 //     barrier and run independently; operands sit in a wave-private LDS area;
 //   * one item per wave per launch (a call with more items than resident waves becomes
 //     several launches); items past the end and skipped entries use empty buffer ranges
-//     (no data moves).
+//     (no data moves);
+//   * each wave requests its tile before its operands, and holds its commit until the
+//     launch's reads could have completed, so that HBM sees a read phase and then a write
+//     phase;
+//   * 64-column tiles while the call fits one launch of the resident grid with them, else
+//     128-column tiles (whole 256-byte rows).
 //   Per token, steps 2 and 4 share ONE reduction over D_k. With S' the decayed state,
 //   p = S'^T k and r = S'^T (scale q) are reduced together with the scalar k.(scale q);
 //   then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q), and
@@ -31,10 +36,9 @@
 // contractions of that form run on the matrix cores.
 //
 // Multi-token form (1 < T <= 8, D_v not a multiple of 128; decode_wave_multi_kernel). One
-// wave owns one
-// (b, h, 64- or 128-column) tile and keeps it in fp32 registers across the tokens, in a
-// scaled form that leaves three FMAs per element and token; the D_k reduction also
-// finishes inside the wave.
+// wave owns one (b, h, 64- or 128-column) tile and keeps it in fp32 registers across the
+// tokens, in a scaled form that leaves three FMAs per element and token; the D_k reduction
+// also finishes inside the wave.
 //
 // All forms: every item issues the same sequence of vector memory instructions whatever
 // its lengths and slot (the accesses that must not happen get empty buffer ranges), and the
@@ -48,8 +52,8 @@ namespace rgdr {
 
 constexpr int kMaxT = 8;  // decode only: at most 8 tokens per call
 
-// Tile width of the wave form: 128 columns (whole 256-byte rows at D_v = 128) when D_v
-// allows it, or 64.
+// Widest tile of the wave form (T = 1): 128 columns (whole 256-byte rows at D_v = 128) when
+// D_v and the call's size call for it (decode_entry), or always 64.
 #ifndef RGDR_WAVE_TILE_V
 #define RGDR_WAVE_TILE_V 128
 #endif
