@@ -45,6 +45,7 @@
 // per-entry index arrays are read with scalar loads, so the in-order vector-memory counter
 // waits never drain the prefetched state. Results are deterministic.
 #include <atomic>
+#include <cstdlib>
 
 #include "rgdr_common.h"
 
@@ -1492,6 +1493,19 @@ static int wall_ticks_per_us() {
     return n;
 }
 
+// The read rate the commit hold assumes, in GB/s: the environment variable
+// RGDR_HOLD_READ_GBPS when it holds a number (0 turns the hold off; read on every call, so a
+// process can change it between calls), else the built-in RGDR_HOLD_READ_GBPS.
+static double hold_read_gbps() {
+    const char *e = std::getenv("RGDR_HOLD_READ_GBPS");
+    if (e && *e) {
+        char *end = nullptr;
+        const double v = std::strtod(e, &end);
+        if (end != e && v >= 0.0) return v;
+    }
+    return RGDR_HOLD_READ_GBPS;
+}
+
 // T = 1: one wave per item. A call with more items than resident waves becomes launches of
 // the resident grid, one after another on the stream. Each launch requests all of its tiles
 // before its commits start, which streams faster than waves that walk several items and
@@ -1504,14 +1518,17 @@ static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const in
     const int chunk = resident_waves<DK, TVW, GATE>();
     if (chunk <= 0) return hipErrorInvalidDevice;
     const int ticks_per_us = wall_ticks_per_us();
+    const double gbps = hold_read_gbps();
     DecodeArgs c = a;
     for (int first = 0; first < a.n_items; first += chunk) {
         c.item0 = first;
         c.n_items = a.n_items - first < chunk ? a.n_items : first + chunk;
         // The launch's tile bytes at the assumed read rate, in clock ticks (bytes / (GB/s)
         // is in nanoseconds).
-        const double read_ns = (double)(c.n_items - first) * DK * TVW * 2 / RGDR_HOLD_READ_GBPS;
-        c.hold = (int)(read_ns * 1e-3 * ticks_per_us);
+        const double read_ns =
+            gbps > 0.0 ? (double)(c.n_items - first) * DK * TVW * 2 / gbps : 0.0;
+        const double ticks = read_ns * 1e-3 * ticks_per_us;
+        c.hold = ticks < 1e9 ? (int)ticks : 1000000000;
         hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, GATE>), dim3(c.n_items - first), dim3(64),
                            pad, stream, c, lens, idx, nacc);
         const hipError_t e = hipGetLastError();

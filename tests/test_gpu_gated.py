@@ -267,3 +267,17 @@ def test_gated_graph_replay_matches_eager(rg, case):
         torch.cuda.synchronize()
         assert np.array_equal(dev_to_bits(out), want_out), f"{case} replay {rep}: out differs"
         assert np.array_equal(dev_to_bits(st), want_st), f"{case} replay {rep}: state differs"
+
+
+@pytest.mark.parametrize("rate", ["0", "100"])
+def test_commit_hold_never_changes_results(rg, monkeypatch, rate):
+    """The T = 1 commit hold only delays the stores: with it off (rate 0) or very long (an
+    assumed read rate of 100 GB/s, so the poll cap ends it) the fused call at the bench
+    shape writes the same bytes as with the default hold."""
+    inp = workloads.make_workload(2, gate_inputs=True)
+    d = upload(inp)
+    out0, st0 = gpu_gated(rg, inp, d=d)
+    monkeypatch.setenv("RGDR_HOLD_READ_GBPS", rate)
+    out1, st1 = gpu_gated(rg, inp, d=d)
+    assert np.array_equal(dev_to_bits(out0), dev_to_bits(out1))
+    assert np.array_equal(dev_to_bits(st0), dev_to_bits(st1))
