@@ -281,3 +281,24 @@ def test_commit_hold_never_changes_results(rg, monkeypatch, rate):
     out1, st1 = gpu_gated(rg, inp, d=d)
     assert np.array_equal(dev_to_bits(out0), dev_to_bits(out1))
     assert np.array_equal(dev_to_bits(st0), dev_to_bits(st1))
+
+
+def test_gated_wide_tiles_absent_and_rejected(rg):
+    """The fused T = 1 call with 128-column tiles (a call too large for 64-column tiles in
+    one launch): absent (L = 0) and rejected (n = 0) tokens commit the incoming state bit for
+    bit and write +0.0 where absent; the rest meets the bar."""
+    B = 40
+    lens = np.ones(B, np.int32)
+    lens[2::5] = 0
+    inp = workloads.make_case(B, 16, 32, 1, 128, 128, 44, seed=83, indices="choice",
+                              lengths=lens, gate=True)
+    inp.num_accepted_tokens = lens.copy()
+    inp.num_accepted_tokens[1::4] = 0
+    out, st = gpu_gated(rg, inp)
+    bits = dev_to_bits(st)
+    for b in range(B):
+        if lens[b] == 0 or inp.num_accepted_tokens[b] == 0:
+            s = inp.ssm_state_indices[b]
+            assert np.array_equal(bits[s], inp.state[s]), f"entry {b}: state changed"
+    assert np.all(dev_to_bits(out)[lens == 0] == 0)
+    check_gated(inp, out, st, oracle_gated(inp), "gated wide tiles absent/rejected")

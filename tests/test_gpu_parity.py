@@ -475,3 +475,26 @@ def test_concurrent_streams_and_host_threads(rg):
     for i in range(2):
         assert np.array_equal(dev_to_bits(got[i][0]), dev_to_bits(want[i][0])), f"case {i}: out"
         assert np.array_equal(dev_to_bits(got[i][1]), dev_to_bits(want[i][1])), f"case {i}: state"
+
+
+@pytest.mark.parametrize("shape", [(40, 16, 32, 128, 128, 48), (40, 4, 16, 64, 512, 48)],
+                         ids=["Dk128", "Dk64_Dv512"])
+def test_single_token_wide_tiles_absent_and_rejected(rg, shape):
+    """T = 1 calls large enough for 128-column tiles (more 64-column items than resident
+    waves): absent tokens (L = 0) and rejected ones (n = 0) commit the incoming state bit
+    for bit, out-of-range slots are skipped, and everything else meets the bar."""
+    B, Hq, Hv, Dk, Dv, N = shape
+    lens = np.ones(B, np.int32)
+    lens[3::7] = 0
+    inp = workloads.make_case(B, Hq, Hv, 1, Dk, Dv, N, seed=81, indices="choice",
+                              lengths=lens)
+    inp.num_accepted_tokens = lens.copy()
+    inp.num_accepted_tokens[5::6] = 0
+    inp.ssm_state_indices[11] = -1
+    out, st = gpu_decode(inp)
+    bits = dev_to_bits(st)
+    for b in range(B):
+        s = inp.ssm_state_indices[b]
+        if 0 <= s < inp.N_slots and (lens[b] == 0 or inp.num_accepted_tokens[b] == 0):
+            assert np.array_equal(bits[s], inp.state[s]), f"entry {b}: state changed"
+    check_decode(inp, out, st, oracle_decode(inp), f"wide tiles {shape}")
