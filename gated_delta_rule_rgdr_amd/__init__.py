@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the computation runs in the HIP kernels of
 ``librgdr.so``; PyTorch supplies device memory and the current stream. There is no CPU
-fallback: if the library is missing, importing the binding's functions raises.
+fallback: if the library is missing, the first call of any binding function raises
+``ImportError``.
 
 * ``rgdr_decode``  -- the recurrent gated-delta-rule decode step (MindSpore Lite API page
   "lite_boost.ops.recurrent_gated_delta_rule"), in place on a bf16 state pool.

@@ -158,3 +158,20 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(RuntimeError, match="GPU"):
         g.rgdr_decode(q, q, q, q[..., 0], q, *([torch.zeros(1, dtype=torch.int32)] * 2),
                       q.float()[..., 0], q.float(), torch.zeros(1, dtype=torch.int32))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """With no librgdr.so the binding raises on its first call; nothing falls back to the
+    CPU (the call never reaches an argument check or a computation)."""
+    import torch
+
+    import gated_delta_rule_rgdr_amd as g
+    monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "librgdr.so"))
+    monkeypatch.setattr(g, "_lib", None)
+    with pytest.raises(ImportError, match="no fallback"):
+        g.library()
+    x = torch.zeros(1)
+    with pytest.raises(ImportError):
+        g.rgdr_decode(x, x, x, x, x, x, x, x, x, x)
+    with pytest.raises(ImportError):
+        g.la_gate(x, x, x)
