@@ -30,12 +30,13 @@
 //   then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q), and
 //   S_new = S' + k (x) u.
 //
-// Chunk form (1 < T <= 8, D_v a multiple of 128; decode_chunk_kernel). Two
-// waves own one (b, h, 128-column) tile; the item's L tokens are unrolled in closed form
-// (decay products, two 8 x 8 Gram matrices, a triangular solve), and the two dense
-// contractions of that form run on the matrix cores.
+// Chunk form (1 < T <= 8, except D_v = 64 with T < 5; where D_v is an odd multiple of 64 the
+// last tile is 64 columns wide; decode_chunk_kernel). Two waves own
+// one (b, h, 128-column) tile; the item's L tokens are unrolled in closed form (decay
+// products, two 8 x 8 Gram matrices, a triangular solve), and the two dense contractions of
+// that form run on the matrix cores.
 //
-// Multi-token form (1 < T <= 8, D_v not a multiple of 128; decode_wave_multi_kernel). One
+// Multi-token form (the other calls with 1 < T <= 8; decode_wave_multi_kernel). One
 // wave owns one (b, h, 64- or 128-column) tile and keeps it in fp32 registers across the
 // tokens, in a scaled form that leaves three FMAs per element and token; the D_k reduction
 // also finishes inside the wave.
@@ -972,8 +973,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// The chunk form serves calls with T >= RGDR_CHUNK_MIN_T and D_v a multiple of 128. Its time hardly depends on the tokens per item; the per-token form's grows with the
-// longest item, and is no lower even at 2 tokens.
+// The chunk form serves calls with T >= RGDR_CHUNK_MIN_T. Its time hardly depends on the
+// tokens per item; the per-token form's grows with the longest item, and is no lower even at
+// 2 tokens.
 #ifndef RGDR_CHUNK_FORM
 #define RGDR_CHUNK_FORM 1
 #endif
@@ -983,6 +985,20 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // The chunk form at D_k = 64 too (0: those calls take the per-token form).
 #ifndef RGDR_CHUNK_DK64
 #define RGDR_CHUNK_DK64 1
+#endif
+// The chunk form for D_v an odd multiple of 64 too, with a last tile of 64 columns (0: those
+// calls take the per-token form). The half tile leaves one of its two waves idle. Measured,
+// H = 32, D_k = 128, all lengths T (chunk against per-token): D_v = 192, B = 32: T = 2 24.6
+// against 25.8 us, T = 3 24.2 against 27.3, T = 8 25.7 against 39.1; D_v = 320, T = 3 35.8
+// against 39.5. At D_v = 64 every tile is half: B = 16 gains from T = 3 (8.7 against
+// 9.1 us), but B = 64 needs two rounds of items and loses at T = 4 (21.2 against 19.3 us),
+// ties near T = 5 and gains at T = 6 (21.4 against 23.2). D_v = 64 therefore takes the chunk
+// form from RGDR_CHUNK_DV64_MIN_T tokens.
+#ifndef RGDR_CHUNK_HALF_TILE
+#define RGDR_CHUNK_HALF_TILE 1
+#endif
+#ifndef RGDR_CHUNK_DV64_MIN_T
+#define RGDR_CHUNK_DV64_MIN_T 5
 #endif
 // Where the chunk form issues its tile loads: RGDR_CHUNK_PRE row blocks with the operand
 // loads, RGDR_CHUNK_POST more once the operands are staged, the rest one block per token
@@ -1212,8 +1228,14 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // Row blocks left for the preparation are issued by every thread's loop, so each wave
     // must prepare rows then: true at D_k = 128; at D_k = 64 none are left.
     static_assert(DK == 128 || PRE + POST == NRB, "interleaved loads need rows in both waves");
-    const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0),
-                              tile_range<DK, TV>(a, m));
+    // A last tile of 64 columns (D_v an odd multiple of 64) leaves wave 1 without columns:
+    // its tile, output and state accesses get empty ranges (its columns would alias the
+    // next row's), and it computes on zeros that nothing reads.
+    // (w is the same in every lane of a wave; readfirstlane tells the compiler so, which
+    // keeps the buffer descriptors built from it in scalar registers.)
+    const bool cols = m.tile * TV + 64 * __builtin_amdgcn_readfirstlane(w) < a.Dv;
+    const uint32_t trange = cols ? tile_range<DK, TV>(a, m) : 0u;
+    const auto rs = make_rsrc(a.pool + (m.state ? tile_base<DK, TV>(a, m) : 0), trange);
     const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 64 * w + 4 * n16) * 2);
     u32x2 raw[NRB][4];
     auto load_rb = [&](int rb) {
@@ -1351,7 +1373,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // Triangular solve, column 64 w + lane; outputs; u of the accepted prefix.
     const int col = 64 * w + lane;
     const size_t bh = (size_t)m.b * a.Hv + m.h;
-    const auto rout = make_rsrc(a.out + bh * a.T * a.Dv, (uint32_t)(a.T * a.Dv * 2));
+    const auto rout = make_rsrc(a.out + bh * a.T * a.Dv, cols ? (uint32_t)(a.T * a.Dv * 2) : 0u);
     const uint32_t ocol = (uint32_t)((m.tile * TV + col) * 2);
     float yc[16];  // this column of Y: [c k]^T S0 for t < 8, then [c scale q]^T S0
 #pragma unroll
@@ -1400,8 +1422,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 
     lds_phase();
     // Commit.
-    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
-                               tile_range<DK, TV>(a, m));
+    const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0), trange);
     if (n == 0) {  // nothing accepted: the incoming bytes
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
@@ -1604,8 +1625,10 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T && D_v % 128 == 0 &&
-                       (D_k == 128 || RGDR_CHUNK_DK64);
+    const bool chunk = RGDR_CHUNK_FORM && (D_k == 128 || RGDR_CHUNK_DK64) &&
+                       T >= RGDR_CHUNK_MIN_T &&
+                       (D_v % 128 == 0 ||
+                        (RGDR_CHUNK_HALF_TILE && (D_v > 64 || T >= RGDR_CHUNK_DV64_MIN_T)));
     const Form form = T == 1 ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;
     // Tile widths. For the multi-token form, the widest tile whose fp32 copy fits a lane
     // (D_k x TV <= 64 x 128 values per wave). For T = 1, 64-column tiles while the whole call
@@ -1622,14 +1645,15 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         if (resident <= 0) return RGDR_ERR_HIP;
         if ((long long)B * H_v * (D_v / 64) > resident) tile_v = 128;
     }
-    const long long items = (long long)B * H_v * (D_v / tile_v);
+    const int ntiles = (D_v + tile_v - 1) / tile_v;  // the chunk form's last tile may be half
+    const long long items = (long long)B * H_v * ntiles;
     if (items > 0x7FFFFFFFLL) return RGDR_ERR_SHAPE;
     a.Hq = H_q;
     a.Hv = H_v;
     a.T = T;
     a.Dv = D_v;
     a.N_slots = N_slots;
-    a.ntiles = D_v / tile_v;
+    a.ntiles = ntiles;
     a.group = H_v / H_q;
     a.n_items = (int)items;
     hipError_t err;

@@ -122,9 +122,9 @@ def test_gated_varlen_T8_nan_padding(rg):
 
 
 def test_gated_fp16_projections(rg):
-    # wave form (T = 1), chunk form (T > 1) at D_k = 128 and 64, per-token form (D_v = 192)
+    # wave form (T = 1), chunk form (T > 1) at D_k = 128 and 64, per-token form (D_v = 64)
     for shape in [(5, 2, 4, 1, 128, 128, 8), (4, 2, 4, 5, 128, 256, 8), (2, 2, 2, 4, 64, 128, 4),
-                  (3, 2, 2, 3, 64, 192, 4)]:
+                  (3, 2, 2, 3, 64, 64, 4)]:
         B, Hq, Hv, T, Dk, Dv, N = shape
         inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=77, indices="choice",
                                   lengths="uniform", gate=True)
@@ -182,7 +182,8 @@ def raw_qk(inp, seed):
     (3, 2, 2, 1, 64, 128, 4),    # wave form, D_k = 64
     (3, 1, 2, 1, 128, 192, 5),   # wave form, 64-column tiles
     (4, 2, 4, 6, 128, 128, 6),   # chunk form (T > 1, D_k = 128), varlen
-    (3, 2, 2, 8, 64, 192, 4),    # per-token multi-token form, D_k = 64, 64-column tiles
+    (3, 2, 2, 8, 64, 192, 4),    # chunk form with a last half tile, D_k = 64
+    (3, 2, 2, 3, 64, 64, 4),     # per-token multi-token form, D_k = 64, 64-column tiles
     (3, 2, 2, 5, 64, 256, 4),    # chunk form at D_k = 64
     (40, 4, 16, 1, 64, 512, 48),  # wave form, 128-column tiles at D_k = 64 (large call)
 ])
@@ -224,18 +225,20 @@ def test_gated_normalize_qk_is_noop_on_unit_inputs(rg):
     assert_tol(bf16_dev_to_f64(st1)[idx], bf16_dev_to_f64(st0)[idx], "unit inputs state")
 
 
-@pytest.mark.parametrize("case", ["workload3", "workload4", "per_token"])
+@pytest.mark.parametrize("case", ["workload3", "workload4", "chunk_half", "per_token"])
 def test_gated_graph_replay_matches_eager(rg, case):
     """The fused call captured in a HIP graph gives the eager bytes on every replay: the chunk
-    form (varlen T = 8), the wave form over several launches of the resident grid (B = 256)
-    and the per-token multi-token form (D_v = 192). Out-of-place, so every replay starts from
+    form (varlen T = 8), the wave form over several launches of the resident grid (B = 256),
+    the chunk form with a last half tile (D_v = 192) and the per-token multi-token form
+    (D_v = 64, T = 3). Out-of-place, so every replay starts from
     the same state; the output and state buffers are reset eagerly between replays."""
     if case == "workload3":
         inp = workloads.make_workload(3, gate_inputs=True)
     elif case == "workload4":
         inp = workloads.make_workload(4, gate_inputs=True)
     else:
-        inp = workloads.make_case(6, 2, 4, 4, 128, 192, 8, seed=41, indices="choice",
+        Dv = 192 if case == "chunk_half" else 64
+        inp = workloads.make_case(6, 2, 4, 3, 128, Dv, 8, seed=41, indices="choice",
                                   lengths="uniform", gate=True)
     say(f"gated graph replay: {case}")
     d = upload(inp)

@@ -123,18 +123,21 @@ def test_page_example_shapes(rg):
 SHAPES = [
     # B, Hq, Hv, T, Dk, Dv, N_slots
     (3, 2, 4, 1, 64, 64, 5),
-    (2, 1, 3, 3, 64, 192, 4),     # 64-wide tiles, 3 per row
-    (4, 2, 2, 8, 128, 320, 6),    # 64-wide tiles, 5 per row (per-token form)
+    (2, 1, 3, 3, 64, 192, 4),     # chunk form at D_k = 64, the second tile half
+    (4, 2, 2, 8, 128, 320, 6),    # chunk form, 3 tiles per row, the last one half
     (2, 4, 8, 5, 128, 384, 3),    # 128-wide tiles, 3 per row
     (5, 5, 5, 2, 128, 64, 9),
     (1, 1, 8, 8, 64, 512, 2),     # MQA; chunk form at D_k = 64
     (7, 2, 6, 4, 128, 128, 11),
     (6, 2, 4, 3, 128, 256, 8),    # T = 3 at D_k = 128: the chunk form, ragged items
-    (4, 2, 4, 3, 128, 192, 7),    # T = 3 at D_k = 128, D_v = 192: the per-token multi-token form
+    (4, 2, 4, 3, 128, 192, 7),    # T = 3 at D_k = 128, D_v = 192: chunk form, half last tile
     (9, 3, 6, 6, 128, 256, 12),   # the chunk form, 2 tiles per row
     (2, 1, 2, 1, 128, 4096, 3),   # the largest D_v: wave form, 64 tiles per row
     (2, 2, 2, 3, 128, 4096, 3),   # the largest D_v: chunk form
     (2, 1, 1, 4, 64, 4096, 2),    # the largest D_v at D_k = 64: chunk form, four row blocks
+    (3, 1, 2, 6, 64, 576, 4),     # chunk form at D_k = 64 with a last half tile
+    (3, 2, 4, 4, 128, 64, 5),     # D_v = 64 with T < 5: the per-token form
+    (3, 2, 4, 6, 64, 64, 5),      # D_v = 64 with T >= 5: the chunk form, one half tile
     (40, 4, 16, 1, 64, 512, 48),  # T = 1 with more 64-column items than resident waves:
                                   # 128-column tiles at D_k = 64, two launches
 ]
@@ -156,28 +159,35 @@ def test_shapes(rg, shape):
 # ---------------------------------------------------------------------------------------
 
 
+# The chunk form (T = 8, D_v = 128) and the per-token form (T = 4, D_v = 64), whose scaled
+# state folds its running decay into the tile when it would leave [2^-64, 2^64].
+EXTREME_FORMS = {"chunk": (8, 128, [8, 5, 8, 3], [8, 5, 6, 3], 8.0),
+                 "per_token": (4, 64, [4, 3, 4, 2], [4, 3, 2, 2], 12.0)}
+
+
+@pytest.mark.parametrize("form", sorted(EXTREME_FORMS))
 @pytest.mark.parametrize("Dk", [128, 64])
 @pytest.mark.parametrize("case", ["strong_decay", "growth", "zero_decay", "mixed_rows"])
-def test_extreme_decays(rg, case, Dk):
+def test_extreme_decays(rg, case, Dk, form):
+    T, Dv, lens, nacc, growth = EXTREME_FORMS[form]
     rng = np.random.default_rng(61)
-    inp = workloads.make_case(4, 2, 4, 8, Dk, 128, 6, seed=62, indices="choice",
-                              lengths=[8, 5, 8, 3])
-    inp.num_accepted_tokens = np.array([8, 5, 6, 3], np.int32)  # one early commit
+    inp = workloads.make_case(4, 2, 4, T, Dk, Dv, 6, seed=62, indices="choice", lengths=lens)
+    inp.num_accepted_tokens = np.array(nacc, np.int32)  # one early commit
     if case == "strong_decay":    # c falls below 2^-64 every other token
         inp.g[:] = -30.0
-    elif case == "growth":        # c passes 2^64 after six tokens
-        inp.g[:] = 8.0
+    elif case == "growth":        # c passes 2^64 before the last token
+        inp.g[:] = growth
     elif case == "zero_decay":    # exp(g) is exactly 0 at token 3: the state is wiped
         inp.g[:] = -1.0
         inp.g[:, :, 3] = -1000.0
     else:                         # every row on its own path
         inp.g[:] = rng.uniform(-25.0, 5.0, inp.g.shape).astype(np.float32)
         inp.gk[:] = -rng.uniform(0.0, 12.0, inp.gk.shape).astype(np.float32)
-    say(f"extreme decays: {case}, D_k {Dk}")
+    say(f"extreme decays: {case}, D_k {Dk}, {form} form")
     out, st = gpu_decode(inp)
     ref = oracle_decode(inp)
     if case != "growth":
-        check_decode(inp, out, st, ref, f"extreme {case} Dk{Dk}")
+        check_decode(inp, out, st, ref, f"extreme {case} Dk{Dk} {form}")
         return
     # Growth (exp(g) > 1) is outside the operator's domain (g and gk negative): states and
     # outputs grow by e^8 per token and a few outputs are near-total cancellations of terms
@@ -212,8 +222,9 @@ def small_case(seed=5, B=6, T=4, lengths="uniform", Dv=128, **kw):
 
 
 # (T, D_v) that select each kernel form: the wave form (T = 1), the chunk form (T > 1, D_v a
-# multiple of 128) and the per-token multi-token form (T > 1, D_v = 192)
-FORMS = {"wave": (1, 128), "chunk": (4, 128), "per_token": (4, 192)}
+# multiple of 128), the chunk form with a last half tile (D_v = 192) and the per-token
+# multi-token form (D_v = 64 with T < 5)
+FORMS = {"wave": (1, 128), "chunk": (4, 128), "chunk_half": (3, 192), "per_token": (3, 64)}
 
 
 @pytest.mark.parametrize("form", sorted(FORMS))
