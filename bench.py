@@ -207,7 +207,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the decode path has "
-              "no cross-GPU work; see the sharding notes in DESIGN.md", file=sys.stderr)
+              "no cross-GPU work (each GPU would serve its own state slots or heads on its "
+              "own), so more GPUs only repeat the one-GPU figure", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
