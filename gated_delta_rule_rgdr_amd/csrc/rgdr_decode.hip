@@ -30,8 +30,8 @@
 //   then u = beta (v - p) and o = r + (k.(scale q)) u, which equals S_new^T (scale q), and
 //   S_new = S' + k (x) u.
 //
-// Chunk form (1 < T <= 8, except D_v = 64 with T < 5; where D_v is an odd multiple of 64 the
-// last tile is 64 columns wide; decode_chunk_kernel). Two waves own
+// Chunk form (1 < T <= 8 at D_k = 128, 5 <= T <= 8 at D_k = 64 or D_v = 64; where D_v is an
+// odd multiple of 64 the last tile is 64 columns wide; decode_chunk_kernel). Two waves own
 // one (b, h, 128-column) tile; the item's L tokens are unrolled in closed form (decay
 // products, two 8 x 8 Gram matrices, a triangular solve), and the two dense contractions of
 // that form run on the matrix cores.
@@ -982,9 +982,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #ifndef RGDR_CHUNK_MIN_T
 #define RGDR_CHUNK_MIN_T 2
 #endif
-// The chunk form at D_k = 64 too (0: those calls take the per-token form).
+// The chunk form at D_k = 64 too (0: those calls take the per-token form), from
+// RGDR_CHUNK_DK64_MIN_T tokens. At D_k = 64 a chunk-form item holds half the state bytes
+// for the same fixed work, and its LDS fits five items per compute unit, so large calls
+// need more rounds of items than the per-token form needs of waves. Measured, all lengths T
+// (chunk against per-token): B = 64, H = 32, D_v = 128: T = 2 17.9 against 13.0 us, T = 3
+// 18.3 against 15.0, T = 4 19.3 against 16.8, T = 5 18.7 against 18.7; B = 16, H = 64,
+// D_v = 512: T = 2 29.8 against 29.3, T = 3 29.8 against 31.4, and at T = 8 (varlen)
+// 30.8 against 37.8.
 #ifndef RGDR_CHUNK_DK64
 #define RGDR_CHUNK_DK64 1
+#endif
+#ifndef RGDR_CHUNK_DK64_MIN_T
+#define RGDR_CHUNK_DK64_MIN_T 5
 #endif
 // The chunk form for D_v an odd multiple of 64 too, with a last tile of 64 columns (0: those
 // calls take the per-token form). The half tile leaves one of its two waves idle. Measured,
@@ -1625,8 +1635,8 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const bool chunk = RGDR_CHUNK_FORM && (D_k == 128 || RGDR_CHUNK_DK64) &&
-                       T >= RGDR_CHUNK_MIN_T &&
+    const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T &&
+                       (D_k == 128 || (RGDR_CHUNK_DK64 && T >= RGDR_CHUNK_DK64_MIN_T)) &&
                        (D_v % 128 == 0 ||
                         (RGDR_CHUNK_HALF_TILE && (D_v > 64 || T >= RGDR_CHUNK_DV64_MIN_T)));
     const Form form = T == 1 ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;

@@ -122,8 +122,8 @@ def test_gated_varlen_T8_nan_padding(rg):
 
 
 def test_gated_fp16_projections(rg):
-    # wave form (T = 1), chunk form (T > 1) at D_k = 128 and 64, per-token form (D_v = 64)
-    for shape in [(5, 2, 4, 1, 128, 128, 8), (4, 2, 4, 5, 128, 256, 8), (2, 2, 2, 4, 64, 128, 4),
+    # wave form (T = 1), chunk form at D_k = 128 and 64, per-token form (D_v = 64, T = 3)
+    for shape in [(5, 2, 4, 1, 128, 128, 8), (4, 2, 4, 5, 128, 256, 8), (2, 2, 2, 5, 64, 128, 4),
                   (3, 2, 2, 3, 64, 64, 4)]:
         B, Hq, Hv, T, Dk, Dv, N = shape
         inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=77, indices="choice",

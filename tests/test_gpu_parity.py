@@ -123,7 +123,8 @@ def test_page_example_shapes(rg):
 SHAPES = [
     # B, Hq, Hv, T, Dk, Dv, N_slots
     (3, 2, 4, 1, 64, 64, 5),
-    (2, 1, 3, 3, 64, 192, 4),     # chunk form at D_k = 64, the second tile half
+    (2, 1, 3, 3, 64, 192, 4),     # D_k = 64 with T < 5: the per-token form, 64-wide tiles
+    (2, 1, 3, 5, 64, 192, 4),     # chunk form at D_k = 64, the second tile half
     (4, 2, 2, 8, 128, 320, 6),    # chunk form, 3 tiles per row, the last one half
     (2, 4, 8, 5, 128, 384, 3),    # 128-wide tiles, 3 per row
     (5, 5, 5, 2, 128, 64, 9),
@@ -134,7 +135,8 @@ SHAPES = [
     (9, 3, 6, 6, 128, 256, 12),   # the chunk form, 2 tiles per row
     (2, 1, 2, 1, 128, 4096, 3),   # the largest D_v: wave form, 64 tiles per row
     (2, 2, 2, 3, 128, 4096, 3),   # the largest D_v: chunk form
-    (2, 1, 1, 4, 64, 4096, 2),    # the largest D_v at D_k = 64: chunk form, four row blocks
+    (2, 1, 1, 5, 64, 4096, 2),    # the largest D_v at D_k = 64: chunk form, four row blocks
+    (2, 1, 1, 4, 64, 4096, 2),    # the largest D_v at D_k = 64, T < 5: the per-token form
     (3, 1, 2, 6, 64, 576, 4),     # chunk form at D_k = 64 with a last half tile
     (3, 2, 4, 4, 128, 64, 5),     # D_v = 64 with T < 5: the per-token form
     (3, 2, 4, 6, 64, 64, 5),      # D_v = 64 with T >= 5: the chunk form, one half tile
