@@ -433,6 +433,10 @@ constexpr int kWaveLdsBytes = 19968;
 #define RGDR_HOLD_READ_GBPS 6400
 #endif
 constexpr int kHoldMaxPolls = 4096;
+// Launches of the T = 1 wave form that read at most this many tile bytes issue their
+// operand loads before their tile (see decode_wave_kernel): 16.8 MB launches gained 15%,
+// 33.5 MB ones were even, 67 MB ones lost 2%.
+constexpr double kOpsFirstBytes = 24.0 * 1024 * 1024;
 
 template <int DK, int TVW>
 struct WaveShape {
@@ -566,7 +570,7 @@ __device__ __forceinline__ void wave_load_state(const DecodeArgs &a, const Item 
                                                        RGDR_STATE_LOAD_POLICY);
 }
 
-template <int DK, int TVW, int GATE>
+template <int DK, int TVW, int GATE, bool OPS_FIRST>
 __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
@@ -578,16 +582,26 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     const int cg = lane % LPW, rg = lane / LPW;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const Item m = resolve(a, Index{lens, idx, nacc}, a.item0 + xcd_item(blockIdx.x, gridDim.x));
-    // The tile first, then the operands. Staging the operands then waits for the whole tile
-    // (the vector memory counter is in order), which costs nothing because the reduction
-    // needs all of it anyway, and the tile's requests reach the memory queues sooner: 23.9
-    // against 25.0 us at B = 64, H_v = 32, D = 128 with the operands issued first. The
-    // staging has no branch: the compiler sinks loads whose results are used only after a
-    // branch below it, which had put the operand loads and their waits ahead of the tile.
+    // Load order. Large launches request the tile first, then the operands: staging the
+    // operands then waits for the whole tile (the vector memory counter is in order), which
+    // costs nothing because the reduction needs all of it anyway, and the tile's requests
+    // reach the saturated memory queues sooner (22.9 against 23.4 us at B = 64, H_v = 32,
+    // D = 128; 94.4 against 96.2 us at B = 256). Small launches, whose memory queues are
+    // not full, request the operands first, so the gate and staging arithmetic runs while
+    // the tile is in flight (B = 8: 6.5 against 7.5 us; B = 16: 7.8 against 9.1 us; one
+    // sequence of 64 heads at D_k = 64, D_v = 512: 5.0 against 5.4 us). The scheduling fence
+    // keeps the compiler from merging the two groups. The staging has no branch: the
+    // compiler sinks loads whose results are used only after a branch below them.
     u32x4 W[RW];
-    wave_load_state<DK, TVW>(a, m, W, cg, rg);
     WaveOps<DK> ops;
-    wave_load_ops<DK, TVW, GATE>(a, m, ops, lane);
+    if constexpr (OPS_FIRST) {
+        wave_load_ops<DK, TVW, GATE>(a, m, ops, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_load_state<DK, TVW>(a, m, W, cg, rg);
+    } else {
+        wave_load_state<DK, TVW>(a, m, W, cg, rg);
+        wave_load_ops<DK, TVW, GATE>(a, m, ops, lane);
+    }
     const float bt = wave_stage_ops<DK, TVW, GATE>(ops, ob, a.scale, a.norm_qk != 0, lane);
 
     // Step 1 (decay) fused with the partial sums of steps 2 and 4.
@@ -1498,7 +1512,7 @@ static int resident_waves() {
         cus <= 0)
         return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, decode_wave_kernel<DK, TVW, GATE>, 64, WaveShape<DK, TVW>::LDS_PAD) !=
+            &per_cu, decode_wave_kernel<DK, TVW, GATE, false>, 64, WaveShape<DK, TVW>::LDS_PAD) !=
                 hipSuccess ||
         per_cu < 1)
         per_cu = 1;
@@ -1560,8 +1574,13 @@ static hipError_t launch_wave(const DecodeArgs &a, const int32_t *lens, const in
             gbps > 0.0 ? (double)(c.n_items - first) * DK * TVW * 2 / gbps : 0.0;
         const double ticks = read_ns * 1e-3 * ticks_per_us;
         c.hold = ticks < 1e9 ? (int)ticks : 1000000000;
-        hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, GATE>), dim3(c.n_items - first), dim3(64),
-                           pad, stream, c, lens, idx, nacc);
+        const double tile_bytes = (double)(c.n_items - first) * DK * TVW * 2;
+        if (tile_bytes <= kOpsFirstBytes)
+            hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, GATE, true>), dim3(c.n_items - first),
+                               dim3(64), pad, stream, c, lens, idx, nacc);
+        else
+            hipLaunchKernelGGL((decode_wave_kernel<DK, TVW, GATE, false>), dim3(c.n_items - first),
+                               dim3(64), pad, stream, c, lens, idx, nacc);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
