@@ -511,3 +511,13 @@ def test_single_token_wide_tiles_absent_and_rejected(rg, shape):
         if 0 <= s < inp.N_slots and (lens[b] == 0 or inp.num_accepted_tokens[b] == 0):
             assert np.array_equal(bits[s], inp.state[s]), f"entry {b}: state changed"
     check_decode(inp, out, st, oracle_decode(inp), f"wide tiles {shape}")
+
+
+@pytest.mark.parametrize("B", [24, 25, 33])
+def test_single_token_load_order_and_tile_width_boundaries(rg, B):
+    """T = 1 at H_v = 32, D = 128 around the launch-size boundaries: B = 24 reads 24 MiB of
+    64-column tiles (operands first), B = 25 a little more (tile first), B = 33 no longer
+    fits one launch with 64-column tiles (128-column tiles). All meet the bar."""
+    inp = workloads.make_case(B, 16, 32, 1, 128, 128, B + 8, seed=90 + B, indices="choice")
+    out, st = gpu_decode(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"T = 1 boundaries, B = {B}")
