@@ -20,9 +20,9 @@
 //   * one item per wave per launch (a call with more items than resident waves becomes
 //     several launches); items past the end and skipped entries use empty buffer ranges
 //     (no data moves);
-//   * each wave requests its tile before its operands, and holds its commit until the
-//     launch's reads could have completed, so that HBM sees a read phase and then a write
-//     phase;
+//   * in large launches each wave requests its tile before its operands (small launches:
+//     operands first), and every wave holds its commit until the launch's reads could have
+//     completed, so that HBM sees a read phase and then a write phase;
 //   * 64-column tiles while the call fits one launch of the resident grid with them, else
 //     128-column tiles (whole 256-byte rows).
 //   Per token, steps 2 and 4 share ONE reduction over D_k. With S' the decayed state,
