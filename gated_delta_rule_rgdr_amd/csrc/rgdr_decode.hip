@@ -588,7 +588,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_kernel(
     // reach the saturated memory queues sooner (22.9 against 23.4 us at B = 64, H_v = 32,
     // D = 128; 94.4 against 96.2 us at B = 256). Small launches, whose memory queues are
     // not full, request the operands first, so the gate and staging arithmetic runs while
-    // the tile is in flight (B = 8: 6.5 against 7.5 us; B = 16: 7.8 against 9.1 us; one
+    // the tile is in flight (B = 8: 6.5 against 7.4 us; B = 16: 7.8 against 9.1 us; one
     // sequence of 64 heads at D_k = 64, D_v = 512: 5.0 against 5.4 us). The scheduling fence
     // keeps the compiler from merging the two groups. The staging has no branch: the
     // compiler sinks loads whose results are used only after a branch below them.
@@ -1511,11 +1511,18 @@ static int resident_waves() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         return 0;
+    // Both issue orders are launched (by the launch's size); a launch must fit one round of
+    // either, so the smaller of the two occupancies counts.
+    int per_cu_ops = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, decode_wave_kernel<DK, TVW, GATE, false>, 64, WaveShape<DK, TVW>::LDS_PAD) !=
-                hipSuccess ||
-        per_cu < 1)
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu_ops, decode_wave_kernel<DK, TVW, GATE, true>, 64,
+            WaveShape<DK, TVW>::LDS_PAD) != hipSuccess)
         per_cu = 1;
+    per_cu = per_cu_ops < per_cu ? per_cu_ops : per_cu;
+    if (per_cu < 1) per_cu = 1;
     n = cus * per_cu;
     cached[dev].store(n, std::memory_order_relaxed);
     return n;
@@ -1539,9 +1546,9 @@ static int wall_ticks_per_us() {
 }
 
 // The read rate the commit hold assumes, in GB/s: the environment variable
-// RGDR_HOLD_READ_GBPS when it holds a number (0 turns the hold off; read on every call, so a
-// process can change it between calls), else the built-in RGDR_HOLD_READ_GBPS.
-static double hold_read_gbps() {
+// RGDR_HOLD_READ_GBPS when it holds a number (0 turns the hold off), else the built-in
+// RGDR_HOLD_READ_GBPS. Read once, at the first single-token call of the process.
+static double hold_read_gbps_env() {
     const char *e = std::getenv("RGDR_HOLD_READ_GBPS");
     if (e && *e) {
         char *end = nullptr;
@@ -1549,6 +1556,10 @@ static double hold_read_gbps() {
         if (end != e && v >= 0.0) return v;
     }
     return RGDR_HOLD_READ_GBPS;
+}
+static double hold_read_gbps() {
+    static const double gbps = hold_read_gbps_env();  // thread-safe one-time initialisation
+    return gbps;
 }
 
 // T = 1: one wave per item. A call with more items than resident waves becomes launches of

@@ -27,8 +27,9 @@
  *     rounded to it with round-to-nearest-even. Arithmetic is fp32.
  *   - Environment: RGDR_HOLD_READ_GBPS (a number, GB/s; 0 = off) sets the HBM read rate
  *     that single-token (T = 1) decode calls assume when they delay their state write-back
- *     until the call's reads could have completed. It is read on every call and changes
- *     timing only, never results. Unset: the built-in rate for MI355X (6400).
+ *     until the call's reads could have completed. It is read once, at the process's first
+ *     single-token call, and changes timing only, never results. Unset: the built-in rate
+ *     for MI355X (6400).
  */
 #ifndef RGDR_H
 #define RGDR_H

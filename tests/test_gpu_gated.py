@@ -95,12 +95,16 @@ def test_gated_bench_workload_full(rg):
     check_gated(inp, out, st, oracle_gated(inp), "gated workload 2")
 
 
-def test_gated_workload4_sampled(rg):
-    """Workload 4 at full size (B=256, 512 slots); the oracle recomputes 32 sampled entries."""
+def test_gated_workload4_all_entries(rg):
+    """Workload 4 at full size (B=256, 512 slots: four launches of the resident grid); the
+    oracle recomputes every entry, in slices of 64 entries to bound its memory."""
     inp = workloads.make_workload(4)
     out, st = gpu_gated(rg, inp)
-    entries = np.random.default_rng(5).choice(inp.B, 32, replace=False)
-    check_gated(inp, out, st, oracle_gated(inp, entries), "gated workload 4", entries)
+    for lo in range(0, inp.B, 64):
+        entries = np.arange(lo, min(lo + 64, inp.B))
+        say(f"gated workload 4: entries {lo}..{entries[-1]}")
+        check_gated(inp, out, st, oracle_gated(inp, entries), f"gated workload 4 [{lo}:]",
+                    entries)
     # slots no entry names are untouched, bit for bit
     untouched = np.setdiff1d(np.arange(inp.N_slots), inp.ssm_state_indices)
     assert np.array_equal(dev_to_bits(st)[untouched], inp.state[untouched])
@@ -272,18 +276,43 @@ def test_gated_graph_replay_matches_eager(rg, case):
         assert np.array_equal(dev_to_bits(st), want_st), f"{case} replay {rep}: state differs"
 
 
+_HOLD_CHILD = r"""
+import sys
+import numpy as np
+sys.path[:0] = [sys.argv[1], sys.argv[1] + "/tests"]
+import gated_delta_rule_rgdr_amd as rg
+import workloads
+from gpu_util import dev_to_bits
+from test_gpu_gated import gpu_gated
+inp = workloads.make_workload(2, gate_inputs=True)
+out, st = gpu_gated(rg, inp)
+np.savez(sys.argv[2], out=dev_to_bits(out), st=dev_to_bits(st))
+print("child done", flush=True)
+"""
+
+
 @pytest.mark.parametrize("rate", ["0", "100"])
-def test_commit_hold_never_changes_results(rg, monkeypatch, rate):
+def test_commit_hold_never_changes_results(rg, tmp_path, rate):
     """The T = 1 commit hold only delays the stores: with it off (rate 0) or very long (an
     assumed read rate of 100 GB/s, so the poll cap ends it) the fused call at the bench
-    shape writes the same bytes as with the default hold."""
+    shape writes the same bytes as with the default hold. The library reads the rate once
+    per process, so the other rate runs in a child process (one at a time, after this
+    process's call has finished)."""
+    import os
+    import subprocess
+    import sys
     inp = workloads.make_workload(2, gate_inputs=True)
-    d = upload(inp)
-    out0, st0 = gpu_gated(rg, inp, d=d)
-    monkeypatch.setenv("RGDR_HOLD_READ_GBPS", rate)
-    out1, st1 = gpu_gated(rg, inp, d=d)
-    assert np.array_equal(dev_to_bits(out0), dev_to_bits(out1))
-    assert np.array_equal(dev_to_bits(st0), dev_to_bits(st1))
+    out0, st0 = gpu_gated(rg, inp)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    dst = str(tmp_path / "hold.npz")
+    env = dict(os.environ, RGDR_HOLD_READ_GBPS=rate)
+    say(f"child process with RGDR_HOLD_READ_GBPS={rate}")
+    r = subprocess.run([sys.executable, "-c", _HOLD_CHILD, root, dst], env=env, timeout=100,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    got = np.load(dst)
+    assert np.array_equal(dev_to_bits(out0), got["out"])
+    assert np.array_equal(dev_to_bits(st0), got["st"])
 
 
 def test_gated_wide_tiles_absent_and_rejected(rg):

@@ -188,13 +188,18 @@ def test_extreme_decays(rg, case, Dk, form):
     say(f"extreme decays: {case}, D_k {Dk}, {form} form")
     out, st = gpu_decode(inp)
     ref = oracle_decode(inp)
-    if case != "growth":
+    if case != "growth" or form == "per_token":
+        # The per-token form computes in plain fp32 on the VALU: held to the decode bar even
+        # outside the operator's domain.
         check_decode(inp, out, st, ref, f"extreme {case} Dk{Dk} {form}")
         return
     # Growth (exp(g) > 1) is outside the operator's domain (g and gk negative): states and
     # outputs grow by e^8 per token and a few outputs are near-total cancellations of terms
-    # ~1e5 times larger. Checked here: everything finite, and each output and each committed
-    # state element within the bar plus 1e-4 of the largest |value| of its (entry, head).
+    # ~1e5 times larger. The chunk form's matrix-core operands carry about 2^-17 of each
+    # value (bf16 high part and remainder), so its error is bounded relative to the item's
+    # largest values, not to each small one. Checked here: everything finite, and each
+    # output and each committed state element within the bar plus 1e-4 of the largest
+    # |value| of its (entry, head).
     out_ref, _, rows = ref
     got = bf16_dev_to_f64(out)
     assert np.all(np.isfinite(got)), "non-finite output"
