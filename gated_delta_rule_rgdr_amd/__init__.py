@@ -11,6 +11,8 @@ fallback: if the library is missing, the first call of any binding function rais
   and leaves ``state`` untouched.
 * ``rgdr_decode_gated`` -- the decode step with the gate front end fused in: takes the raw
   gate projections instead of g and beta.
+* ``rgdr_prefill`` / ``rgdr_prefill_gated`` -- the same recurrence over long sequences
+  (T up to 65536; the page's notes hand prefill to a chunk-level operator), same arguments.
 * ``la_gate`` -- the gate front end (README "com.microsoft.LinearAttentionGate").
 * ``rgdr_validate`` -- synchronous check of the index arrays.
 
@@ -26,7 +28,8 @@ import os
 
 import torch
 
-__all__ = ["rgdr_decode", "rgdr_decode_gated", "recurrent_gated_delta_rule", "la_gate",
+__all__ = ["rgdr_decode", "rgdr_decode_gated", "rgdr_prefill", "rgdr_prefill_gated",
+           "recurrent_gated_delta_rule", "la_gate",
            "rgdr_validate", "VALIDATE",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
            "RGDR_F16", "RGDR_BF16"]
@@ -58,6 +61,10 @@ def library():
     lib.rgdr_decode_gated.restype = C.c_int
     lib.rgdr_decode_gated.argtypes = ([vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7
                                       + [vp] * 2 + [C.c_uint32, vp])
+    lib.rgdr_prefill.restype = C.c_int
+    lib.rgdr_prefill.argtypes = lib.rgdr_decode.argtypes
+    lib.rgdr_prefill_gated.restype = C.c_int
+    lib.rgdr_prefill_gated.argtypes = lib.rgdr_decode_gated.argtypes
     lib.la_gate.restype = C.c_int
     lib.la_gate.argtypes = [vp, vp, vp, vp, C.c_int, i64, i32, vp, C.c_int, vp, C.c_int, vp]
     lib.rgdr_validate.restype = C.c_int
@@ -120,7 +127,7 @@ def _dev(t, name, dtype, ndim=None):
 def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
                 g, gk, num_accepted_tokens, scale=1.0, *, out=None, state_out=None,
                 stream=None):
-    """One decode step; returns ``(out, state_out)``.
+    """One decode step (T <= 8); returns ``(out, state_out)``.
 
     Shapes (page parameter list; the state is a slot pool): query/key bf16
     ``[B,H_q,T,D_k]``, value bf16 ``[B,H_v,T,D_v]``, beta bf16 ``[B,H_v,T]``, state_pool bf16
@@ -128,6 +135,23 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
     arrays int32 ``[B]``. ``state_out`` defaults to ``state_pool`` (in-place update of the
     named slots); ``out`` is allocated if not given.
     """
+    return _plain_call("rgdr_decode", query, key, value, beta, state_pool, actual_seq_lengths,
+                       ssm_state_indices, g, gk, num_accepted_tokens, scale, out, state_out,
+                       stream)
+
+
+def rgdr_prefill(query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
+                 g, gk, num_accepted_tokens, scale=1.0, *, out=None, state_out=None,
+                 stream=None):
+    """The same recurrence over long sequences (T up to 65536, the prefill counterpart the
+    page's notes name); arguments and results as ``rgdr_decode``."""
+    return _plain_call("rgdr_prefill", query, key, value, beta, state_pool, actual_seq_lengths,
+                       ssm_state_indices, g, gk, num_accepted_tokens, scale, out, state_out,
+                       stream)
+
+
+def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
+                g, gk, num_accepted_tokens, scale, out, state_out, stream):
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
     B, Hq, T, Dk = query.shape
@@ -148,7 +172,7 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
     if tuple(key.shape) != (B, Hq, T, Dk) or tuple(value.shape) != (B, Hv, T, Dv) \
             or tuple(beta.shape) != (B, Hv, T) or tuple(g.shape) != (B, Hv, T) \
             or tuple(gk.shape) != (B, Hv, T, Dk) or tuple(state_pool.shape) != (N, Hv, Dk, Dv):
-        raise RuntimeError("rgdr_decode: inconsistent shapes")
+        raise RuntimeError(f"{fn}: inconsistent shapes")
     if out is None:
         out = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=query.device)
     else:
@@ -168,13 +192,13 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
     if VALIDATE:
         _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
-        rc = lib.rgdr_decode(query.data_ptr(), key.data_ptr(), value.data_ptr(),
-                             beta.data_ptr(), state_pool.data_ptr(),
-                             actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
-                             g.data_ptr(), gk.data_ptr(), num_accepted_tokens.data_ptr(),
-                             float(scale), B, Hq, Hv, T, Dk, Dv, N, out.data_ptr(),
-                             state_out.data_ptr(), _stream_handle(stream, query.device))
-    _check(rc, "rgdr_decode")
+        rc = getattr(lib, fn)(query.data_ptr(), key.data_ptr(), value.data_ptr(),
+                              beta.data_ptr(), state_pool.data_ptr(),
+                              actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
+                              g.data_ptr(), gk.data_ptr(), num_accepted_tokens.data_ptr(),
+                              float(scale), B, Hq, Hv, T, Dk, Dv, N, out.data_ptr(),
+                              state_out.data_ptr(), _stream_handle(stream, query.device))
+    _check(rc, fn)
     return out, state_out
 
 
@@ -190,6 +214,25 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
     operator's unit-norm precondition), so raw projections may be passed. Other arguments as
     ``rgdr_decode`` (which takes g and beta instead).
     """
+    return _gated_call("rgdr_decode_gated", query, key, value, a, b, dt_bias, decay_scale,
+                       state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                       num_accepted_tokens, scale, normalize_qk, out, state_out, stream)
+
+
+def rgdr_prefill_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
+                       actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens,
+                       scale=1.0, *, normalize_qk=False, out=None, state_out=None,
+                       stream=None):
+    """``rgdr_prefill`` with the gate fused in, as ``rgdr_decode_gated`` extends
+    ``rgdr_decode``."""
+    return _gated_call("rgdr_prefill_gated", query, key, value, a, b, dt_bias, decay_scale,
+                       state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                       num_accepted_tokens, scale, normalize_qk, out, state_out, stream)
+
+
+def _gated_call(fn, query, key, value, a, b, dt_bias, decay_scale, state_pool,
+                actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens, scale,
+                normalize_qk, out, state_out, stream):
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
     B, Hq, T, Dk = query.shape
@@ -215,7 +258,7 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
             or tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv) \
             or tuple(gk.shape) != (B, Hv, T, Dk) or tuple(state_pool.shape) != (N, Hv, Dk, Dv) \
             or dt_bias.shape[0] != Hv or decay_scale.shape[0] != Hv:
-        raise RuntimeError("rgdr_decode_gated: inconsistent shapes")
+        raise RuntimeError(f"{fn}: inconsistent shapes")
     if out is None:
         out = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=query.device)
     else:
@@ -235,16 +278,16 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
     if VALIDATE:
         _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
-        rc = lib.rgdr_decode_gated(query.data_ptr(), key.data_ptr(), value.data_ptr(),
-                                   a.data_ptr(), b.data_ptr(), dt_bias.data_ptr(),
-                                   decay_scale.data_ptr(), _DTYPE_CODE[a.dtype],
-                                   state_pool.data_ptr(), actual_seq_lengths.data_ptr(),
-                                   ssm_state_indices.data_ptr(), gk.data_ptr(),
-                                   num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T,
-                                   Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
-                                   NORMALIZE_QK if normalize_qk else 0,
-                                   _stream_handle(stream, query.device))
-    _check(rc, "rgdr_decode_gated")
+        rc = getattr(lib, fn)(query.data_ptr(), key.data_ptr(), value.data_ptr(),
+                              a.data_ptr(), b.data_ptr(), dt_bias.data_ptr(),
+                              decay_scale.data_ptr(), _DTYPE_CODE[a.dtype],
+                              state_pool.data_ptr(), actual_seq_lengths.data_ptr(),
+                              ssm_state_indices.data_ptr(), gk.data_ptr(),
+                              num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T,
+                              Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
+                              NORMALIZE_QK if normalize_qk else 0,
+                              _stream_handle(stream, query.device))
+    _check(rc, fn)
     return out, state_out
 
 

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librgdr.so")
 
-SOURCES = ["rgdr_decode.hip", "la_gate.hip", "rgdr_host.cpp"]
+SOURCES = ["rgdr_decode.hip", "rgdr_prefill.hip", "la_gate.hip", "rgdr_host.cpp"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

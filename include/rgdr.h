@@ -1,7 +1,7 @@
 /*
  * rgdr.h -- C ABI of the gfx950 (MI355X) gated-delta-rule decode library.
  *
- * Two operations:
+ * Three operations:
  *
  *   rgdr_decode  The recurrent gated-delta-rule decode step of the MindSpore Lite API page
  *                "lite_boost.ops.recurrent_gated_delta_rule" (algorithm section, parameter
@@ -12,6 +12,9 @@
  *                  2. read    kv = S^T k_t
  *                  3. update  S = S + k_t (x) ((v_t - kv) * beta[t])   (outer product)
  *                  4. output  o_t = S^T (q_t * scale)
+ *   rgdr_prefill The same recurrence over long sequences (T up to 65536): the page's notes
+ *                limit the decode operator to T <= 8 and hand the parallel prefill to a
+ *                chunk-level operator; this is that operator, with rgdr_decode's arguments.
  *   la_gate      The gate front end of the kernel README "com.microsoft.LinearAttentionGate"
  *                (Description; Inputs, Outputs, Type constraints tables):
  *                  decay = decay_scale[h] * softplus(a + dt_bias[h]),  beta = sigmoid(b),
@@ -44,8 +47,9 @@ extern "C" {
 typedef enum {
     RGDR_OK = 0,
     RGDR_ERR_NULL = 1,        /* a required pointer is NULL                                */
-    RGDR_ERR_SHAPE = 2,       /* a size is negative, or zero where not allowed; T > 8;
-                                 H_v % H_q != 0; grid too large; beta requested without b */
+    RGDR_ERR_SHAPE = 2,       /* a size is negative, or zero where not allowed; T > 8
+                                 (decode) or T > 65536 (prefill); H_v % H_q != 0; grid too
+                                 large; beta requested without b                          */
     RGDR_ERR_UNSUPPORTED = 3, /* D_k not in {64, 128}, D_v not a multiple of 64 or above
                                  4096, or an unknown option bit                             */
     RGDR_ERR_RANGE = 4,       /* (validate) a length, count or slot index out of range     */
@@ -136,6 +140,44 @@ rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *va
                               int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
                               int32_t N_slots, void *out, void *state_out, uint32_t flags,
                               hipStream_t stream);
+
+/*
+ * rgdr_prefill -- the recurrence of rgdr_decode over a long sequence per batch entry
+ * (MindSpore Lite page above, notes: the prefill counterpart, a chunk-level operator, of the
+ * T <= 8 decode operator). Arguments, layouts, ownership and semantics are rgdr_decode's
+ * (state pool and slots, valid lengths with +0.0 padded rows, accepted counts, head
+ * sharing, in-place update), with one difference:
+ *   T  1 <= T <= 65536 (the padded sequence length), and T * H_v <= 2^29.
+ * The state is read once and kept in fp32 across all of an entry's tokens; it is rounded to
+ * bf16 once, when it is committed after the entry's first num_accepted_tokens tokens.
+ * Tokens are evaluated in runs of at most 8 in the exact closed form of the recurrence,
+ * whose dense products run on the matrix cores with operands split into bf16 high parts and
+ * remainders (about 16 bits of each operand, fp32 accumulation).
+ * Errors: as rgdr_decode (RGDR_ERR_SHAPE for T > 65536 or T * H_v > 2^29).
+ */
+rgdr_status rgdr_prefill(const void *query, const void *key, const void *value,
+                         const void *beta, const void *state_pool,
+                         const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+                         const float *g, const float *gk, const int32_t *num_accepted_tokens,
+                         float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                         int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                         void *state_out, hipStream_t stream);
+
+/*
+ * rgdr_prefill_gated -- rgdr_prefill with the gate front end fused in, exactly as
+ * rgdr_decode_gated extends rgdr_decode: raw gate projections gate_a, gate_b [B, T, H_v]
+ * (RGDR_F32 or RGDR_F16) and fp32 dt_bias, decay_scale [H_v] instead of g and beta, and the
+ * RGDR_NORMALIZE_QK option. Sizes and errors as rgdr_prefill, plus rgdr_decode_gated's.
+ */
+rgdr_status rgdr_prefill_gated(const void *query, const void *key, const void *value,
+                               const void *gate_a, const void *gate_b, const float *dt_bias,
+                               const float *decay_scale, rgdr_dtype gate_dtype,
+                               const void *state_pool, const int32_t *actual_seq_lengths,
+                               const int32_t *ssm_state_indices, const float *gk,
+                               const int32_t *num_accepted_tokens, float scale, int32_t B,
+                               int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
+                               int32_t N_slots, void *out, void *state_out, uint32_t flags,
+                               hipStream_t stream);
 
 /*
  * la_gate -- decay = decay_scale * softplus(a + dt_bias) and, when beta_out != NULL,

@@ -47,16 +47,22 @@ def upload(inp):
     return d
 
 
-def gpu_decode(inp, d=None, *, inplace=False):
-    """Run rgdr_decode on the GPU; returns (out bf16 tensor, state_out bf16 tensor)."""
+def gpu_decode(inp, d=None, *, inplace=False, fn="rgdr_decode"):
+    """Run rgdr_decode (or another entry with its arguments, such as rgdr_prefill) on the
+    GPU; returns (out bf16 tensor, state_out bf16 tensor)."""
     import gated_delta_rule_rgdr_amd as rg
     d = d or upload(inp)
     pool = d["state"] if inplace else d["state"].clone()
-    out, st = rg.rgdr_decode(d["query"], d["key"], d["value"], d["beta"], pool,
-                             d["actual_seq_lengths"], d["ssm_state_indices"], d["g"], d["gk"],
-                             d["num_accepted_tokens"], inp.scale)
+    out, st = getattr(rg, fn)(d["query"], d["key"], d["value"], d["beta"], pool,
+                              d["actual_seq_lengths"], d["ssm_state_indices"], d["g"], d["gk"],
+                              d["num_accepted_tokens"], inp.scale)
     torch.cuda.synchronize()
     return out, st
+
+
+def gpu_prefill(inp, d=None, *, inplace=False):
+    """Run rgdr_prefill on the GPU; returns (out, state_out) as gpu_decode."""
+    return gpu_decode(inp, d, inplace=inplace, fn="rgdr_prefill")
 
 
 def oracle_decode(inp, **over):
@@ -105,3 +111,69 @@ def check_decode(inp, out_t, state_t, ref, label):
     assert np.array_equal(pool_bits[untouched], inp.state[untouched]), \
         f"{label}: slots no entry names were modified"
     assert np.array_equal(pool_ref_bits[untouched], inp.state[untouched])
+
+
+# ---- the fused gate: oracle chain (fp64 gate, then the fp64 core, no rounding between) ----
+
+
+def gate_tensors(inp, dtype=np.float32):
+    return (torch.from_numpy(inp.gate_a.astype(dtype)).cuda(),
+            torch.from_numpy(inp.gate_b.astype(dtype)).cuda(),
+            torch.from_numpy(inp.dt_bias).cuda(), torch.from_numpy(inp.decay_scale).cuda())
+
+
+def gpu_gated(rg, inp, dtype=np.float32, d=None, normalize_qk=False, fn="rgdr_decode_gated"):
+    """Run a fused-gate entry (rgdr_decode_gated or rgdr_prefill_gated) out of place."""
+    d = d or upload(inp)
+    a, b, dt, ds = gate_tensors(inp, dtype)
+    pool = d["state"].clone()
+    out, st = getattr(rg, fn)(d["query"], d["key"], d["value"], a, b, dt, ds, pool,
+                              d["actual_seq_lengths"], d["ssm_state_indices"], d["gk"],
+                              d["num_accepted_tokens"], inp.scale, normalize_qk=normalize_qk)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def oracle_gated(inp, entries=None, dtype=np.float32, normalize_qk=False):
+    """Oracle chain for the batch entries `entries` (all when None): returns fp64 out
+    [n, H_v, T, D_v] and each entry's committed state [n, H_v, D_k, D_v] (NaN if skipped)."""
+    sel = np.arange(inp.B) if entries is None else np.asarray(entries)
+    g64, b64 = oracle.la_gate(inp.gate_a[sel].astype(dtype), inp.dt_bias, inp.decay_scale,
+                              inp.gate_b[sel].astype(dtype))
+    g64 = np.ascontiguousarray(g64.transpose(0, 2, 1))  # [n, H_v, T]
+    b64 = np.ascontiguousarray(b64.transpose(0, 2, 1))
+    idx = inp.ssm_state_indices[sel]
+    valid = (idx >= 0) & (idx < inp.N_slots)
+    pool_small = oracle.bf16_to_f64(inp.state[idx[valid]])
+    idx_small = np.full(len(sel), -1, np.int32)
+    idx_small[valid] = np.arange(int(valid.sum()), dtype=np.int32)
+    if pool_small.shape[0] == 0:
+        pool_small = np.zeros((1, inp.Hv, inp.Dk, inp.Dv))
+    out, pool_out = oracle.rgdr_f64(
+        oracle.bf16_to_f64(inp.query[sel]), oracle.bf16_to_f64(inp.key[sel]),
+        oracle.bf16_to_f64(inp.value[sel]), b64, pool_small, inp.actual_seq_lengths[sel],
+        idx_small, g64, inp.gk[sel].astype(np.float64), inp.num_accepted_tokens[sel],
+        float(np.float32(inp.scale)), normalize_qk=normalize_qk)
+    rows = np.full((len(sel), inp.Hv, inp.Dk, inp.Dv), np.nan)
+    rows[valid] = pool_out[idx_small[valid]]
+    return out, rows
+
+
+def check_gated(inp, out_t, st_t, ref, label, entries=None):
+    out_ref, rows = ref
+    sel = np.arange(inp.B) if entries is None else np.asarray(entries)
+    out = bf16_dev_to_f64(out_t)[sel]
+    lens = np.clip(inp.actual_seq_lengths[sel], 0, inp.T)
+    idx = inp.ssm_state_indices[sel]
+    valid = (idx >= 0) & (idx < inp.N_slots)
+    mask = np.zeros((len(sel), inp.Hv, inp.T), bool)
+    for i in range(len(sel)):
+        if valid[i]:
+            mask[i, :, :lens[i]] = True
+    assert_tol(out[mask], out_ref[mask], f"{label} out")
+    assert np.all(dev_to_bits(out_t)[sel][~mask] == 0), f"{label}: padded rows not +0.0"
+    pool = bf16_dev_to_f64(st_t)
+    assert_tol(pool[idx[valid]], rows[valid], f"{label} state_out")
+    if entries is None:
+        untouched = np.setdiff1d(np.arange(inp.N_slots), idx[valid])
+        assert np.array_equal(dev_to_bits(st_t)[untouched], inp.state[untouched])

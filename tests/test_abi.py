@@ -31,8 +31,8 @@ def lib():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for want in ("rgdr_decode", "rgdr_decode_gated", "la_gate", "rgdr_validate",
-                 "rgdr_validate_host", "rgdr_status_string"):
+    for want in ("rgdr_decode", "rgdr_decode_gated", "rgdr_prefill", "rgdr_prefill_gated",
+                 "la_gate", "rgdr_validate", "rgdr_validate_host", "rgdr_status_string"):
         assert want in names, names
 
 
@@ -84,6 +84,62 @@ def test_decode_argument_checks(lib):
     bad[7] = 0x10002  # g not 4-byte aligned
     assert _decode(lib, ptrs=bad) == ALIGN
     assert _decode(lib, out=0x20004) == ALIGN
+
+
+def _prefill(lib, ptrs=None, **kw):
+    dims = dict(B=2, Hq=2, Hv=4, T=64, Dk=128, Dv=128, N=4)
+    dims.update(kw)
+    p = [0x10000] * 10 if ptrs is None else ptrs
+    return lib.rgdr_prefill(*p[:10], 1.0, dims["B"], dims["Hq"], dims["Hv"], dims["T"],
+                            dims["Dk"], dims["Dv"], dims["N"], kw.get("out", 0x20000),
+                            kw.get("state_out", 0x30000), None)
+
+
+def test_prefill_argument_checks(lib):
+    assert _prefill(lib, ptrs=[None] * 10, B=0, out=None, state_out=None) == OK
+    for i in range(10):
+        p = [0x10000] * 10
+        p[i] = None
+        assert _prefill(lib, ptrs=p) == NULL, i
+    assert _prefill(lib, out=None) == NULL
+    assert _prefill(lib, T=65537) == SHAPE        # at most 65536 tokens
+    assert _prefill(lib, T=0) == SHAPE
+    assert _prefill(lib, T=65536, Hv=16384, Hq=16384) == SHAPE  # T * H_v > 2^29
+    assert _prefill(lib, Hq=3) == SHAPE
+    assert _prefill(lib, N=0) == SHAPE
+    assert _prefill(lib, Dk=96) == UNSUP
+    assert _prefill(lib, Dv=96) == UNSUP
+    assert _prefill(lib, Dv=4160) == UNSUP
+    bad = [0x10000] * 10
+    bad[0] = 0x10008  # query not 16-byte aligned
+    assert _prefill(lib, ptrs=bad) == ALIGN
+    bad = [0x10000] * 10
+    bad[3] = 0x10001  # beta not 2-byte aligned
+    assert _prefill(lib, ptrs=bad) == ALIGN
+    assert _prefill(lib, state_out=0x30004) == ALIGN
+
+
+def test_prefill_gated_argument_checks(lib):
+    def call(ptrs=None, gdt=F32, flags=0, **kw):
+        dims = dict(B=2, Hq=2, Hv=4, T=64, Dk=128, Dv=128, N=4)
+        dims.update(kw)
+        p = [0x10000] * 12 if ptrs is None else ptrs
+        return lib.rgdr_prefill_gated(*p[:7], gdt, *p[7:12], 1.0, dims["B"], dims["Hq"],
+                                      dims["Hv"], dims["T"], dims["Dk"], dims["Dv"], dims["N"],
+                                      kw.get("out", 0x20000), kw.get("state_out", 0x30000),
+                                      flags, None)
+    assert call(ptrs=[None] * 12, B=0, out=None, state_out=None) == OK
+    for i in range(12):
+        p = [0x10000] * 12
+        p[i] = None
+        assert call(ptrs=p) == NULL, i
+    assert call(gdt=BF16) == DTYPE
+    assert call(T=70000) == SHAPE
+    assert call(Dk=256) == UNSUP
+    assert call(flags=4) == UNSUP
+    p = [0x10000] * 12
+    p[4] = 0x10002  # fp32 projection b not 4-byte aligned
+    assert call(ptrs=p) == ALIGN
 
 
 def _gated(lib, ptrs=None, gdt=F32, **kw):

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import assert_tol, bf16_dev_to_f64, dev_to_bits, say, upload
+from gpu_util import (assert_tol, bf16_dev_to_f64, check_gated, dev_to_bits, gate_tensors,
+                      gpu_gated, oracle_gated, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,69 +23,6 @@ def rg():
     import gated_delta_rule_rgdr_amd as m
     m.library()
     return m
-
-
-def gate_tensors(inp, dtype=np.float32):
-    return (torch.from_numpy(inp.gate_a.astype(dtype)).cuda(),
-            torch.from_numpy(inp.gate_b.astype(dtype)).cuda(),
-            torch.from_numpy(inp.dt_bias).cuda(), torch.from_numpy(inp.decay_scale).cuda())
-
-
-def gpu_gated(rg, inp, dtype=np.float32, d=None, normalize_qk=False):
-    d = d or upload(inp)
-    a, b, dt, ds = gate_tensors(inp, dtype)
-    pool = d["state"].clone()
-    out, st = rg.rgdr_decode_gated(d["query"], d["key"], d["value"], a, b, dt, ds, pool,
-                                   d["actual_seq_lengths"], d["ssm_state_indices"], d["gk"],
-                                   d["num_accepted_tokens"], inp.scale,
-                                   normalize_qk=normalize_qk)
-    torch.cuda.synchronize()
-    return out, st
-
-
-def oracle_gated(inp, entries=None, dtype=np.float32, normalize_qk=False):
-    """Oracle chain for the batch entries `entries` (all when None): returns fp64 out
-    [n, H_v, T, D_v] and each entry's committed state [n, H_v, D_k, D_v] (NaN if skipped)."""
-    sel = np.arange(inp.B) if entries is None else np.asarray(entries)
-    g64, b64 = oracle.la_gate(inp.gate_a[sel].astype(dtype), inp.dt_bias, inp.decay_scale,
-                              inp.gate_b[sel].astype(dtype))
-    g64 = np.ascontiguousarray(g64.transpose(0, 2, 1))  # [n, H_v, T]
-    b64 = np.ascontiguousarray(b64.transpose(0, 2, 1))
-    idx = inp.ssm_state_indices[sel]
-    valid = (idx >= 0) & (idx < inp.N_slots)
-    pool_small = oracle.bf16_to_f64(inp.state[idx[valid]])
-    idx_small = np.full(len(sel), -1, np.int32)
-    idx_small[valid] = np.arange(int(valid.sum()), dtype=np.int32)
-    if pool_small.shape[0] == 0:
-        pool_small = np.zeros((1, inp.Hv, inp.Dk, inp.Dv))
-    out, pool_out = oracle.rgdr_f64(
-        oracle.bf16_to_f64(inp.query[sel]), oracle.bf16_to_f64(inp.key[sel]),
-        oracle.bf16_to_f64(inp.value[sel]), b64, pool_small, inp.actual_seq_lengths[sel],
-        idx_small, g64, inp.gk[sel].astype(np.float64), inp.num_accepted_tokens[sel],
-        float(np.float32(inp.scale)), normalize_qk=normalize_qk)
-    rows = np.full((len(sel), inp.Hv, inp.Dk, inp.Dv), np.nan)
-    rows[valid] = pool_out[idx_small[valid]]
-    return out, rows
-
-
-def check_gated(inp, out_t, st_t, ref, label, entries=None):
-    out_ref, rows = ref
-    sel = np.arange(inp.B) if entries is None else np.asarray(entries)
-    out = bf16_dev_to_f64(out_t)[sel]
-    lens = np.clip(inp.actual_seq_lengths[sel], 0, inp.T)
-    idx = inp.ssm_state_indices[sel]
-    valid = (idx >= 0) & (idx < inp.N_slots)
-    mask = np.zeros((len(sel), inp.Hv, inp.T), bool)
-    for i in range(len(sel)):
-        if valid[i]:
-            mask[i, :, :lens[i]] = True
-    assert_tol(out[mask], out_ref[mask], f"{label} out")
-    assert np.all(dev_to_bits(out_t)[sel][~mask] == 0), f"{label}: padded rows not +0.0"
-    pool = bf16_dev_to_f64(st_t)
-    assert_tol(pool[idx[valid]], rows[valid], f"{label} state_out")
-    if entries is None:
-        untouched = np.setdiff1d(np.arange(inp.N_slots), idx[valid])
-        assert np.array_equal(dev_to_bits(st_t)[untouched], inp.state[untouched])
 
 
 def test_gated_bench_workload_full(rg):
@@ -283,7 +221,7 @@ sys.path[:0] = [sys.argv[1], sys.argv[1] + "/tests"]
 import gated_delta_rule_rgdr_amd as rg
 import workloads
 from gpu_util import dev_to_bits
-from test_gpu_gated import gpu_gated
+from gpu_util import gpu_gated
 inp = workloads.make_workload(2, gate_inputs=True)
 out, st = gpu_gated(rg, inp)
 np.savez(sys.argv[2], out=dev_to_bits(out), st=dev_to_bits(st))

@@ -12,6 +12,10 @@ README, Inputs table):
   2  batched GQA decode:     B=64, H_q=16, H_v=32, T=1, D=128, 256 slots, 64 distinct used
   3  speculative / varlen:   B=32, H_q=H_v=32, T=8, D=128, lengths U{1..8}, 64 slots
   4  gate + recurrence:      B=256, H_q=16, H_v=32, T=1, D=128, 512 slots, raw gate inputs
+  5  chunked prefill:        B=16, H_q=16, H_v=32, T=1024, D=128, 32 slots, 16 distinct used
+                             (the long-sequence counterpart the page's notes name; the pages
+                             give no prefill shape, so this takes workload 2's heads and head
+                             size with 1024-token prompts)
 
 Recipe (one numpy ``default_rng(1000 + id)`` stream, drawn in this order):
   q, k ~ N(0,1) fp64, L2-normalised along D_k per (b, head, t), stored as bf16;
@@ -44,6 +48,7 @@ WORKLOADS = {
     2: dict(B=64, Hq=16, Hv=32, T=1, Dk=128, Dv=128, N_slots=256),
     3: dict(B=32, Hq=32, Hv=32, T=8, Dk=128, Dv=128, N_slots=64),
     4: dict(B=256, Hq=16, Hv=32, T=1, Dk=128, Dv=128, N_slots=512),
+    5: dict(B=16, Hq=16, Hv=32, T=1024, Dk=128, Dv=128, N_slots=32),
 }
 
 WORKLOAD_NAMES = {
@@ -52,6 +57,7 @@ WORKLOAD_NAMES = {
     2: "batched GQA decode B=64 Hq=16 Hv=32 T=1 D=128",
     3: "varlen speculative decode B=32 H=32 T=8 D=128",
     4: "gate + decode B=256 Hq=16 Hv=32 T=1 D=128",
+    5: "chunked prefill B=16 Hq=16 Hv=32 T=1024 D=128",
 }
 
 
@@ -149,7 +155,7 @@ def make_case(B, Hq, Hv, T, Dk, Dv, N_slots, seed, *, zero_state=False, gk_hi=0.
 
 
 def make_workload(wid: int, gate_inputs: bool = False) -> Inputs:
-    """The five workloads, seeded with 1000 + id (see the module docstring)."""
+    """The six workloads, seeded with 1000 + id (see the module docstring)."""
     w = WORKLOADS[wid]
     seed = 1000 + wid
     if wid == 0:
@@ -162,6 +168,8 @@ def make_workload(wid: int, gate_inputs: bool = False) -> Inputs:
         inp = make_case(**w, seed=seed, indices="permutation", lengths="uniform")
     elif wid == 4:
         return make_case(**w, seed=seed, indices="choice", gk_hi=0.05, gate=True)
+    elif wid == 5:
+        inp = make_case(**w, seed=seed, indices="choice")
     else:
         raise KeyError(wid)
     if gate_inputs:
