@@ -1,35 +1,39 @@
 #!/usr/bin/env python3
-"""Benchmark of the gated-delta-rule decode path on one MI355X.
+"""Benchmark of the gated-delta-rule path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--rotate R]
-                    [--cpu-seconds S] [--no-cpu-baseline]
+                    [--extra 1,3,4,5] [--cpu-seconds S] [--no-cpu-baseline]
 
 One step is the whole path over one batch: the gate front end (g = decay_scale *
-softplus(a + dt_bias), beta = sigmoid(b)) and the decode step, in place on the state pool,
+softplus(a + dt_bias), beta = sigmoid(b)) and the recurrence, in place on the state pool,
 in the HIP library through its C ABI. By default the step is one launch of
 rgdr_decode_gated (the gate computed in the decode kernel's prologue); the two-launch chain
 la_gate -> rgdr_decode is timed as well and reported as `unfused_ms_per_step`. The default
 workload is the batched GQA decode shape (B=64, H_q=16, H_v=32, T=1, D_k=D_v=128, a
 256-slot pool, 64 slots in use), with gate inputs that reproduce its g/beta recipe.
+Workload 5 (T = 1024) runs the long-sequence entries, rgdr_prefill_gated and rgdr_prefill.
 
 Measurement:
   * R independent buffer sets (pool and every per-step input/output) are rotated so that
-    consecutive steps stream their state from HBM, not from the 256 MB Infinity Cache;
-    R is chosen so one rotation touches >= 1 GiB of distinct state.
+    consecutive steps stream their data from HBM, not from the 256 MB Infinity Cache: one
+    rotation touches >= 1 GiB of distinct state (decode) or of step data (long sequences).
   * W eager warmup steps; then the K timed steps are captured in one HIP graph (so
     Python launch overhead is not measured), replayed untimed until 25 ms of work have run
     (upload, and the shader clock settling under load), and timed with events on the
     launch stream around a single replay.
-  * The decode kernel's average duration: K back-to-back decode launches over the same
-    rotation, captured in a graph and timed with events around each of 5 replays; the
-    median replay's per-launch mean is the duration (what rocprofv3's kernel trace
-    reports as the average); its roofline uses the method's algorithmic bytes per launch.
-    The gate kernel is timed the same way.
+  * The fused kernel's average duration: K back-to-back calls over the same rotation,
+    captured in a graph and timed with events around each of 5 replays; the median replay's
+    per-call mean is the duration (what rocprofv3's kernel trace reports as the average);
+    its roofline uses the method's algorithmic bytes per call. The unfused kernels are
+    timed the same way.
+  * `workloads`: the same kernel timing for the other workloads (--extra), so one line
+    carries every workload's fused-call duration, roofline fraction and counter traffic.
   * copy_reference: a plain 256 MiB device copy (torch elementwise, read + write), timed
     the same way, as the box's practical streaming rate.
-  * cpu_baseline: the fp64 C oracle repeats the same step on the host for about
-    --cpu-seconds, on one thread and on one thread per host core (batch entries split
-    into contiguous slices, each slice with its own compact copy of its state slots).
+  * cpu_baseline: the fp64 C oracle repeats the step on the host for about --cpu-seconds,
+    on one thread and on one thread per core of the GPU's host share (batch entries split
+    into contiguous slices, each slice with its own compact copy of its state slots); where
+    one full step would take longer than that, on a sample of the step's batch entries.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -45,8 +49,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of peak) + token·head steps/sec, gated-delta decode"
 HBM_PEAK_GBS = 8000.0
-KERNEL_REPLAYS = 5  # kernel durations: median over this many replays of the K-launch graph
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
+KERNEL_REPLAYS = 5  # kernel durations: median over this many replays of the K-call graph
 WARM_MS = 25.0      # untimed graph replays before any timed one, in wall-clock milliseconds
+# The host share of one GPU on the benchmark boxes: the threaded CPU baseline uses at most
+# this many threads, whatever the process's affinity mask shows.
+HOST_CORES_PER_GPU = 16
+PREFILL_WORKLOADS = (5,)
 
 
 def log(msg):
@@ -54,7 +63,7 @@ def log(msg):
 
 
 def decode_bytes(inp):
-    """Algorithmic bytes of one decode call: the state tile of every served (b, h) read and
+    """Algorithmic bytes of one call: the state tile of every served (b, h) read and
     written once (bf16), per valid token-head q+k (shared over H_v/H_q heads), v, out,
     beta, g, gk, and 12 B of index data per batch entry."""
     import numpy as np
@@ -77,20 +86,43 @@ def fused_bytes(inp, decode_b, tok_heads):
     return decode_b + tok_heads * (4 + 4 - 4 - 2) + 2 * 4 * inp.Hv
 
 
-KERNEL_SOURCES = ("gated_delta_rule_rgdr_amd/csrc/rgdr_decode.hip",
+def prefill_mfma_flops(inp):
+    """Matrix-core flops the long-sequence kernel executes per call (not the method's
+    algorithmic flops): per run of up to 8 tokens and per 128-column item, each of its two
+    waves issues 3 x (D_k / 32) x 4 products of 16x16x32 (Y = X^T S on split operands) and
+    2 x (D_k / 16) x 4 of 16x16x16 (the update)."""
+    import numpy as np
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    nacc = np.clip(inp.num_accepted_tokens, 0, lens)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    runs = 0
+    for L, n, ok in zip(lens, nacc, valid):
+        if ok and L > 0:
+            runs += -(-int(L) // 8) + (1 if 0 < n < L and n % 8 else 0)
+    items = inp.Hv * -(-inp.Dv // 128)
+    per_wave = 3 * (inp.Dk // 32) * 4 * 16 * 16 * 32 * 2 + 2 * (inp.Dk // 16) * 4 * 16 * 16 * 16 * 2
+    return runs * items * 2 * per_wave
+
+
+SOURCES_COMMON = ("gated_delta_rule_rgdr_amd/csrc/rgdr_device.h",
                   "gated_delta_rule_rgdr_amd/csrc/rgdr_common.h")
-TRAFFIC_PROFILES = {2: "profiles/rgdr_decode_b64_gqa_d128.md",
+SOURCES_DECODE = ("gated_delta_rule_rgdr_amd/csrc/rgdr_decode.hip",) + SOURCES_COMMON
+SOURCES_PREFILL = ("gated_delta_rule_rgdr_amd/csrc/rgdr_prefill.hip",) + SOURCES_COMMON
+TRAFFIC_PROFILES = {1: "profiles/rgdr_decode_b1_h64_dk64_dv512.md",
+                    2: "profiles/rgdr_decode_b64_gqa_d128.md",
                     3: "profiles/rgdr_decode_varlen_b32_t8_d128.md",
-                    4: "profiles/rgdr_decode_b256_gqa_d128.md"}
+                    4: "profiles/rgdr_decode_b256_gqa_d128.md",
+                    5: "profiles/rgdr_prefill_b16_t1024_gqa_d128.md"}
 
 
-def kernel_code_digest():
-    """sha256 of the decode kernel sources with comments and whitespace removed: an edit to
-    comments keeps the committed counter summaries valid, an edit to code does not."""
+def kernel_code_digest(wid=2):
+    """sha256 of the sources of the kernel that serves workload `wid`, with comments and
+    whitespace removed: an edit to comments keeps the committed counter summaries valid, an
+    edit to code does not."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (SOURCES_PREFILL if wid in PREFILL_WORKLOADS else SOURCES_DECODE):
         text = open(os.path.join(ROOT, f)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -100,8 +132,8 @@ def kernel_code_digest():
 
 def measured_traffic(wid=2):
     """HBM bytes per fused call from the committed rocprofv3 counter summary of workload
-    `wid`, or None when there is none or the decode kernel's code has changed since those
-    counters were taken."""
+    `wid`, or None when there is none or the kernel's code has changed since those counters
+    were taken."""
     import re
     if wid not in TRAFFIC_PROFILES:
         return None
@@ -113,15 +145,18 @@ def measured_traffic(wid=2):
     mh = re.search(r"^kernel_code_sha256:\s*([0-9a-f]{64})", text, re.M)
     if not (mt and mh):
         return None
-    return int(mt.group(1)) if kernel_code_digest() == mh.group(1) else None
+    return int(mt.group(1)) if kernel_code_digest(wid) == mh.group(1) else None
 
 
-def cpu_baseline(inp, step_bytes, tok_heads, seconds):
-    """Time the oracle on the host: the whole step (gate, then decode) over the workload,
-    first on one thread, then on one thread per host core. Each thread takes a contiguous
-    slice of batch entries with a compact copy of the state slots they name (prepared before
-    the clock starts); the oracle runs unchanged on each slice (its C calls release the
-    GIL). Each mode repeats the step for about `seconds`."""
+def cpu_baseline(inp, seconds):
+    """Time the oracle on the host: the whole step (gate, then the recurrence), first on one
+    thread, then on one thread per core of the GPU's host share. Each thread takes a
+    contiguous slice of batch entries with a compact copy of the state slots they name
+    (prepared before the clock starts); the oracle runs unchanged on each slice (its C calls
+    release the GIL). Each mode repeats its sample for about `seconds`. The sample is the
+    whole batch unless one pass would exceed about 1e9 state-element updates per thread
+    (several seconds of the oracle); then it is the first entries of the batch, sized to
+    that, and the rate is that sample's algorithmic bytes over its time."""
     import concurrent.futures as cf
     import platform
 
@@ -129,9 +164,30 @@ def cpu_baseline(inp, step_bytes, tok_heads, seconds):
 
     import oracle
 
-    def slices(n):
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    per_entry = np.maximum(lens, 1).astype(np.float64) * inp.Hv * inp.Dk * inp.Dv
+    budget = 1e9
+
+    def sample_size(threads):
+        total = 0.0
+        for n_ent in range(1, inp.B + 1):
+            total += per_entry[n_ent - 1]
+            if total > budget * threads:
+                return max(n_ent - 1, min(threads, inp.B))
+        return inp.B
+
+    def sub(inp_, bs):
+        import copy
+        s = copy.copy(inp_)
+        for name in ("query", "key", "value", "beta", "g", "gk", "ssm_state_indices",
+                     "actual_seq_lengths", "num_accepted_tokens", "gate_a", "gate_b"):
+            setattr(s, name, getattr(inp_, name)[bs])
+        s.B = len(bs)
+        return s
+
+    def slices(entries, n):
         out = []
-        for bs in np.array_split(np.arange(inp.B), n):
+        for bs in np.array_split(entries, n):
             if len(bs) == 0:
                 continue
             idx = inp.ssm_state_indices[bs]
@@ -154,7 +210,11 @@ def cpu_baseline(inp, step_bytes, tok_heads, seconds):
                          sl["idx"], g32, sl["gk"], sl["nacc"], inp.scale)
 
     def timed(n):
-        parts = slices(n)
+        entries = np.arange(sample_size(n))
+        parts = slices(entries, n)
+        s = sub(inp, entries)
+        db, th = decode_bytes(s)
+        sbytes = fused_bytes(s, db, th)
         t0 = time.perf_counter()
         reps = 0
         with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
@@ -163,14 +223,16 @@ def cpu_baseline(inp, step_bytes, tok_heads, seconds):
                 reps += 1
                 el = time.perf_counter() - t0
                 if el >= seconds:
-                    return reps, el, len(parts)
+                    return reps, el, len(parts), len(entries), sbytes, th
 
     oracle.default()
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    r1, e1, _ = timed(1)
-    log(f"cpu oracle, 1 thread: {r1} steps in {e1:.1f} s")
-    rn, en, used = timed(cores)
-    log(f"cpu oracle, {used} threads: {rn} steps in {en:.1f} s")
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(affinity, HOST_CORES_PER_GPU))
+    r1, e1, _, n1, b1, th1 = timed(1)
+    log(f"cpu oracle, 1 thread: {r1} passes over {n1} entries in {e1:.1f} s")
+    rn, en, used, nn, bn, thn = timed(cores)
+    log(f"cpu oracle, {used} threads: {rn} passes over {nn} entries in {en:.1f} s "
+        f"(affinity mask: {affinity} cores)")
     model = platform.processor() or "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -179,15 +241,205 @@ def cpu_baseline(inp, step_bytes, tok_heads, seconds):
                 break
     except OSError:
         pass
-    return {"value": round(step_bytes * rn / en / 1e9, 4), "unit": "GB/s", "cores": used,
+    what = "full steps of this workload" if nn == inp.B else \
+        f"passes over the first {nn} of the step's {inp.B} batch entries"
+    what1 = "full steps" if n1 == inp.B else f"passes over the first {n1} entries"
+    return {"value": round(bn * rn / en / 1e9, 4), "unit": "GB/s", "cores": used,
             "kind": "oracle",
-            "sample": f"{rn} full steps of this workload (gate + decode, fp64 C oracle) on "
-                      f"{used} threads in {en:.1f} s, batch entries split into {used} slices",
-            "token_head_steps_per_s": round(tok_heads * rn / en, 1),
-            "single_thread": {"value": round(step_bytes * r1 / e1 / 1e9, 4),
-                              "token_head_steps_per_s": round(tok_heads * r1 / e1, 1),
-                              "sample": f"{r1} full steps on 1 thread in {e1:.1f} s"},
-            "cpu_model": model}
+            "sample": f"{rn} {what} (gate + recurrence, fp64 C oracle) on {used} threads in "
+                      f"{en:.1f} s, entries split into {used} slices",
+            "token_head_steps_per_s": round(thn * rn / en, 1),
+            "single_thread": {"value": round(b1 * r1 / e1 / 1e9, 4),
+                              "token_head_steps_per_s": round(th1 * r1 / e1, 1),
+                              "sample": f"{r1} {what1} on 1 thread in {e1:.1f} s"},
+            "cpu_model": model, "affinity_cores": affinity,
+            "threads_cap": f"at most {HOST_CORES_PER_GPU} threads: the host share of one GPU"}
+
+
+class Workload:
+    """Device buffers of one workload, rotated over R sets, and its calls."""
+
+    def __init__(self, wid, dev, rotate=0, steps=200):
+        import numpy as np
+        import torch
+
+        import gated_delta_rule_rgdr_amd as rg
+        import workloads
+        self.rg, self.torch = rg, torch
+        self.wid = wid
+        self.name = workloads.WORKLOAD_NAMES[wid]
+        self.prefill = wid in PREFILL_WORKLOADS
+        inp = self.inp = workloads.make_workload(wid, gate_inputs=True)
+        B, Hv, T, Dk, Dv, N = inp.B, inp.Hv, inp.T, inp.Dk, inp.Dv, inp.N_slots
+        self.dbytes, self.tok_heads = decode_bytes(inp)
+        self.gbytes = gate_bytes(inp)
+        self.step_bytes = fused_bytes(inp, self.dbytes, self.tok_heads)
+        self.n_pairs = int(((inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < N)).sum()) * Hv
+        touched = self.n_pairs * Dk * Dv * 2
+        if self.prefill:
+            touched = self.step_bytes  # every step streams far more than its state
+        R = rotate or max(2, math.ceil((1 << 30) / max(touched, 1)))
+        self.R = min(R, steps) if steps > 0 else R
+
+        def bits(x):
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        base = dict(q=bits(inp.query), k=bits(inp.key), v=bits(inp.value), pool=bits(inp.state),
+                    gk=torch.from_numpy(inp.gk).to(dev), a=torch.from_numpy(inp.gate_a).to(dev),
+                    b=torch.from_numpy(inp.gate_b).to(dev))
+        self.dt = torch.from_numpy(inp.dt_bias).to(dev)
+        self.ds = torch.from_numpy(inp.decay_scale).to(dev)
+        self.lens = torch.from_numpy(inp.actual_seq_lengths).to(dev)
+        self.idx = torch.from_numpy(inp.ssm_state_indices).to(dev)
+        self.nacc = torch.from_numpy(inp.num_accepted_tokens).to(dev)
+        self.sets = []
+        for _ in range(self.R):
+            s = {k_: v_.clone() for k_, v_ in base.items()}
+            s["g"] = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+            s["beta"] = torch.empty((B, T, Hv), dtype=torch.bfloat16, device=dev)
+            s["out"] = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=dev)
+            if T != 1:
+                s["gT"] = torch.empty((B, Hv, T), dtype=torch.float32, device=dev)
+                s["betaT"] = torch.empty((B, Hv, T), dtype=torch.bfloat16, device=dev)
+            self.sets.append(s)
+        del base
+        torch.cuda.synchronize()
+        self.fused_fn = rg.rgdr_prefill_gated if self.prefill else rg.rgdr_decode_gated
+        self.decode_fn = rg.rgdr_prefill if self.prefill else rg.rgdr_decode
+        self.fused_name = "rgdr_prefill_gated" if self.prefill else "rgdr_decode_gated"
+        self.decode_name = "rgdr_prefill" if self.prefill else "rgdr_decode"
+
+    # g and beta come out of the gate as [B, T, H_v]; the recurrence reads [B, H_v, T]. With
+    # T = 1 these are the same bytes. For T > 1 the unfused chain transposes them with torch
+    # (part of the chain's time), while the unfused kernel's own timing reads copies that
+    # were transposed once beforehand.
+    def gate(self, s):
+        self.rg.la_gate(s["a"], self.dt, self.ds, s["b"], decay_dtype=self.torch.float32,
+                        beta_dtype=self.torch.bfloat16, decay_out=s["g"], beta_out=s["beta"])
+
+    def transpose(self, s):
+        s["gT"].copy_(s["g"].transpose(1, 2))
+        s["betaT"].copy_(s["beta"].transpose(1, 2))
+
+    def decode(self, s):
+        inp = self.inp
+        B, Hv, T = inp.B, inp.Hv, inp.T
+        g_ = s["g"].view(B, Hv, T) if T == 1 else s["gT"]
+        be = s["beta"].view(B, Hv, T) if T == 1 else s["betaT"]
+        self.decode_fn(s["q"], s["k"], s["v"], be, s["pool"], self.lens, self.idx, g_, s["gk"],
+                       self.nacc, inp.scale, out=s["out"])
+
+    def fused(self, s):
+        self.fused_fn(s["q"], s["k"], s["v"], s["a"], s["b"], self.dt, self.ds, s["pool"],
+                      self.lens, self.idx, s["gk"], self.nacc, self.inp.scale, out=s["out"])
+
+    def step(self, i):
+        self.fused(self.sets[i % self.R])
+
+    def unfused_step(self, i):
+        s = self.sets[i % self.R]
+        self.gate(s)
+        if self.inp.T != 1:
+            self.transpose(s)
+        self.decode(s)
+
+    def free(self):
+        self.sets = []
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def warm_replays(torch, graph):
+    # Untimed replays (the first also uploads the graph) until WARM_MS of work have run back
+    # to back: the shader clock takes a few milliseconds of load to settle, and a replay
+    # timed straight after capture runs up to 10% slow on the latency-bound multi-token
+    # kernels.
+    t0 = time.perf_counter()
+    while True:
+        graph.replay()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= WARM_MS:
+            break
+
+
+def capture(torch, stream, body, n):
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(n):
+                body(i)
+    stream.wait_stream(cap)
+    return graph
+
+
+def graph_ms(torch, stream, body, n):
+    """Wall time of n calls of body(i) captured in one graph, timed around one replay."""
+    graph = capture(torch, stream, body, n)
+    warm_replays(torch, graph)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def kernel_avg_us(torch, stream, fn, sets, n):
+    """K back-to-back calls of one kernel, captured in a graph, timed with events on the
+    launch stream around each of KERNEL_REPLAYS replays (no per-launch event overhead; this
+    is the duration rocprofv3's kernel trace reports). Returns the median per-call time and
+    every replay's."""
+    g = capture(torch, stream, lambda i: fn(sets[i % len(sets)]), n)
+    warm_replays(torch, g)
+    per = []
+    for _ in range(KERNEL_REPLAYS):
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        g.replay()
+        a1.record(stream)
+        a1.synchronize()
+        per.append(a0.elapsed_time(a1) * 1e3 / n)
+    del g
+    return float(sorted(per)[len(per) // 2]), per
+
+
+def roofline(wl, us):
+    gbs = wl.step_bytes / (us * 1e-6) / 1e9
+    r = {"kernel": wl.fused_name, "bound": "hbm", "achieved": round(gbs, 2),
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+         "traffic": measured_traffic(wl.wid), "bytes_per_launch": wl.step_bytes,
+         "avg_launch_us": round(us, 3)}
+    if wl.prefill:
+        fl = prefill_mfma_flops(wl.inp)
+        tf = fl / (us * 1e-6) / 1e12
+        r["mfma_executed"] = {"flops_per_launch": fl, "achieved_tflops": round(tf, 1),
+                              "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "what": "bf16 matrix-core flops issued (split operands), not "
+                                      "the method's algorithmic flops"}
+    return r
+
+
+def extra_entry(torch, stream, wl, n):
+    """Fused-call duration and roofline of one more workload (kernel timing only)."""
+    for i in range(3):
+        wl.step(i)
+    torch.cuda.synchronize()
+    us, per = kernel_avg_us(torch, stream, wl.fused, wl.sets, n)
+    inp = wl.inp
+    r = roofline(wl, us)
+    r["launch_us_replays"] = [round(x, 3) for x in per]
+    return {"workload": wl.name, "config": {"B": inp.B, "H_q": inp.Hq, "H_v": inp.Hv,
+                                            "T": inp.T, "D_k": inp.Dk, "D_v": inp.Dv,
+                                            "N_slots": inp.N_slots, "rotation_sets": wl.R,
+                                            "calls_timed": n},
+            "call_us": round(us, 3),
+            "token_head_steps_per_s": round(wl.tok_heads / (us * 1e-6), 1),
+            "roofline": r}
 
 
 def main():
@@ -195,8 +447,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5])
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >= 1 GiB)")
+    ap.add_argument("--extra", default="1,3,4,5",
+                    help="other workloads whose fused-call duration the line also carries "
+                         "(comma-separated ids; empty for none)")
+    ap.add_argument("--extra-steps", type=int, default=50,
+                    help="calls per timed graph replay for the --extra workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,86 +468,21 @@ def main():
               "own), so more GPUs only repeat the one-GPU figure", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import gated_delta_rule_rgdr_amd as rg
-    import workloads
 
     rg.library()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wid = args.workload
-    inp = workloads.make_workload(wid, gate_inputs=True)
+    wl = Workload(wid, dev, args.rotate, args.steps)
+    inp = wl.inp
     B, Hq, Hv, T, Dk, Dv, N = inp.B, inp.Hq, inp.Hv, inp.T, inp.Dk, inp.Dv, inp.N_slots
-    dbytes, tok_heads = decode_bytes(inp)
-    gbytes = gate_bytes(inp)
-    step_bytes = fused_bytes(inp, dbytes, tok_heads)
-    touched = int(((inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < N)).sum()) \
-        * Hv * Dk * Dv * 2
-    R = args.rotate or max(2, math.ceil((1 << 30) / max(touched, 1)))
-    R = min(R, args.steps) if args.steps > 0 else R
-    log(f"workload {wid}: {workloads.WORKLOAD_NAMES[wid]}; fused step bytes {step_bytes}, "
-        f"unfused decode {dbytes} + gate {gbytes}; rotation sets {R}")
-
-    def bits(x):
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    base = dict(q=bits(inp.query), k=bits(inp.key), v=bits(inp.value), pool=bits(inp.state),
-                gk=torch.from_numpy(inp.gk).to(dev), a=torch.from_numpy(inp.gate_a).to(dev),
-                b=torch.from_numpy(inp.gate_b).to(dev))
-    dt = torch.from_numpy(inp.dt_bias).to(dev)
-    ds = torch.from_numpy(inp.decay_scale).to(dev)
-    lens = torch.from_numpy(inp.actual_seq_lengths).to(dev)
-    idx = torch.from_numpy(inp.ssm_state_indices).to(dev)
-    nacc = torch.from_numpy(inp.num_accepted_tokens).to(dev)
-    sets = []
-    for _ in range(R):
-        s = {k_: v_.clone() for k_, v_ in base.items()}
-        s["g"] = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
-        s["beta"] = torch.empty((B, T, Hv), dtype=torch.bfloat16, device=dev)
-        s["out"] = torch.empty((B, Hv, T, Dv), dtype=torch.bfloat16, device=dev)
-        if T != 1:
-            s["gT"] = torch.empty((B, Hv, T), dtype=torch.float32, device=dev)
-            s["betaT"] = torch.empty((B, Hv, T), dtype=torch.bfloat16, device=dev)
-        sets.append(s)
-    del base
-    torch.cuda.synchronize()
-
-    # g and beta come out of the gate as [B, T, H_v]; the decode reads [B, H_v, T]. With
-    # T = 1 these are the same bytes. For T > 1 the unfused chain transposes them with torch
-    # (part of the chain's time), while the decode kernel's own timing reads copies that
-    # were transposed once beforehand.
+    log(f"workload {wid}: {wl.name}; fused step bytes {wl.step_bytes}, unfused "
+        f"{wl.decode_name} {wl.dbytes} + gate {wl.gbytes}; rotation sets {wl.R}")
     if T != 1:
         log("note: T > 1; the unfused chain transposes g/beta with torch between its kernels")
-
-    def gate(s):
-        rg.la_gate(s["a"], dt, ds, s["b"], decay_dtype=torch.float32,
-                   beta_dtype=torch.bfloat16, decay_out=s["g"], beta_out=s["beta"])
-
-    def transpose(s):
-        s["gT"].copy_(s["g"].transpose(1, 2))
-        s["betaT"].copy_(s["beta"].transpose(1, 2))
-
-    def decode(s):
-        g_ = s["g"].view(B, Hv, T) if T == 1 else s["gT"]
-        be = s["beta"].view(B, Hv, T) if T == 1 else s["betaT"]
-        rg.rgdr_decode(s["q"], s["k"], s["v"], be, s["pool"], lens, idx, g_, s["gk"], nacc,
-                       inp.scale, out=s["out"])
-
-    def fused(s):
-        rg.rgdr_decode_gated(s["q"], s["k"], s["v"], s["a"], s["b"], dt, ds, s["pool"], lens, idx,
-                             s["gk"], nacc, inp.scale, out=s["out"])
-
-    def step(i):
-        fused(sets[i % R])
-
-    def unfused_step(i):
-        s = sets[i % R]
-        gate(s)
-        if T != 1:
-            transpose(s)
-        decode(s)
 
     def copy_calibration():
         # A plain elementwise copy of known size: 64 Mi fp32 elements read and written once.
@@ -303,103 +495,39 @@ def main():
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        step(i)
+        wl.step(i)
     torch.cuda.synchronize()
     log(f"warmup: {args.warmup} eager steps done")
     if args.eager_only:
         for i in range(args.steps):
-            step(args.warmup + i)
-            unfused_step(args.warmup + i)
+            wl.step(args.warmup + i)
+            wl.unfused_step(args.warmup + i)
         torch.cuda.synchronize()
         log(f"eager pass: {args.steps} steps done")
         if args.copy_calibration:
             copy_calibration()
         return
 
-    # K timed steps in one graph.
     K = args.steps
-
-    def warm_replays(graph):
-        # Untimed replays (the first also uploads the graph) until WARM_MS of work have run
-        # back to back: the shader clock takes a few milliseconds of load to settle, and a
-        # replay timed straight after capture runs up to 10% slow on the latency-bound
-        # multi-token kernels.
-        t0 = time.perf_counter()
-        while True:
-            graph.replay()
-            torch.cuda.synchronize()
-            if (time.perf_counter() - t0) * 1e3 >= WARM_MS:
-                break
-
-    def graph_ms(body, first):
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(K):
-                    body(first + i)
-        stream.wait_stream(cap)
-        warm_replays(graph)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1)
-
-    total_ms = graph_ms(step, args.warmup)
+    total_ms = graph_ms(torch, stream, lambda i: wl.step(args.warmup + i), K)
     ms_per_step = total_ms / K
     log(f"timed: {K} steps in {total_ms:.3f} ms ({ms_per_step * 1e3:.2f} us/step)")
     for i in range(args.warmup):
-        unfused_step(i)
-    unfused_ms = graph_ms(unfused_step, args.warmup) / K
-    log(f"unfused chain (la_gate + rgdr_decode): {unfused_ms * 1e3:.2f} us/step")
+        wl.unfused_step(i)
+    unfused_ms = graph_ms(torch, stream, lambda i: wl.unfused_step(args.warmup + i), K) / K
+    log(f"unfused chain (la_gate + {wl.decode_name}): {unfused_ms * 1e3:.2f} us/step")
 
-    # Kernel durations: K back-to-back launches of one kernel, captured in a graph, timed
-    # with events on the launch stream around one replay (no per-launch event overhead;
-    # this is the duration rocprofv3's kernel trace reports).
-    def kernel_avg_us(fn):
-        g = torch.cuda.CUDAGraph()
-        c = torch.cuda.Stream()
-        c.wait_stream(stream)
-        with torch.cuda.stream(c):
-            with torch.cuda.graph(g, stream=c):
-                for i in range(K):
-                    fn(sets[i % R])
-        stream.wait_stream(c)
-        warm_replays(g)
-        per = []
-        for _ in range(KERNEL_REPLAYS):
-            a0 = torch.cuda.Event(enable_timing=True)
-            a1 = torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            g.replay()
-            a1.record(stream)
-            a1.synchronize()
-            per.append(a0.elapsed_time(a1) * 1e3 / K)
-        del g
-        return float(sorted(per)[len(per) // 2]), per
-
-    fused_us, fused_all = kernel_avg_us(fused)
-    dec_us, _ = kernel_avg_us(decode)
-    gate_us, _ = kernel_avg_us(gate)
-    log(f"fused decode kernel: {fused_us:.2f} us per launch; unfused: decode {dec_us:.2f} us, "
+    fused_us, fused_all = kernel_avg_us(torch, stream, wl.fused, wl.sets, K)
+    dec_us, _ = kernel_avg_us(torch, stream, wl.decode, wl.sets, K)
+    gate_us, _ = kernel_avg_us(torch, stream, wl.gate, wl.sets, K)
+    log(f"fused kernel: {fused_us:.2f} us per call; unfused: {wl.decode_name} {dec_us:.2f} us, "
         f"gate {gate_us:.2f} us (medians of {KERNEL_REPLAYS} replays; fused replays: "
         + " ".join(f"{x:.2f}" for x in fused_all) + ")")
 
     # The box's practical streaming rate: a plain 256 MiB copy (read + write), graph-timed.
     csrc = torch.ones(64 << 20, dtype=torch.float32, device=dev)
     cdst = torch.empty_like(csrc)
-    cg = torch.cuda.CUDAGraph()
-    cs = torch.cuda.Stream()
-    cs.wait_stream(stream)
-    with torch.cuda.stream(cs):
-        with torch.cuda.graph(cg, stream=cs):
-            for _ in range(20):
-                torch.mul(csrc, 1.0, out=cdst)
-    stream.wait_stream(cs)
+    cg = capture(torch, stream, lambda i: torch.mul(csrc, 1.0, out=cdst), 20)
     cg.replay()
     torch.cuda.synchronize()
     c0 = torch.cuda.Event(enable_timing=True)
@@ -416,15 +544,27 @@ def main():
     if args.copy_calibration:
         copy_calibration()
 
-    kernel_gbs = step_bytes / (fused_us * 1e-6) / 1e9
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    steps_per_s = tok_heads / (ms_per_step * 1e-3)
+    value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
+    steps_per_s = wl.tok_heads / (ms_per_step * 1e-3)
+    roof = roofline(wl, fused_us)
+    roof["launch_us_replays"] = [round(x, 3) for x in fused_all]
+    wl.free()
 
-    traffic = measured_traffic(wid)
+    extras = {}
+    for tok in [t for t in args.extra.split(",") if t.strip()]:
+        ew = int(tok)
+        if ew == wid or ew not in range(6):
+            continue
+        e = Workload(ew, dev, 0, args.extra_steps)
+        extras[str(ew)] = extra_entry(torch, stream, e, args.extra_steps)
+        log(f"workload {ew} ({e.name}): {e.fused_name} {extras[str(ew)]['call_us']:.2f} us "
+            f"per call, {100 * extras[str(ew)]['roofline']['frac']:.1f}% of 8 TB/s")
+        e.free()
+        del e
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, step_bytes, tok_heads, args.cpu_seconds)
-    n_pairs = int(((inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < N)).sum()) * Hv
+        cpu = cpu_baseline(inp, args.cpu_seconds)
 
     rec = {
         "metric": METRIC,
@@ -440,23 +580,21 @@ def main():
         "dtype": "f32",
         "storage_dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workloads.WORKLOAD_NAMES[wid] + " (gate + decode step)",
-                   "step": "rgdr_decode_gated (gate fused into the decode kernel)",
+        "config": {"workload": wl.name + " (gate + recurrence step)",
+                   "step": f"{wl.fused_name} (gate fused into the kernel)",
                    "B": B, "H_q": Hq, "H_v": Hv, "T": T, "D_k": Dk, "D_v": Dv,
-                   "N_slots": N, "rotation_sets": R, "parallelism": "none (1 GPU)"},
+                   "N_slots": N, "rotation_sets": wl.R, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "token_head_steps_per_s": round(steps_per_s, 1),
-        "step_bytes": step_bytes,
-        "bytes_per_state_element": round(step_bytes / (n_pairs * Dk * Dv), 4),
+        "step_bytes": wl.step_bytes,
+        "bytes_per_state_element": round(wl.step_bytes / (wl.n_pairs * Dk * Dv), 4),
         "copy_reference": {"gbs": round(copy_gbs, 1), "us": round(copy_us, 2),
                            "what": "torch elementwise copy, 256 MiB read + 256 MiB write"},
-        "roofline": {"kernel": "rgdr_decode_gated", "bound": "hbm",
-                     "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": step_bytes, "avg_launch_us": round(fused_us, 3),
-                     "launch_us_replays": [round(x, 3) for x in fused_all]},
+        "roofline": roof,
         "unfused_ms_per_step": round(unfused_ms, 6),
-        "unfused_kernels_avg_us": {"la_gate": round(gate_us, 3), "rgdr_decode": round(dec_us, 3)},
+        "unfused_kernels_avg_us": {"la_gate": round(gate_us, 3),
+                                   wl.decode_name: round(dec_us, 3)},
+        "workloads": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
