@@ -378,16 +378,16 @@ constexpr int chunk_vbase() { return 24 * DK > 128 * kChunkYS ? 24 * DK : 128 * 
 template <int DK>
 constexpr int chunk_ops() { return chunk_vbase<DK>() + 8 * 128 + 16; }  // floats, 16-B multiple
 
-template <int DK, int GATE>
-__device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, 128, kMaxT> &o, float *ob,
+template <int DK, int GATE, int NT = 128>
+__device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, NT, kMaxT> &o, float *ob,
                                                 float scale, bool norm, int L, int tid) {
-    using Sh = TileShape<DK, 128, 128, kMaxT>;
+    using Sh = TileShape<DK, 128, NT, kMaxT>;
     constexpr int TV = 128;
     float *sd = ob, *sk = ob + 8 * DK, *sq = ob + 16 * DK, *sv = ob + chunk_vbase<DK>();
     float *sb = sv + 8 * TV;
 #pragma unroll
     for (int j = 0; j < Sh::GKV; ++j) {
-        const int e = tid + j * 128;
+        const int e = tid + j * NT;
         const int t = e * 4 / DK, i0 = e * 4 % DK;
         if (t >= kMaxT) continue;
         float g;
@@ -402,7 +402,7 @@ __device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, 128, kMaxT> &
     }
 #pragma unroll
     for (int j = 0; j < Sh::KQV; ++j) {
-        const int e = tid + j * 128;
+        const int e = tid + j * NT;
         const int t = e * 8 / DK, i0 = e * 8 % DK;
         if (t >= kMaxT) continue;  // uniform per 8-lane group; past the last token
         const uint32_t kw[4] = {o.k[j].x, o.k[j].y, o.k[j].z, o.k[j].w};
@@ -435,8 +435,9 @@ __device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, 128, kMaxT> &
     }
 #pragma unroll
     for (int j = 0; j < Sh::VV; ++j) {
-        const int e = tid + j * 128;
+        const int e = tid + j * NT;
         const int t = e / (TV / 8), c8 = e % (TV / 8);
+        if (NT > 128 && t >= kMaxT) continue;  // only with more threads than values
         f32x4 *dst = reinterpret_cast<f32x4 *>(sv + t * TV + c8 * 8);
         dst[0] = f32x4{bf16_lo(o.v[j].x), bf16_hi(o.v[j].x), bf16_lo(o.v[j].y), bf16_hi(o.v[j].y)};
         dst[1] = f32x4{bf16_lo(o.v[j].z), bf16_hi(o.v[j].z), bf16_lo(o.v[j].w), bf16_hi(o.v[j].w)};

@@ -29,10 +29,9 @@ namespace rgdr {
 
 constexpr int kPrefillMaxT = 65536;  // tokens per call: keeps every per-item offset in 32 bits
 
-// Waves per SIMD the kernel is compiled for. At D_k = 128 the fp32 state (128 values per lane)
-// and one run's per-row working set need more than the 256 registers of two waves per SIMD.
+// Waves per SIMD the kernel is compiled for (the register budget).
 #ifndef RGDR_PREFILL_MIN_WAVES
-#define RGDR_PREFILL_MIN_WAVES 1
+#define RGDR_PREFILL_MIN_WAVES 2
 #endif
 
 // f32x4 pair -> bf16 high parts and bf16 remainders, 8 values in k order (x0 first).
@@ -50,62 +49,82 @@ __device__ __forceinline__ void split8(const f32x4 &x0, const f32x4 &x1, bf16x8 
     lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
-// Lane layout (as the decode's chunk form). Lane l = (kg, n16) = (l / 16, l % 16) of wave w
-// holds state rows 16 rb + 4 kg + i (rb < D_k / 16, i < 4) of tile columns 64 w + 4 n16 + c
-// (c < 4) as S[rb][c][i]: the accumulator layout of a 16 x 16 block of rows 16 rb .. + 15 and
-// columns 64 w + 4 n + c (column set c). Rows 4 kg .. 4 kg + 3 of two row blocks are also the
-// 8 k slots of lane group kg in a 16x16x32 product, so the state turns into the B operand of
-// Y = X^T S in the lane that holds it.
+// Eight bf16 values of two 4-element LDS runs (k slots 0..3, then 4..7).
+__device__ __forceinline__ bf16x8 lds_pair8(const uint16_t *p0, const uint16_t *p1) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p0), v = *reinterpret_cast<const uint2 *>(p1);
+    return __builtin_bit_cast(bf16x8, u32x4{u.x, u.y, v.x, v.y});
+}
+
+// Decay range inside which a run's Gram matrices are formed on the matrix cores from the
+// factors c_t k_t (or c_t scale q_t) and k_s / c_s: every c_t of the run within
+// [2^-48, 2^48] keeps both factors and their products far from fp32 overflow. A wave with
+// a row outside it forms that row's share of the matrices directly, from products of the
+// decays between s and t (each in [0, 1] for decays), as the decode does.
+constexpr float kGramLo = 0x1p-48f, kGramHi = 0x1p48f;
+
+// Lane layout. Four waves per item; wave w owns tile columns 32 w .. 32 w + 31 over all D_k
+// rows. Lane l = (kg, n16) = (l / 16, l % 16) holds state rows 16 rb + 4 kg + i (rb < D_k / 16,
+// i < 4) of columns 32 w + 2 n16 + c (c < 2) as S[rb][c][i]: the accumulator layout of the
+// 16 x 16 block of rows 16 rb .. + 15 and columns 32 w + 2 n + c (column set c). Rows
+// 4 kg .. 4 kg + 3 of two row blocks are also the 8 k slots of lane group kg in a 16x16x32
+// product, so the state turns into the B operand of Y = X^T S in the lane that holds it.
+// At 64 state values per lane two waves fit a SIMD.
 template <int DK, int GATE>
-__global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(const DecodeArgs a,
-                                                          const int32_t *__restrict__ lens,
-                                                          const int32_t *__restrict__ idx,
-                                                          const int32_t *__restrict__ nacc) {
+__global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
+    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nacc) {
     static_assert(DK == 64 || DK == 128, "D_k = 64 or 128");
-    constexpr int TV = 128, NT = 128;
+    constexpr int TV = 128, NT = 256, NW = 4;
     constexpr int NRB = DK / 16, NPB = DK / 32;
-    // LDS: staged operands of one run (chunk_stage_ops) | XT hi, lo [16][XS] | KA hi, lo
-    // [D_k][8] | UT [wave][hi, lo] [4 column sets][16][8] | c of each row at the run's end
-    // [D_k] | G partials [wave][64] | M and N [wave][8][8]. Y^T [128][kChunkYS] takes the d,
-    // k and q planes once both waves have prepared their rows.
+    // LDS: staged operands of one run (chunk_stage_ops) | XT hi, lo [16][XS] (c k | c scale
+    // q) | KC hi, lo [16][XS] (k_s / c_s; rows 8..15 stay zero) | KA hi, lo [D_k][8] | UT
+    // [wave][hi, lo][2 column sets][16][8] | c of each row at the run's end [D_k] | direct
+    // Gram partials [2][64] | M and N [wave][8][8]. Y^T [128][kChunkYS] takes the d, k and q
+    // planes once the rows are prepared.
     constexpr int XS = DK + 4;
     constexpr int VB = chunk_vbase<DK>();
     constexpr int OFF_XT = chunk_ops<DK>() * 4;
-    constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
+    constexpr int OFF_KC = OFF_XT + 2 * 16 * XS * 2;
+    constexpr int OFF_KA = OFF_KC + 2 * 16 * XS * 2;
     constexpr int OFF_UT = OFF_KA + 2 * DK * 8 * 2;
-    constexpr int OFF_CL = OFF_UT + 2 * 2 * 64 * 8 * 2;
+    constexpr int OFF_CL = OFF_UT + NW * 2 * 2 * 16 * 8 * 2;
     constexpr int OFF_GP = OFF_CL + DK * 4;
     constexpr int OFF_GS = OFF_GP + 2 * 64 * 4;
-    constexpr int BYTES = OFF_GS + 2 * 2 * 64 * 4;
-    static_assert(BYTES % 16 == 0 && BYTES <= 40960, "LDS carve: four items per compute unit");
+    constexpr int BYTES = OFF_GS + NW * 2 * 64 * 4;
+    static_assert(BYTES % 16 == 0 && BYTES <= 81920, "LDS carve: two items per compute unit");
     constexpr int YS = kChunkYS;
     __shared__ f32x4 lds4[BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
     float *ob = reinterpret_cast<float *>(lb);
     uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
+    uint16_t *kc_hi = reinterpret_cast<uint16_t *>(lb + OFF_KC), *kc_lo = kc_hi + 16 * XS;
     uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + DK * 8;
     float *crow = reinterpret_cast<float *>(lb + OFF_CL);
     float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
 
     const Index x{lens, idx, nacc};
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n16 = lane & 15, kg = lane >> 4;
-    uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT) + w * 2 * 64 * 8, *ut_lo = ut_hi + 64 * 8;
+    const int tid = threadIdx.x, lane = tid & 63, n16 = lane & 15, kg = lane >> 4;
+    // w is the same in every lane of a wave; readfirstlane tells the compiler so, which keeps
+    // the buffer descriptors built from it in scalar registers.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT) + w * 2 * 32 * 8, *ut_lo = ut_hi + 32 * 8;
     float *gsM = reinterpret_cast<float *>(lb + OFF_GS) + w * 2 * 64, *gsN = gsM + 64;
     const Item m = resolve(a, x, xcd_item(blockIdx.x, gridDim.x));
     const int L = m.L, n = m.n;
     auto ycol = [&](int j) { return ob + j * YS; };
 
-    // A last tile of 64 columns (D_v an odd multiple of 64) leaves wave 1 without columns:
-    // its state and output accesses get empty ranges and it computes on zeros.
-    const bool cols = m.tile * TV + 64 * __builtin_amdgcn_readfirstlane(w) < a.Dv;
+    // A last tile of 64 columns (D_v an odd multiple of 64) leaves waves 2 and 3 without
+    // columns: their state and output accesses get empty ranges and they compute on zeros.
+    const bool cols = m.tile * TV + 32 * w < a.Dv;
     const uint32_t trange = cols ? tile_range<DK, TV>(a, m) : 0u;
     const size_t tb = m.state ? tile_base<DK, TV>(a, m) : 0;
     const auto rs = make_rsrc(a.pool + tb, trange);
     const auto rso = make_rsrc(a.pool_out + tb, trange);
-    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 64 * w + 4 * n16) * 2);
+    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 32 * w + 2 * n16) * 2);
     const size_t bh = (size_t)m.b * a.Hv + m.h;
-    const int col = 64 * w + lane;  // this lane's column in the solve
-    const uint32_t ocol = (uint32_t)((m.tile * TV + col) * 2);
+    const int jcol = lane & 31;       // this lane's local column in the solve
+    const int col = 32 * w + jcol;    // lanes 32..63 repeat lanes 0..31 and store nothing
+    const uint32_t ocol = lane < 32 ? (uint32_t)((m.tile * TV + col) * 2) : 0x40000000u;
 
     // Runs of at most kMaxT tokens; the run holding the accepted prefix's end stops there.
     auto run_end = [&](int t0) {
@@ -117,35 +136,39 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
     int t0 = 0, t1 = run_end(0);
     Ops<DK, TV, NT, kMaxT> o;
     load_ops<DK, TV, NT, kMaxT, GATE>(a, m, o, tid, 0, t1);
-    u32x2 raw[NRB][4];
+    uint32_t raw[NRB][4];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b64(
+            raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b32(
                 rs, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_LOAD_POLICY);
-    f32x4 S[NRB][4];
+    // KC rows 8..15 are the unused columns of the Gram products: zero, once.
+    for (int e = tid; e < 2 * 8 * XS; e += NT) {
+        const int half = e / (8 * XS), r = e % (8 * XS);
+        (half ? kc_lo : kc_hi)[8 * XS + r] = 0;
+    }
+    f32x4 S[NRB][2];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            S[rb][0][i] = bf16_lo(raw[rb][i].x);
-            S[rb][1][i] = bf16_hi(raw[rb][i].x);
-            S[rb][2][i] = bf16_lo(raw[rb][i].y);
-            S[rb][3][i] = bf16_hi(raw[rb][i].y);
+            S[rb][0][i] = bf16_lo(raw[rb][i]);
+            S[rb][1][i] = bf16_hi(raw[rb][i]);
         }
     if (n == 0) {  // nothing accepted: commit the incoming bytes
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                store8<RGDR_STATE_STORE_POLICY>(raw[rb][i], rso,
-                                                lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    raw[rb][i], rso, lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2), 0,
+                    RGDR_STATE_STORE_POLICY);
     }
 
     while (t0 < L) {  // uniform over the workgroup
         const int Lc = t1 - t0;
-        chunk_stage_ops<DK, GATE>(o, ob, a.scale, a.norm_qk != 0, Lc, tid);
+        chunk_stage_ops<DK, GATE, NT>(o, ob, a.scale, a.norm_qk != 0, Lc, tid);
         // The next run's operands travel while this run is computed (zeros past the end).
         const int t0n = t1, t1n = t1 < L ? run_end(t1) : t1;
         __builtin_amdgcn_sched_barrier(0);
@@ -153,46 +176,66 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
 
-        // Per-row preparation: thread r owns row r (at D_k = 64 wave 1 has none).
-        float gp[64];  // partial G: [t][s] (s <= t) holds N[t][s], [s][t] (s < t) holds M[t][s]
+        // Per-row preparation: thread r owns row r (waves 0 and 1 at D_k = 128, wave 0 at
+        // D_k = 64).
+        const bool has_rows = 64 * w < DK;
+        bool direct = false;  // this wave forms its rows' Gram shares directly
+        float gp[64];  // direct partial G: [t][s] (s <= t) holds N[t][s], [s][t] (s < t) M[t][s]
 #pragma unroll
         for (int e = 0; e < 64; ++e) gp[e] = 0.f;
-        const bool has_rows = 64 * w < DK;
         if (has_rows) {
             const int row = tid;
-            float d[8], k[8], q[8];
+            float d[8], k[8], q[8], c[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                d[t] = ob[t * DK + row];  // tokens past the run were staged neutral
+                d[t] = ob[t * DK + row];  // tokens past the run were staged neutral (d = 1)
                 k[t] = ob[8 * DK + t * DK + row];
                 q[t] = ob[16 * DK + t * DK + row];
             }
-            float c = 1.f, cend = 1.f;
+            float cc = 1.f, cend = 1.f, cmin = 1.f, cmax = 1.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                c *= d[t];
+                cc *= d[t];
+                c[t] = cc;
+                cmin = fminf(cmin, cc);
+                cmax = fmaxf(cmax, cc);
                 uint16_t hk, lk, hq, lq;
-                split_bf16(c * k[t], hk, lk);
-                split_bf16(c * q[t], hq, lq);
+                split_bf16(cc * k[t], hk, lk);
+                split_bf16(cc * q[t], hq, lq);
                 xt_hi[t * XS + row] = hk;
                 xt_lo[t * XS + row] = lk;
                 xt_hi[(8 + t) * XS + row] = hq;
                 xt_lo[(8 + t) * XS + row] = lq;
-                if (t + 1 == Lc) cend = c;
+                if (t + 1 == Lc) cend = cc;
             }
             crow[row] = cend;
+            direct = __ballot(!(cmin >= kGramLo && cmax <= kGramHi)) != 0;  // NaN: direct
             float ka[8];
+            if (!direct) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                float wv = k[s];  // g(s,s) k_s
-                ka[s] = (s + 1 == Lc) ? wv : 0.f;
-                gp[s * 8 + s] = wv * q[s];
+                for (int s = 0; s < 8; ++s) {
+                    const float kcs = k[s] * __builtin_amdgcn_rcpf(c[s]);  // k_s / c_s
+                    uint16_t h, l;
+                    split_bf16(kcs, h, l);
+                    kc_hi[s * XS + row] = h;
+                    kc_lo[s * XS + row] = l;
+                    ka[s] = s < Lc ? cend * kcs : 0.f;  // g(Lc-1, s) k_s
+                }
+            } else {
 #pragma unroll
-                for (int t = s + 1; t < 8; ++t) {
-                    wv *= d[t];  // g(t,s) k_s
-                    gp[s * 8 + t] = wv * k[t];
-                    gp[t * 8 + s] = wv * q[t];
-                    if (t + 1 == Lc) ka[s] = wv;
+                for (int s = 0; s < 8; ++s) {
+                    kc_hi[s * XS + row] = 0;
+                    kc_lo[s * XS + row] = 0;
+                    float wv = k[s];  // g(s,s) k_s
+                    ka[s] = (s + 1 == Lc) ? wv : 0.f;
+                    gp[s * 8 + s] = wv * q[s];
+#pragma unroll
+                    for (int t = s + 1; t < 8; ++t) {
+                        wv *= d[t];  // g(t,s) k_s
+                        gp[s * 8 + t] = wv * k[t];
+                        gp[t * 8 + s] = wv * q[t];
+                        if (t + 1 == Lc) ka[s] = wv;
+                    }
                 }
             }
             uint16_t kh[8], kl[8];
@@ -205,36 +248,56 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
                 u32x4{kl[0] | ((uint32_t)kl[1] << 16), kl[2] | ((uint32_t)kl[3] << 16),
                       kl[4] | ((uint32_t)kl[5] << 16), kl[6] | ((uint32_t)kl[7] << 16)};
         }
-        // G over this wave's 64 rows: lane e holds entry e.
-        gpart[64 * w + lane] = has_rows ? wave_sum64_transposed(gp, lane) : 0.f;
+        if (w < 2)  // the direct shares of this wave's rows (zero where none): lane e, entry e
+            gpart[64 * w + lane] = direct ? wave_sum64_transposed(gp, lane) : 0.f;
         lds_barrier();
+
+        // M and N: the factored products on the matrix cores (each wave for itself), plus
+        // the direct shares. Lane (kg, n16) holds G[4 kg + i][n16]: row m < 8 is
+        // c_m k_m . (k_s / c_s) = M[m][s] (s < m), row m >= 8 is N[m - 8][s] (s <= m - 8).
         {
-            const float g_e = gpart[lane] + gpart[64 + lane];
-            const int ea = lane >> 3, eb = lane & 7;
-            if (ea < eb)
-                gsM[eb * 8 + ea] = g_e;
-            else
-                gsN[ea * 8 + eb] = g_e;
+            f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pb = 0; pb < NPB; ++pb) {
+                const int r0 = 32 * pb + 4 * kg;
+                const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
+                const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
+                const bf16x8 bh = lds_pair8(kc_hi + n16 * XS + r0, kc_hi + n16 * XS + r0 + 16);
+                const bf16x8 bl = lds_pair8(kc_lo + n16 * XS + r0, kc_lo + n16 * XS + r0 + 16);
+                g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, g, 0, 0, 0);
+                g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, g, 0, 0, 0);
+                g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, g, 0, 0, 0);
+            }
+            if (n16 < 8) {
+                const int s = n16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int mrow = 4 * kg + i;
+                    if (mrow < 8) {
+                        const int e = s * 8 + mrow;  // M[mrow][s], s < mrow
+                        gsM[mrow * 8 + s] = g[i] + gpart[e] + gpart[64 + e];
+                    } else {
+                        const int t = mrow - 8, e = t * 8 + s;  // N[t][s], s <= t
+                        gsN[t * 8 + s] = g[i] + gpart[e] + gpart[64 + e];
+                    }
+                }
+            }
         }
         lds_phase();
 
-        // Y = [c k | c scale q]^T S (16 x 64, this wave's columns), column set c, over
+        // Y = [c k | c scale q]^T S (16 x 32, this wave's columns), column set c, over
         // row-block pairs; three products of the split parts (high x high, low x high,
         // high x low).
-        auto pair8 = [](const uint16_t *p0, const uint16_t *p1) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(p0), v = *reinterpret_cast<const uint2 *>(p1);
-            return __builtin_bit_cast(bf16x8, u32x4{u.x, u.y, v.x, v.y});
-        };
-        f32x4 acc[4];
+        f32x4 acc[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 2; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb) {
             const int r0 = 32 * pb + 4 * kg;
-            const bf16x8 ah = pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
-            const bf16x8 al = pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
+            const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
+            const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < 2; ++c) {
                 bf16x8 sh, sl;
                 split8(S[2 * pb][c], S[2 * pb + 1][c], sh, sl);
                 acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh, acc[c], 0, 0, 0);
@@ -243,14 +306,14 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
             }
         }
         // Y to LDS, transposed: accumulator c holds rows 4 kg .. 4 kg + 3 of column
-        // 64 w + 4 n16 + c.
-        lds_phase();
+        // 32 w + 2 n16 + c. Every wave has prepared its rows (barrier above), so the d, k and
+        // q planes are free.
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<f32x4 *>(ycol(64 * w + 4 * n16 + c) + 4 * kg) = acc[c];
+        for (int c = 0; c < 2; ++c)
+            *reinterpret_cast<f32x4 *>(ycol(32 * w + 2 * n16 + c) + 4 * kg) = acc[c];
         lds_phase();
 
-        // Triangular solve for column 64 w + lane; outputs of the run's tokens.
+        // Triangular solve for column 32 w + (lane & 31); outputs of the run's tokens.
         const auto rout = make_rsrc(a.out + (bh * a.T + t0) * a.Dv,
                                     cols ? (uint32_t)(Lc * a.Dv * 2) : 0u);
         float yc[16];
@@ -285,8 +348,9 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
             uint16_t h[8], l[8];
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) split_bf16(u[s2], h[s2], l[s2]);
-            // local column j = 4 n + c goes to UT position c * 16 + n
-            const int p = (lane & 3) * 16 + (lane >> 2);
+            // local column j = 2 n + c goes to UT position c * 16 + n (lanes 32..63 write
+            // the same values as lanes 0..31)
+            const int p = (jcol & 1) * 16 + (jcol >> 1);
             *reinterpret_cast<u32x4 *>(ut_hi + p * 8) =
                 u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
                       h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
@@ -301,9 +365,9 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
         // carries tokens 4 (kg & 1) .. + 3 of A's high part (kg < 2) or remainder (kg >= 2),
         // against U's high part, then U's remainder. Only this one instruction shape ever
         // accumulates into S.
-        s16x4 buh[4], bul[4];
+        s16x4 buh[2], bul[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
             buh[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_hi + (c * 16 + n16) * 8 + 4 * (kg & 1)));
             bul[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_lo + (c * 16 + n16) * 8 + 4 * (kg & 1)));
         }
@@ -313,7 +377,7 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
             const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
             const s16x4 ak = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ka_lane + 16 * rb * 8));
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < 2; ++c) {
                 S[rb][c] = S[rb][c] * cr;
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, buh[c], S[rb][c], 0, 0, 0);
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bul[c], S[rb][c], 0, 0, 0);
@@ -326,22 +390,22 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    store8<RGDR_STATE_STORE_POLICY>(
-                        u32x2{pack_bf16x2(S[rb][0][i], S[rb][1][i]),
-                              pack_bf16x2(S[rb][2][i], S[rb][3][i])},
-                        rso, lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        pack_bf16x2(S[rb][0][i], S[rb][1][i]), rso,
+                        lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2), 0,
+                        RGDR_STATE_STORE_POLICY);
         }
         lds_barrier();  // the next run's staging reuses every LDS area
     }
 
-    // Padded (or skipped) tokens: +0.0 rows. Lane (r, c8) stores 8 columns of row r of each
-    // group of 8 rows; rows past T fall outside the range.
+    // Padded (or skipped) tokens: +0.0 rows. Lane (r, c4) stores 8 columns of row r of each
+    // group of 16 rows; rows past T fall outside the range.
     if (cols && L < a.T) {
         const int pad = a.T - L;
-        const auto rz = make_rsrc(a.out + (bh * a.T + L) * a.Dv + m.tile * TV + 64 * w,
-                                  (uint32_t)(((pad - 1) * a.Dv + 64) * 2));
-        const uint32_t zoff = (uint32_t)(((lane >> 3) * a.Dv + 8 * (lane & 7)) * 2);
-        for (int t = 0; t < pad; t += 8)
+        const auto rz = make_rsrc(a.out + (bh * a.T + L) * a.Dv + m.tile * TV + 32 * w,
+                                  (uint32_t)(((pad - 1) * a.Dv + 32) * 2));
+        const uint32_t zoff = (uint32_t)(((lane >> 2) * a.Dv + 8 * (lane & 3)) * 2);
+        for (int t = 0; t < pad; t += 16)
             store16<0>(u32x4{0u, 0u, 0u, 0u}, rz, zoff + (uint32_t)(t * a.Dv * 2));
     }
 }
@@ -349,7 +413,7 @@ __global__ __launch_bounds__(128, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(co
 template <int DK, int GATE>
 static hipError_t launch_prefill(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                  const int32_t *nacc, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_kernel<DK, GATE>), dim3(a.n_items), dim3(128), 0, stream, a,
+    hipLaunchKernelGGL((prefill_kernel<DK, GATE>), dim3(a.n_items), dim3(256), 0, stream, a,
                        lens, idx, nacc);
     return hipGetLastError();
 }
