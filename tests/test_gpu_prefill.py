@@ -184,7 +184,7 @@ def test_prefill_chaining(rg):
         check_decode(inp, torch.cat(outs, dim=2), d["pool"], ref, f"{64 // step} calls ({fn})")
 
 
-EXTREMES = ["strong_decay", "zero_decay", "mixed_rows", "growth"]
+EXTREMES = ["strong_decay", "zero_decay", "mixed_rows", "split_rows", "growth"]
 
 
 @pytest.mark.parametrize("case", EXTREMES)
@@ -201,6 +201,8 @@ def test_prefill_extreme_decays(rg, case):
     elif case == "mixed_rows":
         inp.g[:] = rng.uniform(-25.0, 3.0, inp.g.shape).astype(np.float32)
         inp.gk[:] = -rng.uniform(0.0, 12.0, inp.gk.shape).astype(np.float32)
+    elif case == "split_rows":   # rows 64.. decay by e^-10 per token, rows 0..63 mildly:
+        inp.gk[:, :, :, 64:] = -10.0  # their Gram shares are formed two different ways
     else:                         # exp(g) > 1 throughout: outside the operator's domain
         inp.g[:] = 2.5
     out, st = gpu_prefill(inp)
