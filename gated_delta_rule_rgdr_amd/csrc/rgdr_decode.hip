@@ -702,12 +702,12 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 //   o_t = S0^T (c_t scale q_t)  + sum_{s<=t} N[t][s] u_s,  N[t][s] = sum_i g(t,s)_i k_s,i scale q_t,i
 //   u_t = beta_t (v_t - p_t)
 //   S_n = diag(c_{n-1}) S0 + sum_{s<n} (g(n-1,s) k_s) (x) u_s        (the committed state)
-// The two sums over D_k x D_v x L (S0^T [c k | c scale q], and diag(c) S0 plus the rank-n
-// update) are bf16 MFMAs with fp32 accumulation (16x16x32 for the first, 16x16x16 for the
-// second): S0 is bf16 already, and every fp32 operand is split into a bf16 high part and a
-// bf16 remainder, so the products keep about 16 bits of each operand. The rest (decay
-// products, the 8 x 8 matrices M and N, and the triangular solve for u, column by column)
-// is fp32 VALU.
+// The two sums over D_k x D_v x L (S0^T [c k | c scale q], and the rank-n update) are bf16
+// 16x16x32 MFMAs with fp32 accumulation: S0 is bf16 already, and every fp32 operand is split
+// into a bf16 high part and a bf16 remainder, so the products keep about 16 bits of each
+// operand. The rest (decay products, the 8 x 8 matrices M and N, the triangular solve for u,
+// column by column, and the row scaling diag(c) S0 that starts each commit accumulator) is
+// fp32 VALU.
 //
 // Two waves per item. Wave w owns tile columns 64 w .. 64 w + 63 over all D_k rows, so
 // each wave's contraction, solve and update are complete for its columns; only the per-row
@@ -719,10 +719,9 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 // (rb < D_k / 16, i < 4), columns 64 w + 4 n16 .. + 3: 16 lanes cover the wave's 128 bytes of a
 // row. For the contraction the tile's row index is the k index (the 8 k slots of lane group
 // kg hold its rows 4 kg + i of two row blocks) and column 64 w + 4 n + c is element n of
-// column set c. In the commit the block's own 4 rows per lane group are the k slots of
-// diag(c) S0, and the accumulator of block (rb, c) holds exactly the lane's own elements of
-// rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c, so the update lands in the layout the
-// commit stores.
+// column set c. In the commit the accumulator of block (rb, c) holds exactly the lane's own
+// elements of rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c: the lane scales its own loaded
+// values into it, and the update lands in the layout the commit stores.
 // ---------------------------------------------------------------------------------------
 
 // The chunk form serves calls with T >= RGDR_CHUNK_MIN_T. Its time hardly depends on the
@@ -781,8 +780,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     constexpr int TV = 128, NT = 128;
     constexpr int NRB = DK / 16, NPB = DK / 32;  // row blocks of the tile, and their pairs
     // LDS: staged operands (chunk_stage_ops) | XT hi, lo [16][XS] | KA hi, lo [D_k][8] |
-    // UT [wave][hi, lo] [4 column sets][16][8] | diag(c_{n-1}) operands per row | G partials
-    // [wave][64] | M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row)
+    // UT [wave][hi, lo] [4 column sets][16][8] | c_{n-1} per row | G partials [wave][64] |
+    // M and N [wave][8][8]. Y^T [128][16] fp32 (one tile column per 80-byte row)
     // takes the d, k and q planes of the staged operands once both waves have prepared their
     // rows. The row stride of XT is padded (XS = D_k + 4) so the fragment reads of the 16
     // lanes of a lane group fall in different LDS banks; UT is ordered by column set for the
@@ -792,8 +791,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     constexpr int OFF_XT = chunk_ops<DK>() * 4;
     constexpr int OFF_KA = OFF_XT + 2 * 16 * XS * 2;
     constexpr int OFF_UT = OFF_KA + 2 * DK * 8 * 2;
-    constexpr int OFF_DG = OFF_UT + 2 * 2 * 64 * 8 * 2;
-    constexpr int OFF_GP = OFF_DG + DK * 16;
+    constexpr int OFF_CL = OFF_UT + 2 * 2 * 64 * 8 * 2;
+    constexpr int OFF_GP = OFF_CL + DK * 4;
     constexpr int OFF_GS = OFF_GP + 2 * 64 * 4;
     constexpr int BYTES = OFF_GS + 2 * 2 * 64 * 4;
     static_assert(BYTES % 16 == 0 && BYTES <= 40960, "LDS carve: four items per compute unit");
@@ -805,7 +804,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     float *ob = reinterpret_cast<float *>(lb);
     uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
     uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + DK * 8;
-    u32x4 *dg = reinterpret_cast<u32x4 *>(lb + OFF_DG);
+    float *crow = reinterpret_cast<float *>(lb + OFF_CL);
     float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
 
     const Index x{lens, idx, nacc};
@@ -886,16 +885,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
             xt_lo[(8 + t) * XS + row] = lq;
             if (t + 1 == n) cnv = c;
         }
-        {
-            // This row's entry of diag(c_{n-1}) as the A operand of a 16x16x16 MFMA (4 k
-            // slots per lane group): high part, then remainder, each in k slot row % 4 of
-            // the lane group that holds the row.
-            uint16_t ch, cl;
-            split_bf16(cnv, ch, cl);
-            const int j = row & 3, sh = 16 * (j & 1);
-            const uint32_t hw = (uint32_t)ch << sh, lw = (uint32_t)cl << sh;
-            dg[row] = (j >> 1) ? u32x4{0u, hw, 0u, lw} : u32x4{hw, 0u, lw, 0u};
-        }
+        crow[row] = cnv;  // this row's entry of diag(c_{n-1})
         float ka[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -938,10 +928,6 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     // Y = [c k | c scale q]^T S0 (16 x 64, this wave's columns): column set c, accumulated
     // over row-block pairs; the k slots of lane group kg are rows 4 kg .. 4 kg + 3 of block
     // 2p, then of block 2p+1.
-    auto pair8 = [](const uint16_t *p0, const uint16_t *p1) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p0), y = *reinterpret_cast<const uint2 *>(p1);
-        return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
-    };
     auto frag8 = [](const s16x4 f0, const s16x4 f1) {
         const uint2 x = __builtin_bit_cast(uint2, f0), y = __builtin_bit_cast(uint2, f1);
         return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
@@ -952,8 +938,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) {
         const int r0 = 32 * pb + 4 * kg;
-        const bf16x8 ah = pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
-        const bf16x8 al = pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
+        const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
+        const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const bf16x8 bf = frag8(column_frag(raw[2 * pb], c), column_frag(raw[2 * pb + 1], c));
@@ -1031,40 +1017,33 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
                                                 lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
         return;
     }
-    // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block, four 16x16x16 MFMAs per 16 x 16
-    // block, all accumulating into one register set:
-    //  * diag(c) S0: c's high part, then its remainder, against the block's rows as the lane
-    //    group holds them (k slots 4 kg .. 4 kg + 3); the diagonal operand is the row's, in
-    //    the lanes of the group that holds the row, else zero;
-    //  * [g k]^T U: lane group kg carries tokens 4 (kg & 1) .. 4 (kg & 1) + 3 of A's high part
-    //    (kg < 2) or its remainder (kg >= 2), against U's high part, then U's remainder, so
-    //    the four products of the split parts are all taken.
-    // One instruction shape per accumulation chain: on this part a matrix-core instruction
-    // that takes its accumulator from one of another shape can read it before it is
-    // written (the compiler does not separate them), which loses the earlier terms.
-    s16x4 buh[4], bul[4];
+    // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block. The row scaling of the bf16 tile is
+    // an fp32 multiply on the VALU and gives each accumulator its initial value; the rank-n
+    // update is then one 16x16x32 product per block: lane group kg carries A's tokens 0..7 of
+    // its high part (kg even) or remainder (kg odd), against U's high part (kg < 2) or
+    // remainder (kg >= 2), so the four products of the split parts are all taken at once.
+    // Each accumulator sees one matrix-core instruction shape only.
+    bf16x8 bu[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        buh[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_hi + (c * 16 + n16) * 8 + 4 * (kg & 1)));
-        bul[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_lo + (c * 16 + n16) * 8 + 4 * (kg & 1)));
-    }
-    const uint16_t *ka_lane = (kg >> 1 ? ka_lo : ka_hi) + n16 * 8 + 4 * (kg & 1);
-    const bool on_diag = (n16 >> 2) == kg;
+    for (int c = 0; c < 4; ++c)
+        bu[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                               (kg >= 2 ? ut_lo : ut_hi) + (c * 16 + n16) * 8));
+    const uint16_t *ka_lane = ((kg & 1) ? ka_lo : ka_hi) + n16 * 8;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-        const s16x4 ak = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ka_lane + 16 * rb * 8));
-        const u32x4 dv = dg[16 * rb + n16];
-        const s16x4 dh = __builtin_bit_cast(s16x4, make_uint2(on_diag ? dv.x : 0u, on_diag ? dv.y : 0u));
-        const s16x4 dl = __builtin_bit_cast(s16x4, make_uint2(on_diag ? dv.z : 0u, on_diag ? dv.w : 0u));
+        const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(ka_lane + 16 * rb * 8));
         f32x4 D[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const s16x4 sf = column_frag(raw[rb], c);
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dh, sf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dl, sf, D[c], 0, 0, 0);
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, buh[c], D[c], 0, 0, 0);
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bul[c], D[c], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            D[0][i] = cr[i] * bf16_lo(raw[rb][i].x);
+            D[1][i] = cr[i] * bf16_hi(raw[rb][i].x);
+            D[2][i] = cr[i] * bf16_lo(raw[rb][i].y);
+            D[3][i] = cr[i] * bf16_hi(raw[rb][i].y);
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bu[c], D[c], 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             store8<RGDR_STATE_STORE_POLICY>(

@@ -363,6 +363,63 @@ __device__ __forceinline__ float wave_sum64_transposed(const float (&v)[64], int
     return a1[0];
 }
 
+// Eight bf16 values of two 4-element LDS runs (k slots 0..3, then 4..7).
+__device__ __forceinline__ bf16x8 lds_pair8(const uint16_t *p0, const uint16_t *p1) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p0), v = *reinterpret_cast<const uint2 *>(p1);
+    return __builtin_bit_cast(bf16x8, u32x4{u.x, u.y, v.x, v.y});
+}
+
+// Decay range inside which a run's 8 x 8 matrices M and N (the chunk form's closed form) are
+// formed on the matrix cores from the factors c_t k_t (or c_t scale q_t) and k_s / c_s: every
+// c_t of the run within [2^-48, 2^48] keeps both factors and their products far from fp32
+// overflow. A wave with a row outside it forms its rows' share of the matrices directly,
+// from products of the decays between s and t.
+constexpr float kGramLo = 0x1p-48f, kGramHi = 0x1p48f;
+
+// M[t][s] (s < t) and N[t][s] (s <= t) into this wave's tables gsM[t * 8 + s], gsN[t * 8 + s]:
+// the factored products on the matrix cores, XT rows 0..7 (c_t k_t) and 8..15 (c_t scale
+// q_t) against KC rows s = 0..7 (k_s / c_s), high parts and remainders (three products),
+// plus the rows' direct shares in gpart[2][64] (entry e = 8 s + t of M, 8 t + s of N; zero
+// where a wave's rows took the factored form). XT and KC are [rows][XS] bf16, one row per
+// token, D_k columns; lane (kg, n16) ends with G[4 kg + i][n16]. Entries outside s < t
+// (M) and s <= t (N) are written but never read.
+template <int DK, int XS>
+__device__ __forceinline__ void gram_tables(const uint16_t *xt_hi, const uint16_t *xt_lo,
+                                            const uint16_t *kc_hi, const uint16_t *kc_lo,
+                                            const float *gpart, float *gsM, float *gsN, int n16,
+                                            int kg) {
+    f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool tok = n16 < 8;  // KC has rows for tokens 0..7 only; the other columns are zero
+    const int s8 = n16 & 7;
+#pragma unroll
+    for (int pb = 0; pb < DK / 32; ++pb) {
+        const int r0 = 32 * pb + 4 * kg;
+        const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
+        const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
+        bf16x8 bh = lds_pair8(kc_hi + s8 * XS + r0, kc_hi + s8 * XS + r0 + 16);
+        bf16x8 bl = lds_pair8(kc_lo + s8 * XS + r0, kc_lo + s8 * XS + r0 + 16);
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+        bh = tok ? bh : __builtin_bit_cast(bf16x8, zero);
+        bl = tok ? bl : __builtin_bit_cast(bf16x8, zero);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, g, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, g, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, g, 0, 0, 0);
+    }
+    if (tok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int mrow = 4 * kg + i;
+            if (mrow < 8) {
+                const int e = n16 * 8 + mrow;  // M[mrow][n16]
+                gsM[mrow * 8 + n16] = g[i] + gpart[e] + gpart[64 + e];
+            } else {
+                const int t = mrow - 8, e = t * 8 + n16;  // N[t][n16]
+                gsN[t * 8 + n16] = g[i] + gpart[e] + gpart[64 + e];
+            }
+        }
+    }
+}
+
 // Operand staging of the chunk form (128 threads, D_k = 64 or 128, 128-column tiles).
 // Planar per token: the row decays d [8][D_k], k [8][D_k] and scale q [8][D_k], then the
 // tile's v [8][128] and beta [8]. Each thread writes whole 16-byte runs of consecutive rows, so the

@@ -49,19 +49,6 @@ __device__ __forceinline__ void split8(const f32x4 &x0, const f32x4 &x1, bf16x8 
     lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
-// Eight bf16 values of two 4-element LDS runs (k slots 0..3, then 4..7).
-__device__ __forceinline__ bf16x8 lds_pair8(const uint16_t *p0, const uint16_t *p1) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p0), v = *reinterpret_cast<const uint2 *>(p1);
-    return __builtin_bit_cast(bf16x8, u32x4{u.x, u.y, v.x, v.y});
-}
-
-// Decay range inside which a run's Gram matrices are formed on the matrix cores from the
-// factors c_t k_t (or c_t scale q_t) and k_s / c_s: every c_t of the run within
-// [2^-48, 2^48] keeps both factors and their products far from fp32 overflow. A wave with
-// a row outside it forms that row's share of the matrices directly, from products of the
-// decays between s and t (each in [0, 1] for decays), as the decode does.
-constexpr float kGramLo = 0x1p-48f, kGramHi = 0x1p48f;
-
 // Lane layout. Four waves per item; wave w owns tile columns 32 w .. 32 w + 31 over all D_k
 // rows. Lane l = (kg, n16) = (l / 16, l % 16) holds state rows 16 rb + 4 kg + i (rb < D_k / 16,
 // i < 4) of columns 32 w + 2 n16 + c (c < 2) as S[rb][c][i]: the accumulator layout of the
@@ -77,7 +64,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     constexpr int TV = 128, NT = 256, NW = 4;
     constexpr int NRB = DK / 16, NPB = DK / 32;
     // LDS: staged operands of one run (chunk_stage_ops) | XT hi, lo [16][XS] (c k | c scale
-    // q) | KC hi, lo [16][XS] (k_s / c_s; rows 8..15 stay zero) | KA hi, lo [D_k][8] | UT
+    // q) | KC hi, lo [8][XS] (k_s / c_s) | KA hi, lo [D_k][8] | UT
     // [wave][hi, lo][2 column sets][16][8] | c of each row at the run's end [D_k] | direct
     // Gram partials [2][64] | M and N [wave][8][8]. Y^T [128][kChunkYS] takes the d, k and q
     // planes once the rows are prepared.
@@ -85,7 +72,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     constexpr int VB = chunk_vbase<DK>();
     constexpr int OFF_XT = chunk_ops<DK>() * 4;
     constexpr int OFF_KC = OFF_XT + 2 * 16 * XS * 2;
-    constexpr int OFF_KA = OFF_KC + 2 * 16 * XS * 2;
+    constexpr int OFF_KA = OFF_KC + 2 * 8 * XS * 2;
     constexpr int OFF_UT = OFF_KA + 2 * DK * 8 * 2;
     constexpr int OFF_CL = OFF_UT + NW * 2 * 2 * 16 * 8 * 2;
     constexpr int OFF_GP = OFF_CL + DK * 4;
@@ -97,7 +84,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     char *lb = reinterpret_cast<char *>(lds4);
     float *ob = reinterpret_cast<float *>(lb);
     uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
-    uint16_t *kc_hi = reinterpret_cast<uint16_t *>(lb + OFF_KC), *kc_lo = kc_hi + 16 * XS;
+    uint16_t *kc_hi = reinterpret_cast<uint16_t *>(lb + OFF_KC), *kc_lo = kc_hi + 8 * XS;
     uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + DK * 8;
     float *crow = reinterpret_cast<float *>(lb + OFF_CL);
     float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
@@ -143,11 +130,6 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         for (int i = 0; i < 4; ++i)
             raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b32(
                 rs, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_LOAD_POLICY);
-    // KC rows 8..15 are the unused columns of the Gram products: zero, once.
-    for (int e = tid; e < 2 * 8 * XS; e += NT) {
-        const int half = e / (8 * XS), r = e % (8 * XS);
-        (half ? kc_lo : kc_hi)[8 * XS + r] = 0;
-    }
     f32x4 S[NRB][2];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
@@ -253,36 +235,8 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         lds_barrier();
 
         // M and N: the factored products on the matrix cores (each wave for itself), plus
-        // the direct shares. Lane (kg, n16) holds G[4 kg + i][n16]: row m < 8 is
-        // c_m k_m . (k_s / c_s) = M[m][s] (s < m), row m >= 8 is N[m - 8][s] (s <= m - 8).
-        {
-            f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int pb = 0; pb < NPB; ++pb) {
-                const int r0 = 32 * pb + 4 * kg;
-                const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
-                const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
-                const bf16x8 bh = lds_pair8(kc_hi + n16 * XS + r0, kc_hi + n16 * XS + r0 + 16);
-                const bf16x8 bl = lds_pair8(kc_lo + n16 * XS + r0, kc_lo + n16 * XS + r0 + 16);
-                g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, g, 0, 0, 0);
-                g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, g, 0, 0, 0);
-                g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, g, 0, 0, 0);
-            }
-            if (n16 < 8) {
-                const int s = n16;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int mrow = 4 * kg + i;
-                    if (mrow < 8) {
-                        const int e = s * 8 + mrow;  // M[mrow][s], s < mrow
-                        gsM[mrow * 8 + s] = g[i] + gpart[e] + gpart[64 + e];
-                    } else {
-                        const int t = mrow - 8, e = t * 8 + s;  // N[t][s], s <= t
-                        gsN[t * 8 + s] = g[i] + gpart[e] + gpart[64 + e];
-                    }
-                }
-            }
-        }
+        // the direct shares.
+        gram_tables<DK, XS>(xt_hi, xt_lo, kc_hi, kc_lo, gpart, gsM, gsN, n16, kg);
         lds_phase();
 
         // Y = [c k | c scale q]^T S (16 x 32, this wave's columns), column set c, over
