@@ -41,6 +41,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -259,7 +260,7 @@ def cpu_baseline(inp, seconds):
 class Workload:
     """Device buffers of one workload, rotated over R sets, and its calls."""
 
-    def __init__(self, wid, dev, rotate=0, steps=200):
+    def __init__(self, wid, dev, rotate=0, steps=200, batch=None):
         import numpy as np
         import torch
 
@@ -268,8 +269,10 @@ class Workload:
         self.rg, self.torch = rg, torch
         self.wid = wid
         self.name = workloads.WORKLOAD_NAMES[wid]
+        if batch is not None:
+            self.name = re.sub(r"B=\d+", f"B={batch}", self.name)
         self.prefill = wid in PREFILL_WORKLOADS
-        inp = self.inp = workloads.make_workload(wid, gate_inputs=True)
+        inp = self.inp = workloads.make_workload(wid, gate_inputs=True, batch=batch)
         B, Hv, T, Dk, Dv, N = inp.B, inp.Hv, inp.T, inp.Dk, inp.Dv, inp.N_slots
         self.dbytes, self.tok_heads = decode_bytes(inp)
         self.gbytes = gate_bytes(inp)
@@ -449,6 +452,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5])
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >= 1 GiB)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="replace the workload's batch size B (same recipe otherwise)")
     ap.add_argument("--extra", default="1,3,4,5",
                     help="other workloads whose fused-call duration the line also carries "
                          "(comma-separated ids; empty for none)")
@@ -476,7 +481,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wid = args.workload
-    wl = Workload(wid, dev, args.rotate, args.steps)
+    wl = Workload(wid, dev, args.rotate, args.steps, args.batch)
     inp = wl.inp
     B, Hq, Hv, T, Dk, Dv, N = inp.B, inp.Hq, inp.Hv, inp.T, inp.Dk, inp.Dv, inp.N_slots
     log(f"workload {wid}: {wl.name}; fused step bytes {wl.step_bytes}, unfused "

@@ -1,0 +1,60 @@
+"""Seeded random shapes through every entry of the recurrence, against the fp64 oracle.
+
+Each case draws its sizes, lengths, accepted counts and slot indices from one seed, so a
+failure names a reproducible case. Decode calls (T <= 8) cover every kernel form; the
+long-sequence entry covers runs split at the accepted prefix. Values within
+2e-2 + 2e-2 |ref| of the unrounded oracle; padding and untouched slots bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import check_decode, gpu_decode, gpu_prefill, oracle_decode, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import gated_delta_rule_rgdr_amd as m
+    m.library()
+    return m
+
+
+def draw(seed, t_max):
+    rng = np.random.default_rng(seed)
+    Hq = int(rng.choice([1, 2, 4]))
+    Hv = Hq * int(rng.choice([1, 2, 4]))
+    Dk = int(rng.choice([64, 128]))
+    Dv = 64 * int(rng.integers(1, 9))
+    T = int(rng.integers(1, t_max + 1))
+    B = int(rng.integers(1, 7))
+    N = B + int(rng.integers(0, 4))
+    lens = rng.integers(0, T + 1, B).astype(np.int32)
+    inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed=seed + 1, indices="choice",
+                              lengths=lens)
+    nacc = np.array([rng.integers(0, L + 1) for L in lens], np.int32)
+    inp.num_accepted_tokens = nacc
+    if B > 1 and rng.random() < 0.3:
+        inp.ssm_state_indices[int(rng.integers(0, B))] = -1  # a skipped entry
+    return inp
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_decode(rg, seed):
+    inp = draw(900 + seed, 8)
+    say(f"decode case {seed}: B={inp.B} Hq={inp.Hq} Hv={inp.Hv} T={inp.T} Dk={inp.Dk} "
+        f"Dv={inp.Dv} L={inp.actual_seq_lengths.tolist()} n={inp.num_accepted_tokens.tolist()}")
+    out, st = gpu_decode(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"random decode {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill(rg, seed):
+    inp = draw(1900 + seed, 48)
+    say(f"prefill case {seed}: B={inp.B} Hq={inp.Hq} Hv={inp.Hv} T={inp.T} Dk={inp.Dk} "
+        f"Dv={inp.Dv} L={inp.actual_seq_lengths.tolist()} n={inp.num_accepted_tokens.tolist()}")
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"random prefill {seed}")

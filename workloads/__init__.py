@@ -154,9 +154,14 @@ def make_case(B, Hq, Hv, T, Dk, Dv, N_slots, seed, *, zero_state=False, gk_hi=0.
     return inp
 
 
-def make_workload(wid: int, gate_inputs: bool = False) -> Inputs:
-    """The six workloads, seeded with 1000 + id (see the module docstring)."""
-    w = WORKLOADS[wid]
+def make_workload(wid: int, gate_inputs: bool = False, batch: Optional[int] = None) -> Inputs:
+    """The six workloads, seeded with 1000 + id (see the module docstring). ``batch``
+    replaces the batch size B (the recipe is otherwise unchanged; the pool keeps its slots,
+    at least B)."""
+    w = dict(WORKLOADS[wid])
+    if batch is not None:
+        w["B"] = int(batch)
+        w["N_slots"] = max(w["N_slots"], w["B"])
     seed = 1000 + wid
     if wid == 0:
         inp = make_case(**w, seed=seed, zero_state=True, indices="identity")
