@@ -89,20 +89,24 @@ def fused_bytes(inp, decode_b, tok_heads):
 
 def prefill_mfma_flops(inp):
     """Matrix-core flops the long-sequence kernel executes per call (not the method's
-    algorithmic flops): per run of up to 8 tokens and per 128-column item, each of its two
-    waves issues 3 x (D_k / 32) x 4 products of 16x16x32 (Y = X^T S on split operands) and
-    2 x (D_k / 16) x 4 of 16x16x16 (the update)."""
+    algorithmic flops). Per chunk of up to 32 tokens and per 128-column item: each of its four
+    waves issues 24 x (D_k / 32) products of 16x16x32 for [c k | c scale q]^T S, 6 x (D_k / 16)
+    for the rank-32 update and 36 of 16x16x16 for the blockwise solve and the outputs; the
+    item's M and N blocks take 18 x (D_k / 32) of 16x16x32. Chunks split at the accepted
+    prefix's end; chunks shortened by the decay range (rare at these decays) are not counted."""
     import numpy as np
     lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
     nacc = np.clip(inp.num_accepted_tokens, 0, lens)
     valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
-    runs = 0
+    chunks = 0
     for L, n, ok in zip(lens, nacc, valid):
         if ok and L > 0:
-            runs += -(-int(L) // 8) + (1 if 0 < n < L and n % 8 else 0)
+            chunks += -(-int(L) // 32) + (1 if 0 < n < L and n % 32 else 0)
     items = inp.Hv * -(-inp.Dv // 128)
-    per_wave = 3 * (inp.Dk // 32) * 4 * 16 * 16 * 32 * 2 + 2 * (inp.Dk // 16) * 4 * 16 * 16 * 16 * 2
-    return runs * items * 2 * per_wave
+    npb, nrb = inp.Dk // 32, inp.Dk // 16
+    big = 4 * (24 * npb + 6 * nrb) + 18 * npb   # 16x16x32 products per item and chunk
+    small = 4 * 36                              # 16x16x16 products
+    return chunks * items * (big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2)
 
 
 SOURCES_COMMON = ("gated_delta_rule_rgdr_amd/csrc/rgdr_device.h",

@@ -6,123 +6,270 @@
 // is that operator for this library: the same inputs, outputs and semantics as rgdr_decode
 // (slot pool, lengths, accepted counts, head sharing, padding), for any T up to 65536.
 //
-// Design. One workgroup of two waves owns one (entry, value head, 128-column tile) for the
+// Design. One workgroup of four waves owns one (entry, value head, 128-column tile) for the
 // whole sequence. Its state tile is read from HBM once, kept in fp32 in the matrix cores'
-// accumulator layout while the item's tokens are walked in runs of at most 8, and written
-// back once (at the accepted prefix's end). Each run is the exact closed form of the decode
-// kernel's chunk form (decay products c_t, the 8 x 8 matrices M and N, a triangular solve
-// for u, then the committed state diag(c) S + (g k)^T U), with S the running fp32 state:
-//   * Y = [c k | c scale q]^T S on the matrix cores, S split into a bf16 high part and a
-//     bf16 remainder (exact in fp32) against the operands' high parts and remainders, so
-//     the products keep about 16 bits of every operand;
-//   * the row scaling diag(c) S on the VALU, in fp32, on the accumulator registers;
-//   * the rank-8 update (g k)^T U as matrix-core products accumulating into S.
-// The run that holds the accepted prefix's end stops there, so the committed state is a
-// run's end state; the later tokens still produce their outputs. The next run's operands
-// are loaded while the current run is computed. HBM sees the state once in and once out,
+// accumulator layout while the item's tokens are walked in chunks of up to 32, and written
+// back once (at the accepted prefix's end). Each chunk applies the exact closed form of the
+// four steps over its tokens (the unrolled recurrence the decode kernel's chunk form also
+// uses), with the state S0 at the chunk's start:
+//   d_t = exp(g_t) exp(gk_t) (per row), c_t = d_1 ... d_t (c_0 = 1), S' = diag(d_0) S0,
+//   Y_K = [c k]^T S',  Y_Q = [c scale q]^T S',
+//   M[t][s] = sum_i (c_t / c_s)_i k_t,i k_s,i (s < t),  N[t][s] = the same with scale q_t (s <= t),
+//   (I + diag(beta) M) U = diag(beta) (V - Y_K),   O = Y_Q + N U,
+//   S_end = diag(c_last) S' + sum_s diag(c_last / c_s) k_s u_s^T.
+// The two products with S' and the rank-32 update are matrix-core products on the state's
+// own accumulator registers; M and N are matrix-core products of the factors c_t k_t (or
+// c_t scale q_t) and k_s / c_s; the 32 x 32 triangular system is solved blockwise: the two
+// 16 x 16 diagonal blocks are inverted by forward substitution in fp32 on one wave, and
+//   U_0 = A_00 R_0,   U_1 = A_11 (R_1 - M_10 U_0),   A_bb = (I + diag(beta) M_bb)^-1 diag(beta)
+// are matrix-core products. Every fp32 operand of a matrix-core product is split into a bf16
+// high part and a bf16 remainder and three products are summed (high x high, low x high,
+// high x low), so each keeps about 16 bits of both operands; accumulation is fp32.
+//
+// The factored form needs every c_t of the chunk within [2^-96, 2^96] (each factor and their
+// products stay far from fp32 overflow and underflow). A chunk in which some row leaves that
+// range is shortened to end before the first such token (c_0 = 1, so at least one token
+// remains); strong decays therefore give shorter chunks, not a different arithmetic.
+//
+// A chunk that holds the accepted prefix's end stops there, so the committed state is a
+// chunk's end state; the later tokens still produce their outputs. The next chunk's operands
+// are loaded while the current one is computed. HBM sees the state once in and once out,
 // and every operand once.
 #include <climits>
+#include <type_traits>
 
 #include "rgdr_device.h"
 
 namespace rgdr {
 
 constexpr int kPrefillMaxT = 65536;  // tokens per call: keeps every per-item offset in 32 bits
+constexpr int kChunk = 32;           // tokens per chunk
+// Range of the decay products c_t inside which a chunk takes the factored form.
+constexpr float kChunkLo = 0x1p-96f, kChunkHi = 0x1p96f;
 
 // Waves per SIMD the kernel is compiled for (the register budget).
 #ifndef RGDR_PREFILL_MIN_WAVES
 #define RGDR_PREFILL_MIN_WAVES 2
 #endif
 
-// f32x4 pair -> bf16 high parts and bf16 remainders, 8 values in k order (x0 first).
-__device__ __forceinline__ void split8(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi,
-                                       bf16x8 &lo) {
-    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    uint32_t h[4], l[4];
+// Thread mapping and LDS carve of one item (256 threads).
+//   Preparation: thread (r, tg) = (tid / NTG, tid % NTG) owns rows 4 r .. 4 r + 3 of tokens
+//   TPT tg .. TPT tg + TPT - 1; the NTG token groups of a row group are consecutive lanes.
+//   XK, XQ, KD: [hi, lo][32 tokens][XS] bf16: c_t k_t, c_t scale q_t, k_t / c_t by row.
+//   KH: [hi, lo][D_k rows][KS] bf16: (c_last / c_s) k_s, one row per state row.
+//   TD: [2][16][BS] fp32: beta_t M[t][s] of the two diagonal 16 x 16 blocks.
+//   BK: [6 blocks][hi, lo][16][AS] bf16: A_00, A_11, -M_10, N_00, N_10, N_11.
+//   c_last and d_0 per row, beta per token, and the chunk cut.
+template <int DK>
+struct ChunkShape {
+    static constexpr int NRB = DK / 16, NPB = DK / 32;
+    static constexpr int TPT = DK / 32;       // tokens per preparing thread
+    static constexpr int NTG = kChunk / TPT;  // token groups: lanes per row group
+    static_assert((DK / 4) * NTG == 256, "four rows by TPT tokens per thread");
+    static_assert(NTG == 8 || NTG == 16, "token groups inside one 16-lane DPP row");
+    static constexpr int XS = DK + 4, KS = kChunk + 4, AS = 16 + 4, BS = 16 + 4;
+    // The small, often-addressed areas come first, so that every access below 64 KiB takes
+    // its constant part in the LDS instruction's 16-bit offset; KD, read only by the M and N
+    // products, comes last.
+    static constexpr int XBYTES = 2 * kChunk * XS * 2;
+    static constexpr int OFF_CUT = 0;
+    static constexpr int OFF_BT = 16;
+    static constexpr int OFF_D0 = OFF_BT + kChunk * 4;
+    static constexpr int OFF_CL = OFF_D0 + DK * 4;
+    static constexpr int OFF_TD = OFF_CL + DK * 4;
+    static constexpr int OFF_BK = OFF_TD + 2 * 16 * BS * 4;
+    static constexpr int OFF_KH = OFF_BK + 6 * 2 * 16 * AS * 2;
+    static constexpr int OFF_XK = OFF_KH + 2 * DK * KS * 2;
+    static constexpr int OFF_XQ = OFF_XK + XBYTES;
+    static constexpr int OFF_KD = OFF_XQ + XBYTES;
+    static constexpr int BYTES = OFF_KD + XBYTES;
+    static_assert(BYTES % 16 == 0 && BYTES <= 81920, "LDS carve: two items per compute unit");
+    // The q/k norm partials [4 waves][2][32] (preparation only) share the TD area.
+    static_assert(4 * 2 * kChunk * 4 <= 2 * 16 * BS * 4, "norm partials fit TD");
+};
+
+// One chunk's operands in flight: this thread's rows of k, q and gk for its tokens, and the
+// gate values of token lane % 32.
+template <int DK>
+struct ChunkOps {
+    static constexpr int TPT = ChunkShape<DK>::TPT;
+    u32x2 k[TPT], q[TPT];
+    f32x4 gk[TPT];
+    uint32_t ga, gb;  // g (fp32) and beta (bf16), or the raw gate projections a and b
+};
+
+// Issue the loads of tokens t0 .. t0 + len - 1 (ranges stop at len: later tokens read zeros).
+template <int DK, int GATE>
+__device__ __forceinline__ void load_chunk(const DecodeArgs &a, const Item &m, ChunkOps<DK> &o,
+                                           int r, int tg, int lane, int t0, int len) {
+    constexpr int TPT = ChunkShape<DK>::TPT;
+    const size_t bhT = ((size_t)m.b * a.Hv + m.h) * a.T + t0;
+    const size_t qk0 = (((size_t)m.b * a.Hq + m.hq) * a.T + t0) * DK;
+    const uint32_t n = (uint32_t)len;
+    const auto rk = make_rsrc(a.k + qk0, n * DK * 2);
+    const auto rq = make_rsrc(a.q + qk0, n * DK * 2);
+    const auto rgk = make_rsrc(a.gk + bhT * DK, n * DK * 4);
+    const uint32_t e = (uint32_t)(TPT * tg * DK + 4 * r);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        h[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-        // x - hi is exact in fp32
-        l[j] = pack_bf16x2(v[2 * j] - bf16_lo(h[j]), v[2 * j + 1] - bf16_hi(h[j]));
+    for (int j = 0; j < TPT; ++j) {
+        o.k[j] = __builtin_amdgcn_raw_buffer_load_b64(rk, e * 2, j * DK * 2, 0);
+        o.q[j] = __builtin_amdgcn_raw_buffer_load_b64(rq, e * 2, j * DK * 2, 0);
+        o.gk[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rgk, e * 4, j * DK * 4, 0));
     }
-    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
-    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+    const int t = lane & 31;
+    if constexpr (GATE == kGateGiven) {
+        o.ga = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.g + bhT, n * 4), t * 4, 0, 0);
+        o.gb = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.beta + bhT, n * 2), t * 2, 0, 0);
+    } else {
+        o.ga = gate_raw(a, a.ga, GATE, m.b, t0 + t, m.h, t < len);
+        o.gb = gate_raw(a, a.gb, GATE, m.b, t0 + t, m.h, t < len);
+    }
 }
 
-// Lane layout. Four waves per item; wave w owns tile columns 32 w .. 32 w + 31 over all D_k
-// rows. Lane l = (kg, n16) = (l / 16, l % 16) holds state rows 16 rb + 4 kg + i (rb < D_k / 16,
-// i < 4) of columns 32 w + 2 n16 + c (c < 2) as S[rb][c][i]: the accumulator layout of the
-// 16 x 16 block of rows 16 rb .. + 15 and columns 32 w + 2 n + c (column set c). Rows
-// 4 kg .. 4 kg + 3 of two row blocks are also the 8 k slots of lane group kg in a 16x16x32
-// product, so the state turns into the B operand of Y = X^T S in the lane that holds it.
-// At 64 state values per lane two waves fit a SIMD.
+// f32x4 -> bf16 high parts and bf16 remainders (x - hi is exact in fp32), packed in order.
+__device__ __forceinline__ void split4(const f32x4 &x, uint2 &hi, uint2 &lo) {
+    hi.x = pack_bf16x2(x.x, x.y);
+    hi.y = pack_bf16x2(x.z, x.w);
+    lo.x = pack_bf16x2(x.x - bf16_lo(hi.x), x.y - bf16_hi(hi.x));
+    lo.y = pack_bf16x2(x.z - bf16_lo(hi.y), x.w - bf16_hi(hi.y));
+}
+// f32x4 pair -> the same, 8 values in k order (x0 first).
+__device__ __forceinline__ void split8(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
+    uint2 h0, l0, h1, l1;
+    split4(x0, h0, l0);
+    split4(x1, h1, l1);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h0.x, h0.y, h1.x, h1.y});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l0.x, l0.y, l1.x, l1.y});
+}
+__device__ __forceinline__ s16x4 as_s16x4(uint2 v) { return __builtin_bit_cast(s16x4, v); }
+__device__ __forceinline__ bf16x8 cat8(uint2 a, uint2 b) {
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
+// 16 x 16 block G[t][s] = sum_i A[16 tb + t][i] B[16 sb + s][i] over the D_k rows of two
+// [hi, lo][32][XS] operand planes, three products of the split parts. Lane (kg, n16) ends with
+// G[4 kg + i][n16]. The k slots of lane group kg are columns 4 kg .. + 3 and 16 + 4 kg .. + 3
+// of each 32-column group (the same order on both sides).
+template <int DK, int XS>
+__device__ __forceinline__ f32x4 gram_block(const uint16_t *a_hi, const uint16_t *b_hi, int tb,
+                                            int sb, int n16, int kg) {
+    const uint16_t *a_lo = a_hi + kChunk * XS, *b_lo = b_hi + kChunk * XS;
+    f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pb = 0; pb < DK / 32; ++pb) {
+        const int ra = (16 * tb + n16) * XS + 32 * pb + 4 * kg;
+        const int rb = (16 * sb + n16) * XS + 32 * pb + 4 * kg;
+        const bf16x8 ah = lds_pair8(a_hi + ra, a_hi + ra + 16), al = lds_pair8(a_lo + ra, a_lo + ra + 16);
+        const bf16x8 bh = lds_pair8(b_hi + rb, b_hi + rb + 16), bl = lds_pair8(b_lo + rb, b_lo + rb + 16);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, g, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, g, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, g, 0, 0, 0);
+    }
+    return g;
+}
+
+// A 16 x 16 accumulator block (lane (kg, n16): rows 4 kg + i, column n16) into an operand
+// block [hi, lo][16][AS], entries with column > row zeroed when LOWER.
+template <int AS, bool LOWER>
+__device__ __forceinline__ void put_block(uint16_t *blk, const f32x4 &g, float sign, int n16, int kg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * kg + i;
+        const float v = (!LOWER || n16 <= row) ? sign * g[i] : 0.f;
+        uint16_t h, l;
+        split_bf16(v, h, l);
+        blk[row * AS + n16] = h;
+        blk[16 * AS + row * AS + n16] = l;
+    }
+}
+
+// One 16x16x16 product chain of split operands: acc + A x B (high x high, low x high, high x low).
+__device__ __forceinline__ f32x4 mma16(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+}
+
+// Lane layout of the state. Wave w owns tile columns 32 w .. 32 w + 31 over all D_k rows.
+// Lane l = (kg, n16) = (l / 16, l % 16) holds rows 16 rb + 4 kg + i (rb < D_k / 16, i < 4) of
+// columns 32 w + 2 n16 + c (c < 2) as S[rb][c][i]: the accumulator layout of the 16 x 16 block
+// of rows 16 rb .. + 15 and columns 32 w + 2 n + c (column set c). Rows 4 kg .. 4 kg + 3 of two
+// row blocks are also the 8 k slots of lane group kg in a 16x16x32 product, so the state turns
+// into the B operand of Y = X S in the lane that holds it. The chunk's per-token results (Y_K,
+// Y_Q, U, O) use the same layout with tokens for rows: 16 tb + 4 kg + i is the token, and the
+// rows 4 kg .. + 3 of a 16-token block are the k slots of a 16x16x16 product over tokens.
 template <int DK, int GATE>
 __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
     static_assert(DK == 64 || DK == 128, "D_k = 64 or 128");
-    constexpr int TV = 128, NT = 256, NW = 4;
-    constexpr int NRB = DK / 16, NPB = DK / 32;
-    // LDS: staged operands of one run (chunk_stage_ops) | XT hi, lo [16][XS] (c k | c scale
-    // q) | KC hi, lo [8][XS] (k_s / c_s) | KA hi, lo [D_k][8] | UT
-    // [wave][hi, lo][2 column sets][16][8] | c of each row at the run's end [D_k] | direct
-    // Gram partials [2][64] | M and N [wave][8][8]. Y^T [128][kChunkYS] takes the d, k and q
-    // planes once the rows are prepared.
-    constexpr int XS = DK + 4;
-    constexpr int VB = chunk_vbase<DK>();
-    constexpr int OFF_XT = chunk_ops<DK>() * 4;
-    constexpr int OFF_KC = OFF_XT + 2 * 16 * XS * 2;
-    constexpr int OFF_KA = OFF_KC + 2 * 8 * XS * 2;
-    constexpr int OFF_UT = OFF_KA + 2 * DK * 8 * 2;
-    constexpr int OFF_CL = OFF_UT + NW * 2 * 2 * 16 * 8 * 2;
-    constexpr int OFF_GP = OFF_CL + DK * 4;
-    constexpr int OFF_GS = OFF_GP + 2 * 64 * 4;
-    constexpr int BYTES = OFF_GS + NW * 2 * 64 * 4;
-    static_assert(BYTES % 16 == 0 && BYTES <= 81920, "LDS carve: two items per compute unit");
-    constexpr int YS = kChunkYS;
-    __shared__ f32x4 lds4[BYTES / 16];
+    using P = ChunkShape<DK>;
+    constexpr int TV = 128, NRB = P::NRB, NPB = P::NPB, TPT = P::TPT, NTG = P::NTG;
+    constexpr int XS = P::XS, KS = P::KS, AS = P::AS, BS = P::BS;
+    __shared__ f32x4 lds4[P::BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
-    float *ob = reinterpret_cast<float *>(lb);
-    uint16_t *xt_hi = reinterpret_cast<uint16_t *>(lb + OFF_XT), *xt_lo = xt_hi + 16 * XS;
-    uint16_t *kc_hi = reinterpret_cast<uint16_t *>(lb + OFF_KC), *kc_lo = kc_hi + 8 * XS;
-    uint16_t *ka_hi = reinterpret_cast<uint16_t *>(lb + OFF_KA), *ka_lo = ka_hi + DK * 8;
-    float *crow = reinterpret_cast<float *>(lb + OFF_CL);
-    float *gpart = reinterpret_cast<float *>(lb + OFF_GP);
+    uint16_t *xk_hi = reinterpret_cast<uint16_t *>(lb + P::OFF_XK), *xk_lo = xk_hi + kChunk * XS;
+    uint16_t *xq_hi = reinterpret_cast<uint16_t *>(lb + P::OFF_XQ), *xq_lo = xq_hi + kChunk * XS;
+    uint16_t *kd_hi = reinterpret_cast<uint16_t *>(lb + P::OFF_KD), *kd_lo = kd_hi + kChunk * XS;
+    uint16_t *kh_hi = reinterpret_cast<uint16_t *>(lb + P::OFF_KH), *kh_lo = kh_hi + DK * KS;
+    float *td = reinterpret_cast<float *>(lb + P::OFF_TD);
+    float *npart = td;
+    uint16_t *bk = reinterpret_cast<uint16_t *>(lb + P::OFF_BK);
+    float *crow = reinterpret_cast<float *>(lb + P::OFF_CL);
+    float *d0row = reinterpret_cast<float *>(lb + P::OFF_D0);
+    float *bt = reinterpret_cast<float *>(lb + P::OFF_BT);
+    int *cut = reinterpret_cast<int *>(lb + P::OFF_CUT);
+    auto blk = [&](int b) { return bk + b * 2 * 16 * AS; };  // block b: hi, then lo at + 16 AS
 
     const Index x{lens, idx, nacc};
     const int tid = threadIdx.x, lane = tid & 63, n16 = lane & 15, kg = lane >> 4;
     // w is the same in every lane of a wave; readfirstlane tells the compiler so, which keeps
     // the buffer descriptors built from it in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint16_t *ut_hi = reinterpret_cast<uint16_t *>(lb + OFF_UT) + w * 2 * 32 * 8, *ut_lo = ut_hi + 32 * 8;
-    float *gsM = reinterpret_cast<float *>(lb + OFF_GS) + w * 2 * 64, *gsN = gsM + 64;
+    const int r = tid / NTG, tg = tid % NTG;  // preparation: rows 4 r .. + 3, tokens TPT tg ..
     const Item m = resolve(a, x, xcd_item(blockIdx.x, gridDim.x));
     const int L = m.L, n = m.n;
-    auto ycol = [&](int j) { return ob + j * YS; };
 
     // A last tile of 64 columns (D_v an odd multiple of 64) leaves waves 2 and 3 without
-    // columns: their state and output accesses get empty ranges and they compute on zeros.
+    // columns: their state, value and output accesses get empty ranges and they compute on
+    // zeros.
     const bool cols = m.tile * TV + 32 * w < a.Dv;
     const uint32_t trange = cols ? tile_range<DK, TV>(a, m) : 0u;
-    const size_t tb = m.state ? tile_base<DK, TV>(a, m) : 0;
-    const auto rs = make_rsrc(a.pool + tb, trange);
-    const auto rso = make_rsrc(a.pool_out + tb, trange);
+    const size_t tb0 = m.state ? tile_base<DK, TV>(a, m) : 0;
+    const auto rs = make_rsrc(a.pool + tb0, trange);
+    const auto rso = make_rsrc(a.pool_out + tb0, trange);
     const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 32 * w + 2 * n16) * 2);
     const size_t bh = (size_t)m.b * a.Hv + m.h;
-    const int jcol = lane & 31;       // this lane's local column in the solve
-    const int col = 32 * w + jcol;    // lanes 32..63 repeat lanes 0..31 and store nothing
-    const uint32_t ocol = lane < 32 ? (uint32_t)((m.tile * TV + col) * 2) : 0x40000000u;
+    const uint32_t ocol = (uint32_t)((m.tile * TV + 32 * w + 2 * n16) * 2);
+    // Token (or state row) 4 kg + i of a 16-row block: the lane's part in the vector offset,
+    // the rest in the scalar one (4-byte accesses only; see store16 for the wide ones).
+    const uint32_t orow = ocol + (uint32_t)(4 * kg * a.Dv * 2);
+    float dt = 0.f, ds = 0.f;
+    if constexpr (GATE != kGateGiven) gate_head(a, m.h, dt, ds);
+    const bool norm = GATE != kGateGiven && a.norm_qk != 0;
 
-    // Runs of at most kMaxT tokens; the run holding the accepted prefix's end stops there.
-    auto run_end = [&](int t0) {
-        const int t1 = min(t0 + kMaxT, L);
-        return (t0 < n && n < t1) ? n : t1;
+    // Chunks of at most kChunk tokens; the chunk holding the accepted prefix's end stops there.
+    auto chunk_len = [&](int t0) {
+        const int t1 = min(t0 + kChunk, L);
+        return ((t0 < n && n < t1) ? n : t1) - t0;
+    };
+    // This lane's values of tokens 16 tb + 4 kg + i, columns 32 w + 2 n16 + (0, 1).
+    uint32_t vr[2][4];
+    auto load_v = [&](int t0, int len) {
+        const auto rv = make_rsrc(a.v + (bh * a.T + t0) * a.Dv, cols ? (uint32_t)(len * a.Dv * 2) : 0u);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vr[tb][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rv, orow, (uint32_t)((16 * tb + i) * a.Dv * 2), 0);
     };
 
-    // The first run's operands, then the state tile (bf16 -> fp32, exact).
-    int t0 = 0, t1 = run_end(0);
-    Ops<DK, TV, NT, kMaxT> o;
-    load_ops<DK, TV, NT, kMaxT, GATE>(a, m, o, tid, 0, t1);
+    // The first chunk's operands, then the state tile (bf16 -> fp32, exact).
+    int t0 = 0, len = chunk_len(0);
+    ChunkOps<DK> o;
+    load_chunk<DK, GATE>(a, m, o, r, tg, lane, 0, len);
+    load_v(0, len);
     uint32_t raw[NRB][4];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
@@ -144,212 +291,374 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 __builtin_amdgcn_raw_buffer_store_b32(
-                    raw[rb][i], rso, lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2), 0,
+                    raw[rb][i], rso, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2),
                     RGDR_STATE_STORE_POLICY);
     }
+    if (tid == 0) *cut = kChunk;
+    lds_barrier();
 
-    while (t0 < L) {  // uniform over the workgroup
-        const int Lc = t1 - t0;
-        chunk_stage_ops<DK, GATE, NT>(o, ob, a.scale, a.norm_qk != 0, Lc, tid);
-        // The next run's operands travel while this run is computed (zeros past the end).
-        const int t0n = t1, t1n = t1 < L ? run_end(t1) : t1;
-        __builtin_amdgcn_sched_barrier(0);
-        load_ops<DK, TV, NT, kMaxT, GATE>(a, m, o, tid, t0n, t1n - t0n);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-
-        // Per-row preparation: thread r owns row r (waves 0 and 1 at D_k = 128, wave 0 at
-        // D_k = 64).
-        const bool has_rows = 64 * w < DK;
-        bool direct = false;  // this wave forms its rows' Gram shares directly
-        float gp[64];  // direct partial G: [t][s] (s <= t) holds N[t][s], [s][t] (s < t) M[t][s]
-#pragma unroll
-        for (int e = 0; e < 64; ++e) gp[e] = 0.f;
-        if (has_rows) {
-            const int row = tid;
-            float d[8], k[8], q[8], c[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                d[t] = ob[t * DK + row];  // tokens past the run were staged neutral (d = 1)
-                k[t] = ob[8 * DK + t * DK + row];
-                q[t] = ob[16 * DK + t * DK + row];
-            }
-            float cc = 1.f, cend = 1.f, cmin = 1.f, cmax = 1.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                cc *= d[t];
-                c[t] = cc;
-                cmin = fminf(cmin, cc);
-                cmax = fmaxf(cmax, cc);
-                uint16_t hk, lk, hq, lq;
-                split_bf16(cc * k[t], hk, lk);
-                split_bf16(cc * q[t], hq, lq);
-                xt_hi[t * XS + row] = hk;
-                xt_lo[t * XS + row] = lk;
-                xt_hi[(8 + t) * XS + row] = hq;
-                xt_lo[(8 + t) * XS + row] = lq;
-                if (t + 1 == Lc) cend = cc;
-            }
-            crow[row] = cend;
-            direct = __ballot(!(cmin >= kGramLo && cmax <= kGramHi)) != 0;  // NaN: direct
-            float ka[8];
-            if (!direct) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float kcs = k[s] * __builtin_amdgcn_rcpf(c[s]);  // k_s / c_s
-                    uint16_t h, l;
-                    split_bf16(kcs, h, l);
-                    kc_hi[s * XS + row] = h;
-                    kc_lo[s * XS + row] = l;
-                    ka[s] = s < Lc ? cend * kcs : 0.f;  // g(Lc-1, s) k_s
-                }
+    // Preparation of one chunk of Lc tokens from the operands in o (tokens >= Lc were loaded
+    // as zeros, or zeroed): per-token gate values, the decay products c, and the operand
+    // planes XK, XQ, KD, KH with c_last and d_0 per row and beta per token. A row whose c leaves
+    // the factored range lowers *cut to the first such token.
+    auto prep = [&](int Lc) {
+        float egl, btl;  // lane t = lane % 32: exp(g_t) and beta_t (neutral past Lc)
+        {
+            const int t = lane & 31;
+            float g, bv;
+            if constexpr (GATE == kGateGiven) {
+                g = __uint_as_float(o.ga);
+                bv = bf16_to_f32((uint16_t)o.gb);
             } else {
+                g = ds * softplus_fast(gate_value<GATE == kGateF16>(o.ga) + dt);
+                bv = sigmoid_fast(gate_value<GATE == kGateF16>(o.gb));
+            }
+            const bool in = t < Lc;
+            egl = in ? __expf(g) : 1.f;
+            btl = in ? bv : 0.f;
+        }
+        if (w == 0 && lane < kChunk) bt[lane] = btl;
+        float eg[TPT], ks[TPT], qs[TPT], kf[TPT][4], qf[TPT][4];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    kc_hi[s * XS + row] = 0;
-                    kc_lo[s * XS + row] = 0;
-                    float wv = k[s];  // g(s,s) k_s
-                    ka[s] = (s + 1 == Lc) ? wv : 0.f;
-                    gp[s * 8 + s] = wv * q[s];
+        for (int j = 0; j < TPT; ++j) {
+            eg[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (TPT * tg + j), __float_as_int(egl)));
+            kf[j][0] = bf16_lo(o.k[j].x);
+            kf[j][1] = bf16_hi(o.k[j].x);
+            kf[j][2] = bf16_lo(o.k[j].y);
+            kf[j][3] = bf16_hi(o.k[j].y);
+            qf[j][0] = bf16_lo(o.q[j].x);
+            qf[j][1] = bf16_hi(o.q[j].x);
+            qf[j][2] = bf16_lo(o.q[j].y);
+            qf[j][3] = bf16_hi(o.q[j].y);
+            ks[j] = 1.f;
+            qs[j] = a.scale;
+        }
+        if (norm) {  // uniform: L2-normalise each token's q and k over the D_k rows
+            float sk[TPT], sq[TPT];
 #pragma unroll
-                    for (int t = s + 1; t < 8; ++t) {
-                        wv *= d[t];  // g(t,s) k_s
-                        gp[s * 8 + t] = wv * k[t];
-                        gp[t * 8 + s] = wv * q[t];
-                        if (t + 1 == Lc) ka[s] = wv;
-                    }
+            for (int j = 0; j < TPT; ++j) {
+                float a2 = 0.f, b2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a2 = fmaf(kf[j][e], kf[j][e], a2);
+                    b2 = fmaf(qf[j][e], qf[j][e], b2);
+                }
+                sk[j] = colsum<NTG>(a2);  // over this wave's row groups (lanes NTG apart)
+                sq[j] = colsum<NTG>(b2);
+            }
+            if (lane < NTG)
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    npart[(2 * w) * kChunk + TPT * tg + j] = sk[j];
+                    npart[(2 * w + 1) * kChunk + TPT * tg + j] = sq[j];
+                }
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                const int t = TPT * tg + j;
+                float a2 = 0.f, b2 = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    a2 += npart[(2 * v) * kChunk + t];
+                    b2 += npart[(2 * v + 1) * kChunk + t];
+                }
+                ks[j] = inv_norm(a2);
+                qs[j] = a.scale * inv_norm(b2);
+            }
+        }
+        // Decays, and their running products over this thread's tokens (token 0 excluded).
+        float d[TPT][4], cp[TPT][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = 1.f;
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                d[j][e] = eg[j] * __expf(o.gk[j][e]);
+                acc *= (j == 0 && tg == 0) ? 1.f : d[j][e];
+                cp[j][e] = acc;
+            }
+        }
+        // Across the row group's token groups: inclusive products by DPP row shifts, then
+        // the exclusive prefix (shift by one) and the chunk total (last token group).
+        float inc[4], pre[4], clast[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) inc[e] = cp[TPT - 1][e];
+        auto shr = [](float v, auto k) {
+            return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(v),
+                                                              0x110 + decltype(k)::value, 0xF, 0xF, false));
+        };
+#define RGDR_SCAN_STEP(K)                                                         \
+    if constexpr (K < NTG) {                                                      \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                           \
+            const float p = shr(inc[e], std::integral_constant<int, K>{});        \
+            inc[e] = tg >= K ? inc[e] * p : inc[e];                               \
+        }                                                                         \
+    }
+        RGDR_SCAN_STEP(1)
+        RGDR_SCAN_STEP(2)
+        RGDR_SCAN_STEP(4)
+        RGDR_SCAN_STEP(8)
+#undef RGDR_SCAN_STEP
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p = shr(inc[e], std::integral_constant<int, 1>{});
+            pre[e] = tg >= 1 ? p : 1.f;
+            clast[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (lane | (NTG - 1)), __float_as_int(inc[e])));
+        }
+        float cmin = 1.f, cmax = 1.f;
+#pragma unroll
+        for (int j = 0; j < TPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cp[j][e] *= pre[e];  // c_t of row 4 r + e
+                cmin = fminf(cmin, cp[j][e]);
+                cmax = fmaxf(cmax, cp[j][e]);
+            }
+        // Operand planes. Row-major by token for XK, XQ, KD; by state row for KH.
+        float khv[TPT][4];
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const int t = TPT * tg + j;
+            f32x4 vk, vq, vd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kk = kf[j][e] * ks[j];
+                vk[e] = cp[j][e] * kk;
+                vq[e] = cp[j][e] * (qf[j][e] * qs[j]);
+                vd[e] = kk * __builtin_amdgcn_rcpf(cp[j][e]);
+                khv[j][e] = clast[e] * vd[e];
+            }
+            uint2 h, l;
+            const int off = t * XS + 4 * r;
+            split4(vk, h, l);
+            *reinterpret_cast<uint2 *>(xk_hi + off) = h;
+            *reinterpret_cast<uint2 *>(xk_lo + off) = l;
+            split4(vq, h, l);
+            *reinterpret_cast<uint2 *>(xq_hi + off) = h;
+            *reinterpret_cast<uint2 *>(xq_lo + off) = l;
+            split4(vd, h, l);
+            *reinterpret_cast<uint2 *>(kd_hi + off) = h;
+            *reinterpret_cast<uint2 *>(kd_lo + off) = l;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int off = (4 * r + e) * KS + TPT * tg;
+            if constexpr (TPT == 4) {
+                uint2 h, l;
+                split4(f32x4{khv[0][e], khv[1][e], khv[2][e], khv[3][e]}, h, l);
+                *reinterpret_cast<uint2 *>(kh_hi + off) = h;
+                *reinterpret_cast<uint2 *>(kh_lo + off) = l;
+            } else {
+                const uint32_t h = pack_bf16x2(khv[0][e], khv[1][e]);
+                const uint32_t l = pack_bf16x2(khv[0][e] - bf16_lo(h), khv[1][e] - bf16_hi(h));
+                *reinterpret_cast<uint32_t *>(kh_hi + off) = h;
+                *reinterpret_cast<uint32_t *>(kh_lo + off) = l;
+            }
+        }
+        if (tg == 0) {
+            *reinterpret_cast<f32x4 *>(crow + 4 * r) = f32x4{clast[0], clast[1], clast[2], clast[3]};
+            *reinterpret_cast<f32x4 *>(d0row + 4 * r) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
+        }
+        if (!(cmin >= kChunkLo && cmax <= kChunkHi)) {  // rare: find the first token out of range
+            int first = kChunk;
+#pragma unroll
+            for (int j = TPT - 1; j >= 0; --j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!(cp[j][e] >= kChunkLo && cp[j][e] <= kChunkHi)) first = TPT * tg + j;
+            atomicMin(cut, first);
+        }
+    };
+
+    int chunk = 0;
+    while (t0 < L) {  // uniform over the workgroup
+        int Lc = len;
+        for (;;) {
+            prep(Lc);
+            lds_barrier();
+            const int c = *cut;
+            if (c >= Lc) break;
+            // A decay product left the range at token c >= 1: the chunk ends before it.
+            // Zero this thread's operands of the later tokens and prepare again. Nothing
+            // written by the preparation is read before the barrier that ends it, and the
+            // second pass lowers the cut to no token below c (its tokens before c are
+            // unchanged, the later ones neutral), so no other barrier is needed.
+            Lc = c;
+#pragma unroll
+            for (int j = 0; j < TPT; ++j)
+                if (TPT * tg + j >= Lc) {
+                    o.k[j] = u32x2{0u, 0u};
+                    o.q[j] = u32x2{0u, 0u};
+                    o.gk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        const int t0n = t0 + Lc, lenn = t0n < L ? chunk_len(t0n) : 0;
+
+        // M and N blocks, each wave its share (rotating by chunk so that the extra work of
+        // role 0 moves between the SIMDs): role 0 forms beta M of the two diagonal blocks and
+        // inverts them (all in this wave, so no barrier separates the steps); roles 1-3 form
+        // -M_10, N_00, N_10 and N_11 as split operand blocks.
+        const int role = (w + chunk) & 3;
+        if (role == 0) {
+            const f32x4 m00 = gram_block<DK, XS>(xk_hi, kd_hi, 0, 0, n16, kg);
+            const f32x4 m11 = gram_block<DK, XS>(xk_hi, kd_hi, 1, 1, n16, kg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * kg + i;
+                td[row * BS + n16] = bt[row] * m00[i];
+                td[16 * BS + row * BS + n16] = bt[16 + row] * m11[i];
+            }
+            lds_phase();
+            // Forward substitution: lane j < 16 solves (I + T_00) x = e_j, lane 16 + j
+            // (I + T_11) x = e_j, with T = beta M strictly below the diagonal; then
+            // A[.][j] = x beta_j. Lanes 32..63 repeat lanes 0..31 and write nothing.
+            int jc = lane & 15;
+            // recomputed per chunk: hoisted out of the loop, the 16 right-hand sides below
+            // would occupy registers through every phase
+            asm volatile("" : "+v"(jc));
+            const int db = (lane >> 4) & 1;
+            const float *tr = td + db * 16 * BS;
+            float xs[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float acc = rr == jc ? 1.f : 0.f;
+#pragma unroll
+                for (int c = 0; c < rr; ++c) acc = fmaf(-tr[rr * BS + c], xs[c], acc);
+                xs[rr] = acc;
+            }
+            if (lane < 32) {
+                const float bj = bt[16 * db + jc];
+                uint16_t *ab = blk(db);
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    uint16_t h, l;
+                    split_bf16(xs[rr] * bj, h, l);
+                    ab[rr * AS + jc] = h;
+                    ab[16 * AS + rr * AS + jc] = l;
                 }
             }
-            uint16_t kh[8], kl[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) split_bf16(ka[s], kh[s], kl[s]);
-            *reinterpret_cast<u32x4 *>(ka_hi + row * 8) =
-                u32x4{kh[0] | ((uint32_t)kh[1] << 16), kh[2] | ((uint32_t)kh[3] << 16),
-                      kh[4] | ((uint32_t)kh[5] << 16), kh[6] | ((uint32_t)kh[7] << 16)};
-            *reinterpret_cast<u32x4 *>(ka_lo + row * 8) =
-                u32x4{kl[0] | ((uint32_t)kl[1] << 16), kl[2] | ((uint32_t)kl[3] << 16),
-                      kl[4] | ((uint32_t)kl[5] << 16), kl[6] | ((uint32_t)kl[7] << 16)};
+        } else if (role == 1) {
+            put_block<AS, false>(blk(2), gram_block<DK, XS>(xk_hi, kd_hi, 1, 0, n16, kg), -1.f, n16, kg);
+            put_block<AS, true>(blk(3), gram_block<DK, XS>(xq_hi, kd_hi, 0, 0, n16, kg), 1.f, n16, kg);
+        } else if (role == 2) {
+            put_block<AS, false>(blk(4), gram_block<DK, XS>(xq_hi, kd_hi, 1, 0, n16, kg), 1.f, n16, kg);
+        } else {
+            put_block<AS, true>(blk(5), gram_block<DK, XS>(xq_hi, kd_hi, 1, 1, n16, kg), 1.f, n16, kg);
         }
-        if (w < 2)  // the direct shares of this wave's rows (zero where none): lane e, entry e
-            gpart[64 * w + lane] = direct ? wave_sum64_transposed(gp, lane) : 0.f;
-        lds_barrier();
 
-        // M and N: the factored products on the matrix cores (each wave for itself), plus
-        // the direct shares.
-        gram_tables<DK, XS>(xt_hi, xt_lo, kc_hi, kc_lo, gpart, gsM, gsN, n16, kg);
-        lds_phase();
-
-        // Y = [c k | c scale q]^T S (16 x 32, this wave's columns), column set c, over
-        // row-block pairs; three products of the split parts (high x high, low x high,
-        // high x low).
-        f32x4 acc[2];
+        // Y_K = [c k]^T S' and Y_Q = [c scale q]^T S' (32 tokens x this wave's 32 columns),
+        // with S' = diag(d_0) S formed in place; three products of the split parts.
+        f32x4 yk[2][2], yq[2][2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) yk[tb][c] = yq[tb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb) {
-            const int r0 = 32 * pb + 4 * kg;
-            const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
-            const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                bf16x8 sh, sl;
-                split8(S[2 * pb][c], S[2 * pb + 1][c], sh, sl);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh, acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh, acc[c], 0, 0, 0);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl, acc[c], 0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 dv = *reinterpret_cast<const f32x4 *>(d0row + 16 * (2 * pb + h) + 4 * kg);
+                S[2 * pb + h][0] *= dv;
+                S[2 * pb + h][1] *= dv;
+            }
+            bf16x8 sh[2], sl[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) split8(S[2 * pb][c], S[2 * pb + 1][c], sh[c], sl[c]);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int ra = (16 * tb + n16) * XS + 32 * pb + 4 * kg;
+                const bf16x8 kh = lds_pair8(xk_hi + ra, xk_hi + ra + 16), kl = lds_pair8(xk_lo + ra, xk_lo + ra + 16);
+                const bf16x8 qh = lds_pair8(xq_hi + ra, xq_hi + ra + 16), ql = lds_pair8(xq_lo + ra, xq_lo + ra + 16);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    yk[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, sh[c], yk[tb][c], 0, 0, 0);
+                    yk[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, sh[c], yk[tb][c], 0, 0, 0);
+                    yk[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, sl[c], yk[tb][c], 0, 0, 0);
+                    yq[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, sh[c], yq[tb][c], 0, 0, 0);
+                    yq[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, sh[c], yq[tb][c], 0, 0, 0);
+                    yq[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, sl[c], yq[tb][c], 0, 0, 0);
+                }
             }
         }
-        // Y to LDS, transposed: accumulator c holds rows 4 kg .. 4 kg + 3 of column
-        // 32 w + 2 n16 + c. Every wave has prepared its rows (barrier above), so the d, k and
-        // q planes are free.
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-            *reinterpret_cast<f32x4 *>(ycol(32 * w + 2 * n16 + c) + 4 * kg) = acc[c];
-        lds_phase();
+        // The next chunk's operands travel while this one is finished.
+        load_chunk<DK, GATE>(a, m, o, r, tg, lane, t0n, lenn);
+        lds_barrier();  // every operand block is written
+        if (tid == 0) *cut = kChunk;  // every thread read it before the barrier
 
-        // Triangular solve for column 32 w + (lane & 31); outputs of the run's tokens.
-        const auto rout = make_rsrc(a.out + (bh * a.T + t0) * a.Dv,
-                                    cols ? (uint32_t)(Lc * a.Dv * 2) : 0u);
-        float yc[16];
+        // R = V - Y_K for the chunk's tokens (0 past Lc); then the next chunk's values.
+        f32x4 R[2][2];
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-            const f32x4 e = *reinterpret_cast<const f32x4 *>(ycol(col) + 4 * v4);
-            yc[4 * v4] = e.x;
-            yc[4 * v4 + 1] = e.y;
-            yc[4 * v4 + 2] = e.z;
-            yc[4 * v4 + 3] = e.w;
-        }
-        float u[8];
-        uint16_t o16[8];
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float v = ob[VB + t * TV + col];
-            const float bt = ob[VB + 8 * TV + t];
-            float p = yc[t];
-#pragma unroll
-            for (int s2 = 0; s2 < t; ++s2) p = fmaf(gsM[t * 8 + s2], u[s2], p);
-            u[t] = t < Lc ? bt * (v - p) : 0.f;
-            float ov = yc[8 + t];
-#pragma unroll
-            for (int s2 = 0; s2 <= t; ++s2) ov = fmaf(gsN[t * 8 + s2], u[s2], ov);
-            o16[t] = f32_to_bf16(ov);
-        }
-        // rows past the run fall outside the output range and are not written
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            __builtin_amdgcn_raw_buffer_store_b16(o16[t], rout, (uint32_t)(t * a.Dv * 2) + ocol, 0, 0);
-        {
-            uint16_t h[8], l[8];
-#pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) split_bf16(u[s2], h[s2], l[s2]);
-            // local column j = 2 n + c goes to UT position c * 16 + n (lanes 32..63 write
-            // the same values as lanes 0..31)
-            const int p = (jcol & 1) * 16 + (jcol >> 1);
-            *reinterpret_cast<u32x4 *>(ut_hi + p * 8) =
-                u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                      h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
-            *reinterpret_cast<u32x4 *>(ut_lo + p * 8) =
-                u32x4{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16),
-                      l[4] | ((uint32_t)l[5] << 16), l[6] | ((uint32_t)l[7] << 16)};
-        }
-        lds_phase();
-
-        // S = diag(c_end) S + [g k]^T U. The row scaling is an fp32 multiply of the
-        // accumulators; the update is two 16x16x16 products per block into them: lane group kg
-        // carries tokens 4 (kg & 1) .. + 3 of A's high part (kg < 2) or remainder (kg >= 2),
-        // against U's high part, then U's remainder. Only this one instruction shape ever
-        // accumulates into S.
-        s16x4 buh[2], bul[2];
+            for (int i = 0; i < 4; ++i) {
+                const bool in = 16 * tb + 4 * kg + i < Lc;
+                R[tb][0][i] = in ? bf16_lo(vr[tb][i]) - yk[tb][0][i] : 0.f;
+                R[tb][1][i] = in ? bf16_hi(vr[tb][i]) - yk[tb][1][i] : 0.f;
+            }
+        load_v(t0n, lenn);
+        auto blk4 = [&](int b, int lo) {
+            return as_s16x4(*reinterpret_cast<const uint2 *>(blk(b) + lo * 16 * AS + n16 * AS + 4 * kg));
+        };
+        // U_0 = A_00 R_0; U_1 = A_11 (R_1 - M_10 U_0); O = Y_Q + N U (each product its own
+        // 16x16x16 chain; the sums with Y_Q on the VALU).
+        uint2 u0h[2], u0l[2], u1h[2], u1l[2];
+        f32x4 ov[2][2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            buh[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_hi + (c * 16 + n16) * 8 + 4 * (kg & 1)));
-            bul[c] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ut_lo + (c * 16 + n16) * 8 + 4 * (kg & 1)));
+            uint2 rh, rl;
+            split4(R[0][c], rh, rl);
+            const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 u0 = mma16(blk4(0, 0), blk4(0, 1), as_s16x4(rh), as_s16x4(rl), z);
+            split4(u0, u0h[c], u0l[c]);
+            const f32x4 r1 = mma16(blk4(2, 0), blk4(2, 1), as_s16x4(u0h[c]), as_s16x4(u0l[c]), R[1][c]);
+            split4(r1, rh, rl);
+            const f32x4 u1 = mma16(blk4(1, 0), blk4(1, 1), as_s16x4(rh), as_s16x4(rl), z);
+            split4(u1, u1h[c], u1l[c]);
+            const f32x4 n0 = mma16(blk4(3, 0), blk4(3, 1), as_s16x4(u0h[c]), as_s16x4(u0l[c]), z);
+            f32x4 n1 = mma16(blk4(4, 0), blk4(4, 1), as_s16x4(u0h[c]), as_s16x4(u0l[c]), z);
+            n1 = mma16(blk4(5, 0), blk4(5, 1), as_s16x4(u1h[c]), as_s16x4(u1l[c]), n1);
+            ov[0][c] = yq[0][c] + n0;
+            ov[1][c] = yq[1][c] + n1;
         }
-        const uint16_t *ka_lane = (kg >> 1 ? ka_lo : ka_hi) + n16 * 8 + 4 * (kg & 1);
+        {
+            // tokens past the chunk fall outside the output range and are not written
+            const auto rout = make_rsrc(a.out + (bh * a.T + t0) * a.Dv, cols ? (uint32_t)(Lc * a.Dv * 2) : 0u);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        pack_bf16x2(ov[tb][0][i], ov[tb][1][i]), rout, orow,
+                        (uint32_t)((16 * tb + i) * a.Dv * 2), 0);
+        }
+        // S = diag(c_last) S' + KH^T U, one 16x16x32 chain per block over the chunk's tokens
+        // (k slots: tokens 4 kg .. + 3 of U_0, then of U_1).
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
-            const s16x4 ak = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(ka_lane + 16 * rb * 8));
+            const int ra = (16 * rb + n16) * KS + 4 * kg;
+            const bf16x8 ah = lds_pair8(kh_hi + ra, kh_hi + ra + 16), al = lds_pair8(kh_lo + ra, kh_lo + ra + 16);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 S[rb][c] = S[rb][c] * cr;
-                S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, buh[c], S[rb][c], 0, 0, 0);
-                S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bul[c], S[rb][c], 0, 0, 0);
+                S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, cat8(u0h[c], u1h[c]), S[rb][c], 0, 0, 0);
+                S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, cat8(u0h[c], u1h[c]), S[rb][c], 0, 0, 0);
+                S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, cat8(u0l[c], u1l[c]), S[rb][c], 0, 0, 0);
             }
         }
-        t0 = t1;
-        t1 = t1n;
+        t0 = t0n;
+        len = lenn;
+        ++chunk;
         if (t0 == n) {  // the accepted prefix ends here: commit
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     __builtin_amdgcn_raw_buffer_store_b32(
-                        pack_bf16x2(S[rb][0][i], S[rb][1][i]), rso,
-                        lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2), 0,
-                        RGDR_STATE_STORE_POLICY);
+                        pack_bf16x2(S[rb][0][i], S[rb][1][i]), rso, lane_off,
+                        (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_STORE_POLICY);
         }
-        lds_barrier();  // the next run's staging reuses every LDS area
+        lds_barrier();  // the next chunk's preparation reuses every LDS area
     }
 
     // Padded (or skipped) tokens: +0.0 rows. Lane (r, c4) stores 8 columns of row r of each
@@ -363,6 +672,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             store16<0>(u32x4{0u, 0u, 0u, 0u}, rz, zoff + (uint32_t)(t * a.Dv * 2));
     }
 }
+
 
 template <int DK, int GATE>
 static hipError_t launch_prefill(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
