@@ -46,6 +46,7 @@ constexpr int kPrefillMaxT = 65536;  // tokens per call: keeps every per-item of
 constexpr int kChunk = 32;           // tokens per chunk
 // Range of the decay products c_t inside which a chunk takes the factored form.
 constexpr float kChunkLo = 0x1p-96f, kChunkHi = 0x1p96f;
+constexpr float kLog2e = 1.4426950408889634f;  // exp(x) = 2^(x log2 e)
 
 // Waves per SIMD the kernel is compiled for (the register budget).
 #ifndef RGDR_PREFILL_MIN_WAVES
@@ -57,7 +58,7 @@ constexpr float kChunkLo = 0x1p-96f, kChunkHi = 0x1p96f;
 //   TPT tg .. TPT tg + TPT - 1; the NTG token groups of a row group are consecutive lanes.
 //   XK, XQ, KD: [hi, lo][32 tokens][XS] bf16: c_t k_t, c_t scale q_t, k_t / c_t by row.
 //   KH: [hi, lo][D_k rows][KS] bf16: (c_last / c_s) k_s, one row per state row.
-//   TD: [2][16][BS] fp32: beta_t M[t][s] of the two diagonal 16 x 16 blocks.
+//   TD: [2][16][BS] fp32: beta_t M[t][s] of the two diagonal 16 x 16 blocks, by column s.
 //   BK: [6 blocks][hi, lo][16][AS] bf16: A_00, A_11, -M_10, N_00, N_10, N_11.
 //   c_last and d_0 per row, beta per token, and the chunk cut.
 template <int DK>
@@ -198,11 +199,12 @@ __device__ __forceinline__ f32x4 mma16(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f
 // into the B operand of Y = X S in the lane that holds it. The chunk's per-token results (Y_K,
 // Y_Q, U, O) use the same layout with tokens for rows: 16 tb + 4 kg + i is the token, and the
 // rows 4 kg .. + 3 of a 16-token block are the k slots of a 16x16x16 product over tokens.
-template <int DK, int GATE>
+template <int DK, int GATE, bool NORM>
 __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
     static_assert(DK == 64 || DK == 128, "D_k = 64 or 128");
+    static_assert(!NORM || GATE != kGateGiven, "q/k normalisation belongs to the fused front end");
     using P = ChunkShape<DK>;
     constexpr int TV = 128, NRB = P::NRB, NPB = P::NPB, TPT = P::TPT, NTG = P::NTG;
     constexpr int XS = P::XS, KS = P::KS, AS = P::AS, BS = P::BS;
@@ -246,7 +248,6 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const uint32_t orow = ocol + (uint32_t)(4 * kg * a.Dv * 2);
     float dt = 0.f, ds = 0.f;
     if constexpr (GATE != kGateGiven) gate_head(a, m.h, dt, ds);
-    const bool norm = GATE != kGateGiven && a.norm_qk != 0;
 
     // Chunks of at most kChunk tokens; the chunk holding the accepted prefix's end stops there.
     auto chunk_len = [&](int t0) {
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     // planes XK, XQ, KD, KH with c_last and d_0 per row and beta per token. A row whose c leaves
     // the factored range lowers *cut to the first such token.
     auto prep = [&](int Lc) {
-        float egl, btl;  // lane t = lane % 32: exp(g_t) and beta_t (neutral past Lc)
+        float gll, btl;  // lane t = lane % 32: g_t log2(e) and beta_t (neutral past Lc)
         {
             const int t = lane & 31;
             float g, bv;
@@ -314,14 +315,14 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 bv = sigmoid_fast(gate_value<GATE == kGateF16>(o.gb));
             }
             const bool in = t < Lc;
-            egl = in ? __expf(g) : 1.f;
+            gll = in ? g * kLog2e : 0.f;
             btl = in ? bv : 0.f;
         }
         if (w == 0 && lane < kChunk) bt[lane] = btl;
-        float eg[TPT], ks[TPT], qs[TPT], kf[TPT][4], qf[TPT][4];
+        float gl[TPT], ks[TPT], qs[TPT], kf[TPT][4], qf[TPT][4];
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
-            eg[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (TPT * tg + j), __float_as_int(egl)));
+            gl[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (TPT * tg + j), __float_as_int(gll)));
             kf[j][0] = bf16_lo(o.k[j].x);
             kf[j][1] = bf16_hi(o.k[j].x);
             kf[j][2] = bf16_lo(o.k[j].y);
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             ks[j] = 1.f;
             qs[j] = a.scale;
         }
-        if (norm) {  // uniform: L2-normalise each token's q and k over the D_k rows
+        if constexpr (NORM) {  // L2-normalise each token's q and k over the D_k rows
             float sk[TPT], sq[TPT];
 #pragma unroll
             for (int j = 0; j < TPT; ++j) {
@@ -373,7 +374,8 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             float acc = 1.f;
 #pragma unroll
             for (int j = 0; j < TPT; ++j) {
-                d[j][e] = eg[j] * __expf(o.gk[j][e]);
+                // exp(g_t) exp(gk_t,i) as one power of two
+                d[j][e] = __builtin_amdgcn_exp2f(fmaf(o.gk[j][e], kLog2e, gl[j]));
                 acc *= (j == 0 && tg == 0) ? 1.f : d[j][e];
                 cp[j][e] = acc;
             }
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             f32x4 vk, vq, vd;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float kk = kf[j][e] * ks[j];
+                const float kk = NORM ? kf[j][e] * ks[j] : kf[j][e];
                 vk[e] = cp[j][e] * kk;
                 vq[e] = cp[j][e] * (qf[j][e] * qs[j]);
                 vd[e] = kk * __builtin_amdgcn_rcpf(cp[j][e]);
@@ -502,30 +504,32 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         if (role == 0) {
             const f32x4 m00 = gram_block<DK, XS>(xk_hi, kd_hi, 0, 0, n16, kg);
             const f32x4 m11 = gram_block<DK, XS>(xk_hi, kd_hi, 1, 1, n16, kg);
+            // T = beta M of the two diagonal blocks, stored by column: td[c][r] = beta_r M[r][c].
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * kg + i;
-                td[row * BS + n16] = bt[row] * m00[i];
-                td[16 * BS + row * BS + n16] = bt[16 + row] * m11[i];
+                td[n16 * BS + row] = bt[row] * m00[i];
+                td[16 * BS + n16 * BS + row] = bt[16 + row] * m11[i];
             }
             lds_phase();
-            // Forward substitution: lane j < 16 solves (I + T_00) x = e_j, lane 16 + j
-            // (I + T_11) x = e_j, with T = beta M strictly below the diagonal; then
-            // A[.][j] = x beta_j. Lanes 32..63 repeat lanes 0..31 and write nothing.
+            // Forward substitution, column by column: lane j < 16 solves (I + T_00) x = e_j,
+            // lane 16 + j (I + T_11) x = e_j (T strictly below the diagonal); then
+            // A[.][j] = x beta_j. Once x_c is final, the later rows' updates by it are
+            // independent, so the dependent chain is 16 steps long. Lanes 32..63 repeat lanes
+            // 0..31 and write nothing.
             int jc = lane & 15;
             // recomputed per chunk: hoisted out of the loop, the 16 right-hand sides below
             // would occupy registers through every phase
             asm volatile("" : "+v"(jc));
             const int db = (lane >> 4) & 1;
-            const float *tr = td + db * 16 * BS;
+            const float *tcol = td + db * 16 * BS;
             float xs[16];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float acc = rr == jc ? 1.f : 0.f;
+            for (int rr = 0; rr < 16; ++rr) xs[rr] = rr == jc ? 1.f : 0.f;
 #pragma unroll
-                for (int c = 0; c < rr; ++c) acc = fmaf(-tr[rr * BS + c], xs[c], acc);
-                xs[rr] = acc;
-            }
+            for (int c = 0; c < 15; ++c)
+#pragma unroll
+                for (int rr = c + 1; rr < 16; ++rr) xs[rr] = fmaf(-tcol[c * BS + rr], xs[c], xs[rr]);
             if (lane < 32) {
                 const float bj = bt[16 * db + jc];
                 uint16_t *ab = blk(db);
@@ -591,10 +595,15 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool in = 16 * tb + 4 * kg + i < Lc;
-                R[tb][0][i] = in ? bf16_lo(vr[tb][i]) - yk[tb][0][i] : 0.f;
-                R[tb][1][i] = in ? bf16_hi(vr[tb][i]) - yk[tb][1][i] : 0.f;
+                R[tb][0][i] = bf16_lo(vr[tb][i]) - yk[tb][0][i];
+                R[tb][1][i] = bf16_hi(vr[tb][i]) - yk[tb][1][i];
             }
+        if (Lc < kChunk)  // uniform: a short chunk's later tokens (their values may be anything)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * tb + 4 * kg + i >= Lc) R[tb][0][i] = R[tb][1][i] = 0.f;
         load_v(t0n, lenn);
         auto blk4 = [&](int b, int lo) {
             return as_s16x4(*reinterpret_cast<const uint2 *>(blk(b) + lo * 16 * AS + n16 * AS + 4 * kg));
@@ -677,8 +686,15 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 template <int DK, int GATE>
 static hipError_t launch_prefill(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                  const int32_t *nacc, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_kernel<DK, GATE>), dim3(a.n_items), dim3(256), 0, stream, a,
-                       lens, idx, nacc);
+    if constexpr (GATE != kGateGiven) {
+        if (a.norm_qk) {
+            hipLaunchKernelGGL((prefill_kernel<DK, GATE, true>), dim3(a.n_items), dim3(256), 0,
+                               stream, a, lens, idx, nacc);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((prefill_kernel<DK, GATE, false>), dim3(a.n_items), dim3(256), 0, stream,
+                       a, lens, idx, nacc);
     return hipGetLastError();
 }
 
