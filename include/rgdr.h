@@ -150,9 +150,10 @@ rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *va
  *   T  1 <= T <= 65536 (the padded sequence length), and T * H_v <= 2^29.
  * The state is read once and kept in fp32 across all of an entry's tokens; it is rounded to
  * bf16 once, when it is committed after the entry's first num_accepted_tokens tokens.
- * Tokens are evaluated in runs of at most 8 in the exact closed form of the recurrence,
+ * Tokens are evaluated in chunks of at most 32 in the exact closed form of the recurrence,
  * whose dense products run on the matrix cores with operands split into bf16 high parts and
- * remainders (about 16 bits of each operand, fp32 accumulation).
+ * remainders (about 16 bits of each operand, fp32 accumulation); a chunk whose decay
+ * products leave [2^-96, 2^96] is shortened, which changes time, not results.
  * Errors: as rgdr_decode (RGDR_ERR_SHAPE for T > 65536 or T * H_v > 2^29).
  */
 rgdr_status rgdr_prefill(const void *query, const void *key, const void *value,
