@@ -113,7 +113,9 @@ SOURCES_COMMON = ("gated_delta_rule_rgdr_amd/csrc/rgdr_device.h",
                   "gated_delta_rule_rgdr_amd/csrc/rgdr_common.h")
 SOURCES_DECODE = ("gated_delta_rule_rgdr_amd/csrc/rgdr_decode.hip",) + SOURCES_COMMON
 SOURCES_PREFILL = ("gated_delta_rule_rgdr_amd/csrc/rgdr_prefill.hip",) + SOURCES_COMMON
-TRAFFIC_PROFILES = {1: "profiles/rgdr_decode_b1_h64_dk64_dv512.md",
+# Counter summaries by (workload, batch size; None = the workload's own).
+TRAFFIC_PROFILES = {(2, 16): "profiles/rgdr_decode_b16_gqa_d128.md",
+                    1: "profiles/rgdr_decode_b1_h64_dk64_dv512.md",
                     2: "profiles/rgdr_decode_b64_gqa_d128.md",
                     3: "profiles/rgdr_decode_varlen_b32_t8_d128.md",
                     4: "profiles/rgdr_decode_b256_gqa_d128.md",
@@ -135,14 +137,15 @@ def kernel_code_digest(wid=2):
     return h.hexdigest()
 
 
-def measured_traffic(wid=2):
+def measured_traffic(wid=2, batch=None):
     """HBM bytes per fused call from the committed rocprofv3 counter summary of workload
-    `wid`, or None when there is none or the kernel's code has changed since those counters
-    were taken."""
+    `wid` (at batch size `batch`, if it replaces the workload's), or None when there is none
+    or the kernel's code has changed since those counters were taken."""
     import re
-    if wid not in TRAFFIC_PROFILES:
+    key = wid if batch is None else (wid, batch)
+    if key not in TRAFFIC_PROFILES:
         return None
-    path = os.path.join(ROOT, TRAFFIC_PROFILES[wid])
+    path = os.path.join(ROOT, TRAFFIC_PROFILES[key])
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -272,6 +275,7 @@ class Workload:
         import workloads
         self.rg, self.torch = rg, torch
         self.wid = wid
+        self.batch = batch
         self.name = workloads.WORKLOAD_NAMES[wid]
         if batch is not None:
             self.name = re.sub(r"B=\d+", f"B={batch}", self.name)
@@ -418,7 +422,7 @@ def roofline(wl, us):
     gbs = wl.step_bytes / (us * 1e-6) / 1e9
     r = {"kernel": wl.fused_name, "bound": "hbm", "achieved": round(gbs, 2),
          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-         "traffic": measured_traffic(wl.wid), "bytes_per_launch": wl.step_bytes,
+         "traffic": measured_traffic(wl.wid, wl.batch), "bytes_per_launch": wl.step_bytes,
          "avg_launch_us": round(us, 3)}
     if wl.prefill:
         fl = prefill_mfma_flops(wl.inp)
