@@ -496,32 +496,22 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         }
         const int t0n = t0 + Lc, lenn = t0n < L ? chunk_len(t0n) : 0;
 
-        // M and N blocks, each wave its share (rotating by chunk so that the extra work of
-        // role 0 moves between the SIMDs): role 0 forms beta M of the two diagonal blocks and
-        // inverts them (all in this wave, so no barrier separates the steps); roles 1-3 form
-        // -M_10, N_00, N_10 and N_11 as split operand blocks.
+        // M and N blocks, each wave its share (rotating by chunk so that the solves move
+        // between the SIMDs): roles 0 and 1 form beta M of one diagonal block each and invert
+        // it (in the same wave, so no barrier separates the steps); roles 2 and 3 form -M_10,
+        // N_00, N_10 and N_11 as split operand blocks.
         const int role = (w + chunk) & 3;
-        if (role == 0) {
-            const f32x4 m00 = gram_block<DK, XS>(xk_hi, kd_hi, 0, 0, n16, kg);
-            const f32x4 m11 = gram_block<DK, XS>(xk_hi, kd_hi, 1, 1, n16, kg);
-            // T = beta M of the two diagonal blocks, stored by column: td[c][r] = beta_r M[r][c].
+        if (role < 2) {
+            // beta M of diagonal block db = role, inverted by column-oriented forward
+            // substitution (lane j < 16: column j; lanes 16..63 repeat and write nothing)
+            const int db = role;
+            const f32x4 mdd = gram_block<DK, XS>(xk_hi, kd_hi, db, db, n16, kg);
+            float *tcol_w = td + db * 16 * BS;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * kg + i;
-                td[n16 * BS + row] = bt[row] * m00[i];
-                td[16 * BS + n16 * BS + row] = bt[16 + row] * m11[i];
-            }
+            for (int i = 0; i < 4; ++i) tcol_w[n16 * BS + 4 * kg + i] = bt[16 * db + 4 * kg + i] * mdd[i];
             lds_phase();
-            // Forward substitution, column by column: lane j < 16 solves (I + T_00) x = e_j,
-            // lane 16 + j (I + T_11) x = e_j (T strictly below the diagonal); then
-            // A[.][j] = x beta_j. Once x_c is final, the later rows' updates by it are
-            // independent, so the dependent chain is 16 steps long. Lanes 32..63 repeat lanes
-            // 0..31 and write nothing.
             int jc = lane & 15;
-            // recomputed per chunk: hoisted out of the loop, the 16 right-hand sides below
-            // would occupy registers through every phase
             asm volatile("" : "+v"(jc));
-            const int db = (lane >> 4) & 1;
             const float *tcol = td + db * 16 * BS;
             float xs[16];
 #pragma unroll
@@ -530,7 +520,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             for (int c = 0; c < 15; ++c)
 #pragma unroll
                 for (int rr = c + 1; rr < 16; ++rr) xs[rr] = fmaf(-tcol[c * BS + rr], xs[c], xs[rr]);
-            if (lane < 32) {
+            if (lane < 16) {
                 const float bj = bt[16 * db + jc];
                 uint16_t *ab = blk(db);
 #pragma unroll
@@ -541,12 +531,11 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                     ab[16 * AS + rr * AS + jc] = l;
                 }
             }
-        } else if (role == 1) {
+        } else if (role == 2) {
             put_block<AS, false>(blk(2), gram_block<DK, XS>(xk_hi, kd_hi, 1, 0, n16, kg), -1.f, n16, kg);
             put_block<AS, true>(blk(3), gram_block<DK, XS>(xq_hi, kd_hi, 0, 0, n16, kg), 1.f, n16, kg);
-        } else if (role == 2) {
-            put_block<AS, false>(blk(4), gram_block<DK, XS>(xq_hi, kd_hi, 1, 0, n16, kg), 1.f, n16, kg);
         } else {
+            put_block<AS, false>(blk(4), gram_block<DK, XS>(xq_hi, kd_hi, 1, 0, n16, kg), 1.f, n16, kg);
             put_block<AS, true>(blk(5), gram_block<DK, XS>(xq_hi, kd_hi, 1, 1, n16, kg), 1.f, n16, kg);
         }
 

@@ -202,7 +202,7 @@ def test_prefill_extreme_decays(rg, case):
         inp.g[:] = rng.uniform(-25.0, 3.0, inp.g.shape).astype(np.float32)
         inp.gk[:] = -rng.uniform(0.0, 12.0, inp.gk.shape).astype(np.float32)
     elif case == "split_rows":   # rows 64.. decay by e^-10 per token, rows 0..63 mildly:
-        inp.gk[:, :, :, 64:] = -10.0  # their Gram shares are formed two different ways
+        inp.gk[:, :, :, 64:] = -10.0  # those rows alone shorten the chunks
     else:                         # exp(g) > 1 throughout: outside the operator's domain
         inp.g[:] = 2.5
     out, st = gpu_prefill(inp)
@@ -226,6 +226,19 @@ def test_prefill_extreme_decays(rg, case):
             r = rows[b, h]
             assert_tol(pool[inp.ssm_state_indices[b], h], r, f"growth state b{b} h{h}",
                        atol=2e-2 + 1e-4 * np.abs(r).max())
+
+
+@pytest.mark.parametrize("g_val", [-7.0, -2.6])
+def test_prefill_many_short_chunks(rg, g_val):
+    """Decays strong enough that a chunk's decay products leave the factored range after
+    about 10 (g = -7) or 25 (g = -2.6) tokens: chunks are cut at many different positions
+    relative to the 32-token grid, the accepted prefix and the ragged ends."""
+    inp = workloads.make_case(3, 1, 2, 160, 128, 128, 4, seed=7911, indices="choice",
+                              lengths=[160, 131, 70])
+    inp.num_accepted_tokens = np.array([160, 77, 5], np.int32)
+    inp.g[:] = g_val
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"prefill short chunks g={g_val}")
 
 
 @pytest.mark.parametrize("dtype,norm,Dk", [(np.float32, False, 128), (np.float16, False, 128),
