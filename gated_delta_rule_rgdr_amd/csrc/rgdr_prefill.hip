@@ -16,7 +16,9 @@
 //   Y_K = [c k]^T S',  Y_Q = [c scale q]^T S',
 //   M[t][s] = sum_i (c_t / c_s)_i k_t,i k_s,i (s < t),  N[t][s] = the same with scale q_t (s <= t),
 //   (I + diag(beta) M) U = diag(beta) (V - Y_K),   O = Y_Q + N U,
-//   S_end = diag(c_last) S' + sum_s diag(c_last / c_s) k_s u_s^T.
+//   S_end = diag(c_last) S' + sum_s diag(c_last / c_s) k_s u_s^T = diag(c_last) (S' + K_D^T U),
+// with K_D the rows k_s / c_s. The registers hold S' + K_D^T U; c_last scales it into the next
+// chunk's S' (with that chunk's d_0) or into the committed state.
 // The two products with S' and the rank-32 update are matrix-core products on the state's
 // own accumulator registers; M and N are matrix-core products of the factors c_t k_t (or
 // c_t scale q_t) and k_s / c_s; the 32 x 32 triangular system is solved blockwise: the two
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     // as zeros, or zeroed): per-token gate values, the decay products c, and the operand
     // planes XK, XQ, KD, KH with c_last and d_0 per row and beta per token. A row whose c leaves
     // the factored range lowers *cut to the first such token.
-    auto prep = [&](int Lc) {
+    auto prep = [&](int Lc, const f32x4 &cprev) {
         float gll, btl;  // lane t = lane % 32: g_t log2(e) and beta_t (neutral past Lc)
         {
             const int t = lane & 31;
@@ -416,8 +418,9 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 cmin = fminf(cmin, cp[j][e]);
                 cmax = fmaxf(cmax, cp[j][e]);
             }
-        // Operand planes. Row-major by token for XK, XQ, KD; by state row for KH.
-        float khv[TPT][4];
+        // Operand planes. Row-major by token for XK, XQ, KD; KH holds the same split values
+        // as KD, by state row (its bf16 halves regrouped by byte permutes).
+        uint2 dh[TPT], dl[TPT];
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = TPT * tg + j;
@@ -428,7 +431,6 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 vk[e] = cp[j][e] * kk;
                 vq[e] = cp[j][e] * (qf[j][e] * qs[j]);
                 vd[e] = kk * __builtin_amdgcn_rcpf(cp[j][e]);
-                khv[j][e] = clast[e] * vd[e];
             }
             uint2 h, l;
             const int off = t * XS + 4 * r;
@@ -438,28 +440,33 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             split4(vq, h, l);
             *reinterpret_cast<uint2 *>(xq_hi + off) = h;
             *reinterpret_cast<uint2 *>(xq_lo + off) = l;
-            split4(vd, h, l);
-            *reinterpret_cast<uint2 *>(kd_hi + off) = h;
-            *reinterpret_cast<uint2 *>(kd_lo + off) = l;
+            split4(vd, dh[j], dl[j]);
+            *reinterpret_cast<uint2 *>(kd_hi + off) = dh[j];
+            *reinterpret_cast<uint2 *>(kd_lo + off) = dl[j];
         }
+        // Row 4 r + e of KH: the bf16 of row e from each token's packed pair (e even: low
+        // halves, e odd: high halves).
+        auto regroup = [](const uint2 (&v)[TPT], int e, int j0) {
+            const uint32_t x1 = (e < 2) ? v[j0 + 1].x : v[j0 + 1].y, x0 = (e < 2) ? v[j0].x : v[j0].y;
+            return __builtin_amdgcn_perm(x1, x0, (e & 1) ? 0x07060302u : 0x05040100u);
+        };
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int off = (4 * r + e) * KS + TPT * tg;
             if constexpr (TPT == 4) {
-                uint2 h, l;
-                split4(f32x4{khv[0][e], khv[1][e], khv[2][e], khv[3][e]}, h, l);
-                *reinterpret_cast<uint2 *>(kh_hi + off) = h;
-                *reinterpret_cast<uint2 *>(kh_lo + off) = l;
+                *reinterpret_cast<uint2 *>(kh_hi + off) = make_uint2(regroup(dh, e, 0), regroup(dh, e, 2));
+                *reinterpret_cast<uint2 *>(kh_lo + off) = make_uint2(regroup(dl, e, 0), regroup(dl, e, 2));
             } else {
-                const uint32_t h = pack_bf16x2(khv[0][e], khv[1][e]);
-                const uint32_t l = pack_bf16x2(khv[0][e] - bf16_lo(h), khv[1][e] - bf16_hi(h));
-                *reinterpret_cast<uint32_t *>(kh_hi + off) = h;
-                *reinterpret_cast<uint32_t *>(kh_lo + off) = l;
+                *reinterpret_cast<uint32_t *>(kh_hi + off) = regroup(dh, e, 0);
+                *reinterpret_cast<uint32_t *>(kh_lo + off) = regroup(dl, e, 0);
             }
         }
+        // The state is kept as S' + sum_s (k_s / c_s) u_s^T, whose rows c_last scales into the
+        // true state: the next chunk's S' takes c_last (of this one) times its own d_0.
         if (tg == 0) {
             *reinterpret_cast<f32x4 *>(crow + 4 * r) = f32x4{clast[0], clast[1], clast[2], clast[3]};
-            *reinterpret_cast<f32x4 *>(d0row + 4 * r) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
+            *reinterpret_cast<f32x4 *>(d0row + 4 * r) =
+                f32x4{cprev[0] * d[0][0], cprev[1] * d[0][1], cprev[2] * d[0][2], cprev[3] * d[0][3]};
         }
         if (!(cmin >= kChunkLo && cmax <= kChunkHi)) {  // rare: find the first token out of range
             int first = kChunk;
@@ -475,8 +482,12 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     int chunk = 0;
     while (t0 < L) {  // uniform over the workgroup
         int Lc = len;
+        // c_last of the previous chunk for this thread's rows (1 before the first chunk);
+        // read once, since a second preparation pass rewrites crow
+        const f32x4 cprev = (chunk == 0 || tg != 0) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                                     : *reinterpret_cast<const f32x4 *>(crow + 4 * r);
         for (;;) {
-            prep(Lc);
+            prep(Lc, cprev);
             lds_barrier();
             const int c = *cut;
             if (c >= Lc) break;
@@ -629,16 +640,14 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                         pack_bf16x2(ov[tb][0][i], ov[tb][1][i]), rout, orow,
                         (uint32_t)((16 * tb + i) * a.Dv * 2), 0);
         }
-        // S = diag(c_last) S' + KH^T U, one 16x16x32 chain per block over the chunk's tokens
-        // (k slots: tokens 4 kg .. + 3 of U_0, then of U_1).
+        // S = S' + KH^T U (the true state is diag(c_last) S), one 16x16x32 chain per block
+        // over the chunk's tokens (k slots: tokens 4 kg .. + 3 of U_0, then of U_1).
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-            const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
             const int ra = (16 * rb + n16) * KS + 4 * kg;
             const bf16x8 ah = lds_pair8(kh_hi + ra, kh_hi + ra + 16), al = lds_pair8(kh_lo + ra, kh_lo + ra + 16);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                S[rb][c] = S[rb][c] * cr;
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, cat8(u0h[c], u1h[c]), S[rb][c], 0, 0, 0);
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, cat8(u0h[c], u1h[c]), S[rb][c], 0, 0, 0);
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, cat8(u0l[c], u1l[c]), S[rb][c], 0, 0, 0);
@@ -647,14 +656,16 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         t0 = t0n;
         len = lenn;
         ++chunk;
-        if (t0 == n) {  // the accepted prefix ends here: commit
+        if (t0 == n) {  // the accepted prefix ends here: commit diag(c_last) S
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
+            for (int rb = 0; rb < NRB; ++rb) {
+                const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     __builtin_amdgcn_raw_buffer_store_b32(
-                        pack_bf16x2(S[rb][0][i], S[rb][1][i]), rso, lane_off,
+                        pack_bf16x2(S[rb][0][i] * cr[i], S[rb][1][i] * cr[i]), rso, lane_off,
                         (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_STORE_POLICY);
+            }
         }
         lds_barrier();  // the next chunk's preparation reuses every LDS area
     }
