@@ -11,8 +11,7 @@
 
 namespace rgdr {
 
-// Tokens per decode call (the page's decode operator takes at most 8), and per run of the
-// long-sequence form, which walks longer items in runs of this many.
+// Tokens per decode call (the page's decode operator takes at most 8).
 constexpr int kMaxT = 8;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -209,20 +208,15 @@ struct Ops {
 
 // Issue the loads of one item's operands. Ranges cover only valid tokens, so padded tokens
 // are never read (lanes past the range receive zeros and move no data).
-//
-// The loads cover tokens t0 .. t0 + len - 1 of the item (len < 0: its L valid tokens from
-// token 0); the long-sequence form walks an item's tokens in such runs.
 template <int DK, int TV, int NT, int TMAX, int GATE>
 __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
-                                         Ops<DK, TV, NT, TMAX> &o, int tid, int t0 = 0,
-                                         int len = -1) {
+                                         Ops<DK, TV, NT, TMAX> &o, int tid) {
     using Sh = TileShape<DK, TV, NT, TMAX>;
-    const int n_tok = len < 0 ? m.L : len;
-    const size_t bhT = ((size_t)m.b * a.Hv + m.h) * a.T + t0;
-    const uint32_t L = (uint32_t)n_tok;
+    const size_t bhT = ((size_t)m.b * a.Hv + m.h) * a.T;
+    const uint32_t L = (uint32_t)m.L;
     const auto rgk = make_rsrc(a.gk + bhT * DK, L * DK * 4);
     const auto rg = make_rsrc(a.g + bhT, L * 4);
-    const size_t qk0 = (((size_t)m.b * a.Hq + m.hq) * a.T + t0) * DK;
+    const size_t qk0 = ((size_t)m.b * a.Hq + m.hq) * a.T * DK;
     const auto rk = make_rsrc(a.k + qk0, L * DK * 2);
     const auto rq = make_rsrc(a.q + qk0, L * DK * 2);
     const auto rv = make_rsrc(a.v + bhT * a.Dv, L * (uint32_t)a.Dv * 2);
@@ -234,7 +228,7 @@ __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
         if constexpr (GATE == kGateGiven)
             o.g[j] = __builtin_amdgcn_raw_buffer_load_b32(rg, (e * 4 / DK) * 4, 0, 0);
         else
-            o.g[j] = gate_raw(a, a.ga, GATE, m.b, t0 + e * 4 / DK, m.h, e * 4 / DK < n_tok);
+            o.g[j] = gate_raw(a, a.ga, GATE, m.b, e * 4 / DK, m.h, e * 4 / DK < m.L);
     }
 #pragma unroll
     for (int j = 0; j < Sh::KQV; ++j) {
@@ -252,7 +246,7 @@ __device__ __forceinline__ void load_ops(const DecodeArgs &a, const Item &m,
     if constexpr (GATE == kGateGiven) {
         o.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, tid * 2, 0, 0);
     } else {
-        o.beta = gate_raw(a, a.gb, GATE, m.b, t0 + tid, m.h, tid < n_tok);
+        o.beta = gate_raw(a, a.gb, GATE, m.b, tid, m.h, tid < m.L);
         gate_head(a, m.h, o.dt, o.ds);
     }
 }
@@ -369,57 +363,6 @@ __device__ __forceinline__ bf16x8 lds_pair8(const uint16_t *p0, const uint16_t *
     return __builtin_bit_cast(bf16x8, u32x4{u.x, u.y, v.x, v.y});
 }
 
-// Decay range inside which a run's 8 x 8 matrices M and N (the chunk form's closed form) are
-// formed on the matrix cores from the factors c_t k_t (or c_t scale q_t) and k_s / c_s: every
-// c_t of the run within [2^-48, 2^48] keeps both factors and their products far from fp32
-// overflow. A wave with a row outside it forms its rows' share of the matrices directly,
-// from products of the decays between s and t.
-constexpr float kGramLo = 0x1p-48f, kGramHi = 0x1p48f;
-
-// M[t][s] (s < t) and N[t][s] (s <= t) into this wave's tables gsM[t * 8 + s], gsN[t * 8 + s]:
-// the factored products on the matrix cores, XT rows 0..7 (c_t k_t) and 8..15 (c_t scale
-// q_t) against KC rows s = 0..7 (k_s / c_s), high parts and remainders (three products),
-// plus the rows' direct shares in gpart[2][64] (entry e = 8 s + t of M, 8 t + s of N; zero
-// where a wave's rows took the factored form). XT and KC are [rows][XS] bf16, one row per
-// token, D_k columns; lane (kg, n16) ends with G[4 kg + i][n16]. Entries outside s < t
-// (M) and s <= t (N) are written but never read.
-template <int DK, int XS>
-__device__ __forceinline__ void gram_tables(const uint16_t *xt_hi, const uint16_t *xt_lo,
-                                            const uint16_t *kc_hi, const uint16_t *kc_lo,
-                                            const float *gpart, float *gsM, float *gsN, int n16,
-                                            int kg) {
-    f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool tok = n16 < 8;  // KC has rows for tokens 0..7 only; the other columns are zero
-    const int s8 = n16 & 7;
-#pragma unroll
-    for (int pb = 0; pb < DK / 32; ++pb) {
-        const int r0 = 32 * pb + 4 * kg;
-        const bf16x8 ah = lds_pair8(xt_hi + n16 * XS + r0, xt_hi + n16 * XS + r0 + 16);
-        const bf16x8 al = lds_pair8(xt_lo + n16 * XS + r0, xt_lo + n16 * XS + r0 + 16);
-        bf16x8 bh = lds_pair8(kc_hi + s8 * XS + r0, kc_hi + s8 * XS + r0 + 16);
-        bf16x8 bl = lds_pair8(kc_lo + s8 * XS + r0, kc_lo + s8 * XS + r0 + 16);
-        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-        bh = tok ? bh : __builtin_bit_cast(bf16x8, zero);
-        bl = tok ? bl : __builtin_bit_cast(bf16x8, zero);
-        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, g, 0, 0, 0);
-        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, g, 0, 0, 0);
-        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, g, 0, 0, 0);
-    }
-    if (tok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mrow = 4 * kg + i;
-            if (mrow < 8) {
-                const int e = n16 * 8 + mrow;  // M[mrow][n16]
-                gsM[mrow * 8 + n16] = g[i] + gpart[e] + gpart[64 + e];
-            } else {
-                const int t = mrow - 8, e = t * 8 + n16;  // N[t][n16]
-                gsN[t * 8 + n16] = g[i] + gpart[e] + gpart[64 + e];
-            }
-        }
-    }
-}
-
 // Operand staging of the chunk form (128 threads, D_k = 64 or 128, 128-column tiles).
 // Planar per token: the row decays d [8][D_k], k [8][D_k] and scale q [8][D_k], then the
 // tile's v [8][128] and beta [8]. Each thread writes whole 16-byte runs of consecutive rows, so the
@@ -435,9 +378,10 @@ constexpr int chunk_vbase() { return 24 * DK > 128 * kChunkYS ? 24 * DK : 128 * 
 template <int DK>
 constexpr int chunk_ops() { return chunk_vbase<DK>() + 8 * 128 + 16; }  // floats, 16-B multiple
 
-template <int DK, int GATE, int NT = 128>
-__device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, NT, kMaxT> &o, float *ob,
+template <int DK, int GATE>
+__device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, 128, kMaxT> &o, float *ob,
                                                 float scale, bool norm, int L, int tid) {
+    constexpr int NT = 128;
     using Sh = TileShape<DK, 128, NT, kMaxT>;
     constexpr int TV = 128;
     float *sd = ob, *sk = ob + 8 * DK, *sq = ob + 16 * DK, *sv = ob + chunk_vbase<DK>();
@@ -494,7 +438,6 @@ __device__ __forceinline__ void chunk_stage_ops(const Ops<DK, 128, NT, kMaxT> &o
     for (int j = 0; j < Sh::VV; ++j) {
         const int e = tid + j * NT;
         const int t = e / (TV / 8), c8 = e % (TV / 8);
-        if (NT > 128 && t >= kMaxT) continue;  // only with more threads than values
         f32x4 *dst = reinterpret_cast<f32x4 *>(sv + t * TV + c8 * 8);
         dst[0] = f32x4{bf16_lo(o.v[j].x), bf16_hi(o.v[j].x), bf16_lo(o.v[j].y), bf16_hi(o.v[j].y)};
         dst[1] = f32x4{bf16_lo(o.v[j].z), bf16_hi(o.v[j].z), bf16_lo(o.v[j].w), bf16_hi(o.v[j].w)};
