@@ -228,6 +228,16 @@ def test_prefill_extreme_decays(rg, case):
                        atol=2e-2 + 1e-4 * np.abs(r).max())
 
 
+def test_prefill_long_sequence(rg):
+    """4096 tokens (128 chunks of 32) with ragged lengths and an accepted prefix deep in the
+    sequence: errors do not accumulate past the bar over a long walk."""
+    inp = workloads.make_case(2, 1, 2, 4096, 128, 128, 3, seed=7921, indices="choice",
+                              lengths=[4096, 3001])
+    inp.num_accepted_tokens = np.array([4096, 2777], np.int32)
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), "prefill T=4096")
+
+
 @pytest.mark.parametrize("g_val", [-7.0, -2.6])
 def test_prefill_many_short_chunks(rg, g_val):
     """Decays strong enough that a chunk's decay products leave the factored range after
