@@ -22,7 +22,7 @@
 // The two products with S' and the rank-32 update are matrix-core products on the state's
 // own accumulator registers; M and N are matrix-core products of the factors c_t k_t (or
 // c_t scale q_t) and k_s / c_s; the 32 x 32 triangular system is solved blockwise: the two
-// 16 x 16 diagonal blocks are inverted by forward substitution in fp32 on one wave, and
+// 16 x 16 diagonal blocks are inverted by forward substitution in fp32 (one wave each), and
 //   U_0 = A_00 R_0,   U_1 = A_11 (R_1 - M_10 U_0),   A_bb = (I + diag(beta) M_bb)^-1 diag(beta)
 // are matrix-core products. Every fp32 operand of a matrix-core product is split into a bf16
 // high part and a bf16 remainder and three products are summed (high x high, low x high,

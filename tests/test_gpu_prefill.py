@@ -29,12 +29,12 @@ def rg():
 
 # B, Hq, Hv, T, Dk, Dv, N_slots; lengths U{1..T}
 SHAPES = [
-    (3, 2, 4, 16, 128, 128, 5),     # two full runs of 8
+    (3, 2, 4, 16, 128, 128, 5),     # half a chunk
     (4, 2, 4, 64, 128, 256, 6),     # two tiles per head
-    (2, 1, 2, 512, 128, 128, 3),    # 64 runs
+    (2, 1, 2, 512, 128, 128, 3),    # 16 chunks
     (3, 1, 3, 40, 64, 192, 4),      # D_k = 64, a last tile of 64 columns
     (2, 4, 4, 33, 64, 512, 3),      # the example page's head size
-    (5, 4, 8, 9, 128, 64, 7),       # T = 9 (a run of 8 and one of 1); every tile half
+    (5, 4, 8, 9, 128, 64, 7),       # T = 9; every tile half
     (2, 1, 1, 3, 128, 128, 2),      # T < 8 is accepted too
     (2, 2, 2, 20, 128, 4096, 3),    # the largest D_v
 ]
