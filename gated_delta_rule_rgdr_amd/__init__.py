@@ -9,6 +9,8 @@ fallback: if the library is missing, the first call of any binding function rais
   "lite_boost.ops.recurrent_gated_delta_rule"), in place on a bf16 state pool.
 * ``recurrent_gated_delta_rule`` -- the page's functional form: returns ``(out, state_out)``
   and leaves ``state`` untouched.
+* ``rgdr_decode_snapshots`` -- ``rgdr_decode`` that also returns the state after every
+  token (speculative decoding: the state of each candidate accepted prefix).
 * ``rgdr_decode_gated`` -- the decode step with the gate front end fused in: takes the raw
   gate projections instead of g and beta.
 * ``rgdr_prefill`` / ``rgdr_prefill_gated`` -- the same recurrence over long sequences
@@ -28,7 +30,7 @@ import os
 
 import torch
 
-__all__ = ["rgdr_decode", "rgdr_decode_gated", "rgdr_prefill", "rgdr_prefill_gated",
+__all__ = ["rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated", "rgdr_prefill", "rgdr_prefill_gated",
            "recurrent_gated_delta_rule", "la_gate",
            "rgdr_validate", "VALIDATE",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
@@ -58,6 +60,8 @@ def library():
     vp, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
     lib.rgdr_decode.restype = C.c_int
     lib.rgdr_decode.argtypes = [vp] * 10 + [f32] + [i32] * 7 + [vp, vp, vp]
+    lib.rgdr_decode_snapshots.restype = C.c_int
+    lib.rgdr_decode_snapshots.argtypes = [vp] * 10 + [f32] + [i32] * 7 + [vp, vp, vp, vp]
     lib.rgdr_decode_gated.restype = C.c_int
     lib.rgdr_decode_gated.argtypes = ([vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7
                                       + [vp] * 2 + [C.c_uint32, vp])
@@ -140,6 +144,38 @@ def rgdr_decode(query, key, value, beta, state_pool, actual_seq_lengths, ssm_sta
                        stream)
 
 
+def rgdr_decode_snapshots(query, key, value, beta, state_pool, actual_seq_lengths,
+                          ssm_state_indices, g, gk, num_accepted_tokens, scale=1.0, *,
+                          out=None, state_out=None, state_snapshots=None, stream=None):
+    """``rgdr_decode`` that also stores the state after every token; returns
+    ``(out, state_out, state_snapshots)``.
+
+    ``state_snapshots``: bf16 ``[B, T, H_v, D_k, D_v]``, allocated (uninitialised) if not
+    given. Entry ``[b, t]`` is written for ``t`` below the clamped length of entry ``b`` when
+    its slot is valid, and holds the state after its first ``t + 1`` tokens; other entries
+    keep what the buffer held.
+    """
+    if not isinstance(query, torch.Tensor) or not isinstance(value, torch.Tensor) \
+            or not isinstance(state_pool, torch.Tensor):
+        raise TypeError("query, value and state_pool must be torch.Tensor")
+    if query.dim() != 4 or value.dim() != 4 or state_pool.dim() != 4:
+        raise RuntimeError("query, value and state_pool must have 4 dimensions")
+    B, _, T, Dk = query.shape
+    Hv, Dv = value.shape[1], value.shape[3]
+    if state_snapshots is None:
+        state_snapshots = torch.empty((B, T, Hv, Dk, Dv), dtype=torch.bfloat16,
+                                      device=query.device)
+    else:
+        _dev(state_snapshots, "state_snapshots", torch.bfloat16, 5)
+        if tuple(state_snapshots.shape) != (B, T, Hv, Dk, Dv):
+            raise RuntimeError("state_snapshots must be [B, T, H_v, D_k, D_v]")
+    out, state_out = _plain_call("rgdr_decode_snapshots", query, key, value, beta, state_pool,
+                                 actual_seq_lengths, ssm_state_indices, g, gk,
+                                 num_accepted_tokens, scale, out, state_out, stream,
+                                 extra=(state_snapshots,))
+    return out, state_out, state_snapshots
+
+
 def rgdr_prefill(query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
                  g, gk, num_accepted_tokens, scale=1.0, *, out=None, state_out=None,
                  stream=None):
@@ -151,7 +187,7 @@ def rgdr_prefill(query, key, value, beta, state_pool, actual_seq_lengths, ssm_st
 
 
 def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
-                g, gk, num_accepted_tokens, scale, out, state_out, stream):
+                g, gk, num_accepted_tokens, scale, out, state_out, stream, extra=()):
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
     B, Hq, T, Dk = query.shape
@@ -188,7 +224,7 @@ def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm
     _same_device(query, key=key, value=value, beta=beta, state_pool=state_pool,
                  actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
                  g=g, gk=gk, num_accepted_tokens=num_accepted_tokens, out=out,
-                 state_out=state_out)
+                 state_out=state_out, **{f"extra{i}": t for i, t in enumerate(extra)})
     if VALIDATE:
         _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
@@ -197,7 +233,8 @@ def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm
                               actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
                               g.data_ptr(), gk.data_ptr(), num_accepted_tokens.data_ptr(),
                               float(scale), B, Hq, Hv, T, Dk, Dv, N, out.data_ptr(),
-                              state_out.data_ptr(), _stream_handle(stream, query.device))
+                              state_out.data_ptr(), *[t.data_ptr() for t in extra],
+                              _stream_handle(stream, query.device))
     _check(rc, fn)
     return out, state_out
 

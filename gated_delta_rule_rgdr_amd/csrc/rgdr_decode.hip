@@ -518,9 +518,10 @@ __device__ __forceinline__ void spread32(const float (&in)[4], float (&out)[8]) 
 // Second staging pass of the multi-token form: rewrite each row's (d, k, scale q) of every
 // token as (c k, c scale q, k / c, fold multiplier), with c the running decay described
 // above, and store per token the scalar k.(scale q) and whether the token folds. cc
-// receives each row's c after token n - 1 (the commit). Lane l owns rows l and l + 64.
-template <int DK, int TV>
-__device__ __forceinline__ void scale_ops(float *ob, float *cc, int L, int n, int lane) {
+// receives each row's c after token n - 1 (the commit), and cs (with SNAP) each row's c
+// after every token, [t][D_k]. Lane l owns rows l and l + 64.
+template <int DK, int TV, bool SNAP = false>
+__device__ __forceinline__ void scale_ops(float *ob, float *cc, float *cs, int L, int n, int lane) {
     using Sh = TileShape<DK, TV, 64, kMaxT>;
     constexpr int RL = DK / 64;
     float c[RL];
@@ -556,10 +557,14 @@ __device__ __forceinline__ void scale_ops(float *ob, float *cc, int L, int n, in
 #pragma unroll
             for (int j = 0; j < RL; ++j) cc[lane + 64 * j] = c[j];
         }
+        if constexpr (SNAP) {
+#pragma unroll
+            for (int j = 0; j < RL; ++j) cs[t * DK + lane + 64 * j] = c[j];
+        }
     }
 }
 
-template <int DK, int TV, int GATE>
+template <int DK, int TV, int GATE, bool SNAP = false>
 __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
@@ -568,10 +573,12 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
     static_assert(R * Sh::CPL <= 128, "fp32 tile per lane");
     static_assert(DK == 64 || DK == 128, "rows per lane in scale_ops");
     static_assert(LPR == 8 || LPR == 16, "transposed reduction");
-    // per token: rows (4 floats) | v[TV] | beta, k.(scale q), fold flag, pad; then cc[DK]
-    __shared__ f32x4 lds4[(Sh::OPS + DK) / 4];
+    // per token: rows (4 floats) | v[TV] | beta, k.(scale q), fold flag, pad; then cc[DK];
+    // with SNAP, each row's c after every token [kMaxT][DK]
+    __shared__ f32x4 lds4[(Sh::OPS + DK + (SNAP ? kMaxT * DK : 0)) / 4];
     float *ob = reinterpret_cast<float *>(lds4);
     float *cc = ob + Sh::OPS;
+    float *cs = cc + DK;
     const Index x{lens, idx, nacc};
     const int lane = threadIdx.x;
     const int cg = lane % LPR, rg = lane / LPR;
@@ -583,7 +590,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
     u32x4 raw[R];
     load_state<DK, TV, 64>(a, m, raw, rg, cg);
     stage_ops<DK, TV, 64, kMaxT, GATE>(o, ob, a.scale, a.norm_qk != 0, lane);
-    scale_ops<DK, TV>(ob, cc, m.L, m.n, lane);
+    scale_ops<DK, TV, SNAP>(ob, cc, cs, m.L, m.n, lane);
 
     const auto rso = make_rsrc(a.pool_out + (m.state ? tile_base<DK, TV>(a, m) : 0),
                                tile_range<DK, TV>(a, m));
@@ -669,6 +676,21 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
             const float kc = tb[4 * (rg + RPP * r) + 2];
 #pragma unroll
             for (int c = 0; c < 8; ++c) S[r][c] = fmaf(kc, U[c], S[r][c]);
+        }
+        if constexpr (SNAP) {  // the state after token t: c St, as the commit below
+            const size_t sb = (((size_t)m.b * a.T + t) * a.Hv + m.h) * DK * a.Dv +
+                              (size_t)m.tile * TV;
+            const auto rsn = make_rsrc(a.snap + sb, (uint32_t)(DK * a.Dv - m.tile * TV) * 2);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float cr = cs[t * DK + rg + RPP * r];
+                store16<RGDR_STATE_STORE_POLICY>(
+                    u32x4{pack_bf16x2(S[r][0] * cr, S[r][1] * cr),
+                          pack_bf16x2(S[r][2] * cr, S[r][3] * cr),
+                          pack_bf16x2(S[r][4] * cr, S[r][5] * cr),
+                          pack_bf16x2(S[r][6] * cr, S[r][7] * cr)},
+                    rsn, lane_off + r * row_step);
+            }
         }
         if (t + 1 == m.n) {  // the accepted prefix ends here: commit c St
 #pragma unroll
@@ -1158,8 +1180,15 @@ template <int DK, int TV, int GATE>
 static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
                                     const int32_t *idx, const int32_t *nacc,
                                     hipStream_t stream) {
-    hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE>), dim3(a.n_items), dim3(64), 0,
-                       stream, a, lens, idx, nacc);
+    if constexpr (GATE == kGateGiven) {  // per-token states: rgdr_decode_snapshots only
+        if (a.snap) {
+            hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE, true>), dim3(a.n_items),
+                               dim3(64), 0, stream, a, lens, idx, nacc);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE, false>), dim3(a.n_items),
+                       dim3(64), 0, stream, a, lens, idx, nacc);
     return hipGetLastError();
 }
 
@@ -1217,13 +1246,16 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
     if ((D_k != 64 && D_k != 128) || D_v % 64 != 0 || D_v > 4096) return RGDR_ERR_UNSUPPORTED;
     if (!aligned(a.v, 16) || !aligned(a.pool, 16) || !aligned(a.out, 16) ||
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
-        !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
+        !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4) ||
+        !aligned(a.snap, 16))
         return RGDR_ERR_ALIGN;
     const bool chunk = RGDR_CHUNK_FORM && T >= RGDR_CHUNK_MIN_T &&
                        (D_k == 128 || (RGDR_CHUNK_DK64 && T >= RGDR_CHUNK_DK64_MIN_T)) &&
                        (D_v % 128 == 0 ||
                         (RGDR_CHUNK_HALF_TILE && (D_v > 64 || T >= RGDR_CHUNK_DV64_MIN_T)));
-    const Form form = T == 1 ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;
+    // Per-token states exist only in the per-token form, which serves every T then.
+    const Form form = a.snap ? kFormWaveMulti : T == 1 ? kFormWave : chunk ? kFormChunk
+                                                                   : kFormWaveMulti;
     // Tile widths. For the multi-token form, the widest tile whose fp32 copy fits a lane
     // (D_k x TV <= 64 x 128 values per wave). For T = 1, 64-column tiles while the whole call
     // then fits in one launch of the resident grid: twice the waves, each with half the
@@ -1286,6 +1318,35 @@ extern "C" rgdr_status rgdr_decode(const void *query, const void *key, const voi
     a.gk = gk;
     a.out = static_cast<uint16_t *>(out);
     a.pool_out = static_cast<uint16_t *>(state_out);
+    a.scale = scale;
+    return decode_entry(a, kGateGiven, B, H_q, H_v, T, D_k, D_v, N_slots, actual_seq_lengths,
+                        ssm_state_indices, num_accepted_tokens, stream);
+}
+
+extern "C" rgdr_status rgdr_decode_snapshots(
+    const void *query, const void *key, const void *value, const void *beta,
+    const void *state_pool, const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+    const float *g, const float *gk, const int32_t *num_accepted_tokens, float scale,
+    int32_t B, int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
+    void *out, void *state_out, void *state_snapshots, hipStream_t stream) {
+    using namespace rgdr;
+    if (B == 0) return RGDR_OK;
+    if (!query || !key || !value || !beta || !state_pool || !actual_seq_lengths ||
+        !ssm_state_indices || !g || !gk || !num_accepted_tokens || !out || !state_out ||
+        !state_snapshots)
+        return RGDR_ERR_NULL;
+    if (!aligned(beta, 2) || !aligned(g, 4)) return RGDR_ERR_ALIGN;
+    DecodeArgs a = {};
+    a.q = static_cast<const uint16_t *>(query);
+    a.k = static_cast<const uint16_t *>(key);
+    a.v = static_cast<const uint16_t *>(value);
+    a.beta = static_cast<const uint16_t *>(beta);
+    a.pool = static_cast<const uint16_t *>(state_pool);
+    a.g = g;
+    a.gk = gk;
+    a.out = static_cast<uint16_t *>(out);
+    a.pool_out = static_cast<uint16_t *>(state_out);
+    a.snap = static_cast<uint16_t *>(state_snapshots);
     a.scale = scale;
     return decode_entry(a, kGateGiven, B, H_q, H_v, T, D_k, D_v, N_slots, actual_seq_lengths,
                         ssm_state_indices, num_accepted_tokens, stream);

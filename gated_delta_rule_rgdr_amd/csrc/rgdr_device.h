@@ -60,6 +60,8 @@ struct DecodeArgs {
     // T = 1 wave form: ticks of the constant wall clock (s_memrealtime) each wave waits,
     // counted from its own start, before it writes its tile back; 0 = no wait.
     int hold;
+    // Per-token states [B, T, H_v, D_k, D_v] bf16 (rgdr_decode_snapshots only).
+    uint16_t *snap;
 };
 
 // How an item's g and beta arrive: given (bf16 beta, fp32 g), or computed from raw gate

@@ -12,6 +12,7 @@
  *                  2. read    kv = S^T k_t
  *                  3. update  S = S + k_t (x) ((v_t - kv) * beta[t])   (outer product)
  *                  4. output  o_t = S^T (q_t * scale)
+ *                rgdr_decode_snapshots also stores S after every token.
  *   rgdr_prefill The same recurrence over long sequences (T up to 65536): the page's notes
  *                limit the decode operator to T <= 8 and hand the parallel prefill to a
  *                chunk-level operator; this is that operator, with rgdr_decode's arguments.
@@ -108,6 +109,33 @@ rgdr_status rgdr_decode(const void *query, const void *key, const void *value,
                         float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
                         int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
                         void *state_out, hipStream_t stream);
+
+/*
+ * rgdr_decode_snapshots -- rgdr_decode that also stores the state after every token.
+ * The page's num_accepted_tokens parameter serves speculative decoding: a step evaluates
+ * T drafted tokens and commits the state after the accepted prefix. A caller that learns
+ * the accepted count only after the step needs the state after each candidate prefix;
+ * this call writes all of them in the same pass.
+ *
+ *   state_snapshots  bf16 [B, T, H_v, D_k, D_v], 16-byte aligned, owned by the caller.
+ *                    Entry (b, t, h) receives the state of value head h of batch entry b
+ *                    after its first t + 1 tokens (after step 3 of token t), rounded as the
+ *                    committed state is, for every t below the clamped length L of entry b
+ *                    whose slot is valid. Other entries (t >= L, skipped entries) are not
+ *                    written. With n = num_accepted_tokens[b] >= 1, entry (b, n - 1) holds
+ *                    the same bytes as the committed slot.
+ *   All other arguments, results and errors: as rgdr_decode (RGDR_ERR_NULL also for
+ *   state_snapshots, RGDR_ERR_ALIGN for its alignment). Every T <= 8 runs the per-token
+ *   form; the snapshots add B * T * H_v * D_k * D_v * 2 bytes of HBM writes.
+ */
+rgdr_status rgdr_decode_snapshots(const void *query, const void *key, const void *value,
+                                  const void *beta, const void *state_pool,
+                                  const int32_t *actual_seq_lengths,
+                                  const int32_t *ssm_state_indices, const float *g,
+                                  const float *gk, const int32_t *num_accepted_tokens,
+                                  float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                  int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                                  void *state_out, void *state_snapshots, hipStream_t stream);
 
 /*
  * rgdr_decode_gated -- rgdr_decode with the gate front end fused in: instead of g and beta,

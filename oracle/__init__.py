@@ -52,6 +52,10 @@ def _bind(lib):
     lib.oracle_rgdr_bf16.argtypes = (
         [_u16p, _u16p, _u16p, _u16p, _u16p, _i32p, _i32p, _f32p, _f32p, _i32p, C.c_float]
         + ints + [_f64p, _u16p, C.c_void_p, C.c_int])
+    lib.oracle_rgdr_bf16_snapshots.restype = C.c_int
+    lib.oracle_rgdr_bf16_snapshots.argtypes = (
+        [_u16p, _u16p, _u16p, _u16p, _u16p, _i32p, _i32p, _f32p, _f32p, _i32p, C.c_float]
+        + ints + [_f64p, _u16p, C.c_void_p, _f64p])
     lib.oracle_rgdr_f64.restype = C.c_int
     lib.oracle_rgdr_f64.argtypes = (
         [_f64p, _f64p, _f64p, _f64p, _f64p, _i32p, _i32p, _f64p, _f64p, _i32p, C.c_double]
@@ -142,6 +146,31 @@ class Oracle:
             raise RuntimeError(f"oracle_rgdr_bf16 failed with code {rc}")
         return out, state_out, rows
 
+    def rgdr_bf16_snapshots(self, query, key, value, beta, state_pool, actual_seq_lengths,
+                            ssm_state_indices, g, gk, num_accepted_tokens, scale_value=1.0):
+        """``rgdr_bf16`` plus the state after every token: returns
+        ``(out, state_out, rows, snaps)`` with ``snaps`` fp64 ``[B, T, H_v, D_k, D_v]``, entry
+        (b, t) the unrounded state after the first t + 1 tokens of entry b, for t below its
+        clamped length and a valid slot (NaN elsewhere)."""
+        B, Hq, Hv, T, Dk, Dv, N_slots = _dims(query, value, state_pool)
+        out = np.full((B, Hv, T, Dv), np.nan)
+        state_out = np.array(state_pool, dtype=np.uint16, copy=True, order="C")
+        rows = np.full((B, Hv, Dk, Dv), np.nan)
+        snaps = np.full((B, T, Hv, Dk, Dv), np.nan)
+        rc = self.lib.oracle_rgdr_bf16_snapshots(
+            np.ascontiguousarray(query, np.uint16), np.ascontiguousarray(key, np.uint16),
+            np.ascontiguousarray(value, np.uint16), np.ascontiguousarray(beta, np.uint16),
+            np.ascontiguousarray(state_pool, np.uint16),
+            np.ascontiguousarray(actual_seq_lengths, np.int32),
+            np.ascontiguousarray(ssm_state_indices, np.int32),
+            np.ascontiguousarray(g, np.float32), np.ascontiguousarray(gk, np.float32),
+            np.ascontiguousarray(num_accepted_tokens, np.int32),
+            float(np.float32(scale_value)), B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out,
+            rows.ctypes.data, snaps)
+        if rc != 0:
+            raise RuntimeError(f"oracle_rgdr_bf16_snapshots failed with code {rc}")
+        return out, state_out, rows, snaps
+
     def rgdr_f64(self, query, key, value, beta, state_pool, actual_seq_lengths,
                  ssm_state_indices, g, gk, num_accepted_tokens, scale_value=1.0, *,
                  normalize_qk=False):
@@ -221,6 +250,10 @@ def f64_to_bf16(x):
 
 def rgdr_bf16(*args, **kw):
     return default().rgdr_bf16(*args, **kw)
+
+
+def rgdr_bf16_snapshots(*args, **kw):
+    return default().rgdr_bf16_snapshots(*args, **kw)
 
 
 def rgdr_f64(*args, **kw):

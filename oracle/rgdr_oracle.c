@@ -138,11 +138,12 @@ static double rd(const void *p, int ty, size_t i)
  * q, k   : [T][D_k] (this pair's query/key head); v: [T][D_v]; beta, g: [T];
  * gk     : [T][D_k]; out: [T][D_v] (rows t >= L are set to zero).
  * kv, u  : D_v-long scratch.
+ * snap   : NULL, or where S after token t (t < L) goes: snap + t * snap_stride.
  */
 static void gdr_pair(double *S, double *Scommit, int L, int n, int T, int Dk, int Dv,
                      const double *q, const double *k, const double *v, const double *beta,
                      const double *g, const double *gk, double scale, double *out,
-                     double *kv, double *u)
+                     double *kv, double *u, double *snap, size_t snap_stride)
 {
     size_t nS = (size_t)Dk * Dv;
     if (n == 0)
@@ -182,6 +183,8 @@ static void gdr_pair(double *S, double *Scommit, int L, int n, int T, int Dk, in
         }
         if (t + 1 == n)
             memcpy(Scommit, S, nS * sizeof(double));
+        if (snap)
+            memcpy(snap + (size_t)t * snap_stride, S, nS * sizeof(double));
     }
     for (int t = L; t < T; ++t)
         for (int j = 0; j < Dv; ++j)
@@ -214,6 +217,7 @@ typedef struct {
     void *pool_out; int pool_out_ty;       /* [N_slots, H_v, D_k, D_v]; may alias pool */
     double *rows_out;                      /* optional [B, H_v, D_k, D_v], unrounded */
     int normalize_qk;                      /* nonzero: L2-normalise q and k per token */
+    double *snap_out;                      /* optional [B, T, H_v, D_k, D_v], unrounded */
 } rgdr_args;
 
 static int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -278,7 +282,9 @@ static int rgdr_drive(const rgdr_args *a)
             }
             for (size_t e = 0; e < nS; ++e)
                 S[e] = rd(a->pool, a->pool_ty, so + e);
-            gdr_pair(S, Sc, L, n, T, Dk, Dv, q, k, v, beta, g, gk, a->scale, out, kv, u);
+            double *snap = a->snap_out ? a->snap_out + ((size_t)b * T * a->Hv + h) * nS : NULL;
+            gdr_pair(S, Sc, L, n, T, Dk, Dv, q, k, v, beta, g, gk, a->scale, out, kv, u,
+                     snap, (size_t)a->Hv * nS);
             /* commit slot ssm_state_indices[b]; the returned state feeds the next call */
             if (a->pool_out_ty == TY_BF16) {
                 uint16_t *po = (uint16_t *)a->pool_out + so;
@@ -314,7 +320,30 @@ int oracle_rgdr_bf16(const uint16_t *query, const uint16_t *key, const uint16_t 
     rgdr_args a = {query, key, value, beta, g, gk, TY_BF16, TY_BF16, TY_BF16, TY_BF16,
                    TY_F32, TY_F32, pool, TY_BF16, lens, idx, nacc, (double)scale,
                    B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_BF16, rows_out,
-                   normalize_qk};
+                   normalize_qk, NULL};
+    return rgdr_drive(&a);
+}
+
+/*
+ * oracle_rgdr_bf16, and the state after each token: snap_out [B, T, H_v, D_k, D_v]
+ * receives, for every batch entry b with a valid slot and every t < L_b (the clamped
+ * length), the state after its first t + 1 tokens, unrounded; other entries are not
+ * written. The page's num_accepted_tokens commits one such state; these are all of them.
+ */
+int oracle_rgdr_bf16_snapshots(const uint16_t *query, const uint16_t *key,
+                               const uint16_t *value, const uint16_t *beta,
+                               const uint16_t *pool, const int32_t *lens, const int32_t *idx,
+                               const float *g, const float *gk, const int32_t *nacc,
+                               float scale, int B, int Hq, int Hv, int T, int Dk, int Dv,
+                               int N_slots, double *out, uint16_t *state_out,
+                               double *rows_out, double *snap_out)
+{
+    if (!snap_out)
+        return 1;
+    rgdr_args a = {query, key, value, beta, g, gk, TY_BF16, TY_BF16, TY_BF16, TY_BF16,
+                   TY_F32, TY_F32, pool, TY_BF16, lens, idx, nacc, (double)scale,
+                   B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_BF16, rows_out,
+                   0, snap_out};
     return rgdr_drive(&a);
 }
 
@@ -329,7 +358,7 @@ int oracle_rgdr_f64(const double *query, const double *key, const double *value,
     rgdr_args a = {query, key, value, beta, g, gk, TY_F64, TY_F64, TY_F64, TY_F64,
                    TY_F64, TY_F64, pool, TY_F64, lens, idx, nacc, scale,
                    B, Hq, Hv, T, Dk, Dv, N_slots, out, state_out, TY_F64, NULL,
-                   normalize_qk};
+                   normalize_qk, NULL};
     return rgdr_drive(&a);
 }
 

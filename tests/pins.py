@@ -456,6 +456,70 @@ def pin_bf16_api_matches_core(o):
     assert np.array_equal(pool_b, o.f64_to_bf16(pool_f))
 
 
+def _bf16_case(rng, B, Hq, Hv, T, Dk, Dv, N, lens, nacc, zero_state=False):
+    """An f64 case rounded to bf16 storage (the bf16 entry point's inputs)."""
+    c = f64_case(rng, B, Hq, Hv, T, Dk, Dv, N, lens=lens, zero_state=zero_state)
+    to_bits = lambda x: torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16).copy()
+    return dict(query=to_bits(c["query"]), key=to_bits(c["key"]), value=to_bits(c["value"]),
+                beta=to_bits(c["beta"]), state_pool=to_bits(c["state_pool"]),
+                actual_seq_lengths=c["actual_seq_lengths"],
+                ssm_state_indices=c["ssm_state_indices"], g=c["g"].astype(np.float32),
+                gk=c["gk"].astype(np.float32), num_accepted_tokens=np.asarray(nacc, np.int32),
+                scale_value=float(np.float32(c["scale_value"])))
+
+
+def pin_snapshots_prefix(o):
+    """The state after token t is the state a call commits when it accepts t + 1 tokens
+    (num_accepted_tokens marks the accepted prefix): snapshot (b, t) equals, bit for bit,
+    the committed state of the same call with num_accepted_tokens = t + 1, for every t below
+    the clamped length; snapshot (b, n - 1) is the call's own committed state; entries past
+    the length or of a skipped slot are left unwritten; out and state_out are those of the
+    call without snapshots."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hv, T, Dk, Dv, N = 4, 2, 4, 6, 5, 3, 5
+    c = _bf16_case(rng, B, Hq, Hv, T, Dk, Dv, N, lens=[6, 4, 9, 0], nacc=[2, 4, 5, 0])
+    c["ssm_state_indices"] = np.array([3, 0, 1, -1], np.int32)
+    out, st, rows, snaps = o.rgdr_bf16_snapshots(**c)
+    out2, st2, rows2 = o.rgdr_bf16(**c, want_rows=True)
+    bits_equal(out, out2)
+    assert np.array_equal(st, st2)
+    lens = np.clip(c["actual_seq_lengths"], 0, T)
+    for b in range(3):
+        bits_equal(snaps[b, c["num_accepted_tokens"][b] - 1], rows2[b])
+        for t in range(T):
+            if t < lens[b]:
+                a = dict(c)
+                a["num_accepted_tokens"] = np.array([min(t + 1, L) for L in lens], np.int32)
+                _, _, r = o.rgdr_bf16(**a, want_rows=True)
+                bits_equal(snaps[b, t], r[b])
+            else:
+                assert np.isnan(snaps[b, t]).all()
+    assert np.isnan(snaps[3]).all()  # skipped slot, zero length
+
+
+def pin_snapshots_zero_state_closed_form(o):
+    """S0 = 0, two tokens: the state after token 0 is beta_0 k_0 (x) v_0 whatever the
+    decay; after token 1 it is D S_1 + k_1 (x) beta_1 (v_1 - (D S_1)^T k_1) with
+    D = diag(exp(g_1) exp(gk_1))."""
+    rng = np.random.default_rng(23)
+    B, H, T, Dk, Dv, N = 2, 2, 2, 6, 4, 2
+    c = _bf16_case(rng, B, H, H, T, Dk, Dv, N, lens=[2, 2], nacc=[2, 2], zero_state=True)
+    _, _, _, snaps = o.rgdr_bf16_snapshots(**c)
+    dec = lambda x: torch.from_numpy(np.asarray(x).view(np.int16).copy()).view(
+        torch.bfloat16).double().numpy()
+    k, v, beta = dec(c["key"]), dec(c["value"]), dec(c["beta"])
+    g, gk = c["g"].astype(np.float64), c["gk"].astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            s1 = beta[b, h, 0] * np.outer(k[b, h, 0], v[b, h, 0])
+            close(snaps[b, 0, h], s1, 1e-13, 1e-16)
+            d = np.exp(g[b, h, 1]) * np.exp(gk[b, h, 1])
+            s1d = d[:, None] * s1
+            u = beta[b, h, 1] * (v[b, h, 1] - s1d.T @ k[b, h, 1])
+            close(snaps[b, 1, h], s1d + np.outer(k[b, h, 1], u), 1e-12, 1e-15)
+
+
 # ------------------------------------------------------------------------------------
 # Gate pins
 # ------------------------------------------------------------------------------------

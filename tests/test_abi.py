@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for want in ("rgdr_decode", "rgdr_decode_gated", "rgdr_prefill", "rgdr_prefill_gated",
+    for want in ("rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated", "rgdr_prefill",
+                 "rgdr_prefill_gated",
                  "la_gate", "rgdr_validate", "rgdr_validate_host", "rgdr_status_string"):
         assert want in names, names
 
@@ -84,6 +85,33 @@ def test_decode_argument_checks(lib):
     bad[7] = 0x10002  # g not 4-byte aligned
     assert _decode(lib, ptrs=bad) == ALIGN
     assert _decode(lib, out=0x20004) == ALIGN
+
+
+def _snapshots(lib, ptrs=None, **kw):
+    dims = dict(B=2, Hq=2, Hv=4, T=4, Dk=128, Dv=128, N=4)
+    dims.update(kw)
+    p = [0x10000] * 10 if ptrs is None else ptrs
+    return lib.rgdr_decode_snapshots(*p[:10], 1.0, dims["B"], dims["Hq"], dims["Hv"],
+                                     dims["T"], dims["Dk"], dims["Dv"], dims["N"],
+                                     kw.get("out", 0x20000), kw.get("state_out", 0x30000),
+                                     kw.get("snap", 0x40000), None)
+
+
+def test_snapshots_argument_checks(lib):
+    assert _snapshots(lib, ptrs=[None] * 10, B=0, out=None, state_out=None, snap=None) == OK
+    for i in range(10):
+        p = [0x10000] * 10
+        p[i] = None
+        assert _snapshots(lib, ptrs=p) == NULL, i
+    assert _snapshots(lib, snap=None) == NULL
+    assert _snapshots(lib, snap=0x40008) == ALIGN  # snapshots not 16-byte aligned
+    assert _snapshots(lib, T=9) == SHAPE
+    assert _snapshots(lib, Hq=3, Hv=4) == SHAPE
+    assert _snapshots(lib, Dk=96) == UNSUP
+    assert _snapshots(lib, Dv=96) == UNSUP
+    bad = [0x10000] * 10
+    bad[3] = 0x10001  # beta not 2-byte aligned
+    assert _snapshots(lib, ptrs=bad) == ALIGN
 
 
 def _prefill(lib, ptrs=None, **kw):

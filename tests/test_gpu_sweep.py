@@ -2,7 +2,7 @@
 
 Each case draws its sizes, lengths, accepted counts and slot indices from one seed, so a
 failure names a reproducible case. Decode calls (T <= 8) cover every kernel form; the
-long-sequence entry covers runs split at the accepted prefix. Values within
+long-sequence entry covers chunks split at the accepted prefix. Values within
 2e-2 + 2e-2 |ref| of the unrounded oracle; padding and untouched slots bit for bit.
 """
 import numpy as np

@@ -29,6 +29,8 @@ MUTANTS = {
     "output_drops_scale": ("(qt[i] * scale);", "(qt[i]);"),
     "output_uses_key": ("(qt[i] * scale);", "(kt[i] * scale);"),
     "commit_off_by_one": ("if (t + 1 == n)", "if (t == n)"),
+    "snapshot_head_major": ("memcpy(snap + (size_t)t * snap_stride,", "memcpy(snap + (size_t)t * nS,"),
+    "snapshot_at_commit_only": ("if (snap)\n", "if (snap && t + 1 == n)\n"),
     "padding_not_zeroed": ("out[(size_t)t * Dv + j] = 0.0;", "(void)out;"),
     "gqa_modulo_map": ("int hq = (int)(((long long)h * a->Hq) / a->Hv);", "int hq = h % a->Hq;"),
     "length_not_clamped_low": ("int L = clampi(a->lens[b], 0, T);",
