@@ -180,3 +180,47 @@ def check_gated(inp, out_t, st_t, ref, label, entries=None):
     if entries is None:
         untouched = np.setdiff1d(np.arange(inp.N_slots), idx[valid])
         assert np.array_equal(dev_to_bits(st_t)[untouched], inp.state[untouched])
+
+
+# ---- per-token state snapshots ----
+
+SENTINEL = np.uint16(0xFFED)  # a quiet NaN whose payload no rounding produces
+
+
+def check_snapshots(rg, inp, label):
+    """Run rgdr_decode_snapshots on a sentinel-filled buffer and compare out, the committed
+    slots and every snapshot entry with the oracle; unwritten entries must keep the
+    sentinel, and the snapshot after the accepted prefix must be the committed slot's bytes."""
+    d = upload(inp)
+    pool = d["state"].clone()
+    snap = torch.full((inp.B, inp.T, inp.Hv, inp.Dk, inp.Dv), int(SENTINEL.view(np.int16)),
+                      dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    out, st, snap_r = rg.rgdr_decode_snapshots(
+        d["query"], d["key"], d["value"], d["beta"], pool, d["actual_seq_lengths"],
+        d["ssm_state_indices"], d["g"], d["gk"], d["num_accepted_tokens"], inp.scale,
+        state_snapshots=snap)
+    torch.cuda.synchronize()
+    assert snap_r.data_ptr() == snap.data_ptr()
+    o_out, o_pool, o_rows, o_snaps = oracle.rgdr_bf16_snapshots(
+        inp.query, inp.key, inp.value, inp.beta, inp.state, inp.actual_seq_lengths,
+        inp.ssm_state_indices, inp.g, inp.gk, inp.num_accepted_tokens, inp.scale)
+    check_decode(inp, out, st, (o_out, o_pool, o_rows), label)
+
+    got = bf16_dev_to_f64(snap)
+    bits = dev_to_bits(snap)
+    pool_bits = dev_to_bits(st)
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    written = np.zeros((inp.B, inp.T), bool)
+    for b in range(inp.B):
+        if valid[b]:
+            written[b, :lens[b]] = True
+    assert np.array_equal(np.isfinite(o_snaps).all(axis=(2, 3, 4)), written)
+    assert_tol(got[written], o_snaps[written], f"{label} snapshots")
+    assert np.all(bits[~written] == SENTINEL), f"{label}: unwritten snapshot entries changed"
+    n_acc = np.clip(inp.num_accepted_tokens, 0, lens)
+    for b in range(inp.B):
+        if valid[b] and n_acc[b] >= 1:
+            assert np.array_equal(bits[b, n_acc[b] - 1], pool_bits[inp.ssm_state_indices[b]]), \
+                f"{label}: entry {b}: snapshot {n_acc[b] - 1} is not the committed state"
+    say(f"  {label}: {int(written.sum())} snapshot entries written")

@@ -2,7 +2,8 @@
 
 Each case draws its sizes, lengths, accepted counts and slot indices from one seed, so a
 failure names a reproducible case. Decode calls (T <= 8) cover every kernel form; the
-long-sequence entry covers chunks split at the accepted prefix. Values within
+long-sequence entry covers chunks split at the accepted prefix; the snapshot entry covers
+the per-token states (unwritten entries and the committed prefix bit for bit). Values within
 2e-2 + 2e-2 |ref| of the unrounded oracle; padding and untouched slots bit for bit.
 """
 import numpy as np
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import check_decode, gpu_decode, gpu_prefill, oracle_decode, say
+from gpu_util import check_decode, check_snapshots, gpu_decode, gpu_prefill, oracle_decode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +59,11 @@ def test_random_prefill(rg, seed):
         f"Dv={inp.Dv} L={inp.actual_seq_lengths.tolist()} n={inp.num_accepted_tokens.tolist()}")
     out, st = gpu_prefill(inp)
     check_decode(inp, out, st, oracle_decode(inp), f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_snapshots(rg, seed):
+    inp = draw(2900 + seed, 8)
+    say(f"snapshot case {seed}: B={inp.B} Hq={inp.Hq} Hv={inp.Hv} T={inp.T} Dk={inp.Dk} "
+        f"Dv={inp.Dv} L={inp.actual_seq_lengths.tolist()} n={inp.num_accepted_tokens.tolist()}")
+    check_snapshots(rg, inp, f"random snapshots {seed}")
