@@ -70,6 +70,32 @@ def test_chunk_form_more_items_than_resident(rg):
     check_decode(inp, out, st, oracle_decode(inp), "chunk form, 1536 items")
 
 
+@pytest.mark.parametrize("case", ["varlen", "one_extra_round", "skips_and_half_tiles"])
+def test_chunk_form_dk64_more_items_than_resident(rg, case):
+    """The matrix-core form at D_k = 64 with more items than the device holds at once (six
+    per compute unit): later items start as earlier ones finish. Every entry is checked
+    against the oracle: the example page's head size at B = 16, H = 64, D_v = 512, T = 8
+    varlen (4096 items, about 2.7 rounds); a call just past one round (1728 items); and
+    skipped slots, entries with nothing accepted and half tiles (D_v = 320) among 2304
+    items."""
+    if case == "varlen":
+        inp = workloads.make_case(16, 16, 64, 8, 64, 512, 24, seed=48, indices="choice",
+                                  lengths="uniform")
+    elif case == "one_extra_round":
+        inp = workloads.make_case(9, 8, 64, 6, 64, 384, 9, seed=49, indices="permutation",
+                                  lengths="uniform")
+    else:
+        inp = workloads.make_case(12, 8, 64, 8, 64, 320, 14, seed=50, indices="choice",
+                                  lengths="uniform")
+        inp.ssm_state_indices[[2, 7]] = [-1, 14]  # skipped entries
+        inp.num_accepted_tokens[[0, 5]] = 0       # nothing accepted
+        inp.num_accepted_tokens[3] = max(1, inp.actual_seq_lengths[3] - 2)
+    items = inp.B * inp.Hv * ((inp.Dv + 127) // 128)
+    say(f"chunk form D_k=64 ({case}): {items} items")
+    out, st = gpu_decode(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"chunk form D_k=64 {case}")
+
+
 def test_workload4_gate_then_decode(rg):
     """la_gate feeds rgdr_decode (g fp32, beta bf16); the oracle chain uses its own gate."""
     inp = workloads.make_workload(4)
