@@ -172,7 +172,7 @@ def rgdr_decode_snapshots(query, key, value, beta, state_pool, actual_seq_length
     out, state_out = _plain_call("rgdr_decode_snapshots", query, key, value, beta, state_pool,
                                  actual_seq_lengths, ssm_state_indices, g, gk,
                                  num_accepted_tokens, scale, out, state_out, stream,
-                                 extra=(state_snapshots,))
+                                 extra={"state_snapshots": state_snapshots})
     return out, state_out, state_snapshots
 
 
@@ -187,7 +187,8 @@ def rgdr_prefill(query, key, value, beta, state_pool, actual_seq_lengths, ssm_st
 
 
 def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
-                g, gk, num_accepted_tokens, scale, out, state_out, stream, extra=()):
+                g, gk, num_accepted_tokens, scale, out, state_out, stream, extra=None):
+    extra = extra or {}  # further output buffers, passed after state_out in this order
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
     B, Hq, T, Dk = query.shape
@@ -224,7 +225,7 @@ def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm
     _same_device(query, key=key, value=value, beta=beta, state_pool=state_pool,
                  actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
                  g=g, gk=gk, num_accepted_tokens=num_accepted_tokens, out=out,
-                 state_out=state_out, **{f"extra{i}": t for i, t in enumerate(extra)})
+                 state_out=state_out, **extra)
     if VALIDATE:
         _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
@@ -233,7 +234,7 @@ def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm
                               actual_seq_lengths.data_ptr(), ssm_state_indices.data_ptr(),
                               g.data_ptr(), gk.data_ptr(), num_accepted_tokens.data_ptr(),
                               float(scale), B, Hq, Hv, T, Dk, Dv, N, out.data_ptr(),
-                              state_out.data_ptr(), *[t.data_ptr() for t in extra],
+                              state_out.data_ptr(), *[t.data_ptr() for t in extra.values()],
                               _stream_handle(stream, query.device))
     _check(rc, fn)
     return out, state_out
