@@ -794,7 +794,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 #endif
 
 
-template <int DK, int GATE>
+template <int DK, int GATE, bool SNAP = false>
 __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
@@ -880,6 +880,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
 #pragma unroll
     for (int e = 0; e < 64; ++e) gp[e] = 0.f;
     const bool has_rows = 64 * w < DK;
+    float dkeep[8], kkeep[8];  // with SNAP, this thread's row: decay and k per token
     if (has_rows) {
         const int row = tid;
         float d[8], k[8], q[8];
@@ -888,6 +889,13 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
             d[t] = ob[t * DK + row];  // padded tokens were staged neutral
             k[t] = ob[8 * DK + t * DK + row];
             q[t] = ob[16 * DK + t * DK + row];
+        }
+        if constexpr (SNAP) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                dkeep[t] = d[t];
+                kkeep[t] = k[t];
+            }
         }
         float c = 1.f, cnv = 1.f;
 #pragma unroll
@@ -1016,7 +1024,8 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
     {
         uint16_t h[8], l[8];
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) split_bf16(s2 < n ? u[s2] : 0.f, h[s2], l[s2]);
+        // (with SNAP every token's u: each state's k weights are zero past its last token)
+        for (int s2 = 0; s2 < 8; ++s2) split_bf16(SNAP || s2 < n ? u[s2] : 0.f, h[s2], l[s2]);
         // local column j = 4 n + c goes to UT position c * 16 + n
         const int p = (lane & 3) * 16 + (lane >> 2);
         *reinterpret_cast<u32x4 *>(ut_hi + p * 8) =
@@ -1037,7 +1046,7 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
             for (int i = 0; i < 4; ++i)
                 store8<RGDR_STATE_STORE_POLICY>(raw[rb][i], rso,
                                                 lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
-        return;
+        if constexpr (!SNAP) return;
     }
     // S_n = diag(c_{n-1}) S0 + [g k]^T U, block by block. The row scaling of the bf16 tile is
     // an fp32 multiply on the VALU and gives each accumulator its initial value; the rank-n
@@ -1051,26 +1060,68 @@ __global__ __launch_bounds__(128, 2) void decode_chunk_kernel(
         bu[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
                                                (kg >= 2 ? ut_lo : ut_hi) + (c * 16 + n16) * 8));
     const uint16_t *ka_lane = ((kg & 1) ? ka_lo : ka_hi) + n16 * 8;
+    auto commit = [&](const __amdgpu_buffer_rsrc_t &dst, const __amdgpu_buffer_rsrc_t &dst2,
+                      bool both) {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(ka_lane + 16 * rb * 8));
-        f32x4 D[4];
+        for (int rb = 0; rb < NRB; ++rb) {
+            const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
+            const bf16x8 ak = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(ka_lane + 16 * rb * 8));
+            f32x4 D[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            D[0][i] = cr[i] * bf16_lo(raw[rb][i].x);
-            D[1][i] = cr[i] * bf16_hi(raw[rb][i].x);
-            D[2][i] = cr[i] * bf16_lo(raw[rb][i].y);
-            D[3][i] = cr[i] * bf16_hi(raw[rb][i].y);
+            for (int i = 0; i < 4; ++i) {
+                D[0][i] = cr[i] * bf16_lo(raw[rb][i].x);
+                D[1][i] = cr[i] * bf16_hi(raw[rb][i].x);
+                D[2][i] = cr[i] * bf16_lo(raw[rb][i].y);
+                D[3][i] = cr[i] * bf16_hi(raw[rb][i].y);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bu[c], D[c], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 pk{pack_bf16x2(D[0][i], D[1][i]), pack_bf16x2(D[2][i], D[3][i])};
+                const uint32_t off = lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2);
+                store8<RGDR_STATE_STORE_POLICY>(pk, dst, off);
+                if (both) store8<RGDR_STATE_STORE_POLICY>(pk, dst2, off);
+            }
         }
+    };
+    if constexpr (!SNAP) {
+        commit(rso, rso, false);
+    } else {
+        // The state after every token t < L, in token order: S_t = diag(c_t) S0 +
+        // [g(t, .) k]^T U, the commit's products with each row's weights for t (zero past t).
+        // The one for t = n - 1 is also the commit, stored to the pool from the same registers.
+        const uint32_t srange = cols ? (uint32_t)(DK * a.Dv - m.tile * TV) * 2 : 0u;
+        float c = 1.f;
+        for (int t = 0; t < L; ++t) {  // uniform: L is the item's
+            if (has_rows) {
+                const int row = tid;
+                float kt[8];
+                float wv = 1.f;  // g(t, s) as s runs down from t
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            D[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bu[c], D[c], 0, 0, 0);
+                for (int s2 = 7; s2 >= 0; --s2) {
+                    kt[s2] = s2 <= t ? wv * kkeep[s2] : 0.f;
+                    if (s2 <= t) wv *= dkeep[s2];
+                }
+                c *= dkeep[t];
+                uint16_t kh[8], kl[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            store8<RGDR_STATE_STORE_POLICY>(
-                u32x2{pack_bf16x2(D[0][i], D[1][i]), pack_bf16x2(D[2][i], D[3][i])},
-                rso, lane_off + (uint32_t)((16 * rb + i) * a.Dv * 2));
+                for (int s2 = 0; s2 < 8; ++s2) split_bf16(kt[s2], kh[s2], kl[s2]);
+                *reinterpret_cast<u32x4 *>(ka_hi + row * 8) =
+                    u32x4{kh[0] | ((uint32_t)kh[1] << 16), kh[2] | ((uint32_t)kh[3] << 16),
+                          kh[4] | ((uint32_t)kh[5] << 16), kh[6] | ((uint32_t)kh[7] << 16)};
+                *reinterpret_cast<u32x4 *>(ka_lo + row * 8) =
+                    u32x4{kl[0] | ((uint32_t)kl[1] << 16), kl[2] | ((uint32_t)kl[3] << 16),
+                          kl[4] | ((uint32_t)kl[5] << 16), kl[6] | ((uint32_t)kl[7] << 16)};
+                crow[row] = c;
+            }
+            lds_barrier();
+            const size_t sb = (((size_t)m.b * a.T + t) * a.Hv + m.h) * DK * a.Dv +
+                              (size_t)m.tile * TV;
+            commit(make_rsrc(a.snap + sb, srange), rso, t + 1 == n);
+            lds_barrier();  // every wave has read this token's weights
+        }
     }
 }
 
@@ -1197,6 +1248,13 @@ static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
 template <int DK, int GATE>
 static hipError_t launch_chunk(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                const int32_t *nacc, hipStream_t stream) {
+    if constexpr (GATE == kGateGiven) {  // per-token states: rgdr_decode_snapshots only
+        if (a.snap) {
+            hipLaunchKernelGGL((decode_chunk_kernel<DK, GATE, true>), dim3(a.n_items), dim3(128),
+                               0, stream, a, lens, idx, nacc);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((decode_chunk_kernel<DK, GATE>), dim3(a.n_items), dim3(128), 0, stream, a,
                        lens, idx, nacc);
     return hipGetLastError();
@@ -1253,9 +1311,9 @@ static rgdr_status decode_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q,
                        (D_k == 128 || (RGDR_CHUNK_DK64 && T >= RGDR_CHUNK_DK64_MIN_T)) &&
                        (D_v % 128 == 0 ||
                         (RGDR_CHUNK_HALF_TILE && (D_v > 64 || T >= RGDR_CHUNK_DV64_MIN_T)));
-    // Per-token states exist only in the per-token form, which serves every T then.
-    const Form form = a.snap ? kFormWaveMulti : T == 1 ? kFormWave : chunk ? kFormChunk
-                                                                   : kFormWaveMulti;
+    // Per-token states: the chunk form where it serves the call, else the per-token form
+    // (also for T = 1: the single-token form keeps no snapshot path).
+    const Form form = T == 1 && !a.snap ? kFormWave : chunk ? kFormChunk : kFormWaveMulti;
     // Tile widths. For the multi-token form, the widest tile whose fp32 copy fits a lane
     // (D_k x TV <= 64 x 128 values per wave). For T = 1, 64-column tiles while the whole call
     // then fits in one launch of the resident grid: twice the waves, each with half the
