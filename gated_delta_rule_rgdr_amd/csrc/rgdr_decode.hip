@@ -744,6 +744,11 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 // column set c. In the commit the accumulator of block (rb, c) holds exactly the lane's own
 // elements of rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c: the lane scales its own loaded
 // values into it, and the update lands in the layout the commit stores.
+//
+// SNAP (rgdr_decode_snapshots): the state after token t is the same expression with n - 1
+// replaced by t, S_t = diag(c_t) S0 + sum_{s<=t} (g(t,s) k_s) (x) u_s, so after the solve the
+// commit's products are taken once per t < L, with each row's weights for t, and stored to
+// snapshot t (and, for t = n - 1, to the pool).
 // ---------------------------------------------------------------------------------------
 
 // The chunk form serves calls with T >= RGDR_CHUNK_MIN_T. Its time hardly depends on the

@@ -125,9 +125,9 @@ rgdr_status rgdr_decode(const void *query, const void *key, const void *value,
  *                    written. With n = num_accepted_tokens[b] >= 1, entry (b, n - 1) holds
  *                    the same bytes as the committed slot.
  *   All other arguments, results and errors: as rgdr_decode (RGDR_ERR_NULL also for
- *   state_snapshots, RGDR_ERR_ALIGN for its alignment). Every T <= 8 runs the per-token
- *   form; the snapshots add D_k * D_v * 2 bytes of HBM writes per written entry and value
- *   head (at most B * T * H_v * D_k * D_v * 2 in all).
+ *   state_snapshots, RGDR_ERR_ALIGN for its alignment). The snapshots add D_k * D_v * 2
+ *   bytes of HBM writes per written entry and value head (at most B * T * H_v * D_k * D_v * 2
+ *   in all).
  */
 rgdr_status rgdr_decode_snapshots(const void *query, const void *key, const void *value,
                                   const void *beta, const void *state_pool,
