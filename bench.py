@@ -2,7 +2,7 @@
 """Benchmark of the gated-delta-rule path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--rotate R]
-                    [--extra 1,3,4,5] [--cpu-seconds S] [--no-cpu-baseline]
+                    [--extra 1,3,4,5] [--snapshots 3] [--cpu-seconds S] [--no-cpu-baseline]
 
 One step is the whole path over one batch: the gate front end (g = decay_scale *
 softplus(a + dt_bias), beta = sigmoid(b)) and the recurrence, in place on the state pool,
@@ -27,7 +27,9 @@ Measurement:
     its roofline uses the method's algorithmic bytes per call. The unfused kernels are
     timed the same way.
   * `workloads`: the same kernel timing for the other workloads (--extra), so one line
-    carries every workload's fused-call duration, roofline fraction and counter traffic.
+    carries every workload's fused-call duration, roofline fraction and counter traffic;
+    and `<id>_snapshots` (--snapshots): rgdr_decode_snapshots, the step that also stores
+    the state after every token, at that workload.
   * copy_reference: a plain 256 MiB device copy (torch elementwise, read + write), timed
     the same way, as the box's practical streaming rate.
   * cpu_baseline: the fp64 C oracle repeats the step on the host for about --cpu-seconds,
@@ -453,6 +455,47 @@ def extra_entry(torch, stream, wl, n):
             "roofline": r}
 
 
+def snapshot_entry(torch, stream, wl, n):
+    """Duration and roofline of rgdr_decode_snapshots at one workload: the decode step that
+    also stores the state after every token (g and beta from the gate beforehand, as that
+    entry takes them). Its algorithmic bytes are the decode's plus D_k * D_v * 2 per written
+    snapshot (every token t < L of every served entry and value head)."""
+    import numpy as np
+    inp = wl.inp
+    B, Hv, T, Dk, Dv = inp.B, inp.Hv, inp.T, inp.Dk, inp.Dv
+    for s in wl.sets:
+        wl.gate(s)
+        if T != 1:
+            wl.transpose(s)
+        s["snap"] = torch.empty((B, T, Hv, Dk, Dv), dtype=torch.bfloat16, device=s["q"].device)
+    torch.cuda.synchronize()
+
+    def call(s):
+        g_ = s["g"].view(B, Hv, T) if T == 1 else s["gT"]
+        be = s["beta"].view(B, Hv, T) if T == 1 else s["betaT"]
+        wl.rg.rgdr_decode_snapshots(s["q"], s["k"], s["v"], be, s["pool"], wl.lens, wl.idx, g_,
+                                    s["gk"], wl.nacc, inp.scale, out=s["out"],
+                                    state_snapshots=s["snap"])
+
+    for s in wl.sets[:3]:
+        call(s)
+    torch.cuda.synchronize()
+    us, per = kernel_avg_us(torch, stream, call, wl.sets, n)
+    lens = np.clip(inp.actual_seq_lengths, 0, T)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    by = wl.dbytes + int(lens[valid].sum()) * Hv * Dk * Dv * 2
+    gbs = by / (us * 1e-6) / 1e9
+    return {"workload": wl.name, "call": "rgdr_decode_snapshots (state after every token)",
+            "config": {"B": B, "H_q": inp.Hq, "H_v": Hv, "T": T, "D_k": Dk, "D_v": Dv,
+                       "N_slots": inp.N_slots, "rotation_sets": wl.R, "calls_timed": n},
+            "call_us": round(us, 3),
+            "roofline": {"kernel": "rgdr_decode_snapshots", "bound": "hbm",
+                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": by, "avg_launch_us": round(us, 3),
+                         "launch_us_replays": [round(x, 3) for x in per]}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +508,9 @@ def main():
     ap.add_argument("--extra", default="1,3,4,5",
                     help="other workloads whose fused-call duration the line also carries "
                          "(comma-separated ids; empty for none)")
+    ap.add_argument("--snapshots", default="3",
+                    help="workload at which the line also carries rgdr_decode_snapshots "
+                         "(the state after every token); empty for none")
     ap.add_argument("--extra-steps", type=int, default=50,
                     help="calls per timed graph replay for the --extra workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -572,6 +618,17 @@ def main():
         extras[str(ew)] = extra_entry(torch, stream, e, args.extra_steps)
         log(f"workload {ew} ({e.name}): {e.fused_name} {extras[str(ew)]['call_us']:.2f} us "
             f"per call, {100 * extras[str(ew)]['roofline']['frac']:.1f}% of 8 TB/s")
+        e.free()
+        del e
+
+    if args.snapshots.strip():
+        sw = int(args.snapshots)
+        e = Workload(sw, dev, 0, args.extra_steps)
+        if not e.prefill:
+            extras[f"{sw}_snapshots"] = snapshot_entry(torch, stream, e, args.extra_steps)
+            log(f"workload {sw} with per-token states: rgdr_decode_snapshots "
+                f"{extras[f'{sw}_snapshots']['call_us']:.2f} us per call, "
+                f"{100 * extras[f'{sw}_snapshots']['roofline']['frac']:.1f}% of 8 TB/s")
         e.free()
         del e
 
