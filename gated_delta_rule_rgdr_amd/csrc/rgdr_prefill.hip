@@ -486,6 +486,12 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         // read once, since a second preparation pass rewrites crow
         const f32x4 cprev = (chunk == 0 || tg != 0) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                                      : *reinterpret_cast<const f32x4 *>(crow + 4 * r);
+        // Issue priority rises with the phase of the chunk (preparation 0, M and N blocks 1,
+        // Y 2, the rest 3). Each SIMD holds a wave of each of the unit's two items, and the
+        // wave further into its chunk goes first: its matrix-core chains stay fed while the
+        // other item's preparation fills their gaps, instead of the two competing for issue
+        // slots (one level for everything after the preparation: 4% faster; these four: 9%).
+        __builtin_amdgcn_s_setprio(0);
         for (;;) {
             prep(Lc, cprev);
             lds_barrier();
@@ -507,6 +513,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         }
         const int t0n = t0 + Lc, lenn = t0n < L ? chunk_len(t0n) : 0;
 
+        __builtin_amdgcn_s_setprio(1);
         // M and N blocks, each wave its share (rotating by chunk so that the solves move
         // between the SIMDs): roles 0 and 1 form beta M of one diagonal block each and invert
         // it (in the same wave, so no barrier separates the steps); roles 2 and 3 form -M_10,
@@ -550,6 +557,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             put_block<AS, true>(blk(5), gram_block<DK, XS>(xq_hi, kd_hi, 1, 1, n16, kg), 1.f, n16, kg);
         }
 
+        __builtin_amdgcn_s_setprio(2);
         // Y_K = [c k]^T S' and Y_Q = [c scale q]^T S' (32 tokens x this wave's 32 columns),
         // with S' = diag(d_0) S formed in place; three products of the split parts.
         f32x4 yk[2][2], yq[2][2];
@@ -589,6 +597,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         lds_barrier();  // every operand block is written
         if (tid == 0) *cut = kChunk;  // every thread read it before the barrier
 
+        __builtin_amdgcn_s_setprio(3);
         // R = V - Y_K for the chunk's tokens (0 past Lc); then the next chunk's values.
         f32x4 R[2][2];
 #pragma unroll
