@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import check_snapshots as run_and_check, say
+from gpu_util import check_snapshots as run_and_check, dev_to_bits, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,9 @@ CASES = [
     (5, 1, 2, 3, 64, 64, 7, 14, "uniform", "draw"),      # D_k = 64, 64-column tiles
     (4, 2, 4, 1, 128, 128, 4, 15, [1, 0, 1, 1], None),   # T = 1, an empty entry
     (8, 16, 32, 8, 128, 128, 16, 16, "uniform", "draw"), # the varlen speculative shape
+    (1, 1, 2, 8, 128, 4096, 2, 18, [7], [5]),            # D_v = 4096: 32 tiles per head
+    (3, 2, 2, 8, 128, 320, 4, 19, "uniform", "draw"),    # chunk form, last tile 64 columns
+    (4, 2, 4, 6, 64, 192, 5, 20, "uniform", "draw"),     # chunk form at D_k = 64, half tile
 ]
 
 
@@ -70,3 +73,31 @@ def test_snapshots_workload3(rg):
     inp = workloads.make_workload(3)
     say(f"snapshots: {workloads.WORKLOAD_NAMES[3]}")
     run_and_check(rg, inp, "snapshots workload 3")
+
+
+def test_snapshots_out_of_place(rg):
+    """state_out a separate buffer: the pool is left as it was, state_out receives the
+    committed slots (and keeps its other bytes), and the snapshots are those of the
+    in-place call, bit for bit."""
+    inp = workloads.make_case(4, 2, 4, 5, 128, 128, 6, 21, indices="choice", lengths="uniform")
+    d = upload(inp)
+    pool = d["state"].clone()
+    fill = torch.full_like(pool.view(torch.int16), 0x1234).view(torch.bfloat16)
+    st_out = fill.clone()
+    args = (d["query"], d["key"], d["value"], d["beta"], pool, d["actual_seq_lengths"],
+            d["ssm_state_indices"], d["g"], d["gk"], d["num_accepted_tokens"], inp.scale)
+    out1, st1, sn1 = rg.rgdr_decode_snapshots(*args, state_out=st_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bits(pool), inp.state), "the pool was modified"
+    named = inp.ssm_state_indices
+    others = np.setdiff1d(np.arange(inp.N_slots), named)
+    assert np.all(dev_to_bits(st1)[others] == 0x1234), "state_out slots no entry names changed"
+    pool2 = d["state"].clone()
+    out2, st2, sn2 = rg.rgdr_decode_snapshots(*args[:4], pool2, *args[5:])
+    torch.cuda.synchronize()
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    for b in range(inp.B):
+        assert np.array_equal(dev_to_bits(sn1)[b, :lens[b]], dev_to_bits(sn2)[b, :lens[b]])
+    assert np.array_equal(dev_to_bits(out1), dev_to_bits(out2))
+    assert np.array_equal(dev_to_bits(st1)[named], dev_to_bits(st2)[named])
+    say("  out-of-place snapshots: equal to the in-place call")
