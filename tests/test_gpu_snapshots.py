@@ -101,3 +101,48 @@ def test_snapshots_out_of_place(rg):
     assert np.array_equal(dev_to_bits(out1), dev_to_bits(out2))
     assert np.array_equal(dev_to_bits(st1)[named], dev_to_bits(st2)[named])
     say("  out-of-place snapshots: equal to the in-place call")
+
+
+def test_snapshots_graph_replay_matches_eager(rg):
+    """rgdr_decode_snapshots captured in a HIP graph (the chunk form at the varlen
+    speculative shape) gives the eager bytes of out, the committed slots and every written
+    snapshot on each of four replays, with eager work on the device between them."""
+    inp = workloads.make_workload(3)
+    d = upload(inp)
+    out = torch.empty((inp.B, inp.Hv, inp.T, inp.Dv), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty_like(d["state"])
+    snap = torch.empty((inp.B, inp.T, inp.Hv, inp.Dk, inp.Dv), dtype=torch.bfloat16,
+                       device="cuda")
+
+    def step():
+        rg.rgdr_decode_snapshots(d["query"], d["key"], d["value"], d["beta"], d["state"],
+                                 d["actual_seq_lengths"], d["ssm_state_indices"], d["g"],
+                                 d["gk"], d["num_accepted_tokens"], inp.scale, out=out,
+                                 state_out=st, state_snapshots=snap)
+
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    st.copy_(d["state"])
+    step()
+    torch.cuda.synchronize()
+    want = (dev_to_bits(out), dev_to_bits(st), dev_to_bits(snap))
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.zero_()
+        snap.zero_()
+        st.copy_(d["state"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (dev_to_bits(out), dev_to_bits(st), dev_to_bits(snap))
+        assert np.array_equal(got[0], want[0]), f"replay {rep}: out differs"
+        assert np.array_equal(got[1], want[1]), f"replay {rep}: state differs"
+        for b in range(inp.B):
+            assert np.array_equal(got[2][b, :lens[b]], want[2][b, :lens[b]]), \
+                f"replay {rep}: snapshots of entry {b} differ"
+    say("  snapshot graph replays equal the eager call")
