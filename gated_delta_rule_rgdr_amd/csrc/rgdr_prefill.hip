@@ -28,10 +28,15 @@
 // high part and a bf16 remainder and three products are summed (high x high, low x high,
 // high x low), so each keeps about 16 bits of both operands; accumulation is fp32.
 //
-// The factored form needs every c_t of the chunk within [2^-96, 2^96] (each factor and their
-// products stay far from fp32 overflow and underflow). A chunk in which some row leaves that
-// range is shortened to end before the first such token (c_0 = 1, so at least one token
-// remains); strong decays therefore give shorter chunks, not a different arithmetic.
+// The closed form holds with c measured from any per-row reference: with c'_t = c_t / r and
+// S'' = diag(r) S', Y_K = [c' k]^T S'', M and N take the ratios c'_t / c'_s = c_t / c_s, and
+// S_end = diag(c'_last) (S'' + K'^T U) with K' the rows k_s / c'_s. Each row takes the
+// middle of its chunk, r = 2^(L_last / 2) with L_t = log2 c_t (sums of the decays' log2,
+// formed in log space so that no product under- or overflows), and the factored form needs
+// every c'_t within [2^-96, 2^96] (each factor and their products stay far from fp32
+// overflow and underflow): a chunk whose decay products span up to 2^192. A chunk in which
+// some row leaves that range is shortened (c_0 = 1, so at least one token remains); strong
+// decays therefore give shorter chunks, not a different arithmetic.
 //
 // A chunk that holds the accepted prefix's end stops there, so the committed state is a
 // chunk's end state; the later tokens still produce their outputs. The next chunk's operands
@@ -46,8 +51,9 @@ namespace rgdr {
 
 constexpr int kPrefillMaxT = 65536;  // tokens per call: keeps every per-item offset in 32 bits
 constexpr int kChunk = 32;           // tokens per chunk
-// Range of the decay products c_t inside which a chunk takes the factored form.
-constexpr float kChunkLo = 0x1p-96f, kChunkHi = 0x1p96f;
+// Range (log2) of the decay products c'_t around the chunk's middle inside which a chunk takes
+// the factored form.
+constexpr float kChunkLog2 = 96.f;
 constexpr float kLog2e = 1.4426950408889634f;  // exp(x) = 2^(x log2 e)
 
 // Waves per SIMD the kernel is compiled for (the register budget).
@@ -369,33 +375,34 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 qs[j] = a.scale * inv_norm(b2);
             }
         }
-        // Decays, and their running products over this thread's tokens (token 0 excluded).
-        float d[TPT][4], cp[TPT][4];
+        // log2 of the decays exp(g_t) exp(gk_t,i), and their running sums over this thread's
+        // tokens (token 0 excluded): L_t = log2 c_t.
+        float ld0[4], lc[TPT][4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float acc = 1.f;
+            float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < TPT; ++j) {
-                // exp(g_t) exp(gk_t,i) as one power of two
-                d[j][e] = __builtin_amdgcn_exp2f(fmaf(o.gk[j][e], kLog2e, gl[j]));
-                acc *= (j == 0 && tg == 0) ? 1.f : d[j][e];
-                cp[j][e] = acc;
+                const float l = fmaf(o.gk[j][e], kLog2e, gl[j]);
+                if (j == 0) ld0[e] = l;
+                acc += (j == 0 && tg == 0) ? 0.f : l;
+                lc[j][e] = acc;
             }
         }
-        // Across the row group's token groups: inclusive products by DPP row shifts, then
-        // the exclusive prefix (shift by one) and the chunk total (last token group).
-        float inc[4], pre[4], clast[4];
+        // Across the row group's token groups: inclusive sums by DPP row shifts, then the
+        // exclusive prefix (shift by one) and the chunk total (last token group).
+        float inc[4], pre[4], llast[4], lref[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) inc[e] = cp[TPT - 1][e];
+        for (int e = 0; e < 4; ++e) inc[e] = lc[TPT - 1][e];
         auto shr = [](float v, auto k) {
-            return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(v),
+            return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(0.f), __float_as_int(v),
                                                               0x110 + decltype(k)::value, 0xF, 0xF, false));
         };
 #define RGDR_SCAN_STEP(K)                                                         \
     if constexpr (K < NTG) {                                                      \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                           \
             const float p = shr(inc[e], std::integral_constant<int, K>{});        \
-            inc[e] = tg >= K ? inc[e] * p : inc[e];                               \
+            inc[e] = tg >= K ? inc[e] + p : inc[e];                               \
         }                                                                         \
     }
         RGDR_SCAN_STEP(1)
@@ -406,17 +413,21 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float p = shr(inc[e], std::integral_constant<int, 1>{});
-            pre[e] = tg >= 1 ? p : 1.f;
-            clast[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (lane | (NTG - 1)), __float_as_int(inc[e])));
+            pre[e] = tg >= 1 ? p : 0.f;
+            llast[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (lane | (NTG - 1)), __float_as_int(inc[e])));
+            lref[e] = 0.5f * llast[e];  // the row's reference: the middle of its chunk
         }
-        float cmin = 1.f, cmax = 1.f;
+        // c'_t = 2^(L_t - L_ref); out-of-range (or NaN) exponents mark the chunk for a cut.
+        float cp[TPT][4];
+        bool out_of_range = false;
 #pragma unroll
         for (int j = 0; j < TPT; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                cp[j][e] *= pre[e];  // c_t of row 4 r + e
-                cmin = fminf(cmin, cp[j][e]);
-                cmax = fmaxf(cmax, cp[j][e]);
+                lc[j][e] += pre[e];  // L_t of row 4 r + e
+                const float x = lc[j][e] - lref[e];
+                out_of_range |= !(x >= -kChunkLog2 && x <= kChunkLog2);
+                cp[j][e] = __builtin_amdgcn_exp2f(x);
             }
         // Operand planes. Row-major by token for XK, XQ, KD; KH holds the same split values
         // as KD, by state row (its bf16 halves regrouped by byte permutes).
@@ -461,20 +472,33 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 *reinterpret_cast<uint32_t *>(kh_lo + off) = regroup(dl, e, 0);
             }
         }
-        // The state is kept as S' + sum_s (k_s / c_s) u_s^T, whose rows c_last scales into the
-        // true state: the next chunk's S' takes c_last (of this one) times its own d_0.
+        // The state is kept as S'' + sum_s (k_s / c'_s) u_s^T, whose rows c'_last scales into
+        // the true state: the next chunk's S'' takes c'_last (of this one) times its own d_0
+        // and reference.
         if (tg == 0) {
-            *reinterpret_cast<f32x4 *>(crow + 4 * r) = f32x4{clast[0], clast[1], clast[2], clast[3]};
-            *reinterpret_cast<f32x4 *>(d0row + 4 * r) =
-                f32x4{cprev[0] * d[0][0], cprev[1] * d[0][1], cprev[2] * d[0][2], cprev[3] * d[0][3]};
+            f32x4 cl, dr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cl[e] = __builtin_amdgcn_exp2f(llast[e] - lref[e]);
+                dr[e] = cprev[e] * __builtin_amdgcn_exp2f(ld0[e] + lref[e]);
+            }
+            *reinterpret_cast<f32x4 *>(crow + 4 * r) = cl;
+            *reinterpret_cast<f32x4 *>(d0row + 4 * r) = dr;
         }
-        if (!(cmin >= kChunkLo && cmax <= kChunkHi)) {  // rare: find the first token out of range
+        if (out_of_range) {  // rare: find where this row's chunk must end
             int first = kChunk;
 #pragma unroll
             for (int j = TPT - 1; j >= 0; --j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (!(cp[j][e] >= kChunkLo && cp[j][e] <= kChunkHi)) first = TPT * tg + j;
+                for (int e = 0; e < 4; ++e) {
+                    // A row whose whole chunk spans more than 2^(2 * 96) ends before its first
+                    // token beyond that span from the start (token 0 never is); otherwise
+                    // before its first token out of range around the middle.
+                    const bool wide = !(llast[e] >= -2.f * kChunkLog2 && llast[e] <= 2.f * kChunkLog2);
+                    const float x = wide ? lc[j][e] : lc[j][e] - lref[e];
+                    const float lim = wide ? 2.f * kChunkLog2 : kChunkLog2;
+                    if (!(x >= -lim && x <= lim)) first = TPT * tg + j;
+                }
             atomicMin(cut, first);
         }
     };
@@ -499,9 +523,10 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             if (c >= Lc) break;
             // A decay product left the range at token c >= 1: the chunk ends before it.
             // Zero this thread's operands of the later tokens and prepare again. Nothing
-            // written by the preparation is read before the barrier that ends it, and the
-            // second pass lowers the cut to no token below c (its tokens before c are
-            // unchanged, the later ones neutral), so no other barrier is needed.
+            // written by the preparation is read before the barrier that ends it. The next
+            // pass takes a new reference and, outside the operator's domain (growth mixed
+            // with decay), may lower the cut again: every thread reads it before any can.
+            lds_barrier();
             Lc = c;
 #pragma unroll
             for (int j = 0; j < TPT; ++j)

@@ -1,4 +1,4 @@
-"""The closed form the matrix-core decode evaluates for T > 1, checked against the oracle.
+"""The closed forms the matrix-core kernels evaluate, checked against the oracle.
 
 The GPU's chunk form does not step through the tokens: for one (entry, value head) with
 row decays d_t = exp(g_t) exp(gk_t), decay products c_t = d_0 ... d_t and
@@ -110,3 +110,131 @@ def test_closed_form_detects_a_wrong_decay_product():
     for t in range(T):
         u_right[t] = beta[0, 0, t] * (v[0, 0, t] - A[t] - M[t, :t] @ u_right[:t])
     assert np.abs(u - u_right).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------------------
+# The long-sequence kernel's steps: chunks of up to 32 tokens in the factored closed form,
+# decay products measured from each row's middle of the chunk, the state carried with a
+# pending per-row factor, the triangular system solved in 16-token blocks.
+# ---------------------------------------------------------------------------------------
+
+
+def long_sequence_form(S0, q, k, v, beta, g, gk, scale, L, n, chunk=32, span=96.0, mid=True):
+    """One (entry, value head) through the long-sequence kernel's steps in fp64. Returns
+    (out [L, D_v], committed state [D_k, D_v], chunk lengths). mid=False measures the decay
+    products from the chunk's start instead of each row's middle."""
+    Dk, Dv = S0.shape
+    log2d = (g[:, None] + gk) / np.log(2.0)          # log2 of each row's decay, [T, D_k]
+    out = np.zeros((L, Dv))
+    keep, pend = S0.copy(), np.ones(Dk)              # the true state is diag(pend) keep
+    committed = S0.copy() if n == 0 else None
+    lengths = []
+    t0 = 0
+    while t0 < L:
+        t1 = min(t0 + chunk, L)
+        if t0 < n < t1:
+            t1 = n                                   # the chunk holding n - 1 ends there
+        while True:                                  # cut by the decay range
+            Lt = np.zeros((t1 - t0, Dk))            # L_t = log2 c_t, token 0's decay excluded
+            Lt[1:] = np.cumsum(log2d[t0 + 1:t1], axis=0)
+            lref = 0.5 * Lt[-1] if mid else np.zeros(Dk)   # each row's reference
+            with np.errstate(invalid="ignore"):      # a zero decay gives -inf - -inf here
+                x = Lt - lref
+                if np.all(np.abs(x) <= span):
+                    break
+                cuts = []
+                for i in np.nonzero(~(np.abs(x) <= span).all(axis=0))[0]:
+                    wide = mid and abs(Lt[-1, i]) > 2 * span
+                    y, lim = (Lt[:, i], 2 * span) if wide else (x[:, i], span)
+                    cuts.append(int(np.nonzero(~(np.abs(y) <= lim))[0][0]))
+            t1 = t0 + min(cuts)
+        Lc = t1 - t0
+        lengths.append(Lc)
+        cp = 2.0 ** x                                # c'_t
+        S2 = (pend * 2.0 ** (log2d[t0] + lref))[:, None] * keep   # S'' = diag(r) diag(d_0) S
+        kk, qs, bt = k[t0:t1], scale * q[t0:t1], beta[t0:t1]
+        Xk, Xq, Kd = cp * kk, cp * qs, kk / cp
+        YK, YQ = Xk @ S2, Xq @ S2
+        M = np.tril(Xk @ Kd.T, -1)                   # M[t][s] = sum_i (c_t / c_s) k_t k_s, s < t
+        N = np.tril(Xq @ Kd.T)                       # N[t][s], s <= t
+        R = v[t0:t1] - YK
+        U = np.zeros((Lc, Dv))
+        for a in range(0, Lc, 16):                   # U_b = A_bb (R_b - M_b,<b U_<b)
+            b = min(a + 16, Lc)
+            Abb = np.linalg.inv(np.eye(b - a) + bt[a:b, None] * M[a:b, a:b]) * bt[None, a:b]
+            U[a:b] = Abb @ (R[a:b] - M[a:b, :a] @ U[:a])
+        out[t0:t1] = YQ + N @ U
+        keep = S2 + Kd.T @ U                         # S'' + K'^T U
+        pend = 2.0 ** (Lt[-1] - lref)                # c'_last
+        t0 = t1
+        if t0 == n:
+            committed = pend[:, None] * keep
+    return out, committed, lengths
+
+
+def _long_case(rng, T, Dk, Dv, g, gk):
+    q = rng.standard_normal((1, 1, T, Dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((1, 1, T, Dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, 1, T, Dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((1, 1, T))))
+    pool = 0.3 * rng.standard_normal((1, 1, Dk, Dv))
+    return q, k, v, beta, pool, g.reshape(1, 1, T), gk.reshape(1, 1, T, Dk)
+
+
+@pytest.mark.parametrize("case", ["mild", "strong", "very_strong", "mixed_rows", "zero_decay"])
+def test_long_sequence_form_equals_the_recurrence(case):
+    """The steps agree with the oracle's token-by-token recurrence to 1e-10 (relative to the
+    largest value): mild decays (chunks of 32, then a ragged end, the accepted count inside a
+    chunk); decays of 4.5 and 12 nats per token (chunks cut around the middle, and rows whose
+    whole chunk spans more than 2^192); rows decaying at different rates; and a decay of
+    exactly zero (the state wiped)."""
+    rng = np.random.default_rng({"mild": 1, "strong": 2, "very_strong": 3, "mixed_rows": 4,
+                                 "zero_decay": 5}[case])
+    T, Dk, Dv = 90, 12, 7
+    g = -np.log1p(np.exp(rng.standard_normal(T)))
+    gk = -rng.uniform(1e-3, 0.1, (T, Dk))
+    if case == "strong":
+        g[:] = -4.5
+    elif case == "very_strong":
+        g[:] = -12.0
+    elif case == "mixed_rows":
+        gk[:, : Dk // 2] = -rng.uniform(3.0, 9.0, (T, Dk // 2))
+    elif case == "zero_decay":
+        g[40] = -np.inf
+    q, k, v, beta, pool, g3, gk4 = _long_case(rng, T, Dk, Dv, g, gk)
+    L, n = 90, 50
+    lens, nacc = np.array([L], np.int32), np.array([n], np.int32)
+    out_ref, pool_ref = oracle.rgdr_f64(q, k, v, beta, pool, lens, np.zeros(1, np.int32), g3,
+                                        gk4, nacc, 1.0 / np.sqrt(Dk))
+    out, S, lengths = long_sequence_form(pool[0, 0], q[0, 0], k[0, 0], v[0, 0], beta[0, 0], g,
+                                         gk, 1.0 / np.sqrt(Dk), L, n)
+    assert sum(lengths) == L
+    if case == "mild":
+        assert lengths == [32, 18, 32, 8]            # split at n = 50, then the ragged end
+    if case in ("strong", "very_strong", "mixed_rows"):
+        assert max(lengths) < 32                     # the range cut the chunks
+    scale_o = np.abs(out_ref[0, 0, :L]).max()
+    np.testing.assert_allclose(out, out_ref[0, 0, :L], rtol=1e-10, atol=1e-10 * scale_o)
+    np.testing.assert_allclose(S, pool_ref[0, 0], rtol=1e-10,
+                               atol=1e-10 * np.abs(pool_ref[0, 0]).max())
+
+
+@pytest.mark.parametrize("g_val", [-0.3, -4.5])
+def test_long_sequence_form_reference_is_free(g_val):
+    """The per-row reference cancels: measuring the decay products from the chunk's start
+    (so a chunk may span only 2^96, and strong decays cut it earlier) gives the same outputs
+    and state as the middle reference, to 1e-12 relative."""
+    rng = np.random.default_rng(6)
+    T, Dk, Dv = 70, 8, 5
+    g = np.full(T, g_val)
+    gk = -rng.uniform(1e-3, 0.1, (T, Dk))
+    q, k, v, beta, pool, _, _ = _long_case(rng, T, Dk, Dv, g, gk)
+    args = (pool[0, 0], q[0, 0], k[0, 0], v[0, 0], beta[0, 0], g, gk, 0.5, T, 45)
+    o_mid, s_mid, l_mid = long_sequence_form(*args)
+    o_start, s_start, l_start = long_sequence_form(*args, mid=False)
+    if g_val < -1:
+        assert max(l_start) < max(l_mid) < 32      # the two references cut differently
+    else:
+        assert l_start == l_mid == [32, 13, 25]
+    np.testing.assert_allclose(o_start, o_mid, rtol=1e-12, atol=1e-12 * np.abs(o_mid).max())
+    np.testing.assert_allclose(s_start, s_mid, rtol=1e-12, atol=1e-12 * np.abs(s_mid).max())

@@ -80,9 +80,10 @@ def test_prefill_nan_padding_bitexact(rg):
 
 def test_prefill_accepted_prefix(rg):
     """n < L: the committed state equals that of a call that stops after n tokens, bit for
-    bit; outputs of tokens before n equal those of the n = L call bit for bit; everything
-    meets the bar against the oracle. Counts at a run boundary (8, 16), inside a run (13),
-    zero and the full length."""
+    bit; outputs of tokens before n equal those of the n = L call within the bar (the chunk
+    that ends at n measures its decays from its own middle, so they may differ in rounding);
+    everything meets the bar against the oracle. Counts inside the first chunk of 32 (8, 13,
+    16, 20 of 21), zero and the full length."""
     lens = [30, 30, 30, 30, 30, 21]
     nacc = [8, 16, 13, 0, 30, 20]
     full = workloads.make_case(6, 2, 4, 32, 128, 128, 8, seed=7301, indices="choice",
@@ -92,9 +93,9 @@ def test_prefill_accepted_prefix(rg):
                               lengths=lens)
     acc.num_accepted_tokens = np.array(nacc, np.int32)
     out_a, st_a = gpu_prefill(acc)
-    of, oa = dev_to_bits(out_f), dev_to_bits(out_a)
+    of, oa = bf16_dev_to_f64(out_f), bf16_dev_to_f64(out_a)
     for b, n in enumerate(nacc):
-        assert np.array_equal(oa[b, :, :n], of[b, :, :n]), f"entry {b}: outputs before {n}"
+        assert_tol(oa[b, :, :n], of[b, :, :n], f"entry {b}: outputs before {n}")
     short = workloads.make_case(6, 2, 4, 32, 128, 128, 8, seed=7301, indices="choice",
                                 lengths=lens)
     short.actual_seq_lengths = acc.num_accepted_tokens.copy()
@@ -238,11 +239,12 @@ def test_prefill_long_sequence(rg):
     check_decode(inp, out, st, oracle_decode(inp), "prefill T=4096")
 
 
-@pytest.mark.parametrize("g_val", [-7.0, -2.6])
+@pytest.mark.parametrize("g_val", [-12.0, -7.0, -4.5])
 def test_prefill_many_short_chunks(rg, g_val):
-    """Decays strong enough that a chunk's decay products leave the factored range after
-    about 10 (g = -7) or 25 (g = -2.6) tokens: chunks are cut at many different positions
-    relative to the 32-token grid, the accepted prefix and the ragged ends."""
+    """Decays strong enough that a chunk's decay products span more than 2^192 (the factored
+    range around the chunk's middle) after about 11 (g = -12), 19 (g = -7) or 29 (g = -4.5)
+    tokens: chunks are cut at many different positions relative to the 32-token grid, the
+    accepted prefix and the ragged ends."""
     inp = workloads.make_case(3, 1, 2, 160, 128, 128, 4, seed=7911, indices="choice",
                               lengths=[160, 131, 70])
     inp.num_accepted_tokens = np.array([160, 77, 5], np.int32)
