@@ -239,6 +239,17 @@ def test_prefill_long_sequence(rg):
     check_decode(inp, out, st, oracle_decode(inp), "prefill T=4096")
 
 
+def test_prefill_max_length(rg):
+    """The longest sequence the call accepts, 65536 tokens (2048 chunks), two value heads
+    sharing one query head: a full entry and a ragged one whose accepted prefix ends
+    mid-chunk, deep in the sequence."""
+    inp = workloads.make_case(2, 1, 2, 65536, 128, 128, 3, seed=7925, indices="choice",
+                              lengths=[65536, 60001])
+    inp.num_accepted_tokens = np.array([65536, 41234], np.int32)
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), "prefill T=65536")
+
+
 @pytest.mark.parametrize("g_val", [-12.0, -7.0, -4.5])
 def test_prefill_many_short_chunks(rg, g_val):
     """Decays strong enough that a chunk's decay products span more than 2^192 (the factored
