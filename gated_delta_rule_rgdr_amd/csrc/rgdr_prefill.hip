@@ -33,10 +33,14 @@
 // S_end = diag(c'_last) (S'' + K'^T U) with K' the rows k_s / c'_s. Each row takes the
 // middle of its chunk, r = 2^(L_last / 2) with L_t = log2 c_t (sums of the decays' log2,
 // formed in log space so that no product under- or overflows), and the factored form needs
-// every c'_t within [2^-96, 2^96] (each factor and their products stay far from fp32
-// overflow and underflow): a chunk whose decay products span up to 2^192. A chunk in which
-// some row leaves that range is shortened (c_0 = 1, so at least one token remains); strong
-// decays therefore give shorter chunks, not a different arithmetic.
+// every c'_t within [2^-96, 2^96]: a chunk whose decay products span up to 2^192. Each
+// factor, and S'' (at most 2^96 times the state), then stays far from fp32's limits. Every
+// pair the form keeps (s <= t) has c'_t / c'_s = c_t / c_s <= 1 in the operator's domain,
+// so its products stay within the operands' size. The pairs above the diagonal may
+// overflow: the forward substitution never reads them, and the N blocks replace them by
+// zeros with a select, so an inf or NaN there never reaches a kept entry. A chunk in which some row leaves that range is shortened (a
+// row's first token lies within it, so at least one token remains); strong decays
+// therefore give shorter chunks, not a different arithmetic.
 //
 // A chunk that holds the accepted prefix's end stops there, so the committed state is a
 // chunk's end state; the later tokens still produce their outputs. The next chunk's operands

@@ -182,7 +182,8 @@ rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *va
  * Tokens are evaluated in chunks of at most 32 in the exact closed form of the recurrence,
  * whose dense products run on the matrix cores with operands split into bf16 high parts and
  * remainders (about 16 bits of each operand, fp32 accumulation); a chunk whose decay
- * products span more than 2^192 is shortened, which changes time, not results.
+ * products span more than 2^192 is shortened. That costs time and moves rounding, since
+ * chunk boundaries group the arithmetic, but leaves the precision unchanged.
  * Errors: as rgdr_decode (RGDR_ERR_SHAPE for T > 65536 or T * H_v > 2^29).
  */
 rgdr_status rgdr_prefill(const void *query, const void *key, const void *value,
