@@ -30,7 +30,8 @@ import os
 
 import torch
 
-__all__ = ["rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated", "rgdr_prefill", "rgdr_prefill_gated",
+__all__ = ["rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated",
+           "rgdr_decode_gated_snapshots", "rgdr_prefill", "rgdr_prefill_gated",
            "recurrent_gated_delta_rule", "la_gate",
            "rgdr_validate", "VALIDATE",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
@@ -65,6 +66,9 @@ def library():
     lib.rgdr_decode_gated.restype = C.c_int
     lib.rgdr_decode_gated.argtypes = ([vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7
                                       + [vp] * 2 + [C.c_uint32, vp])
+    lib.rgdr_decode_gated_snapshots.restype = C.c_int
+    lib.rgdr_decode_gated_snapshots.argtypes = ([vp] * 7 + [C.c_int] + [vp] * 5 + [f32]
+                                                + [i32] * 7 + [vp] * 3 + [C.c_uint32, vp])
     lib.rgdr_prefill.restype = C.c_int
     lib.rgdr_prefill.argtypes = lib.rgdr_decode.argtypes
     lib.rgdr_prefill_gated.restype = C.c_int
@@ -155,6 +159,16 @@ def rgdr_decode_snapshots(query, key, value, beta, state_pool, actual_seq_length
     its slot is valid, and holds the state after its first ``t + 1`` tokens; other entries
     keep what the buffer held.
     """
+    state_snapshots = _snapshot_buffer(query, value, state_pool, state_snapshots)
+    out, state_out = _plain_call("rgdr_decode_snapshots", query, key, value, beta, state_pool,
+                                 actual_seq_lengths, ssm_state_indices, g, gk,
+                                 num_accepted_tokens, scale, out, state_out, stream,
+                                 extra={"state_snapshots": state_snapshots})
+    return out, state_out, state_snapshots
+
+
+def _snapshot_buffer(query, value, state_pool, state_snapshots):
+    """The per-token state buffer of a snapshot call: checked, or allocated uninitialised."""
     if not isinstance(query, torch.Tensor) or not isinstance(value, torch.Tensor) \
             or not isinstance(state_pool, torch.Tensor):
         raise TypeError("query, value and state_pool must be torch.Tensor")
@@ -163,17 +177,11 @@ def rgdr_decode_snapshots(query, key, value, beta, state_pool, actual_seq_length
     B, _, T, Dk = query.shape
     Hv, Dv = value.shape[1], value.shape[3]
     if state_snapshots is None:
-        state_snapshots = torch.empty((B, T, Hv, Dk, Dv), dtype=torch.bfloat16,
-                                      device=query.device)
-    else:
-        _dev(state_snapshots, "state_snapshots", torch.bfloat16, 5)
-        if tuple(state_snapshots.shape) != (B, T, Hv, Dk, Dv):
-            raise RuntimeError("state_snapshots must be [B, T, H_v, D_k, D_v]")
-    out, state_out = _plain_call("rgdr_decode_snapshots", query, key, value, beta, state_pool,
-                                 actual_seq_lengths, ssm_state_indices, g, gk,
-                                 num_accepted_tokens, scale, out, state_out, stream,
-                                 extra={"state_snapshots": state_snapshots})
-    return out, state_out, state_snapshots
+        return torch.empty((B, T, Hv, Dk, Dv), dtype=torch.bfloat16, device=query.device)
+    _dev(state_snapshots, "state_snapshots", torch.bfloat16, 5)
+    if tuple(state_snapshots.shape) != (B, T, Hv, Dk, Dv):
+        raise RuntimeError("state_snapshots must be [B, T, H_v, D_k, D_v]")
+    return state_snapshots
 
 
 def rgdr_prefill(query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
@@ -257,6 +265,22 @@ def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
                        num_accepted_tokens, scale, normalize_qk, out, state_out, stream)
 
 
+def rgdr_decode_gated_snapshots(query, key, value, a, b, dt_bias, decay_scale, state_pool,
+                                actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens,
+                                scale=1.0, *, normalize_qk=False, out=None, state_out=None,
+                                state_snapshots=None, stream=None):
+    """``rgdr_decode_gated`` that also stores the state after every token, as
+    ``rgdr_decode_snapshots`` extends ``rgdr_decode``; returns
+    ``(out, state_out, state_snapshots)`` with the buffer as described there."""
+    state_snapshots = _snapshot_buffer(query, value, state_pool, state_snapshots)
+    out, state_out = _gated_call("rgdr_decode_gated_snapshots", query, key, value, a, b,
+                                 dt_bias, decay_scale, state_pool, actual_seq_lengths,
+                                 ssm_state_indices, gk, num_accepted_tokens, scale,
+                                 normalize_qk, out, state_out, stream,
+                                 extra={"state_snapshots": state_snapshots})
+    return out, state_out, state_snapshots
+
+
 def rgdr_prefill_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
                        actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens,
                        scale=1.0, *, normalize_qk=False, out=None, state_out=None,
@@ -270,7 +294,8 @@ def rgdr_prefill_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool
 
 def _gated_call(fn, query, key, value, a, b, dt_bias, decay_scale, state_pool,
                 actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens, scale,
-                normalize_qk, out, state_out, stream):
+                normalize_qk, out, state_out, stream, extra=None):
+    extra = extra or {}  # further output buffers, passed after state_out in this order
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
     B, Hq, T, Dk = query.shape
@@ -312,7 +337,8 @@ def _gated_call(fn, query, key, value, a, b, dt_bias, decay_scale, state_pool,
     _same_device(query, key=key, value=value, a=a, b=b, dt_bias=dt_bias,
                  decay_scale=decay_scale, state_pool=state_pool,
                  actual_seq_lengths=actual_seq_lengths, ssm_state_indices=ssm_state_indices,
-                 gk=gk, num_accepted_tokens=num_accepted_tokens, out=out, state_out=state_out)
+                 gk=gk, num_accepted_tokens=num_accepted_tokens, out=out, state_out=state_out,
+                 **extra)
     if VALIDATE:
         _validate_indices(actual_seq_lengths, ssm_state_indices, num_accepted_tokens, T, N)
     with torch.cuda.device(query.device):
@@ -323,6 +349,7 @@ def _gated_call(fn, query, key, value, a, b, dt_bias, decay_scale, state_pool,
                               ssm_state_indices.data_ptr(), gk.data_ptr(),
                               num_accepted_tokens.data_ptr(), float(scale), B, Hq, Hv, T,
                               Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
+                              *[t.data_ptr() for t in extra.values()],
                               NORMALIZE_QK if normalize_qk else 0,
                               _stream_handle(stream, query.device))
     _check(rc, fn)

@@ -745,7 +745,7 @@ __global__ __launch_bounds__(64, RGDR_WAVE_MIN_WAVES) void decode_wave_multi_ker
 // elements of rows 16 rb + 4 kg + i, column 64 w + 4 n16 + c: the lane scales its own loaded
 // values into it, and the update lands in the layout the commit stores.
 //
-// SNAP (rgdr_decode_snapshots): the state after token t is the same expression with n - 1
+// SNAP (the snapshot entries): the state after token t is the same expression with n - 1
 // replaced by t, S_t = diag(c_t) S0 + sum_{s<=t} (g(t,s) k_s) (x) u_s, so after the solve the
 // commit's products are taken once per t < L, with each row's weights for t, and stored to
 // snapshot t (and, for t = n - 1, to the pool).
@@ -1236,12 +1236,10 @@ template <int DK, int TV, int GATE>
 static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
                                     const int32_t *idx, const int32_t *nacc,
                                     hipStream_t stream) {
-    if constexpr (GATE == kGateGiven) {  // per-token states: rgdr_decode_snapshots only
-        if (a.snap) {
-            hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE, true>), dim3(a.n_items),
-                               dim3(64), 0, stream, a, lens, idx, nacc);
-            return hipGetLastError();
-        }
+    if (a.snap) {  // per-token states (the snapshot entries)
+        hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE, true>), dim3(a.n_items),
+                           dim3(64), 0, stream, a, lens, idx, nacc);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((decode_wave_multi_kernel<DK, TV, GATE, false>), dim3(a.n_items),
                        dim3(64), 0, stream, a, lens, idx, nacc);
@@ -1253,12 +1251,10 @@ static hipError_t launch_wave_multi(const DecodeArgs &a, const int32_t *lens,
 template <int DK, int GATE>
 static hipError_t launch_chunk(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                const int32_t *nacc, hipStream_t stream) {
-    if constexpr (GATE == kGateGiven) {  // per-token states: rgdr_decode_snapshots only
-        if (a.snap) {
-            hipLaunchKernelGGL((decode_chunk_kernel<DK, GATE, true>), dim3(a.n_items), dim3(128),
-                               0, stream, a, lens, idx, nacc);
-            return hipGetLastError();
-        }
+    if (a.snap) {  // per-token states (the snapshot entries)
+        hipLaunchKernelGGL((decode_chunk_kernel<DK, GATE, true>), dim3(a.n_items), dim3(128), 0,
+                           stream, a, lens, idx, nacc);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((decode_chunk_kernel<DK, GATE>), dim3(a.n_items), dim3(128), 0, stream, a,
                        lens, idx, nacc);
@@ -1415,22 +1411,22 @@ extern "C" rgdr_status rgdr_decode_snapshots(
                         ssm_state_indices, num_accepted_tokens, stream);
 }
 
-extern "C" rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *value,
-                                         const void *gate_a, const void *gate_b,
-                                         const float *dt_bias, const float *decay_scale,
-                                         rgdr_dtype gate_dtype, const void *state_pool,
-                                         const int32_t *actual_seq_lengths,
-                                         const int32_t *ssm_state_indices, const float *gk,
-                                         const int32_t *num_accepted_tokens, float scale,
-                                         int32_t B, int32_t H_q, int32_t H_v, int32_t T,
-                                         int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
-                                         void *state_out, uint32_t flags, hipStream_t stream) {
-    using namespace rgdr;
+namespace rgdr {
+// Argument checks and marshalling shared by the two fused-gate decode entries.
+static rgdr_status decode_gated(const void *query, const void *key, const void *value,
+                                const void *gate_a, const void *gate_b, const float *dt_bias,
+                                const float *decay_scale, rgdr_dtype gate_dtype,
+                                const void *state_pool, const int32_t *actual_seq_lengths,
+                                const int32_t *ssm_state_indices, const float *gk,
+                                const int32_t *num_accepted_tokens, float scale, int32_t B,
+                                int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
+                                int32_t N_slots, void *out, void *state_out, void *snap,
+                                bool snap_required, uint32_t flags, hipStream_t stream) {
     if (flags & ~(uint32_t)RGDR_NORMALIZE_QK) return RGDR_ERR_UNSUPPORTED;
     if (B == 0) return RGDR_OK;
     if (!query || !key || !value || !gate_a || !gate_b || !dt_bias || !decay_scale ||
         !state_pool || !actual_seq_lengths || !ssm_state_indices || !gk ||
-        !num_accepted_tokens || !out || !state_out)
+        !num_accepted_tokens || !out || !state_out || (snap_required && !snap))
         return RGDR_ERR_NULL;
     if (gate_dtype != RGDR_F32 && gate_dtype != RGDR_F16) return RGDR_ERR_DTYPE;
     const uintptr_t esz = gate_dtype == RGDR_F16 ? 2 : 4;
@@ -1450,8 +1446,39 @@ extern "C" rgdr_status rgdr_decode_gated(const void *query, const void *key, con
     a.norm_qk = (flags & RGDR_NORMALIZE_QK) ? 1 : 0;
     a.out = static_cast<uint16_t *>(out);
     a.pool_out = static_cast<uint16_t *>(state_out);
+    a.snap = static_cast<uint16_t *>(snap);
     a.scale = scale;
     return decode_entry(a, gate_dtype == RGDR_F16 ? kGateF16 : kGateF32, B, H_q, H_v, T, D_k,
                         D_v, N_slots, actual_seq_lengths, ssm_state_indices,
                         num_accepted_tokens, stream);
+}
+}  // namespace rgdr
+
+extern "C" rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *value,
+                                         const void *gate_a, const void *gate_b,
+                                         const float *dt_bias, const float *decay_scale,
+                                         rgdr_dtype gate_dtype, const void *state_pool,
+                                         const int32_t *actual_seq_lengths,
+                                         const int32_t *ssm_state_indices, const float *gk,
+                                         const int32_t *num_accepted_tokens, float scale,
+                                         int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                         int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                                         void *state_out, uint32_t flags, hipStream_t stream) {
+    return rgdr::decode_gated(query, key, value, gate_a, gate_b, dt_bias, decay_scale,
+                              gate_dtype, state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                              num_accepted_tokens, scale, B, H_q, H_v, T, D_k, D_v, N_slots, out,
+                              state_out, nullptr, false, flags, stream);
+}
+
+extern "C" rgdr_status rgdr_decode_gated_snapshots(
+    const void *query, const void *key, const void *value, const void *gate_a,
+    const void *gate_b, const float *dt_bias, const float *decay_scale, rgdr_dtype gate_dtype,
+    const void *state_pool, const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+    const float *gk, const int32_t *num_accepted_tokens, float scale, int32_t B, int32_t H_q,
+    int32_t H_v, int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+    void *state_out, void *state_snapshots, uint32_t flags, hipStream_t stream) {
+    return rgdr::decode_gated(query, key, value, gate_a, gate_b, dt_bias, decay_scale,
+                              gate_dtype, state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                              num_accepted_tokens, scale, B, H_q, H_v, T, D_k, D_v, N_slots, out,
+                              state_out, state_snapshots, true, flags, stream);
 }

@@ -12,7 +12,8 @@
  *                  2. read    kv = S^T k_t
  *                  3. update  S = S + k_t (x) ((v_t - kv) * beta[t])   (outer product)
  *                  4. output  o_t = S^T (q_t * scale)
- *                rgdr_decode_snapshots also stores S after every token.
+ *                rgdr_decode_snapshots (and rgdr_decode_gated_snapshots, with the gate
+ *                fused in) also store S after every token.
  *   rgdr_prefill The same recurrence over long sequences (T up to 65536): the page's notes
  *                limit the decode operator to T <= 8 and hand the parallel prefill to a
  *                chunk-level operator; this is that operator, with rgdr_decode's arguments.
@@ -169,6 +170,28 @@ rgdr_status rgdr_decode_gated(const void *query, const void *key, const void *va
                               int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
                               int32_t N_slots, void *out, void *state_out, uint32_t flags,
                               hipStream_t stream);
+
+/*
+ * rgdr_decode_gated_snapshots -- rgdr_decode_gated that also stores the state after every
+ * token, as rgdr_decode_snapshots extends rgdr_decode (the same speculative-decoding use of
+ * the page's num_accepted_tokens, with the gate computed in the kernel).
+ *
+ *   state_snapshots  bf16 [B, T, H_v, D_k, D_v], 16-byte aligned, owned by the caller;
+ *                    written exactly as by rgdr_decode_snapshots.
+ *   All other arguments, results and errors: as rgdr_decode_gated (RGDR_ERR_NULL also for
+ *   state_snapshots, RGDR_ERR_ALIGN for its alignment).
+ */
+rgdr_status rgdr_decode_gated_snapshots(const void *query, const void *key, const void *value,
+                                        const void *gate_a, const void *gate_b,
+                                        const float *dt_bias, const float *decay_scale,
+                                        rgdr_dtype gate_dtype, const void *state_pool,
+                                        const int32_t *actual_seq_lengths,
+                                        const int32_t *ssm_state_indices, const float *gk,
+                                        const int32_t *num_accepted_tokens, float scale,
+                                        int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                        int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                                        void *state_out, void *state_snapshots, uint32_t flags,
+                                        hipStream_t stream);
 
 /*
  * rgdr_prefill -- the recurrence of rgdr_decode over a long sequence per batch entry

@@ -5,6 +5,7 @@ Tolerance for bf16 outputs produced from fp32 arithmetic, against the UNROUNDED 
 oracle value: |gpu - ref| <= 2e-2 + 2e-2 |ref| per element. Indexing, padding and
 untouched slots are compared bit for bit.
 """
+import copy
 import sys
 
 import numpy as np
@@ -187,14 +188,42 @@ def check_gated(inp, out_t, st_t, ref, label, entries=None):
 SENTINEL = np.uint16(0xFFED)  # a quiet NaN whose payload no rounding produces
 
 
+def _sentinel_buffer(inp):
+    return torch.full((inp.B, inp.T, inp.Hv, inp.Dk, inp.Dv), int(SENTINEL.view(np.int16)),
+                      dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def _check_snapshot_buffer(inp, snap, st, o_snaps, label):
+    """Every written entry within the bar of the oracle's state after that token, every other
+    entry still the sentinel, and the entry after the accepted prefix equal to the committed
+    slot's bytes."""
+    got = bf16_dev_to_f64(snap)
+    bits = dev_to_bits(snap)
+    pool_bits = dev_to_bits(st)
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    written = np.zeros((inp.B, inp.T), bool)
+    for b in range(inp.B):
+        if valid[b]:
+            written[b, :lens[b]] = True
+    assert np.isfinite(o_snaps[written]).all()
+    assert_tol(got[written], o_snaps[written], f"{label} snapshots")
+    assert np.all(bits[~written] == SENTINEL), f"{label}: unwritten snapshot entries changed"
+    n_acc = np.clip(inp.num_accepted_tokens, 0, lens)
+    for b in range(inp.B):
+        if valid[b] and n_acc[b] >= 1:
+            assert np.array_equal(bits[b, n_acc[b] - 1], pool_bits[inp.ssm_state_indices[b]]), \
+                f"{label}: entry {b}: snapshot {n_acc[b] - 1} is not the committed state"
+    say(f"  {label}: {int(written.sum())} snapshot entries written")
+
+
 def check_snapshots(rg, inp, label):
     """Run rgdr_decode_snapshots on a sentinel-filled buffer and compare out, the committed
     slots and every snapshot entry with the oracle; unwritten entries must keep the
     sentinel, and the snapshot after the accepted prefix must be the committed slot's bytes."""
     d = upload(inp)
     pool = d["state"].clone()
-    snap = torch.full((inp.B, inp.T, inp.Hv, inp.Dk, inp.Dv), int(SENTINEL.view(np.int16)),
-                      dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    snap = _sentinel_buffer(inp)
     out, st, snap_r = rg.rgdr_decode_snapshots(
         d["query"], d["key"], d["value"], d["beta"], pool, d["actual_seq_lengths"],
         d["ssm_state_indices"], d["g"], d["gk"], d["num_accepted_tokens"], inp.scale,
@@ -205,10 +234,6 @@ def check_snapshots(rg, inp, label):
         inp.query, inp.key, inp.value, inp.beta, inp.state, inp.actual_seq_lengths,
         inp.ssm_state_indices, inp.g, inp.gk, inp.num_accepted_tokens, inp.scale)
     check_decode(inp, out, st, (o_out, o_pool, o_rows), label)
-
-    got = bf16_dev_to_f64(snap)
-    bits = dev_to_bits(snap)
-    pool_bits = dev_to_bits(st)
     lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
     valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
     written = np.zeros((inp.B, inp.T), bool)
@@ -216,11 +241,29 @@ def check_snapshots(rg, inp, label):
         if valid[b]:
             written[b, :lens[b]] = True
     assert np.array_equal(np.isfinite(o_snaps).all(axis=(2, 3, 4)), written)
-    assert_tol(got[written], o_snaps[written], f"{label} snapshots")
-    assert np.all(bits[~written] == SENTINEL), f"{label}: unwritten snapshot entries changed"
-    n_acc = np.clip(inp.num_accepted_tokens, 0, lens)
-    for b in range(inp.B):
-        if valid[b] and n_acc[b] >= 1:
-            assert np.array_equal(bits[b, n_acc[b] - 1], pool_bits[inp.ssm_state_indices[b]]), \
-                f"{label}: entry {b}: snapshot {n_acc[b] - 1} is not the committed state"
-    say(f"  {label}: {int(written.sum())} snapshot entries written")
+    _check_snapshot_buffer(inp, snap, st, o_snaps, label)
+
+
+def check_gated_snapshots(rg, inp, label, dtype=np.float32, normalize_qk=False):
+    """Run rgdr_decode_gated_snapshots on a sentinel-filled buffer. out and the committed
+    slots are compared with the oracle chain (la_gate, then the recurrence) as for
+    rgdr_decode_gated. Snapshot t of an entry is compared with the state that the same chain
+    commits when t + 1 tokens are accepted, which is that snapshot's definition. Buffer
+    checks as check_snapshots."""
+    d = upload(inp)
+    a, b, dt, ds = gate_tensors(inp, dtype)
+    pool = d["state"].clone()
+    snap = _sentinel_buffer(inp)
+    out, st, snap_r = rg.rgdr_decode_gated_snapshots(
+        d["query"], d["key"], d["value"], a, b, dt, ds, pool, d["actual_seq_lengths"],
+        d["ssm_state_indices"], d["gk"], d["num_accepted_tokens"], inp.scale,
+        normalize_qk=normalize_qk, state_snapshots=snap)
+    torch.cuda.synchronize()
+    assert snap_r.data_ptr() == snap.data_ptr()
+    check_gated(inp, out, st, oracle_gated(inp, dtype=dtype, normalize_qk=normalize_qk), label)
+    o_snaps = np.full((inp.B, inp.T, inp.Hv, inp.Dk, inp.Dv), np.nan)
+    for t in range(inp.T):
+        prefix = copy.copy(inp)
+        prefix.num_accepted_tokens = np.full(inp.B, t + 1, np.int32)
+        o_snaps[:, t] = oracle_gated(prefix, dtype=dtype, normalize_qk=normalize_qk)[1]
+    _check_snapshot_buffer(inp, snap, st, o_snaps, label)

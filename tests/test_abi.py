@@ -31,8 +31,8 @@ def lib():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for want in ("rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated", "rgdr_prefill",
-                 "rgdr_prefill_gated",
+    for want in ("rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated",
+                 "rgdr_decode_gated_snapshots", "rgdr_prefill", "rgdr_prefill_gated",
                  "la_gate", "rgdr_validate", "rgdr_validate_host", "rgdr_status_string"):
         assert want in names, names
 
@@ -193,11 +193,44 @@ def test_gated_decode_argument_checks(lib):
     p = [0x10000] * 12
     p[3] = 0x10002  # fp32 gate projection a not 4-byte aligned
     assert _gated(lib, ptrs=p) == ALIGN
-    assert _gated(lib, ptrs=p, gdt=F16) != ALIGN  # fp16 needs only 2-byte alignment: goes on
+    # fp16 needs only 2-byte alignment: the call passes the alignment check and stops at the
+    # next host check (more than 2^31 items), so nothing is launched on any machine
+    assert _gated(lib, ptrs=p, gdt=F16, T=2, B=1 << 20, Hq=1 << 10, Hv=1 << 10, Dv=4096) == SHAPE
     # option bits: RGDR_NORMALIZE_QK (1) is known, any other bit is refused before launch
     assert _gated(lib, flags=2) == UNSUP
     assert _gated(lib, flags=0x80000001) == UNSUP
     assert _gated(lib, ptrs=[None] * 12, B=0, out=None, state_out=None, flags=1) == OK
+
+
+def _gated_snapshots(lib, ptrs=None, gdt=F32, **kw):
+    dims = dict(B=2, Hq=2, Hv=4, T=4, Dk=128, Dv=128, N=4)
+    dims.update(kw)
+    p = [0x10000] * 12 if ptrs is None else ptrs
+    return lib.rgdr_decode_gated_snapshots(
+        *p[:7], gdt, *p[7:12], 1.0, dims["B"], dims["Hq"], dims["Hv"], dims["T"], dims["Dk"],
+        dims["Dv"], dims["N"], kw.get("out", 0x20000), kw.get("state_out", 0x30000),
+        kw.get("snap", 0x40000), kw.get("flags", 0), None)
+
+
+def test_gated_snapshots_argument_checks(lib):
+    assert _gated_snapshots(lib, ptrs=[None] * 12, B=0, out=None, state_out=None,
+                            snap=None) == OK
+    for i in range(12):
+        p = [0x10000] * 12
+        p[i] = None
+        assert _gated_snapshots(lib, ptrs=p) == NULL, i
+    assert _gated_snapshots(lib, snap=None) == NULL
+    assert _gated_snapshots(lib, snap=0x40008) == ALIGN  # snapshots not 16-byte aligned
+    assert _gated_snapshots(lib, gdt=BF16) == DTYPE
+    assert _gated_snapshots(lib, flags=2) == UNSUP
+    assert _gated_snapshots(lib, snap=None, flags=2) == UNSUP  # flags are checked first
+    assert _gated_snapshots(lib, T=9) == SHAPE
+    assert _gated_snapshots(lib, Hq=3) == SHAPE
+    assert _gated_snapshots(lib, Dk=96) == UNSUP
+    assert _gated_snapshots(lib, Dv=96) == UNSUP
+    p = [0x10000] * 12
+    p[4] = 0x10002  # fp32 gate projection b not 4-byte aligned
+    assert _gated_snapshots(lib, ptrs=p) == ALIGN
 
 
 def test_gate_argument_checks(lib):

@@ -1,6 +1,7 @@
-"""GPU parity of rgdr_decode_snapshots: the decode step that also stores the state after
-every token (the per-prefix states a speculative-decoding caller needs when it learns the
-accepted count, the page's num_accepted_tokens, only after the step).
+"""GPU parity of rgdr_decode_snapshots and rgdr_decode_gated_snapshots: the decode step
+(plain, or with the gate fused in) that also stores the state after every token (the
+per-prefix states a speculative-decoding caller needs when it learns the accepted count,
+the page's num_accepted_tokens, only after the step).
 
 Against the fp64 oracle on the same seeded bytes:
   - out and the committed slots: as rgdr_decode (2e-2 + 2e-2 |ref|, indexing bit for bit);
@@ -15,7 +16,8 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import check_snapshots as run_and_check, dev_to_bits, say, upload
+from gpu_util import (bf16_dev_to_f64, check_gated_snapshots,
+                      check_snapshots as run_and_check, dev_to_bits, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,3 +148,88 @@ def test_snapshots_graph_replay_matches_eager(rg):
             assert np.array_equal(got[2][b, :lens[b]], want[2][b, :lens[b]]), \
                 f"replay {rep}: snapshots of entry {b} differ"
     say("  snapshot graph replays equal the eager call")
+
+
+GATED_CASES = [
+    # B, Hq, Hv, T, Dk, Dv, N, seed, lengths, n_acc, gate dtype, normalize q/k
+    (6, 2, 4, 5, 128, 256, 9, 31, "uniform", "draw", np.float32, False),  # chunk form
+    (4, 2, 4, 8, 128, 128, 6, 32, "uniform", "draw", np.float16, True),   # fp16 gate, norm
+    (5, 1, 2, 3, 64, 64, 7, 33, "uniform", "draw", np.float32, True),     # per-token form
+    (3, 4, 4, 8, 64, 128, 3, 34, [8, 1, 6], [3, 1, 0], np.float16, False),  # D_k = 64
+    (4, 2, 4, 1, 128, 128, 4, 35, [1, 0, 1, 1], None, np.float32, False),  # T = 1
+    (3, 2, 2, 8, 128, 320, 4, 36, "uniform", "draw", np.float32, True),   # half last tile
+]
+
+
+@pytest.mark.parametrize("case", range(len(GATED_CASES)))
+def test_gated_snapshots_parity(rg, case):
+    B, Hq, Hv, T, Dk, Dv, N, seed, lengths, nacc, dtype, norm = GATED_CASES[case]
+    inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, N, seed, indices="choice",
+                              lengths=lengths, gate=True)
+    if nacc == "draw":
+        rng = np.random.default_rng(seed + 100)
+        inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
+    elif nacc is not None:
+        inp.num_accepted_tokens = np.asarray(nacc, np.int32)
+    say(f"gated snapshots case {case}: B={B} Hq={Hq} Hv={Hv} T={T} Dk={Dk} Dv={Dv} "
+        f"gate {np.dtype(dtype).name} norm={norm} L={inp.actual_seq_lengths.tolist()} "
+        f"n={inp.num_accepted_tokens.tolist()}")
+    check_gated_snapshots(rg, inp, f"gated snapshots case {case}", dtype=dtype,
+                          normalize_qk=norm)
+
+
+def test_gated_snapshots_skipped_slot_and_clamps(rg):
+    """With the gate fused in: a skipped slot writes no snapshot; lengths above T and
+    accepted counts above L are clamped."""
+    inp = workloads.make_case(4, 2, 4, 6, 128, 128, 6, 37, indices="choice",
+                              lengths=[6, 9, 3, 6], gate=True)
+    inp.ssm_state_indices[2] = 6  # == N_slots: skipped
+    inp.num_accepted_tokens = np.asarray([2, 9, 3, 7], np.int32)
+    say("gated snapshots: skipped slot, clamped length and count")
+    check_gated_snapshots(rg, inp, "gated snapshots skipped/clamped")
+
+
+def test_gated_snapshots_workload3(rg):
+    """The varlen speculative workload at full size with raw gate projections."""
+    inp = workloads.make_workload(3, gate_inputs=True)
+    say(f"gated snapshots: {workloads.WORKLOAD_NAMES[3]}")
+    check_gated_snapshots(rg, inp, "gated snapshots workload 3")
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+def test_snapshot_calls_match_their_plain_calls(rg, gated):
+    """A snapshot call's out and committed slots against the same call without snapshots,
+    on the same inputs. out is bit for bit in both kernel forms, and so are the committed
+    slots in the per-token form. The chunk form's snapshot loop forms each row's key
+    weights g(t, s) k_s in another order (decay products first), so its committed slots may
+    differ by one bf16 unit in the last place."""
+    for Dk, Dv, T, form in ((128, 128, 8, "chunk"), (64, 64, 3, "per-token")):
+        inp = workloads.make_case(4, 2, 4, T, Dk, Dv, 6, 38 + T, indices="choice",
+                                  lengths="uniform", gate=gated)
+        rng = np.random.default_rng(39)
+        inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
+        d = upload(inp)
+        tail = (d["actual_seq_lengths"], d["ssm_state_indices"], d["gk"],
+                d["num_accepted_tokens"], inp.scale)
+        p1, p2 = d["state"].clone(), d["state"].clone()
+        if gated:
+            gate = tuple(torch.from_numpy(x).cuda()
+                         for x in (inp.gate_a, inp.gate_b, inp.dt_bias, inp.decay_scale))
+            head = (d["query"], d["key"], d["value"]) + gate
+            o1, s1 = rg.rgdr_decode_gated(*head, p1, *tail)
+            o2, s2, _ = rg.rgdr_decode_gated_snapshots(*head, p2, *tail)
+        else:
+            head = (d["query"], d["key"], d["value"], d["beta"])
+            plain_tail = (d["actual_seq_lengths"], d["ssm_state_indices"], d["g"], d["gk"],
+                          d["num_accepted_tokens"], inp.scale)
+            o1, s1 = rg.rgdr_decode(*head, p1, *plain_tail)
+            o2, s2, _ = rg.rgdr_decode_snapshots(*head, p2, *plain_tail)
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_to_bits(o1), dev_to_bits(o2)), f"{form}: out differs"
+        if form == "per-token":
+            assert np.array_equal(dev_to_bits(s1), dev_to_bits(s2)), f"{form}: state differs"
+        else:
+            a1, a2 = bf16_dev_to_f64(s1), bf16_dev_to_f64(s2)
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(a1), 1e-30))) - 7)
+            assert np.all(np.abs(a1 - a2) <= ulp), f"{form}: state differs by more than 1 ulp"
+            say(f"  {form}: {int((a1 != a2).sum())} of {a1.size} state values differ by 1 ulp")
