@@ -46,6 +46,7 @@
 // chunk's end state; the later tokens still produce their outputs. The next chunk's operands
 // are loaded while the current one is computed. HBM sees the state once in and once out,
 // and every operand once.
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -155,6 +156,27 @@ __device__ __forceinline__ void split8(const f32x4 &x0, const f32x4 &x1, bf16x8 
     lo = __builtin_bit_cast(bf16x8, u32x4{l0.x, l0.y, l1.x, l1.y});
 }
 __device__ __forceinline__ s16x4 as_s16x4(uint2 v) { return __builtin_bit_cast(s16x4, v); }
+
+// NW consecutive 32-bit words (2 NW bf16 columns of one row) in one buffer access.
+template <int NW, int POL>
+__device__ __forceinline__ void load_words(uint32_t (&w)[NW], __amdgpu_buffer_rsrc_t rs,
+                                           uint32_t voff, uint32_t soff) {
+    if constexpr (NW == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, POL);
+    } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, POL);
+        w[0] = v.x;
+        w[1] = v.y;
+    }
+}
+template <int NW, int POL>
+__device__ __forceinline__ void store_words(const uint32_t (&w)[NW], __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t voff, uint32_t soff) {
+    if constexpr (NW == 1)
+        __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, voff, soff, POL);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rs, voff, soff, POL);
+}
 __device__ __forceinline__ bf16x8 cat8(uint2 a, uint2 b) {
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
@@ -203,22 +225,26 @@ __device__ __forceinline__ f32x4 mma16(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
 }
 
-// Lane layout of the state. Wave w owns tile columns 32 w .. 32 w + 31 over all D_k rows.
-// Lane l = (kg, n16) = (l / 16, l % 16) holds rows 16 rb + 4 kg + i (rb < D_k / 16, i < 4) of
-// columns 32 w + 2 n16 + c (c < 2) as S[rb][c][i]: the accumulator layout of the 16 x 16 block
-// of rows 16 rb .. + 15 and columns 32 w + 2 n + c (column set c). Rows 4 kg .. 4 kg + 3 of two
+// Lane layout of the state. Wave w owns the WC = 16 NC tile columns WC w .. WC w + WC - 1
+// over all D_k rows (NC = 2: 128-column tiles; NC = 4: 256-column tiles, D_k = 64 only, where
+// the state still takes 64 values per lane). Lane l = (kg, n16) = (l / 16, l % 16) holds rows
+// 16 rb + 4 kg + i (rb < D_k / 16, i < 4) of columns WC w + NC n16 + c (c < NC) as
+// S[rb][c][i]: the accumulator layout of the 16 x 16 block of rows 16 rb .. + 15 and columns
+// WC w + NC n + c (column set c). Rows 4 kg .. 4 kg + 3 of two
 // row blocks are also the 8 k slots of lane group kg in a 16x16x32 product, so the state turns
 // into the B operand of Y = X S in the lane that holds it. The chunk's per-token results (Y_K,
 // Y_Q, U, O) use the same layout with tokens for rows: 16 tb + 4 kg + i is the token, and the
 // rows 4 kg .. + 3 of a 16-token block are the k slots of a 16x16x16 product over tokens.
-template <int DK, int GATE, bool NORM>
+template <int DK, int GATE, bool NORM, int NC>
 __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
     static_assert(DK == 64 || DK == 128, "D_k = 64 or 128");
     static_assert(!NORM || GATE != kGateGiven, "q/k normalisation belongs to the fused front end");
+    static_assert(NC == 2 || (NC == 4 && DK == 64), "256-column tiles at D_k = 64 only");
     using P = ChunkShape<DK>;
-    constexpr int TV = 128, NRB = P::NRB, NPB = P::NPB, TPT = P::TPT, NTG = P::NTG;
+    constexpr int WC = 16 * NC, TV = 4 * WC, NW = NC / 2;  // NW: 32-bit words per lane row
+    constexpr int NRB = P::NRB, NPB = P::NPB, TPT = P::TPT, NTG = P::NTG;
     constexpr int XS = P::XS, KS = P::KS, AS = P::AS, BS = P::BS;
     __shared__ f32x4 lds4[P::BYTES / 16];
     char *lb = reinterpret_cast<char *>(lds4);
@@ -244,19 +270,19 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const Item m = resolve(a, x, xcd_item(blockIdx.x, gridDim.x));
     const int L = m.L, n = m.n;
 
-    // A last tile of 64 columns (D_v an odd multiple of 64) leaves waves 2 and 3 without
+    // A narrower last tile (D_v not a multiple of the tile) leaves the waves past D_v without
     // columns: their state, value and output accesses get empty ranges and they compute on
     // zeros.
-    const bool cols = m.tile * TV + 32 * w < a.Dv;
+    const bool cols = m.tile * TV + WC * w < a.Dv;
     const uint32_t trange = cols ? tile_range<DK, TV>(a, m) : 0u;
     const size_t tb0 = m.state ? tile_base<DK, TV>(a, m) : 0;
     const auto rs = make_rsrc(a.pool + tb0, trange);
     const auto rso = make_rsrc(a.pool_out + tb0, trange);
-    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + 32 * w + 2 * n16) * 2);
+    const uint32_t lane_off = (uint32_t)((4 * kg * a.Dv + WC * w + NC * n16) * 2);
     const size_t bh = (size_t)m.b * a.Hv + m.h;
-    const uint32_t ocol = (uint32_t)((m.tile * TV + 32 * w + 2 * n16) * 2);
+    const uint32_t ocol = (uint32_t)((m.tile * TV + WC * w + NC * n16) * 2);
     // Token (or state row) 4 kg + i of a 16-row block: the lane's part in the vector offset,
-    // the rest in the scalar one (4-byte accesses only; see store16 for the wide ones).
+    // the rest in the scalar one (4- and 8-byte accesses only; see store16 for the wide ones).
     const uint32_t orow = ocol + (uint32_t)(4 * kg * a.Dv * 2);
     float dt = 0.f, ds = 0.f;
     if constexpr (GATE != kGateGiven) gate_head(a, m.h, dt, ds);
@@ -266,16 +292,15 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         const int t1 = min(t0 + kChunk, L);
         return ((t0 < n && n < t1) ? n : t1) - t0;
     };
-    // This lane's values of tokens 16 tb + 4 kg + i, columns 32 w + 2 n16 + (0, 1).
-    uint32_t vr[2][4];
+    // This lane's values of tokens 16 tb + 4 kg + i, columns WC w + NC n16 + (0 .. NC - 1).
+    uint32_t vr[2][4][NW];
     auto load_v = [&](int t0, int len) {
         const auto rv = make_rsrc(a.v + (bh * a.T + t0) * a.Dv, cols ? (uint32_t)(len * a.Dv * 2) : 0u);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                vr[tb][i] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rv, orow, (uint32_t)((16 * tb + i) * a.Dv * 2), 0);
+                load_words<NW, 0>(vr[tb][i], rv, orow, (uint32_t)((16 * tb + i) * a.Dv * 2));
     };
 
     // The first chunk's operands, then the state tile (bf16 -> fp32, exact).
@@ -283,29 +308,28 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     ChunkOps<DK> o;
     load_chunk<DK, GATE>(a, m, o, r, tg, lane, 0, len);
     load_v(0, len);
-    uint32_t raw[NRB][4];
+    uint32_t raw[NRB][4][NW];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            raw[rb][i] = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_LOAD_POLICY);
-    f32x4 S[NRB][2];
+            load_words<NW, RGDR_STATE_LOAD_POLICY>(raw[rb][i], rs, lane_off,
+                                                   (uint32_t)((16 * rb + i) * a.Dv * 2));
+    f32x4 S[NRB][NC];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            S[rb][0][i] = bf16_lo(raw[rb][i]);
-            S[rb][1][i] = bf16_hi(raw[rb][i]);
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                S[rb][c][i] = (c & 1) ? bf16_hi(raw[rb][i][c >> 1]) : bf16_lo(raw[rb][i][c >> 1]);
     if (n == 0) {  // nothing accepted: commit the incoming bytes
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    raw[rb][i], rso, lane_off, (uint32_t)((16 * rb + i) * a.Dv * 2),
-                    RGDR_STATE_STORE_POLICY);
+                store_words<NW, RGDR_STATE_STORE_POLICY>(raw[rb][i], rso, lane_off,
+                                                         (uint32_t)((16 * rb + i) * a.Dv * 2));
     }
     if (tid == 0) *cut = kChunk;
     lds_barrier();
@@ -589,29 +613,29 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         __builtin_amdgcn_s_setprio(2);
         // Y_K = [c k]^T S' and Y_Q = [c scale q]^T S' (32 tokens x this wave's 32 columns),
         // with S' = diag(d_0) S formed in place; three products of the split parts.
-        f32x4 yk[2][2], yq[2][2];
+        f32x4 yk[2][NC], yq[2][NC];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) yk[tb][c] = yq[tb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < NC; ++c) yk[tb][c] = yq[tb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const f32x4 dv = *reinterpret_cast<const f32x4 *>(d0row + 16 * (2 * pb + h) + 4 * kg);
-                S[2 * pb + h][0] *= dv;
-                S[2 * pb + h][1] *= dv;
-            }
-            bf16x8 sh[2], sl[2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) split8(S[2 * pb][c], S[2 * pb + 1][c], sh[c], sl[c]);
+                for (int c = 0; c < NC; ++c) S[2 * pb + h][c] *= dv;
+            }
+            bf16x8 sh[NC], sl[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) split8(S[2 * pb][c], S[2 * pb + 1][c], sh[c], sl[c]);
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 const int ra = (16 * tb + n16) * XS + 32 * pb + 4 * kg;
                 const bf16x8 kh = lds_pair8(xk_hi + ra, xk_hi + ra + 16), kl = lds_pair8(xk_lo + ra, xk_lo + ra + 16);
                 const bf16x8 qh = lds_pair8(xq_hi + ra, xq_hi + ra + 16), ql = lds_pair8(xq_lo + ra, xq_lo + ra + 16);
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
+                for (int c = 0; c < NC; ++c) {
                     yk[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, sh[c], yk[tb][c], 0, 0, 0);
                     yk[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, sh[c], yk[tb][c], 0, 0, 0);
                     yk[tb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, sl[c], yk[tb][c], 0, 0, 0);
@@ -628,30 +652,33 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 
         __builtin_amdgcn_s_setprio(3);
         // R = V - Y_K for the chunk's tokens (0 past Lc); then the next chunk's values.
-        f32x4 R[2][2];
+        f32x4 R[2][NC];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                R[tb][0][i] = bf16_lo(vr[tb][i]) - yk[tb][0][i];
-                R[tb][1][i] = bf16_hi(vr[tb][i]) - yk[tb][1][i];
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    R[tb][c][i] = ((c & 1) ? bf16_hi(vr[tb][i][c >> 1]) : bf16_lo(vr[tb][i][c >> 1])) -
+                                  yk[tb][c][i];
         if (Lc < kChunk)  // uniform: a short chunk's later tokens (their values may be anything)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (16 * tb + 4 * kg + i >= Lc) R[tb][0][i] = R[tb][1][i] = 0.f;
+                    if (16 * tb + 4 * kg + i >= Lc)
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) R[tb][c][i] = 0.f;
         load_v(t0n, lenn);
         auto blk4 = [&](int b, int lo) {
             return as_s16x4(*reinterpret_cast<const uint2 *>(blk(b) + lo * 16 * AS + n16 * AS + 4 * kg));
         };
         // U_0 = A_00 R_0; U_1 = A_11 (R_1 - M_10 U_0); O = Y_Q + N U (each product its own
         // 16x16x16 chain; the sums with Y_Q on the VALU).
-        uint2 u0h[2], u0l[2], u1h[2], u1l[2];
-        f32x4 ov[2][2];
+        uint2 u0h[NC], u0l[NC], u1h[NC], u1l[NC];
+        f32x4 ov[2][NC];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NC; ++c) {
             uint2 rh, rl;
             split4(R[0][c], rh, rl);
             const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -673,10 +700,12 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        pack_bf16x2(ov[tb][0][i], ov[tb][1][i]), rout, orow,
-                        (uint32_t)((16 * tb + i) * a.Dv * 2), 0);
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t wo[NW];
+#pragma unroll
+                    for (int j = 0; j < NW; ++j) wo[j] = pack_bf16x2(ov[tb][2 * j][i], ov[tb][2 * j + 1][i]);
+                    store_words<NW, 0>(wo, rout, orow, (uint32_t)((16 * tb + i) * a.Dv * 2));
+                }
         }
         // S = S' + KH^T U (the true state is diag(c_last) S), one 16x16x32 chain per block
         // over the chunk's tokens (k slots: tokens 4 kg .. + 3 of U_0, then of U_1).
@@ -685,7 +714,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             const int ra = (16 * rb + n16) * KS + 4 * kg;
             const bf16x8 ah = lds_pair8(kh_hi + ra, kh_hi + ra + 16), al = lds_pair8(kh_lo + ra, kh_lo + ra + 16);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, cat8(u0h[c], u1h[c]), S[rb][c], 0, 0, 0);
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, cat8(u0h[c], u1h[c]), S[rb][c], 0, 0, 0);
                 S[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, cat8(u0l[c], u1l[c]), S[rb][c], 0, 0, 0);
@@ -699,41 +728,77 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             for (int rb = 0; rb < NRB; ++rb) {
                 const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        pack_bf16x2(S[rb][0][i] * cr[i], S[rb][1][i] * cr[i]), rso, lane_off,
-                        (uint32_t)((16 * rb + i) * a.Dv * 2), RGDR_STATE_STORE_POLICY);
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t ws[NW];
+#pragma unroll
+                    for (int j = 0; j < NW; ++j)
+                        ws[j] = pack_bf16x2(S[rb][2 * j][i] * cr[i], S[rb][2 * j + 1][i] * cr[i]);
+                    store_words<NW, RGDR_STATE_STORE_POLICY>(ws, rso, lane_off,
+                                                             (uint32_t)((16 * rb + i) * a.Dv * 2));
+                }
             }
         }
         lds_barrier();  // the next chunk's preparation reuses every LDS area
     }
 
-    // Padded (or skipped) tokens: +0.0 rows. Lane (r, c4) stores 8 columns of row r of each
-    // group of 16 rows; rows past T fall outside the range.
+    // Padded (or skipped) tokens: +0.0 rows. Each lane stores 8 of the wave's WC columns of
+    // one row, in groups of 64 / (WC / 8) rows; rows past T fall outside the range.
     if (cols && L < a.T) {
+        constexpr int CG = WC / 8, RG = 64 / CG;  // 8-column groups per row, rows per store
         const int pad = a.T - L;
-        const auto rz = make_rsrc(a.out + (bh * a.T + L) * a.Dv + m.tile * TV + 32 * w,
-                                  (uint32_t)(((pad - 1) * a.Dv + 32) * 2));
-        const uint32_t zoff = (uint32_t)(((lane >> 2) * a.Dv + 8 * (lane & 3)) * 2);
-        for (int t = 0; t < pad; t += 16)
+        const auto rz = make_rsrc(a.out + (bh * a.T + L) * a.Dv + m.tile * TV + WC * w,
+                                  (uint32_t)(((pad - 1) * a.Dv + WC) * 2));
+        const uint32_t zoff = (uint32_t)(((lane / CG) * a.Dv + 8 * (lane % CG)) * 2);
+        for (int t = 0; t < pad; t += RG)
             store16<0>(u32x4{0u, 0u, 0u, 0u}, rz, zoff + (uint32_t)(t * a.Dv * 2));
     }
 }
 
 
-template <int DK, int GATE>
+template <int DK, int GATE, int NC>
 static hipError_t launch_prefill(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                  const int32_t *nacc, hipStream_t stream) {
     if constexpr (GATE != kGateGiven) {
         if (a.norm_qk) {
-            hipLaunchKernelGGL((prefill_kernel<DK, GATE, true>), dim3(a.n_items), dim3(256), 0,
-                               stream, a, lens, idx, nacc);
+            hipLaunchKernelGGL((prefill_kernel<DK, GATE, true, NC>), dim3(a.n_items), dim3(256),
+                               0, stream, a, lens, idx, nacc);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prefill_kernel<DK, GATE, false>), dim3(a.n_items), dim3(256), 0, stream,
-                       a, lens, idx, nacc);
+    hipLaunchKernelGGL((prefill_kernel<DK, GATE, false, NC>), dim3(a.n_items), dim3(256), 0,
+                       stream, a, lens, idx, nacc);
     return hipGetLastError();
+}
+
+template <int DK, int NC>
+static hipError_t launch_prefill_gate(int gate, const DecodeArgs &a, const int32_t *lens,
+                                      const int32_t *idx, const int32_t *nacc,
+                                      hipStream_t stream) {
+    return gate == kGateGiven ? launch_prefill<DK, kGateGiven, NC>(a, lens, idx, nacc, stream)
+           : gate == kGateF32 ? launch_prefill<DK, kGateF32, NC>(a, lens, idx, nacc, stream)
+                              : launch_prefill<DK, kGateF16, NC>(a, lens, idx, nacc, stream);
+}
+
+// Items of the D_k = 64 kernel with 128-column tiles that the current device holds at once
+// (compute units times workgroups per compute unit), queried once per device; 0 if the
+// query fails.
+static int prefill_resident_items_dk64() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, prefill_kernel<64, kGateGiven, false, 2>, 256, 0) != hipSuccess ||
+        per_cu <= 0)
+        return 0;
+    n = cus * per_cu;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
@@ -750,7 +815,17 @@ static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
-    const int ntiles = (D_v + 127) / 128;  // the last tile may be 64 columns wide
+    // Tiles of 128 columns (the last may be 64 wide). At D_k = 64, 256-column tiles (D_v a
+    // multiple of 256) when the call has more 128-column items than the device holds at once:
+    // half as many items, each with the state bytes of a D_k = 128 item, so fewer rounds of
+    // items pay the per-chunk work that does not scale with the columns.
+    int tile_v = 128;
+    if (D_k == 64 && D_v % 256 == 0) {
+        const int resident = prefill_resident_items_dk64();
+        if (resident <= 0) return RGDR_ERR_HIP;
+        if ((long long)B * H_v * (D_v / 128) > resident) tile_v = 256;
+    }
+    const int ntiles = (D_v + tile_v - 1) / tile_v;
     const long long items = (long long)B * H_v * ntiles;
     if (items > INT_MAX) return RGDR_ERR_SHAPE;
     a.Hq = H_q;
@@ -764,13 +839,11 @@ static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q
     a.item0 = 0;
     hipError_t err;
     if (D_k == 128)
-        err = gate == kGateGiven ? launch_prefill<128, kGateGiven>(a, lens, idx, nacc, stream)
-              : gate == kGateF32 ? launch_prefill<128, kGateF32>(a, lens, idx, nacc, stream)
-                                 : launch_prefill<128, kGateF16>(a, lens, idx, nacc, stream);
+        err = launch_prefill_gate<128, 2>(gate, a, lens, idx, nacc, stream);
+    else if (tile_v == 256)
+        err = launch_prefill_gate<64, 4>(gate, a, lens, idx, nacc, stream);
     else
-        err = gate == kGateGiven ? launch_prefill<64, kGateGiven>(a, lens, idx, nacc, stream)
-              : gate == kGateF32 ? launch_prefill<64, kGateF32>(a, lens, idx, nacc, stream)
-                                 : launch_prefill<64, kGateF16>(a, lens, idx, nacc, stream);
+        err = launch_prefill_gate<64, 2>(gate, a, lens, idx, nacc, stream);
     return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
 }
 

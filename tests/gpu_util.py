@@ -12,6 +12,7 @@ import numpy as np
 import torch
 
 import oracle
+import workloads
 
 ATOL = 2e-2
 RTOL = 2e-2
@@ -181,6 +182,17 @@ def check_gated(inp, out_t, st_t, ref, label, entries=None):
     if entries is None:
         untouched = np.setdiff1d(np.arange(inp.N_slots), idx[valid])
         assert np.array_equal(dev_to_bits(st_t)[untouched], inp.state[untouched])
+
+
+def raw_qk(inp, seed):
+    """Replace the case's unit-norm q and k by raw projections: each head vector scaled by
+    its own factor in [0.05, 20] (bf16 again), so the unit-norm precondition does not hold."""
+    rng = np.random.default_rng(seed)
+    for name in ("query", "key"):
+        x = oracle.bf16_to_f64(getattr(inp, name))
+        f = rng.uniform(0.05, 20.0, x.shape[:-1] + (1,))
+        setattr(inp, name, workloads.to_bf16_bits(x * f))
+    return inp
 
 
 # ---- per-token state snapshots ----

@@ -9,10 +9,9 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import workloads
 from gpu_util import (assert_tol, bf16_dev_to_f64, check_gated, dev_to_bits, gate_tensors,
-                      gpu_gated, oracle_gated, say, upload)
+                      gpu_gated, oracle_gated, raw_qk, say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,17 +105,6 @@ def test_gated_matches_unfused_chain(rg):
     assert_tol(bf16_dev_to_f64(out_f), bf16_dev_to_f64(out_u), "fused vs unfused out")
     idx = inp.ssm_state_indices
     assert_tol(bf16_dev_to_f64(st_f)[idx], bf16_dev_to_f64(st_u)[idx], "fused vs unfused state")
-
-
-def raw_qk(inp, seed):
-    """Replace the case's unit-norm q and k by raw projections: each head vector scaled by
-    its own factor in [0.05, 20] (bf16 again), so the unit-norm precondition does not hold."""
-    rng = np.random.default_rng(seed)
-    for name in ("query", "key"):
-        x = oracle.bf16_to_f64(getattr(inp, name))
-        f = rng.uniform(0.05, 20.0, x.shape[:-1] + (1,))
-        setattr(inp, name, workloads.to_bf16_bits(x * f))
-    return inp
 
 
 @pytest.mark.parametrize("shape", [

@@ -13,8 +13,8 @@ import torch
 
 import workloads
 from gpu_util import (assert_tol, bf16_dev_to_f64, check_decode, check_gated, dev_to_bits,
-                      gpu_decode, gpu_gated, gpu_prefill, oracle_decode, oracle_gated, say,
-                      upload)
+                      gpu_decode, gpu_gated, gpu_prefill, oracle_decode, oracle_gated, raw_qk,
+                      say, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,67 @@ def test_prefill_shapes(rg, shape):
     say(f"prefill {shape}, lengths {inp.actual_seq_lengths.tolist()}")
     out, st = gpu_prefill(inp)
     check_decode(inp, out, st, oracle_decode(inp), f"prefill {shape}")
+
+
+# D_k = 64 calls with more 128-column items than the device holds at once (two per compute
+# unit: 512 on MI355X) take 256-column tiles when D_v allows; B, Hq, Hv, T, Dv, N_slots
+WIDE = [
+    (4, 16, 64, 40, 512, 6),     # the example page's head size, 1024 narrow items
+    (5, 8, 64, 35, 256, 7),      # one wide tile per head, 640 narrow items
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "B%d_Hq%d_Hv%d_T%d_Dv%d" % s[:5])
+def test_prefill_wide_tiles(rg, shape):
+    """256-column tiles at D_k = 64: ragged lengths, accepted prefixes inside and at the end
+    of chunks, head sharing, a skipped slot, against the oracle (values) and bit for bit
+    (padded rows, untouched slots)."""
+    B, Hq, Hv, T, Dv, N = shape
+    inp = workloads.make_case(B, Hq, Hv, T, 64, Dv, N, seed=7300 + Dv, indices="choice",
+                              lengths="uniform")
+    rng = np.random.default_rng(7301 + Dv)
+    inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
+    inp.ssm_state_indices[1] = N  # skipped entry
+    assert B * Hv * Dv // 128 > 512
+    say(f"prefill wide tiles {shape}, lengths {inp.actual_seq_lengths.tolist()}")
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"prefill wide {shape}")
+
+
+def test_prefill_wide_tiles_equal_narrow_tiles(rg):
+    """The same entries through 256-column tiles (one call of 4 entries: 1024 narrow items)
+    and through 128-column tiles (two calls of 2 entries: 512 narrow items each, which the
+    device holds at once) give the same bits: a column's arithmetic and an item's chunk cuts
+    do not depend on the tile width."""
+    inp = workloads.make_case(4, 16, 64, 70, 64, 512, 4, seed=7320, indices="permutation",
+                              lengths="uniform")
+    rng = np.random.default_rng(7321)
+    inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
+    inp.g[2] *= 6.0  # strong decays in one entry: its chunks are cut
+    out_w, st_w = gpu_prefill(inp)
+    d = upload(inp)
+    pool = d["state"].clone()
+    outs = []
+    for half in (slice(0, 2), slice(2, 4)):
+        o, pool = rg.rgdr_prefill(d["query"][half], d["key"][half], d["value"][half],
+                                  d["beta"][half], pool, d["actual_seq_lengths"][half],
+                                  d["ssm_state_indices"][half], d["g"][half], d["gk"][half],
+                                  d["num_accepted_tokens"][half], inp.scale)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bits(out_w), dev_to_bits(torch.cat(outs))), "out differs"
+    assert np.array_equal(dev_to_bits(st_w), dev_to_bits(pool)), "state differs"
+
+
+def test_prefill_gated_wide_tiles(rg):
+    """The fused gate (fp16 projections) with in-kernel q/k normalisation of raw q and k on
+    256-column tiles."""
+    inp = workloads.make_case(4, 16, 64, 24, 64, 512, 5, seed=7310, indices="choice",
+                              lengths="uniform", gate=True)
+    inp = raw_qk(inp, 7311)
+    out, st = gpu_gated(rg, inp, np.float16, normalize_qk=True, fn="rgdr_prefill_gated")
+    check_gated(inp, out, st, oracle_gated(inp, dtype=np.float16, normalize_qk=True),
+                "prefill gated wide tiles")
 
 
 @pytest.mark.parametrize("T", [16, 64, 512])
