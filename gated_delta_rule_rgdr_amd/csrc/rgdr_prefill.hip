@@ -652,23 +652,29 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 
         __builtin_amdgcn_s_setprio(3);
         // R = V - Y_K for the chunk's tokens (0 past Lc); then the next chunk's values.
+        // (Written out per column pair: the loop form of these two statements schedules the
+        // D_k = 128 kernel differently and measured 1.2% slower.)
         f32x4 R[2][NC];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    R[tb][c][i] = ((c & 1) ? bf16_hi(vr[tb][i][c >> 1]) : bf16_lo(vr[tb][i][c >> 1])) -
-                                  yk[tb][c][i];
+            for (int i = 0; i < 4; ++i) {
+                R[tb][0][i] = bf16_lo(vr[tb][i][0]) - yk[tb][0][i];
+                R[tb][1][i] = bf16_hi(vr[tb][i][0]) - yk[tb][1][i];
+                if constexpr (NC == 4) {
+                    R[tb][2][i] = bf16_lo(vr[tb][i][1]) - yk[tb][2][i];
+                    R[tb][3][i] = bf16_hi(vr[tb][i][1]) - yk[tb][3][i];
+                }
+            }
         if (Lc < kChunk)  // uniform: a short chunk's later tokens (their values may be anything)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (16 * tb + 4 * kg + i >= Lc)
-#pragma unroll
-                        for (int c = 0; c < NC; ++c) R[tb][c][i] = 0.f;
+                    if (16 * tb + 4 * kg + i >= Lc) {
+                        R[tb][0][i] = R[tb][1][i] = 0.f;
+                        if constexpr (NC == 4) R[tb][2][i] = R[tb][3][i] = 0.f;
+                    }
         load_v(t0n, lenn);
         auto blk4 = [&](int b, int lo) {
             return as_s16x4(*reinterpret_cast<const uint2 *>(blk(b) + lo * 16 * AS + n16 * AS + 4 * kg));
@@ -748,7 +754,8 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         const int pad = a.T - L;
         const auto rz = make_rsrc(a.out + (bh * a.T + L) * a.Dv + m.tile * TV + WC * w,
                                   (uint32_t)(((pad - 1) * a.Dv + WC) * 2));
-        const uint32_t zoff = (uint32_t)(((lane / CG) * a.Dv + 8 * (lane % CG)) * 2);
+        const uint32_t ul = (uint32_t)lane;
+        const uint32_t zoff = ((ul / CG) * (uint32_t)a.Dv + 8 * (ul % CG)) * 2;
         for (int t = 0; t < pad; t += RG)
             store16<0>(u32x4{0u, 0u, 0u, 0u}, rz, zoff + (uint32_t)(t * a.Dv * 2));
     }
