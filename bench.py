@@ -2,7 +2,7 @@
 """Benchmark of the gated-delta-rule path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--rotate R]
-                    [--extra 1,3,4,5] [--snapshots 3] [--cpu-seconds S] [--no-cpu-baseline]
+                    [--extra 1,3,4,5,6] [--snapshots 3] [--cpu-seconds S] [--no-cpu-baseline]
 
 One step is the whole path over one batch: the gate front end (g = decay_scale *
 softplus(a + dt_bias), beta = sigmoid(b)) and the recurrence, in place on the state pool,
@@ -11,7 +11,8 @@ rgdr_decode_gated (the gate computed in the decode kernel's prologue); the two-l
 la_gate -> rgdr_decode is timed as well and reported as `unfused_ms_per_step`. The default
 workload is the batched GQA decode shape (B=64, H_q=16, H_v=32, T=1, D_k=D_v=128, a
 256-slot pool, 64 slots in use), with gate inputs that reproduce its g/beta recipe.
-Workload 5 (T = 1024) runs the long-sequence entries, rgdr_prefill_gated and rgdr_prefill.
+Workloads 5 and 6 (T = 1024; D = 128, and the example page's head size D_k = 64, D_v = 512)
+run the long-sequence entries, rgdr_prefill_gated and rgdr_prefill.
 
 Measurement:
   * R independent buffer sets (pool and every per-step input/output) are rotated so that
@@ -58,7 +59,7 @@ WARM_MS = 25.0      # untimed graph replays before any timed one, in wall-clock 
 # The host share of one GPU on the benchmark boxes: the threaded CPU baseline uses at most
 # this many threads, whatever the process's affinity mask shows.
 HOST_CORES_PER_GPU = 16
-PREFILL_WORKLOADS = (5,)
+PREFILL_WORKLOADS = (5, 6)
 
 
 def log(msg):
@@ -89,13 +90,16 @@ def fused_bytes(inp, decode_b, tok_heads):
     return decode_b + tok_heads * (4 + 4 - 4 - 2) + 2 * 4 * inp.Hv
 
 
-def prefill_mfma_flops(inp):
+def prefill_mfma_flops(inp, cus):
     """Matrix-core flops the long-sequence kernel executes per call (not the method's
     algorithmic flops). Per chunk of up to 32 tokens and per 128-column item: each of its four
     waves issues 24 x (D_k / 32) products of 16x16x32 for [c k | c scale q]^T S, 6 x (D_k / 16)
     for the rank-32 update and 36 of 16x16x16 for the blockwise solve and the outputs; the
-    item's M and N blocks take 18 x (D_k / 32) of 16x16x32. Chunks split at the accepted
-    prefix's end; chunks shortened by the decay range (rare at these decays) are not counted."""
+    item's M and N blocks take 18 x (D_k / 32) of 16x16x32. A 256-column item (D_k = 64, taken
+    by the library when D_v is a multiple of 256 and the call has more 128-column items than
+    the device's `cus` compute units hold at two per unit) doubles each wave's share and keeps
+    the M and N blocks. Chunks split at the accepted prefix's end; chunks shortened by the
+    decay range (rare at these decays) are not counted."""
     import numpy as np
     lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
     nacc = np.clip(inp.num_accepted_tokens, 0, lens)
@@ -104,10 +108,12 @@ def prefill_mfma_flops(inp):
     for L, n, ok in zip(lens, nacc, valid):
         if ok and L > 0:
             chunks += -(-int(L) // 32) + (1 if 0 < n < L and n % 32 else 0)
-    items = inp.Hv * -(-inp.Dv // 128)
+    wide = inp.Dk == 64 and inp.Dv % 256 == 0 and inp.B * inp.Hv * (inp.Dv // 128) > 2 * cus
+    per_wave = 2 if wide else 1                 # column sets per lane, in pairs
+    items = inp.Hv * -(-inp.Dv // (128 * per_wave))
     npb, nrb = inp.Dk // 32, inp.Dk // 16
-    big = 4 * (24 * npb + 6 * nrb) + 18 * npb   # 16x16x32 products per item and chunk
-    small = 4 * 36                              # 16x16x16 products
+    big = 4 * (24 * npb + 6 * nrb) * per_wave + 18 * npb  # 16x16x32 products per item, chunk
+    small = 4 * 36 * per_wave                   # 16x16x16 products
     return chunks * items * (big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2)
 
 
@@ -121,7 +127,8 @@ TRAFFIC_PROFILES = {(2, 16): "profiles/rgdr_decode_b16_gqa_d128.md",
                     2: "profiles/rgdr_decode_b64_gqa_d128.md",
                     3: "profiles/rgdr_decode_varlen_b32_t8_d128.md",
                     4: "profiles/rgdr_decode_b256_gqa_d128.md",
-                    5: "profiles/rgdr_prefill_b16_t1024_gqa_d128.md"}
+                    5: "profiles/rgdr_prefill_b16_t1024_gqa_d128.md",
+                    6: "profiles/rgdr_prefill_b4_h64_t1024_dk64_dv512.md"}
 
 
 def kernel_code_digest(wid=2):
@@ -276,6 +283,7 @@ class Workload:
         import gated_delta_rule_rgdr_amd as rg
         import workloads
         self.rg, self.torch = rg, torch
+        self.cus = torch.cuda.get_device_properties(dev).multi_processor_count
         self.wid = wid
         self.batch = batch
         self.name = workloads.WORKLOAD_NAMES[wid]
@@ -427,7 +435,7 @@ def roofline(wl, us):
          "traffic": measured_traffic(wl.wid, wl.batch), "bytes_per_launch": wl.step_bytes,
          "avg_launch_us": round(us, 3)}
     if wl.prefill:
-        fl = prefill_mfma_flops(wl.inp)
+        fl = prefill_mfma_flops(wl.inp, wl.cus)
         tf = fl / (us * 1e-6) / 1e12
         r["mfma_executed"] = {"flops_per_launch": fl, "achieved_tflops": round(tf, 1),
                               "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
@@ -501,11 +509,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6])
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >= 1 GiB)")
     ap.add_argument("--batch", type=int, default=None,
                     help="replace the workload's batch size B (same recipe otherwise)")
-    ap.add_argument("--extra", default="1,3,4,5",
+    ap.add_argument("--extra", default="1,3,4,5,6",
                     help="other workloads whose fused-call duration the line also carries "
                          "(comma-separated ids; empty for none)")
     ap.add_argument("--snapshots", default="3",
@@ -612,7 +620,7 @@ def main():
     extras = {}
     for tok in [t for t in args.extra.split(",") if t.strip()]:
         ew = int(tok)
-        if ew == wid or ew not in range(6):
+        if ew == wid or ew not in range(7):
             continue
         e = Workload(ew, dev, 0, args.extra_steps)
         extras[str(ew)] = extra_entry(torch, stream, e, args.extra_steps)
