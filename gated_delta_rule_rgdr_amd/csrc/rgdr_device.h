@@ -60,7 +60,7 @@ struct DecodeArgs {
     // T = 1 wave form: ticks of the constant wall clock (s_memrealtime) each wave waits,
     // counted from its own start, before it writes its tile back; 0 = no wait.
     int hold;
-    // Per-token states [B, T, H_v, D_k, D_v] bf16 (rgdr_decode_snapshots only).
+    // Per-token states [B, T, H_v, D_k, D_v] bf16 (the snapshot entries; null otherwise).
     uint16_t *snap;
 };
 
