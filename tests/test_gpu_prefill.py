@@ -55,6 +55,9 @@ def test_prefill_shapes(rg, shape):
 WIDE = [
     (4, 16, 64, 40, 512, 6),     # the example page's head size, 1024 narrow items
     (5, 8, 64, 35, 256, 7),      # one wide tile per head, 640 narrow items
+    (2, 4, 16, 20, 4096, 3),     # the largest D_v: 16 wide tiles per head
+    (3, 16, 64, 18, 768, 4),     # three wide tiles per head
+    (4, 16, 64, 18, 320, 6),     # D_v not a multiple of 256: 128-column tiles at any size
 ]
 
 
@@ -69,7 +72,7 @@ def test_prefill_wide_tiles(rg, shape):
     rng = np.random.default_rng(7301 + Dv)
     inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
     inp.ssm_state_indices[1] = N  # skipped entry
-    assert B * Hv * Dv // 128 > 512
+    assert B * Hv * -(-Dv // 128) > 512
     say(f"prefill wide tiles {shape}, lengths {inp.actual_seq_lengths.tolist()}")
     out, st = gpu_prefill(inp)
     check_decode(inp, out, st, oracle_decode(inp), f"prefill wide {shape}")
