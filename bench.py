@@ -95,10 +95,11 @@ def prefill_mfma_flops(inp, cus):
     algorithmic flops). Per chunk of up to 32 tokens and per 128-column item: each of its four
     waves issues 24 x (D_k / 32) products of 16x16x32 for [c k | c scale q]^T S, 6 x (D_k / 16)
     for the rank-32 update and 36 of 16x16x16 for the blockwise solve and the outputs; the
-    item's M and N blocks take 18 x (D_k / 32) of 16x16x32. A 256-column item (D_k = 64, taken
-    by the library when D_v is a multiple of 256 and the call has more 128-column items than
-    the device's `cus` compute units hold at two per unit) doubles each wave's share and keeps
-    the M and N blocks. Chunks split at the accepted prefix's end; chunks shortened by the
+    item's M and N blocks take 18 x (D_k / 32) of 16x16x32. The library's other tile widths
+    scale each wave's share with the columns and keep the M and N blocks: 256-column items
+    at D_k = 64 when D_v is a multiple of 256 and the call has more 128-column items than
+    the device's `cus` compute units hold at two per unit; 64-column items at D_k = 128
+    when it has at most cus / 2 of them. Chunks split at the accepted prefix's end; chunks shortened by the
     decay range (rare at these decays) are not counted."""
     import numpy as np
     lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
@@ -108,12 +109,17 @@ def prefill_mfma_flops(inp, cus):
     for L, n, ok in zip(lens, nacc, valid):
         if ok and L > 0:
             chunks += -(-int(L) // 32) + (1 if 0 < n < L and n % 32 else 0)
-    wide = inp.Dk == 64 and inp.Dv % 256 == 0 and inp.B * inp.Hv * (inp.Dv // 128) > 2 * cus
-    per_wave = 2 if wide else 1                 # column sets per lane, in pairs
-    items = inp.Hv * -(-inp.Dv // (128 * per_wave))
+    narrow_items = inp.B * inp.Hv * -(-inp.Dv // 128)
+    if inp.Dk == 64 and inp.Dv % 256 == 0 and narrow_items > 2 * cus:
+        nc = 4                                  # column sets per lane
+    elif inp.Dk == 128 and 2 * narrow_items <= cus:
+        nc = 1
+    else:
+        nc = 2
+    items = inp.Hv * -(-inp.Dv // (64 * nc))
     npb, nrb = inp.Dk // 32, inp.Dk // 16
-    big = 4 * (24 * npb + 6 * nrb) * per_wave + 18 * npb  # 16x16x32 products per item, chunk
-    small = 4 * 36 * per_wave                   # 16x16x16 products
+    big = 4 * (12 * npb + 3 * nrb) * nc + 18 * npb  # 16x16x32 products per item and chunk
+    small = 4 * 18 * nc                         # 16x16x16 products
     return chunks * items * (big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2)
 
 

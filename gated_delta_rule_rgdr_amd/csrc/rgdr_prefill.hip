@@ -157,11 +157,14 @@ __device__ __forceinline__ void split8(const f32x4 &x0, const f32x4 &x1, bf16x8 
 }
 __device__ __forceinline__ s16x4 as_s16x4(uint2 v) { return __builtin_bit_cast(s16x4, v); }
 
-// NW consecutive 32-bit words (2 NW bf16 columns of one row) in one buffer access.
-template <int NW, int POL>
-__device__ __forceinline__ void load_words(uint32_t (&w)[NW], __amdgpu_buffer_rsrc_t rs,
-                                           uint32_t voff, uint32_t soff) {
-    if constexpr (NW == 1) {
+// NC consecutive bf16 columns of one row (1, 2 or 4) in one buffer access, as (NC + 1) / 2
+// 32-bit words (one column: the low half).
+template <int NC, int POL>
+__device__ __forceinline__ void load_cols(uint32_t (&w)[(NC + 1) / 2], __amdgpu_buffer_rsrc_t rs,
+                                          uint32_t voff, uint32_t soff) {
+    if constexpr (NC == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, POL);
+    } else if constexpr (NC == 2) {
         w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, POL);
     } else {
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, POL);
@@ -169,10 +172,13 @@ __device__ __forceinline__ void load_words(uint32_t (&w)[NW], __amdgpu_buffer_rs
         w[1] = v.y;
     }
 }
-template <int NW, int POL>
-__device__ __forceinline__ void store_words(const uint32_t (&w)[NW], __amdgpu_buffer_rsrc_t rs,
-                                            uint32_t voff, uint32_t soff) {
-    if constexpr (NW == 1)
+template <int NC, int POL>
+__device__ __forceinline__ void store_cols(const uint32_t (&w)[(NC + 1) / 2],
+                                           __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                           uint32_t soff) {
+    if constexpr (NC == 1)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[0], rs, voff, soff, POL);
+    else if constexpr (NC == 2)
         __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, voff, soff, POL);
     else
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rs, voff, soff, POL);
@@ -227,7 +233,8 @@ __device__ __forceinline__ f32x4 mma16(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f
 
 // Lane layout of the state. Wave w owns the WC = 16 NC tile columns WC w .. WC w + WC - 1
 // over all D_k rows (NC = 2: 128-column tiles; NC = 4: 256-column tiles, D_k = 64 only, where
-// the state still takes 64 values per lane). Lane l = (kg, n16) = (l / 16, l % 16) holds rows
+// the state still takes 64 values per lane; NC = 1: 64-column tiles, D_k = 128 only, for
+// calls with few items). Lane l = (kg, n16) = (l / 16, l % 16) holds rows
 // 16 rb + 4 kg + i (rb < D_k / 16, i < 4) of columns WC w + NC n16 + c (c < NC) as
 // S[rb][c][i]: the accumulator layout of the 16 x 16 block of rows 16 rb .. + 15 and columns
 // WC w + NC n + c (column set c). Rows 4 kg .. 4 kg + 3 of two
@@ -241,9 +248,10 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const int32_t *__restrict__ nacc) {
     static_assert(DK == 64 || DK == 128, "D_k = 64 or 128");
     static_assert(!NORM || GATE != kGateGiven, "q/k normalisation belongs to the fused front end");
-    static_assert(NC == 2 || (NC == 4 && DK == 64), "256-column tiles at D_k = 64 only");
+    static_assert(NC == 2 || (NC == 4 && DK == 64) || (NC == 1 && DK == 128),
+                  "256-column tiles at D_k = 64 only, 64-column tiles at D_k = 128 only");
     using P = ChunkShape<DK>;
-    constexpr int WC = 16 * NC, TV = 4 * WC, NW = NC / 2;  // NW: 32-bit words per lane row
+    constexpr int WC = 16 * NC, TV = 4 * WC, NW = (NC + 1) / 2;  // NW: words per lane row
     constexpr int NRB = P::NRB, NPB = P::NPB, TPT = P::TPT, NTG = P::NTG;
     constexpr int XS = P::XS, KS = P::KS, AS = P::AS, BS = P::BS;
     __shared__ f32x4 lds4[P::BYTES / 16];
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                load_words<NW, 0>(vr[tb][i], rv, orow, (uint32_t)((16 * tb + i) * a.Dv * 2));
+                load_cols<NC, 0>(vr[tb][i], rv, orow, (uint32_t)((16 * tb + i) * a.Dv * 2));
     };
 
     // The first chunk's operands, then the state tile (bf16 -> fp32, exact).
@@ -313,8 +321,8 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            load_words<NW, RGDR_STATE_LOAD_POLICY>(raw[rb][i], rs, lane_off,
-                                                   (uint32_t)((16 * rb + i) * a.Dv * 2));
+            load_cols<NC, RGDR_STATE_LOAD_POLICY>(raw[rb][i], rs, lane_off,
+                                                  (uint32_t)((16 * rb + i) * a.Dv * 2));
     f32x4 S[NRB][NC];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
@@ -328,8 +336,8 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                store_words<NW, RGDR_STATE_STORE_POLICY>(raw[rb][i], rso, lane_off,
-                                                         (uint32_t)((16 * rb + i) * a.Dv * 2));
+                store_cols<NC, RGDR_STATE_STORE_POLICY>(raw[rb][i], rso, lane_off,
+                                                        (uint32_t)((16 * rb + i) * a.Dv * 2));
     }
     if (tid == 0) *cut = kChunk;
     lds_barrier();
@@ -660,7 +668,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 R[tb][0][i] = bf16_lo(vr[tb][i][0]) - yk[tb][0][i];
-                R[tb][1][i] = bf16_hi(vr[tb][i][0]) - yk[tb][1][i];
+                if constexpr (NC >= 2) R[tb][1][i] = bf16_hi(vr[tb][i][0]) - yk[tb][1][i];
                 if constexpr (NC == 4) {
                     R[tb][2][i] = bf16_lo(vr[tb][i][1]) - yk[tb][2][i];
                     R[tb][3][i] = bf16_hi(vr[tb][i][1]) - yk[tb][3][i];
@@ -672,7 +680,10 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (16 * tb + 4 * kg + i >= Lc) {
-                        R[tb][0][i] = R[tb][1][i] = 0.f;
+                        if constexpr (NC == 1)
+                            R[tb][0][i] = 0.f;
+                        else
+                            R[tb][0][i] = R[tb][1][i] = 0.f;
                         if constexpr (NC == 4) R[tb][2][i] = R[tb][3][i] = 0.f;
                     }
         load_v(t0n, lenn);
@@ -709,8 +720,13 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 for (int i = 0; i < 4; ++i) {
                     uint32_t wo[NW];
 #pragma unroll
-                    for (int j = 0; j < NW; ++j) wo[j] = pack_bf16x2(ov[tb][2 * j][i], ov[tb][2 * j + 1][i]);
-                    store_words<NW, 0>(wo, rout, orow, (uint32_t)((16 * tb + i) * a.Dv * 2));
+                    for (int j = 0; j < NW; ++j) {
+                        if constexpr (NC == 1)
+                            wo[j] = pack_bf16x2(ov[tb][0][i], 0.f);
+                        else
+                            wo[j] = pack_bf16x2(ov[tb][2 * j][i], ov[tb][2 * j + 1][i]);
+                    }
+                    store_cols<NC, 0>(wo, rout, orow, (uint32_t)((16 * tb + i) * a.Dv * 2));
                 }
         }
         // S = S' + KH^T U (the true state is diag(c_last) S), one 16x16x32 chain per block
@@ -737,10 +753,14 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 for (int i = 0; i < 4; ++i) {
                     uint32_t ws[NW];
 #pragma unroll
-                    for (int j = 0; j < NW; ++j)
-                        ws[j] = pack_bf16x2(S[rb][2 * j][i] * cr[i], S[rb][2 * j + 1][i] * cr[i]);
-                    store_words<NW, RGDR_STATE_STORE_POLICY>(ws, rso, lane_off,
-                                                             (uint32_t)((16 * rb + i) * a.Dv * 2));
+                    for (int j = 0; j < NW; ++j) {
+                        if constexpr (NC == 1)
+                            ws[j] = pack_bf16x2(S[rb][0][i] * cr[i], 0.f);
+                        else
+                            ws[j] = pack_bf16x2(S[rb][2 * j][i] * cr[i], S[rb][2 * j + 1][i] * cr[i]);
+                    }
+                    store_cols<NC, RGDR_STATE_STORE_POLICY>(ws, rso, lane_off,
+                                                            (uint32_t)((16 * rb + i) * a.Dv * 2));
                 }
             }
         }
@@ -786,6 +806,20 @@ static hipError_t launch_prefill_gate(int gate, const DecodeArgs &a, const int32
                               : launch_prefill<DK, kGateF16, NC>(a, lens, idx, nacc, stream);
 }
 
+// Compute units of the current device, queried once per device; 0 if the query fails.
+static int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // Items of the D_k = 64 kernel with 128-column tiles that the current device holds at once
 // (compute units times workgroups per compute unit), queried once per device; 0 if the
 // query fails.
@@ -826,11 +860,24 @@ static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q
     // multiple of 256) when the call has more 128-column items than the device holds at once:
     // half as many items, each with the state bytes of a D_k = 128 item, so fewer rounds of
     // items pay the per-chunk work that does not scale with the columns.
+    // At D_k = 128, 64-column tiles when the call has at most half as many 128-column items
+    // as the device has compute units. Such a call runs at one item's chain of chunks, and
+    // the chain is bound by its compute unit's issue of the column work (the contraction
+    // with the state, the update, the state's split). Twice the items, each with half the
+    // columns and still one per unit, shorten it; the per-token preparation is repeated.
     int tile_v = 128;
+    bool narrow = false;
     if (D_k == 64 && D_v % 256 == 0) {
         const int resident = prefill_resident_items_dk64();
         if (resident <= 0) return RGDR_ERR_HIP;
         if ((long long)B * H_v * (D_v / 128) > resident) tile_v = 256;
+    } else if (D_k == 128) {
+        const int cus = device_cus();
+        if (cus <= 0) return RGDR_ERR_HIP;
+        if (2LL * B * H_v * ((D_v + 127) / 128) <= cus) {
+            narrow = true;
+            tile_v = 64;
+        }
     }
     const int ntiles = (D_v + tile_v - 1) / tile_v;
     const long long items = (long long)B * H_v * ntiles;
@@ -845,7 +892,9 @@ static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q
     a.n_items = (int)items;
     a.item0 = 0;
     hipError_t err;
-    if (D_k == 128)
+    if (D_k == 128 && narrow)
+        err = launch_prefill_gate<128, 1>(gate, a, lens, idx, nacc, stream);
+    else if (D_k == 128)
         err = launch_prefill_gate<128, 2>(gate, a, lens, idx, nacc, stream);
     else if (tile_v == 256)
         err = launch_prefill_gate<64, 4>(gate, a, lens, idx, nacc, stream);

@@ -103,6 +103,43 @@ def test_prefill_wide_tiles_equal_narrow_tiles(rg):
     assert np.array_equal(dev_to_bits(st_w), dev_to_bits(pool)), "state differs"
 
 
+def test_prefill_four_wave_tiles_at_d128(rg):
+    """More 128-column items than half the compute units (144 here): the call keeps
+    128-column tiles, against the oracle, with ragged lengths and accepted prefixes."""
+    inp = workloads.make_case(9, 8, 16, 40, 128, 128, 12, seed=7330, indices="choice",
+                              lengths="uniform")
+    rng = np.random.default_rng(7331)
+    inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
+    assert 2 * inp.B * inp.Hv > 256
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), "prefill 128-column tiles at D_k = 128")
+
+
+def test_prefill_narrow_tiles_equal_wide_tiles(rg):
+    """At D_k = 128 a call with few items takes 64-column tiles. The same entries as one call
+    (144 items, 128-column tiles) and as one call per entry (16 items each, 64-column tiles)
+    give the same bits: a column's arithmetic and an item's chunk cuts do not depend on the
+    tile width."""
+    inp = workloads.make_case(9, 8, 16, 70, 128, 192, 9, seed=7340, indices="permutation",
+                              lengths="uniform")
+    rng = np.random.default_rng(7341)
+    inp.num_accepted_tokens = rng.integers(0, inp.actual_seq_lengths + 1).astype(np.int32)
+    inp.g[4] *= 6.0  # strong decays in one entry: its chunks are cut
+    out_w, st_w = gpu_prefill(inp)
+    d = upload(inp)
+    pool = d["state"].clone()
+    outs = []
+    for b in range(inp.B):
+        e = slice(b, b + 1)
+        o, pool = rg.rgdr_prefill(d["query"][e], d["key"][e], d["value"][e], d["beta"][e], pool,
+                                  d["actual_seq_lengths"][e], d["ssm_state_indices"][e],
+                                  d["g"][e], d["gk"][e], d["num_accepted_tokens"][e], inp.scale)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bits(out_w), dev_to_bits(torch.cat(outs))), "out differs"
+    assert np.array_equal(dev_to_bits(st_w), dev_to_bits(pool)), "state differs"
+
+
 def test_prefill_gated_wide_tiles(rg):
     """The fused gate (fp16 projections) with in-kernel q/k normalisation of raw q and k on
     256-column tiles."""
