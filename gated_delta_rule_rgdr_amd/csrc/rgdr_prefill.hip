@@ -6,8 +6,9 @@
 // is that operator for this library: the same inputs, outputs and semantics as rgdr_decode
 // (slot pool, lengths, accepted counts, head sharing, padding), for any T up to 65536.
 //
-// Design. One workgroup of four waves owns one (entry, value head, 128-column tile) for the
-// whole sequence. Its state tile is read from HBM once, kept in fp32 in the matrix cores'
+// Design. One workgroup of four waves owns one (entry, value head, column tile) for the
+// whole sequence: 128 columns, or 256 at D_k = 64 when a call has more items than the device
+// holds at once, or 64 at D_k = 128 when it leaves most compute units idle. Its state tile is read from HBM once, kept in fp32 in the matrix cores'
 // accumulator layout while the item's tokens are walked in chunks of up to 32, and written
 // back once (at the accepted prefix's end). Each chunk applies the exact closed form of the
 // four steps over its tokens (the unrolled recurrence the decode kernel's chunk form also
