@@ -52,13 +52,33 @@ def test_random_decode(rg, seed):
     check_decode(inp, out, st, oracle_decode(inp), f"random decode {seed}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_prefill(rg, seed):
     inp = draw(1900 + seed, 48)
     say(f"prefill case {seed}: B={inp.B} Hq={inp.Hq} Hv={inp.Hv} T={inp.T} Dk={inp.Dk} "
         f"Dv={inp.Dv} L={inp.actual_seq_lengths.tolist()} n={inp.num_accepted_tokens.tolist()}")
     out, st = gpu_prefill(inp)
     check_decode(inp, out, st, oracle_decode(inp), f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_prefill_wide_tiles(rg, seed):
+    """Random D_k = 64 calls with more 128-column items than the device holds at once (512 on
+    MI355X), so that D_v a multiple of 256 takes 256-column tiles and other D_v keep 128."""
+    rng = np.random.default_rng(2900 + seed)
+    Hq = int(rng.choice([8, 16, 32]))
+    Hv = 64
+    Dv = int(rng.choice([256, 320, 512, 768]))
+    B = int(-(-513 * 128 // (Hv * Dv))) + int(rng.integers(0, 3))
+    T = int(rng.integers(2, 25))
+    lens = rng.integers(0, T + 1, B).astype(np.int32)
+    inp = workloads.make_case(B, Hq, Hv, T, 64, Dv, B + 1, seed=2950 + seed, indices="choice",
+                              lengths=lens)
+    inp.num_accepted_tokens = np.array([rng.integers(0, L + 1) for L in lens], np.int32)
+    assert B * Hv * -(-Dv // 128) > 512
+    say(f"wide prefill case {seed}: B={B} Hq={Hq} Dv={Dv} T={T} L={lens.tolist()}")
+    out, st = gpu_prefill(inp)
+    check_decode(inp, out, st, oracle_decode(inp), f"random wide prefill {seed}")
 
 
 @pytest.mark.parametrize("seed", range(10))
