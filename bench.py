@@ -134,7 +134,8 @@ TRAFFIC_PROFILES = {(2, 16): "profiles/rgdr_decode_b16_gqa_d128.md",
                     3: "profiles/rgdr_decode_varlen_b32_t8_d128.md",
                     4: "profiles/rgdr_decode_b256_gqa_d128.md",
                     5: "profiles/rgdr_prefill_b16_t1024_gqa_d128.md",
-                    6: "profiles/rgdr_prefill_b4_h64_t1024_dk64_dv512.md"}
+                    6: "profiles/rgdr_prefill_b4_h64_t1024_dk64_dv512.md",
+                    (3, "snapshots"): "profiles/rgdr_decode_snapshots_varlen_b32_t8_d128.md"}
 
 
 def kernel_code_digest(wid=2):
@@ -154,8 +155,9 @@ def kernel_code_digest(wid=2):
 
 def measured_traffic(wid=2, batch=None):
     """HBM bytes per fused call from the committed rocprofv3 counter summary of workload
-    `wid` (at batch size `batch`, if it replaces the workload's), or None when there is none
-    or the kernel's code has changed since those counters were taken."""
+    `wid` (at batch size `batch`, if it replaces the workload's; "snapshots" for the
+    rgdr_decode_snapshots call), or None when there is none or the kernel's code has
+    changed since those counters were taken."""
     import re
     key = wid if batch is None else (wid, batch)
     if key not in TRAFFIC_PROFILES:
@@ -469,11 +471,11 @@ def extra_entry(torch, stream, wl, n):
             "roofline": r}
 
 
-def snapshot_entry(torch, stream, wl, n):
-    """Duration and roofline of rgdr_decode_snapshots at one workload: the decode step that
-    also stores the state after every token (g and beta from the gate beforehand, as that
-    entry takes them). Its algorithmic bytes are the decode's plus D_k * D_v * 2 per written
-    snapshot (every token t < L of every served entry and value head)."""
+def snapshot_setup(torch, wl):
+    """The rgdr_decode_snapshots call at workload `wl` (g and beta from the gate beforehand,
+    as that entry takes them, and a snapshot buffer per buffer set) and its algorithmic
+    bytes: the decode's plus D_k * D_v * 2 per written snapshot (every token t < L of every
+    served entry and value head)."""
     import numpy as np
     inp = wl.inp
     B, Hv, T, Dk, Dv = inp.B, inp.Hv, inp.T, inp.Dk, inp.Dv
@@ -491,13 +493,21 @@ def snapshot_entry(torch, stream, wl, n):
                                     s["gk"], wl.nacc, inp.scale, out=s["out"],
                                     state_snapshots=s["snap"])
 
+    lens = np.clip(inp.actual_seq_lengths, 0, T)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    return call, wl.dbytes + int(lens[valid].sum()) * Hv * Dk * Dv * 2
+
+
+def snapshot_entry(torch, stream, wl, n):
+    """Duration and roofline of rgdr_decode_snapshots at one workload: the decode step that
+    also stores the state after every token (see snapshot_setup for its bytes)."""
+    inp = wl.inp
+    B, Hv, T, Dk, Dv = inp.B, inp.Hv, inp.T, inp.Dk, inp.Dv
+    call, by = snapshot_setup(torch, wl)
     for s in wl.sets[:3]:
         call(s)
     torch.cuda.synchronize()
     us, per = kernel_avg_us(torch, stream, call, wl.sets, n)
-    lens = np.clip(inp.actual_seq_lengths, 0, T)
-    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
-    by = wl.dbytes + int(lens[valid].sum()) * Hv * Dk * Dv * 2
     gbs = by / (us * 1e-6) / 1e9
     return {"workload": wl.name, "call": "rgdr_decode_snapshots (state after every token)",
             "config": {"B": B, "H_q": inp.Hq, "H_v": Hv, "T": T, "D_k": Dk, "D_v": Dv,
@@ -505,7 +515,8 @@ def snapshot_entry(torch, stream, wl, n):
             "call_us": round(us, 3),
             "roofline": {"kernel": "rgdr_decode_snapshots", "bound": "hbm",
                          "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(wl.wid, "snapshots"),
                          "bytes_per_launch": by, "avg_launch_us": round(us, 3),
                          "launch_us_replays": [round(x, 3) for x in per]}}
 
@@ -577,6 +588,12 @@ def main():
             wl.unfused_step(args.warmup + i)
         torch.cuda.synchronize()
         log(f"eager pass: {args.steps} steps done")
+        if args.snapshots.strip() == str(wid) and not wl.prefill:
+            call, _ = snapshot_setup(torch, wl)
+            for i in range(args.steps):
+                call(wl.sets[i % len(wl.sets)])
+            torch.cuda.synchronize()
+            log(f"eager pass: {args.steps} rgdr_decode_snapshots calls done")
         if args.copy_calibration:
             copy_calibration()
         return
