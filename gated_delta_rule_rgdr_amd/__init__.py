@@ -32,6 +32,7 @@ import torch
 
 __all__ = ["rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated",
            "rgdr_decode_gated_snapshots", "rgdr_prefill", "rgdr_prefill_gated",
+           "rgdr_prefill_ws", "rgdr_prefill_gated_ws", "rgdr_prefill_workspace_size",
            "recurrent_gated_delta_rule", "la_gate",
            "rgdr_validate", "VALIDATE",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
@@ -73,6 +74,13 @@ def library():
     lib.rgdr_prefill.argtypes = lib.rgdr_decode.argtypes
     lib.rgdr_prefill_gated.restype = C.c_int
     lib.rgdr_prefill_gated.argtypes = lib.rgdr_decode_gated.argtypes
+    lib.rgdr_prefill_workspace_size.restype = C.c_int
+    lib.rgdr_prefill_workspace_size.argtypes = [i32] * 5 + [C.POINTER(C.c_size_t)]
+    lib.rgdr_prefill_ws.restype = C.c_int
+    lib.rgdr_prefill_ws.argtypes = [vp] * 10 + [f32] + [i32] * 7 + [vp, vp, vp, C.c_size_t, vp]
+    lib.rgdr_prefill_gated_ws.restype = C.c_int
+    lib.rgdr_prefill_gated_ws.argtypes = ([vp] * 7 + [C.c_int] + [vp] * 5 + [f32] + [i32] * 7
+                                          + [vp] * 2 + [C.c_uint32, vp, C.c_size_t, vp])
     lib.la_gate.restype = C.c_int
     lib.la_gate.argtypes = [vp, vp, vp, vp, C.c_int, i64, i32, vp, C.c_int, vp, C.c_int, vp]
     lib.rgdr_validate.restype = C.c_int
@@ -194,8 +202,44 @@ def rgdr_prefill(query, key, value, beta, state_pool, actual_seq_lengths, ssm_st
                        stream)
 
 
+def rgdr_prefill_workspace_size(B, H_v, T, D_k, D_v, device=None):
+    """Bytes of workspace ``rgdr_prefill_ws`` uses for a call of these sizes on ``device``
+    (0: such a call runs in one pass and needs none)."""
+    lib = library()
+    n = C.c_size_t(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        rc = lib.rgdr_prefill_workspace_size(B, H_v, T, D_k, D_v, C.byref(n))
+    _check(rc, "rgdr_prefill_workspace_size")
+    return n.value
+
+
+def _workspace(query, value, state_pool, workspace):
+    """The caller's workspace (a uint8 CUDA tensor), or one allocated for the call."""
+    if workspace is None:
+        B, _, T, Dk = query.shape
+        Hv, Dv = value.shape[1], value.shape[3]
+        nbytes = rgdr_prefill_workspace_size(B, Hv, T, Dk, Dv, query.device)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=query.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise RuntimeError("workspace must be a contiguous uint8 CUDA tensor")
+    return workspace
+
+
+def rgdr_prefill_ws(query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
+                    g, gk, num_accepted_tokens, scale=1.0, *, workspace=None, out=None,
+                    state_out=None, stream=None):
+    """``rgdr_prefill`` with a workspace (a uint8 CUDA tensor of at least
+    ``rgdr_prefill_workspace_size`` bytes; allocated for the call when None). Calls of few
+    sequences then evaluate all segments of a sequence at once."""
+    workspace = _workspace(query, value, state_pool, workspace)
+    return _plain_call("rgdr_prefill_ws", query, key, value, beta, state_pool,
+                       actual_seq_lengths, ssm_state_indices, g, gk, num_accepted_tokens, scale,
+                       out, state_out, stream, workspace=workspace)
+
+
 def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,
-                g, gk, num_accepted_tokens, scale, out, state_out, stream, extra=None):
+                g, gk, num_accepted_tokens, scale, out, state_out, stream, extra=None,
+                workspace=None):
     extra = extra or {}  # further output buffers, passed after state_out in this order
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
@@ -243,9 +287,16 @@ def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm
                               g.data_ptr(), gk.data_ptr(), num_accepted_tokens.data_ptr(),
                               float(scale), B, Hq, Hv, T, Dk, Dv, N, out.data_ptr(),
                               state_out.data_ptr(), *[t.data_ptr() for t in extra.values()],
-                              _stream_handle(stream, query.device))
+                              *_ws_args(workspace, query), _stream_handle(stream, query.device))
     _check(rc, fn)
     return out, state_out
+
+
+def _ws_args(workspace, ref):
+    if workspace is None:
+        return ()
+    _same_device(ref, workspace=workspace)
+    return (workspace.data_ptr(), workspace.numel())
 
 
 def rgdr_decode_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool,
@@ -292,9 +343,22 @@ def rgdr_prefill_gated(query, key, value, a, b, dt_bias, decay_scale, state_pool
                        num_accepted_tokens, scale, normalize_qk, out, state_out, stream)
 
 
+def rgdr_prefill_gated_ws(query, key, value, a, b, dt_bias, decay_scale, state_pool,
+                          actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens,
+                          scale=1.0, *, normalize_qk=False, workspace=None, out=None,
+                          state_out=None, stream=None):
+    """``rgdr_prefill_gated`` with a workspace, as ``rgdr_prefill_ws`` extends
+    ``rgdr_prefill``."""
+    workspace = _workspace(query, value, state_pool, workspace)
+    return _gated_call("rgdr_prefill_gated_ws", query, key, value, a, b, dt_bias, decay_scale,
+                       state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                       num_accepted_tokens, scale, normalize_qk, out, state_out, stream,
+                       workspace=workspace)
+
+
 def _gated_call(fn, query, key, value, a, b, dt_bias, decay_scale, state_pool,
                 actual_seq_lengths, ssm_state_indices, gk, num_accepted_tokens, scale,
-                normalize_qk, out, state_out, stream, extra=None):
+                normalize_qk, out, state_out, stream, extra=None, workspace=None):
     extra = extra or {}  # further output buffers, passed after state_out in this order
     lib = library()
     _dev(query, "query", torch.bfloat16, 4)
@@ -351,7 +415,7 @@ def _gated_call(fn, query, key, value, a, b, dt_bias, decay_scale, state_pool,
                               Dk, Dv, N, out.data_ptr(), state_out.data_ptr(),
                               *[t.data_ptr() for t in extra.values()],
                               NORMALIZE_QK if normalize_qk else 0,
-                              _stream_handle(stream, query.device))
+                              *_ws_args(workspace, query), _stream_handle(stream, query.device))
     _check(rc, fn)
     return out, state_out
 

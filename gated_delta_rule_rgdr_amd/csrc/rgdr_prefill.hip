@@ -184,6 +184,38 @@ __device__ __forceinline__ void store_cols(const uint32_t (&w)[(NC + 1) / 2],
     else
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rs, voff, soff, POL);
 }
+// NC consecutive fp32 columns of one row in one buffer access (the segmented form's
+// workspace).
+template <int NC>
+__device__ __forceinline__ void load_cols_f32(float (&v)[NC], __amdgpu_buffer_rsrc_t rs,
+                                              uint32_t voff, uint32_t soff) {
+    if constexpr (NC == 1) {
+        v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+    } else if constexpr (NC == 2) {
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+        v[0] = __uint_as_float(x.x);
+        v[1] = __uint_as_float(x.y);
+    } else {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = __uint_as_float(x[c]);
+    }
+}
+template <int NC>
+__device__ __forceinline__ void store_cols_f32(const float (&v)[NC], __amdgpu_buffer_rsrc_t rs,
+                                               uint32_t voff, uint32_t soff) {
+    if constexpr (NC == 1) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), rs, voff, soff, 0);
+    } else if constexpr (NC == 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v[0]), __float_as_uint(v[1])},
+                                              rs, voff, soff, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                  __float_as_uint(v[3])},
+            rs, voff, soff, 0);
+    }
+}
 __device__ __forceinline__ bf16x8 cat8(uint2 a, uint2 b) {
     return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
@@ -243,7 +275,16 @@ __device__ __forceinline__ f32x4 mma16(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f
 // into the B operand of Y = X S in the lane that holds it. The chunk's per-token results (Y_K,
 // Y_Q, U, O) use the same layout with tokens for rows: 16 tb + 4 kg + i is the token, and the
 // rows 4 kg .. + 3 of a 16-token block are the k slots of a 16x16x16 product over tokens.
-template <int DK, int GATE, bool NORM, int NC>
+//
+// SEG selects the form. 0: the single pass above. The segmented form cuts each entry's tokens
+// into segments (at the accepted count too) and runs the kernel twice over all segments at
+// once, with a sequential scan between (prefill_scan_kernel). Every state column follows the
+// recurrence on its own, with its own column of v, so a segment maps its incoming state S to
+// Phi S + Psi: Psi is the end state from zero, and the columns of Phi are the end states of
+// the identity's columns with v = 0. SEG = 1 evaluates both at once, as D_v + D_k columns,
+// and stores them in fp32; SEG = 2 starts each segment from its true incoming state (fp32,
+// from the scan) and writes the outputs. Neither reads nor commits the pool; the scan does.
+template <int DK, int GATE, bool NORM, int NC, int SEG = 0>
 __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
@@ -276,13 +317,38 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     // the buffer descriptors built from it in scalar registers.
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = tid / NTG, tg = tid % NTG;  // preparation: rows 4 r .. + 3, tokens TPT tg ..
-    const Item m = resolve(a, x, xcd_item(blockIdx.x, gridDim.x));
+    // Items (entry, value head, tile), or (entry, value head, segment, tile) when segmented.
+    int it = xcd_item(blockIdx.x, gridDim.x), seg = 0;
+    if constexpr (SEG != 0) {
+        const int tl = it % a.ntiles, rest = it / a.ntiles;
+        seg = rest % a.nseg;
+        it = (rest / a.nseg) * a.ntiles + tl;
+    }
+    const Item m = resolve(a, x, it);
     const int L = m.L, n = m.n;
+    // Tokens tbeg .. tend - 1 of the entry; the chunk holding ncut (the accepted prefix's
+    // end) stops there. A segment is seg_len tokens of [0, n), or of [n, L) after the
+    // ceil(n / seg_len) segments of the prefix.
+    int tbeg = 0, tend = L, ncut = n;
+    if constexpr (SEG != 0) {
+        const int sl = a.seg_len, na = (n + sl - 1) / sl;
+        tbeg = seg < na ? seg * sl : n + (seg - na) * sl;
+        tend = min(tbeg + sl, seg < na ? n : L);
+        if (tbeg >= tend) {  // an empty segment: only the first segment's outputs remain
+            if (SEG == 1 || seg != 0) return;
+            tbeg = tend = 0;
+        }
+        ncut = tend;
+    }
+    // Columns: D_v state columns, then (SEG = 1) the D_k columns of Phi.
+    const int ncols = SEG == 1 ? a.Dv + DK : a.Dv;
+    const int colw = m.tile * TV + WC * w;  // this wave's first column
+    const bool phi = SEG == 1 && colw >= a.Dv;  // a wave's columns are all of Psi or of Phi
 
     // A narrower last tile (D_v not a multiple of the tile) leaves the waves past D_v without
     // columns: their state, value and output accesses get empty ranges and they compute on
     // zeros.
-    const bool cols = m.tile * TV + WC * w < a.Dv;
+    const bool cols = colw < ncols;
     const uint32_t trange = cols ? tile_range<DK, TV>(a, m) : 0u;
     const size_t tb0 = m.state ? tile_base<DK, TV>(a, m) : 0;
     const auto rs = make_rsrc(a.pool + tb0, trange);
@@ -298,13 +364,14 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 
     // Chunks of at most kChunk tokens; the chunk holding the accepted prefix's end stops there.
     auto chunk_len = [&](int t0) {
-        const int t1 = min(t0 + kChunk, L);
-        return ((t0 < n && n < t1) ? n : t1) - t0;
+        const int t1 = min(t0 + kChunk, tend);
+        return ((t0 < ncut && ncut < t1) ? ncut : t1) - t0;
     };
     // This lane's values of tokens 16 tb + 4 kg + i, columns WC w + NC n16 + (0 .. NC - 1).
     uint32_t vr[2][4][NW];
     auto load_v = [&](int t0, int len) {
-        const auto rv = make_rsrc(a.v + (bh * a.T + t0) * a.Dv, cols ? (uint32_t)(len * a.Dv * 2) : 0u);
+        const auto rv = make_rsrc(a.v + (bh * a.T + t0) * a.Dv,
+                                  cols && !phi ? (uint32_t)(len * a.Dv * 2) : 0u);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -313,32 +380,57 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     };
 
     // The first chunk's operands, then the state tile (bf16 -> fp32, exact).
-    int t0 = 0, len = chunk_len(0);
+    int t0 = tbeg, len = chunk_len(tbeg);
     ChunkOps<DK> o;
-    load_chunk<DK, GATE>(a, m, o, r, tg, lane, 0, len);
-    load_v(0, len);
-    uint32_t raw[NRB][4][NW];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            load_cols<NC, RGDR_STATE_LOAD_POLICY>(raw[rb][i], rs, lane_off,
-                                                  (uint32_t)((16 * rb + i) * a.Dv * 2));
+    load_chunk<DK, GATE>(a, m, o, r, tg, lane, t0, len);
+    load_v(t0, len);
     f32x4 S[NRB][NC];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-                S[rb][c][i] = (c & 1) ? bf16_hi(raw[rb][i][c >> 1]) : bf16_lo(raw[rb][i][c >> 1]);
-    if (n == 0) {  // nothing accepted: commit the incoming bytes
+    // The segment's workspace rows (SEG != 0): [entry, head, segment][D_k rows][ncols] fp32.
+    const size_t wrow0 = ((bh * a.nseg + seg) * DK) * (size_t)ncols;
+    const uint32_t wlane = (uint32_t)((4 * kg * ncols + colw + NC * n16) * 4);
+    if constexpr (SEG == 1) {
+        // Psi from zero; Phi from the identity (column D_v + j holds row j's unit vector)
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                store_cols<NC, RGDR_STATE_STORE_POLICY>(raw[rb][i], rso, lane_off,
-                                                        (uint32_t)((16 * rb + i) * a.Dv * 2));
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    S[rb][c][i] = (colw + NC * n16 + c - a.Dv == 16 * rb + 4 * kg + i) ? 1.f : 0.f;
+    } else if constexpr (SEG == 2) {
+        const auto rsw = make_rsrc(a.ws_s + wrow0, cols ? (uint32_t)(DK * ncols * 4) : 0u);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v[NC];
+                load_cols_f32<NC>(v, rsw, wlane, (uint32_t)((16 * rb + i) * ncols * 4));
+#pragma unroll
+                for (int c = 0; c < NC; ++c) S[rb][c][i] = v[c];
+            }
+    } else {
+        uint32_t raw[NRB][4][NW];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                load_cols<NC, RGDR_STATE_LOAD_POLICY>(raw[rb][i], rs, lane_off,
+                                                      (uint32_t)((16 * rb + i) * a.Dv * 2));
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    S[rb][c][i] = (c & 1) ? bf16_hi(raw[rb][i][c >> 1]) : bf16_lo(raw[rb][i][c >> 1]);
+        if (n == 0) {  // nothing accepted: commit the incoming bytes
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    store_cols<NC, RGDR_STATE_STORE_POLICY>(raw[rb][i], rso, lane_off,
+                                                            (uint32_t)((16 * rb + i) * a.Dv * 2));
+        }
     }
     if (tid == 0) *cut = kChunk;
     lds_barrier();
@@ -541,7 +633,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     };
 
     int chunk = 0;
-    while (t0 < L) {  // uniform over the workgroup
+    while (t0 < tend) {  // uniform over the workgroup
         int Lc = len;
         // c_last of the previous chunk for this thread's rows (1 before the first chunk);
         // read once, since a second preparation pass rewrites crow
@@ -573,7 +665,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                     o.gk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
         }
-        const int t0n = t0 + Lc, lenn = t0n < L ? chunk_len(t0n) : 0;
+        const int t0n = t0 + Lc, lenn = t0n < tend ? chunk_len(t0n) : 0;
 
         __builtin_amdgcn_s_setprio(1);
         // M and N blocks, each wave its share (rotating by chunk so that the solves move
@@ -712,7 +804,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
             ov[0][c] = yq[0][c] + n0;
             ov[1][c] = yq[1][c] + n1;
         }
-        {
+        if constexpr (SEG != 1) {
             // tokens past the chunk fall outside the output range and are not written
             const auto rout = make_rsrc(a.out + (bh * a.T + t0) * a.Dv, cols ? (uint32_t)(Lc * a.Dv * 2) : 0u);
 #pragma unroll
@@ -746,7 +838,21 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         t0 = t0n;
         len = lenn;
         ++chunk;
-        if (t0 == n) {  // the accepted prefix ends here: commit diag(c_last) S
+        if (SEG == 1 && t0 == tend) {  // the segment's end state diag(c_last) S, in fp32
+            const auto rsw = make_rsrc(a.ws_e + wrow0, cols ? (uint32_t)(DK * ncols * 4) : 0u);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v[NC];
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) v[c] = S[rb][c][i] * cr[i];
+                    store_cols_f32<NC>(v, rsw, wlane, (uint32_t)((16 * rb + i) * ncols * 4));
+                }
+            }
+        }
+        if (SEG == 0 && t0 == n) {  // the accepted prefix ends here: commit diag(c_last) S
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
@@ -769,8 +875,9 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     }
 
     // Padded (or skipped) tokens: +0.0 rows. Each lane stores 8 of the wave's WC columns of
-    // one row, in groups of 64 / (WC / 8) rows; rows past T fall outside the range.
-    if (cols && L < a.T) {
+    // one row, in groups of 64 / (WC / 8) rows; rows past T fall outside the range. (The
+    // segmented form's first segment stores them.)
+    if (cols && L < a.T && SEG != 1 && seg == 0) {
         constexpr int CG = WC / 8, RG = 64 / CG;  // 8-column groups per row, rows per store
         const int pad = a.T - L;
         const auto rz = make_rsrc(a.out + (bh * a.T + L) * a.Dv + m.tile * TV + WC * w,
@@ -783,28 +890,102 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 }
 
 
-template <int DK, int GATE, int NC>
+// The segmented form's scan over an entry's segments, for one (entry, value head, 16-column
+// strip): thread t holds row t / 2 of columns 8 (t % 2) .. + 7 of the strip in fp32. From the
+// pool's state S, each segment j in order stores S as segment j's incoming state, then takes
+// S = Phi_j S + Psi_j (fp32, summed over the D_k rows in order). S is committed (bf16, round
+// to nearest even) at the segment boundary that is the accepted count n: before segment
+// ceil(n / seg_len), or after the last one.
+template <int DK>
+__global__ __launch_bounds__(2 * DK) void prefill_scan_kernel(
+    const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nacc) {
+    constexpr int SS = 16 + 4;  // LDS row stride of the strip (floats)
+    __shared__ float sl[DK * SS];
+    const int strips = a.Dv / 16;
+    const int strip = blockIdx.x % strips, bh = blockIdx.x / strips;
+    const int h = bh % a.Hv, b = bh / a.Hv;
+    const int slot = idx[b];
+    if (slot < 0 || slot >= a.N_slots) return;  // skipped entry: no state read or written
+    const int L = min(max(lens[b], 0), a.T), n = min(max(nacc[b], 0), L);
+    const int sl_len = a.seg_len, na = (n + sl_len - 1) / sl_len;
+    const int ns = na + (L - n + sl_len - 1) / sl_len;
+    const int t = threadIdx.x, i = t >> 1, half = t & 1;
+    const int c0 = strip * 16 + 8 * half;
+    const int dw = a.Dv + DK;
+    const size_t prow = (((size_t)slot * a.Hv + h) * DK + i) * a.Dv + c0;
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(a.pool + prow);
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        s[2 * e] = bf16_lo(raw[e]);
+        s[2 * e + 1] = bf16_hi(raw[e]);
+    }
+    for (int j = 0;; ++j) {
+        if (j == na) {  // the state after the accepted prefix
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[2 * e], s[2 * e + 1]);
+            *reinterpret_cast<u32x4 *>(a.pool_out + prow) = w;
+        }
+        if (j == ns) break;
+        const size_t seg0 = ((size_t)bh * a.nseg + j) * DK;
+        float *sin = a.ws_s + (seg0 + i) * a.Dv + c0;
+        *reinterpret_cast<f32x4 *>(sin) = f32x4{s[0], s[1], s[2], s[3]};
+        *reinterpret_cast<f32x4 *>(sin + 4) = f32x4{s[4], s[5], s[6], s[7]};
+        *reinterpret_cast<f32x4 *>(sl + i * SS + 8 * half) = f32x4{s[0], s[1], s[2], s[3]};
+        *reinterpret_cast<f32x4 *>(sl + i * SS + 8 * half + 4) = f32x4{s[4], s[5], s[6], s[7]};
+        __syncthreads();
+        const float *e = a.ws_e + (seg0 + i) * dw;
+        const f32x4 p0 = *reinterpret_cast<const f32x4 *>(e + c0);
+        const f32x4 p1 = *reinterpret_cast<const f32x4 *>(e + c0 + 4);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < DK; k += 4) {
+            const f32x4 ph = *reinterpret_cast<const f32x4 *>(e + a.Dv + k);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sl + (k + kk) * SS + 8 * half);
+                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sl + (k + kk) * SS + 8 * half + 4);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[c] = fmaf(ph[kk], x0[c], acc[c]);
+                    acc[4 + c] = fmaf(ph[kk], x1[c], acc[4 + c]);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s[c] = acc[c] + p0[c];
+            s[4 + c] = acc[4 + c] + p1[c];
+        }
+        __syncthreads();  // every thread has read the strip before it is rewritten
+    }
+}
+
+// One launch of n_items items, times nseg segments in the segmented passes.
+template <int DK, int GATE, int NC, int SEG = 0>
 static hipError_t launch_prefill(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
                                  const int32_t *nacc, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_items * (SEG ? (unsigned)a.nseg : 1u));
     if constexpr (GATE != kGateGiven) {
         if (a.norm_qk) {
-            hipLaunchKernelGGL((prefill_kernel<DK, GATE, true, NC>), dim3(a.n_items), dim3(256),
-                               0, stream, a, lens, idx, nacc);
+            hipLaunchKernelGGL((prefill_kernel<DK, GATE, true, NC, SEG>), grid, dim3(256), 0,
+                               stream, a, lens, idx, nacc);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prefill_kernel<DK, GATE, false, NC>), dim3(a.n_items), dim3(256), 0,
-                       stream, a, lens, idx, nacc);
+    hipLaunchKernelGGL((prefill_kernel<DK, GATE, false, NC, SEG>), grid, dim3(256), 0, stream,
+                       a, lens, idx, nacc);
     return hipGetLastError();
 }
 
-template <int DK, int NC>
+template <int DK, int NC, int SEG = 0>
 static hipError_t launch_prefill_gate(int gate, const DecodeArgs &a, const int32_t *lens,
                                       const int32_t *idx, const int32_t *nacc,
                                       hipStream_t stream) {
-    return gate == kGateGiven ? launch_prefill<DK, kGateGiven, NC>(a, lens, idx, nacc, stream)
-           : gate == kGateF32 ? launch_prefill<DK, kGateF32, NC>(a, lens, idx, nacc, stream)
-                              : launch_prefill<DK, kGateF16, NC>(a, lens, idx, nacc, stream);
+    return gate == kGateGiven ? launch_prefill<DK, kGateGiven, NC, SEG>(a, lens, idx, nacc, stream)
+           : gate == kGateF32 ? launch_prefill<DK, kGateF32, NC, SEG>(a, lens, idx, nacc, stream)
+                              : launch_prefill<DK, kGateF16, NC, SEG>(a, lens, idx, nacc, stream);
 }
 
 // Compute units of the current device, queried once per device; 0 if the query fails.
@@ -843,10 +1024,62 @@ static int prefill_resident_items_dk64() {
     return n;
 }
 
+// The segmented form: segments per entry and their length, and the workspace they take.
+// It pays where a call leaves most of the device idle: the single pass then runs at one
+// item's chain of chunks, while the segmented passes run every segment at once and do about
+// three times the chunk work (twice in the first pass, which carries Phi's D_k columns beside
+// the D_v of Psi, once in the second). The segments are sized so that the second pass fills
+// one round of two items per compute unit, and the form is taken from kSegMin of them.
+constexpr int kSegMin = 6, kSegMax = 16, kSegMinLen = 64;
+struct SegPlan {
+    int nseg = 0, seg_len = 0;  // segments allocated per (entry, head); tokens per segment
+    size_t off_s = 0, bytes = 0;  // incoming states at off_s; workspace bytes
+};
+static bool seg_plan(long long B, long long H_v, int T, int D_k, int D_v, int cus, SegPlan &p) {
+    const long long per = B * H_v * ((D_v + 127) / 128);  // second-pass items per segment
+    if (cus <= 0 || per <= 0) return false;
+    const long long fit = 2LL * cus / per;
+    const int want = (int)(fit < kSegMax ? fit : kSegMax);
+    if (want < kSegMin) return false;
+    int sl = (T + want - 1) / want;
+    sl = (sl + kChunk - 1) / kChunk * kChunk;
+    if (sl < kSegMinLen) return false;
+    p.seg_len = sl;
+    p.nseg = (T + sl - 1) / sl + 1;  // the accepted count may split one segment in two
+    const size_t rows = (size_t)B * H_v * p.nseg * D_k;
+    p.off_s = (rows * (D_v + D_k) * 4 + 255) / 256 * 256;
+    p.bytes = p.off_s + rows * D_v * 4;
+    return true;
+}
+
+template <int DK>
+static hipError_t launch_segmented(DecodeArgs &a, int gate, long long B, const SegPlan &p,
+                                   const int32_t *lens, const int32_t *idx, const int32_t *nacc,
+                                   void *ws, hipStream_t stream) {
+    a.ws_e = static_cast<float *>(ws);
+    a.ws_s = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_s);
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    a.item0 = 0;
+    // first pass: each segment's [Psi | Phi], D_v + D_k columns in 128-column tiles
+    a.ntiles = (a.Dv + DK + 127) / 128;
+    a.n_items = (int)(B * a.Hv * a.ntiles);
+    hipError_t err = launch_prefill_gate<DK, 2, 1>(gate, a, lens, idx, nacc, stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((prefill_scan_kernel<DK>), dim3((unsigned)(B * a.Hv * (a.Dv / 16))),
+                       dim3(2 * DK), 0, stream, a, lens, idx, nacc);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // second pass: each segment from its incoming state, the outputs
+    a.ntiles = (a.Dv + 127) / 128;
+    a.n_items = (int)(B * a.Hv * a.ntiles);
+    return launch_prefill_gate<DK, 2, 2>(gate, a, lens, idx, nacc, stream);
+}
+
 static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
                                  int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
                                  const int32_t *lens, const int32_t *idx, const int32_t *nacc,
-                                 hipStream_t stream) {
+                                 void *ws, size_t ws_bytes, hipStream_t stream) {
     if (B < 0 || H_q <= 0 || H_v <= 0 || T <= 0 || D_k <= 0 || D_v <= 0 || N_slots <= 0)
         return RGDR_ERR_SHAPE;
     if (T > kPrefillMaxT || H_v % H_q != 0) return RGDR_ERR_SHAPE;
@@ -857,6 +1090,23 @@ static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q
         !aligned(a.pool_out, 16) || !aligned(a.q, 16) || !aligned(a.k, 16) ||
         !aligned(a.gk, 16) || !aligned(lens, 4) || !aligned(idx, 4) || !aligned(nacc, 4))
         return RGDR_ERR_ALIGN;
+    if (ws != nullptr) {  // the segmented form, where it pays and the workspace holds it
+        const int cus = device_cus();
+        if (cus <= 0) return RGDR_ERR_HIP;
+        SegPlan p;
+        if (seg_plan(B, H_v, T, D_k, D_v, cus, p) && ws_bytes >= p.bytes && aligned(ws, 256)) {
+            a.Hq = H_q;
+            a.Hv = H_v;
+            a.T = T;
+            a.Dv = D_v;
+            a.N_slots = N_slots;
+            a.group = H_v / H_q;
+            const hipError_t err =
+                D_k == 128 ? launch_segmented<128>(a, gate, B, p, lens, idx, nacc, ws, stream)
+                           : launch_segmented<64>(a, gate, B, p, lens, idx, nacc, ws, stream);
+            return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
+        }
+    }
     // Tiles of 128 columns (the last may be 64 wide). At D_k = 64, 256-column tiles (D_v a
     // multiple of 256) when the call has more 128-column items than the device holds at once:
     // half as many items, each with the state bytes of a D_k = 128 item, so fewer rounds of
@@ -904,20 +1154,16 @@ static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q
     return err == hipSuccess ? RGDR_OK : RGDR_ERR_HIP;
 }
 
-}  // namespace rgdr
-
-extern "C" rgdr_status rgdr_prefill(const void *query, const void *key, const void *value,
-                                    const void *beta, const void *state_pool,
-                                    const int32_t *actual_seq_lengths,
-                                    const int32_t *ssm_state_indices, const float *g,
-                                    const float *gk, const int32_t *num_accepted_tokens,
-                                    float scale, int32_t B, int32_t H_q, int32_t H_v,
-                                    int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
-                                    void *out, void *state_out, hipStream_t stream) {
-    using namespace rgdr;
+static rgdr_status prefill_given(const void *query, const void *key, const void *value,
+                                 const void *beta, const void *state_pool, const int32_t *lens,
+                                 const int32_t *idx, const float *g, const float *gk,
+                                 const int32_t *nacc, float scale, int32_t B, int32_t H_q,
+                                 int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
+                                 int32_t N_slots, void *out, void *state_out, void *ws,
+                                 size_t ws_bytes, hipStream_t stream) {
     if (B == 0) return RGDR_OK;
-    if (!query || !key || !value || !beta || !state_pool || !actual_seq_lengths ||
-        !ssm_state_indices || !g || !gk || !num_accepted_tokens || !out || !state_out)
+    if (!query || !key || !value || !beta || !state_pool || !lens || !idx || !g || !gk ||
+        !nacc || !out || !state_out)
         return RGDR_ERR_NULL;
     if (!aligned(beta, 2) || !aligned(g, 4)) return RGDR_ERR_ALIGN;
     DecodeArgs a = {};
@@ -931,23 +1177,23 @@ extern "C" rgdr_status rgdr_prefill(const void *query, const void *key, const vo
     a.out = static_cast<uint16_t *>(out);
     a.pool_out = static_cast<uint16_t *>(state_out);
     a.scale = scale;
-    return prefill_entry(a, kGateGiven, B, H_q, H_v, T, D_k, D_v, N_slots, actual_seq_lengths,
-                         ssm_state_indices, num_accepted_tokens, stream);
+    return prefill_entry(a, kGateGiven, B, H_q, H_v, T, D_k, D_v, N_slots, lens, idx, nacc, ws,
+                         ws_bytes, stream);
 }
 
-extern "C" rgdr_status rgdr_prefill_gated(
-    const void *query, const void *key, const void *value, const void *gate_a,
-    const void *gate_b, const float *dt_bias, const float *decay_scale, rgdr_dtype gate_dtype,
-    const void *state_pool, const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
-    const float *gk, const int32_t *num_accepted_tokens, float scale, int32_t B, int32_t H_q,
-    int32_t H_v, int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
-    void *state_out, uint32_t flags, hipStream_t stream) {
-    using namespace rgdr;
+static rgdr_status prefill_gated(const void *query, const void *key, const void *value,
+                                 const void *gate_a, const void *gate_b, const float *dt_bias,
+                                 const float *decay_scale, rgdr_dtype gate_dtype,
+                                 const void *state_pool, const int32_t *lens,
+                                 const int32_t *idx, const float *gk, const int32_t *nacc,
+                                 float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                 int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                                 void *state_out, uint32_t flags, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
     if (flags & ~(uint32_t)RGDR_NORMALIZE_QK) return RGDR_ERR_UNSUPPORTED;
     if (B == 0) return RGDR_OK;
     if (!query || !key || !value || !gate_a || !gate_b || !dt_bias || !decay_scale ||
-        !state_pool || !actual_seq_lengths || !ssm_state_indices || !gk ||
-        !num_accepted_tokens || !out || !state_out)
+        !state_pool || !lens || !idx || !gk || !nacc || !out || !state_out)
         return RGDR_ERR_NULL;
     if (gate_dtype != RGDR_F32 && gate_dtype != RGDR_F16) return RGDR_ERR_DTYPE;
     const uintptr_t esz = gate_dtype == RGDR_F16 ? 2 : 4;
@@ -969,6 +1215,78 @@ extern "C" rgdr_status rgdr_prefill_gated(
     a.pool_out = static_cast<uint16_t *>(state_out);
     a.scale = scale;
     return prefill_entry(a, gate_dtype == RGDR_F16 ? kGateF16 : kGateF32, B, H_q, H_v, T, D_k,
-                         D_v, N_slots, actual_seq_lengths, ssm_state_indices,
-                         num_accepted_tokens, stream);
+                         D_v, N_slots, lens, idx, nacc, ws, ws_bytes, stream);
+}
+
+}  // namespace rgdr
+
+extern "C" rgdr_status rgdr_prefill(const void *query, const void *key, const void *value,
+                                    const void *beta, const void *state_pool,
+                                    const int32_t *actual_seq_lengths,
+                                    const int32_t *ssm_state_indices, const float *g,
+                                    const float *gk, const int32_t *num_accepted_tokens,
+                                    float scale, int32_t B, int32_t H_q, int32_t H_v,
+                                    int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
+                                    void *out, void *state_out, hipStream_t stream) {
+    return rgdr::prefill_given(query, key, value, beta, state_pool, actual_seq_lengths,
+                               ssm_state_indices, g, gk, num_accepted_tokens, scale, B, H_q,
+                               H_v, T, D_k, D_v, N_slots, out, state_out, nullptr, 0, stream);
+}
+
+extern "C" rgdr_status rgdr_prefill_gated(
+    const void *query, const void *key, const void *value, const void *gate_a,
+    const void *gate_b, const float *dt_bias, const float *decay_scale, rgdr_dtype gate_dtype,
+    const void *state_pool, const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+    const float *gk, const int32_t *num_accepted_tokens, float scale, int32_t B, int32_t H_q,
+    int32_t H_v, int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+    void *state_out, uint32_t flags, hipStream_t stream) {
+    return rgdr::prefill_gated(query, key, value, gate_a, gate_b, dt_bias, decay_scale,
+                               gate_dtype, state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                               num_accepted_tokens, scale, B, H_q, H_v, T, D_k, D_v, N_slots,
+                               out, state_out, flags, nullptr, 0, stream);
+}
+
+extern "C" rgdr_status rgdr_prefill_workspace_size(int32_t B, int32_t H_v, int32_t T,
+                                                   int32_t D_k, int32_t D_v, size_t *bytes) {
+    using namespace rgdr;
+    if (!bytes) return RGDR_ERR_NULL;
+    *bytes = 0;
+    if (B < 0 || H_v <= 0 || T <= 0 || D_k <= 0 || D_v <= 0 || T > kPrefillMaxT)
+        return RGDR_ERR_SHAPE;
+    if ((D_k != 64 && D_k != 128) || D_v % 64 != 0 || D_v > 4096) return RGDR_ERR_UNSUPPORTED;
+    if (B == 0) return RGDR_OK;
+    const int cus = device_cus();
+    if (cus <= 0) return RGDR_ERR_HIP;
+    SegPlan p;
+    if (seg_plan(B, H_v, T, D_k, D_v, cus, p)) *bytes = p.bytes;
+    return RGDR_OK;
+}
+
+extern "C" rgdr_status rgdr_prefill_ws(const void *query, const void *key, const void *value,
+                                       const void *beta, const void *state_pool,
+                                       const int32_t *actual_seq_lengths,
+                                       const int32_t *ssm_state_indices, const float *g,
+                                       const float *gk, const int32_t *num_accepted_tokens,
+                                       float scale, int32_t B, int32_t H_q, int32_t H_v,
+                                       int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots,
+                                       void *out, void *state_out, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return rgdr::prefill_given(query, key, value, beta, state_pool, actual_seq_lengths,
+                               ssm_state_indices, g, gk, num_accepted_tokens, scale, B, H_q,
+                               H_v, T, D_k, D_v, N_slots, out, state_out, workspace,
+                               workspace_bytes, stream);
+}
+
+extern "C" rgdr_status rgdr_prefill_gated_ws(
+    const void *query, const void *key, const void *value, const void *gate_a,
+    const void *gate_b, const float *dt_bias, const float *decay_scale, rgdr_dtype gate_dtype,
+    const void *state_pool, const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+    const float *gk, const int32_t *num_accepted_tokens, float scale, int32_t B, int32_t H_q,
+    int32_t H_v, int32_t T, int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+    void *state_out, uint32_t flags, void *workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+    return rgdr::prefill_gated(query, key, value, gate_a, gate_b, dt_bias, decay_scale,
+                               gate_dtype, state_pool, actual_seq_lengths, ssm_state_indices, gk,
+                               num_accepted_tokens, scale, B, H_q, H_v, T, D_k, D_v, N_slots,
+                               out, state_out, flags, workspace, workspace_bytes, stream);
 }

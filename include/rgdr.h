@@ -17,6 +17,8 @@
  *   rgdr_prefill The same recurrence over long sequences (T up to 65536): the page's notes
  *                limit the decode operator to T <= 8 and hand the parallel prefill to a
  *                chunk-level operator; this is that operator, with rgdr_decode's arguments.
+ *                rgdr_prefill_ws (and rgdr_prefill_gated_ws) take a caller's workspace, with
+ *                which calls of few sequences run all of a sequence's segments at once.
  *   la_gate      The gate front end of the kernel README "com.microsoft.LinearAttentionGate"
  *                (Description; Inputs, Outputs, Type constraints tables):
  *                  decay = decay_scale[h] * softplus(a + dt_bias[h]),  beta = sigmoid(b),
@@ -24,7 +26,8 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers to row-major, contiguous buffers owned by
- *     the caller. The library allocates nothing and keeps no pointer after returning.
+ *     the caller. The library allocates nothing and keeps no pointer after returning; a
+ *     call that needs scratch memory takes it as a workspace argument.
  *   - Calls are asynchronous on `stream` (0 = the null stream). The return value reports
  *     only errors that the host can see before launching (arguments, shapes, alignment,
  *     a failed launch); when it is not RGDR_OK nothing was launched.
@@ -39,6 +42,7 @@
 #ifndef RGDR_H
 #define RGDR_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -232,6 +236,61 @@ rgdr_status rgdr_prefill_gated(const void *query, const void *key, const void *v
                                int32_t H_q, int32_t H_v, int32_t T, int32_t D_k, int32_t D_v,
                                int32_t N_slots, void *out, void *state_out, uint32_t flags,
                                hipStream_t stream);
+
+/*
+ * rgdr_prefill_workspace_size -- the workspace rgdr_prefill_ws and rgdr_prefill_gated_ws
+ * use for a call of these sizes on the current device: *bytes = 0 when such a call runs in
+ * one pass (it then needs none). Sizes as rgdr_prefill; H_q does not matter.
+ * Errors: RGDR_ERR_NULL (bytes NULL), RGDR_ERR_SHAPE, RGDR_ERR_UNSUPPORTED as rgdr_prefill;
+ * RGDR_ERR_HIP if the device cannot be queried.
+ */
+rgdr_status rgdr_prefill_workspace_size(int32_t B, int32_t H_v, int32_t T, int32_t D_k,
+                                        int32_t D_v, size_t *bytes);
+
+/*
+ * rgdr_prefill_ws -- rgdr_prefill (same arguments, results and errors) with a workspace.
+ * The recurrence maps each segment of tokens affinely: a segment takes its incoming state S
+ * to Phi S + Psi, where Psi is its end state from a zero state and Phi (D_k x D_k) is the
+ * product of its tokens' factors (I - beta_t k_t k_t^T) diag(exp(g_t) exp(gk_t)) (MindSpore
+ * Lite page above, algorithm section: steps 1 and 3 are linear in S, with v entering only
+ * through Psi). Where a call has too few (entry, value head) pairs to fill the device, the
+ * entries' tokens are cut into segments (at num_accepted_tokens too), every segment's Phi
+ * and Psi are evaluated at once, a short sequential scan composes them in fp32 into each
+ * segment's incoming state and commits the state after the accepted prefix, and every
+ * segment then produces its outputs from its incoming state at once.
+ *   workspace        device memory of at least rgdr_prefill_workspace_size's bytes, 256-byte
+ *                    aligned, owned by the caller, not read before it is written; the call
+ *                    uses it until it completes on `stream`. Calls that share a workspace
+ *                    must be ordered (the same stream, or synchronised).
+ *   workspace_bytes  its size.
+ * With workspace NULL, or smaller than the size query, or where the size query gives 0, the
+ * call runs rgdr_prefill's single pass. Both forms hold the same precision (fp32 state,
+ * products of split bf16 operands); their rounding differs, since the segmented form
+ * groups the arithmetic by segment.
+ */
+rgdr_status rgdr_prefill_ws(const void *query, const void *key, const void *value,
+                            const void *beta, const void *state_pool,
+                            const int32_t *actual_seq_lengths, const int32_t *ssm_state_indices,
+                            const float *g, const float *gk, const int32_t *num_accepted_tokens,
+                            float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                            int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                            void *state_out, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * rgdr_prefill_gated_ws -- rgdr_prefill_gated with a workspace, as rgdr_prefill_ws extends
+ * rgdr_prefill.
+ */
+rgdr_status rgdr_prefill_gated_ws(const void *query, const void *key, const void *value,
+                                  const void *gate_a, const void *gate_b, const float *dt_bias,
+                                  const float *decay_scale, rgdr_dtype gate_dtype,
+                                  const void *state_pool, const int32_t *actual_seq_lengths,
+                                  const int32_t *ssm_state_indices, const float *gk,
+                                  const int32_t *num_accepted_tokens, float scale, int32_t B,
+                                  int32_t H_q, int32_t H_v, int32_t T, int32_t D_k,
+                                  int32_t D_v, int32_t N_slots, void *out, void *state_out,
+                                  uint32_t flags, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * la_gate -- decay = decay_scale * softplus(a + dt_bias) and, when beta_out != NULL,

@@ -33,6 +33,7 @@ def test_header_declares_the_operations():
     names = declared_functions()
     for want in ("rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated",
                  "rgdr_decode_gated_snapshots", "rgdr_prefill", "rgdr_prefill_gated",
+                 "rgdr_prefill_ws", "rgdr_prefill_gated_ws", "rgdr_prefill_workspace_size",
                  "la_gate", "rgdr_validate", "rgdr_validate_host", "rgdr_status_string"):
         assert want in names, names
 
@@ -292,3 +293,51 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         g.rgdr_decode(x, x, x, x, x, x, x, x, x, x)
     with pytest.raises(ImportError):
         g.la_gate(x, x, x)
+
+
+def test_prefill_workspace_entries_argument_checks(lib):
+    """The workspace size query and the workspace entries reject bad arguments before any
+    HIP call (the size query needs the device only for sizes it accepts)."""
+    import ctypes as C
+    n = C.c_size_t(123)
+    assert lib.rgdr_prefill_workspace_size(1, 4, 1024, 128, 128, None) == NULL
+    assert lib.rgdr_prefill_workspace_size(1, 4, 0, 128, 128, C.byref(n)) == SHAPE
+    assert n.value == 0
+    assert lib.rgdr_prefill_workspace_size(1, 4, 65537, 128, 128, C.byref(n)) == SHAPE
+    assert lib.rgdr_prefill_workspace_size(-1, 4, 64, 128, 128, C.byref(n)) == SHAPE
+    assert lib.rgdr_prefill_workspace_size(1, 4, 64, 96, 128, C.byref(n)) == UNSUP
+    assert lib.rgdr_prefill_workspace_size(1, 4, 64, 128, 96, C.byref(n)) == UNSUP
+    assert lib.rgdr_prefill_workspace_size(0, 4, 64, 128, 128, C.byref(n)) == OK
+    assert n.value == 0
+
+    def call(ptrs=None, **kw):
+        dims = dict(B=2, Hq=2, Hv=4, T=64, Dk=128, Dv=128, N=4)
+        dims.update(kw)
+        p = [0x10000] * 10 if ptrs is None else ptrs
+        return lib.rgdr_prefill_ws(*p[:10], 1.0, dims["B"], dims["Hq"], dims["Hv"], dims["T"],
+                                   dims["Dk"], dims["Dv"], dims["N"], kw.get("out", 0x20000),
+                                   kw.get("state_out", 0x30000), 0x40000, 1 << 20, None)
+    assert call(ptrs=[None] * 10, B=0, out=None, state_out=None) == OK
+    for i in range(10):
+        p = [0x10000] * 10
+        p[i] = None
+        assert call(ptrs=p) == NULL, i
+    assert call(T=65537) == SHAPE
+    assert call(Dk=64, Dv=100) == UNSUP
+    bad = [0x10000] * 10
+    bad[2] = 0x10004  # value not 16-byte aligned
+    assert call(ptrs=bad) == ALIGN
+
+    def gcall(ptrs=None, gdt=F32, flags=0, **kw):
+        dims = dict(B=2, Hq=2, Hv=4, T=64, Dk=128, Dv=128, N=4)
+        dims.update(kw)
+        p = [0x10000] * 12 if ptrs is None else ptrs
+        return lib.rgdr_prefill_gated_ws(*p[:7], gdt, *p[7:12], 1.0, dims["B"], dims["Hq"],
+                                         dims["Hv"], dims["T"], dims["Dk"], dims["Dv"],
+                                         dims["N"], 0x20000, 0x30000, flags, 0x40000, 1 << 20,
+                                         None)
+    assert gcall(ptrs=[None] * 12, B=0) == OK
+    assert gcall(ptrs=[None] + [0x10000] * 11) == NULL
+    assert gcall(gdt=BF16) == DTYPE
+    assert gcall(flags=4) == UNSUP
+    assert gcall(Hq=3) == SHAPE
