@@ -59,7 +59,7 @@ WARM_MS = 25.0      # untimed graph replays before any timed one, in wall-clock 
 # The host share of one GPU on the benchmark boxes: the threaded CPU baseline uses at most
 # this many threads, whatever the process's affinity mask shows.
 HOST_CORES_PER_GPU = 16
-PREFILL_WORKLOADS = (5, 6)
+PREFILL_WORKLOADS = (5, 6, 7)
 
 
 def log(msg):
@@ -121,6 +121,35 @@ def prefill_mfma_flops(inp, cus):
     big = 4 * (12 * npb + 3 * nrb) * nc + 18 * npb  # 16x16x32 products per item and chunk
     small = 4 * 18 * nc                         # 16x16x16 products
     return chunks * items * (big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2)
+
+
+def segmented_mfma_flops(inp, cus):
+    """Matrix-core flops the segmented form's two passes execute per call (the scan's fp32
+    products run on the VALU and are not counted). Segments as the library cuts them: the
+    second pass's items per segment (128-column tiles) fill two per compute unit, at most
+    16 segments, each a multiple of 32 tokens; the prefix [0, n) and the rest [n, L) are
+    cut separately. Each segment is walked in chunks of up to 32 tokens; the first pass
+    carries D_v + D_k columns, the second D_v."""
+    import numpy as np
+    per = inp.B * inp.Hv * -(-inp.Dv // 128)
+    want = min(16, 2 * cus // per)
+    sl = -(-(-(-inp.T // want)) // 32) * 32
+    lens = np.clip(inp.actual_seq_lengths, 0, inp.T)
+    nacc = np.clip(inp.num_accepted_tokens, 0, lens)
+    valid = (inp.ssm_state_indices >= 0) & (inp.ssm_state_indices < inp.N_slots)
+    chunks = 0
+    for L, n, ok in zip(lens, nacc, valid):
+        if not ok:
+            continue
+        for a0, a1 in ((0, int(n)), (int(n), int(L))):
+            for t0 in range(a0, a1, sl):
+                chunks += -(-(min(t0 + sl, a1) - t0) // 32)
+    npb, nrb = inp.Dk // 32, inp.Dk // 16
+    big = 4 * (12 * npb + 3 * nrb) * 2 + 18 * npb
+    small = 4 * 18 * 2
+    per_item_chunk = big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2
+    items = inp.Hv * (-(-(inp.Dv + inp.Dk) // 128) + -(-inp.Dv // 128))
+    return chunks * items * per_item_chunk
 
 
 SOURCES_COMMON = ("gated_delta_rule_rgdr_amd/csrc/rgdr_device.h",
@@ -337,6 +366,19 @@ class Workload:
         self.decode_fn = rg.rgdr_prefill if self.prefill else rg.rgdr_decode
         self.fused_name = "rgdr_prefill_gated" if self.prefill else "rgdr_decode_gated"
         self.decode_name = "rgdr_prefill" if self.prefill else "rgdr_decode"
+        # Long sequences with too few (entry, head) pairs to fill the device take the
+        # segmented form, through the workspace entries (one workspace, every call in order
+        # on one stream).
+        self.ws_bytes = rg.rgdr_prefill_workspace_size(B, Hv, T, Dk, Dv, dev) if self.prefill else 0
+        self.ws = None
+        if self.ws_bytes:
+            self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+            ws = self.ws
+            self.single_fused_fn = self.fused_fn
+            self.fused_fn = lambda *a_, **k_: rg.rgdr_prefill_gated_ws(*a_, workspace=ws, **k_)
+            self.decode_fn = lambda *a_, **k_: rg.rgdr_prefill_ws(*a_, workspace=ws, **k_)
+            self.fused_name = "rgdr_prefill_gated_ws (segmented)"
+            self.decode_name = "rgdr_prefill_ws (segmented)"
 
     # g and beta come out of the gate as [B, T, H_v]; the recurrence reads [B, H_v, T]. With
     # T = 1 these are the same bytes. For T > 1 the unfused chain transposes them with torch
@@ -362,6 +404,12 @@ class Workload:
         self.fused_fn(s["q"], s["k"], s["v"], s["a"], s["b"], self.dt, self.ds, s["pool"],
                       self.lens, self.idx, s["gk"], self.nacc, self.inp.scale, out=s["out"])
 
+    def single_fused(self, s):
+        """The single-pass fused call (segmented workloads: the form the workspace replaces)."""
+        self.single_fused_fn(s["q"], s["k"], s["v"], s["a"], s["b"], self.dt, self.ds,
+                             s["pool"], self.lens, self.idx, s["gk"], self.nacc, self.inp.scale,
+                             out=s["out"])
+
     def step(self, i):
         self.fused(self.sets[i % self.R])
 
@@ -374,6 +422,8 @@ class Workload:
 
     def free(self):
         self.sets = []
+        self.ws = None
+        self.fused_fn = self.decode_fn = None
         self.torch.cuda.synchronize()
         self.torch.cuda.empty_cache()
 
@@ -443,7 +493,8 @@ def roofline(wl, us):
          "traffic": measured_traffic(wl.wid, wl.batch), "bytes_per_launch": wl.step_bytes,
          "avg_launch_us": round(us, 3)}
     if wl.prefill:
-        fl = prefill_mfma_flops(wl.inp, wl.cus)
+        fl = (segmented_mfma_flops(wl.inp, wl.cus) if wl.ws_bytes
+              else prefill_mfma_flops(wl.inp, wl.cus))
         tf = fl / (us * 1e-6) / 1e12
         r["mfma_executed"] = {"flops_per_launch": fl, "achieved_tflops": round(tf, 1),
                               "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
@@ -462,6 +513,11 @@ def extra_entry(torch, stream, wl, n):
     inp = wl.inp
     r = roofline(wl, us)
     r["launch_us_replays"] = [round(x, 3) for x in per]
+    if wl.ws_bytes:  # the segmented form: three launches per call; the single pass beside it
+        r["launches_per_call"] = 3
+        r["workspace_bytes"] = wl.ws_bytes
+        sus, _ = kernel_avg_us(torch, stream, wl.single_fused, wl.sets, max(4, n // 4))
+        r["single_pass_us"] = round(sus, 3)
     return {"workload": wl.name, "config": {"B": inp.B, "H_q": inp.Hq, "H_v": inp.Hv,
                                             "T": inp.T, "D_k": inp.Dk, "D_v": inp.Dv,
                                             "N_slots": inp.N_slots, "rotation_sets": wl.R,
@@ -526,11 +582,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: auto, >= 1 GiB)")
     ap.add_argument("--batch", type=int, default=None,
                     help="replace the workload's batch size B (same recipe otherwise)")
-    ap.add_argument("--extra", default="1,3,4,5,6",
+    ap.add_argument("--extra", default="1,3,4,5,6,7",
                     help="other workloads whose fused-call duration the line also carries "
                          "(comma-separated ids; empty for none)")
     ap.add_argument("--snapshots", default="3",
@@ -643,7 +699,7 @@ def main():
     extras = {}
     for tok in [t for t in args.extra.split(",") if t.strip()]:
         ew = int(tok)
-        if ew == wid or ew not in range(7):
+        if ew == wid or ew not in range(8):
             continue
         e = Workload(ew, dev, 0, args.extra_steps)
         extras[str(ew)] = extra_entry(torch, stream, e, args.extra_steps)

@@ -891,17 +891,24 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 
 
 // The segmented form's scan over an entry's segments, for one (entry, value head, 16-column
-// strip): thread t holds row t / 2 of columns 8 (t % 2) .. + 7 of the strip in fp32. From the
-// pool's state S, each segment j in order stores S as segment j's incoming state, then takes
-// S = Phi_j S + Psi_j (fp32, summed over the D_k rows in order). S is committed (bf16, round
-// to nearest even) at the segment boundary that is the accepted count n: before segment
-// ceil(n / seg_len), or after the last one.
+// strip). Wave w holds rows 32 w .. 32 w + 31 of the strip in fp32, in the matrix cores'
+// accumulator layout: lane (g, n) = (lane / 16, lane % 16) holds rows 16 rb + 4 g + i (rb =
+// 2 w, 2 w + 1; i < 4) of column n. From the pool's state S, each segment j in order stores S
+// as segment j's incoming state, then takes S = Phi_j S + Psi_j: Psi_j starts each 16 x 16
+// accumulator, and Phi_j S is a 16x16x32 product per (row block, 32-row block of S), with
+// both operands split into bf16 high parts and remainders (three products, fp32
+// accumulation). The accumulators of row blocks 2 p and 2 p + 1 are exactly the B operand of
+// the product over rows 32 p .. + 31 in the same lanes (k slots 4 g .. + 3, then 16 + 4 g ..
+// + 3), so each wave shares its split rows through LDS and reads the others'. Segment
+// j + 1's rows of Phi and Psi are loaded while segment j is computed. S is committed (bf16,
+// round to nearest even) at the segment boundary that is the accepted count n: before
+// segment ceil(n / seg_len), or after the last one.
 template <int DK>
 __global__ __launch_bounds__(2 * DK) void prefill_scan_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
-    constexpr int SS = 16 + 4;  // LDS row stride of the strip (floats)
-    __shared__ float sl[DK * SS];
+    constexpr int NWV = DK / 32;  // waves: wave w owns the K block (32 rows) w
+    __shared__ uint2 bfr[2][NWV][4][64];  // [segment parity][K block][hi lo x 2 halves][lane]
     const int strips = a.Dv / 16;
     const int strip = blockIdx.x % strips, bh = blockIdx.x / strips;
     const int h = bh % a.Hv, b = bh / a.Hv;
@@ -910,55 +917,91 @@ __global__ __launch_bounds__(2 * DK) void prefill_scan_kernel(
     const int L = min(max(lens[b], 0), a.T), n = min(max(nacc[b], 0), L);
     const int sl_len = a.seg_len, na = (n + sl_len - 1) / sl_len;
     const int ns = na + (L - n + sl_len - 1) / sl_len;
-    const int t = threadIdx.x, i = t >> 1, half = t & 1;
-    const int c0 = strip * 16 + 8 * half;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nn = lane & 15, g = lane >> 4;
+    const int col = strip * 16 + nn;
     const int dw = a.Dv + DK;
-    const size_t prow = (((size_t)slot * a.Hv + h) * DK + i) * a.Dv + c0;
-    const u32x4 raw = *reinterpret_cast<const u32x4 *>(a.pool + prow);
-    float s[8];
+    // this lane's state rows: 16 (2 w + r) + 4 g + i, column col
+    auto srow = [&](int r, int i) { return 32 * w + 16 * r + 4 * g + i; };
+    const size_t pbase = ((size_t)slot * a.Hv + h) * DK * a.Dv + col;
+    f32x4 st[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        s[2 * e] = bf16_lo(raw[e]);
-        s[2 * e + 1] = bf16_hi(raw[e]);
-    }
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[r][i] = bf16_to_f32(a.pool[pbase + (size_t)srow(r, i) * a.Dv]);
+    // Segment j's operands for this lane: A fragments of Phi_j (rows 16 (2 w + r) + nn, k slots
+    // of K block p: 32 p + 4 g .. + 3 and 32 p + 16 + 4 g .. + 3) and Psi_j at the state rows.
+    f32x4 ph[2][NWV][2], ps[2], phn[2][NWV][2], psn[2];
+    auto load_seg = [&](int j) {
+        const float *e = a.ws_e + ((size_t)bh * a.nseg + j) * DK * dw;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float *prow = e + (size_t)(32 * w + 16 * r + nn) * dw + a.Dv;
+#pragma unroll
+            for (int p = 0; p < NWV; ++p) {
+                phn[r][p][0] = *reinterpret_cast<const f32x4 *>(prow + 32 * p + 4 * g);
+                phn[r][p][1] = *reinterpret_cast<const f32x4 *>(prow + 32 * p + 16 + 4 * g);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) psn[r][i] = e[(size_t)srow(r, i) * dw + col];
+        }
+    };
+    if (ns > 0) load_seg(0);
     for (int j = 0;; ++j) {
         if (j == na) {  // the state after the accepted prefix
-            u32x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[2 * e], s[2 * e + 1]);
-            *reinterpret_cast<u32x4 *>(a.pool_out + prow) = w;
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.pool_out[pbase + (size_t)srow(r, i) * a.Dv] = f32_to_bf16(st[r][i]);
         }
         if (j == ns) break;
-        const size_t seg0 = ((size_t)bh * a.nseg + j) * DK;
-        float *sin = a.ws_s + (seg0 + i) * a.Dv + c0;
-        *reinterpret_cast<f32x4 *>(sin) = f32x4{s[0], s[1], s[2], s[3]};
-        *reinterpret_cast<f32x4 *>(sin + 4) = f32x4{s[4], s[5], s[6], s[7]};
-        *reinterpret_cast<f32x4 *>(sl + i * SS + 8 * half) = f32x4{s[0], s[1], s[2], s[3]};
-        *reinterpret_cast<f32x4 *>(sl + i * SS + 8 * half + 4) = f32x4{s[4], s[5], s[6], s[7]};
-        __syncthreads();
-        const float *e = a.ws_e + (seg0 + i) * dw;
-        const f32x4 p0 = *reinterpret_cast<const f32x4 *>(e + c0);
-        const f32x4 p1 = *reinterpret_cast<const f32x4 *>(e + c0 + 4);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < DK; k += 4) {
-            const f32x4 ph = *reinterpret_cast<const f32x4 *>(e + a.Dv + k);
+        float *sin = a.ws_s + ((size_t)bh * a.nseg + j) * DK * a.Dv + col;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sl + (k + kk) * SS + 8 * half);
-                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sl + (k + kk) * SS + 8 * half + 4);
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    acc[c] = fmaf(ph[kk], x0[c], acc[c]);
-                    acc[4 + c] = fmaf(ph[kk], x1[c], acc[4 + c]);
-                }
+            for (int i = 0; i < 4; ++i) sin[(size_t)srow(r, i) * a.Dv] = st[r][i];
+        {
+            uint2 h0, l0, h1, l1;
+            split4(st[0], h0, l0);
+            split4(st[1], h1, l1);
+            bfr[j & 1][w][0][lane] = h0;
+            bfr[j & 1][w][1][lane] = h1;
+            bfr[j & 1][w][2][lane] = l0;
+            bfr[j & 1][w][3][lane] = l1;
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            ps[r] = psn[r];
+#pragma unroll
+            for (int p = 0; p < NWV; ++p) {
+                ph[r][p][0] = phn[r][p][0];
+                ph[r][p][1] = phn[r][p][1];
             }
         }
+        if (j + 1 < ns) load_seg(j + 1);
+        lds_barrier();  // (LDS only: the next segment's loads stay in flight)
+        bf16x8 bh8[NWV], bl8[NWV];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            s[c] = acc[c] + p0[c];
-            s[4 + c] = acc[4 + c] + p1[c];
+        for (int p = 0; p < NWV; ++p) {
+            bh8[p] = cat8(bfr[j & 1][p][0][lane], bfr[j & 1][p][1][lane]);
+            bl8[p] = cat8(bfr[j & 1][p][2][lane], bfr[j & 1][p][3][lane]);
         }
-        __syncthreads();  // every thread has read the strip before it is rewritten
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            f32x4 acc = ps[r];
+#pragma unroll
+            for (int p = 0; p < NWV; ++p) {
+                uint2 ah0, al0, ah1, al1;
+                split4(ph[r][p][0], ah0, al0);
+                split4(ph[r][p][1], ah1, al1);
+                const bf16x8 ah = cat8(ah0, ah1), al = cat8(al0, al1);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8[p], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8[p], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl8[p], acc, 0, 0, 0);
+            }
+            st[r] = acc;
+        }
     }
 }
 

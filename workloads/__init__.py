@@ -19,6 +19,9 @@ README, Inputs table):
   6  chunked prefill:        B=4, H_q=H_v=64, T=1024, D_k=64, D_v=512, 8 slots, 4 distinct
                              (the same reading at the page example's head size, with the
                              step bytes of workload 5)
+  7  single-prompt prefill:  B=1, H_q=16, H_v=32, T=8192, D=128, 2 slots, 1 used (workload
+                             5's heads with one long prompt: too few (entry, head) pairs to
+                             fill the device, the case the segmented form serves)
 
 Recipe (one numpy ``default_rng(1000 + id)`` stream, drawn in this order):
   q, k ~ N(0,1) fp64, L2-normalised along D_k per (b, head, t), stored as bf16;
@@ -29,7 +32,7 @@ Recipe (one numpy ``default_rng(1000 + id)`` stream, drawn in this order):
   a, b ~ N(0,1) fp32 [B,T,H_v]; dt_bias ~ N(0,1) fp32 [H_v]; A_log ~ U(0, ln 16) fp32
   [H_v]; decay_scale = -exp(A_log) in fp32 (the gated-DeltaNet choice the README names).
 
-With ``gate_inputs=True`` a workload without its own gate inputs (0-3, 5, 6) also gets raw gate
+With ``gate_inputs=True`` a workload without its own gate inputs (0-3, 5-7) also gets raw gate
 projections, drawn after everything else: a, b ~ N(0,1) fp32 [B,T,H_v], dt_bias = 0 and
 decay_scale = -1. The gate then yields g = -softplus(a) and beta = sigmoid(b), the same
 distributions the recipe draws g and beta from, so the whole path (gate, then decode)
@@ -53,6 +56,7 @@ WORKLOADS = {
     4: dict(B=256, Hq=16, Hv=32, T=1, Dk=128, Dv=128, N_slots=512),
     5: dict(B=16, Hq=16, Hv=32, T=1024, Dk=128, Dv=128, N_slots=32),
     6: dict(B=4, Hq=64, Hv=64, T=1024, Dk=64, Dv=512, N_slots=8),
+    7: dict(B=1, Hq=16, Hv=32, T=8192, Dk=128, Dv=128, N_slots=2),
 }
 
 WORKLOAD_NAMES = {
@@ -63,6 +67,7 @@ WORKLOAD_NAMES = {
     4: "gate + decode B=256 Hq=16 Hv=32 T=1 D=128",
     5: "chunked prefill B=16 Hq=16 Hv=32 T=1024 D=128",
     6: "chunked prefill B=4 H=64 T=1024 Dk=64 Dv=512",
+    7: "single-prompt prefill B=1 Hq=16 Hv=32 T=8192 D=128",
 }
 
 
@@ -160,7 +165,7 @@ def make_case(B, Hq, Hv, T, Dk, Dv, N_slots, seed, *, zero_state=False, gk_hi=0.
 
 
 def make_workload(wid: int, gate_inputs: bool = False, batch: Optional[int] = None) -> Inputs:
-    """The seven workloads, seeded with 1000 + id (see the module docstring). ``batch``
+    """The eight workloads, seeded with 1000 + id (see the module docstring). ``batch``
     replaces the batch size B (the recipe is otherwise unchanged; the pool keeps its slots,
     at least B)."""
     w = dict(WORKLOADS[wid])
@@ -178,7 +183,7 @@ def make_workload(wid: int, gate_inputs: bool = False, batch: Optional[int] = No
         inp = make_case(**w, seed=seed, indices="permutation", lengths="uniform")
     elif wid == 4:
         return make_case(**w, seed=seed, indices="choice", gk_hi=0.05, gate=True)
-    elif wid in (5, 6):
+    elif wid in (5, 6, 7):
         inp = make_case(**w, seed=seed, indices="choice")
     else:
         raise KeyError(wid)
