@@ -33,6 +33,7 @@ import torch
 __all__ = ["rgdr_decode", "rgdr_decode_snapshots", "rgdr_decode_gated",
            "rgdr_decode_gated_snapshots", "rgdr_prefill", "rgdr_prefill_gated",
            "rgdr_prefill_ws", "rgdr_prefill_gated_ws", "rgdr_prefill_workspace_size",
+           "rgdr_prefill_noalloc",
            "recurrent_gated_delta_rule", "la_gate",
            "rgdr_validate", "VALIDATE",
            "rgdr_validate_host", "status_string", "library", "LIB_PATH", "RGDR_F32",
@@ -74,6 +75,8 @@ def library():
     lib.rgdr_prefill.argtypes = lib.rgdr_decode.argtypes
     lib.rgdr_prefill_gated.restype = C.c_int
     lib.rgdr_prefill_gated.argtypes = lib.rgdr_decode_gated.argtypes
+    lib.rgdr_prefill_noalloc.restype = C.c_int
+    lib.rgdr_prefill_noalloc.argtypes = lib.rgdr_decode.argtypes
     lib.rgdr_prefill_workspace_size.restype = C.c_int
     lib.rgdr_prefill_workspace_size.argtypes = [i32] * 5 + [C.POINTER(C.c_size_t)]
     lib.rgdr_prefill_ws.restype = C.c_int
@@ -235,6 +238,17 @@ def rgdr_prefill_ws(query, key, value, beta, state_pool, actual_seq_lengths, ssm
     return _plain_call("rgdr_prefill_ws", query, key, value, beta, state_pool,
                        actual_seq_lengths, ssm_state_indices, g, gk, num_accepted_tokens, scale,
                        out, state_out, stream, workspace=workspace)
+
+
+def rgdr_prefill_noalloc(query, key, value, beta, state_pool, actual_seq_lengths,
+                         ssm_state_indices, g, gk, num_accepted_tokens, scale=1.0, *, out=None,
+                         state_out=None, stream=None):
+    """``rgdr_prefill_ws`` whose workspace is the library's fixed 128 MiB device array: the
+    call allocates no device memory itself (``out`` and ``state_out`` are still allocated
+    here when not given). Calls that overlap on one device race on that array."""
+    return _plain_call("rgdr_prefill_noalloc", query, key, value, beta, state_pool,
+                       actual_seq_lengths, ssm_state_indices, g, gk, num_accepted_tokens, scale,
+                       out, state_out, stream)
 
 
 def _plain_call(fn, query, key, value, beta, state_pool, actual_seq_lengths, ssm_state_indices,

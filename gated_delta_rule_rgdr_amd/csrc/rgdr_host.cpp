@@ -64,6 +64,8 @@ extern "C" const char *rgdr_status_string(rgdr_status s) {
     case RGDR_ERR_DTYPE: return "RGDR_ERR_DTYPE: dtype not allowed for this argument";
     case RGDR_ERR_HIP: return "RGDR_ERR_HIP: a HIP runtime call failed";
     case RGDR_ERR_ALIGN: return "RGDR_ERR_ALIGN: a pointer is not aligned as required";
+    case RGDR_ERR_SCRATCH: return "RGDR_ERR_SCRATCH: the call needs more scratch memory than "
+                                  "rgdr_prefill_noalloc's fixed 128 MiB array";
     }
     return "unknown rgdr_status";
 }

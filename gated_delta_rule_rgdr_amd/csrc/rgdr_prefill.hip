@@ -1261,6 +1261,27 @@ static rgdr_status prefill_gated(const void *query, const void *key, const void 
                          D_v, N_slots, lens, idx, nacc, ws, ws_bytes, stream);
 }
 
+// Allocation-free form of rgdr_prefill_ws: the segmented form's workspace is this file-scope
+// device array, held by every device the library runs on until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is a stand-in, not a device
+// address): each device's address is looked up once, with that device current.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+static rgdr_status scratch_address(void **out) {
+    static std::atomic<void *> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RGDR_ERR_HIP;
+    void *p = cached[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return RGDR_ERR_HIP;
+        cached[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return RGDR_OK;
+}
+
 }  // namespace rgdr
 
 extern "C" rgdr_status rgdr_prefill(const void *query, const void *key, const void *value,
@@ -1332,4 +1353,33 @@ extern "C" rgdr_status rgdr_prefill_gated_ws(
                                gate_dtype, state_pool, actual_seq_lengths, ssm_state_indices, gk,
                                num_accepted_tokens, scale, B, H_q, H_v, T, D_k, D_v, N_slots,
                                out, state_out, flags, workspace, workspace_bytes, stream);
+}
+
+extern "C" rgdr_status rgdr_prefill_noalloc(const void *query, const void *key,
+                                            const void *value, const void *beta,
+                                            const void *state_pool,
+                                            const int32_t *actual_seq_lengths,
+                                            const int32_t *ssm_state_indices, const float *g,
+                                            const float *gk,
+                                            const int32_t *num_accepted_tokens, float scale,
+                                            int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                            int32_t D_k, int32_t D_v, int32_t N_slots,
+                                            void *out, void *state_out, hipStream_t stream) {
+    using namespace rgdr;
+    size_t need = 0;
+    if (B > 0 && H_q > 0 && H_v > 0 && T > 0 && T <= kPrefillMaxT && (D_k == 64 || D_k == 128) &&
+        D_v > 0 && D_v % 64 == 0 && D_v <= 4096) {
+        // sizes the other checks refuse fall through to them below
+        const rgdr_status st = rgdr_prefill_workspace_size(B, H_v, T, D_k, D_v, &need);
+        if (st != RGDR_OK) return st;
+        if (need > kScratchBytes) return RGDR_ERR_SCRATCH;
+    }
+    void *ws = nullptr;
+    if (need > 0) {
+        const rgdr_status st = scratch_address(&ws);
+        if (st != RGDR_OK) return st;
+    }
+    return prefill_given(query, key, value, beta, state_pool, actual_seq_lengths,
+                         ssm_state_indices, g, gk, num_accepted_tokens, scale, B, H_q, H_v, T,
+                         D_k, D_v, N_slots, out, state_out, ws, ws ? kScratchBytes : 0, stream);
 }

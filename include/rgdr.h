@@ -62,7 +62,9 @@ typedef enum {
     RGDR_ERR_DUPLICATE = 5,   /* (validate) two batch entries name the same slot           */
     RGDR_ERR_DTYPE = 6,       /* a dtype code not allowed for that argument                 */
     RGDR_ERR_HIP = 7,         /* a HIP runtime call failed                                  */
-    RGDR_ERR_ALIGN = 8        /* a pointer is not aligned as its argument requires          */
+    RGDR_ERR_ALIGN = 8,       /* a pointer is not aligned as its argument requires          */
+    RGDR_ERR_SCRATCH = 9      /* (rgdr_prefill_noalloc) the call needs more scratch memory
+                                 than the library's fixed array holds                       */
 } rgdr_status;
 
 typedef enum { RGDR_F32 = 0, RGDR_F16 = 1, RGDR_BF16 = 2 } rgdr_dtype;
@@ -291,6 +293,28 @@ rgdr_status rgdr_prefill_gated_ws(const void *query, const void *key, const void
                                   int32_t D_v, int32_t N_slots, void *out, void *state_out,
                                   uint32_t flags, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/*
+ * rgdr_prefill_noalloc -- rgdr_prefill_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * arguments as rgdr_prefill, results as rgdr_prefill_ws with a workspace of 128 MiB. The
+ * workspace is a fixed device array inside the library (128 MiB on every device the library
+ * runs on, held until the process ends); the call allocates nothing. The segmented form's
+ * workspace is written before it is read, so nothing in it needs clearing between calls.
+ * Every call on one device uses the same array: calls that may overlap on one device (other
+ * streams, other threads) race and must be ordered by the caller.
+ * Errors: as rgdr_prefill; RGDR_ERR_SCRATCH where the segmented form would need more than
+ * 128 MiB (no call of the library's current segment plan does: its largest takes about
+ * 112 MiB); RGDR_ERR_HIP if the array's device address cannot be looked up.
+ */
+rgdr_status rgdr_prefill_noalloc(const void *query, const void *key, const void *value,
+                                 const void *beta, const void *state_pool,
+                                 const int32_t *actual_seq_lengths,
+                                 const int32_t *ssm_state_indices, const float *g,
+                                 const float *gk, const int32_t *num_accepted_tokens,
+                                 float scale, int32_t B, int32_t H_q, int32_t H_v, int32_t T,
+                                 int32_t D_k, int32_t D_v, int32_t N_slots, void *out,
+                                 void *state_out, hipStream_t stream);
 
 /*
  * la_gate -- decay = decay_scale * softplus(a + dt_bias) and, when beta_out != NULL,

@@ -13,7 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rgdr.h")
 
-OK, NULL, SHAPE, UNSUP, RANGE, DUP, DTYPE, HIP, ALIGN = range(9)
+OK, NULL, SHAPE, UNSUP, RANGE, DUP, DTYPE, HIP, ALIGN, SCRATCH = range(10)
 F32, F16, BF16 = 0, 1, 2
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import gated_delta_rule_rgdr_amd as g
-    for code in range(9):
+    for code in range(10):
         s = g.status_string(code)
         assert s.startswith("RGDR_")
     assert g.status_string(99) == "unknown rgdr_status"
