@@ -891,26 +891,29 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
 
 
 // The segmented form's scan over an entry's segments, for one (entry, value head, 16-column
-// strip). Wave w holds rows 32 w .. 32 w + 31 of the strip in fp32, in the matrix cores'
-// accumulator layout: lane (g, n) = (lane / 16, lane % 16) holds rows 16 rb + 4 g + i (rb =
-// 2 w, 2 w + 1; i < 4) of column n. From the pool's state S, each segment j in order stores S
-// as segment j's incoming state, then takes S = Phi_j S + Psi_j: Psi_j starts each 16 x 16
-// accumulator, and Phi_j S is a 16x16x32 product per (row block, 32-row block of S), with
-// both operands split into bf16 high parts and remainders (three products, fp32
-// accumulation). The accumulators of row blocks 2 p and 2 p + 1 are exactly the B operand of
-// the product over rows 32 p .. + 31 in the same lanes (k slots 4 g .. + 3, then 16 + 4 g ..
-// + 3), so each wave shares its split rows through LDS and reads the others'. Segment
-// j + 1's rows of Phi and Psi are loaded while segment j is computed. S is committed (bf16,
-// round to nearest even) at the segment boundary that is the accepted count n: before
-// segment ceil(n / seg_len), or after the last one.
+// strip). Wave w holds rows 16 w .. 16 w + 15 of the strip in fp32, in the matrix cores'
+// accumulator layout: lane (g, n) = (lane / 16, lane % 16) holds rows 16 w + 4 g + i (i < 4)
+// of column n. From the pool's state S, each segment j in order stores S as segment j's
+// incoming state, then takes S = Phi_j S + Psi_j: Psi_j starts the accumulator, and Phi_j S
+// is a 16x16x32 product per 32-row block p of S, with both operands split into bf16 high
+// parts and remainders (three products, fp32 accumulation). The accumulators of waves 2 p and
+// 2 p + 1 are exactly the B operand of the product over rows 32 p .. + 31 in the same lanes
+// (k slots 4 g .. + 3, then 16 + 4 g .. + 3), so the waves share their split rows through
+// LDS. Each segment's rows of Phi and Psi are loaded SCAN_AHEAD segments before they are
+// used (rotating register sets, no copies), so the chain of segments waits on the products
+// only. S is committed (bf16, round to nearest even) at the segment boundary that is the
+// accepted count n: before segment ceil(n / seg_len), or after the last one.
+constexpr int SCAN_AHEAD = 4;
 template <int DK>
-__global__ __launch_bounds__(2 * DK) void prefill_scan_kernel(
+__global__ __launch_bounds__(4 * DK) void prefill_scan_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nacc) {
-    constexpr int NWV = DK / 32;  // waves: wave w owns the K block (32 rows) w
-    __shared__ uint2 bfr[2][NWV][4][64];  // [segment parity][K block][hi lo x 2 halves][lane]
-    const int strips = a.Dv / 16;
-    const int strip = blockIdx.x % strips, bh = blockIdx.x / strips;
+    constexpr int NWV = DK / 16, NKB = DK / 32;  // waves (row blocks); 32-row blocks of S
+    __shared__ uint2 bfr[2][NWV][2][64];  // [segment parity][row block][hi, lo][lane]
+    // The strips of one head are consecutive items, and the remap keeps consecutive items on
+    // one XCD, so a head's Phi and Psi are fetched into one L2 and read there by all strips.
+    const int strips = a.Dv / 16, it = xcd_item(blockIdx.x, gridDim.x);
+    const int strip = it % strips, bh = it / strips;
     const int h = bh % a.Hv, b = bh / a.Hv;
     const int slot = idx[b];
     if (slot < 0 || slot >= a.N_slots) return;  // skipped entry: no state read or written
@@ -921,87 +924,83 @@ __global__ __launch_bounds__(2 * DK) void prefill_scan_kernel(
     const int nn = lane & 15, g = lane >> 4;
     const int col = strip * 16 + nn;
     const int dw = a.Dv + DK;
-    // this lane's state rows: 16 (2 w + r) + 4 g + i, column col
-    auto srow = [&](int r, int i) { return 32 * w + 16 * r + 4 * g + i; };
-    const size_t pbase = ((size_t)slot * a.Hv + h) * DK * a.Dv + col;
-    f32x4 st[2];
+    const int row0 = 16 * w + 4 * g;  // this lane's state rows row0 .. row0 + 3, column col
+    const size_t tbase = ((size_t)slot * a.Hv + h) * DK * a.Dv;  // the (slot, head) state
+    const uint32_t lofs = (uint32_t)(row0 * a.Dv + col);          // this lane's first element
+    f32x4 st;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[r][i] = bf16_to_f32(a.pool[pbase + (size_t)srow(r, i) * a.Dv]);
-    // Segment j's operands for this lane: A fragments of Phi_j (rows 16 (2 w + r) + nn, k slots
-    // of K block p: 32 p + 4 g .. + 3 and 32 p + 16 + 4 g .. + 3) and Psi_j at the state rows.
-    f32x4 ph[2][NWV][2], ps[2], phn[2][NWV][2], psn[2];
-    auto load_seg = [&](int j) {
-        const float *e = a.ws_e + ((size_t)bh * a.nseg + j) * DK * dw;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float *prow = e + (size_t)(32 * w + 16 * r + nn) * dw + a.Dv;
-#pragma unroll
-            for (int p = 0; p < NWV; ++p) {
-                phn[r][p][0] = *reinterpret_cast<const f32x4 *>(prow + 32 * p + 4 * g);
-                phn[r][p][1] = *reinterpret_cast<const f32x4 *>(prow + 32 * p + 16 + 4 * g);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) psn[r][i] = e[(size_t)srow(r, i) * dw + col];
-        }
+    for (int i = 0; i < 4; ++i) st[i] = bf16_to_f32(a.pool[tbase + lofs + (size_t)i * a.Dv]);
+    // One segment's operands for this lane: A fragments of Phi_j (row 16 w + nn; k slots of
+    // 32-row block p: 32 p + 4 g .. + 3 and 32 p + 16 + 4 g .. + 3) and Psi_j at the state rows.
+    struct Seg {
+        f32x4 ph[NKB][2];
+        f32x4 ps;
     };
-    if (ns > 0) load_seg(0);
-    for (int j = 0;; ++j) {
-        if (j == na) {  // the state after the accepted prefix
+    auto load_seg = [&](Seg &o, int j) {
+        // Unconditional (a segment past the last re-reads the last allocated one, unused),
+        // so that the wait counts stay static.
+        j = min(j, a.nseg - 1);
+        const float *e = a.ws_e + ((size_t)bh * a.nseg + j) * DK * dw;
+        const float *prow = e + (size_t)(16 * w + nn) * dw + a.Dv;
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.pool_out[pbase + (size_t)srow(r, i) * a.Dv] = f32_to_bf16(st[r][i]);
+        for (int p = 0; p < NKB; ++p) {
+            o.ph[p][0] = *reinterpret_cast<const f32x4 *>(prow + 32 * p + 4 * g);
+            o.ph[p][1] = *reinterpret_cast<const f32x4 *>(prow + 32 * p + 16 + 4 * g);
         }
-        if (j == ns) break;
-        float *sin = a.ws_s + ((size_t)bh * a.nseg + j) * DK * a.Dv + col;
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sin[(size_t)srow(r, i) * a.Dv] = st[r][i];
+        for (int i = 0; i < 4; ++i) o.ps[i] = e[(size_t)(row0 + i) * dw + col];
+    };
+    // Segment j with its operands o; then o takes segment j + SCAN_AHEAD. Returns false
+    // once every segment is done.
+    auto step = [&](Seg &o, int j) {
         {
-            uint2 h0, l0, h1, l1;
-            split4(st[0], h0, l0);
-            split4(st[1], h1, l1);
-            bfr[j & 1][w][0][lane] = h0;
-            bfr[j & 1][w][1][lane] = h1;
-            bfr[j & 1][w][2][lane] = l0;
-            bfr[j & 1][w][3][lane] = l1;
+            // The state after the accepted prefix, stored at j == na (otherwise an empty
+            // range drops the stores, which keeps the wait counts static).
+            // (the descriptor is uniform; the lane's offset travels in the vector operand)
+            const auto rc = make_rsrc(a.pool_out + tbase, j == na ? (uint32_t)(DK * a.Dv * 2) : 0u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(st[i]), rc,
+                                                      (lofs + (uint32_t)(i * a.Dv)) * 2, 0, 0);
         }
+        if (j >= ns) return false;
+        float *sin = a.ws_s + ((size_t)bh * a.nseg + j) * DK * a.Dv + (size_t)row0 * a.Dv + col;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            ps[r] = psn[r];
-#pragma unroll
-            for (int p = 0; p < NWV; ++p) {
-                ph[r][p][0] = phn[r][p][0];
-                ph[r][p][1] = phn[r][p][1];
-            }
+        for (int i = 0; i < 4; ++i) sin[(size_t)i * a.Dv] = st[i];
+        {
+            uint2 hi, lo;
+            split4(st, hi, lo);
+            bfr[j & 1][w][0][lane] = hi;
+            bfr[j & 1][w][1][lane] = lo;
         }
-        if (j + 1 < ns) load_seg(j + 1);
-        lds_barrier();  // (LDS only: the next segment's loads stay in flight)
-        bf16x8 bh8[NWV], bl8[NWV];
+        lds_barrier();  // (LDS only: later segments' loads stay in flight)
+        f32x4 acc = o.ps;
 #pragma unroll
-        for (int p = 0; p < NWV; ++p) {
-            bh8[p] = cat8(bfr[j & 1][p][0][lane], bfr[j & 1][p][1][lane]);
-            bl8[p] = cat8(bfr[j & 1][p][2][lane], bfr[j & 1][p][3][lane]);
+        for (int p = 0; p < NKB; ++p) {
+            const bf16x8 bh8 = cat8(bfr[j & 1][2 * p][0][lane], bfr[j & 1][2 * p + 1][0][lane]);
+            const bf16x8 bl8 = cat8(bfr[j & 1][2 * p][1][lane], bfr[j & 1][2 * p + 1][1][lane]);
+            uint2 ah0, al0, ah1, al1;
+            split4(o.ph[p][0], ah0, al0);
+            split4(o.ph[p][1], ah1, al1);
+            const bf16x8 ah = cat8(ah0, ah1), al = cat8(al0, al1);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl8, acc, 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            f32x4 acc = ps[r];
-#pragma unroll
-            for (int p = 0; p < NWV; ++p) {
-                uint2 ah0, al0, ah1, al1;
-                split4(ph[r][p][0], ah0, al0);
-                split4(ph[r][p][1], ah1, al1);
-                const bf16x8 ah = cat8(ah0, ah1), al = cat8(al0, al1);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh8[p], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh8[p], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl8[p], acc, 0, 0, 0);
-            }
-            st[r] = acc;
-        }
+        st = acc;
+        load_seg(o, j + SCAN_AHEAD);
+        return true;
+    };
+    static_assert(SCAN_AHEAD == 4, "four rotating operand sets");
+    Seg s0, s1, s2, s3;
+    load_seg(s0, 0);
+    load_seg(s1, 1);
+    load_seg(s2, 2);
+    load_seg(s3, 3);
+    // The parity buffers of bfr alternate by segment; a segment's writes reach the buffer the
+    // segment before last read only after every wave passed the last segment's barrier.
+    for (int j = 0;; j += SCAN_AHEAD) {
+        if (!step(s0, j) || !step(s1, j + 1) || !step(s2, j + 2) || !step(s3, j + 3)) break;
     }
 }
 
@@ -1110,7 +1109,7 @@ static hipError_t launch_segmented(DecodeArgs &a, int gate, long long B, const S
     hipError_t err = launch_prefill_gate<DK, 2, 1>(gate, a, lens, idx, nacc, stream);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((prefill_scan_kernel<DK>), dim3((unsigned)(B * a.Hv * (a.Dv / 16))),
-                       dim3(2 * DK), 0, stream, a, lens, idx, nacc);
+                       dim3(4 * DK), 0, stream, a, lens, idx, nacc);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     // second pass: each segment from its incoming state, the outputs
