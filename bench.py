@@ -164,6 +164,7 @@ TRAFFIC_PROFILES = {(2, 16): "profiles/rgdr_decode_b16_gqa_d128.md",
                     4: "profiles/rgdr_decode_b256_gqa_d128.md",
                     5: "profiles/rgdr_prefill_b16_t1024_gqa_d128.md",
                     6: "profiles/rgdr_prefill_b4_h64_t1024_dk64_dv512.md",
+                    7: "profiles/rgdr_prefill_segmented_b1_t8192_gqa_d128.md",
                     (3, "snapshots"): "profiles/rgdr_decode_snapshots_varlen_b32_t8_d128.md"}
 
 

@@ -62,11 +62,6 @@ struct DecodeArgs {
     int hold;
     // Per-token states [B, T, H_v, D_k, D_v] bf16 (the snapshot entries; null otherwise).
     uint16_t *snap;
-    // Segmented long-sequence form (caller's workspace): each segment's transfer [Psi | Phi]
-    // fp32 [B, H_v, nseg, D_k, D_v + D_k], and each segment's incoming state fp32
-    // [B, H_v, nseg, D_k, D_v]; seg_len tokens per segment (a multiple of the chunk).
-    float *ws_e, *ws_s;
-    int nseg, seg_len;
 };
 
 // How an item's g and beta arrive: given (bf16 beta, fp32 g), or computed from raw gate

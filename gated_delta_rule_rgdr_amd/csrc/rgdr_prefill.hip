@@ -62,6 +62,14 @@ constexpr int kChunk = 32;           // tokens per chunk
 constexpr float kChunkLog2 = 96.f;
 constexpr float kLog2e = 1.4426950408889634f;  // exp(x) = 2^(x log2 e)
 
+// The segmented form's workspace (a caller's, or the fixed array): each segment's transfer
+// [Psi | Phi] fp32 [B, H_v, nseg, D_k, D_v + D_k], and each segment's incoming state fp32
+// [B, H_v, nseg, D_k, D_v]; seg_len tokens per segment (a multiple of the chunk).
+struct SegArgs {
+    float *ws_e, *ws_s;
+    int nseg, seg_len;
+};
+
 // Waves per SIMD the kernel is compiled for (the register budget).
 #ifndef RGDR_PREFILL_MIN_WAVES
 #define RGDR_PREFILL_MIN_WAVES 2
@@ -287,7 +295,7 @@ __device__ __forceinline__ f32x4 mma16(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f
 template <int DK, int GATE, bool NORM, int NC, int SEG = 0>
 __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nacc) {
+    const int32_t *__restrict__ nacc, const SegArgs sg) {
     static_assert(DK == 64 || DK == 128, "D_k = 64 or 128");
     static_assert(!NORM || GATE != kGateGiven, "q/k normalisation belongs to the fused front end");
     static_assert(NC == 2 || (NC == 4 && DK == 64) || (NC == 1 && DK == 128),
@@ -321,8 +329,8 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     int it = xcd_item(blockIdx.x, gridDim.x), seg = 0;
     if constexpr (SEG != 0) {
         const int tl = it % a.ntiles, rest = it / a.ntiles;
-        seg = rest % a.nseg;
-        it = (rest / a.nseg) * a.ntiles + tl;
+        seg = rest % sg.nseg;
+        it = (rest / sg.nseg) * a.ntiles + tl;
     }
     const Item m = resolve(a, x, it);
     const int L = m.L, n = m.n;
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     // ceil(n / seg_len) segments of the prefix.
     int tbeg = 0, tend = L, ncut = n;
     if constexpr (SEG != 0) {
-        const int sl = a.seg_len, na = (n + sl - 1) / sl;
+        const int sl = sg.seg_len, na = (n + sl - 1) / sl;
         tbeg = seg < na ? seg * sl : n + (seg - na) * sl;
         tend = min(tbeg + sl, seg < na ? n : L);
         if (tbeg >= tend) {  // an empty segment: only the first segment's outputs remain
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
     load_v(t0, len);
     f32x4 S[NRB][NC];
     // The segment's workspace rows (SEG != 0): [entry, head, segment][D_k rows][ncols] fp32.
-    const size_t wrow0 = ((bh * a.nseg + seg) * DK) * (size_t)ncols;
+    const size_t wrow0 = ((bh * sg.nseg + seg) * DK) * (size_t)ncols;
     const uint32_t wlane = (uint32_t)((4 * kg * ncols + colw + NC * n16) * 4);
     if constexpr (SEG == 1) {
         // Psi from zero; Phi from the identity (column D_v + j holds row j's unit vector)
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
                 for (int c = 0; c < NC; ++c)
                     S[rb][c][i] = (colw + NC * n16 + c - a.Dv == 16 * rb + 4 * kg + i) ? 1.f : 0.f;
     } else if constexpr (SEG == 2) {
-        const auto rsw = make_rsrc(a.ws_s + wrow0, cols ? (uint32_t)(DK * ncols * 4) : 0u);
+        const auto rsw = make_rsrc(sg.ws_s + wrow0, cols ? (uint32_t)(DK * ncols * 4) : 0u);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -839,7 +847,7 @@ __global__ __launch_bounds__(256, RGDR_PREFILL_MIN_WAVES) void prefill_kernel(
         len = lenn;
         ++chunk;
         if (SEG == 1 && t0 == tend) {  // the segment's end state diag(c_last) S, in fp32
-            const auto rsw = make_rsrc(a.ws_e + wrow0, cols ? (uint32_t)(DK * ncols * 4) : 0u);
+            const auto rsw = make_rsrc(sg.ws_e + wrow0, cols ? (uint32_t)(DK * ncols * 4) : 0u);
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 const f32x4 cr = *reinterpret_cast<const f32x4 *>(crow + 16 * rb + 4 * kg);
@@ -907,7 +915,7 @@ constexpr int SCAN_AHEAD = 4;
 template <int DK>
 __global__ __launch_bounds__(4 * DK) void prefill_scan_kernel(
     const DecodeArgs a, const int32_t *__restrict__ lens, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nacc) {
+    const int32_t *__restrict__ nacc, const SegArgs sg) {
     constexpr int NWV = DK / 16, NKB = DK / 32;  // waves (row blocks); 32-row blocks of S
     __shared__ uint2 bfr[2][NWV][2][64];  // [segment parity][row block][hi, lo][lane]
     // The strips of one head are consecutive items, and the remap keeps consecutive items on
@@ -918,7 +926,7 @@ __global__ __launch_bounds__(4 * DK) void prefill_scan_kernel(
     const int slot = idx[b];
     if (slot < 0 || slot >= a.N_slots) return;  // skipped entry: no state read or written
     const int L = min(max(lens[b], 0), a.T), n = min(max(nacc[b], 0), L);
-    const int sl_len = a.seg_len, na = (n + sl_len - 1) / sl_len;
+    const int sl_len = sg.seg_len, na = (n + sl_len - 1) / sl_len;
     const int ns = na + (L - n + sl_len - 1) / sl_len;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nn = lane & 15, g = lane >> 4;
@@ -939,8 +947,8 @@ __global__ __launch_bounds__(4 * DK) void prefill_scan_kernel(
     auto load_seg = [&](Seg &o, int j) {
         // Unconditional (a segment past the last re-reads the last allocated one, unused),
         // so that the wait counts stay static.
-        j = min(j, a.nseg - 1);
-        const float *e = a.ws_e + ((size_t)bh * a.nseg + j) * DK * dw;
+        j = min(j, sg.nseg - 1);
+        const float *e = sg.ws_e + ((size_t)bh * sg.nseg + j) * DK * dw;
         const float *prow = e + (size_t)(16 * w + nn) * dw + a.Dv;
 #pragma unroll
         for (int p = 0; p < NKB; ++p) {
@@ -964,7 +972,7 @@ __global__ __launch_bounds__(4 * DK) void prefill_scan_kernel(
                                                       (lofs + (uint32_t)(i * a.Dv)) * 2, 0, 0);
         }
         if (j >= ns) return false;
-        float *sin = a.ws_s + ((size_t)bh * a.nseg + j) * DK * a.Dv + (size_t)row0 * a.Dv + col;
+        float *sin = sg.ws_s + ((size_t)bh * sg.nseg + j) * DK * a.Dv + (size_t)row0 * a.Dv + col;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sin[(size_t)i * a.Dv] = st[i];
         {
@@ -1007,27 +1015,28 @@ __global__ __launch_bounds__(4 * DK) void prefill_scan_kernel(
 // One launch of n_items items, times nseg segments in the segmented passes.
 template <int DK, int GATE, int NC, int SEG = 0>
 static hipError_t launch_prefill(const DecodeArgs &a, const int32_t *lens, const int32_t *idx,
-                                 const int32_t *nacc, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_items * (SEG ? (unsigned)a.nseg : 1u));
+                                 const int32_t *nacc, const SegArgs &sg, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_items * (SEG ? (unsigned)sg.nseg : 1u));
     if constexpr (GATE != kGateGiven) {
         if (a.norm_qk) {
             hipLaunchKernelGGL((prefill_kernel<DK, GATE, true, NC, SEG>), grid, dim3(256), 0,
-                               stream, a, lens, idx, nacc);
+                               stream, a, lens, idx, nacc, sg);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((prefill_kernel<DK, GATE, false, NC, SEG>), grid, dim3(256), 0, stream,
-                       a, lens, idx, nacc);
+                       a, lens, idx, nacc, sg);
     return hipGetLastError();
 }
 
 template <int DK, int NC, int SEG = 0>
 static hipError_t launch_prefill_gate(int gate, const DecodeArgs &a, const int32_t *lens,
                                       const int32_t *idx, const int32_t *nacc,
-                                      hipStream_t stream) {
-    return gate == kGateGiven ? launch_prefill<DK, kGateGiven, NC, SEG>(a, lens, idx, nacc, stream)
-           : gate == kGateF32 ? launch_prefill<DK, kGateF32, NC, SEG>(a, lens, idx, nacc, stream)
-                              : launch_prefill<DK, kGateF16, NC, SEG>(a, lens, idx, nacc, stream);
+                                      hipStream_t stream, const SegArgs &sg = SegArgs{}) {
+    return gate == kGateGiven
+               ? launch_prefill<DK, kGateGiven, NC, SEG>(a, lens, idx, nacc, sg, stream)
+           : gate == kGateF32 ? launch_prefill<DK, kGateF32, NC, SEG>(a, lens, idx, nacc, sg, stream)
+                              : launch_prefill<DK, kGateF16, NC, SEG>(a, lens, idx, nacc, sg, stream);
 }
 
 // Compute units of the current device, queried once per device; 0 if the query fails.
@@ -1098,24 +1107,25 @@ template <int DK>
 static hipError_t launch_segmented(DecodeArgs &a, int gate, long long B, const SegPlan &p,
                                    const int32_t *lens, const int32_t *idx, const int32_t *nacc,
                                    void *ws, hipStream_t stream) {
-    a.ws_e = static_cast<float *>(ws);
-    a.ws_s = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_s);
-    a.nseg = p.nseg;
-    a.seg_len = p.seg_len;
+    SegArgs sg;
+    sg.ws_e = static_cast<float *>(ws);
+    sg.ws_s = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_s);
+    sg.nseg = p.nseg;
+    sg.seg_len = p.seg_len;
     a.item0 = 0;
     // first pass: each segment's [Psi | Phi], D_v + D_k columns in 128-column tiles
     a.ntiles = (a.Dv + DK + 127) / 128;
     a.n_items = (int)(B * a.Hv * a.ntiles);
-    hipError_t err = launch_prefill_gate<DK, 2, 1>(gate, a, lens, idx, nacc, stream);
+    hipError_t err = launch_prefill_gate<DK, 2, 1>(gate, a, lens, idx, nacc, stream, sg);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((prefill_scan_kernel<DK>), dim3((unsigned)(B * a.Hv * (a.Dv / 16))),
-                       dim3(4 * DK), 0, stream, a, lens, idx, nacc);
+                       dim3(4 * DK), 0, stream, a, lens, idx, nacc, sg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     // second pass: each segment from its incoming state, the outputs
     a.ntiles = (a.Dv + 127) / 128;
     a.n_items = (int)(B * a.Hv * a.ntiles);
-    return launch_prefill_gate<DK, 2, 2>(gate, a, lens, idx, nacc, stream);
+    return launch_prefill_gate<DK, 2, 2>(gate, a, lens, idx, nacc, stream, sg);
 }
 
 static rgdr_status prefill_entry(DecodeArgs &a, int gate, int32_t B, int32_t H_q, int32_t H_v,
