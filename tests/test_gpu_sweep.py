@@ -87,3 +87,29 @@ def test_random_snapshots(rg, seed):
     say(f"snapshot case {seed}: B={inp.B} Hq={inp.Hq} Hv={inp.Hv} T={inp.T} Dk={inp.Dk} "
         f"Dv={inp.Dv} L={inp.actual_seq_lengths.tolist()} n={inp.num_accepted_tokens.tolist()}")
     check_snapshots(rg, inp, f"random snapshots {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_segmented(rg, seed):
+    """Random calls of one or two long entries through rgdr_prefill_ws, sized so that the
+    segmented form serves them: ragged lengths, accepted counts anywhere (0 and L included),
+    a skipped slot now and then."""
+    rng = np.random.default_rng(3900 + seed)
+    Hq = int(rng.choice([1, 2]))
+    Hv = Hq * int(rng.choice([1, 2]))
+    Dk = int(rng.choice([64, 128]))
+    Dv = 64 * int(rng.integers(1, 5))
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(520, 1201))
+    lens = rng.integers(0, T + 1, B).astype(np.int32)
+    lens[0] = max(lens[0], 520)
+    inp = workloads.make_case(B, Hq, Hv, T, Dk, Dv, B + 1, seed=3950 + seed, indices="choice",
+                              lengths=lens)
+    inp.num_accepted_tokens = np.array([rng.integers(0, L + 1) for L in lens], np.int32)
+    if B > 1 and rng.random() < 0.3:
+        inp.ssm_state_indices[1] = -1
+    assert rg.rgdr_prefill_workspace_size(B, Hv, T, Dk, Dv) > 0
+    say(f"segmented case {seed}: B={B} Hq={Hq} Hv={Hv} T={T} Dk={Dk} Dv={Dv} "
+        f"L={lens.tolist()} n={inp.num_accepted_tokens.tolist()}")
+    out, st = gpu_decode(inp, fn="rgdr_prefill_ws")
+    check_decode(inp, out, st, oracle_decode(inp), f"random segmented {seed}")
