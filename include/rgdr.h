@@ -27,7 +27,8 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers to row-major, contiguous buffers owned by
  *     the caller. The library allocates nothing and keeps no pointer after returning; a
- *     call that needs scratch memory takes it as a workspace argument.
+ *     call that needs scratch memory takes it as a workspace argument, except
+ *     rgdr_prefill_noalloc, which uses a fixed device array inside the library.
  *   - Calls are asynchronous on `stream` (0 = the null stream). The return value reports
  *     only errors that the host can see before launching (arguments, shapes, alignment,
  *     a failed launch); when it is not RGDR_OK nothing was launched.
