@@ -129,7 +129,7 @@ def segmented_mfma_flops(inp, cus):
     second pass's items per segment (128-column tiles) fill two per compute unit, at most
     16 segments, each a multiple of 32 tokens; the prefix [0, n) and the rest [n, L) are
     cut separately. Each segment is walked in chunks of up to 32 tokens; the first pass
-    carries D_v + D_k columns, the second D_v."""
+    carries D_v + D_k columns and computes no outputs, the second carries D_v."""
     import numpy as np
     per = inp.B * inp.Hv * -(-inp.Dv // 128)
     want = min(16, 2 * cus // per)
@@ -145,11 +145,14 @@ def segmented_mfma_flops(inp, cus):
             for t0 in range(a0, a1, sl):
                 chunks += -(-(min(t0 + sl, a1) - t0) // 32)
     npb, nrb = inp.Dk // 32, inp.Dk // 16
-    big = 4 * (12 * npb + 3 * nrb) * 2 + 18 * npb
-    small = 4 * 18 * 2
-    per_item_chunk = big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2
-    items = inp.Hv * (-(-(inp.Dv + inp.Dk) // 128) + -(-inp.Dv // 128))
-    return chunks * items * per_item_chunk
+    # second pass: the single pass's products at 128-column tiles; first pass: no outputs,
+    # so [c scale q]^T S and the N U products are not issued (the M and N blocks are)
+    big_b, small_b = 4 * (12 * npb + 3 * nrb) * 2 + 18 * npb, 4 * 18 * 2
+    big_a, small_a = 4 * (6 * npb + 3 * nrb) * 2 + 18 * npb, 4 * 9 * 2
+    fl = lambda big, small: big * 16 * 16 * 32 * 2 + small * 16 * 16 * 16 * 2
+    items_a = inp.Hv * -(-(inp.Dv + inp.Dk) // 128)
+    items_b = inp.Hv * -(-inp.Dv // 128)
+    return chunks * (items_a * fl(big_a, small_a) + items_b * fl(big_b, small_b))
 
 
 SOURCES_COMMON = ("gated_delta_rule_rgdr_amd/csrc/rgdr_device.h",
