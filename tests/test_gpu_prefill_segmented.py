@@ -167,3 +167,44 @@ def test_segmented_gated(rg, normalize_qk):
     torch.cuda.synchronize()
     check_gated(inp, out, st, oracle_gated(inp, dtype=dtype, normalize_qk=normalize_qk),
                 f"segmented gated nqk={normalize_qk}")
+
+
+def test_segmented_noalloc_graph_replays(rg):
+    """rgdr_prefill_noalloc captured in a HIP graph (the segmented form's three launches on
+    the library's fixed array, out of place) gives the eager call's bytes of out and the
+    committed slots on each of four replays, with eager work on the device between them."""
+    inp = workloads.make_case(2, 2, 4, 900, 128, 128, 3, seed=8800, indices="choice",
+                              lengths="uniform")
+    inp.actual_seq_lengths[0] = 900
+    inp.num_accepted_tokens[:] = [700, inp.actual_seq_lengths[1]]
+    assert segmented(rg, inp)
+    d = upload(inp)
+    out = torch.empty((inp.B, inp.Hv, inp.T, inp.Dv), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty_like(d["state"])
+
+    def step():
+        rg.rgdr_prefill_noalloc(d["query"], d["key"], d["value"], d["beta"], d["state"],
+                                d["actual_seq_lengths"], d["ssm_state_indices"], d["g"],
+                                d["gk"], d["num_accepted_tokens"], inp.scale, out=out,
+                                state_out=st)
+
+    st.copy_(d["state"])
+    step()  # eager: also fills the library's per-device lookups before the capture
+    torch.cuda.synchronize()
+    want = (dev_to_bits(out), dev_to_bits(st))
+    check_decode(inp, out, st, oracle_decode(inp), "segmented noalloc, eager")
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.zero_()
+        st.copy_(d["state"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_to_bits(out), want[0]), f"replay {rep}: out differs"
+        assert np.array_equal(dev_to_bits(st), want[1]), f"replay {rep}: state differs"
