@@ -305,8 +305,8 @@ rgdr_status rgdr_prefill_gated_ws(const void *query, const void *key, const void
  * Every call on one device uses the same array: calls that may overlap on one device (other
  * streams, other threads) race and must be ordered by the caller.
  * Errors: as rgdr_prefill; RGDR_ERR_SCRATCH where the segmented form would need more than
- * 128 MiB (no call of the library's current segment plan does: its largest takes about
- * 112 MiB); RGDR_ERR_HIP if the array's device address cannot be looked up.
+ * 128 MiB (no call of the library's current segment plan does: its largest takes
+ * 108 MiB); RGDR_ERR_HIP if the array's device address cannot be looked up.
  */
 rgdr_status rgdr_prefill_noalloc(const void *query, const void *key, const void *value,
                                  const void *beta, const void *state_pool,
